@@ -1,0 +1,63 @@
+// Internal helpers shared by the liblsq translation units (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string>
+
+#include "../../include/lsq.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ errors
+namespace lsq {
+void set_error(const char* fmt, ...);
+int fail(int code, const char* fmt, ...);
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+}  // namespace lsq
+
+#define LSQ_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return lsq::fail(LSQ_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), \
+                       __FILE__, __LINE__);                                            \
+  } while (0)
+
+#define LSQ_CHECK(cond, code, ...)              \
+  do {                                          \
+    if (!(cond)) return lsq::fail(code, __VA_ARGS__); \
+  } while (0)
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Two float32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// ------------------------------------------------------------------ timing hooks
+namespace lsq {
+// Kernel families credited by the profiler (lsq_prof_*).
+enum ProfKind { PROF_GEMM_FWD = 0, PROF_GEMM_BWD = 1, PROF_LORA = 2, PROF_ATTN = 3, PROF_OTHER = 4, PROF_N = 5 };
+bool prof_on();
+// Returns an opaque token; prof_end credits flops/bytes to the family.
+int prof_begin(hipStream_t s);
+void prof_end(int token, hipStream_t s, ProfKind kind, double flops, double bytes);
+}  // namespace lsq

@@ -1,0 +1,72 @@
+// Internal interface of the NF4-LoRA GEMM kernels (see gemm.hip).
+#pragma once
+#include "common.h"
+
+namespace lsq {
+
+enum Epi { EPI_BF16 = 0, EPI_F32 = 1, EPI_F32_RESID = 2 };
+
+struct WeightRef {
+  int kind;              // LSQ_W_NF4 / LSQ_W_BF16
+  const void* data;      // packed [N, K/2] or bf16 [N, K]
+  const float* absmax;   // [N, K/64]
+  int N, K;
+};
+
+struct SegEnds {
+  int end[4];
+};
+
+// Forward: out[M, N] = X[M, K] W^T + U[:, seg] Bl^T (+ bias) (+ resid).
+// Columns [seg_end[s-1], seg_end[s]) use U columns [seg_ucol[s], seg_ucol[s] + r).
+struct FwdParams {
+  const uint16_t* X;
+  int64_t ldx;
+  int kind;
+  const void* W;
+  const float* absmax;
+  int M, N, K;
+  const uint16_t* U;     // scaled down-projection, bf16 [M, ldu]; unused when r == 0
+  int ldu;
+  const uint16_t* Bl;    // [N, r]
+  int r;
+  int nseg;
+  int seg_end[4];
+  int seg_ucol[4];
+  const uint16_t* bias;  // [N] or null
+  const float* resid;    // [M, ldc] float32 (EPI_F32_RESID)
+  void* out;
+  int64_t ldc;
+};
+
+// Backward: out[M, K] = dY[M, N] W + G[M, rr] Al[rr, K] (+ resid).
+struct BwdParams {
+  const uint16_t* dY;
+  int64_t ldy;
+  int kind;
+  const void* W;
+  const float* absmax;
+  int M, N, K;
+  const uint16_t* G;     // scaled, bf16 [M, ldg]
+  int64_t ldg;
+  const uint16_t* Al;    // stacked A, bf16 [rr, K]
+  int rr;
+  const float* resid;
+  void* out;
+  int64_t ldc;
+};
+
+int gemm_fwd(const FwdParams& p, int epi, hipStream_t s);
+int gemm_bwd(const BwdParams& p, int epi, hipStream_t s);
+// U[M, rr] = bf16(s X A^T), A = stacked [rr, K].
+int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
+              int64_t ldu, hipStream_t st);
+// G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]); bt_ws holds N * r bf16.
+int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
+           float s, uint16_t* G, int64_t ldg, uint16_t* bt_ws, hipStream_t st);
+// Token-dimension reduction C = S^T L (small_rows: [ns, nl]; else [nl, ns]).
+size_t lora_tn_ws_bytes(int M, int ns, int nl);
+int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
+            float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st);
+
+}  // namespace lsq

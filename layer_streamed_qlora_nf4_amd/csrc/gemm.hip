@@ -1,0 +1,944 @@
+// NF4-LoRA linear kernels for gfx950: the fused dequantize + GEMM + LoRA
+// forward, the transposed-decode backward for dX, and the skinny LoRA GEMMs.
+//
+// The pages run the base linear through bitsandbytes (a fused 4-bit GEMM for
+// few rows, dequantize + matmul otherwise, and a backward that always
+// dequantises because no transposed 4-bit GEMM exists: LS-docs "Bit-exact is
+// two claims, not one"; "v0.76.0 changes the code").  Here both directions
+// decode NF4 inside the GEMM: packed codes and float32 absmax stream from HBM
+// (0.5625 B per weight), each workgroup decodes its weight tile once into LDS
+// as bf16 through a 16-entry level table, and bf16 MFMA 16x16x32 tiles with
+// float32 accumulation consume it.  The LoRA up-projection U B^T (forward) and
+// G A (backward) ride in the same accumulators.  The kernel chosen depends on
+// (M, N, K, r) only, so resident and streamed runs execute identical code.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "gemm.h"
+#include "nf4_levels.h"
+
+namespace lsq {
+namespace {
+
+constexpr int BK = 64;          // reduction step = one NF4 block
+constexpr int NTHREADS = 256;   // 4 waves
+
+// ------------------------------------------------------------------ LDS tiles
+// A tile row r holds 64 bf16 of the reduction dimension as 8 chunks of 16 B;
+// chunk c of row r lives at chunk position c ^ (r & 7), so the 8 lanes of a
+// 128-bit LDS pass read 8 different bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// Transposed weight tile (backward): row = output column k, 64 reduction values.
+// The swizzle also folds in k >> 3 so the transposing writes (rows 8 apart)
+// spread over banks too.
+__device__ __forceinline__ int swzt(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base, int idx) {
+  return *reinterpret_cast<const bf16x8*>(base + idx);
+}
+__device__ __forceinline__ bf16x8 u4_as_frag(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// XCD-aware tile order: consecutive workgroup ids go to different XCDs, so
+// hand each XCD a contiguous range of tiles (row-major over M tiles): the
+// tiles one XCD runs together share their activation rows in its L2.
+__device__ __forceinline__ int remap_tile(int g, int total) {
+  if ((total & 7) != 0) return g;
+  return (g & 7) * (total >> 3) + (g >> 3);
+}
+
+// Decode 8 packed bytes' worth... one 32-bit word = 8 NF4 codes (bytes in
+// memory order, even element in the high nibble) into 4 bf16 pairs.
+__device__ __forceinline__ void decode_word(uint32_t w, float a, const float* lut, uint32_t out[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t byte = (w >> (8 * j)) & 0xFFu;
+    float v0 = lut[byte >> 4] * a;
+    float v1 = lut[byte & 15u] * a;
+    out[j] = pack_bf16x2(v0, v1);
+  }
+}
+
+// =========================================================== forward (NT)
+// C[M, N] = X[M, K] W[N, K]^T + U_seg[M, r] Bl[N, r]^T (+ bias) (+ resid)
+template <int BM, int BN, int WKIND, int EPI>
+__global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  constexpr int A_CHUNKS = BM * 8 / NTHREADS;                                   // 16-B chunks per thread
+  constexpr int B_CHUNKS = (WKIND == LSQ_W_NF4) ? (BN * 2 / NTHREADS) : (BN * 8 / NTHREADS);
+  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const uint16_t* __restrict__ X = p.X;
+  const int K = p.K, nk = K / BK;
+
+  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+  float rabs[B_CHUNKS];
+
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int m = m0 + row;
+      ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(X + (int64_t)m * p.ldx + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if (WKIND == LSQ_W_NF4) {
+      const uint8_t* W = static_cast<const uint8_t*>(p.W);
+#pragma unroll
+      for (int i = 0; i < B_CHUNKS; ++i) {
+        int q = tid + i * NTHREADS, row = q >> 1, h = q & 1;
+        int n = n0 + row;
+        if (n < p.N) {
+          rb[i] = *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16);
+          rabs[i] = p.absmax[(int64_t)n * (K / 64) + kt];
+        } else {
+          rb[i] = make_uint4(0, 0, 0, 0);
+          rabs[i] = 0.f;
+        }
+      }
+    } else {
+      const uint16_t* W = static_cast<const uint16_t*>(p.W);
+#pragma unroll
+      for (int i = 0; i < B_CHUNKS; ++i) {
+        int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+        int n = n0 + row;
+        rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
+    }
+    if (WKIND == LSQ_W_NF4) {
+#pragma unroll
+      for (int i = 0; i < B_CHUNKS; ++i) {
+        int q = tid + i * NTHREADS, row = q >> 1, h = q & 1;
+        uint32_t words[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t o[4];
+          decode_word(words[w], rabs[i], lut, o);
+          *reinterpret_cast<uint4*>(&Bs[buf][swz(row, h * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_CHUNKS; ++i) {
+        int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+        *reinterpret_cast<uint4*>(&Bs[buf][swz(row, c)]) = rb[i];
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_tile(0);
+  __syncthreads();  // lut
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TN];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = lds_frag(Bs[cur], swz(wn * WN + j * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // LoRA up-projection: acc += U_seg B^T, one or more extra 32-wide reduction steps.
+  if (p.r > 0) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col0 = n0 + wn * WN + j * 16;
+      if (col0 >= p.N) continue;
+      int s = 0;
+      while (s + 1 < p.nseg && col0 >= p.seg_end[s]) ++s;
+      const int ucol = p.seg_ucol[s];
+      const int col = col0 + (lane & 15);
+      for (int kc = 0; kc < p.r; kc += 32) {
+        const int kk = kc + 8 * g;
+        uint4 bv = (col < p.N && kk < p.r) ? *reinterpret_cast<const uint4*>(p.Bl + (int64_t)col * p.r + kk)
+                                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = m0 + wm * WM + i * 16 + (lane & 15);
+          uint4 av = (row < p.M && kk < p.r)
+                         ? *reinterpret_cast<const uint4*>(p.U + (int64_t)row * p.ldu + ucol + kk)
+                         : make_uint4(0, 0, 0, 0);
+          acc[i][j] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[i][j]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: lane holds C[4 (lane >> 4) + v][lane & 15] of each 16x16 tile.
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WN + j * 16 + (lane & 15);
+    if (col >= p.N) continue;
+    const float bias = p.bias ? bf16_bits_to_f32(p.bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+        if (row >= p.M) continue;
+        float val = acc[i][j][v] + bias;
+        const int64_t o = (int64_t)row * p.ldc + col;
+        if (EPI == EPI_BF16) {
+          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(val);
+        } else if (EPI == EPI_F32) {
+          static_cast<float*>(p.out)[o] = val;
+        } else {
+          static_cast<float*>(p.out)[o] = p.resid[o] + val;
+        }
+      }
+    }
+  }
+}
+
+// =========================================================== backward (NN)
+// C[M, K] = dY[M, N] W[N, K] + G[M, rr] Al[rr, K] (+ resid)
+// The weight slab (64 rows of W) is decoded straight into a transposed LDS
+// tile Bt[k][n] so that each lane's 8 reduction values are contiguous.
+template <int BM, int BO, int WKIND, int EPI>
+__global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
+  constexpr int WM = BM / 2, WO = BO / 2, TM = WM / 16, TO = WO / 16;
+  constexpr int A_CHUNKS = BM * 8 / NTHREADS;
+  // Transposing loads: each thread owns a 4 (rows n) x 8 (cols k) micro-tile.
+  constexpr int MT_PER_THREAD = (64 / 4) * (BO / 8) / NTHREADS;
+  static_assert(MT_PER_THREAD >= 1, "BO too small");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bt[2][BO * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wo = wave & 1;
+  const int tiles_o = (p.K + BO - 1) / BO;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
+  const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const int K = p.K;
+  const int nk_main = (p.N + BK - 1) / BK;
+  const int nk_lora = (p.rr + BK - 1) / BK;
+  const int nk = nk_main + nk_lora;
+
+  // micro-tile coordinates: lanes 8 apart in q, neighbouring rg pairs in a pass
+  auto mt_coords = [&](int i, int& rg, int& q) {
+    int u = tid + i * NTHREADS;
+    q = (u & 7) | (((u >> 4) & ((BO / 8 / 8) - 1)) << 3);
+    rg = ((u >> 3) & 1) | ((u >> (4 + __builtin_ctz(BO / 64))) << 1);
+  };
+
+  uint4 ra[A_CHUNKS];
+  uint32_t rq[MT_PER_THREAD][4];     // NF4: 4 rows x 4 bytes
+  float rabs[MT_PER_THREAD][4];
+  uint4 rw[MT_PER_THREAD][4];        // bf16: 4 rows x 16 bytes
+
+  auto load_tile = [&](int kt) {
+    const bool lora = kt >= nk_main;
+    const int r0 = (lora ? kt - nk_main : kt) * BK;   // reduction offset
+    const uint16_t* Asrc = lora ? p.G : p.dY;
+    const int64_t lda = lora ? p.ldg : p.ldy;
+    const int red_lim = lora ? p.rr : p.N;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int m = m0 + row, rcol = r0 + c * 8;
+      ra[i] = (m < p.M && rcol < red_lim) ? *reinterpret_cast<const uint4*>(Asrc + (int64_t)m * lda + rcol)
+                                          : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MT_PER_THREAD; ++i) {
+      int rg, q;
+      mt_coords(i, rg, q);
+      const int kcol = o0 + q * 8;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int n = r0 + rg * 4 + rr;
+        const bool ok = n < red_lim && kcol < K;
+        if (!lora && WKIND == LSQ_W_NF4) {
+          const uint8_t* W = static_cast<const uint8_t*>(p.W);
+          rq[i][rr] = ok ? *reinterpret_cast<const uint32_t*>(W + (int64_t)n * (K / 2) + kcol / 2) : 0u;
+          rabs[i][rr] = ok ? p.absmax[(int64_t)n * (K / 64) + kcol / 64] : 0.f;
+        } else {
+          const uint16_t* W = lora ? p.Al : static_cast<const uint16_t*>(p.W);
+          rw[i][rr] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + kcol) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf, int kt) {
+    const bool lora = kt >= nk_main;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < MT_PER_THREAD; ++i) {
+      int rg, q;
+      mt_coords(i, rg, q);
+      // vals[rr][c]: weight (row rg*4+rr, column q*8+c) as bf16 bits
+      uint32_t pairs[4][4];  // pairs[rr][j] = (col 2j, col 2j+1) of row rr
+      if (!lora && WKIND == LSQ_W_NF4) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) decode_word(rq[i][rr], rabs[i][rr], lut, pairs[rr]);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pairs[rr][0] = rw[i][rr].x;
+          pairs[rr][1] = rw[i][rr].y;
+          pairs[rr][2] = rw[i][rr].z;
+          pairs[rr][3] = rw[i][rr].w;
+        }
+      }
+      // Column c of the micro-tile -> 4 consecutive reduction values (rows) = 8 bytes.
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int sel = (c & 1) ? 0x07060302 : 0x05040100;  // pick high or low halves
+        uint32_t lo = __builtin_amdgcn_perm(pairs[1][c >> 1], pairs[0][c >> 1], sel);
+        uint32_t hi = __builtin_amdgcn_perm(pairs[3][c >> 1], pairs[2][c >> 1], sel);
+        const int krow = q * 8 + c;
+        const int nbase = rg * 4;   // 0..60, chunk nbase/8, half (nbase%8)/4
+        uint16_t* dst = &Bt[buf][swzt(krow, nbase >> 3) + (nbase & 7)];
+        *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+      }
+    }
+  };
+
+  f32x4 acc[TM][TO];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_tile(0);
+  __syncthreads();
+  store_tile(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TO];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TO; ++j) bfr[j] = lds_frag(Bt[cur], swzt(wo * WO + j * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TO; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1, kt + 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < TO; ++j) {
+    const int col = o0 + wo * WO + j * 16 + (lane & 15);
+    if (col >= K) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+        if (row >= p.M) continue;
+        const int64_t o = (int64_t)row * p.ldc + col;
+        float val = acc[i][j][v];
+        if (EPI == EPI_BF16) {
+          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(val);
+        } else if (EPI == EPI_F32) {
+          static_cast<float*>(p.out)[o] = val;
+        } else {
+          static_cast<float*>(p.out)[o] = p.resid[o] + val;
+        }
+      }
+    }
+  }
+}
+
+// =========================================================== LoRA down: U = s X A^T
+// One workgroup per 16 rows; the 4 waves split K and their partial 16 x rr
+// tiles are summed in LDS in wave order (fixed, deterministic).
+__global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M, int K,
+                                                             const uint16_t* __restrict__ A, int rr, float s,
+                                                             uint16_t* __restrict__ U, int64_t ldu) {
+  __shared__ float part[4][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 16;
+  const int nct = (rr + 15) / 16;
+  const int kq = ((K / 32 + 3) / 4) * 32;  // per-wave K range, multiple of 32
+  const int kb = wave * kq, ke = min(K, kb + kq);
+  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  const int row = m0 + (lane & 15);
+  const int g = lane >> 4;
+  for (int k = kb; k < ke; k += 32) {
+    const int kk = k + 8 * g;
+    uint4 av = (row < M && kk < K) ? *reinterpret_cast<const uint4*>(X + (int64_t)row * ldx + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nct) break;
+      const int c = ct * 16 + (lane & 15);
+      uint4 bv = (c < rr && kk < K) ? *reinterpret_cast<const uint4*>(A + (int64_t)c * K + kk) : make_uint4(0, 0, 0, 0);
+      acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    if (ct >= nct) break;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
+  }
+  __syncthreads();
+  for (int e = tid; e < 16 * rr; e += NTHREADS) {
+    const int r = e / rr, c = e % rr;
+    if (m0 + r >= M) continue;
+    float v = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
+    U[(int64_t)(m0 + r) * ldu + c] = f32_to_bf16_bits(s * v);
+  }
+}
+
+// B [N, r] -> Bt [r, N] (bf16), so the G kernel reads 8 reduction values contiguously.
+__global__ void transpose_rows_kernel(const uint16_t* __restrict__ B, int N, int r, uint16_t* __restrict__ Bt) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)N * r) return;
+  int n = e / r, j = e % r;
+  Bt[(int64_t)j * N + n] = B[e];
+}
+
+// =========================================================== LoRA G = s dY_seg B_seg
+// One workgroup per 16 rows; for each segment the waves split its N range.
+__global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __restrict__ dY, int64_t ldy, int M, int N,
+                                                          const uint16_t* __restrict__ Bt, int r, int nseg,
+                                                          SegEnds segs, float s, uint16_t* __restrict__ G,
+                                                          int64_t ldg) {
+  __shared__ float part[4][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 16;
+  const int row = m0 + (lane & 15), g = lane >> 4;
+  const int nct = (r + 15) / 16;
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    const int nb = sgi == 0 ? 0 : segs.end[sgi - 1], ne = segs.end[sgi];
+    const int len = ne - nb;
+    const int q = (((len + 31) / 32 + 3) / 4) * 32;  // per-wave share, whole 32-chunks
+    const int kb = nb + wave * q, ke = min(ne, kb + q);
+    f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    for (int k = kb; k < ke; k += 32) {
+      const int kk = k + 8 * g;
+      uint4 av = (row < M && kk < ne) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct >= nct) break;
+        const int c = ct * 16 + (lane & 15);
+        uint4 bv = (c < r && kk < ne) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
+        acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nct) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * r; e += NTHREADS) {
+      const int rrow = e / r, c = e % r;
+      if (m0 + rrow >= M) continue;
+      float v = ((part[0][rrow][c] + part[1][rrow][c]) + part[2][rrow][c]) + part[3][rrow][c];
+      G[(int64_t)(m0 + rrow) * ldg + sgi * r + c] = f32_to_bf16_bits(s * v);
+    }
+  }
+}
+
+// =========================================================== LoRA weight grads
+// C = S^T L over the token dimension M: S [M, ns] (ns <= 64), L [M, nl].
+// SMALL_ROWS: C[ns, nl] row-major (dA = G^T X);  else C[nl, ns] (dB = dY^T U).
+// Grid: (nl / 64 column tiles) x splits; each split sums a fixed token range;
+// with splits > 1 the partials land in ws and reduce_splits adds them in order.
+template <bool SMALL_ROWS>
+__global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __restrict__ S, int64_t lds_, int ns,
+                                                           const uint16_t* __restrict__ Lm, int64_t ldl, int nl, int M,
+                                                           int rows_per_split, float* __restrict__ out,
+                                                           int64_t ldo, int accumulate, int direct) {
+  __shared__ float sL[32][65];
+  __shared__ float sS[32][65];
+  const int tid = threadIdx.x;
+  const int l0 = blockIdx.x * 64;
+  const int split = blockIdx.y;
+  const int mb = split * rows_per_split, me = min(M, mb + rows_per_split);
+  const int li = tid & 63, sg = tid >> 6;  // this thread: column l0+li, small indices sg, sg+4, ...
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int m = mb; m < me; m += 32) {
+    // stage 32 rows x 64 cols of L and 32 x ns of S as float
+    for (int e = tid; e < 32 * 8; e += NTHREADS) {
+      const int rr = e >> 3, c8 = (e & 7) * 8;
+      const int mm = m + rr, col = l0 + c8;
+      uint4 v = (mm < me && col < nl) ? *reinterpret_cast<const uint4*>(Lm + (int64_t)mm * ldl + col) : make_uint4(0, 0, 0, 0);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sL[rr][c8 + 2 * j] = bf_lo(w[j]);
+        sL[rr][c8 + 2 * j + 1] = bf_hi(w[j]);
+      }
+    }
+    for (int e = tid; e < 32 * ns; e += NTHREADS) {
+      const int rr = e / ns, c = e % ns;
+      const int mm = m + rr;
+      sS[rr][c] = (mm < me) ? bf16_bits_to_f32(S[(int64_t)mm * lds_ + c]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      const float lv = sL[rr][li];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = sg + 4 * i;
+        if (c < ns) acc[i] = fmaf(sS[rr][c], lv, acc[i]);
+      }
+    }
+    __syncthreads();
+  }
+  const int col = l0 + li;
+  if (col >= nl) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = sg + 4 * i;
+    if (c >= ns) continue;
+    const int64_t o = SMALL_ROWS ? (int64_t)c * ldo + col : (int64_t)col * ldo + c;
+    if (direct) {
+      out[o] = accumulate ? out[o] + acc[i] : acc[i];
+    } else {
+      out[(int64_t)split * ((int64_t)ns * nl) + (SMALL_ROWS ? (int64_t)c * nl + col : (int64_t)col * ns + c)] = acc[i];
+    }
+  }
+}
+
+// out[i, j] (+)= sum over splits, in split order.  Partials are packed [splits][rows][cols].
+__global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int rows, int cols,
+                                     float* __restrict__ out, int64_t ldo, int accumulate) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)rows * cols;
+  if (e >= n) return;
+  float v = 0.f;
+  for (int sp = 0; sp < splits; ++sp) v += part[sp * n + e];
+  const int64_t o = (e / cols) * ldo + (e % cols);
+  out[o] = accumulate ? out[o] + v : v;
+}
+
+// =========================================================== float32 variants
+// The float32 tier: dequantized weights are the exact float32 products and
+// every product is accumulated in float32, one output per thread in a fixed
+// order.  Used for the single-linear float32 checks, not on the hot path.
+__device__ __forceinline__ float w_f32(const lsq::WeightRef& W, int n, int k) {
+  if (W.kind == LSQ_W_NF4) {
+    const uint8_t byte = static_cast<const uint8_t*>(W.data)[(int64_t)n * (W.K / 2) + k / 2];
+    const uint32_t code = (k & 1) ? (byte & 15u) : (byte >> 4);
+    return kNF4LevelsDev[code] * W.absmax[(int64_t)n * (W.K / 64) + k / 64];
+  }
+  return bf16_bits_to_f32(static_cast<const uint16_t*>(W.data)[(int64_t)n * W.K + k]);
+}
+
+__global__ void f32_lora_down_kernel(const float* X, int M, int K, const float* A, int r, float s, float* U) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * r) return;
+  int m = e / r, j = e % r;
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) acc = fmaf(X[(int64_t)m * K + k], A[(int64_t)j * K + k], acc);
+  U[e] = s * acc;
+}
+
+__global__ void f32_linear_fwd_kernel(const float* X, int M, lsq::WeightRef W, const float* U, const float* Bl, int r,
+                                      const uint16_t* bias, float* Y) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)M * W.N) return;
+  int m = e / W.N, n = e % W.N;
+  float acc = 0.f;
+  for (int k = 0; k < W.K; ++k) acc = fmaf(X[(int64_t)m * W.K + k], w_f32(W, n, k), acc);
+  float lo = 0.f;
+  for (int j = 0; j < r; ++j) lo = fmaf(U[(int64_t)m * r + j], Bl[(int64_t)n * r + j], lo);
+  Y[e] = acc + lo + (bias ? bf16_bits_to_f32(bias[n]) : 0.f);
+}
+
+__global__ void f32_g_kernel(const float* dY, int M, int N, const float* Bl, int r, float s, float* G) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * r) return;
+  int m = e / r, j = e % r;
+  float acc = 0.f;
+  for (int n = 0; n < N; ++n) acc = fmaf(dY[(int64_t)m * N + n], Bl[(int64_t)n * r + j], acc);
+  G[e] = s * acc;
+}
+
+__global__ void f32_linear_dx_kernel(const float* dY, int M, lsq::WeightRef W, const float* G, const float* A, int r,
+                                     float* dX) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)M * W.K) return;
+  int m = e / W.K, k = e % W.K;
+  float acc = 0.f;
+  for (int n = 0; n < W.N; ++n) acc = fmaf(dY[(int64_t)m * W.N + n], w_f32(W, n, k), acc);
+  float lo = 0.f;
+  for (int j = 0; j < r; ++j) lo = fmaf(G[(int64_t)m * r + j], A[(int64_t)j * W.K + k], lo);
+  dX[e] = acc + lo;
+}
+
+// C[a, b] (+)= sum_m P[m, a] Q[m, b]   (dA = G^T X with P = G; dB = dY^T U with P = dY)
+__global__ void f32_tn_kernel(const float* P, int na, const float* Q, int nb, int M, float* C, int accumulate) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)na * nb) return;
+  int a = e / nb, b = e % nb;
+  float acc = 0.f;
+  for (int m = 0; m < M; ++m) acc = fmaf(P[(int64_t)m * na + a], Q[(int64_t)m * nb + b], acc);
+  C[e] = accumulate ? C[e] + acc : acc;
+}
+
+template <int BM, int BN, int WK, int EPI>
+void launch_fwd(const FwdParams& p, hipStream_t s) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  gemm_fwd_kernel<BM, BN, WK, EPI><<<tiles, NTHREADS, 0, s>>>(p);
+}
+
+template <int BM, int BO, int WK, int EPI>
+void launch_bwd(const BwdParams& p, hipStream_t s) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.K + BO - 1) / BO);
+  gemm_bwd_kernel<BM, BO, WK, EPI><<<tiles, NTHREADS, 0, s>>>(p);
+}
+
+template <int BM, int BN, int WK>
+void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s) {
+  if (epi == EPI_BF16) launch_fwd<BM, BN, WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_fwd<BM, BN, WK, EPI_F32>(p, s);
+  else launch_fwd<BM, BN, WK, EPI_F32_RESID>(p, s);
+}
+
+template <int BM, int BO, int WK>
+void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
+  if (epi == EPI_BF16) launch_bwd<BM, BO, WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_bwd<BM, BO, WK, EPI_F32>(p, s);
+  else launch_bwd<BM, BO, WK, EPI_F32_RESID>(p, s);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+int gemm_fwd(const FwdParams& p, int epi, hipStream_t s) {
+  LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
+  LSQ_CHECK(p.r == 0 || (p.r % 8 == 0 && p.ldu % 8 == 0), LSQ_ERR_SHAPE, "gemm: LoRA rank must be a multiple of 8");
+  if (p.M == 0 || p.N == 0) return LSQ_OK;
+  const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.N * p.r;
+  const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
+  const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
+  int tok = prof_begin(s);
+  // 128 x 128 tiles, 4 waves of 64 x 64.
+  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<128, 128, LSQ_W_NF4>(p, epi, s);
+  else dispatch_fwd_epi<128, 128, LSQ_W_BF16>(p, epi, s);
+  prof_end(tok, s, PROF_GEMM_FWD, flops, bytes);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int gemm_bwd(const BwdParams& p, int epi, hipStream_t s) {
+  LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
+  LSQ_CHECK(p.N % 8 == 0 && p.rr % 8 == 0 && p.ldy % 8 == 0 && p.ldg % 8 == 0, LSQ_ERR_SHAPE,
+            "gemm_bwd: N=%d and rank %d must be multiples of 8", p.N, p.rr);
+  if (p.M == 0 || p.K == 0) return LSQ_OK;
+  const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
+  const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
+  const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
+  int tok = prof_begin(s);
+  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<128, 128, LSQ_W_NF4>(p, epi, s);
+  else dispatch_bwd_epi<128, 128, LSQ_W_BF16>(p, epi, s);
+  prof_end(tok, s, PROF_GEMM_BWD, flops, bytes);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
+              int64_t ldu, hipStream_t st) {
+  LSQ_CHECK(rr >= 1 && rr <= 64 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr, K);
+  if (M == 0) return LSQ_OK;
+  int tok = prof_begin(st);
+  lora_down_kernel<<<(M + 15) / 16, NTHREADS, 0, st>>>(X, ldx, M, K, A, rr, s, U, ldu);
+  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)K * rr, 2.0 * M * (double)K + 2.0 * rr * K + 2.0 * M * rr);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
+           float s, uint16_t* G, int64_t ldg, uint16_t* bt_ws, hipStream_t st) {
+  LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4, LSQ_ERR_SHAPE, "lora_g: bad rank/segments");
+  if (M == 0) return LSQ_OK;
+  int tok = prof_begin(st);
+  const int64_t nel = (int64_t)N * r;
+  transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, st>>>(B, N, r, bt_ws);
+  lora_g_kernel<<<(M + 15) / 16, NTHREADS, 0, st>>>(dY, ldy, M, N, bt_ws, r, nseg, segs, s, G, ldg);
+  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)N * r, 2.0 * M * (double)N + 4.0 * N * r + 2.0 * M * r * nseg);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+size_t lora_tn_ws_bytes(int M, int ns, int nl) {
+  int tiles = (nl + 63) / 64;
+  int splits = std::max(1, std::min((M + 255) / 256, (512 + tiles - 1) / tiles));
+  return splits > 1 ? (size_t)splits * ns * nl * sizeof(float) : 0;
+}
+
+int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
+            float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
+  LSQ_CHECK(ns >= 1 && ns <= 64, LSQ_ERR_SHAPE, "lora_tn: small dim %d unsupported", ns);
+  LSQ_CHECK(nl % 8 == 0 && ldl % 8 == 0, LSQ_ERR_SHAPE, "lora_tn: large dim must be a multiple of 8");
+  const int tiles = (nl + 63) / 64;
+  const int splits = std::max(1, std::min((M + 255) / 256, (512 + tiles - 1) / tiles));
+  const int rows_per_split = ((M + splits - 1) / splits + 31) / 32 * 32;
+  const bool direct = splits == 1;
+  LSQ_CHECK(direct || (ws && ws_bytes >= lora_tn_ws_bytes(M, ns, nl)), LSQ_ERR_WORKSPACE, "lora_tn: workspace too small");
+  if (M == 0) {
+    if (!accumulate) {
+      for (int i = 0; i < (small_rows ? ns : nl); ++i)
+        LSQ_HIP(hipMemsetAsync(out + (int64_t)i * ldo, 0, sizeof(float) * (small_rows ? nl : ns), st));
+    }
+    return LSQ_OK;
+  }
+  int tok = prof_begin(st);
+  dim3 grid(tiles, splits);
+  if (small_rows)
+    lora_tn_kernel<true><<<grid, NTHREADS, 0, st>>>(S, lds_, ns, L, ldl, nl, M, rows_per_split, direct ? out : ws, ldo,
+                                                    accumulate, direct ? 1 : 0);
+  else
+    lora_tn_kernel<false><<<grid, NTHREADS, 0, st>>>(S, lds_, ns, L, ldl, nl, M, rows_per_split, direct ? out : ws, ldo,
+                                                     accumulate, direct ? 1 : 0);
+  if (!direct) {
+    const int rows = small_rows ? ns : nl, cols = small_rows ? nl : ns;
+    const int64_t n = (int64_t)rows * cols;
+    reduce_splits_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(ws, splits, rows, cols, out, ldo, accumulate);
+  }
+  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)ns * nl, 2.0 * M * (double)(ns + nl) + 4.0 * ns * nl);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+}  // namespace lsq
+
+// ================================================================== C ABI
+namespace {
+using namespace lsq;
+
+int check_weight(const lsq_weight* W) {
+  LSQ_CHECK(W && W->data, LSQ_ERR_INVALID, "weight: null");
+  LSQ_CHECK(W->kind == LSQ_W_NF4 || W->kind == LSQ_W_BF16, LSQ_ERR_INVALID, "weight: bad kind %d", W->kind);
+  LSQ_CHECK(W->kind == LSQ_W_BF16 || W->absmax, LSQ_ERR_INVALID, "weight: NF4 needs absmax");
+  LSQ_CHECK(W->n_out > 0 && W->n_in > 0 && W->n_in % 64 == 0 && W->n_out < (1 << 30) && W->n_in < (1 << 30),
+            LSQ_ERR_SHAPE, "weight: n_in must be a positive multiple of 64 (got %lld x %lld)", (long long)W->n_out,
+            (long long)W->n_in);
+  LSQ_CHECK(aligned16(W->data) && (!W->absmax || aligned16(W->absmax)), LSQ_ERR_ALIGN, "weight: unaligned pointer");
+  return LSQ_OK;
+}
+
+WeightRef ref_of(const lsq_weight* W) {
+  return WeightRef{W->kind, W->data, W->absmax, (int)W->n_out, (int)W->n_in};
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+size_t nf4_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
+  const size_t el = dtype == LSQ_F32 ? 4 : 2;
+  size_t b = align256(M * r * el) * 2             // U (recomputed or forward scratch) and G
+             + align256(N * r * 2);               // B transposed
+  b += align256(lora_tn_ws_bytes((int)M, r, (int)K)) + align256(lora_tn_ws_bytes((int)M, r, (int)N));
+  return b + 256;
+}
+
+int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, int64_t M, const void* A,
+                        const void* B, int32_t r, float scale, int32_t dtype, void* Y, void* U_out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (int e = check_weight(W)) return e;
+  LSQ_CHECK(X && A && B && Y, LSQ_ERR_INVALID, "linear_fwd: null pointer");
+  LSQ_CHECK(dtype == LSQ_BF16 || dtype == LSQ_F32, LSQ_ERR_INVALID, "linear_fwd: bad dtype");
+  LSQ_CHECK(M >= 0 && M < (1 << 30) && r >= 8 && r <= 64 && r % 8 == 0, LSQ_ERR_SHAPE,
+            "linear_fwd: need 0 <= M, r in {8, 16, ..., 64} (got M=%lld r=%d)", (long long)M, r);
+  LSQ_CHECK(aligned16(X) && aligned16(A) && aligned16(B) && aligned16(Y) && (!U_out || aligned16(U_out)) &&
+                (!bias || aligned16(bias)) && (!ws || aligned16(ws)),
+            LSQ_ERR_ALIGN, "linear_fwd: unaligned pointer");
+  const size_t need = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype);
+  LSQ_CHECK(U_out || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
+  hipStream_t s = as_stream(stream);
+  const WeightRef w = ref_of(W);
+  const int Mi = (int)M;
+  if (dtype == LSQ_F32) {
+    float* U = U_out ? static_cast<float*>(U_out) : static_cast<float*>(ws);
+    f32_lora_down_kernel<<<(Mi * r + 255) / 256, 256, 0, s>>>(static_cast<const float*>(X), Mi, w.K,
+                                                             static_cast<const float*>(A), r, scale, U);
+    const int64_t n = (int64_t)Mi * w.N;
+    if (n > 0)
+      f32_linear_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const float*>(X), Mi, w, U,
+                                                                       static_cast<const float*>(B), r,
+                                                                       static_cast<const uint16_t*>(bias),
+                                                                       static_cast<float*>(Y));
+    LSQ_HIP(hipGetLastError());
+    return LSQ_OK;
+  }
+  uint16_t* U = U_out ? static_cast<uint16_t*>(U_out) : static_cast<uint16_t*>(ws);
+  if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale, U,
+                        r, s))
+    return e;
+  FwdParams p{};
+  p.X = static_cast<const uint16_t*>(X);
+  p.ldx = w.K;
+  p.kind = w.kind;
+  p.W = w.data;
+  p.absmax = w.absmax;
+  p.M = Mi;
+  p.N = w.N;
+  p.K = w.K;
+  p.U = U;
+  p.ldu = r;
+  p.Bl = static_cast<const uint16_t*>(B);
+  p.r = r;
+  p.nseg = 1;
+  p.seg_end[0] = w.N;
+  p.seg_ucol[0] = 0;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = Y;
+  p.ldc = w.N;
+  return gemm_fwd(p, EPI_BF16, s);
+}
+
+int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, int64_t M, const void* A,
+                        const void* B, int32_t r, float scale, int32_t dtype, const void* dY, void* dX, float* dA,
+                        float* dB, int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_weight(W)) return e;
+  LSQ_CHECK(X && A && B && dY && dX && dA && dB, LSQ_ERR_INVALID, "linear_bwd: null pointer");
+  LSQ_CHECK(dtype == LSQ_BF16 || dtype == LSQ_F32, LSQ_ERR_INVALID, "linear_bwd: bad dtype");
+  LSQ_CHECK(M >= 0 && M < (1 << 30) && r >= 8 && r <= 64 && r % 8 == 0, LSQ_ERR_SHAPE, "linear_bwd: bad M or r");
+  LSQ_CHECK(aligned16(X) && aligned16(A) && aligned16(B) && aligned16(dY) && aligned16(dX) && aligned16(dA) &&
+                aligned16(dB) && (!U_in || aligned16(U_in)) && (!ws || aligned16(ws)),
+            LSQ_ERR_ALIGN, "linear_bwd: unaligned pointer");
+  const size_t need = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype);
+  LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_bwd: workspace %zu < %zu", ws_bytes, need);
+  hipStream_t s = as_stream(stream);
+  const WeightRef w = ref_of(W);
+  const int Mi = (int)M;
+  char* wsp = static_cast<char*>(ws);
+  const size_t el = dtype == LSQ_F32 ? 4 : 2;
+  void* Uw = wsp;
+  wsp += align256((size_t)Mi * r * el);
+  void* Gw = wsp;
+  wsp += align256((size_t)Mi * r * el);
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(wsp);
+  wsp += align256((size_t)w.N * r * 2);
+  float* tn1 = reinterpret_cast<float*>(wsp);
+  const size_t tn1_b = align256(lora_tn_ws_bytes(Mi, r, w.K));
+  wsp += tn1_b;
+  float* tn2 = reinterpret_cast<float*>(wsp);
+  const size_t tn2_b = align256(lora_tn_ws_bytes(Mi, r, w.N));
+
+  if (dtype == LSQ_F32) {
+    const float* U = static_cast<const float*>(U_in);
+    if (!U) {
+      f32_lora_down_kernel<<<(Mi * r + 255) / 256, 256, 0, s>>>(static_cast<const float*>(X), Mi, w.K,
+                                                               static_cast<const float*>(A), r, scale,
+                                                               static_cast<float*>(Uw));
+      U = static_cast<const float*>(Uw);
+    }
+    float* G = static_cast<float*>(Gw);
+    f32_g_kernel<<<(Mi * r + 255) / 256, 256, 0, s>>>(static_cast<const float*>(dY), Mi, w.N,
+                                                     static_cast<const float*>(B), r, scale, G);
+    const int64_t nx = (int64_t)Mi * w.K;
+    if (nx > 0)
+      f32_linear_dx_kernel<<<(unsigned)((nx + 255) / 256), 256, 0, s>>>(static_cast<const float*>(dY), Mi, w, G,
+                                                                        static_cast<const float*>(A), r,
+                                                                        static_cast<float*>(dX));
+    f32_tn_kernel<<<(unsigned)((r * w.K + 255) / 256), 256, 0, s>>>(G, r, static_cast<const float*>(X), w.K, Mi, dA,
+                                                                    accumulate);
+    f32_tn_kernel<<<(unsigned)((w.N * r + 255) / 256), 256, 0, s>>>(static_cast<const float*>(dY), w.N, U, r, Mi, dB,
+                                                                    accumulate);
+    LSQ_HIP(hipGetLastError());
+    return LSQ_OK;
+  }
+  const uint16_t* U = static_cast<const uint16_t*>(U_in);
+  if (!U) {
+    if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale,
+                          static_cast<uint16_t*>(Uw), r, s))
+      return e;
+    U = static_cast<const uint16_t*>(Uw);
+  }
+  uint16_t* G = static_cast<uint16_t*>(Gw);
+  SegEnds segs{};
+  segs.end[0] = w.N;
+  if (int e = lora_g(static_cast<const uint16_t*>(dY), w.N, Mi, w.N, static_cast<const uint16_t*>(B), r, 1, segs,
+                     scale, G, r, Bt, s))
+    return e;
+  BwdParams p{};
+  p.dY = static_cast<const uint16_t*>(dY);
+  p.ldy = w.N;
+  p.kind = w.kind;
+  p.W = w.data;
+  p.absmax = w.absmax;
+  p.M = Mi;
+  p.N = w.N;
+  p.K = w.K;
+  p.G = G;
+  p.ldg = r;
+  p.Al = static_cast<const uint16_t*>(A);
+  p.rr = r;
+  p.out = dX;
+  p.ldc = w.K;
+  if (int e = gemm_bwd(p, EPI_BF16, s)) return e;
+  if (int e = lora_tn(G, r, r, static_cast<const uint16_t*>(X), w.K, w.K, Mi, true, dA, w.K, accumulate, tn1, tn1_b, s))
+    return e;
+  return lora_tn(U, r, r, static_cast<const uint16_t*>(dY), w.N, w.N, Mi, false, dB, r, accumulate, tn2, tn2_b, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// NF4 blockwise quantize / dequantize (gfx950).
+//
+// The shard store is written once, offline, quantising each frozen linear to
+// NF4 as it goes (LS-docs "Shard cache"; About).  Format: 64-element blocks
+// along a row, one float32 absmax per block, code = nearest NormalFloat-4
+// level to fp32(x / absmax), even element in the high nibble.  These kernels
+// are HBM-bound: 2 B read + 0.5625 B written per weight (quantize) and the
+// reverse (dequantize).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+#include "nf4_levels.h"
+
+namespace {
+
+struct Thresholds {
+  float t[16];  // t[j] = largest float32 <= midpoint(level j, level j+1); t[15] unused
+};
+
+// x / a > t[j]  <=>  x / a lies strictly above the exact midpoint, for every
+// float32 quotient: t[j] is the midpoint rounded toward -inf, so no float32
+// value lies strictly between t[j] and the midpoint.  An exact tie therefore
+// goes to the lower level.
+Thresholds make_thresholds() {
+  Thresholds th{};
+  for (int j = 0; j < 15; ++j) {
+    double m = (static_cast<double>(lsq::kNF4Levels[j]) + static_cast<double>(lsq::kNF4Levels[j + 1])) * 0.5;
+    float t = static_cast<float>(m);
+    if (static_cast<double>(t) > m) t = nextafterf(t, -INFINITY);
+    th.t[j] = t;
+  }
+  th.t[15] = INFINITY;
+  return th;
+}
+
+__device__ __forceinline__ uint32_t code_of(float n, const Thresholds& th) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (n > th.t[j]) ? 1u : 0u;
+  return c;
+}
+
+// One thread per 64-element block.
+__global__ void __launch_bounds__(256) nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t n_blocks,
+                                                           uint8_t* __restrict__ packed, float* __restrict__ absmax,
+                                                           int32_t* __restrict__ flag, Thresholds th) {
+  int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= n_blocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(w + b * 64);
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = src[i];
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(v);
+  float a = 0.f;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float lo = bf_lo(u[i]), hi = bf_hi(u[i]);
+    finite = finite && isfinite(lo) && isfinite(hi);
+    a = fmaxf(a, fmaxf(fabsf(lo), fabsf(hi)));
+  }
+  if (!finite && flag) atomicOr(flag, 1);
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t pair = u[i * 4 + j];  // elements 2(4i+j) (low half) and 2(4i+j)+1 (high half)
+      float e0 = bf_lo(pair), e1 = bf_hi(pair);
+      uint32_t c0 = 7, c1 = 7;
+      if (a > 0.f) {
+        c0 = code_of(e0 / a, th);
+        c1 = code_of(e1 / a, th);
+      }
+      word |= ((c0 << 4) | c1) << (8 * j);
+    }
+    out[i] = word;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(packed + b * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  absmax[b] = a;
+}
+
+// One thread per 8 packed bytes (16 weights, inside one block).
+template <bool OUT_F32>
+__global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ packed,
+                                                          const float* __restrict__ absmax, int64_t n_chunks,
+                                                          void* __restrict__ out) {
+  int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= n_chunks) return;
+  u32x2 p = *reinterpret_cast<const u32x2*>(packed + c * 8);
+  float a = absmax[c >> 2];
+  float vals[16];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t byte = (p[w] >> (8 * j)) & 0xFF;
+      vals[w * 8 + 2 * j] = lsq::kNF4LevelsDev[byte >> 4] * a;
+      vals[w * 8 + 2 * j + 1] = lsq::kNF4LevelsDev[byte & 15] * a;
+    }
+  }
+  if (OUT_F32) {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + c * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = make_float4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + c * 16);
+    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+}  // namespace
+
+namespace lsq {
+int launch_nf4_quantize(const void* w, int64_t n_out, int64_t n_in, void* packed, float* absmax, int32_t* flag,
+                        hipStream_t s) {
+  static const Thresholds th = make_thresholds();
+  int64_t n_blocks = n_out * (n_in / 64);
+  if (n_blocks == 0) return LSQ_OK;
+  dim3 grid(static_cast<unsigned>((n_blocks + 255) / 256));
+  nf4_quantize_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(w), n_blocks, static_cast<uint8_t*>(packed),
+                                           absmax, flag, th);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+}  // namespace lsq
+
+extern "C" {
+
+void lsq_nf4_codebook(float out[16]) {
+  for (int i = 0; i < 16; ++i) out[i] = lsq::kNF4Levels[i];
+}
+
+int nf4_quantize(const void* w_bf16_dev, int64_t n_out, int64_t n_in, void* packed_dev, float* absmax_dev,
+                 int32_t* flag_dev, void* stream) {
+  LSQ_CHECK(w_bf16_dev && packed_dev && absmax_dev, LSQ_ERR_INVALID, "nf4_quantize: null pointer");
+  LSQ_CHECK(n_out >= 0 && n_in >= 0 && n_in % 64 == 0, LSQ_ERR_SHAPE,
+            "nf4_quantize: n_in must be a multiple of 64 (got %lld x %lld)", (long long)n_out, (long long)n_in);
+  LSQ_CHECK(lsq::aligned16(w_bf16_dev) && lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev), LSQ_ERR_ALIGN,
+            "nf4_quantize: pointers must be 16-byte aligned");
+  return lsq::launch_nf4_quantize(w_bf16_dev, n_out, n_in, packed_dev, absmax_dev, flag_dev, lsq::as_stream(stream));
+}
+
+int nf4_dequantize(const void* packed_dev, const float* absmax_dev, int64_t n_out, int64_t n_in, int32_t out_dtype,
+                   void* w_out_dev, void* stream) {
+  LSQ_CHECK(packed_dev && absmax_dev && w_out_dev, LSQ_ERR_INVALID, "nf4_dequantize: null pointer");
+  LSQ_CHECK(out_dtype == LSQ_BF16 || out_dtype == LSQ_F32, LSQ_ERR_INVALID, "nf4_dequantize: bad dtype");
+  LSQ_CHECK(n_out >= 0 && n_in >= 0 && n_in % 64 == 0, LSQ_ERR_SHAPE,
+            "nf4_dequantize: n_in must be a multiple of 64");
+  LSQ_CHECK(lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev) && lsq::aligned16(w_out_dev), LSQ_ERR_ALIGN,
+            "nf4_dequantize: pointers must be 16-byte aligned");
+  int64_t n_chunks = n_out * n_in / 16;
+  if (n_chunks == 0) return LSQ_OK;
+  dim3 grid(static_cast<unsigned>((n_chunks + 255) / 256));
+  hipStream_t s = lsq::as_stream(stream);
+  if (out_dtype == LSQ_F32)
+    nf4_dequant_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_chunks,
+                                                  w_out_dev);
+  else
+    nf4_dequant_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_chunks,
+                                                   w_out_dev);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+}  // extern "C"

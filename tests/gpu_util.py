@@ -1,0 +1,45 @@
+"""Helpers for the GPU parity tests: device buffers from seeded host arrays."""
+import ctypes as C
+
+import numpy as np
+import torch
+
+from layer_streamed_qlora_nf4_amd import lib
+
+
+def dev_bits(bits, device="cuda"):
+    """uint16 bf16 bit patterns -> int16 device tensor holding the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def dev(x, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def host_bits(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def bits_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def stream():
+    return lib.stream_handle(torch.cuda.current_stream())
+
+
+def empty_bytes(n, device="cuda"):
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+def rel_err(got, ref):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def print_case(**kw):
+    print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)

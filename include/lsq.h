@@ -274,6 +274,14 @@ size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t 
 int lsq_train_step(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res,
                    const int32_t* ids_dev, int32_t batch, int32_t seq, float* loss_dev,
                    float* logits_out, int32_t flags, void* ws, size_t ws_bytes);
+/* The same step, also copying (both nullable, float32, [n_layers + 1, batch*seq,
+ * hidden]) every layer's input x_i (x_trace[n_layers] = the final residual) and
+ * the gradient arriving at every layer's output (dx_trace[i] = dL/dx_i), so a
+ * checker can recompute each layer from the exact inputs this run used. */
+int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res,
+                          const int32_t* ids_dev, int32_t batch, int32_t seq, float* loss_dev,
+                          float* logits_out, int32_t flags, void* ws, size_t ws_bytes,
+                          float* x_trace, float* dx_trace);
 
 /* ------------------------------------------------------ VRAM pre-flight
  * Predict the peak device memory of a streamed step for this exact batch and

@@ -36,7 +36,7 @@ struct ProfRec {
   int kind;
   double flops, bytes;
 };
-constexpr int kPoolPairs = 16384;
+constexpr int kPoolPairs = 1 << 17;
 struct Prof {
   std::mutex mu;
   bool on = false;

@@ -1,0 +1,52 @@
+// Internal interface of the per-layer kernels (see layer_ops.hip).
+#pragma once
+#include "common.h"
+
+namespace lsq {
+
+// qkv: bf16 [B*S, ld] with q heads | k heads | v heads per token row.
+struct AttnArgs {
+  const uint16_t* qkv;
+  int64_t ld;
+  int S, nh, nkv, hd;
+  float scale;
+  uint16_t* out;    // [B*S, ldo], head h at column h*hd
+  int64_t ldo;
+  float* lse;       // [B, nh, S], base-2 log-sum-exp of the scaled scores
+  const float2* rope;  // [S, hd/2] (cos, sin); q and k are rotated on load
+  float* out_f32;      // nullable: the same output in float32 (kept for the backward)
+};
+
+struct AttnBwdArgs {
+  const uint16_t* qkv;
+  int64_t ld;
+  int S, nh, nkv, hd;
+  float scale;
+  const uint16_t* O;    // forward output [B*S, ldo]
+  const float* O_f32;   // the same in float32
+  const uint16_t* dO;   // its gradient   [B*S, ldo]
+  int64_t ldo;
+  const float* lse;
+  const float* D;       // [B*S, nh] rowsum(dO * O) (filled by attention_bwd)
+  uint16_t* dqkv;       // [B*S, ld], same layout as qkv; dq, dk w.r.t. the unrotated q, k
+  const float2* rope;
+};
+
+int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
+                uint16_t* y_lo = nullptr);
+int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
+                float* dx, uint16_t* dx_b, hipStream_t s);
+int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+int rope_table(int S, int head_dim, float theta, float* table, hipStream_t s);
+int rope_apply(uint16_t* buf, int64_t ld, int T, int S, int n_rot_heads, int head_dim, const float* table, int inverse,
+               hipStream_t s);
+int attention_fwd(const AttnArgs& a, int B, hipStream_t s);
+int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s);
+int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s);
+int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* dgu, hipStream_t s);
+int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V, float* x, int32_t* bad, hipStream_t s);
+// dlogits (and, if non-null, dlogits_lo = bf16 of the remainder) for the head backward.
+int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,
+                  uint16_t* dlogits_lo, float* loss, hipStream_t s);
+
+}  // namespace lsq

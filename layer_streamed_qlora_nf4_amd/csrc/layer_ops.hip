@@ -1,0 +1,780 @@
+// Per-layer kernels around the linears: RMSNorm, rotary embedding, causal
+// GQA attention, SwiGLU, embedding gather and the next-token cross-entropy.
+//
+// The streamed layer is the model family's own decoder layer (LS-docs "How
+// it works": transformers' classes); the maths of each piece is the Llama /
+// Qwen2 one.  The residual stream is kept in float32 between kernels; the
+// GEMM operands are bf16.  Every reduction has a fixed order (no atomics), so
+// a resident and a streamed run of the same shapes give identical bits.
+#include <math.h>
+
+#include "common.h"
+#include "layer_ops.h"
+
+namespace lsq {
+namespace {
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// One wave per row: y = bf16(w * x / sqrt(mean(x^2) + eps)); rstd saved.
+// With y_lo, the output is also written as the bf16 rounding of its own
+// remainder (y ~ y + y_lo to about 16 bits), for GEMMs run as two bf16 passes.
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
+                                                          int T, int H, float eps, uint16_t* __restrict__ y,
+                                                          float* __restrict__ rstd, uint16_t* __restrict__ y_lo) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
+  float ss = 0.f;
+  for (int i = lane; i < H / 4; i += 64) {
+    float4 v = xr[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = warp_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (rstd && lane == 0) rstd[row] = r;
+  const uint2* wr = reinterpret_cast<const uint2*>(w);
+  uint2* yr = reinterpret_cast<uint2*>(y + (int64_t)row * H);
+  uint2* lr = y_lo ? reinterpret_cast<uint2*>(y_lo + (int64_t)row * H) : nullptr;
+  for (int i = lane; i < H / 4; i += 64) {
+    float4 v = xr[i];
+    uint2 ww = wr[i];
+    const float o0 = bf_lo(ww.x) * (v.x * r), o1 = bf_hi(ww.x) * (v.y * r);
+    const float o2 = bf_lo(ww.y) * (v.z * r), o3 = bf_hi(ww.y) * (v.w * r);
+    const uint2 hi = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    yr[i] = hi;
+    if (lr)
+      lr[i] = make_uint2(pack_bf16x2(o0 - bf_lo(hi.x), o1 - bf_hi(hi.x)), pack_bf16x2(o2 - bf_lo(hi.y), o3 - bf_hi(hi.y)));
+  }
+}
+
+// dx = gres + r (w dy) - x r^3 sum(w dy x) / H ; also a bf16 copy of dx.
+__global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
+                                                          const float* __restrict__ dy, const float* __restrict__ gres,
+                                                          int T, int H, float eps, float* __restrict__ dx,
+                                                          uint16_t* __restrict__ dx_b) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
+  const float4* dr = reinterpret_cast<const float4*>(dy + (int64_t)row * H);
+  const uint2* wr = reinterpret_cast<const uint2*>(w);
+  float ss = 0.f, dot = 0.f;
+  for (int i = lane; i < H / 4; i += 64) {
+    float4 v = xr[i], d = dr[i];
+    uint2 ww = wr[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    dot += bf_lo(ww.x) * d.x * v.x + bf_hi(ww.x) * d.y * v.y + bf_lo(ww.y) * d.z * v.z + bf_hi(ww.y) * d.w * v.w;
+  }
+  ss = warp_sum(ss);
+  dot = warp_sum(dot);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  const float c = r * r * r * dot / (float)H;
+  float4* outr = reinterpret_cast<float4*>(dx + (int64_t)row * H);
+  const float4* gr = gres ? reinterpret_cast<const float4*>(gres + (int64_t)row * H) : nullptr;
+  uint2* ob = dx_b ? reinterpret_cast<uint2*>(dx_b + (int64_t)row * H) : nullptr;
+  for (int i = lane; i < H / 4; i += 64) {
+    float4 v = xr[i], d = dr[i];
+    uint2 ww = wr[i];
+    float4 o;
+    o.x = r * bf_lo(ww.x) * d.x - v.x * c;
+    o.y = r * bf_hi(ww.x) * d.y - v.y * c;
+    o.z = r * bf_lo(ww.y) * d.z - v.z * c;
+    o.w = r * bf_hi(ww.y) * d.w - v.w * c;
+    if (gr) {
+      float4 g = gr[i];
+      o.x += g.x;
+      o.y += g.y;
+      o.z += g.z;
+      o.w += g.w;
+    }
+    outr[i] = o;
+    if (ob) ob[i] = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+  }
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ y) {
+  int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 v = *reinterpret_cast<const float4*>(x + i);
+  *reinterpret_cast<uint2*>(y + i) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+// ------------------------------------------------------------------ rotary
+// table[s][i] = (cos, sin) of s * theta^(-2i/d), computed in float64.
+__global__ void rope_table_kernel(int S, int half, double theta, float2* __restrict__ table) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= S * half) return;
+  int s = e / half, i = e % half;
+  double inv = pow(theta, -2.0 * i / (2.0 * half));
+  double a = (double)s * inv;
+  table[e] = make_float2((float)cos(a), (float)sin(a));
+}
+
+// Rotate-half on the q and k heads of a [T, ld] bf16 buffer, in place.
+// inverse != 0 applies the transposed rotation (the backward).
+__global__ void rope_kernel(uint16_t* __restrict__ buf, int64_t ld, int T, int S, int n_rot_heads, int half,
+                            const float2* __restrict__ table, int inverse) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T * n_rot_heads * half;
+  if (e >= total) return;
+  const int i = e % half;
+  const int h = (e / half) % n_rot_heads;
+  const int t = e / ((int64_t)half * n_rot_heads);
+  const int s = t % S;
+  const float2 cs = table[(int64_t)s * half + i];
+  const float sn = inverse ? -cs.y : cs.y;
+  uint16_t* p = buf + (int64_t)t * ld + (int64_t)h * 2 * half;
+  const float x1 = bf16_bits_to_f32(p[i]), x2 = bf16_bits_to_f32(p[i + half]);
+  p[i] = f32_to_bf16_bits(x1 * cs.x - x2 * sn);
+  p[i + half] = f32_to_bf16_bits(x2 * cs.x + x1 * sn);
+}
+
+// ------------------------------------------------------------------ attention
+// Causal GQA attention on 64-query x 64-key tiles in float32 (one workgroup
+// per (query block, head, batch)); scores are kept in base 2:
+// s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
+constexpr int AT = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int HD>
+struct AttnSmem {
+  float q[AT][HD + 4];
+  float k[AT][HD + 4];
+  float v[AT][HD + 4];
+  float p[AT][AT + 4];
+};
+
+template <int HD>
+__device__ __forceinline__ void load_rows(float (*dst)[HD + 4], const uint16_t* src, int64_t ld, int row0, int nrows_valid) {
+  // 64 rows x HD bf16 -> float; 8 elements per thread-iteration
+  for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
+    const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nrows_valid) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * ld + c);
+    dst[r][c + 0] = bf_lo(v.x);
+    dst[r][c + 1] = bf_hi(v.x);
+    dst[r][c + 2] = bf_lo(v.y);
+    dst[r][c + 3] = bf_hi(v.y);
+    dst[r][c + 4] = bf_lo(v.z);
+    dst[r][c + 5] = bf_hi(v.z);
+    dst[r][c + 6] = bf_lo(v.w);
+    dst[r][c + 7] = bf_hi(v.w);
+  }
+}
+
+// Rotary embedding applied in float32 to rows already staged in LDS (position
+// pos0 + r for row r), so q and k are rounded to bf16 only once, by the GEMM.
+template <int HD>
+__device__ __forceinline__ void rope_rows(float (*x)[HD + 4], int pos0, int nvalid, const float2* __restrict__ table) {
+  constexpr int HALF = HD / 2;
+  for (int e = threadIdx.x; e < AT * HALF; e += 256) {
+    const int r = e / HALF, i = e % HALF;
+    if (r >= nvalid) continue;
+    const float2 cs = table[(int64_t)(pos0 + r) * HALF + i];
+    const float x1 = x[r][i], x2 = x[r][i + HALF];
+    x[r][i] = x1 * cs.x - x2 * cs.y;
+    x[r][i + HALF] = x2 * cs.x + x1 * cs.y;
+  }
+}
+
+// Gradient through the rotation for a thread's DPT output dims (the
+// transposed rotation): dims d and d +- HD/2 live in lanes c4 and c4 ^ 8.
+template <int HD, int DPT>
+__device__ __forceinline__ void rope_bwd_regs(float (&g)[DPT], int pos, int c4, const float2* __restrict__ table) {
+  constexpr int HALF = HD / 2;
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) {
+    const float other = __shfl_xor(g[d], 8, 64);
+    const int i = (DPT * c4 + d) % HALF;
+    const float2 cs = table[(int64_t)pos * HALF + i];
+    g[d] = (c4 < 8) ? g[d] * cs.x + other * cs.y : g[d] * cs.x - other * cs.y;
+  }
+}
+
+// S tile for thread (rows 4*r4.., cols 4*c4..): acc[i][j] = sum_d A[r][d] B[c][d]
+template <int HD>
+__device__ __forceinline__ void tile_dot(const float (*A)[HD + 4], const float (*B)[HD + 4], int r4, int c4, float acc[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int d = 0; d < HD; d += 4) {
+    float4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4*>(&A[4 * r4 + i][d]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(&B[4 * c4 + j][d]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] += a[i].x * b[j].x + a[i].y * b[j].y + a[i].z * b[j].z + a[i].w * b[j].w;
+  }
+}
+
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnSmem<HD>& sm = *reinterpret_cast<AttnSmem<HD>*>(smem_raw);
+  constexpr int DPT = HD / 16;  // output dims per thread
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.nh / a.nkv);
+  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  const int q0 = qb * AT;
+  const int nq_valid = min(AT, a.S - q0);
+  const int64_t rowbase = (int64_t)b * a.S;
+  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
+  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
+  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
+  load_rows<HD>(sm.q, Q, a.ld, q0, nq_valid);
+  __syncthreads();
+  rope_rows<HD>(sm.q, q0, nq_valid, a.rope);
+  const float sc = a.scale * kLog2e;
+  float m[4], l[4], o[4][DPT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) o[i][d] = 0.f;
+  }
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * AT;
+    __syncthreads();
+    load_rows<HD>(sm.k, Kp, a.ld, k0, min(AT, a.S - k0));
+    load_rows<HD>(sm.v, Vp, a.ld, k0, min(AT, a.S - k0));
+    __syncthreads();
+    rope_rows<HD>(sm.k, k0, min(AT, a.S - k0), a.rope);
+    __syncthreads();
+    float s[4][4];
+    tile_dot<HD>(sm.q, sm.k, r4, c4, s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = q0 + 4 * r4 + i;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kj = k0 + 4 * c4 + j;
+        s[i][j] = (kj <= qi && kj < a.S) ? s[i][j] * sc : -INFINITY;
+        mx = fmaxf(mx, s[i][j]);
+      }
+      mx = group16_max(mx);
+      const float mn = fmaxf(m[i], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[i] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = (s[i][j] == -INFINITY) ? 0.f : exp2f(s[i][j] - mn);
+        sm.p[4 * r4 + i][4 * c4 + j] = pv;
+        rs += pv;
+      }
+      rs = group16_sum(rs);
+      l[i] = l[i] * alpha + rs;
+      m[i] = mn;
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) o[i][d] *= alpha;
+    }
+    __syncthreads();
+    for (int j = 0; j < AT; ++j) {
+      float vv[DPT];
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) vv[d] = sm.v[j][DPT * c4 + d];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = sm.p[4 * r4 + i][j];
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) o[i][d] = fmaf(pv, vv[d], o[i][d]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + 4 * r4 + i;
+    if (qi >= a.S) continue;
+    const float inv = 1.f / l[i];
+    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD + DPT * c4;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 2)
+      *reinterpret_cast<uint32_t*>(out + d) = pack_bf16x2(o[i][d] * inv, o[i][d + 1] * inv);
+    if (a.out_f32) {
+      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD + DPT * c4;
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) of[d] = o[i][d] * inv;
+    }
+    if (c4 == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[i] + log2f(l[i]);
+  }
+}
+
+// D[t][h] = sum_d dO[t, h, d] * O[t, h, d], with the float32 O of the forward:
+// D must equal sum_j P_j dP_j, and a rounded O breaks that identity exactly
+// where attention is peaked and dP_j - D cancels.
+__global__ void attn_dot_kernel(const uint16_t* __restrict__ dO, const float* __restrict__ O, int64_t ldo, int T,
+                                int nh, int hd, float* __restrict__ D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t, h)
+  if (row >= (int64_t)T * nh) return;
+  const int t = row / nh, h = row % nh;
+  const uint16_t* a = dO + (int64_t)t * ldo + (int64_t)h * hd;
+  const float* b = O + (int64_t)t * ldo + (int64_t)h * hd;
+  float s = 0.f;
+  for (int d = lane; d < hd; d += 64) s += bf16_bits_to_f32(a[d]) * b[d];
+  s = warp_sum(s);
+  if (lane == 0) D[row] = s;
+}
+
+template <int HD>
+struct AttnBwdSmem {
+  float a[AT][HD + 4];   // Q (dK/dV kernel) or K (dQ kernel)
+  float b[AT][HD + 4];   // dO (dK/dV) or V (dQ)
+  float k[AT][HD + 4];   // this block's K (dK/dV) or Q (dQ)
+  float v[AT][HD + 4];   // this block's V (dK/dV) or dO (dQ)
+  float p[AT][AT + 4];    // P, then dS (dK/dV kernel); dS (dQ kernel)
+  float lse[AT];
+  float dd[AT];
+};
+
+// dK and dV for one key block of one KV head: loop over its query heads and
+// the query blocks at or after it.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
+  constexpr int DPT = HD / 16;
+  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  const int k0 = kb * AT;
+  const int group = a.nh / a.nkv;
+  const int64_t rowbase = (int64_t)b * a.S;
+  const float sc = a.scale * kLog2e;
+  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, min(AT, a.S - k0));
+  load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, min(AT, a.S - k0));
+  __syncthreads();
+  rope_rows<HD>(sm.k, k0, min(AT, a.S - k0), a.rope);
+  float dk[4][DPT], dv[4][DPT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) dk[i][d] = dv[i][d] = 0.f;
+  const int nqb = (a.S + AT - 1) / AT;
+  for (int hh = 0; hh < group; ++hh) {
+    const int h = g * group + hh;
+    for (int qb = kb; qb < nqb; ++qb) {
+      const int q0 = qb * AT;
+      const int nqv = min(AT, a.S - q0);
+      __syncthreads();
+      load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);
+      load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);
+      if (t < AT) {
+        const bool ok = t < nqv;
+        sm.lse[t] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + t] : 0.f;
+        sm.dd[t] = ok ? a.D[(rowbase + q0 + t) * a.nh + h] : 0.f;
+      }
+      __syncthreads();
+      rope_rows<HD>(sm.a, q0, nqv, a.rope);
+      __syncthreads();
+      // rows = queries (r4), cols = keys (c4)
+      float s[4][4], dp[4][4];
+      tile_dot<HD>(sm.a, sm.k, r4, c4, s);
+      tile_dot<HD>(sm.b, sm.v, r4, c4, dp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = q0 + 4 * r4 + i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kj = k0 + 4 * c4 + j;
+          const bool ok = kj <= qi && qi < a.S && kj < a.S;
+          s[i][j] = ok ? exp2f(s[i][j] * sc - sm.lse[4 * r4 + i]) : 0.f;   // P
+          sm.p[4 * r4 + i][4 * c4 + j] = s[i][j];
+        }
+      }
+      __syncthreads();
+      // dV[k][d] += sum_q P[q][k] dO[q][d]; thread owns keys 4*r4.., dims DPT*c4..
+      for (int q = 0; q < AT; ++q) {
+        float dov[DPT];
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) dov[d] = sm.b[q][DPT * c4 + d];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = sm.p[q][4 * r4 + i];
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) dv[i][d] = fmaf(p, dov[d], dv[i][d]);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm.p[4 * r4 + i][4 * c4 + j] = s[i][j] * (dp[i][j] - sm.dd[4 * r4 + i]);  // dS
+      __syncthreads();
+      // dK[k][d] += sum_q dS[q][k] Q[q][d]
+      for (int q = 0; q < AT; ++q) {
+        float qv[DPT];
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) qv[d] = sm.a[q][DPT * c4 + d];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ds = sm.p[q][4 * r4 + i];
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) dk[i][d] = fmaf(ds, qv[d], dk[i][d]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kj = k0 + 4 * r4 + i;
+    rope_bwd_regs<HD, DPT>(dk[i], min(kj, a.S - 1), c4, a.rope);
+    if (kj >= a.S) continue;
+    uint16_t* dkp = a.dqkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + g) * HD + DPT * c4;
+    uint16_t* dvp = a.dqkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + a.nkv + g) * HD + DPT * c4;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 2) {
+      *reinterpret_cast<uint32_t*>(dkp + d) = pack_bf16x2(dk[i][d] * a.scale, dk[i][d + 1] * a.scale);
+      *reinterpret_cast<uint32_t*>(dvp + d) = pack_bf16x2(dv[i][d], dv[i][d + 1]);
+    }
+  }
+}
+
+// dQ for one query block of one head.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
+  constexpr int DPT = HD / 16;
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.nh / a.nkv);
+  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  const int q0 = qb * AT;
+  const int nqv = min(AT, a.S - q0);
+  const int64_t rowbase = (int64_t)b * a.S;
+  const float sc = a.scale * kLog2e;
+  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);      // Q
+  load_rows<HD>(sm.v, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);     // dO
+  if (t < AT) {
+    const bool ok = t < nqv;
+    sm.lse[t] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + t] : 0.f;
+    sm.dd[t] = ok ? a.D[(rowbase + q0 + t) * a.nh + h] : 0.f;
+  }
+  __syncthreads();
+  rope_rows<HD>(sm.k, q0, nqv, a.rope);
+  float dq[4][DPT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) dq[i][d] = 0.f;
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * AT;
+    __syncthreads();
+    load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, min(AT, a.S - k0));          // K
+    load_rows<HD>(sm.b, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, min(AT, a.S - k0));  // V
+    __syncthreads();
+    rope_rows<HD>(sm.a, k0, min(AT, a.S - k0), a.rope);
+    __syncthreads();
+    float s[4][4], dp[4][4];
+    tile_dot<HD>(sm.k, sm.a, r4, c4, s);
+    tile_dot<HD>(sm.v, sm.b, r4, c4, dp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = q0 + 4 * r4 + i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kj = k0 + 4 * c4 + j;
+        const bool ok = kj <= qi && qi < a.S && kj < a.S;
+        const float p = ok ? exp2f(s[i][j] * sc - sm.lse[4 * r4 + i]) : 0.f;
+        sm.p[4 * r4 + i][4 * c4 + j] = p * (dp[i][j] - sm.dd[4 * r4 + i]);
+      }
+    }
+    __syncthreads();
+    for (int j = 0; j < AT; ++j) {
+      float kv[DPT];
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) kv[d] = sm.a[j][DPT * c4 + d];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ds = sm.p[4 * r4 + i][j];
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) dq[i][d] = fmaf(ds, kv[d], dq[i][d]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + 4 * r4 + i;
+    rope_bwd_regs<HD, DPT>(dq[i], min(qi, a.S - 1), c4, a.rope);
+    if (qi >= a.S) continue;
+    uint16_t* dqp = a.dqkv + (rowbase + qi) * a.ld + (int64_t)h * HD + DPT * c4;
+#pragma unroll
+    for (int d = 0; d < DPT; d += 2)
+      *reinterpret_cast<uint32_t*>(dqp + d) = pack_bf16x2(dq[i][d] * a.scale, dq[i][d + 1] * a.scale);
+  }
+}
+
+// ------------------------------------------------------------------ SwiGLU
+// gu [T, 2I] (gate | up) -> m [T, I] = bf16(silu(g) * u)
+__global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ m) {
+  int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
+  if (e >= (int64_t)T * I) return;
+  const int64_t t = e / I, i = e % I;
+  const uint32_t gw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + i);
+  const uint32_t uw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + I + i);
+  float g0 = bf_lo(gw), g1 = bf_hi(gw), u0 = bf_lo(uw), u1 = bf_hi(uw);
+  float s0 = g0 / (1.f + __expf(-g0)), s1 = g1 / (1.f + __expf(-g1));
+  *reinterpret_cast<uint32_t*>(m + e) = pack_bf16x2(s0 * u0, s1 * u1);
+}
+
+// dgu [T, 2I]: dg = dm u sig(g) (1 + g (1 - sig(g))), du = dm silu(g)
+__global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ gu, const uint16_t* __restrict__ dm, int T, int I,
+                                  uint16_t* __restrict__ dgu) {
+  int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
+  if (e >= (int64_t)T * I) return;
+  const int64_t t = e / I, i = e % I;
+  const uint32_t gw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + i);
+  const uint32_t uw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + I + i);
+  const uint32_t dw = *reinterpret_cast<const uint32_t*>(dm + e);
+  float g[2] = {bf_lo(gw), bf_hi(gw)}, u[2] = {bf_lo(uw), bf_hi(uw)}, d[2] = {bf_lo(dw), bf_hi(dw)};
+  float dg[2], du[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float sg = 1.f / (1.f + __expf(-g[j]));
+    dg[j] = d[j] * u[j] * sg * (1.f + g[j] * (1.f - sg));
+    du[j] = d[j] * g[j] * sg;
+  }
+  *reinterpret_cast<uint32_t*>(dgu + t * 2 * I + i) = pack_bf16x2(dg[0], dg[1]);
+  *reinterpret_cast<uint32_t*>(dgu + t * 2 * I + I + i) = pack_bf16x2(du[0], du[1]);
+}
+
+// ------------------------------------------------------------------ embedding
+__global__ void embed_kernel(const int32_t* __restrict__ ids, const uint16_t* __restrict__ table, int T, int H, int V,
+                             float* __restrict__ x, int32_t* __restrict__ bad) {
+  int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= (int64_t)T * H) return;
+  const int t = e / H, c = e % H;
+  int id = ids[t];
+  if (id < 0 || id >= V) {
+    if (bad && c == 0) atomicOr(bad, 1);
+    id = 0;
+  }
+  const uint2 w = *reinterpret_cast<const uint2*>(table + (int64_t)id * H + c);
+  *reinterpret_cast<float4*>(x + e) = make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+}
+
+// ------------------------------------------------------------------ cross-entropy
+// One workgroup per row t of logits [T, V] (float32).  Rows whose position is
+// the last of its sequence have no target: zero loss, zero gradient.
+// loss_rows[t] = lse - logit[target]; dlogits[t] = bf16((softmax - onehot) / count).
+__global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
+                                                 int T, int S, int V, float inv_count, float* __restrict__ loss_rows,
+                                                 uint16_t* __restrict__ dlogits, uint16_t* __restrict__ dlogits_lo) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* row = logits + (int64_t)t * V;
+  const bool has_target = (t % S) != S - 1;
+  const int target = has_target ? ids[t + 1] : -1;
+  float mx = -INFINITY;
+  for (int i = tid; i < V; i += 256) mx = fmaxf(mx, row[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int i = tid; i < V; i += 256) sum += __expf(row[i] - mx);
+  sum = warp_sum(sum);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  sum = ((red[0] + red[1]) + red[2]) + red[3];
+  const float lse = mx + __logf(sum);
+  uint16_t* drow = dlogits + (int64_t)t * V;
+  uint16_t* lrow = dlogits_lo ? dlogits_lo + (int64_t)t * V : nullptr;
+  const float inv_sum = 1.f / sum;
+  for (int i = tid; i < V; i += 256) {
+    float g = 0.f;
+    if (has_target) g = (__expf(row[i] - mx) * inv_sum - (i == target ? 1.f : 0.f)) * inv_count;
+    const uint16_t hb = f32_to_bf16_bits(g);
+    drow[i] = hb;
+    if (lrow) lrow[i] = f32_to_bf16_bits(g - bf16_bits_to_f32(hb));
+  }
+  if (tid == 0) loss_rows[t] = has_target ? lse - row[target] : 0.f;
+}
+
+// loss = sum of loss_rows (fixed order: per-thread strided partials, then a tree) * inv_count
+__global__ void __launch_bounds__(256) loss_sum_kernel(const float* __restrict__ loss_rows, int T, float inv_count,
+                                                       float* __restrict__ loss) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  float s = 0.f;
+  for (int i = tid; i < T; i += 256) s += loss_rows[i];
+  s = warp_sum(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) *loss = (((red[0] + red[1]) + red[2]) + red[3]) * inv_count;
+}
+
+template <int HD>
+size_t attn_fwd_smem() { return sizeof(AttnSmem<HD>); }
+template <int HD>
+size_t attn_bwd_smem() { return sizeof(AttnBwdSmem<HD>); }
+
+}  // namespace
+
+// ================================================================== launchers
+int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
+                uint16_t* y_lo) {
+  LSQ_CHECK(H % 4 == 0, LSQ_ERR_SHAPE, "rmsnorm: hidden %d must be a multiple of 4", H);
+  if (T == 0) return LSQ_OK;
+  rmsnorm_fwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, w, T, H, eps, y, rstd, y_lo);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
+                float* dx, uint16_t* dx_b, hipStream_t s) {
+  if (T == 0) return LSQ_OK;
+  rmsnorm_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, w, dy, gres, T, H, eps, dx, dx_b);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
+  LSQ_CHECK(n % 4 == 0, LSQ_ERR_SHAPE, "to_bf16: n %% 4 != 0");
+  if (n == 0) return LSQ_OK;
+  f32_to_bf16_kernel<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(x, n, y);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int rope_table(int S, int head_dim, float theta, float* table, hipStream_t s) {
+  const int half = head_dim / 2;
+  if (S == 0) return LSQ_OK;
+  rope_table_kernel<<<(S * half + 255) / 256, 256, 0, s>>>(S, half, (double)theta, reinterpret_cast<float2*>(table));
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int rope_apply(uint16_t* buf, int64_t ld, int T, int S, int n_rot_heads, int head_dim, const float* table, int inverse,
+               hipStream_t s) {
+  const int half = head_dim / 2;
+  const int64_t total = (int64_t)T * n_rot_heads * half;
+  if (total == 0) return LSQ_OK;
+  rope_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(buf, ld, T, S, n_rot_heads, half,
+                                                              reinterpret_cast<const float2*>(table), inverse);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+template <typename K>
+int allow_smem(K* kernel, size_t bytes) {
+  LSQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)bytes));
+  return LSQ_OK;
+}
+
+int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
+  LSQ_CHECK(a.hd == 64 || a.hd == 128, LSQ_ERR_SHAPE, "attention: head_dim %d unsupported (64 or 128)", a.hd);
+  LSQ_CHECK(a.nkv > 0 && a.nh % a.nkv == 0, LSQ_ERR_SHAPE, "attention: n_heads %% n_kv_heads != 0");
+  if (B == 0 || a.S == 0) return LSQ_OK;
+  static int init = [] {
+    int e = allow_smem(attn_fwd_kernel<128>, attn_fwd_smem<128>());
+    return e ? e : allow_smem(attn_fwd_kernel<64>, attn_fwd_smem<64>());
+  }();
+  if (init) return init;
+  dim3 grid((a.S + AT - 1) / AT, a.nh, B);
+  const double flops = 2.0 * 2.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
+  int tok = prof_begin(s);
+  if (a.hd == 128)
+    attn_fwd_kernel<128><<<grid, 256, attn_fwd_smem<128>(), s>>>(a);
+  else
+    attn_fwd_kernel<64><<<grid, 256, attn_fwd_smem<64>(), s>>>(a);
+  prof_end(tok, s, PROF_ATTN, flops, 0.0);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
+  LSQ_CHECK(a.hd == 64 || a.hd == 128, LSQ_ERR_SHAPE, "attention: head_dim %d unsupported", a.hd);
+  if (B == 0 || a.S == 0) return LSQ_OK;
+  static int init = [] {
+    int e = allow_smem(attn_bwd_dkdv_kernel<128>, attn_bwd_smem<128>());
+    if (!e) e = allow_smem(attn_bwd_dq_kernel<128>, attn_bwd_smem<128>());
+    if (!e) e = allow_smem(attn_bwd_dkdv_kernel<64>, attn_bwd_smem<64>());
+    if (!e) e = allow_smem(attn_bwd_dq_kernel<64>, attn_bwd_smem<64>());
+    return e;
+  }();
+  if (init) return init;
+  const int T = B * a.S;
+  const double flops = 2.0 * 5.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
+  int tok = prof_begin(s);
+  attn_dot_kernel<<<(unsigned)(((int64_t)T * a.nh + 3) / 4), 256, 0, s>>>(a.dO, a.O_f32, a.ldo, T, a.nh, a.hd, D);
+  AttnBwdArgs b = a;
+  b.D = D;
+  dim3 g1((a.S + AT - 1) / AT, a.nkv, B), g2((a.S + AT - 1) / AT, a.nh, B);
+  if (a.hd == 128) {
+    attn_bwd_dkdv_kernel<128><<<g1, 256, attn_bwd_smem<128>(), s>>>(b);
+    attn_bwd_dq_kernel<128><<<g2, 256, attn_bwd_smem<128>(), s>>>(b);
+  } else {
+    attn_bwd_dkdv_kernel<64><<<g1, 256, attn_bwd_smem<64>(), s>>>(b);
+    attn_bwd_dq_kernel<64><<<g2, 256, attn_bwd_smem<64>(), s>>>(b);
+  }
+  prof_end(tok, s, PROF_ATTN, flops, 0.0);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s) {
+  LSQ_CHECK(I % 2 == 0, LSQ_ERR_SHAPE, "swiglu: odd intermediate");
+  const int64_t n = (int64_t)T * I / 2;
+  if (n == 0) return LSQ_OK;
+  swiglu_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, T, I, m);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* dgu, hipStream_t s) {
+  const int64_t n = (int64_t)T * I / 2;
+  if (n == 0) return LSQ_OK;
+  swiglu_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, dm, T, I, dgu);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V, float* x, int32_t* bad, hipStream_t s) {
+  LSQ_CHECK(H % 4 == 0, LSQ_ERR_SHAPE, "embed: hidden %% 4 != 0");
+  const int64_t n = (int64_t)T * H / 4;
+  if (n == 0) return LSQ_OK;
+  embed_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ids, table, T, H, V, x, bad);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,
+                  uint16_t* dlogits_lo, float* loss, hipStream_t s) {
+  const int T = B * S;
+  if (T == 0) return LSQ_OK;
+  const float inv_count = S > 1 ? 1.f / (float)(B * (S - 1)) : 0.f;
+  ce_kernel<<<T, 256, 0, s>>>(logits, ids, T, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
+  loss_sum_kernel<<<1, 256, 0, s>>>(loss_rows, T, inv_count, loss);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+}  // namespace lsq

@@ -1,0 +1,567 @@
+// Streaming runtime: shard store, VRAM layer pool, training step, pre-flight.
+//
+// What the pages describe and this file implements (LS-docs "How it works";
+// "Turn it on"; About): the frozen base is rewritten once into one shard per
+// decoder layer, held in page-locked host memory; a small pool of N
+// pre-allocated VRAM buffers (2..8) receives one layer at a time on a
+// dedicated copy stream, layer i+1 while layer i computes; only the
+// embedding, final norm, head and the adapters (with their gradients) stay
+// resident.  The backward re-reads every layer (recompute) and must never read
+// a slot that has been refilled (LS-docs "If you streamed a 32B or larger
+// model in NF4"): a slot's free event is recorded after the last kernel that
+// reads it and every refill waits on it.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+#include "gemm.h"
+#include "layer.h"
+#include "layer_ops.h"
+
+using namespace lsq;
+
+namespace {
+uint64_t up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+struct BlobHeader {
+  char magic[8];  // "LSQBLOB1"
+  int32_t layer, weight_kind, hidden, n_heads, n_kv_heads, head_dim, intermediate, lora_r, qkv_bias;
+  uint64_t total_bytes;
+};
+}  // namespace
+
+// ================================================================== store
+struct lsq_store {
+  lsq_model_cfg cfg;
+  uint64_t layer_bytes;
+  char* host;
+  bool pinned;
+};
+
+extern "C" {
+
+int shard_store_create(const lsq_model_cfg* cfg, int32_t flags, lsq_store** out) {
+  if (int e = check_cfg(cfg)) return e;
+  LSQ_CHECK(out, LSQ_ERR_INVALID, "shard_store_create: null out");
+  lsq_blob_layout L;
+  blob_layout(cfg, &L);
+  const uint64_t total = L.total_bytes * (uint64_t)cfg->n_layers;
+  lsq_store* st = new (std::nothrow) lsq_store{*cfg, L.total_bytes, nullptr, false};
+  LSQ_CHECK(st, LSQ_ERR_OOM, "shard_store_create: out of host memory");
+  bool want_pin = !(flags & LSQ_STORE_FORCE_PAGEABLE);
+  if (want_pin) {
+    void* p = nullptr;
+    hipError_t e = (flags & LSQ_STORE_FAIL_PIN) ? hipErrorOutOfMemory : hipHostMalloc(&p, total, hipHostMallocDefault);
+    if (e == hipSuccess) {
+      st->host = static_cast<char*>(p);
+      st->pinned = true;
+    } else {
+      (void)hipGetLastError();  // clear the failed page-lock before anything else runs
+      if (!(flags & LSQ_STORE_ALLOW_PAGEABLE)) {
+        delete st;
+        return fail(LSQ_ERR_OOM, "could not page-lock the %.2f GB shard store (%s); refusing (pass "
+                    "LSQ_STORE_ALLOW_PAGEABLE to fall back to a pageable store)", total / 1e9, hipGetErrorString(e));
+      }
+      fprintf(stderr, "[lsq] could not page-lock the %.2f GB shard store; falling back to a PAGEABLE store: "
+              "host-to-device copies become synchronous and stop overlapping compute\n", total / 1e9);
+    }
+  }
+  if (!st->host) {
+    st->host = static_cast<char*>(aligned_alloc(4096, up(total, 4096)));
+    if (!st->host) {
+      delete st;
+      return fail(LSQ_ERR_OOM, "shard_store_create: cannot allocate %.2f GB of host memory", total / 1e9);
+    }
+  }
+  *out = st;
+  return LSQ_OK;
+}
+
+void shard_store_destroy(lsq_store* st) {
+  if (!st) return;
+  if (st->pinned)
+    (void)hipHostFree(st->host);
+  else
+    free(st->host);
+  delete st;
+}
+
+int32_t shard_store_is_pinned(const lsq_store* st) { return st && st->pinned ? 1 : 0; }
+uint64_t shard_store_layer_bytes(const lsq_store* st) { return st ? st->layer_bytes : 0; }
+const void* shard_store_layer_host(const lsq_store* st, int32_t layer) {
+  if (!st || layer < 0 || layer >= st->cfg.n_layers) return nullptr;
+  return st->host + (uint64_t)layer * st->layer_bytes;
+}
+
+int shard_store_write_layer(lsq_store* st, int32_t layer, const lsq_layer_src* src, void* staging, size_t staging_bytes,
+                            void* stream) {
+  LSQ_CHECK(st && src && staging, LSQ_ERR_INVALID, "shard_store_write_layer: null pointer");
+  LSQ_CHECK(layer >= 0 && layer < st->cfg.n_layers, LSQ_ERR_INVALID, "shard_store_write_layer: layer %d", layer);
+  LSQ_CHECK(staging_bytes >= st->layer_bytes + 256, LSQ_ERR_WORKSPACE, "shard_store_write_layer: staging too small");
+  LSQ_CHECK(aligned16(staging), LSQ_ERR_ALIGN, "shard_store_write_layer: unaligned staging");
+  const lsq_model_cfg* c = &st->cfg;
+  for (int i = 0; i < 7; ++i) LSQ_CHECK(src->w[i] && aligned16(src->w[i]), LSQ_ERR_INVALID, "layer src: weight %d", i);
+  LSQ_CHECK(src->norm1 && src->norm2, LSQ_ERR_INVALID, "layer src: norms");
+  if (c->qkv_bias) LSQ_CHECK(src->bias[0] && src->bias[1] && src->bias[2], LSQ_ERR_INVALID, "layer src: biases");
+  hipStream_t s = as_stream(stream);
+  lsq_blob_layout L;
+  blob_layout(c, &L);
+  const Dims d = dims_of(c);
+  char* blob = static_cast<char*>(staging);
+  int32_t* flag = reinterpret_cast<int32_t*>(blob + st->layer_bytes);
+  LSQ_HIP(hipMemsetAsync(blob, 0, st->layer_bytes + 256, s));
+  BlobHeader hdr{};
+  memcpy(hdr.magic, "LSQBLOB1", 8);
+  hdr.layer = layer;
+  hdr.weight_kind = c->weight_kind;
+  hdr.hidden = c->hidden;
+  hdr.n_heads = c->n_heads;
+  hdr.n_kv_heads = c->n_kv_heads;
+  hdr.head_dim = c->head_dim;
+  hdr.intermediate = c->intermediate;
+  hdr.lora_r = c->lora_r;
+  hdr.qkv_bias = c->qkv_bias;
+  hdr.total_bytes = st->layer_bytes;
+  LSQ_HIP(hipMemcpyAsync(blob, &hdr, sizeof(hdr), hipMemcpyHostToDevice, s));
+  // projections in group order: qkv = q,k,v ; o ; gate|up = gate,up ; down
+  const int group_of[7] = {0, 0, 0, 1, 2, 2, 3};
+  const int rows_of[7] = {d.Nq, d.Nkv, d.Nkv, d.H, d.I, d.I, d.H};
+  int row_off[7];
+  for (int i = 0, g = -1, acc = 0; i < 7; ++i) {
+    if (group_of[i] != g) {
+      g = group_of[i];
+      acc = 0;
+    }
+    row_off[i] = acc;
+    acc += rows_of[i];
+  }
+  for (int i = 0; i < 7; ++i) {
+    const int g = group_of[i];
+    const int64_t K = d.gK[g];
+    if (c->weight_kind == LSQ_W_NF4) {
+      void* packed = blob + L.w_off[g] + (uint64_t)row_off[i] * (K / 2);
+      float* absmax = reinterpret_cast<float*>(blob + L.absmax_off[g] + (uint64_t)row_off[i] * (K / 64) * 4);
+      if (int e = nf4_quantize(src->w[i], rows_of[i], K, packed, absmax, flag, stream)) return e;
+    } else {
+      LSQ_HIP(hipMemcpyAsync(blob + L.w_off[g] + (uint64_t)row_off[i] * K * 2, src->w[i], (size_t)rows_of[i] * K * 2,
+                             hipMemcpyDeviceToDevice, s));
+    }
+  }
+  LSQ_HIP(hipMemcpyAsync(blob + L.norm1_off, src->norm1, 2ull * d.H, hipMemcpyDeviceToDevice, s));
+  LSQ_HIP(hipMemcpyAsync(blob + L.norm2_off, src->norm2, 2ull * d.H, hipMemcpyDeviceToDevice, s));
+  if (c->qkv_bias) {
+    LSQ_HIP(hipMemcpyAsync(blob + L.bias_off, src->bias[0], 2ull * d.Nq, hipMemcpyDeviceToDevice, s));
+    LSQ_HIP(hipMemcpyAsync(blob + L.bias_off + 2ull * d.Nq, src->bias[1], 2ull * d.Nkv, hipMemcpyDeviceToDevice, s));
+    LSQ_HIP(hipMemcpyAsync(blob + L.bias_off + 2ull * (d.Nq + d.Nkv), src->bias[2], 2ull * d.Nkv,
+                           hipMemcpyDeviceToDevice, s));
+  }
+  int32_t host_flag = 0;
+  LSQ_HIP(hipMemcpyAsync(st->host + (uint64_t)layer * st->layer_bytes, blob, st->layer_bytes, hipMemcpyDeviceToHost,
+                         s));
+  LSQ_HIP(hipMemcpyAsync(&host_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  LSQ_HIP(hipStreamSynchronize(s));
+  LSQ_CHECK(host_flag == 0, LSQ_ERR_NONFINITE, "shard_store_write_layer: layer %d has a NaN or Inf weight", layer);
+  return LSQ_OK;
+}
+
+}  // extern "C"
+
+// ================================================================== pool
+namespace {
+struct Slot {
+  int layer = -1;
+  bool held = false;
+  bool ready_recorded = false;
+  bool free_recorded = false;
+  uint64_t last_use = 0;
+  hipEvent_t ready = nullptr, free_ev = nullptr;
+};
+constexpr int kCopyTimers = 1024;
+}  // namespace
+
+struct lsq_pool {
+  const lsq_store* store;
+  int n;
+  char* dev;
+  uint64_t stride;
+  hipStream_t compute, copy;
+  int flags;
+  bool resident;
+  std::vector<Slot> slots;
+  uint64_t tick = 0;
+  lsq_pool_stats stats{};
+  std::vector<hipEvent_t> tev;  // copy timing pairs (ring)
+  int tev_used = 0;
+};
+
+namespace {
+int find_slot(lsq_pool* p, int layer) {
+  for (int i = 0; i < p->n; ++i)
+    if (p->slots[i].layer == layer) return i;
+  return -1;
+}
+
+int copy_into(lsq_pool* p, int si, int layer) {
+  Slot& sl = p->slots[si];
+  char* dst = p->dev + (uint64_t)si * p->stride;
+  if (sl.free_recorded) LSQ_HIP(hipStreamWaitEvent(p->copy, sl.free_ev, 0));
+  if (p->flags & LSQ_POOL_POISON) LSQ_HIP(hipMemsetAsync(dst, 0xFF, p->store->layer_bytes, p->copy));
+  const bool timed = p->tev_used < kCopyTimers;
+  if (timed) LSQ_HIP(hipEventRecord(p->tev[2 * p->tev_used], p->copy));
+  LSQ_HIP(hipMemcpyAsync(dst, shard_store_layer_host(p->store, layer), p->store->layer_bytes, hipMemcpyHostToDevice,
+                         p->copy));
+  if (timed) {
+    LSQ_HIP(hipEventRecord(p->tev[2 * p->tev_used + 1], p->copy));
+    ++p->tev_used;
+  }
+  LSQ_HIP(hipEventRecord(sl.ready, p->copy));
+  sl.ready_recorded = true;
+  sl.layer = layer;
+  sl.last_use = ++p->tick;
+  p->stats.copies += 1;
+  p->stats.copy_bytes += p->store->layer_bytes;
+  return LSQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots, uint64_t slot_stride,
+                      void* compute_stream, void* copy_stream, int32_t flags, lsq_pool** out) {
+  LSQ_CHECK(store && dev_slots && out, LSQ_ERR_INVALID, "layer_pool_create: null pointer");
+  const bool resident = flags & LSQ_POOL_RESIDENT;
+  if (resident)
+    LSQ_CHECK(n_buffers == store->cfg.n_layers, LSQ_ERR_INVALID, "resident pool needs n_buffers == n_layers");
+  else
+    LSQ_CHECK(n_buffers >= 2 && n_buffers <= 8, LSQ_ERR_INVALID,
+              "stream_buffers must be in [2, 8] (got %d): a refusal, not a clamp", n_buffers);
+  LSQ_CHECK(slot_stride >= store->layer_bytes && slot_stride % 4096 == 0 && aligned16(dev_slots), LSQ_ERR_ALIGN,
+            "layer_pool_create: slot stride must cover a blob and be a multiple of 4096");
+  LSQ_CHECK(compute_stream != copy_stream || resident, LSQ_ERR_INVALID,
+            "layer_pool_create: the copy stream must differ from the compute stream");
+  lsq_pool* p = new (std::nothrow) lsq_pool();
+  LSQ_CHECK(p, LSQ_ERR_OOM, "layer_pool_create: out of memory");
+  p->store = store;
+  p->n = n_buffers;
+  p->dev = static_cast<char*>(dev_slots);
+  p->stride = slot_stride;
+  p->compute = as_stream(compute_stream);
+  p->copy = as_stream(copy_stream);
+  p->flags = flags;
+  p->resident = resident;
+  p->slots.resize(n_buffers);
+  p->tev.resize(2 * kCopyTimers);
+  for (auto& e : p->tev) LSQ_HIP(hipEventCreate(&e));
+  for (auto& s : p->slots) {
+    LSQ_HIP(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming));
+    LSQ_HIP(hipEventCreateWithFlags(&s.free_ev, hipEventDisableTiming));
+  }
+  if (resident) {
+    for (int i = 0; i < n_buffers; ++i)
+      if (int e = copy_into(p, i, i)) return e;
+    LSQ_HIP(hipStreamSynchronize(p->copy));
+  }
+  *out = p;
+  return LSQ_OK;
+}
+
+void layer_pool_destroy(lsq_pool* p) {
+  if (!p) return;
+  (void)hipStreamSynchronize(p->copy);
+  for (auto& e : p->tev) (void)hipEventDestroy(e);
+  for (auto& s : p->slots) {
+    (void)hipEventDestroy(s.ready);
+    (void)hipEventDestroy(s.free_ev);
+  }
+  delete p;
+}
+
+int stream_layer_prefetch(lsq_pool* p, int32_t layer) {
+  LSQ_CHECK(p && layer >= 0 && layer < p->store->cfg.n_layers, LSQ_ERR_INVALID, "prefetch: bad layer %d", layer);
+  int si = find_slot(p, layer);
+  if (si >= 0) {
+    p->stats.hits += 1;
+    p->slots[si].last_use = ++p->tick;
+    return LSQ_OK;
+  }
+  LSQ_CHECK(!p->resident, LSQ_ERR_STATE, "prefetch: resident pool lost layer %d", layer);
+  int victim = -1;
+  for (int i = 0; i < p->n; ++i) {
+    if (p->slots[i].held) continue;
+    if (victim < 0 || p->slots[i].last_use < p->slots[victim].last_use) victim = i;
+  }
+  LSQ_CHECK(victim >= 0, LSQ_ERR_STATE, "prefetch: every slot is held (release a layer first)");
+  return copy_into(p, victim, layer);
+}
+
+int layer_pool_acquire(lsq_pool* p, int32_t layer, const void** blob_dev) {
+  LSQ_CHECK(p && blob_dev, LSQ_ERR_INVALID, "acquire: null pointer");
+  int si = find_slot(p, layer);
+  LSQ_CHECK(si >= 0, LSQ_ERR_STATE, "acquire: layer %d was never prefetched", layer);
+  Slot& sl = p->slots[si];
+  if (sl.ready_recorded && !p->resident) LSQ_HIP(hipStreamWaitEvent(p->compute, sl.ready, 0));
+  sl.held = true;
+  sl.last_use = ++p->tick;
+  *blob_dev = p->dev + (uint64_t)si * p->stride;
+  return LSQ_OK;
+}
+
+int layer_pool_release(lsq_pool* p, int32_t layer) {
+  LSQ_CHECK(p, LSQ_ERR_INVALID, "release: null pool");
+  int si = find_slot(p, layer);
+  LSQ_CHECK(si >= 0 && p->slots[si].held, LSQ_ERR_STATE, "release: layer %d is not held", layer);
+  Slot& sl = p->slots[si];
+  LSQ_HIP(hipEventRecord(sl.free_ev, p->compute));
+  sl.free_recorded = true;
+  sl.held = false;
+  return LSQ_OK;
+}
+
+int layer_pool_stats(lsq_pool* p, int32_t reset, lsq_pool_stats* out) {
+  LSQ_CHECK(p && out, LSQ_ERR_INVALID, "layer_pool_stats: null pointer");
+  double ms = 0.0;
+  for (int t = 0; t < p->tev_used; ++t) {
+    LSQ_HIP(hipEventSynchronize(p->tev[2 * t + 1]));
+    float e = 0.f;
+    LSQ_HIP(hipEventElapsedTime(&e, p->tev[2 * t], p->tev[2 * t + 1]));
+    ms += e;
+  }
+  p->stats.copy_ms += ms;
+  p->tev_used = 0;
+  *out = p->stats;
+  if (reset) p->stats = lsq_pool_stats{};
+  return LSQ_OK;
+}
+
+}  // extern "C"
+
+// ================================================================== step
+namespace {
+struct StepWs {
+  float* xs;         // (L+1) x [T, H] layer inputs (checkpoints)
+  float* dxa;        // [T, H]
+  float* dxb;        // [T, H]
+  uint16_t* xf;      // [T, H]  final-norm output, bf16
+  uint16_t* xf_lo;   // [T, H]  bf16 of its remainder
+  float* logits;     // [T, V]
+  uint16_t* dlogits; // [T, V]
+  uint16_t* dlogits_lo; // [T, V]
+  float* loss_rows;  // [T]
+  float* dxf;        // [T, H]
+  int32_t* bad;      // [1]
+  void* layer;       // layer workspace
+  size_t layer_bytes;
+  size_t total;
+};
+
+StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base) {
+  const uint64_t T = (uint64_t)B * S, H = c->hidden, V = c->vocab;
+  StepWs w{};
+  uint64_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](uint64_t bytes) -> void* {
+    void* r = base ? p + off : nullptr;
+    off = up(off + std::max<uint64_t>(bytes, 1), 256);
+    return r;
+  };
+  w.xs = static_cast<float*>(take(4 * T * H * (c->n_layers + 1)));
+  w.dxa = static_cast<float*>(take(4 * T * H));
+  w.dxb = static_cast<float*>(take(4 * T * H));
+  w.xf = static_cast<uint16_t*>(take(2 * T * H));
+  w.xf_lo = static_cast<uint16_t*>(take(2 * T * H));
+  w.logits = static_cast<float*>(take(4 * T * V));
+  w.dlogits = static_cast<uint16_t*>(take(2 * T * V));
+  w.dlogits_lo = static_cast<uint16_t*>(take(2 * T * V));
+  w.loss_rows = static_cast<float*>(take(4 * T));
+  w.dxf = static_cast<float*>(take(4 * T * H));
+  w.bad = static_cast<int32_t*>(take(4));
+  w.layer_bytes = layer_ws_bytes(c, B, S);
+  w.layer = take(w.layer_bytes);
+  w.total = off;
+  return w;
+}
+
+struct AliasCtx {
+  lsq_pool* pool;
+  int layer;
+  int other;
+  int rc;
+};
+
+// Control for the aliasing defect: hand the slot back after the recompute and
+// let a different layer's copy land in it before the backward GEMMs read it.
+int early_release_hook(void* vctx) {
+  AliasCtx* a = static_cast<AliasCtx*>(vctx);
+  lsq_pool* p = a->pool;
+  const int si = find_slot(p, a->layer);
+  if (si < 0) return fail(LSQ_ERR_STATE, "early release: layer %d not in a slot", a->layer);
+  if (int e = layer_pool_release(p, a->layer)) return e;
+  if (int e = copy_into(p, si, a->other)) return e;
+  LSQ_HIP(hipStreamWaitEvent(p->compute, p->slots[si].ready, 0));
+  return LSQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq) {
+  if (check_cfg(cfg) || batch < 1 || seq < 1) return 0;
+  return carve_step(cfg, batch, seq, nullptr).total;
+}
+
+int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
+                          int32_t B, int32_t S, float* loss, float* logits_out, int32_t flags, void* ws,
+                          size_t ws_bytes, float* x_trace, float* dx_trace) {
+  if (int e = check_cfg(cfg)) return e;
+  LSQ_CHECK(pool && res && ids && loss && ws, LSQ_ERR_INVALID, "lsq_train_step: null pointer");
+  LSQ_CHECK(res->embed && res->head && res->final_norm && res->lora && (res->lora_grad || (flags & LSQ_STEP_FORWARD_ONLY)),
+            LSQ_ERR_INVALID, "lsq_train_step: resident tensors missing");
+  LSQ_CHECK(B >= 1 && S >= 2 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "lsq_train_step: bad batch/seq");
+  LSQ_CHECK(memcmp(cfg, &pool->store->cfg, sizeof(lsq_model_cfg)) == 0, LSQ_ERR_INVALID,
+            "lsq_train_step: cfg differs from the store's");
+  const size_t need = carve_step(cfg, B, S, nullptr).total;
+  LSQ_CHECK(ws_bytes >= need, LSQ_ERR_WORKSPACE, "lsq_train_step: workspace %zu < %zu", ws_bytes, need);
+  LSQ_CHECK(!(flags & LSQ_STEP_DEBUG_EARLY_RELEASE) || (cfg->n_layers >= 2 && !pool->resident), LSQ_ERR_INVALID,
+            "early-release control needs a streamed pool and >= 2 layers");
+  const int L = cfg->n_layers, T = B * S, H = cfg->hidden, V = cfg->vocab;
+  hipStream_t s = pool->compute;
+  StepWs w = carve_step(cfg, B, S, ws);
+  lsq_lora_layout LL;
+  lora_layout(cfg, &LL);
+  const uint16_t* lora = static_cast<const uint16_t*>(res->lora);
+  float* xs = w.xs;
+  auto x_at = [&](int i) { return xs + (uint64_t)i * T * H; };
+  float* logits = logits_out ? logits_out : w.logits;
+
+  LSQ_HIP(hipMemsetAsync(w.bad, 0, 4, s));
+  if (int e = embed_gather(ids, static_cast<const uint16_t*>(res->embed), T, H, V, x_at(0), w.bad, s)) return e;
+  // ---- forward: prefetch one ahead, acquire, compute, release
+  if (int e = stream_layer_prefetch(pool, 0)) return e;
+  for (int i = 0; i < L; ++i) {
+    const void* blob = nullptr;
+    if (int e = layer_pool_acquire(pool, i, &blob)) return e;
+    if (i + 1 < L)
+      if (int e = stream_layer_prefetch(pool, i + 1)) return e;
+    if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s))
+      return e;
+    if (int e = layer_pool_release(pool, i)) return e;
+  }
+  // ---- head and loss (resident).  The head GEMMs take their float32 operand
+  // (final-norm output, dlogits) as a bf16 pair hi + lo, two MFMA passes into
+  // one float32 accumulator, so the gradient that enters the stack carries
+  // no bf16 rounding of its own.
+  if (int e = rmsnorm_fwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s,
+                          w.xf_lo))
+    return e;
+  for (int pass = 0; pass < 2; ++pass) {
+    FwdParams p{};
+    p.X = pass ? w.xf_lo : w.xf;
+    p.ldx = H;
+    p.kind = LSQ_W_BF16;
+    p.W = res->head;
+    p.M = T;
+    p.N = V;
+    p.K = H;
+    p.r = 0;
+    p.nseg = 1;
+    p.seg_end[0] = V;
+    p.resid = logits;
+    p.out = logits;
+    p.ldc = V;
+    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s)) return e;
+  }
+  if (int e = cross_entropy(logits, ids, B, S, V, w.loss_rows, w.dlogits, w.dlogits_lo, loss, s)) return e;
+  if (flags & LSQ_STEP_FORWARD_ONLY) return LSQ_OK;
+  for (int pass = 0; pass < 2; ++pass) {
+    BwdParams p{};
+    p.dY = pass ? w.dlogits_lo : w.dlogits;
+    p.ldy = V;
+    p.kind = LSQ_W_BF16;
+    p.W = res->head;
+    p.M = T;
+    p.N = V;
+    p.K = H;
+    p.rr = 0;
+    p.resid = w.dxf;
+    p.out = w.dxf;
+    p.ldc = H;
+    if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s)) return e;
+  }
+  float* dcur = w.dxa;
+  float* dnext = w.dxb;
+  if (int e = rmsnorm_bwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), w.dxf, nullptr, T, H, cfg->rms_eps,
+                          dcur, nullptr, s))
+    return e;
+  const size_t act = sizeof(float) * (size_t)T * H;
+  if (x_trace) LSQ_HIP(hipMemcpyAsync(x_trace, xs, act * (L + 1), hipMemcpyDeviceToDevice, s));
+  if (dx_trace) LSQ_HIP(hipMemcpyAsync(dx_trace + (size_t)L * T * H, dcur, act, hipMemcpyDeviceToDevice, s));
+  // ---- backward: the same stream of layers in reverse, recompute inside each layer
+  if (int e = stream_layer_prefetch(pool, L - 1)) return e;
+  for (int i = L - 1; i >= 0; --i) {
+    const void* blob = nullptr;
+    if (int e = layer_pool_acquire(pool, i, &blob)) return e;
+    if (i - 1 >= 0)
+      if (int e = stream_layer_prefetch(pool, i - 1)) return e;
+    const bool early = flags & LSQ_STEP_DEBUG_EARLY_RELEASE;
+    AliasCtx actx{pool, i, (i + 1) % L, 0};
+    LayerHook hook{early_release_hook, &actx};
+    float* grad = res->lora_grad + (uint64_t)i * LL.layer_elems;
+    if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
+                          s, early ? &hook : nullptr))
+      return e;
+    if (!early)
+      if (int e = layer_pool_release(pool, i)) return e;
+    std::swap(dcur, dnext);
+    if (dx_trace) LSQ_HIP(hipMemcpyAsync(dx_trace + (size_t)i * T * H, dcur, act, hipMemcpyDeviceToDevice, s));
+  }
+  return LSQ_OK;
+}
+
+int lsq_train_step(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids, int32_t B,
+                   int32_t S, float* loss, float* logits_out, int32_t flags, void* ws, size_t ws_bytes) {
+  return lsq_train_step_traced(cfg, pool, res, ids, B, S, loss, logits_out, flags, ws, ws_bytes, nullptr, nullptr);
+}
+
+// ================================================================== pre-flight
+int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers,
+                      lsq_vram_breakdown* out) {
+  if (int e = check_cfg(cfg)) return e;
+  LSQ_CHECK(out && batch >= 1 && seq >= 2 && n_buffers >= 2, LSQ_ERR_INVALID, "vram_predict_peak: bad arguments");
+  lsq_blob_layout BL;
+  blob_layout(cfg, &BL);
+  lsq_lora_layout LL;
+  lora_layout(cfg, &LL);
+  const uint64_t T = (uint64_t)batch * seq, H = cfg->hidden;
+  out->slots = (uint64_t)n_buffers * BL.total_bytes;
+  out->resident = 2ull * cfg->vocab * H * (cfg->tied ? 1 : 2) + 2 * H;
+  out->adapters = LL.layer_elems * (uint64_t)cfg->n_layers * (2 + 4);
+  out->checkpoints = 4 * T * H * (cfg->n_layers + 1);
+  out->step_workspace = carve_step(cfg, batch, seq, nullptr).total - out->checkpoints;
+  out->total = out->slots + out->resident + out->adapters + out->checkpoints + out->step_workspace + 4 * T + 64;
+  return LSQ_OK;
+}
+
+int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers, uint64_t free_override,
+                  lsq_vram_breakdown* out) {
+  lsq_vram_breakdown b{};
+  if (int e = vram_predict_peak(cfg, batch, seq, n_buffers, &b)) return e;
+  if (out) *out = b;
+  uint64_t free_b = free_override;
+  if (!free_b) {
+    size_t f = 0, t = 0;
+    LSQ_HIP(hipMemGetInfo(&f, &t));
+    free_b = f;
+  }
+  LSQ_CHECK(b.total <= free_b, LSQ_ERR_REFUSED,
+            "a streaming step is predicted to need %.2f GB of VRAM but only %.2f GB is free (batch %d x seq %d; "
+            "logits %.2f GB, checkpoints %.2f GB, %d layer buffers %.2f GB)",
+            b.total / 1e9, free_b / 1e9, batch, seq, 6.0 * batch * seq * cfg->vocab / 1e9, b.checkpoints / 1e9,
+            n_buffers, b.slots / 1e9);
+  return LSQ_OK;
+}
+
+}  // extern "C"

@@ -104,6 +104,8 @@ _SIGS = {
     "lsq_step_workspace_size": (_SZ, [C.POINTER(ModelCfg), _I32, _I32]),
     "lsq_train_step": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32, _P,
                                  _SZ]),
+    "lsq_train_step_traced": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32,
+                                        _P, _SZ, _P, _P]),
     "vram_predict_peak": (C.c_int, [C.POINTER(ModelCfg), _I32, _I32, _I32, C.POINTER(VramBreakdown)]),
     "lsq_preflight": (C.c_int, [C.POINTER(ModelCfg), _I32, _I32, _I32, _U64, C.POINTER(VramBreakdown)]),
     "lsq_prof_enable": (C.c_int, [_I32]),

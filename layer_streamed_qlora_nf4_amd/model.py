@@ -1,0 +1,179 @@
+"""Thin driver over liblsq: device memory and streams from PyTorch, every
+computation in the library.
+
+Store      the per-layer shard store (pinned host arena), written once from
+           seeded synthetic bf16 weights through nf4_quantize on the GPU.
+Resident   embedding, final norm, head, adapters and adapter gradients.
+Runner     a layer pool (streamed N slots, or resident) with its compute and
+           copy streams and the step workspace; ``step`` is one lsq_train_step.
+"""
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import lib, synth
+
+PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def _bits_to_dev(bits, device):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr())
+
+
+class Store:
+    """One layer blob per decoder layer in a host arena (pinned unless refused)."""
+
+    def __init__(self, cfg, device="cuda", flags=0, layer_source=None):
+        self.cfg = cfg
+        self.ccfg = lib.model_cfg(cfg)
+        h = C.c_void_p()
+        lib.call("shard_store_create", C.byref(self.ccfg), flags, C.byref(h))
+        self.handle = h
+        self.layer_bytes = int(lib.raw("shard_store_layer_bytes")(h))
+        self.pinned = bool(lib.raw("shard_store_is_pinned")(h))
+        src = layer_source or (lambda i: synth.layer_weights(cfg, cfg.wid, i))
+        stream = torch.cuda.current_stream(device)
+        staging = torch.empty(self.layer_bytes + 256, dtype=torch.uint8, device=device)
+        for i in range(cfg.n_layers):
+            w = src(i)
+            dev = {k: _bits_to_dev(v, device) for k, v in w.items()}
+            ls = lib.LayerSrc()
+            for j, name in enumerate(PROJ):
+                ls.w[j] = dev[name].data_ptr()
+            ls.norm1 = dev["norm1"].data_ptr()
+            ls.norm2 = dev["norm2"].data_ptr()
+            if cfg.qkv_bias:
+                for j, name in enumerate(("bq", "bk", "bv")):
+                    ls.bias[j] = dev[name].data_ptr()
+            lib.call("shard_store_write_layer", h, i, C.byref(ls), _ptr(staging), staging.numel(),
+                     lib.stream_handle(stream))
+            del dev
+        del staging
+
+    def host_blob(self, i):
+        p = lib.raw("shard_store_layer_host")(self.handle, i)
+        return np.ctypeslib.as_array((C.c_uint8 * self.layer_bytes).from_address(p))
+
+    def close(self):
+        if self.handle:
+            lib.raw("shard_store_destroy")(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lora_arena_host(cfg, layers=None):
+    """Host bf16 bits of every layer's adapters in the library's stacked layout."""
+    L = lib.lora_layout(cfg)
+    n = cfg.n_layers if layers is None else layers
+    arena = np.zeros((n, L.layer_elems), dtype=np.uint16)
+    for i in range(n):
+        ad = synth.layer_lora(cfg, cfg.wid, i)
+        groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+        for g, names in enumerate(groups):
+            A = np.concatenate([ad[nm][0] for nm in names], axis=0)
+            B = np.concatenate([ad[nm][1] for nm in names], axis=0)
+            arena[i, L.a_off[g]:L.a_off[g] + A.size] = A.ravel()
+            arena[i, L.b_off[g]:L.b_off[g] + B.size] = B.ravel()
+    return arena
+
+
+def split_lora_grads(cfg, grad_layer):
+    """float32 gradient block of one layer -> name -> (dA [r, in], dB [out, r])."""
+    L = lib.lora_layout(cfg)
+    r = cfg.lora_r
+    out = {}
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    for g, names in enumerate(groups):
+        ao, bo = L.a_off[g], L.b_off[g]
+        for nm in names:
+            n_out, n_in = cfg.proj_shape(nm)
+            dA = grad_layer[ao:ao + r * n_in].reshape(r, n_in)
+            dB = grad_layer[bo:bo + n_out * r].reshape(n_out, r)
+            out[nm] = (dA, dB)
+            ao += r * n_in
+            bo += n_out * r
+    return out
+
+
+class Resident:
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        rw = synth.resident_weights(cfg, cfg.wid)
+        self.embed = _bits_to_dev(rw["embed"], device)
+        self.head = self.embed if cfg.tied else _bits_to_dev(rw["head"], device)
+        self.final_norm = _bits_to_dev(rw["final_norm"], device)
+        self.lora = _bits_to_dev(lora_arena_host(cfg), device)
+        self.layer_elems = self.lora.shape[1]
+
+    def new_grads(self):
+        return torch.zeros(self.lora.shape, dtype=torch.float32, device=self.lora.device)
+
+    def struct(self, grads):
+        return lib.Resident(self.embed.data_ptr(), self.head.data_ptr(), self.final_norm.data_ptr(),
+                            self.lora.data_ptr(), grads.data_ptr() if grads is not None else None)
+
+
+class Runner:
+    """A pool over a store plus the step workspace.  mode: 'streamed' or 'resident'."""
+
+    def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda"):
+        self.cfg, self.store, self.res = cfg, store, resident
+        self.ccfg = lib.model_cfg(cfg)
+        self.compute = torch.cuda.Stream(device)
+        self.copy = torch.cuda.Stream(device)
+        stride = (store.layer_bytes + 4095) // 4096 * 4096
+        n = cfg.n_layers if mode == "resident" else (n_buffers or cfg.n_buffers)
+        flags = pool_flags | (lib.LSQ_POOL_RESIDENT if mode == "resident" else 0)
+        self.slots = torch.empty(n * stride, dtype=torch.uint8, device=device)
+        h = C.c_void_p()
+        lib.call("layer_pool_create", store.handle, n, _ptr(self.slots), stride, lib.stream_handle(self.compute),
+                 lib.stream_handle(self.copy), flags, C.byref(h))
+        self.pool = h
+        self.n_buffers = n
+        self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq))
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        self.grads = resident.new_grads()
+
+    def step(self, ids, forward_only=False, early_release=False, logits=None, x_trace=None, dx_trace=None):
+        flags = (lib.LSQ_STEP_FORWARD_ONLY if forward_only else 0) | \
+                (lib.LSQ_STEP_DEBUG_EARLY_RELEASE if early_release else 0)
+        self.compute.wait_stream(torch.cuda.current_stream())
+        rs = self.res.struct(self.grads)
+        opt = (lambda t: _ptr(t) if t is not None else None)
+        if x_trace is None and dx_trace is None:
+            lib.call("lsq_train_step", C.byref(self.ccfg), self.pool, C.byref(rs), _ptr(ids), self.cfg.batch,
+                     self.cfg.seq, _ptr(self.loss), opt(logits), flags, _ptr(self.ws), self.ws_bytes)
+        else:
+            lib.call("lsq_train_step_traced", C.byref(self.ccfg), self.pool, C.byref(rs), _ptr(ids), self.cfg.batch,
+                     self.cfg.seq, _ptr(self.loss), opt(logits), flags, _ptr(self.ws), self.ws_bytes,
+                     opt(x_trace), opt(dx_trace))
+        torch.cuda.current_stream().wait_stream(self.compute)
+        return self.loss
+
+    def stats(self, reset=False):
+        st = lib.PoolStats()
+        lib.call("layer_pool_stats", self.pool, int(reset), C.byref(st))
+        return st
+
+    def close(self):
+        if self.pool:
+            torch.cuda.synchronize()
+            lib.raw("layer_pool_destroy")(self.pool)
+            self.pool = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,130 @@
+"""GPU parity of decoder_layer_fwd / decoder_layer_bwd against the oracle."""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+from layer_streamed_qlora_nf4_amd import configs, lib, model, synth
+from oracle import layer as olayer
+from oracle import nf4 as onf4
+from tests.gpu_util import bits_f64, dev, empty_bytes, print_case, ptr, rel_err, stream
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def oracle_cfg(cfg):
+    return olayer.LayerCfg(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.eps,
+                           cfg.theta, cfg.qkv_bias)
+
+
+def oracle_layer_params(cfg, layer, rows=None):
+    """Oracle weights (float64) from the same seeded bits the store was written from."""
+    w = synth.layer_weights(cfg, cfg.wid, layer)
+    W = {}
+    for name in model.PROJ:
+        if cfg.quant == "nf4":
+            packed, absmax = onf4.quantize(w[name])
+            W[name] = onf4.dequantize_bf16_f64(packed, absmax)
+        else:
+            W[name] = bits_f64(w[name])
+    for k in ("norm1", "norm2", "bq", "bk", "bv"):
+        if k in w:
+            W[k] = bits_f64(w[k])
+    ad = {n: (bits_f64(a), bits_f64(b)) for n, (a, b) in synth.layer_lora(cfg, cfg.wid, layer).items()}
+    return W, ad
+
+
+def run_layer(cfg, x_bits, dout_f32, want_bwd=True):
+    cfg1 = cfg.with_(n_layers=1)
+    store = model.Store(cfg1)
+    blob = dev(store.host_blob(0).copy())
+    lora = dev(model.lora_arena_host(cfg1)[0].view(np.int16))
+    ccfg = lib.model_cfg(cfg1)
+    B, S, H = cfg.batch, cfg.seq, cfg.hidden
+    wsb = lib.raw("decoder_layer_workspace_size")(C.byref(ccfg), B, S)
+    ws = empty_bytes(wsb)
+    x = dev(bits_f64(x_bits).astype(np.float32))
+    xo = torch.empty_like(x)
+    lib.call("decoder_layer_fwd", C.byref(ccfg), ptr(blob), ptr(lora), ptr(x), B, S, ptr(xo), ptr(ws), wsb, stream())
+    out = {"x_out": xo}
+    if want_bwd:
+        dxo = dev(dout_f32)
+        dxi = torch.empty_like(x)
+        grad = torch.zeros(lora.numel(), dtype=torch.float32, device="cuda")
+        lib.call("decoder_layer_bwd", C.byref(ccfg), ptr(blob), ptr(lora), ptr(x), ptr(dxo), B, S, ptr(dxi), ptr(grad),
+                 0, ptr(ws), wsb, stream())
+        out["dx_in"] = dxi
+        out["grad"] = grad
+    torch.cuda.synchronize()
+    store.close()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def inputs(cfg, seq=None):
+    S = seq or cfg.seq
+    x = synth.normal_bf16((cfg.batch, S, cfg.hidden), 0.0, 1.0, (cfg.wid, 99, synth.TENSOR_IDS["x"]))
+    d = synth.normal_bf16((cfg.batch, S, cfg.hidden), 0.0, 1.0, (cfg.wid, 99, synth.TENSOR_IDS["dx_out"]))
+    return x, bits_f64(d).astype(np.float32)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_QWEN,
+                                 configs.TINY.with_(name="tiny-b1-s200", batch=1, seq=200, wid=11)])
+def test_decoder_layer_matches_oracle(gpu, cfg):
+    print_case(test="decoder_layer", cfg=cfg.name, B=cfg.batch, S=cfg.seq)
+    x_bits, dout = inputs(cfg)
+    got = run_layer(cfg, x_bits, dout)
+    W, ad = oracle_layer_params(cfg, 0)
+    oc = oracle_cfg(cfg)
+    x = bits_f64(x_bits)
+    ref_out = olayer.layer_fwd(oc, x, W, ad, cfg.lora_scale)
+    ref_dx, ref_g = olayer.layer_bwd(oc, x, W, ad, cfg.lora_scale, dout.astype(np.float64))
+    assert rel_err(got["x_out"].reshape(ref_out.shape), ref_out) <= TOL
+    assert rel_err(got["dx_in"].reshape(ref_dx.shape), ref_dx) <= TOL
+    g = model.split_lora_grads(cfg, got["grad"])
+    for name in model.PROJ:
+        for which in (0, 1):
+            e = rel_err(g[name][which], ref_g[name][which])
+            assert e <= TOL, f"{name} d{'AB'[which]}: {e:.3e}"
+
+
+def test_8b_layer_short_sequence_matches_oracle(gpu):
+    """Full 8B widths (every GEMM at its real N and K), a short ragged sequence."""
+    cfg = configs.LAYER_8B.with_(seq=100, wid=12)
+    print_case(test="decoder_layer_8b", S=cfg.seq)
+    x_bits, dout = inputs(cfg)
+    got = run_layer(cfg, x_bits, dout)
+    W, ad = oracle_layer_params(cfg, 0)
+    oc = oracle_cfg(cfg)
+    x = bits_f64(x_bits)
+    ref_out = olayer.layer_fwd(oc, x, W, ad, cfg.lora_scale)
+    ref_dx, ref_g = olayer.layer_bwd(oc, x, W, ad, cfg.lora_scale, dout.astype(np.float64))
+    assert rel_err(got["x_out"].reshape(ref_out.shape), ref_out) <= TOL
+    assert rel_err(got["dx_in"].reshape(ref_dx.shape), ref_dx) <= TOL
+    g = model.split_lora_grads(cfg, got["grad"])
+    for name in model.PROJ:
+        for which in (0, 1):
+            assert rel_err(g[name][which], ref_g[name][which]) <= TOL, (name, which)
+
+
+def test_8b_layer_full_sequence_prefix_matches_oracle(gpu):
+    """The 1 x 2048-token 8B layer as the bench runs it; causality makes the
+    first 64 output rows a function of the first 64 inputs only."""
+    cfg = configs.LAYER_8B
+    print_case(test="decoder_layer_8b_full", S=cfg.seq)
+    x_bits, dout = inputs(cfg)
+    got = run_layer(cfg, x_bits, dout, want_bwd=False)
+    W, ad = oracle_layer_params(cfg, 0)
+    P = 64
+    ref = olayer.layer_fwd(oracle_cfg(cfg), bits_f64(x_bits)[:, :P], W, ad, cfg.lora_scale)
+    assert rel_err(got["x_out"].reshape(1, cfg.seq, -1)[:, :P], ref) <= TOL
+
+
+def test_layer_rejects_bad_arguments(gpu):
+    cfg = configs.TINY.with_(n_layers=1)
+    ccfg = lib.model_cfg(cfg)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("decoder_layer_fwd", C.byref(ccfg), C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1, 8,
+                 C.c_void_p(512), C.c_void_p(1024), 16, None)
+    assert e.value.status == "LSQ_ERR_WORKSPACE"

@@ -1,0 +1,158 @@
+"""The streamed training step: oracle parity on small stacks, streamed ==
+resident bit for bit (logits and every adapter gradient, counted n of n), and
+the aliasing control that must break the gradients."""
+import numpy as np
+import pytest
+import torch
+
+from layer_streamed_qlora_nf4_amd import configs, lib, model, synth
+from oracle import layer as olayer
+from oracle import model as omodel
+from tests.gpu_util import bits_f64, print_case, rel_err
+from tests.test_gpu_layer import oracle_cfg, oracle_layer_params
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def ids_for(cfg):
+    return synth.token_ids(cfg.batch, cfg.seq, cfg.vocab, (cfg.wid, 500, synth.TENSOR_IDS["ids"]))
+
+
+def run(cfg, mode, store, res, ids, early=False, n_buffers=None):
+    r = model.Runner(cfg, store, res, mode=mode, n_buffers=n_buffers)
+    logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+    loss = r.step(ids, logits=logits, early_release=early).clone()
+    torch.cuda.synchronize()
+    out = dict(loss=loss.item(), logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy(), stats=r.stats())
+    r.close()
+    return out
+
+
+def oracle_step(cfg, ids_np):
+    rw = synth.resident_weights(cfg, cfg.wid)
+    emb = bits_f64(rw["embed"])
+    head = emb if cfg.tied else bits_f64(rw["head"])
+    params = [oracle_layer_params(cfg, i) for i in range(cfg.n_layers)]
+    return omodel.stack_fwd_bwd(oracle_cfg(cfg), ids_np.astype(np.int64), emb, lambda i: params[i], cfg.n_layers,
+                                bits_f64(rw["final_norm"]), head, cfg.lora_scale)
+
+
+def traced_step(cfg, store, res, ids, mode="streamed"):
+    r = model.Runner(cfg, store, res, mode=mode)
+    T, H, L = cfg.tokens, cfg.hidden, cfg.n_layers
+    logits = torch.empty((T, cfg.vocab), dtype=torch.float32, device="cuda")
+    xt = torch.empty((L + 1, T, H), dtype=torch.float32, device="cuda")
+    dxt = torch.empty((L + 1, T, H), dtype=torch.float32, device="cuda")
+    loss = r.step(ids, logits=logits, x_trace=xt, dx_trace=dxt).item()
+    torch.cuda.synchronize()
+    out = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy(), x=xt.cpu().numpy(),
+               dx=dxt.cpu().numpy())
+    r.close()
+    return out
+
+
+def check_layers_against_oracle(cfg, got, layers, tol=TOL):
+    """Each sampled layer recomputed by the oracle from the exact input and upstream
+    gradient this run used (bf16 rounding does not compound across layers here)."""
+    oc = oracle_cfg(cfg)
+    B, S, H = cfg.batch, cfg.seq, cfg.hidden
+    for i in layers:
+        W, ad = oracle_layer_params(cfg, i)
+        x = got["x"][i].astype(np.float64).reshape(B, S, H)
+        out = olayer.layer_fwd(oc, x, W, ad, cfg.lora_scale)
+        e = rel_err(got["x"][i + 1].reshape(B, S, H), out)
+        assert e <= tol, f"layer {i} forward: {e:.3e}"
+        dx, g_ref = olayer.layer_bwd(oc, x, W, ad, cfg.lora_scale, got["dx"][i + 1].astype(np.float64).reshape(B, S, H))
+        e = rel_err(got["dx"][i].reshape(B, S, H), dx)
+        assert e <= tol, f"layer {i} dx: {e:.3e}"
+        g = model.split_lora_grads(cfg, got["grads"][i])
+        for name in model.PROJ:
+            for which in (0, 1):
+                e = rel_err(g[name][which], g_ref[name][which])
+                assert e <= tol, f"layer {i} {name} d{'AB'[which]}: {e:.3e}"
+
+
+def check_head_against_oracle(cfg, got, ids_np, tol=TOL):
+    rw = synth.resident_weights(cfg, cfg.wid)
+    head = bits_f64(rw["embed"] if cfg.tied else rw["head"])
+    fn = bits_f64(rw["final_norm"])
+    B, S, H = cfg.batch, cfg.seq, cfg.hidden
+    xL = got["x"][cfg.n_layers].astype(np.float64).reshape(B, S, H)
+    logits = olayer.rmsnorm(xL, fn, cfg.eps) @ head.T
+    assert rel_err(got["logits"].reshape(logits.shape), logits) <= tol
+    loss, dlogits = omodel.ce_loss_and_grad(logits, ids_np.astype(np.int64))
+    assert abs(got["loss"] - loss) <= tol * abs(loss)
+    dxL = olayer.rmsnorm_bwd(xL, fn, cfg.eps, dlogits @ head)
+    assert rel_err(got["dx"][cfg.n_layers].reshape(B, S, H), dxL) <= tol
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_QWEN])
+def test_streamed_step_matches_oracle(gpu, cfg):
+    print_case(test="stack_oracle", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids_np = ids_for(cfg)
+    ids = torch.from_numpy(ids_np).cuda()
+    got = traced_step(cfg, store, res, ids)
+    # end to end: loss and logits against the oracle's own forward of the whole stack
+    loss, logits, _ = oracle_step(cfg, ids_np)
+    assert abs(got["loss"] - loss) <= TOL * abs(loss)
+    assert rel_err(got["logits"].reshape(logits.shape), logits) <= TOL
+    # the head and every layer, each from the exact inputs this step used
+    check_head_against_oracle(cfg, got, ids_np)
+    check_layers_against_oracle(cfg, got, range(cfg.n_layers))
+
+
+def _compare_bitwise(cfg, a, b):
+    assert a["loss"] == b["loss"]
+    assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32)), "logits differ"
+    exact = total = 0
+    for i in range(cfg.n_layers):
+        ga = model.split_lora_grads(cfg, a["grads"][i])
+        gb = model.split_lora_grads(cfg, b["grads"][i])
+        for name in model.PROJ:
+            for which in (0, 1):
+                total += 1
+                exact += int(np.array_equal(ga[name][which].view(np.uint32), gb[name][which].view(np.uint32)))
+    return exact, total
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_QWEN, configs.TINY.with_(name="tiny-5L", n_layers=5,
+                                                                                     n_buffers=3, wid=13)])
+def test_streamed_equals_resident_and_control_breaks_it(gpu, cfg):
+    print_case(test="streamed_vs_resident", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    resident = run(cfg, "resident", store, res, ids)
+    streamed = run(cfg, "streamed", store, res, ids)
+    exact, total = _compare_bitwise(cfg, resident, streamed)
+    print(f"streamed == resident: {exact} of {total} gradient tensors bit-identical, max|dlogit| = 0.0")
+    assert exact == total == cfg.n_layers * 14
+    # slot reuse: the last layers at the turn and the first at the next step are not re-copied
+    assert streamed["stats"].copies == 2 * cfg.n_layers - min(cfg.n_buffers, cfg.n_layers)
+    # the control: a slot refilled before its backward GEMMs must change the gradients
+    bad = run(cfg, "streamed", store, res, ids, early=True)
+    assert np.array_equal(bad["logits"].view(np.uint32), resident["logits"].view(np.uint32))
+    exact_bad, _ = _compare_bitwise(cfg, resident, {**bad, "logits": resident["logits"], "loss": resident["loss"]})
+    print(f"early-release control: {exact_bad} of {total} gradient tensors bit-identical")
+    assert exact_bad < total
+
+
+def test_step_is_deterministic_and_repeats(gpu):
+    cfg = configs.TINY
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    r = model.Runner(cfg, store, res)
+    losses, grads = [], []
+    for _ in range(3):
+        losses.append(r.step(ids).item())
+        grads.append(r.grads.cpu().numpy().copy())
+    assert losses[0] == losses[1] == losses[2]
+    assert np.array_equal(grads[0], grads[2])
+    st = r.stats()
+    # first step copies 2L - N, every later step 2L - 2N (layer 0.. N-1 stay in their slots)
+    assert st.copies == (2 * cfg.n_layers - cfg.n_buffers) + 2 * (2 * cfg.n_layers - 2 * cfg.n_buffers)
+    r.close()

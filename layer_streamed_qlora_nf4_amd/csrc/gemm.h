@@ -37,6 +37,8 @@ struct FwdParams {
   const float* resid;    // [M, ldc] float32 (EPI_F32_RESID)
   void* out;
   int64_t ldc;
+  float* part;           // split-K partials [splits, M, N] (workspace); set by gemm_fwd
+  int splits;
 };
 
 // Backward: out[M, K] = dY[M, N] W + G[M, rr] Al[rr, K] (+ resid).
@@ -54,16 +56,60 @@ struct BwdParams {
   const float* resid;
   void* out;
   int64_t ldc;
+  float* part;           // split-K partials [splits, M, K] (workspace); set by gemm_bwd
+  int splits;
 };
 
-int gemm_fwd(const FwdParams& p, int epi, hipStream_t s);
-int gemm_bwd(const BwdParams& p, int epi, hipStream_t s);
-// U[M, rr] = bf16(s X A^T), A = stacked [rr, K].
+// Split-K: a launch with fewer tiles than the chip has CUs splits its
+// reduction into a fixed number of ranges (a pure function of the shape),
+// writes float32 partials and sums them in split order in a second kernel.
+int gemm_fwd_splits(int M, int N, int K);
+int gemm_bwd_splits(int M, int N, int K, int rr);
+size_t gemm_fwd_ws_bytes(int M, int N, int K);
+size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr);
+
+// ws: split-K partial buffer (>= the *_ws_bytes query), may be null when that is 0.
+int gemm_fwd(const FwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
+int gemm_bwd(const BwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
+// Reduction chunks of lora_g, each inside one segment.
+struct GChunks {
+  int begin[128], end[128];
+  int n;
+};
+
+// U[M, rr] = bf16(s X A^T), A = stacked [rr, K]; ws holds the chunk partials.
+size_t lora_down_ws_bytes(int M, int K, int rr);
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, hipStream_t st);
-// G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]); bt_ws holds N * r bf16.
+              int64_t ldu, float* ws, size_t ws_bytes, hipStream_t st);
+// G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]); ws holds B transposed and partials.
+size_t lora_g_ws_bytes(int M, int N, int r);
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, uint16_t* bt_ws, hipStream_t st);
+           float s, uint16_t* G, int64_t ldg, float* ws, size_t ws_bytes, hipStream_t st);
+// One reduction over the token dimension, C = S^T L: S [M, ns] (ns <= 64, a
+// multiple of 8), L [M, nl]; small_rows: out [ns, nl] (dA); else out [nl, ns] (dB).
+struct TnTask {
+  const uint16_t* S;
+  int64_t lds;
+  int ns;
+  const uint16_t* L;
+  int64_t ldl;
+  int nl;
+  float* out;
+  int64_t ldo;
+  int small_rows;
+  int tile0;          // set by lora_grads
+};
+struct TnBatch {
+  TnTask t[8];
+  int ntasks, M, accumulate;
+};
+struct SegFinish {
+  int c0[4], c1[4], col[4];
+  int n;
+};
+// Every task of one group in one launch, no partials (fixed token order per output).
+int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream_t st);
+
 // Token-dimension reduction C = S^T L (small_rows: [ns, nl]; else [nl, ns]).
 size_t lora_tn_ws_bytes(int M, int ns, int nl);
 int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,

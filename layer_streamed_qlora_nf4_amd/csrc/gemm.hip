@@ -69,18 +69,20 @@ __device__ __forceinline__ void decode_word(uint32_t w, float a, const float* lu
 
 // =========================================================== forward (NT)
 // C[M, N] = X[M, K] W[N, K]^T + U_seg[M, r] Bl[N, r]^T (+ bias) (+ resid)
-template <int BM, int BN, int WKIND, int EPI>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
-  constexpr int A_CHUNKS = BM * 8 / NTHREADS;                                   // 16-B chunks per thread
-  constexpr int B_CHUNKS = (WKIND == LSQ_W_NF4) ? (BN * 2 / NTHREADS) : (BN * 8 / NTHREADS);
-  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+template <int BM, int BN, int WGM, int WGN, int WKIND, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_fwd_kernel(FwdParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
+  constexpr int A_TOTAL = BM * 8;                                                // 16-B chunks of the A tile
+  constexpr int B_TOTAL = (WKIND == LSQ_W_NF4) ? BN * 2 : BN * 8;
+  constexpr int A_CHUNKS = (A_TOTAL + NT - 1) / NT, B_CHUNKS = (B_TOTAL + NT - 1) / NT;
+  static_assert(TM >= 1 && TN >= 1 && A_TOTAL % NT == 0, "bad tile");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
   __shared__ float lut[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
@@ -88,7 +90,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
   if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const uint16_t* __restrict__ X = p.X;
-  const int K = p.K, nk = K / BK;
+  const int K = p.K, nk_all = K / BK;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   uint4 ra[A_CHUNKS], rb[B_CHUNKS];
   float rabs[B_CHUNKS];
@@ -97,7 +102,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int q = tid + i * NT, row = q >> 3, c = q & 7;
       int m = m0 + row;
       ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(X + (int64_t)m * p.ldx + k0 + c * 8) : make_uint4(0, 0, 0, 0);
     }
@@ -105,9 +110,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
       const uint8_t* W = static_cast<const uint8_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NTHREADS, row = q >> 1, h = q & 1;
+        int q = tid + i * NT, row = q >> 1, h = q & 1;
         int n = n0 + row;
-        if (n < p.N) {
+        if (q < B_TOTAL && n < p.N) {
           rb[i] = *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16);
           rabs[i] = p.absmax[(int64_t)n * (K / 64) + kt];
         } else {
@@ -119,9 +124,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
       const uint16_t* W = static_cast<const uint16_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+        int q = tid + i * NT, row = q >> 3, c = q & 7;
         int n = n0 + row;
-        rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+        rb[i] = (q < B_TOTAL && n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -129,13 +134,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int q = tid + i * NT, row = q >> 3, c = q & 7;
       *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
     }
     if (WKIND == LSQ_W_NF4) {
 #pragma unroll
       for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NTHREADS, row = q >> 1, h = q & 1;
+        int q = tid + i * NT, row = q >> 1, h = q & 1;
+        if (q >= B_TOTAL) break;
         uint32_t words[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -147,7 +153,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+        int q = tid + i * NT, row = q >> 3, c = q & 7;
+        if (q >= B_TOTAL) break;
         *reinterpret_cast<uint4*>(&Bs[buf][swz(row, c)]) = rb[i];
       }
     }
@@ -159,13 +166,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
+  if (kbeg < nk) load_tile(kbeg);
   __syncthreads();  // lut
-  store_tile(0);
+  if (kbeg < nk) store_tile(0);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  for (int kt = kbeg; kt < nk; ++kt) {
+    const int cur = (kt - kbeg) & 1;
     if (kt + 1 < nk) load_tile(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -185,7 +192,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
   }
 
   // LoRA up-projection: acc += U_seg B^T, one or more extra 32-wide reduction steps.
-  if (p.r > 0) {
+  if (p.r > 0 && split == 0) {
     const int g = lane >> 4;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -212,6 +219,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
   }
 
   // Epilogue: lane holds C[4 (lane >> 4) + v][lane & 15] of each 16x16 tile.
+  if (p.splits > 1) {
+    float* part = p.part + (int64_t)split * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + j * 16 + (lane & 15);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+          if (row < p.M) part[(int64_t)row * p.N + col] = acc[i][j][v];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int col = n0 + wn * WN + j * 16 + (lane & 15);
@@ -241,19 +264,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fwd_kernel(FwdParams p) {
 // C[M, K] = dY[M, N] W[N, K] + G[M, rr] Al[rr, K] (+ resid)
 // The weight slab (64 rows of W) is decoded straight into a transposed LDS
 // tile Bt[k][n] so that each lane's 8 reduction values are contiguous.
-template <int BM, int BO, int WKIND, int EPI>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
-  constexpr int WM = BM / 2, WO = BO / 2, TM = WM / 16, TO = WO / 16;
-  constexpr int A_CHUNKS = BM * 8 / NTHREADS;
+template <int BM, int BO, int WGM, int WGN, int WKIND, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WO = BO / WGN, TM = WM / 16, TO = WO / 16;
+  constexpr int A_TOTAL = BM * 8;
+  constexpr int A_CHUNKS = (A_TOTAL + NT - 1) / NT;
   // Transposing loads: each thread owns a 4 (rows n) x 8 (cols k) micro-tile.
-  constexpr int MT_PER_THREAD = (64 / 4) * (BO / 8) / NTHREADS;
-  static_assert(MT_PER_THREAD >= 1, "BO too small");
+  constexpr int MT_TOTAL = (64 / 4) * (BO / 8);
+  constexpr int MT_PER_THREAD = (MT_TOTAL + NT - 1) / NT;
+  static_assert(TM >= 1 && TO >= 1 && A_TOTAL % NT == 0 && BO >= 128, "bad tile");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bt[2][BO * 64];
   __shared__ float lut[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wo = wave & 1;
+  const int wm = wave / WGN, wo = wave % WGN;
   const int tiles_o = (p.K + BO - 1) / BO;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
@@ -263,11 +289,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
   const int K = p.K;
   const int nk_main = (p.N + BK - 1) / BK;
   const int nk_lora = (p.rr + BK - 1) / BK;
-  const int nk = nk_main + nk_lora;
+  const int nk_all = nk_main + nk_lora;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   // micro-tile coordinates: lanes 8 apart in q, neighbouring rg pairs in a pass
   auto mt_coords = [&](int i, int& rg, int& q) {
-    int u = tid + i * NTHREADS;
+    int u = tid + i * NT;
     q = (u & 7) | (((u >> 4) & ((BO / 8 / 8) - 1)) << 3);
     rg = ((u >> 3) & 1) | ((u >> (4 + __builtin_ctz(BO / 64))) << 1);
   };
@@ -285,13 +314,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
     const int red_lim = lora ? p.rr : p.N;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int q = tid + i * NT, row = q >> 3, c = q & 7;
       int m = m0 + row, rcol = r0 + c * 8;
       ra[i] = (m < p.M && rcol < red_lim) ? *reinterpret_cast<const uint4*>(Asrc + (int64_t)m * lda + rcol)
                                           : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < MT_PER_THREAD; ++i) {
+      if (tid + i * NT >= MT_TOTAL) break;
       int rg, q;
       mt_coords(i, rg, q);
       const int kcol = o0 + q * 8;
@@ -315,11 +345,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
     const bool lora = kt >= nk_main;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NTHREADS, row = q >> 3, c = q & 7;
+      int q = tid + i * NT, row = q >> 3, c = q & 7;
       *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < MT_PER_THREAD; ++i) {
+      if (tid + i * NT >= MT_TOTAL) break;
       int rg, q;
       mt_coords(i, rg, q);
       // vals[rr][c]: weight (row rg*4+rr, column q*8+c) as bf16 bits
@@ -356,12 +387,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
+  if (kbeg < nk) load_tile(kbeg);
   __syncthreads();
-  store_tile(0, 0);
+  if (kbeg < nk) store_tile(0, kbeg);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  for (int kt = kbeg; kt < nk; ++kt) {
+    const int cur = (kt - kbeg) & 1;
     if (kt + 1 < nk) load_tile(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -380,6 +411,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
     __syncthreads();
   }
 
+  if (p.splits > 1) {
+    float* part = p.part + (int64_t)split * p.M * K;
+#pragma unroll
+    for (int j = 0; j < TO; ++j) {
+      const int col = o0 + wo * WO + j * 16 + (lane & 15);
+      if (col >= K) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+          if (row < p.M) part[(int64_t)row * K + col] = acc[i][j][v];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TO; ++j) {
     const int col = o0 + wo * WO + j * 16 + (lane & 15);
@@ -405,20 +452,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_bwd_kernel(BwdParams p) {
 }
 
 // =========================================================== LoRA down: U = s X A^T
-// One workgroup per 16 rows; the 4 waves split K and their partial 16 x rr
-// tiles are summed in LDS in wave order (fixed, deterministic).
+// Grid (M / 16 row blocks, K / 512 chunks): each workgroup's 4 waves take 128
+// of its chunk's columns each and sum their 16 x rr tiles in wave order; the
+// chunk partials are then summed in chunk order by lora_finish_kernel.
+constexpr int KCHUNK = 512;
 __global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M, int K,
-                                                             const uint16_t* __restrict__ A, int rr, float s,
-                                                             uint16_t* __restrict__ U, int64_t ldu) {
-  __shared__ float part[4][16][64];
+                                                             const uint16_t* __restrict__ A, int rr,
+                                                             float* __restrict__ part) {
+  __shared__ float red[4][16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * 16, chunk = blockIdx.y;
   const int nct = (rr + 15) / 16;
-  const int kq = ((K / 32 + 3) / 4) * 32;  // per-wave K range, multiple of 32
-  const int kb = wave * kq, ke = min(K, kb + kq);
+  const int kb = chunk * KCHUNK + wave * (KCHUNK / 4), ke = min(K, kb + KCHUNK / 4);
   f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
   const int row = m0 + (lane & 15);
   const int g = lane >> 4;
+#pragma unroll 4
   for (int k = kb; k < ke; k += 32) {
     const int kk = k + 8 * g;
     uint4 av = (row < M && kk < K) ? *reinterpret_cast<const uint4*>(X + (int64_t)row * ldx + kk) : make_uint4(0, 0, 0, 0);
@@ -434,15 +483,26 @@ __global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __r
   for (int ct = 0; ct < 4; ++ct) {
     if (ct >= nct) break;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
+    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
   }
   __syncthreads();
+  float* out = part + (int64_t)chunk * M * rr;
   for (int e = tid; e < 16 * rr; e += NTHREADS) {
     const int r = e / rr, c = e % rr;
     if (m0 + r >= M) continue;
-    float v = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
-    U[(int64_t)(m0 + r) * ldu + c] = f32_to_bf16_bits(s * v);
+    out[(int64_t)(m0 + r) * rr + c] = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
   }
+}
+
+// dst[m, col0 + c] = bf16(s * sum over chunks of part[chunk, m, c]) for c < w
+__global__ void lora_finish_kernel(const float* __restrict__ part, int nchunks, int M, int w, float s,
+                                   uint16_t* __restrict__ dst, int64_t ld, int col0) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)M * w) return;
+  const int64_t m = e / w, c = e % w;
+  float v = 0.f;
+  for (int k = 0; k < nchunks; ++k) v += part[(int64_t)k * M * w + e];
+  dst[m * ld + col0 + c] = f32_to_bf16_bits(s * v);
 }
 
 // B [N, r] -> Bt [r, N] (bf16), so the G kernel reads 8 reduction values contiguously.
@@ -454,113 +514,187 @@ __global__ void transpose_rows_kernel(const uint16_t* __restrict__ B, int N, int
 }
 
 // =========================================================== LoRA G = s dY_seg B_seg
-// One workgroup per 16 rows; for each segment the waves split its N range.
+// Grid (M / 16 row blocks, chunks of 512 reduction columns within one segment).
 __global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __restrict__ dY, int64_t ldy, int M, int N,
-                                                          const uint16_t* __restrict__ Bt, int r, int nseg,
-                                                          SegEnds segs, float s, uint16_t* __restrict__ G,
-                                                          int64_t ldg) {
-  __shared__ float part[4][16][64];
+                                                          const uint16_t* __restrict__ Bt, int r, GChunks ch,
+                                                          float* __restrict__ part) {
+  __shared__ float red[4][16][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * 16, chunk = blockIdx.y;
   const int row = m0 + (lane & 15), g = lane >> 4;
   const int nct = (r + 15) / 16;
-  for (int sgi = 0; sgi < nseg; ++sgi) {
-    const int nb = sgi == 0 ? 0 : segs.end[sgi - 1], ne = segs.end[sgi];
-    const int len = ne - nb;
-    const int q = (((len + 31) / 32 + 3) / 4) * 32;  // per-wave share, whole 32-chunks
-    const int kb = nb + wave * q, ke = min(ne, kb + q);
-    f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-    for (int k = kb; k < ke; k += 32) {
-      const int kk = k + 8 * g;
-      uint4 av = (row < M && kk < ne) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct >= nct) break;
-        const int c = ct * 16 + (lane & 15);
-        uint4 bv = (c < r && kk < ne) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
-        acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
-      }
-    }
-    __syncthreads();
+  const int cb = ch.begin[chunk], ce = ch.end[chunk];
+  const int kb = cb + wave * (KCHUNK / 4), ke = min(ce, kb + KCHUNK / 4);
+  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll 4
+  for (int k = kb; k < ke; k += 32) {
+    const int kk = k + 8 * g;
+    uint4 av = (row < M && kk < ce) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
+      const int c = ct * 16 + (lane & 15);
+      uint4 bv = (c < r && kk < ce) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
+      acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
+    }
+  }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
-    }
-    __syncthreads();
-    for (int e = tid; e < 16 * r; e += NTHREADS) {
-      const int rrow = e / r, c = e % r;
-      if (m0 + rrow >= M) continue;
-      float v = ((part[0][rrow][c] + part[1][rrow][c]) + part[2][rrow][c]) + part[3][rrow][c];
-      G[(int64_t)(m0 + rrow) * ldg + sgi * r + c] = f32_to_bf16_bits(s * v);
-    }
+  for (int ct = 0; ct < 4; ++ct) {
+    if (ct >= nct) break;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
+  }
+  __syncthreads();
+  float* out = part + (int64_t)chunk * M * r;
+  for (int e = tid; e < 16 * r; e += NTHREADS) {
+    const int rr = e / r, c = e % r;
+    if (m0 + rr >= M) continue;
+    out[(int64_t)(m0 + rr) * r + c] = ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c];
   }
 }
 
 // =========================================================== LoRA weight grads
-// C = S^T L over the token dimension M: S [M, ns] (ns <= 64), L [M, nl].
+// C = S^T L over the token dimension M: S [M, ns], L [M, nl] (bf16).
 // SMALL_ROWS: C[ns, nl] row-major (dA = G^T X);  else C[nl, ns] (dB = dY^T U).
-// Grid: (nl / 64 column tiles) x splits; each split sums a fixed token range;
-// with splits > 1 the partials land in ws and reduce_splits adds them in order.
+// Grid (nl / 256 column tiles, token splits, ns / 16 slices).  A thread owns 4
+// adjacent columns x 16 small indices (64 accumulators) and walks its wave's
+// tokens reading L straight from HBM (coalesced) and S as wave-uniform loads;
+// the 4 waves' sums meet in LDS in wave order.  With splits > 1 the partials
+// go to ws and reduce_splits adds them in split order.
 template <bool SMALL_ROWS>
 __global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __restrict__ S, int64_t lds_, int ns,
                                                            const uint16_t* __restrict__ Lm, int64_t ldl, int nl, int M,
                                                            int rows_per_split, float* __restrict__ out,
                                                            int64_t ldo, int accumulate, int direct) {
-  __shared__ float sL[32][65];
-  __shared__ float sS[32][65];
-  const int tid = threadIdx.x;
-  const int l0 = blockIdx.x * 64;
+  __shared__ float red[3][64][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = blockIdx.x * 256 + lane * 4;
   const int split = blockIdx.y;
+  const int j0 = blockIdx.z * 16;
+  const int nj = min(16, ns - j0);
   const int mb = split * rows_per_split, me = min(M, mb + rows_per_split);
-  const int li = tid & 63, sg = tid >> 6;  // this thread: column l0+li, small indices sg, sg+4, ...
-  float acc[16];
+  float acc[16][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int m = mb; m < me; m += 32) {
-    // stage 32 rows x 64 cols of L and 32 x ns of S as float
-    for (int e = tid; e < 32 * 8; e += NTHREADS) {
-      const int rr = e >> 3, c8 = (e & 7) * 8;
-      const int mm = m + rr, col = l0 + c8;
-      uint4 v = (mm < me && col < nl) ? *reinterpret_cast<const uint4*>(Lm + (int64_t)mm * ldl + col) : make_uint4(0, 0, 0, 0);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sL[rr][c8 + 2 * j] = bf_lo(w[j]);
-        sL[rr][c8 + 2 * j + 1] = bf_hi(w[j]);
-      }
-    }
-    for (int e = tid; e < 32 * ns; e += NTHREADS) {
-      const int rr = e / ns, c = e % ns;
-      const int mm = m + rr;
-      sS[rr][c] = (mm < me) ? bf16_bits_to_f32(S[(int64_t)mm * lds_ + c]) : 0.f;
-    }
-    __syncthreads();
+    for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
+  const bool colok = col < nl;
+  const bool wide = nj > 8;
 #pragma unroll 4
-    for (int rr = 0; rr < 32; ++rr) {
-      const float lv = sL[rr][li];
+  for (int m = mb + wave; m < me; m += 4) {
+    const uint2 lv = colok ? *reinterpret_cast<const uint2*>(Lm + (int64_t)m * ldl + col) : make_uint2(0, 0);
+    const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
+    // 8 or 16 small-side values of this token: wave-uniform 16-byte loads
+    const uint4* srow = reinterpret_cast<const uint4*>(S + (int64_t)m * lds_ + j0);
+    const uint4 s0 = srow[0];
+    const uint4 s1 = wide ? srow[1] : make_uint4(0, 0, 0, 0);
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = sg + 4 * i;
-        if (c < ns) acc[i] = fmaf(sS[rr][c], lv, acc[i]);
+    for (int j = 0; j < 16; ++j) {
+      const float sv = (j & 1) ? bf_hi(sw[j >> 1]) : bf_lo(sw[j >> 1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv, l4[c], acc[j][c]);
+    }
+  }
+  // waves 1..3 park their sums; wave 0 adds them in order
+  for (int j = 0; j < 16; ++j) {
+    if (wave > 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red[wave - 1][lane][j * 4 + c] = acc[j][c];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || !colok) return;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= nj) break;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
+      const int a = j0 + j, b = col + c;
+      if (b >= nl) continue;
+      if (direct) {
+        const int64_t o = SMALL_ROWS ? (int64_t)a * ldo + b : (int64_t)b * ldo + a;
+        out[o] = accumulate ? out[o] + v : v;
+      } else {
+        out[(int64_t)split * ((int64_t)ns * nl) + (SMALL_ROWS ? (int64_t)a * nl + b : (int64_t)b * ns + a)] = v;
       }
     }
-    __syncthreads();
   }
-  const int col = l0 + li;
-  if (col >= nl) return;
+}
+
+// All adapter-gradient reductions of one linear group in one launch: one
+// dA task (the group's stacked G^T X) and one dB task per segment (dY_seg^T
+// U_seg).  Each workgroup owns 256 output columns x 16 small indices over all
+// tokens (the 4 waves interleave tokens and meet in LDS in wave order), so no
+// partials and no second pass.
+__global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
+  __shared__ float red[3][64][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int ti = 0;
+  while (ti + 1 < bt.ntasks && (int)blockIdx.x >= bt.t[ti + 1].tile0) ++ti;
+  const TnTask& tk = bt.t[ti];
+  const int local = blockIdx.x - tk.tile0;
+  const int ncol = (tk.nl + 255) / 256;
+  const int col = (local % ncol) * 256 + lane * 4;
+  const int j0 = (local / ncol) * 16;
+  const int nj = min(16, tk.ns - j0);
+  float acc[16][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = sg + 4 * i;
-    if (c >= ns) continue;
-    const int64_t o = SMALL_ROWS ? (int64_t)c * ldo + col : (int64_t)col * ldo + c;
-    if (direct) {
-      out[o] = accumulate ? out[o] + acc[i] : acc[i];
-    } else {
-      out[(int64_t)split * ((int64_t)ns * nl) + (SMALL_ROWS ? (int64_t)c * nl + col : (int64_t)col * ns + c)] = acc[i];
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
+  const bool colok = col < tk.nl;
+  const bool wide = nj > 8;
+#pragma unroll 4
+  for (int m = wave; m < bt.M; m += 4) {
+    const uint2 lv = colok ? *reinterpret_cast<const uint2*>(tk.L + (int64_t)m * tk.ldl + col) : make_uint2(0, 0);
+    const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
+    const uint4* srow = reinterpret_cast<const uint4*>(tk.S + (int64_t)m * tk.lds + j0);
+    const uint4 s0 = srow[0];
+    const uint4 s1 = wide ? srow[1] : make_uint4(0, 0, 0, 0);
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sv = (j & 1) ? bf_hi(sw[j >> 1]) : bf_lo(sw[j >> 1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv, l4[c], acc[j][c]);
     }
   }
+  for (int j = 0; j < 16; ++j) {
+    if (wave > 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red[wave - 1][lane][j * 4 + c] = acc[j][c];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || !colok) return;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= nj) break;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
+      const int a = j0 + j, b = col + c;
+      if (b >= tk.nl) continue;
+      const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
+      tk.out[o] = bt.accumulate ? tk.out[o] + v : v;
+    }
+  }
+}
+
+// G finish for several segments at once: segment s sums chunks [c0, c1) of part.
+__global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinish sf, int M, int r, float s,
+                                        uint16_t* __restrict__ dst, int64_t ld) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)M * r;
+  if (e >= per * sf.n) return;
+  const int sg = e / per;
+  const int64_t i = e % per;
+  const int64_t m = i / r, c = i % r;
+  float v = 0.f;
+  for (int k = sf.c0[sg]; k < sf.c1[sg]; ++k) v += part[(int64_t)k * per + i];
+  dst[m * ld + sf.col[sg] + c] = f32_to_bf16_bits(s * v);
 }
 
 // out[i, j] (+)= sum over splits, in split order.  Partials are packed [splits][rows][cols].
@@ -640,104 +774,281 @@ __global__ void f32_tn_kernel(const float* P, int na, const float* Q, int nb, in
   C[e] = accumulate ? C[e] + acc : acc;
 }
 
-template <int BM, int BN, int WK, int EPI>
+// out[m, n] = epilogue(sum over splits of part[s, m, n], in split order) (+ bias) (+ resid)
+template <int EPI>
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                     const uint16_t* __restrict__ bias, const float* __restrict__ resid,
+                                     void* __restrict__ out, int64_t ldc) {
+  const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int64_t total = (int64_t)M * N;
+  if (e >= total) return;
+  float4 v = *reinterpret_cast<const float4*>(part + e);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 w = *reinterpret_cast<const float4*>(part + (int64_t)sp * total + e);
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  const int64_t row = e / N, col = e % N;
+  float r[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (bias) r[i] += bf16_bits_to_f32(bias[col + i]);
+    const int64_t o = row * ldc + col + i;
+    if (EPI == EPI_BF16)
+      static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(r[i]);
+    else if (EPI == EPI_F32)
+      static_cast<float*>(out)[o] = r[i];
+    else
+      static_cast<float*>(out)[o] = resid[o] + r[i];
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  gemm_fwd_kernel<BM, BN, WK, EPI><<<tiles, NTHREADS, 0, s>>>(p);
+  gemm_fwd_kernel<BM, BN, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
 }
 
-template <int BM, int BO, int WK, int EPI>
+template <int BM, int BO, int WGM, int WGN, int WK, int EPI>
 void launch_bwd(const BwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.K + BO - 1) / BO);
-  gemm_bwd_kernel<BM, BO, WK, EPI><<<tiles, NTHREADS, 0, s>>>(p);
+  gemm_bwd_kernel<BM, BO, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
 }
 
-template <int BM, int BN, int WK>
+void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* bias, const float* resid, void* out,
+                   int64_t ldc, int epi, hipStream_t s) {
+  const int64_t n4 = ((int64_t)M * N) / 4;
+  const unsigned grid = (unsigned)((n4 + 255) / 256);
+  if (epi == EPI_BF16)
+    splitk_reduce_kernel<EPI_BF16><<<grid, 256, 0, s>>>(part, splits, M, N, bias, resid, out, ldc);
+  else if (epi == EPI_F32)
+    splitk_reduce_kernel<EPI_F32><<<grid, 256, 0, s>>>(part, splits, M, N, bias, resid, out, ldc);
+  else
+    splitk_reduce_kernel<EPI_F32_RESID><<<grid, 256, 0, s>>>(part, splits, M, N, bias, resid, out, ldc);
+}
+
+int choose_splits(int tiles, int ksteps) {
+  if (tiles >= 256) return 1;
+  int sp = 512 / std::max(1, tiles);
+  sp = std::min(sp, std::max(1, ksteps / 8));   // keep >= 8 reduction steps per split
+  return std::max(1, std::min(8, sp));
+}
+
+template <int BM, int BN, int WGM, int WGN, int WK>
 void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_fwd<BM, BN, WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_fwd<BM, BN, WK, EPI_F32>(p, s);
-  else launch_fwd<BM, BN, WK, EPI_F32_RESID>(p, s);
+  if (epi == EPI_BF16) launch_fwd<BM, BN, WGM, WGN, WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_fwd<BM, BN, WGM, WGN, WK, EPI_F32>(p, s);
+  else launch_fwd<BM, BN, WGM, WGN, WK, EPI_F32_RESID>(p, s);
 }
 
-template <int BM, int BO, int WK>
+template <int BM, int BO, int WGM, int WGN, int WK>
 void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_bwd<BM, BO, WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_bwd<BM, BO, WK, EPI_F32>(p, s);
-  else launch_bwd<BM, BO, WK, EPI_F32_RESID>(p, s);
+  if (epi == EPI_BF16) launch_bwd<BM, BO, WGM, WGN, WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_bwd<BM, BO, WGM, WGN, WK, EPI_F32>(p, s);
+  else launch_bwd<BM, BO, WGM, WGN, WK, EPI_F32_RESID>(p, s);
 }
+
+// Tile shape of each direction (compile-time; tuned on gfx950).  Kernel
+// choice is a pure function of the shape, never of where the weights live.
+#ifndef LSQ_FWD_TILE
+#define LSQ_FWD_TILE 128, 128, 2, 2
+#endif
+#ifndef LSQ_BWD_TILE
+#define LSQ_BWD_TILE 128, 128, 2, 2
+#endif
+constexpr int kFwdTile[4] = {LSQ_FWD_TILE};
+constexpr int kBwdTile[4] = {LSQ_BWD_TILE};
 
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
-int gemm_fwd(const FwdParams& p, int epi, hipStream_t s) {
+int gemm_fwd_splits(int M, int N, int K) {
+  return choose_splits(((M + kFwdTile[0] - 1) / kFwdTile[0]) * ((N + kFwdTile[1] - 1) / kFwdTile[1]), K / 64);
+}
+int gemm_bwd_splits(int M, int N, int K, int rr) {
+  return choose_splits(((M + kBwdTile[0] - 1) / kBwdTile[0]) * ((K + kBwdTile[1] - 1) / kBwdTile[1]),
+                       (N + 63) / 64 + (rr + 63) / 64);
+}
+size_t gemm_fwd_ws_bytes(int M, int N, int K) {
+  const int sp = gemm_fwd_splits(M, N, K);
+  return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+}
+size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
+  const int sp = gemm_bwd_splits(M, N, K, rr);
+  return sp > 1 ? (size_t)sp * M * K * sizeof(float) : 0;
+}
+
+int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
+  FwdParams p = p_in;
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
   LSQ_CHECK(p.r == 0 || (p.r % 8 == 0 && p.ldu % 8 == 0), LSQ_ERR_SHAPE, "gemm: LoRA rank must be a multiple of 8");
   if (p.M == 0 || p.N == 0) return LSQ_OK;
+  p.splits = gemm_fwd_splits(p.M, p.N, p.K);
+  if (p.splits > 1) {
+    LSQ_CHECK(ws && ws_bytes >= gemm_fwd_ws_bytes(p.M, p.N, p.K) && p.N % 4 == 0, LSQ_ERR_WORKSPACE,
+              "gemm_fwd: split-K needs %zu bytes of workspace", gemm_fwd_ws_bytes(p.M, p.N, p.K));
+    p.part = static_cast<float*>(ws);
+  }
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.N * p.r;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
   int tok = prof_begin(s);
   // 128 x 128 tiles, 4 waves of 64 x 64.
-  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<128, 128, LSQ_W_NF4>(p, epi, s);
-  else dispatch_fwd_epi<128, 128, LSQ_W_BF16>(p, epi, s);
+  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_NF4>(p, epi, s);
+  else dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_BF16>(p, epi, s);
+  if (p.splits > 1) launch_reduce(p.part, p.splits, p.M, p.N, p.bias, p.resid, p.out, p.ldc, epi, s);
   prof_end(tok, s, PROF_GEMM_FWD, flops, bytes);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
-int gemm_bwd(const BwdParams& p, int epi, hipStream_t s) {
+int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
+  BwdParams p = p_in;
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
   LSQ_CHECK(p.N % 8 == 0 && p.rr % 8 == 0 && p.ldy % 8 == 0 && p.ldg % 8 == 0, LSQ_ERR_SHAPE,
             "gemm_bwd: N=%d and rank %d must be multiples of 8", p.N, p.rr);
   if (p.M == 0 || p.K == 0) return LSQ_OK;
+  p.splits = gemm_bwd_splits(p.M, p.N, p.K, p.rr);
+  if (p.splits > 1) {
+    LSQ_CHECK(ws && ws_bytes >= gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr), LSQ_ERR_WORKSPACE,
+              "gemm_bwd: split-K needs %zu bytes of workspace", gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr));
+    p.part = static_cast<float*>(ws);
+  }
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
   int tok = prof_begin(s);
-  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<128, 128, LSQ_W_NF4>(p, epi, s);
-  else dispatch_bwd_epi<128, 128, LSQ_W_BF16>(p, epi, s);
+  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_NF4>(p, epi, s);
+  else dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_BF16>(p, epi, s);
+  if (p.splits > 1) launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);
   prof_end(tok, s, PROF_GEMM_BWD, flops, bytes);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
+size_t lora_down_ws_bytes(int M, int K, int rr) {
+  return (size_t)((K + KCHUNK - 1) / KCHUNK) * M * rr * sizeof(float);
+}
+
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, hipStream_t st) {
+              int64_t ldu, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(rr >= 1 && rr <= 64 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr, K);
   if (M == 0) return LSQ_OK;
+  LSQ_CHECK(ws && ws_bytes >= lora_down_ws_bytes(M, K, rr), LSQ_ERR_WORKSPACE, "lora_down: workspace too small");
+  const int nch = (K + KCHUNK - 1) / KCHUNK;
   int tok = prof_begin(st);
-  lora_down_kernel<<<(M + 15) / 16, NTHREADS, 0, st>>>(X, ldx, M, K, A, rr, s, U, ldu);
+  lora_down_kernel<<<dim3((M + 15) / 16, nch), NTHREADS, 0, st>>>(X, ldx, M, K, A, rr, ws);
+  lora_finish_kernel<<<(M * rr + 255) / 256, 256, 0, st>>>(ws, nch, M, rr, s, U, ldu, 0);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)K * rr, 2.0 * M * (double)K + 2.0 * rr * K + 2.0 * M * rr);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
+static GChunks g_chunks(int N, int nseg, const SegEnds& segs, int seg_of[128]) {
+  GChunks ch{};
+  ch.n = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int nb = sg == 0 ? 0 : segs.end[sg - 1], ne = segs.end[sg];
+    for (int b = nb; b < ne; b += KCHUNK) {
+      ch.begin[ch.n] = b;
+      ch.end[ch.n] = std::min(ne, b + KCHUNK);
+      seg_of[ch.n] = sg;
+      ++ch.n;
+    }
+  }
+  return ch;
+}
+
+size_t lora_g_ws_bytes(int M, int N, int r) {
+  // chunks <= N / KCHUNK + one partial chunk per segment (at most 4)
+  return (size_t)((N + KCHUNK - 1) / KCHUNK + 4) * M * r * sizeof(float) + (size_t)N * r * 2 + 256;
+}
+
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, uint16_t* bt_ws, hipStream_t st) {
+           float s, uint16_t* G, int64_t ldg, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4, LSQ_ERR_SHAPE, "lora_g: bad rank/segments");
   if (M == 0) return LSQ_OK;
+  LSQ_CHECK(ws && ws_bytes >= lora_g_ws_bytes(M, N, r), LSQ_ERR_WORKSPACE, "lora_g: workspace too small");
+  int seg_of[128];
+  LSQ_CHECK((N + KCHUNK - 1) / KCHUNK + nseg <= 128, LSQ_ERR_SHAPE, "lora_g: too many reduction chunks (N=%d)", N);
+  GChunks ch = g_chunks(N, nseg, segs, seg_of);
+  uint16_t* bt = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)N * r * 2 + 255) & ~size_t(255)));
   int tok = prof_begin(st);
   const int64_t nel = (int64_t)N * r;
-  transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, st>>>(B, N, r, bt_ws);
-  lora_g_kernel<<<(M + 15) / 16, NTHREADS, 0, st>>>(dY, ldy, M, N, bt_ws, r, nseg, segs, s, G, ldg);
+  transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, st>>>(B, N, r, bt);
+  lora_g_kernel<<<dim3((M + 15) / 16, ch.n), NTHREADS, 0, st>>>(dY, ldy, M, N, bt, r, ch, part);
+  // each segment's chunks are consecutive: sum them in order into its G columns
+  SegFinish sf{};
+  for (int c0 = 0; c0 < ch.n;) {
+    int c1 = c0;
+    while (c1 < ch.n && seg_of[c1] == seg_of[c0]) ++c1;
+    sf.c0[sf.n] = c0;
+    sf.c1[sf.n] = c1;
+    sf.col[sf.n] = seg_of[c0] * r;
+    ++sf.n;
+    c0 = c1;
+  }
+  const int64_t nfin = (int64_t)M * r * sf.n;
+  lora_finish_segs_kernel<<<(unsigned)((nfin + 255) / 256), 256, 0, st>>>(part, sf, M, r, s, G, ldg);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)N * r, 2.0 * M * (double)N + 4.0 * N * r + 2.0 * M * r * nseg);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
+int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream_t st) {
+  LSQ_CHECK(ntasks >= 1 && ntasks <= 8, LSQ_ERR_INVALID, "lora_grads: 1..8 tasks");
+  TnBatch bt{};
+  int tiles = 0;
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < ntasks; ++i) {
+    const TnTask& t = tasks[i];
+    LSQ_CHECK(t.ns >= 8 && t.ns <= 64 && t.ns % 8 == 0 && t.nl % 4 == 0 && t.ldl % 4 == 0 && t.lds % 8 == 0 &&
+                  (reinterpret_cast<uintptr_t>(t.S) & 15) == 0 && (reinterpret_cast<uintptr_t>(t.L) & 7) == 0,
+              LSQ_ERR_SHAPE, "lora_grads: task %d shape/alignment", i);
+    bt.t[i] = t;
+    bt.t[i].tile0 = tiles;
+    tiles += ((t.nl + 255) / 256) * ((t.ns + 15) / 16);
+    flops += 2.0 * M * (double)t.ns * t.nl;
+    bytes += 2.0 * M * (double)(t.ns + t.nl) + 4.0 * t.ns * t.nl;
+  }
+  bt.ntasks = ntasks;
+  bt.M = M;
+  bt.accumulate = accumulate;
+  if (M == 0 && !accumulate) {
+    for (int i = 0; i < ntasks; ++i) {
+      const TnTask& t = tasks[i];
+      for (int r = 0; r < (t.small_rows ? t.ns : t.nl); ++r)
+        LSQ_HIP(hipMemsetAsync(t.out + (int64_t)r * t.ldo, 0, sizeof(float) * (t.small_rows ? t.nl : t.ns), st));
+    }
+    return LSQ_OK;
+  }
+  int tok = prof_begin(st);
+  lora_grads_kernel<<<tiles, NTHREADS, 0, st>>>(bt);
+  prof_end(tok, st, PROF_LORA, flops, bytes);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+static int tn_splits(int M, int nl, int ns) {
+  const int tiles = ((nl + 255) / 256) * ((ns + 15) / 16);
+  return std::max(1, std::min(std::max(1, M / 64), (512 + tiles - 1) / tiles));
+}
+
 size_t lora_tn_ws_bytes(int M, int ns, int nl) {
-  int tiles = (nl + 63) / 64;
-  int splits = std::max(1, std::min((M + 255) / 256, (512 + tiles - 1) / tiles));
-  return splits > 1 ? (size_t)splits * ns * nl * sizeof(float) : 0;
+  const int sp = tn_splits(M, nl, ns);
+  return sp > 1 ? (size_t)sp * ns * nl * sizeof(float) : 0;
 }
 
 int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
             float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(ns >= 1 && ns <= 64, LSQ_ERR_SHAPE, "lora_tn: small dim %d unsupported", ns);
-  LSQ_CHECK(nl % 8 == 0 && ldl % 8 == 0, LSQ_ERR_SHAPE, "lora_tn: large dim must be a multiple of 8");
-  const int tiles = (nl + 63) / 64;
-  const int splits = std::max(1, std::min((M + 255) / 256, (512 + tiles - 1) / tiles));
-  const int rows_per_split = ((M + splits - 1) / splits + 31) / 32 * 32;
+  LSQ_CHECK(ns >= 8 && ns <= 64 && ns % 8 == 0, LSQ_ERR_SHAPE, "lora_tn: small dim %d unsupported", ns);
+  LSQ_CHECK(nl % 4 == 0 && ldl % 4 == 0 && lds_ % 8 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0, LSQ_ERR_SHAPE,
+            "lora_tn: large dim must be a multiple of 4, small rows 16-byte aligned");
+  const int splits = tn_splits(M, nl, ns);
+  const int rows_per_split = (M + splits - 1) / splits;
   const bool direct = splits == 1;
   LSQ_CHECK(direct || (ws && ws_bytes >= lora_tn_ws_bytes(M, ns, nl)), LSQ_ERR_WORKSPACE, "lora_tn: workspace too small");
   if (M == 0) {
@@ -748,7 +1059,7 @@ int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t 
     return LSQ_OK;
   }
   int tok = prof_begin(st);
-  dim3 grid(tiles, splits);
+  dim3 grid((nl + 255) / 256, splits, (ns + 15) / 16);
   if (small_rows)
     lora_tn_kernel<true><<<grid, NTHREADS, 0, st>>>(S, lds_, ns, L, ldl, nl, M, rows_per_split, direct ? out : ws, ldo,
                                                     accumulate, direct ? 1 : 0);
@@ -795,8 +1106,9 @@ extern "C" {
 size_t nf4_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
   const size_t el = dtype == LSQ_F32 ? 4 : 2;
   size_t b = align256(M * r * el) * 2             // U (recomputed or forward scratch) and G
-             + align256(N * r * 2);               // B transposed
+             + align256(std::max(lora_down_ws_bytes((int)M, (int)K, r), lora_g_ws_bytes((int)M, (int)N, r)));
   b += align256(lora_tn_ws_bytes((int)M, r, (int)K)) + align256(lora_tn_ws_bytes((int)M, r, (int)N));
+  b += align256(std::max(gemm_fwd_ws_bytes((int)M, (int)N, (int)K), gemm_bwd_ws_bytes((int)M, (int)N, (int)K, r)));
   return b + 256;
 }
 
@@ -812,7 +1124,7 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
                 (!bias || aligned16(bias)) && (!ws || aligned16(ws)),
             LSQ_ERR_ALIGN, "linear_fwd: unaligned pointer");
   const size_t need = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype);
-  LSQ_CHECK(U_out || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
+  LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
   hipStream_t s = as_stream(stream);
   const WeightRef w = ref_of(W);
   const int Mi = (int)M;
@@ -830,9 +1142,16 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
     return LSQ_OK;
   }
   uint16_t* U = U_out ? static_cast<uint16_t*>(U_out) : static_cast<uint16_t*>(ws);
+  LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
+  const size_t lw_off = align256((size_t)Mi * r * 2) * 2;
+  const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
   if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale, U,
-                        r, s))
+                        r, reinterpret_cast<float*>(static_cast<char*>(ws) + lw_off), lw_bytes, s))
     return e;
+  const size_t part_off = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype) - 256 -
+                          align256(std::max(gemm_fwd_ws_bytes(Mi, w.N, w.K), gemm_bwd_ws_bytes(Mi, w.N, w.K, r)));
+  void* part = ws ? static_cast<char*>(ws) + part_off : nullptr;
+  const size_t part_bytes = ws && ws_bytes > part_off ? ws_bytes - part_off : 0;
   FwdParams p{};
   p.X = static_cast<const uint16_t*>(X);
   p.ldx = w.K;
@@ -852,7 +1171,7 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
   p.bias = static_cast<const uint16_t*>(bias);
   p.out = Y;
   p.ldc = w.N;
-  return gemm_fwd(p, EPI_BF16, s);
+  return gemm_fwd(p, EPI_BF16, s, part, part_bytes);
 }
 
 int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, int64_t M, const void* A,
@@ -876,13 +1195,17 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   wsp += align256((size_t)Mi * r * el);
   void* Gw = wsp;
   wsp += align256((size_t)Mi * r * el);
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(wsp);
-  wsp += align256((size_t)w.N * r * 2);
+  float* lw = reinterpret_cast<float*>(wsp);
+  const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
+  wsp += lw_bytes;
   float* tn1 = reinterpret_cast<float*>(wsp);
   const size_t tn1_b = align256(lora_tn_ws_bytes(Mi, r, w.K));
   wsp += tn1_b;
   float* tn2 = reinterpret_cast<float*>(wsp);
   const size_t tn2_b = align256(lora_tn_ws_bytes(Mi, r, w.N));
+  wsp += tn2_b;
+  void* part = wsp;
+  const size_t part_bytes = align256(std::max(gemm_fwd_ws_bytes(Mi, w.N, w.K), gemm_bwd_ws_bytes(Mi, w.N, w.K, r)));
 
   if (dtype == LSQ_F32) {
     const float* U = static_cast<const float*>(U_in);
@@ -910,7 +1233,7 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   const uint16_t* U = static_cast<const uint16_t*>(U_in);
   if (!U) {
     if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale,
-                          static_cast<uint16_t*>(Uw), r, s))
+                          static_cast<uint16_t*>(Uw), r, lw, lw_bytes, s))
       return e;
     U = static_cast<const uint16_t*>(Uw);
   }
@@ -918,7 +1241,7 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   SegEnds segs{};
   segs.end[0] = w.N;
   if (int e = lora_g(static_cast<const uint16_t*>(dY), w.N, Mi, w.N, static_cast<const uint16_t*>(B), r, 1, segs,
-                     scale, G, r, Bt, s))
+                     scale, G, r, lw, lw_bytes, s))
     return e;
   BwdParams p{};
   p.dY = static_cast<const uint16_t*>(dY);
@@ -935,7 +1258,7 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   p.rr = r;
   p.out = dX;
   p.ldc = w.K;
-  if (int e = gemm_bwd(p, EPI_BF16, s)) return e;
+  if (int e = gemm_bwd(p, EPI_BF16, s, part, part_bytes)) return e;
   if (int e = lora_tn(G, r, r, static_cast<const uint16_t*>(X), w.K, w.K, Mi, true, dA, w.K, accumulate, tn1, tn1_b, s))
     return e;
   return lora_tn(U, r, r, static_cast<const uint16_t*>(dY), w.N, w.N, Mi, false, dB, r, accumulate, tn2, tn2_b, s);

@@ -129,16 +129,41 @@ struct LayerWs {
   uint16_t* dattn;    // [T, Nq]
   float* D;           // [T, nh]
   uint16_t* dqkv;     // [T, Nqkv]
-  uint16_t* bt;       // [max N, r] transposed adapter B
+  float* dk_part;     // [T, nh, hd] per-query-head dK, dV partials
+  float* dv_part;
+  float* lws;         // scratch of the LoRA down / G kernels
+  size_t lws_bytes;
   float* tn;          // token-reduction partials
   size_t tn_bytes;
+  void* gemm;         // split-K partials of the layer's GEMMs
+  size_t gemm_bytes;
   size_t total;
 };
+
+static size_t gemm_need(const Dims& d, int T) {
+  size_t m = 0;
+  for (int g = 0; g < 4; ++g) {
+    const int rr = (g == 0 ? 3 : g == 2 ? 2 : 1) * d.r;
+    m = std::max(m, gemm_fwd_ws_bytes(T, d.gN[g], d.gK[g]));
+    m = std::max(m, gemm_bwd_ws_bytes(T, d.gN[g], d.gK[g], rr));
+  }
+  return m;
+}
 
 static size_t tn_need(const Dims& d, int T) {
   size_t m = 0;
   const int nls[] = {d.H, d.I, d.Nq, d.Nkv, d.Nqkv, 2 * d.I};
   for (int nl : nls) m = std::max(m, lora_tn_ws_bytes(T, d.r, nl));
+  return m;
+}
+
+static size_t lws_need(const Dims& d, int T) {
+  size_t m = 0;
+  for (int g = 0; g < 4; ++g) {
+    const int rr = (g == 0 ? 3 : g == 2 ? 2 : 1) * d.r;
+    m = std::max(m, lora_down_ws_bytes(T, d.gK[g], rr));
+    m = std::max(m, lora_g_ws_bytes(T, d.gN[g], d.r));
+  }
   return m;
 }
 
@@ -166,6 +191,10 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd)
   w.gu = static_cast<uint16_t*>(take(2 * T * 2 * d.I));
   w.m = static_cast<uint16_t*>(take(2 * T * d.I));
   w.U_d = static_cast<uint16_t*>(take(2 * T * d.r));
+  w.gemm_bytes = gemm_need(d, (int)T);
+  w.gemm = take(w.gemm_bytes);
+  w.lws_bytes = lws_need(d, (int)T);
+  w.lws = static_cast<float*>(take(w.lws_bytes));
   if (bwd) {
     w.attn_f32 = static_cast<float*>(take(4 * T * d.Nq));
     w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
@@ -177,7 +206,8 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd)
     w.dattn = static_cast<uint16_t*>(take(2 * T * d.Nq));
     w.D = static_cast<float*>(take(4 * T * d.nh));
     w.dqkv = static_cast<uint16_t*>(take(2 * T * d.Nqkv));
-    w.bt = static_cast<uint16_t*>(take(2ull * std::max(d.Nqkv, std::max(d.H, 2 * d.I)) * d.r));
+    w.dk_part = static_cast<float*>(take(4 * T * d.nh * d.hd));
+    w.dv_part = static_cast<float*>(take(4 * T * d.nh * d.hd));
     w.tn_bytes = tn_need(d, (int)T);
     w.tn = static_cast<float*>(take(w.tn_bytes));
   }
@@ -282,7 +312,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   TRY(rope_table(S, d.hd, c->rope_theta, w.rope, s));
   // attention block
   TRY(rmsnorm_fwd(x_in, bv.norm1, T, d.H, c->rms_eps, w.xn1, nullptr, s));
-  TRY(lora_down(w.xn1, d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, s));
+  TRY(lora_down(w.xn1, d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.xn1, T, bv.w[0], w.U_qkv, 3 * r, lv.B[0], r);
     p.nseg = 3;
@@ -294,23 +324,23 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     p.seg_ucol[2] = 2 * r;
     p.bias = bv.bias;
     p.out = w.qkv;
-    TRY(gemm_fwd(p, EPI_BF16, s));
+    TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   {
     AttnArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, d.Nq, w.lse,
                reinterpret_cast<const float2*>(w.rope), w.attn_f32};
     TRY(attention_fwd(a, B, s));
   }
-  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, s));
+  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.attn, T, bv.w[1], w.U_o, r, lv.B[1], r);
     p.resid = x_in;
     p.out = w.h;
-    TRY(gemm_fwd(p, EPI_F32_RESID, s));
+    TRY(gemm_fwd(p, EPI_F32_RESID, s, w.gemm, w.gemm_bytes));
   }
   // MLP block
   TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, nullptr, s));
-  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, s));
+  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.xn2, T, bv.w[2], w.U_gu, 2 * r, lv.B[2], r);
     p.nseg = 2;
@@ -319,34 +349,39 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     p.seg_ucol[0] = 0;
     p.seg_ucol[1] = r;
     p.out = w.gu;
-    TRY(gemm_fwd(p, EPI_BF16, s));
+    TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   TRY(swiglu_fwd(w.gu, T, d.I, w.m, s));
-  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, s));
+  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.lws, w.lws_bytes, s));
   if (x_out) {
     FwdParams p = fwd_params(w.m, T, bv.w[3], w.U_d, r, lv.B[3], r);
     p.resid = w.h;
     p.out = x_out;
-    TRY(gemm_fwd(p, EPI_F32_RESID, s));
+    TRY(gemm_fwd(p, EPI_F32_RESID, s, w.gemm, w.gemm_bytes));
   }
   return LSQ_OK;
 }
 
-// dA rows of each segment and dB rows of each segment for one stacked group.
+// dA of the whole stacked group (G^T X, one task) and dB of each segment
+// (dY_seg^T U_seg), in one launch.
 static int adapter_grads(const Dims& d, int T, const uint16_t* G, int ldg, const uint16_t* U, int ldu,
                          const uint16_t* X, int Kx, const uint16_t* dY, int ldy, int nseg, const int* seg_end,
                          float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
   const int r = d.r;
+  TnTask tasks[8];
+  int n = 0;
+  if (nseg * r <= 64) {
+    tasks[n++] = TnTask{G, ldg, nseg * r, X, Kx, Kx, gA, Kx, 1, 0};
+  } else {
+    for (int sg = 0; sg < nseg; ++sg)
+      tasks[n++] = TnTask{G + sg * r, ldg, r, X, Kx, Kx, gA + (int64_t)sg * r * Kx, Kx, 1, 0};
+  }
   for (int sg = 0; sg < nseg; ++sg) {
     const int nb = sg == 0 ? 0 : seg_end[sg - 1], ne = seg_end[sg];
-    // dA_seg [r, Kx] = G_seg^T X
-    TRY(lora_tn(G + sg * r, ldg, r, X, Kx, Kx, T, true, gA + (int64_t)sg * r * Kx, Kx, accumulate, w.tn, w.tn_bytes,
-                s));
-    // dB_seg [ne-nb, r] = dY[:, nb:ne]^T U_seg
-    TRY(lora_tn(U + sg * r, ldu, r, dY + nb, ldy, ne - nb, T, false, gB + (int64_t)nb * r, r, accumulate, w.tn,
-                w.tn_bytes, s));
+    tasks[n++] = TnTask{U + sg * r, ldu, r, dY + nb, ldy, ne - nb, gB + (int64_t)nb * r, r, 0, 0};
   }
-  return LSQ_OK;
+  (void)w;
+  return lora_grads(tasks, n, T, accumulate, s);
 }
 
 static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraView& lv, const float* x_in,
@@ -367,11 +402,11 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- down projection: out = h + down(m)
   TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[3], r, 1, one, sc, w.G, r, w.bt, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[3], r, 1, one, sc, w.G, r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[3], w.G, r, lv.A[3], r);
     p.out = w.dm;
-    TRY(gemm_bwd(p, EPI_BF16, s));
+    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[1] = {d.H};
@@ -382,11 +417,11 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   SegEnds two{};
   two.end[0] = d.I;
   two.end[1] = 2 * d.I;
-  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.B[2], r, 2, two, sc, w.G, 2 * r, w.bt, s));
+  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.B[2], r, 2, two, sc, w.G, 2 * r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dgu, T, bv.w[2], w.G, 2 * r, lv.A[2], 2 * r);
     p.out = w.dxn;
-    TRY(gemm_bwd(p, EPI_F32, s));
+    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[2] = {d.I, 2 * d.I};
@@ -397,11 +432,11 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   TRY(rmsnorm_bwd(w.h, bv.norm2, w.dxn, dx_out, T, d.H, c->rms_eps, w.dh, w.dy_b, s));
   // ---- o projection
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[1], r, 1, one, sc, w.G, r, w.bt, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[1], r, 1, one, sc, w.G, r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[1], w.G, r, lv.A[1], r);
     p.out = w.dattn;
-    TRY(gemm_bwd(p, EPI_BF16, s));
+    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[1] = {d.H};
@@ -410,7 +445,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- attention (rotary applied inside, in float32)
   {
     AttnBwdArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, w.attn_f32, w.dattn, d.Nq,
-                  w.lse, nullptr, w.dqkv, reinterpret_cast<const float2*>(w.rope)};
+                  w.lse, nullptr, w.dqkv, reinterpret_cast<const float2*>(w.rope), w.dk_part, w.dv_part};
     TRY(attention_bwd(a, B, w.D, s));
   }
   // ---- q, k, v projections
@@ -418,11 +453,11 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   three.end[0] = d.Nq;
   three.end[1] = d.Nq + d.Nkv;
   three.end[2] = d.Nqkv;
-  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.B[0], r, 3, three, sc, w.G, 3 * r, w.bt, s));
+  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.B[0], r, 3, three, sc, w.G, 3 * r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], 3 * r);
     p.out = w.dxn;
-    TRY(gemm_bwd(p, EPI_F32, s));
+    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};

@@ -30,6 +30,8 @@ struct AttnBwdArgs {
   const float* D;       // [B*S, nh] rowsum(dO * O) (filled by attention_bwd)
   uint16_t* dqkv;       // [B*S, ld], same layout as qkv; dq, dk w.r.t. the unrotated q, k
   const float2* rope;
+  float* dk_part;       // [B, nh, S, hd] per-query-head partials (workspace)
+  float* dv_part;
 };
 
 int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,

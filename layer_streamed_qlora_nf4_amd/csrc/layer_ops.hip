@@ -137,19 +137,11 @@ __global__ void rope_kernel(uint16_t* __restrict__ buf, int64_t ld, int T, int S
 }
 
 // ------------------------------------------------------------------ attention
-// Causal GQA attention on 64-query x 64-key tiles in float32 (one workgroup
-// per (query block, head, batch)); scores are kept in base 2:
+// Causal GQA attention on 64-query x 64-key tiles (one workgroup per (query
+// block, head, batch)), staged in LDS as float32; scores are kept in base 2:
 // s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
 constexpr int AT = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-
-template <int HD>
-struct AttnSmem {
-  float q[AT][HD + 4];
-  float k[AT][HD + 4];
-  float v[AT][HD + 4];
-  float p[AT][AT + 4];
-};
 
 template <int HD>
 __device__ __forceinline__ void load_rows(float (*dst)[HD + 4], const uint16_t* src, int64_t ld, int row0, int nrows_valid) {
@@ -184,41 +176,6 @@ __device__ __forceinline__ void rope_rows(float (*x)[HD + 4], int pos0, int nval
   }
 }
 
-// Gradient through the rotation for a thread's DPT output dims (the
-// transposed rotation): dims d and d +- HD/2 live in lanes c4 and c4 ^ 8.
-template <int HD, int DPT>
-__device__ __forceinline__ void rope_bwd_regs(float (&g)[DPT], int pos, int c4, const float2* __restrict__ table) {
-  constexpr int HALF = HD / 2;
-#pragma unroll
-  for (int d = 0; d < DPT; ++d) {
-    const float other = __shfl_xor(g[d], 8, 64);
-    const int i = (DPT * c4 + d) % HALF;
-    const float2 cs = table[(int64_t)pos * HALF + i];
-    g[d] = (c4 < 8) ? g[d] * cs.x + other * cs.y : g[d] * cs.x - other * cs.y;
-  }
-}
-
-// S tile for thread (rows 4*r4.., cols 4*c4..): acc[i][j] = sum_d A[r][d] B[c][d]
-template <int HD>
-__device__ __forceinline__ void tile_dot(const float (*A)[HD + 4], const float (*B)[HD + 4], int r4, int c4, float acc[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int d = 0; d < HD; d += 4) {
-    float4 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4*>(&A[4 * r4 + i][d]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(&B[4 * c4 + j][d]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] += a[i].x * b[j].x + a[i].y * b[j].y + a[i].z * b[j].z + a[i].w * b[j].w;
-  }
-}
-
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -230,14 +187,32 @@ __device__ __forceinline__ float group16_sum(float v) {
   return v;
 }
 
+// float32 MFMA 16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
+// D[4 (l / 16) + v][l % 16] comes back in element v.  Attention runs on these
+// so every operand (rotated q and k, P, dS) stays in float32.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int HD>
+struct AttnSmem {
+  float q[AT][HD + 4];
+  float k[AT][HD + 4];
+  float v[AT][HD + 4];
+  float p[4][16][AT + 4];   // per-wave P tile, row = query
+};
+
+// Forward: one workgroup per (query block of 64, head, batch); wave w owns
+// queries 16w .. 16w+15 and keeps its rotated q rows in registers.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnSmem<HD>& sm = *reinterpret_cast<AttnSmem<HD>*>(smem_raw);
-  constexpr int DPT = HD / 16;  // output dims per thread
+  constexpr int KS = HD / 4, DT = HD / 16;
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.nh / a.nkv);
-  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
   const int q0 = qb * AT;
   const int nq_valid = min(AT, a.S - q0);
   const int64_t rowbase = (int64_t)b * a.S;
@@ -247,79 +222,84 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   load_rows<HD>(sm.q, Q, a.ld, q0, nq_valid);
   __syncthreads();
   rope_rows<HD>(sm.q, q0, nq_valid, a.rope);
+  __syncthreads();
+  float qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qa[ks] = sm.q[16 * w + lr][4 * ks + lg];
   const float sc = a.scale * kLog2e;
-  float m[4], l[4], o[4][DPT];
+  float m[4], l[4];
+  f32x4 o[DT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-#pragma unroll
-    for (int d = 0; d < DPT; ++d) o[i][d] = 0.f;
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
   }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * AT;
+    const int nk_valid = min(AT, a.S - k0);
     __syncthreads();
-    load_rows<HD>(sm.k, Kp, a.ld, k0, min(AT, a.S - k0));
-    load_rows<HD>(sm.v, Vp, a.ld, k0, min(AT, a.S - k0));
+    load_rows<HD>(sm.k, Kp, a.ld, k0, nk_valid);
+    load_rows<HD>(sm.v, Vp, a.ld, k0, nk_valid);
     __syncthreads();
-    rope_rows<HD>(sm.k, k0, min(AT, a.S - k0), a.rope);
+    rope_rows<HD>(sm.k, k0, nk_valid, a.rope);
     __syncthreads();
-    float s[4][4];
-    tile_dot<HD>(sm.q, sm.k, r4, c4, s);
+    f32x4 st[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = q0 + 4 * r4 + i;
+    for (int jt = 0; jt < 4; ++jt) st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) st[jt] = mfma_f32(qa[ks], sm.k[16 * jt + lr][4 * ks + lg], st[jt]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = q0 + 16 * w + 4 * lg + v;
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kj = k0 + 4 * c4 + j;
-        s[i][j] = (kj <= qi && kj < a.S) ? s[i][j] * sc : -INFINITY;
-        mx = fmaxf(mx, s[i][j]);
+      for (int jt = 0; jt < 4; ++jt) {
+        const int kj = k0 + 16 * jt + lr;
+        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
+        mx = fmaxf(mx, st[jt][v]);
       }
       mx = group16_max(mx);
-      const float mn = fmaxf(m[i], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[i] - mn);
+      const float mn = fmaxf(m[v], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
       float rs = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pv = (s[i][j] == -INFINITY) ? 0.f : exp2f(s[i][j] - mn);
-        sm.p[4 * r4 + i][4 * c4 + j] = pv;
+      for (int jt = 0; jt < 4; ++jt) {
+        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
+        sm.p[w][4 * lg + v][16 * jt + lr] = pv;
         rs += pv;
       }
       rs = group16_sum(rs);
-      l[i] = l[i] * alpha + rs;
-      m[i] = mn;
+      l[v] = l[v] * alpha + rs;
+      m[v] = mn;
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) o[i][d] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
     }
     __syncthreads();
-    for (int j = 0; j < AT; ++j) {
-      float vv[DPT];
+#pragma unroll 4
+    for (int ks = 0; ks < AT / 4; ++ks) {
+      const float pa = sm.p[w][lr][4 * ks + lg];
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) vv[d] = sm.v[j][DPT * c4 + d];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = sm.p[4 * r4 + i][j];
-#pragma unroll
-        for (int d = 0; d < DPT; ++d) o[i][d] = fmaf(pv, vv[d], o[i][d]);
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_f32(pa, sm.v[4 * ks + lg][16 * dt + lr], o[dt]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qi = q0 + 4 * r4 + i;
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
     if (qi >= a.S) continue;
-    const float inv = 1.f / l[i];
-    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD + DPT * c4;
+    const float inv = 1.f / l[v];
+    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
 #pragma unroll
-    for (int d = 0; d < DPT; d += 2)
-      *reinterpret_cast<uint32_t*>(out + d) = pack_bf16x2(o[i][d] * inv, o[i][d + 1] * inv);
+    for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
     if (a.out_f32) {
-      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD + DPT * c4;
+      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) of[d] = o[i][d] * inv;
+      for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
     }
-    if (c4 == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[i] + log2f(l[i]);
+    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
   }
 }
 
@@ -332,198 +312,255 @@ __global__ void attn_dot_kernel(const uint16_t* __restrict__ dO, const float* __
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t, h)
   if (row >= (int64_t)T * nh) return;
   const int t = row / nh, h = row % nh;
-  const uint16_t* a = dO + (int64_t)t * ldo + (int64_t)h * hd;
-  const float* b = O + (int64_t)t * ldo + (int64_t)h * hd;
+  const uint16_t* x = dO + (int64_t)t * ldo + (int64_t)h * hd;
+  const float* y = O + (int64_t)t * ldo + (int64_t)h * hd;
   float s = 0.f;
-  for (int d = lane; d < hd; d += 64) s += bf16_bits_to_f32(a[d]) * b[d];
+  for (int d = lane; d < hd; d += 64) s += bf16_bits_to_f32(x[d]) * y[d];
   s = warp_sum(s);
   if (lane == 0) D[row] = s;
 }
 
 template <int HD>
 struct AttnBwdSmem {
-  float a[AT][HD + 4];   // Q (dK/dV kernel) or K (dQ kernel)
-  float b[AT][HD + 4];   // dO (dK/dV) or V (dQ)
-  float k[AT][HD + 4];   // this block's K (dK/dV) or Q (dQ)
-  float v[AT][HD + 4];   // this block's V (dK/dV) or dO (dQ)
-  float p[AT][AT + 4];    // P, then dS (dK/dV kernel); dS (dQ kernel)
+  float a[AT][HD + 4];      // Q rows (rotated)
+  float b[AT][HD + 4];      // dO rows
+  float k[AT][HD + 4];      // K rows (rotated)
+  float v[AT][HD + 4];      // V rows
+  float p[4][16][AT + 4];   // per-wave transposition tile
   float lse[AT];
   float dd[AT];
 };
 
-// dK and dV for one key block of one KV head: loop over its query heads and
-// the query blocks at or after it.
+// One query head's contribution to dK and dV of one key block, over the query
+// blocks at or after it, as float32 partials; attn_dkdv_reduce_kernel sums the
+// group's heads in head order.  Wave w owns keys 16w .. 16w+15.  Scores are
+// formed transposed (S^T = K Q^T) so P^T and dS^T come out key-major.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
-  constexpr int DPT = HD / 16;
-  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  constexpr int KS = HD / 4, DT = HD / 16;
+  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
   const int k0 = kb * AT;
   const int group = a.nh / a.nkv;
+  const int g = h / group;
   const int64_t rowbase = (int64_t)b * a.S;
   const float sc = a.scale * kLog2e;
-  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, min(AT, a.S - k0));
-  load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, min(AT, a.S - k0));
+  const int nk_valid = min(AT, a.S - k0);
+  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, nk_valid);
+  load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, nk_valid);
   __syncthreads();
-  rope_rows<HD>(sm.k, k0, min(AT, a.S - k0), a.rope);
-  float dk[4][DPT], dv[4][DPT];
+  rope_rows<HD>(sm.k, k0, nk_valid, a.rope);
+  __syncthreads();
+  float ka[KS], va[KS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int ks = 0; ks < KS; ++ks) {
+    ka[ks] = sm.k[16 * w + lr][4 * ks + lg];
+    va[ks] = sm.v[16 * w + lr][4 * ks + lg];
+  }
+  f32x4 dk[DT], dv[DT];
 #pragma unroll
-    for (int d = 0; d < DPT; ++d) dk[i][d] = dv[i][d] = 0.f;
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nqb = (a.S + AT - 1) / AT;
-  for (int hh = 0; hh < group; ++hh) {
-    const int h = g * group + hh;
-    for (int qb = kb; qb < nqb; ++qb) {
-      const int q0 = qb * AT;
-      const int nqv = min(AT, a.S - q0);
-      __syncthreads();
-      load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);
-      load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);
-      if (t < AT) {
-        const bool ok = t < nqv;
-        sm.lse[t] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + t] : 0.f;
-        sm.dd[t] = ok ? a.D[(rowbase + q0 + t) * a.nh + h] : 0.f;
+  for (int qb = kb; qb < nqb; ++qb) {
+    const int q0 = qb * AT;
+    const int nqv = min(AT, a.S - q0);
+    __syncthreads();
+    load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);
+    load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);
+    if (tid < AT) {
+      const bool ok = tid < nqv;
+      sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
+      sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
+    }
+    __syncthreads();
+    rope_rows<HD>(sm.a, q0, nqv, a.rope);
+    __syncthreads();
+    // S^T[k][q] and dP^T[k][q] for the wave's 16 keys x 64 queries
+    f32x4 st[4], dpt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        st[jt] = mfma_f32(ka[ks], sm.a[16 * jt + lr][4 * ks + lg], st[jt]);
+        dpt[jt] = mfma_f32(va[ks], sm.b[16 * jt + lr][4 * ks + lg], dpt[jt]);
       }
-      __syncthreads();
-      rope_rows<HD>(sm.a, q0, nqv, a.rope);
-      __syncthreads();
-      // rows = queries (r4), cols = keys (c4)
-      float s[4][4], dp[4][4];
-      tile_dot<HD>(sm.a, sm.k, r4, c4, s);
-      tile_dot<HD>(sm.b, sm.v, r4, c4, dp);
+    // P^T, written key-major into the wave's tile
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = q0 + 4 * r4 + i;
+    for (int v = 0; v < 4; ++v) {
+      const int kj = k0 + 16 * w + 4 * lg + v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kj = k0 + 4 * c4 + j;
-          const bool ok = kj <= qi && qi < a.S && kj < a.S;
-          s[i][j] = ok ? exp2f(s[i][j] * sc - sm.lse[4 * r4 + i]) : 0.f;   // P
-          sm.p[4 * r4 + i][4 * c4 + j] = s[i][j];
-        }
-      }
-      __syncthreads();
-      // dV[k][d] += sum_q P[q][k] dO[q][d]; thread owns keys 4*r4.., dims DPT*c4..
-      for (int q = 0; q < AT; ++q) {
-        float dov[DPT];
-#pragma unroll
-        for (int d = 0; d < DPT; ++d) dov[d] = sm.b[q][DPT * c4 + d];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = sm.p[q][4 * r4 + i];
-#pragma unroll
-          for (int d = 0; d < DPT; ++d) dv[i][d] = fmaf(p, dov[d], dv[i][d]);
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sm.p[4 * r4 + i][4 * c4 + j] = s[i][j] * (dp[i][j] - sm.dd[4 * r4 + i]);  // dS
-      __syncthreads();
-      // dK[k][d] += sum_q dS[q][k] Q[q][d]
-      for (int q = 0; q < AT; ++q) {
-        float qv[DPT];
-#pragma unroll
-        for (int d = 0; d < DPT; ++d) qv[d] = sm.a[q][DPT * c4 + d];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ds = sm.p[q][4 * r4 + i];
-#pragma unroll
-          for (int d = 0; d < DPT; ++d) dk[i][d] = fmaf(ds, qv[d], dk[i][d]);
-        }
+      for (int jt = 0; jt < 4; ++jt) {
+        const int qi = q0 + 16 * jt + lr;
+        const bool ok = kj <= qi && qi < a.S && kj < a.S;
+        const float pv = ok ? exp2f(st[jt][v] * sc - sm.lse[16 * jt + lr]) : 0.f;
+        st[jt][v] = pv;
+        sm.p[w][4 * lg + v][16 * jt + lr] = pv;
       }
     }
+    __syncthreads();
+    // dV[k][d] += sum_q P^T[k][q] dO[q][d]
+#pragma unroll 4
+    for (int ks = 0; ks < AT / 4; ++ks) {
+      const float pa = sm.p[w][lr][4 * ks + lg];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dv[dt] = mfma_f32(pa, sm.b[4 * ks + lg][16 * dt + lr], dv[dt]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+        sm.p[w][4 * lg + v][16 * jt + lr] = st[jt][v] * (dpt[jt][v] - sm.dd[16 * jt + lr]);   // dS^T
+    __syncthreads();
+    // dK[k][d] += sum_q dS^T[k][q] Q[q][d]
+#pragma unroll 4
+    for (int ks = 0; ks < AT / 4; ++ks) {
+      const float da = sm.p[w][lr][4 * ks + lg];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dk[dt] = mfma_f32(da, sm.a[4 * ks + lg][16 * dt + lr], dk[dt]);
+    }
   }
+  // partials [b][h][s][HD], float32; scale and rotation applied by the reduce
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kj = k0 + 4 * r4 + i;
-    rope_bwd_regs<HD, DPT>(dk[i], min(kj, a.S - 1), c4, a.rope);
+  for (int v = 0; v < 4; ++v) {
+    const int kj = k0 + 16 * w + 4 * lg + v;
     if (kj >= a.S) continue;
-    uint16_t* dkp = a.dqkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + g) * HD + DPT * c4;
-    uint16_t* dvp = a.dqkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + a.nkv + g) * HD + DPT * c4;
+    const int64_t o = (((int64_t)b * a.nh + h) * a.S + kj) * HD;
 #pragma unroll
-    for (int d = 0; d < DPT; d += 2) {
-      *reinterpret_cast<uint32_t*>(dkp + d) = pack_bf16x2(dk[i][d] * a.scale, dk[i][d + 1] * a.scale);
-      *reinterpret_cast<uint32_t*>(dvp + d) = pack_bf16x2(dv[i][d], dv[i][d + 1]);
+    for (int dt = 0; dt < DT; ++dt) {
+      a.dk_part[o + 16 * dt + lr] = dk[dt][v];
+      a.dv_part[o + 16 * dt + lr] = dv[dt][v];
     }
   }
 }
 
-// dQ for one query block of one head.
+// dK, dV of each KV head = sum of its query heads' partials (head order); dK
+// is scaled and taken back through the rotation, both rounded once to bf16.
+__global__ void attn_dkdv_reduce_kernel(AttnBwdArgs a, int B) {
+  const int half = a.hd / 2;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * a.S * a.nkv * half;
+  if (e >= total) return;
+  const int i = e % half;
+  const int g = (e / half) % a.nkv;
+  const int64_t bs = e / ((int64_t)half * a.nkv);   // b * S + s
+  const int b = bs / a.S, s = bs % a.S;
+  const int group = a.nh / a.nkv;
+  float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
+  for (int hh = 0; hh < group; ++hh) {
+    const int64_t o = (((int64_t)b * a.nh + g * group + hh) * a.S + s) * a.hd;
+    k1 += a.dk_part[o + i];
+    k2 += a.dk_part[o + i + half];
+    v1 += a.dv_part[o + i];
+    v2 += a.dv_part[o + i + half];
+  }
+  k1 *= a.scale;
+  k2 *= a.scale;
+  const float2 cs = a.rope[(int64_t)s * half + i];
+  uint16_t* row = a.dqkv + bs * a.ld;
+  row[(int64_t)(a.nh + g) * a.hd + i] = f32_to_bf16_bits(k1 * cs.x + k2 * cs.y);
+  row[(int64_t)(a.nh + g) * a.hd + i + half] = f32_to_bf16_bits(k2 * cs.x - k1 * cs.y);
+  row[(int64_t)(a.nh + a.nkv + g) * a.hd + i] = f32_to_bf16_bits(v1);
+  row[(int64_t)(a.nh + a.nkv + g) * a.hd + i + half] = f32_to_bf16_bits(v2);
+}
+
+// dQ for one query block of one head; wave w owns queries 16w .. 16w+15.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
-  constexpr int DPT = HD / 16;
+  constexpr int KS = HD / 4, DT = HD / 16;
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.nh / a.nkv);
-  const int t = threadIdx.x, r4 = t >> 4, c4 = t & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
   const int q0 = qb * AT;
   const int nqv = min(AT, a.S - q0);
   const int64_t rowbase = (int64_t)b * a.S;
   const float sc = a.scale * kLog2e;
-  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);      // Q
-  load_rows<HD>(sm.v, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);     // dO
-  if (t < AT) {
-    const bool ok = t < nqv;
-    sm.lse[t] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + t] : 0.f;
-    sm.dd[t] = ok ? a.D[(rowbase + q0 + t) * a.nh + h] : 0.f;
+  load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);      // Q
+  load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);     // dO
+  if (tid < AT) {
+    const bool ok = tid < nqv;
+    sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
+    sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
   }
   __syncthreads();
-  rope_rows<HD>(sm.k, q0, nqv, a.rope);
-  float dq[4][DPT];
+  rope_rows<HD>(sm.a, q0, nqv, a.rope);
+  __syncthreads();
+  float qa[KS], oa[KS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int ks = 0; ks < KS; ++ks) {
+    qa[ks] = sm.a[16 * w + lr][4 * ks + lg];
+    oa[ks] = sm.b[16 * w + lr][4 * ks + lg];
+  }
+  float lse_r[4], dd_r[4];
 #pragma unroll
-    for (int d = 0; d < DPT; ++d) dq[i][d] = 0.f;
+  for (int v = 0; v < 4; ++v) {
+    lse_r[v] = sm.lse[16 * w + 4 * lg + v];
+    dd_r[v] = sm.dd[16 * w + 4 * lg + v];
+  }
+  f32x4 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * AT;
+    const int nkv = min(AT, a.S - k0);
     __syncthreads();
-    load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, min(AT, a.S - k0));          // K
-    load_rows<HD>(sm.b, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, min(AT, a.S - k0));  // V
+    load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, nkv);          // K
+    load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, nkv);  // V
     __syncthreads();
-    rope_rows<HD>(sm.a, k0, min(AT, a.S - k0), a.rope);
+    rope_rows<HD>(sm.k, k0, nkv, a.rope);
     __syncthreads();
-    float s[4][4], dp[4][4];
-    tile_dot<HD>(sm.k, sm.a, r4, c4, s);
-    tile_dot<HD>(sm.v, sm.b, r4, c4, dp);
+    f32x4 st[4], dpt[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = q0 + 4 * r4 + i;
+    for (int jt = 0; jt < 4; ++jt) st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kj = k0 + 4 * c4 + j;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        st[jt] = mfma_f32(qa[ks], sm.k[16 * jt + lr][4 * ks + lg], st[jt]);
+        dpt[jt] = mfma_f32(oa[ks], sm.v[16 * jt + lr][4 * ks + lg], dpt[jt]);
+      }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = q0 + 16 * w + 4 * lg + v;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int kj = k0 + 16 * jt + lr;
         const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float p = ok ? exp2f(s[i][j] * sc - sm.lse[4 * r4 + i]) : 0.f;
-        sm.p[4 * r4 + i][4 * c4 + j] = p * (dp[i][j] - sm.dd[4 * r4 + i]);
+        const float pv = ok ? exp2f(st[jt][v] * sc - lse_r[v]) : 0.f;
+        sm.p[w][4 * lg + v][16 * jt + lr] = pv * (dpt[jt][v] - dd_r[v]);   // dS
       }
     }
     __syncthreads();
-    for (int j = 0; j < AT; ++j) {
-      float kv[DPT];
+#pragma unroll 4
+    for (int ks = 0; ks < AT / 4; ++ks) {
+      const float da = sm.p[w][lr][4 * ks + lg];
 #pragma unroll
-      for (int d = 0; d < DPT; ++d) kv[d] = sm.a[j][DPT * c4 + d];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ds = sm.p[4 * r4 + i][j];
-#pragma unroll
-        for (int d = 0; d < DPT; ++d) dq[i][d] = fmaf(ds, kv[d], dq[i][d]);
-      }
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mfma_f32(da, sm.k[4 * ks + lg][16 * dt + lr], dq[dt]);
     }
   }
+  // scale, then back through the rotation: dims d and d + HD/2 sit in tiles dt and dt + DT/2
+  constexpr int HALF_T = DT / 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qi = q0 + 4 * r4 + i;
-    rope_bwd_regs<HD, DPT>(dq[i], min(qi, a.S - 1), c4, a.rope);
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
     if (qi >= a.S) continue;
-    uint16_t* dqp = a.dqkv + (rowbase + qi) * a.ld + (int64_t)h * HD + DPT * c4;
+    uint16_t* dqp = a.dqkv + (rowbase + qi) * a.ld + (int64_t)h * HD;
 #pragma unroll
-    for (int d = 0; d < DPT; d += 2)
-      *reinterpret_cast<uint32_t*>(dqp + d) = pack_bf16x2(dq[i][d] * a.scale, dq[i][d + 1] * a.scale);
+    for (int dt = 0; dt < HALF_T; ++dt) {
+      const int i = 16 * dt + lr;
+      const float2 cs = a.rope[(int64_t)qi * (HD / 2) + i];
+      const float g1 = dq[dt][v] * a.scale, g2 = dq[dt + HALF_T][v] * a.scale;
+      dqp[i] = f32_to_bf16_bits(g1 * cs.x + g2 * cs.y);
+      dqp[i + HD / 2] = f32_to_bf16_bits(g2 * cs.x - g1 * cs.y);
+    }
   }
 }
 
@@ -727,7 +764,8 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   attn_dot_kernel<<<(unsigned)(((int64_t)T * a.nh + 3) / 4), 256, 0, s>>>(a.dO, a.O_f32, a.ldo, T, a.nh, a.hd, D);
   AttnBwdArgs b = a;
   b.D = D;
-  dim3 g1((a.S + AT - 1) / AT, a.nkv, B), g2((a.S + AT - 1) / AT, a.nh, B);
+  LSQ_CHECK(a.dk_part && a.dv_part, LSQ_ERR_WORKSPACE, "attention_bwd: partial buffers missing");
+  dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
   if (a.hd == 128) {
     attn_bwd_dkdv_kernel<128><<<g1, 256, attn_bwd_smem<128>(), s>>>(b);
     attn_bwd_dq_kernel<128><<<g2, 256, attn_bwd_smem<128>(), s>>>(b);
@@ -735,6 +773,8 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
     attn_bwd_dkdv_kernel<64><<<g1, 256, attn_bwd_smem<64>(), s>>>(b);
     attn_bwd_dq_kernel<64><<<g2, 256, attn_bwd_smem<64>(), s>>>(b);
   }
+  const int64_t nred = (int64_t)B * a.S * a.nkv * (a.hd / 2);
+  attn_dkdv_reduce_kernel<<<(unsigned)((nred + 255) / 256), 256, 0, s>>>(b, B);
   prof_end(tok, s, PROF_ATTN, flops, 0.0);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

@@ -353,6 +353,8 @@ struct StepWs {
   float* loss_rows;  // [T]
   float* dxf;        // [T, H]
   int32_t* bad;      // [1]
+  void* gemm;        // split-K partials of the head GEMMs
+  size_t gemm_bytes;
   void* layer;       // layer workspace
   size_t layer_bytes;
   size_t total;
@@ -379,6 +381,8 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base) {
   w.loss_rows = static_cast<float*>(take(4 * T));
   w.dxf = static_cast<float*>(take(4 * T * H));
   w.bad = static_cast<int32_t*>(take(4));
+  w.gemm_bytes = std::max(gemm_fwd_ws_bytes((int)T, (int)V, (int)H), gemm_bwd_ws_bytes((int)T, (int)V, (int)H, 0));
+  w.gemm = take(w.gemm_bytes);
   w.layer_bytes = layer_ws_bytes(c, B, S);
   w.layer = take(w.layer_bytes);
   w.total = off;
@@ -472,7 +476,7 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     p.resid = logits;
     p.out = logits;
     p.ldc = V;
-    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s)) return e;
+    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
   }
   if (int e = cross_entropy(logits, ids, B, S, V, w.loss_rows, w.dlogits, w.dlogits_lo, loss, s)) return e;
   if (flags & LSQ_STEP_FORWARD_ONLY) return LSQ_OK;
@@ -489,7 +493,7 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     p.resid = w.dxf;
     p.out = w.dxf;
     p.ldc = H;
-    if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s)) return e;
+    if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
   }
   float* dcur = w.dxa;
   float* dnext = w.dxb;

@@ -1,0 +1,156 @@
+"""Host-side checks that need no GPU: the library loads and exports every
+symbol the header declares, its constants and layouts agree with the oracle's
+closed forms, the pre-flight refuses what does not fit, the store's page-lock
+fallback behaves as documented, and bad arguments fail before any launch."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from layer_streamed_qlora_nf4_amd import configs, lib
+from oracle import nf4 as onf4
+from oracle import sizes as osizes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lsq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\s*\**\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_library_exports_every_declared_symbol():
+    lib.load()
+    cdll = C.CDLL(lib.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 30
+    missing = [n for n in names if not hasattr(cdll, n)]
+    assert missing == [], missing
+    assert lib.load().missing_symbols == []
+    assert set(lib.exported_symbols()) <= set(names)
+
+
+def test_codebook_is_the_oracle_codebook_bitwise():
+    got = np.array(lib.codebook(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), onf4.codebook().view(np.uint32))
+
+
+SHAPES = {"llama8b": (configs.STACK_8B, (4096, 32, 8, 128, 14336, False)),
+          "qwen72b": (configs.STACK_72B, (8192, 64, 8, 128, 29568, True))}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_blob_layout_matches_closed_form(name):
+    cfg, shape = SHAPES[name]
+    L = lib.blob_layout(cfg)
+    algo = osizes.layer_bytes_fp32_absmax(shape)
+    # 4 KiB header and 4 KiB alignment of each of the 8 weight sections + small tensors
+    assert algo <= L.total_bytes <= algo + 4096 * 12
+    assert L.total_bytes % 4096 == 0
+    for off in list(L.w_off) + list(L.absmax_off):
+        assert off % 4096 == 0
+    nq, nkv, H, I = shape[1] * shape[3], shape[2] * shape[3], shape[0], shape[4]
+    assert L.absmax_off[0] - L.w_off[0] >= (nq + 2 * nkv) * H // 2
+    if name == "llama8b":
+        assert L.total_bytes == 122703872       # 117.02 MiB: the blob every step moves twice
+
+
+def test_bf16_blob_and_lora_layout():
+    cfg = configs.STACK_3B_BF16
+    L = lib.blob_layout(cfg)
+    lin = osizes.layer_linear_params(2048, 16, 2, 128, 11008)
+    assert 2 * lin <= L.total_bytes <= 2 * lin + 4096 * 12
+    assert list(L.absmax_off) == [0, 0, 0, 0] and L.bias_off > 0
+    ll = lib.lora_layout(configs.STACK_8B)
+    r, H, I = 16, 4096, 14336
+    params = r * (3 * H + 4096 + 2 * H + I) + r * (6144 + H + 2 * I + H)
+    assert params <= ll.layer_elems <= params + 8 * 128
+
+
+def _cfg_struct(cfg):
+    return C.byref(lib.model_cfg(cfg))
+
+
+def test_vram_prediction_terms_and_refusal():
+    cfg = configs.STACK_8B
+    b = lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, C.byref(b))
+    blob = lib.blob_layout(cfg).total_bytes
+    assert b.slots == 2 * blob
+    assert b.resident == 2 * 2 * cfg.vocab * cfg.hidden + 2 * cfg.hidden
+    assert b.checkpoints == 4 * 512 * cfg.hidden * (cfg.n_layers + 1)
+    assert b.total >= b.slots + b.resident + b.adapters + b.checkpoints + b.step_workspace
+    # the logits term scales with batch x seq x vocab: that is what streaming does not bound
+    b2 = lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 4, 512, 2, C.byref(b2))
+    assert b2.step_workspace - b.step_workspace >= 3 * 512 * cfg.vocab * 6
+    # refused before any GPU work when the (overridden) free memory is too small
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, int(b.total) - 1, None)
+    assert e.value.status == "LSQ_ERR_REFUSED"
+    assert "predicted to need" in str(e.value)
+    lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, int(b.total), None)
+
+
+def test_store_pageable_fallback_and_refusal(capfd):
+    cfg = configs.TINY
+    h = C.c_void_p()
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("shard_store_create", _cfg_struct(cfg), lib.LSQ_STORE_FAIL_PIN, C.byref(h))
+    assert e.value.status == "LSQ_ERR_OOM" and "page-lock" in str(e.value)
+    lib.call("shard_store_create", _cfg_struct(cfg), lib.LSQ_STORE_FAIL_PIN | lib.LSQ_STORE_ALLOW_PAGEABLE, C.byref(h))
+    assert lib.raw("shard_store_is_pinned")(h) == 0
+    assert "PAGEABLE" in capfd.readouterr().err
+    assert lib.raw("shard_store_layer_bytes")(h) == lib.blob_layout(cfg).total_bytes
+    base = lib.raw("shard_store_layer_host")(h, 0)
+    assert lib.raw("shard_store_layer_host")(h, 1) == base + lib.blob_layout(cfg).total_bytes
+    assert lib.raw("shard_store_layer_host")(h, cfg.n_layers) is None
+    lib.raw("shard_store_destroy")(h)
+    lib.call("shard_store_create", _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h))
+    assert lib.raw("shard_store_is_pinned")(h) == 0
+    lib.raw("shard_store_destroy")(h)
+
+
+def test_arguments_are_refused_before_any_launch():
+    cfg = configs.TINY
+    bad = cfg.with_(lora_r=12)
+    with pytest.raises(lib.LsqError) as e:
+        lib.blob_layout(bad)
+    assert e.value.status == "LSQ_ERR_SHAPE"
+    w = lib.Weight(lib.LSQ_W_NF4, 0, 4096, 8192, 64, 96)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("nf4_lora_linear_fwd", C.byref(w), None, C.c_void_p(4096), 8, C.c_void_p(4096), C.c_void_p(4096), 8,
+                 2.0, lib.LSQ_BF16, C.c_void_p(4096), None, None, 0, None)
+    assert e.value.status == "LSQ_ERR_SHAPE"
+    w = lib.Weight(lib.LSQ_W_NF4, 0, 4096 + 8, 8192, 64, 128)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("nf4_lora_linear_fwd", C.byref(w), None, C.c_void_p(4096), 8, C.c_void_p(4096), C.c_void_p(4096), 8,
+                 2.0, lib.LSQ_BF16, C.c_void_p(4096), None, None, 0, None)
+    assert e.value.status == "LSQ_ERR_ALIGN"
+    # stream_buffers outside [2, 8] is a refusal, not a clamp
+    h = C.c_void_p()
+    lib.call("shard_store_create", _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h))
+    p = C.c_void_p()
+    for n in (1, 9):
+        with pytest.raises(lib.LsqError) as e:
+            lib.call("layer_pool_create", h, n, C.c_void_p(1 << 20), 1 << 20, C.c_void_p(1), C.c_void_p(2), 0,
+                     C.byref(p))
+        assert e.value.status == "LSQ_ERR_INVALID" and "[2, 8]" in str(e.value)
+    lib.raw("shard_store_destroy")(h)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("decoder_layer_fwd", _cfg_struct(cfg.with_(n_layers=1)), C.c_void_p(4096), C.c_void_p(4096),
+                 C.c_void_p(4096), 1, 8, C.c_void_p(8192), C.c_void_p(16384), 16, None)
+    assert e.value.status == "LSQ_ERR_WORKSPACE"
+
+
+def test_workspace_queries_are_consistent():
+    for cfg in (configs.TINY, configs.STACK_8B, configs.STACK_3B_BF16):
+        c = _cfg_struct(cfg)
+        lw = lib.raw("decoder_layer_workspace_size")(c, cfg.batch, cfg.seq)
+        sw = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq)
+        assert 0 < lw < sw
+        assert lib.raw("decoder_layer_workspace_size")(c, cfg.batch, 2 * cfg.seq) > lw

@@ -55,7 +55,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // ------------------------------------------------------------------ timing hooks
 namespace lsq {
 // Kernel families credited by the profiler (lsq_prof_*).
-enum ProfKind { PROF_GEMM_FWD = 0, PROF_GEMM_BWD = 1, PROF_LORA = 2, PROF_ATTN = 3, PROF_OTHER = 4, PROF_N = 5 };
+enum ProfKind {
+  PROF_GEMM_FWD = 0,   // NF4-weight tile kernels
+  PROF_GEMM_BWD = 1,
+  PROF_LORA = 2,
+  PROF_ATTN = 3,
+  PROF_OTHER = 4,
+  PROF_GEMM_BF16 = 5,  // bf16-weight tile kernels (bf16 base, the head), both directions
+  PROF_N = 6
+};
 bool prof_on();
 // Returns an opaque token; prof_end credits flops/bytes to the family.
 int prof_begin(hipStream_t s);

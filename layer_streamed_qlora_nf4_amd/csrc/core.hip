@@ -45,7 +45,8 @@ struct Prof {
   int used = 0;
   int dropped = 0;
 } g_prof;
-const char* kNames[PROF_N] = {"gemm_fwd_nf4_lora", "gemm_bwd_nf4_lora", "lora_skinny", "attention", "other"};
+const char* kNames[PROF_N] = {"gemm_fwd_nf4_lora", "gemm_bwd_nf4_lora", "lora_skinny", "attention", "other",
+                              "gemm_bf16_weights"};
 }  // namespace
 
 bool prof_on() { return g_prof.on; }

@@ -20,6 +20,12 @@
 #include "gemm.h"
 #include "nf4_levels.h"
 
+// Forward schedule: 1 = ping-pong wave groups (gemm_fwd_pp_kernel), 0 = the
+// plain double-buffered kernel of any tile shape.
+#ifndef LSQ_FWD_PP
+#define LSQ_FWD_PP 1
+#endif
+
 namespace lsq {
 namespace {
 
@@ -66,6 +72,88 @@ __device__ __forceinline__ void decode_word(uint32_t w, float a, const float* lu
     out[j] = pack_bf16x2(v0, v1);
   }
 }
+
+// LoRA up-projection folded into the tile: acc += U_seg B^T, one or more
+// extra 32-wide reduction steps (split 0 only).  r0, c0: the wave's first row
+// and column.
+template <int TM, int TN>
+__device__ __forceinline__ void fwd_lora_up(const FwdParams& p, f32x4 (&acc)[TM][TN], int r0, int c0, int lane,
+                                            int split) {
+  if (p.r <= 0 || split != 0) return;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col0 = c0 + j * 16;
+    if (col0 >= p.N) continue;
+    int s = 0;
+    while (s + 1 < p.nseg && col0 >= p.seg_end[s]) ++s;
+    const int ucol = p.seg_ucol[s];
+    const int col = col0 + (lane & 15);
+    for (int kc = 0; kc < p.r; kc += 32) {
+      const int kk = kc + 8 * g;
+      uint4 bv = (col < p.N && kk < p.r) ? *reinterpret_cast<const uint4*>(p.Bl + (int64_t)col * p.r + kk)
+                                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = r0 + i * 16 + (lane & 15);
+        uint4 av = (row < p.M && kk < p.r) ? *reinterpret_cast<const uint4*>(p.U + (int64_t)row * p.ldu + ucol + kk)
+                                           : make_uint4(0, 0, 0, 0);
+        acc[i][j] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[i][j]);
+      }
+    }
+  }
+}
+
+// Epilogue: lane holds C[4 (lane >> 4) + v][lane & 15] of each 16x16 tile.
+// Split-K launches write fp32 partials; otherwise bias, residual and the
+// output conversion are applied here.
+template <int TM, int TN, int EPI>
+__device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x4 (&acc)[TM][TN], int r0, int c0, int lane,
+                                          int split) {
+  if (p.splits > 1) {
+    float* part = p.part + (int64_t)split * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = c0 + j * 16 + (lane & 15);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = r0 + i * 16 + 4 * (lane >> 4) + v;
+          if (row < p.M) part[(int64_t)row * p.N + col] = acc[i][j][v];
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = c0 + j * 16 + (lane & 15);
+    if (col >= p.N) continue;
+    const float bias = p.bias ? bf16_bits_to_f32(p.bias[col]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = r0 + i * 16 + 4 * (lane >> 4) + v;
+        if (row >= p.M) continue;
+        float val = acc[i][j][v] + bias;
+        const int64_t o = (int64_t)row * p.ldc + col;
+        if (EPI == EPI_BF16) {
+          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(val);
+        } else if (EPI == EPI_F32) {
+          static_cast<float*>(p.out)[o] = val;
+        } else {
+          static_cast<float*>(p.out)[o] = p.resid[o] + val;
+        }
+      }
+    }
+  }
+}
+
+// Workgroup barrier that waits for this wave's LDS traffic only: global loads
+// still in flight (the next k-step's prefetch) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // =========================================================== forward (NT)
 // C[M, N] = X[M, K] W[N, K]^T + U_seg[M, r] Bl[N, r]^T (+ bias) (+ resid)
@@ -191,73 +279,143 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_fwd_kernel(FwdParams p
     __syncthreads();
   }
 
-  // LoRA up-projection: acc += U_seg B^T, one or more extra 32-wide reduction steps.
-  if (p.r > 0 && split == 0) {
-    const int g = lane >> 4;
+  fwd_lora_up<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+  fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+}
+
+// Ping-pong forward: 256 x 256 tile, 8 waves in two groups of 4 (one wave
+// per SIMD in each).  Group g owns tile rows [128 g, 128 g + 128) and loads /
+// decodes that half of the A and B tiles.  Each k-step has two halves split by
+// barriers: in half h, group h runs its MFMAs on the current LDS buffer while
+// the other group writes its share of the next k-step into the other buffer
+// and issues the global loads of the one after.  A SIMD therefore always has
+// one wave feeding the matrix unit and one doing NF4 decode on the VALU.
+template <int WKIND, int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128, TM = WM / 16, TN = WN / 16, GT = 256;
+  constexpr int A_CH = 128 * 8 / GT;                                  // 16-B A chunks per thread
+  constexpr int B_CH = (WKIND == LSQ_W_NF4) ? 128 * 2 / GT : 128 * 8 / GT;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, gtid = tid & (GT - 1);
+  const int wm = grp * 2 + ((wave >> 1) & 1), wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const int K = p.K, nk_all = K / BK;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
+
+  uint4 ra[A_CH], rb[B_CH];
+  float rabs[B_CH];
+  const int arow0 = grp * 128;   // this group's share: rows [arow0, arow0 + 128) of both tiles
+
+  auto load_share = [&](int kt) {
+    const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col0 = n0 + wn * WN + j * 16;
-      if (col0 >= p.N) continue;
-      int s = 0;
-      while (s + 1 < p.nseg && col0 >= p.seg_end[s]) ++s;
-      const int ucol = p.seg_ucol[s];
-      const int col = col0 + (lane & 15);
-      for (int kc = 0; kc < p.r; kc += 32) {
-        const int kk = kc + 8 * g;
-        uint4 bv = (col < p.N && kk < p.r) ? *reinterpret_cast<const uint4*>(p.Bl + (int64_t)col * p.r + kk)
-                                           : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7, m = m0 + row;
+      ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(p.X + (int64_t)m * p.ldx + k0 + c * 8)
+                        : make_uint4(0, 0, 0, 0);
+    }
+    if (WKIND == LSQ_W_NF4) {
+      const uint8_t* W = static_cast<const uint8_t*>(p.W);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = m0 + wm * WM + i * 16 + (lane & 15);
-          uint4 av = (row < p.M && kk < p.r)
-                         ? *reinterpret_cast<const uint4*>(p.U + (int64_t)row * p.ldu + ucol + kk)
-                         : make_uint4(0, 0, 0, 0);
-          acc[i][j] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[i][j]);
-        }
+      for (int i = 0; i < B_CH; ++i) {
+        const int q = gtid + i * GT, n = n0 + arow0 + (q >> 1), h = q & 1;
+        const bool ok = n < p.N;
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16) : make_uint4(0, 0, 0, 0);
+        rabs[i] = ok ? p.absmax[(int64_t)n * (K / 64) + kt] : 0.f;
+      }
+    } else {
+      const uint16_t* W = static_cast<const uint16_t*>(p.W);
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int q = gtid + i * GT, n = n0 + arow0 + (q >> 3), c = q & 7;
+        rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
       }
     }
-  }
+  };
 
-  // Epilogue: lane holds C[4 (lane >> 4) + v][lane & 15] of each 16x16 tile.
-  if (p.splits > 1) {
-    float* part = p.part + (int64_t)split * p.M * p.N;
+  auto store_share = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + j * 16 + (lane & 15);
-      if (col >= p.N) continue;
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7;
+      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
+    }
+    if (WKIND == LSQ_W_NF4) {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int q = gtid + i * GT, row = arow0 + (q >> 1), h = q & 1;
+        const uint32_t words[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t o[4];
+          decode_word(words[w], rabs[i], lut, o);
+          *reinterpret_cast<uint4*>(&Bs[buf][swz(row, h * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7;
+        *reinterpret_cast<uint4*>(&Bs[buf][swz(row, c)]) = rb[i];
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_step = [&](int cur) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TN];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = lds_frag(Bs[cur], swz(wn * WN + j * 16 + (lane & 15), chunk));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
-          if (row < p.M) part[(int64_t)row * p.N + col] = acc[i][j][v];
-        }
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
     }
-    return;
-  }
+  };
+
+  // Prologue: both groups fill buffer 0 with k-step kbeg and prefetch kbeg + 1.
+  if (kbeg < nk) load_share(kbeg);
+  __syncthreads();  // lut
+  if (kbeg < nk) store_share(0);
+  if (kbeg + 1 < nk) load_share(kbeg + 1);
+  lds_barrier();
+
+  for (int kt = kbeg; kt < nk; ++kt) {
+    const int cur = (kt - kbeg) & 1;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WN + j * 16 + (lane & 15);
-    if (col >= p.N) continue;
-    const float bias = p.bias ? bf16_bits_to_f32(p.bias[col]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
-        if (row >= p.M) continue;
-        float val = acc[i][j][v] + bias;
-        const int64_t o = (int64_t)row * p.ldc + col;
-        if (EPI == EPI_BF16) {
-          static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(val);
-        } else if (EPI == EPI_F32) {
-          static_cast<float*>(p.out)[o] = val;
-        } else {
-          static_cast<float*>(p.out)[o] = p.resid[o] + val;
-        }
+    for (int half = 0; half < 2; ++half) {
+      if (grp == half) {
+        mfma_step(cur);
+      } else if (kt + 1 < nk) {
+        store_share(cur ^ 1);
+        if (kt + 2 < nk) load_share(kt + 2);
       }
+      lds_barrier();
     }
   }
+
+  fwd_lora_up<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+  fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
 }
 
 // =========================================================== backward (NN)
@@ -808,7 +966,12 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 template <int BM, int BN, int WGM, int WGN, int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+#if LSQ_FWD_PP
+  static_assert(BM == 256 && BN == 256 && WGM * WGN == 8, "ping-pong forward is 256 x 256 with 8 waves");
+  gemm_fwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+#else
   gemm_fwd_kernel<BM, BN, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
+#endif
 }
 
 template <int BM, int BO, int WGM, int WGN, int WK, int EPI>
@@ -829,11 +992,26 @@ void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* 
     splitk_reduce_kernel<EPI_F32_RESID><<<grid, 256, 0, s>>>(part, splits, M, N, bias, resid, out, ldc);
 }
 
-int choose_splits(int tiles, int ksteps) {
-  if (tiles >= 256) return 1;
-  int sp = 512 / std::max(1, tiles);
-  sp = std::min(sp, std::max(1, ksteps / 8));   // keep >= 8 reduction steps per split
-  return std::max(1, std::min(8, sp));
+// Split count from a small cost model: a launch runs in rounds of 256
+// workgroups (one large tile per CU), each round as long as its split's
+// reduction steps; every extra split writes and re-reads an fp32 partial of the
+// whole output.  Per-step time is the tile's flops at ~40% of one CU's MFMA
+// peak; partial traffic is priced at 4 TB/s.
+int choose_splits(int tiles, int ksteps, double out_elems, double tile_flops_per_step) {
+  const double step_us = tile_flops_per_step / (0.4 * 2.5e15 / 256) * 1e6;
+  int best = 1;
+  double best_t = 1e30;
+  for (int sp = 1; sp <= 8; ++sp) {
+    if (sp > 1 && ksteps / sp < 4) break;
+    const double rounds = (double)((tiles * sp + 255) / 256);
+    const double steps = (double)((ksteps + sp - 1) / sp);
+    const double t = rounds * steps * step_us + (sp > 1 ? 8.0 * sp * out_elems / 4e6 : 0.0);
+    if (t < best_t * 0.97) {   // a split must win clearly to be taken
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
 }
 
 template <int BM, int BN, int WGM, int WGN, int WK>
@@ -853,10 +1031,10 @@ void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
 // Tile shape of each direction (compile-time; tuned on gfx950).  Kernel
 // choice is a pure function of the shape, never of where the weights live.
 #ifndef LSQ_FWD_TILE
-#define LSQ_FWD_TILE 128, 128, 2, 2
+#define LSQ_FWD_TILE 256, 256, 4, 2
 #endif
 #ifndef LSQ_BWD_TILE
-#define LSQ_BWD_TILE 128, 128, 2, 2
+#define LSQ_BWD_TILE 256, 256, 4, 2
 #endif
 constexpr int kFwdTile[4] = {LSQ_FWD_TILE};
 constexpr int kBwdTile[4] = {LSQ_BWD_TILE};
@@ -865,11 +1043,12 @@ constexpr int kBwdTile[4] = {LSQ_BWD_TILE};
 
 // ------------------------------------------------------------------ launchers
 int gemm_fwd_splits(int M, int N, int K) {
-  return choose_splits(((M + kFwdTile[0] - 1) / kFwdTile[0]) * ((N + kFwdTile[1] - 1) / kFwdTile[1]), K / 64);
+  return choose_splits(((M + kFwdTile[0] - 1) / kFwdTile[0]) * ((N + kFwdTile[1] - 1) / kFwdTile[1]), K / 64,
+                       (double)M * N, 2.0 * kFwdTile[0] * kFwdTile[1] * 64);
 }
 int gemm_bwd_splits(int M, int N, int K, int rr) {
   return choose_splits(((M + kBwdTile[0] - 1) / kBwdTile[0]) * ((K + kBwdTile[1] - 1) / kBwdTile[1]),
-                       (N + 63) / 64 + (rr + 63) / 64);
+                       (N + 63) / 64 + (rr + 63) / 64, (double)M * K, 2.0 * kBwdTile[0] * kBwdTile[1] * 64);
 }
 size_t gemm_fwd_ws_bytes(int M, int N, int K) {
   const int sp = gemm_fwd_splits(M, N, K);
@@ -894,12 +1073,16 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.N * p.r;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
+  // The profiler brackets the tile kernel alone; a split-K reduction is credited separately.
   int tok = prof_begin(s);
-  // 128 x 128 tiles, 4 waves of 64 x 64.
   if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_NF4>(p, epi, s);
   else dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_BF16>(p, epi, s);
-  if (p.splits > 1) launch_reduce(p.part, p.splits, p.M, p.N, p.bias, p.resid, p.out, p.ldc, epi, s);
-  prof_end(tok, s, PROF_GEMM_FWD, flops, bytes);
+  prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_FWD : PROF_GEMM_BF16, flops, bytes);
+  if (p.splits > 1) {
+    tok = prof_begin(s);
+    launch_reduce(p.part, p.splits, p.M, p.N, p.bias, p.resid, p.out, p.ldc, epi, s);
+    prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * p.splits * p.M * (double)p.N + 2.0 * p.M * (double)p.N);
+  }
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -922,8 +1105,12 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   int tok = prof_begin(s);
   if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_NF4>(p, epi, s);
   else dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_BF16>(p, epi, s);
-  if (p.splits > 1) launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);
-  prof_end(tok, s, PROF_GEMM_BWD, flops, bytes);
+  prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_BWD : PROF_GEMM_BF16, flops, bytes);
+  if (p.splits > 1) {
+    tok = prof_begin(s);
+    launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);
+    prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * p.splits * p.M * (double)p.K + 2.0 * p.M * (double)p.K);
+  }
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }

@@ -7,7 +7,7 @@ because the backward recomputes it (LS-docs "How it works"); recomputation
 does not change the mathematics, so this oracle simply computes the forward
 again inside the backward.
 
-Readings of transformers' Llama / Qwen2 decoder layer (listed in the design doc):
+Readings of transformers' Llama / Qwen2 decoder layer (the pages print none of it):
 
 * RMSNorm: y = w * x / sqrt(mean(x^2) + eps).
 * Rotary embedding, rotate-half form, on head_dim d: for i < d/2 the pair

@@ -7,7 +7,7 @@ Plain LoRA only, no DoRA / VeRA and friends (LS-docs "Honest scope").  Adapter
 tensor names lora_A / lora_B follow PEFT (LS-docs "Read this first": the key
 names of a saved adapter).
 
-Reading of PEFT's plain LoRA (listed in the design doc): A is [r, K], B is [N, r],
+Reading of PEFT's plain LoRA (the pages print none of it): A is [r, K], B is [N, r],
 scale s = alpha / r, dropout 0, so for X [M, K] and base W [N, K]
 
     U  = X A^T                       [M, r]

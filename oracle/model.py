@@ -7,7 +7,7 @@ for the embedding, norms or head (LS-docs "Honest scope": a LoRA target on a
 streamed head or embedding is refused).  The non-quantised tensors stay in the
 store dtype (LS-docs "How it works", scope of the NF4 comparison).
 
-Readings (listed in the design doc): the loss is the mean cross-entropy over the
+Readings (the pages leave these open): the loss is the mean cross-entropy over the
 B*(S-1) next-token positions of each sequence; a tied model uses the
 embedding matrix as its head.
 

@@ -4,7 +4,7 @@ What the pages fix: the frozen base is rewritten once, offline, one shard per
 decoder layer, quantising to NF4 as it goes, which makes the store about four
 times smaller than bf16 (LS-docs "Shard cache"; About; LS-docs "Turn it on").
 The pages do not print the codebook, the block rule or the packing.  Readings
-taken here (each listed in the design doc):
+taken here (the pages leave each open):
 
 1. Codebook: the NormalFloat-4 construction of the QLoRA paper (Dettmers et
    al., 2023): 8 positive normal quantiles and 7 negative ones, with one

@@ -8,7 +8,7 @@ for 72B (LS-docs "Honest scope"), 2.10 GB for the untied 8B embedding and head,
 and a 5.70 GB store once those moved into it (LS-docs "Why NF4 also made the
 3B row faster"; "Disk space and the second cache").
 
-Reading (listed in the design doc): those figures are reproduced exactly by a
+Reading: those figures are reproduced exactly by a
 layout with 4-bit codes, an 8-bit absmax per 64-element block and one float32
 second-level scale per 256 blocks, bf16 norms and biases, in decimal GB (the
 72B figure is in GiB).  This build stores a plain float32 absmax per block

@@ -53,6 +53,7 @@ struct BwdParams {
   int64_t ldg;
   const uint16_t* Al;    // stacked A, bf16 [rr, K]
   int rr;
+  const uint16_t* AlT;   // Al transposed [K, rr] (workspace; set by gemm_bwd)
   const float* resid;
   void* out;
   int64_t ldc;
@@ -78,17 +79,20 @@ struct GChunks {
 };
 
 // U[M, rr] = bf16(s X A^T), A = stacked [rr, K]; ws holds the chunk partials.
+// U32 (nullable, ld ldu32) receives the same values before the bf16 rounding.
 size_t lora_down_ws_bytes(int M, int K, int rr);
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, float* ws, size_t ws_bytes, hipStream_t st);
+              int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, hipStream_t st);
 // G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]); ws holds B transposed and partials.
+// G32 (nullable, ld ldg32) receives the unrounded values.
 size_t lora_g_ws_bytes(int M, int N, int r);
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, float* ws, size_t ws_bytes, hipStream_t st);
-// One reduction over the token dimension, C = S^T L: S [M, ns] (ns <= 64, a
-// multiple of 8), L [M, nl]; small_rows: out [ns, nl] (dA); else out [nl, ns] (dB).
+           float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, hipStream_t st);
+// One reduction over the token dimension, C = S^T L: S [M, ns] float32 (ns <=
+// 64, a multiple of 8), L [M, nl] bf16; small_rows: out [ns, nl] (dA); else
+// out [nl, ns] (dB).  The small side is the unrounded U or G.
 struct TnTask {
-  const uint16_t* S;
+  const float* S;
   int64_t lds;
   int ns;
   const uint16_t* L;
@@ -112,7 +116,7 @@ int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream
 
 // Token-dimension reduction C = S^T L (small_rows: [ns, nl]; else [nl, ns]).
 size_t lora_tn_ws_bytes(int M, int ns, int nl);
-int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
+int lora_tn(const float* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
             float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace lsq

@@ -25,6 +25,9 @@
 #ifndef LSQ_FWD_PP
 #define LSQ_FWD_PP 1
 #endif
+#ifndef LSQ_BWD_PP
+#define LSQ_BWD_PP 1
+#endif
 
 namespace lsq {
 namespace {
@@ -319,9 +322,11 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
 
   auto load_share = [&](int kt) {
     const int k0 = kt * BK;
+    int gt = gtid;   // opaque copy: addresses are rebuilt per call, not held in registers
+    asm volatile("" : "+v"(gt));
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7, m = m0 + row;
+      const int q = gt + i * GT, row = arow0 + (q >> 3), c = q & 7, m = m0 + row;
       ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(p.X + (int64_t)m * p.ldx + k0 + c * 8)
                         : make_uint4(0, 0, 0, 0);
     }
@@ -329,7 +334,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
       const uint8_t* W = static_cast<const uint8_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int q = gtid + i * GT, n = n0 + arow0 + (q >> 1), h = q & 1;
+        const int q = gt + i * GT, n = n0 + arow0 + (q >> 1), h = q & 1;
         const bool ok = n < p.N;
         rb[i] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16) : make_uint4(0, 0, 0, 0);
         rabs[i] = ok ? p.absmax[(int64_t)n * (K / 64) + kt] : 0.f;
@@ -338,7 +343,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
       const uint16_t* W = static_cast<const uint16_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int q = gtid + i * GT, n = n0 + arow0 + (q >> 3), c = q & 7;
+        const int q = gt + i * GT, n = n0 + arow0 + (q >> 3), c = q & 7;
         rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
       }
     }
@@ -569,17 +574,26 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
     __syncthreads();
   }
 
+  bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
+}
+
+// Backward epilogue (lane layout as in fwd_store); columns are the weight's
+// input dimension K.
+template <int TM, int TO, int EPI>
+__device__ __forceinline__ void bwd_store(const BwdParams& p, const f32x4 (&acc)[TM][TO], int r0, int c0, int lane,
+                                          int split) {
+  const int K = p.K;
   if (p.splits > 1) {
     float* part = p.part + (int64_t)split * p.M * K;
 #pragma unroll
     for (int j = 0; j < TO; ++j) {
-      const int col = o0 + wo * WO + j * 16 + (lane & 15);
+      const int col = c0 + j * 16 + (lane & 15);
       if (col >= K) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+          const int row = r0 + i * 16 + 4 * (lane >> 4) + v;
           if (row < p.M) part[(int64_t)row * K + col] = acc[i][j][v];
         }
     }
@@ -587,16 +601,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
   }
 #pragma unroll
   for (int j = 0; j < TO; ++j) {
-    const int col = o0 + wo * WO + j * 16 + (lane & 15);
+    const int col = c0 + j * 16 + (lane & 15);
     if (col >= K) continue;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + v;
+        const int row = r0 + i * 16 + 4 * (lane >> 4) + v;
         if (row >= p.M) continue;
         const int64_t o = (int64_t)row * p.ldc + col;
-        float val = acc[i][j][v];
+        const float val = acc[i][j][v];
         if (EPI == EPI_BF16) {
           static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(val);
         } else if (EPI == EPI_F32) {
@@ -607,6 +621,194 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
       }
     }
   }
+}
+
+// LoRA term of the backward folded into the tile: acc += G[:, 0:rr] Al, one
+// or more extra 32-wide reduction steps (split 0 only), with Al read from its
+// transposed copy AlT [K, rr] so each lane's 8 reduction values are contiguous.
+template <int TM, int TO>
+__device__ __forceinline__ void bwd_lora_up(const BwdParams& p, f32x4 (&acc)[TM][TO], int r0, int c0, int lane,
+                                            int split) {
+  if (p.rr <= 0 || split != 0) return;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < TO; ++j) {
+    const int col = c0 + j * 16 + (lane & 15);
+    for (int kc = 0; kc < p.rr; kc += 32) {
+      const int kk = kc + 8 * g;
+      const uint4 bv = (col < p.K && kk < p.rr) ? *reinterpret_cast<const uint4*>(p.AlT + (int64_t)col * p.rr + kk)
+                                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = r0 + i * 16 + (lane & 15);
+        const uint4 av = (row < p.M && kk < p.rr) ? *reinterpret_cast<const uint4*>(p.G + (int64_t)row * p.ldg + kk)
+                                                  : make_uint4(0, 0, 0, 0);
+        acc[i][j] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[i][j]);
+      }
+    }
+  }
+}
+
+// Transposed micro-tile coordinates of the backward weight slab (BO output
+// columns x 64 reduction rows): micro-tile u covers rows 4 rg .. 4 rg + 3 and
+// columns 8 q .. 8 q + 7; lanes 8 apart in q, neighbouring rg pairs in a pass.
+template <int BO>
+__device__ __forceinline__ void bwd_mt_coords(int u, int& rg, int& q) {
+  q = (u & 7) | (((u >> 4) & ((BO / 8 / 8) - 1)) << 3);
+  rg = ((u >> 3) & 1) | ((u >> (4 + __builtin_ctz(BO / 64))) << 1);
+}
+
+// Decode (or copy) one micro-tile held in registers and write it transposed
+// into Bt: column c of the micro-tile becomes 4 consecutive reduction values.
+template <bool NF4, int RB>
+__device__ __forceinline__ void bwd_store_mt(uint16_t* Bt, int rg, int q, const uint32_t (&rb)[RB], const float* lut) {
+  // rb: NF4 -> codes of rows 0..3 in rb[0..3], their absmax bits in rb[4..7];
+  //     bf16 -> rows 0..3 as four 16-byte groups.
+  uint32_t pairs[4][4];  // pairs[rr][j] = (col 2j, col 2j+1) of row rr
+  if (NF4) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) decode_word(rb[rr], __uint_as_float(rb[4 + rr]), lut, pairs[rr]);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pairs[rr][w] = rb[(4 * rr + w) % RB];
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int sel = (c & 1) ? 0x07060302 : 0x05040100;  // high or low halves
+    const uint32_t lo = __builtin_amdgcn_perm(pairs[1][c >> 1], pairs[0][c >> 1], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(pairs[3][c >> 1], pairs[2][c >> 1], sel);
+    const int krow = q * 8 + c, nbase = rg * 4;
+    *reinterpret_cast<u32x2*>(Bt + swzt(krow, nbase >> 3) + (nbase & 7)) = u32x2{lo, hi};
+  }
+}
+
+// Ping-pong backward: the forward's schedule over the NN product.  Group g
+// runs the MFMAs of rows [128 g, 128 g + 128) and produces half of the next
+// k-step: its own dY (or G) rows and half of the weight slab's micro-tiles.
+template <int WKIND, int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
+  constexpr int BM = 256, BO = 256, WM = 64, WO = 128, TM = WM / 16, TO = WO / 16, GT = 256;
+  constexpr int A_CH = 128 * 8 / GT;           // 16-B dY chunks per thread
+  constexpr int MT_TOTAL = (64 / 4) * (BO / 8);
+  static_assert(MT_TOTAL == 2 * GT, "one micro-tile per producer thread");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bt[2][BO * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, gtid = tid & (GT - 1);
+  const int wm = grp * 2 + ((wave >> 1) & 1), wo = wave & 1;
+  const int tiles_o = (p.K + BO - 1) / BO;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
+  const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const int K = p.K;
+  const int nk_all = (p.N + BK - 1) / BK;   // the LoRA term is added after the main loop
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
+
+  const int arow0 = grp * 128;
+  int mrg, mq;
+  bwd_mt_coords<BO>(grp * GT + gtid, mrg, mq);
+  constexpr int RB = (WKIND == LSQ_W_NF4) ? 8 : 16;
+  uint4 ra[A_CH];
+  uint32_t rb[RB];   // the micro-tile: NF4 codes + absmax bits, or bf16 rows (see bwd_store_mt)
+
+  auto load_share = [&](int kt) {
+    const int r0 = kt * BK;
+    int gt = gtid, lq = mq, lrg = mrg;   // opaque copies: addresses are rebuilt per call, not held
+    asm volatile("" : "+v"(gt), "+v"(lq), "+v"(lrg));
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = gt + i * GT, row = arow0 + (q >> 3), c = q & 7;
+      const int m = m0 + row, rcol = r0 + c * 8;
+      ra[i] = (m < p.M && rcol < p.N) ? *reinterpret_cast<const uint4*>(p.dY + (int64_t)m * p.ldy + rcol)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+    const int kcol = o0 + lq * 8;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int n = r0 + lrg * 4 + rr;
+      const bool ok = n < p.N && kcol < K;
+      if (WKIND == LSQ_W_NF4) {
+        const uint8_t* W = static_cast<const uint8_t*>(p.W);
+        rb[rr] = ok ? *reinterpret_cast<const uint32_t*>(W + (int64_t)n * (K / 2) + kcol / 2) : 0u;
+        rb[4 + rr] = ok ? __float_as_uint(p.absmax[(int64_t)n * (K / 64) + kcol / 64]) : 0u;
+      } else {
+        const uint16_t* W = static_cast<const uint16_t*>(p.W);
+        const uint4 v = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + kcol) : make_uint4(0, 0, 0, 0);
+        rb[(4 * rr) % RB] = v.x;
+        rb[(4 * rr + 1) % RB] = v.y;
+        rb[(4 * rr + 2) % RB] = v.z;
+        rb[(4 * rr + 3) % RB] = v.w;
+      }
+    }
+  };
+
+  auto store_share = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7;
+      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
+    }
+    int q = mq;
+    asm volatile("" : "+v"(q));
+    bwd_store_mt<WKIND == LSQ_W_NF4, RB>(Bt[buf], mrg, q, rb, lut);
+  };
+
+  f32x4 acc[TM][TO];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_step = [&](int cur) {
+    // The transposed tile's swizzle differs per 16-row block; recompute its
+    // addresses here (an empty asm hides the base from loop-invariant code
+    // motion) instead of holding 16 of them in registers across the loop.
+    int brow = wo * WO + (lane & 15);
+    asm volatile("" : "+v"(brow));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TO];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TO; ++j) bfr[j] = lds_frag(Bt[cur], swzt(brow + j * 16, chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TO; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  if (kbeg < nk) load_share(kbeg);
+  __syncthreads();  // lut
+  if (kbeg < nk) store_share(0);
+  if (kbeg + 1 < nk) load_share(kbeg + 1);
+  lds_barrier();
+
+  for (int kt = kbeg; kt < nk; ++kt) {
+    const int cur = (kt - kbeg) & 1;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (grp == half) {
+        mfma_step(cur);
+      } else if (kt + 1 < nk) {
+        store_share(cur ^ 1);
+        if (kt + 2 < nk) load_share(kt + 2);
+      }
+      lds_barrier();
+    }
+  }
+  bwd_lora_up<TM, TO>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
+  bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
 }
 
 // =========================================================== LoRA down: U = s X A^T
@@ -654,13 +856,20 @@ __global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __r
 
 // dst[m, col0 + c] = bf16(s * sum over chunks of part[chunk, m, c]) for c < w
 __global__ void lora_finish_kernel(const float* __restrict__ part, int nchunks, int M, int w, float s,
-                                   uint16_t* __restrict__ dst, int64_t ld, int col0) {
+                                   uint16_t* __restrict__ dst, int64_t ld, float* __restrict__ dst32, int64_t ld32) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (int64_t)M * w) return;
   const int64_t m = e / w, c = e % w;
   float v = 0.f;
   for (int k = 0; k < nchunks; ++k) v += part[(int64_t)k * M * w + e];
-  dst[m * ld + col0 + c] = f32_to_bf16_bits(s * v);
+  v *= s;
+  dst[m * ld + c] = f32_to_bf16_bits(v);
+  if (dst32) dst32[m * ld32 + c] = v;
+}
+
+__global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, int64_t n, float* __restrict__ dst) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) dst[e] = bf16_bits_to_f32(src[e]);
 }
 
 // B [N, r] -> Bt [r, N] (bf16), so the G kernel reads 8 reduction values contiguously.
@@ -719,8 +928,20 @@ __global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __rest
 // tokens reading L straight from HBM (coalesced) and S as wave-uniform loads;
 // the 4 waves' sums meet in LDS in wave order.  With splits > 1 the partials
 // go to ws and reduce_splits adds them in split order.
+// 8 or 16 float32 small-side values of one token: wave-uniform 16-byte loads.
+__device__ __forceinline__ void load_small16(const float* row, bool wide, float (&sv)[16]) {
+  const float4* p = reinterpret_cast<const float4*>(row);
+  const float4 a = p[0], b = p[1];
+  const float4 c = wide ? p[2] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 d = wide ? p[3] : make_float4(0.f, 0.f, 0.f, 0.f);
+  sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
+  sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
+  sv[8] = c.x; sv[9] = c.y; sv[10] = c.z; sv[11] = c.w;
+  sv[12] = d.x; sv[13] = d.y; sv[14] = d.z; sv[15] = d.w;
+}
+
 template <bool SMALL_ROWS>
-__global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __restrict__ S, int64_t lds_, int ns,
+__global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const float* __restrict__ S, int64_t lds_, int ns,
                                                            const uint16_t* __restrict__ Lm, int64_t ldl, int nl, int M,
                                                            int rows_per_split, float* __restrict__ out,
                                                            int64_t ldo, int accumulate, int direct) {
@@ -742,19 +963,15 @@ __global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __res
   for (int m = mb + wave; m < me; m += 4) {
     const uint2 lv = colok ? *reinterpret_cast<const uint2*>(Lm + (int64_t)m * ldl + col) : make_uint2(0, 0);
     const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
-    // 8 or 16 small-side values of this token: wave-uniform 16-byte loads
-    const uint4* srow = reinterpret_cast<const uint4*>(S + (int64_t)m * lds_ + j0);
-    const uint4 s0 = srow[0];
-    const uint4 s1 = wide ? srow[1] : make_uint4(0, 0, 0, 0);
-    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float sv[16];
+    load_small16(S + (int64_t)m * lds_ + j0, wide, sv);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float sv = (j & 1) ? bf_hi(sw[j >> 1]) : bf_lo(sw[j >> 1]);
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv, l4[c], acc[j][c]);
-    }
+      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv[j], l4[c], acc[j][c]);
   }
   // waves 1..3 park their sums; wave 0 adds them in order
+#pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (wave > 0) {
 #pragma unroll
@@ -765,7 +982,7 @@ __global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __res
   if (wave != 0 || !colok) return;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    if (j >= nj) break;
+    if (j >= nj) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
@@ -789,9 +1006,12 @@ __global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const uint16_t* __res
 __global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
   __shared__ float red[3][64][65];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int ti = 0;
-  while (ti + 1 < bt.ntasks && (int)blockIdx.x >= bt.t[ti + 1].tile0) ++ti;
-  const TnTask& tk = bt.t[ti];
+  // Pick this workgroup's task with constant indices only: a dynamically
+  // indexed kernel-argument array would be copied to scratch memory.
+  TnTask tk = bt.t[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    if (i < bt.ntasks && (int)blockIdx.x >= bt.t[i].tile0) tk = bt.t[i];
   const int local = blockIdx.x - tk.tile0;
   const int ncol = (tk.nl + 255) / 256;
   const int col = (local % ncol) * 256 + lane * 4;
@@ -808,17 +1028,14 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
   for (int m = wave; m < bt.M; m += 4) {
     const uint2 lv = colok ? *reinterpret_cast<const uint2*>(tk.L + (int64_t)m * tk.ldl + col) : make_uint2(0, 0);
     const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
-    const uint4* srow = reinterpret_cast<const uint4*>(tk.S + (int64_t)m * tk.lds + j0);
-    const uint4 s0 = srow[0];
-    const uint4 s1 = wide ? srow[1] : make_uint4(0, 0, 0, 0);
-    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float sv[16];
+    load_small16(tk.S + (int64_t)m * tk.lds + j0, wide, sv);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float sv = (j & 1) ? bf_hi(sw[j >> 1]) : bf_lo(sw[j >> 1]);
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv, l4[c], acc[j][c]);
-    }
+      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv[j], l4[c], acc[j][c]);
   }
+#pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (wave > 0) {
 #pragma unroll
@@ -829,7 +1046,7 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
   if (wave != 0 || !colok) return;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    if (j >= nj) break;
+    if (j >= nj) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
@@ -843,7 +1060,8 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
 
 // G finish for several segments at once: segment s sums chunks [c0, c1) of part.
 __global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinish sf, int M, int r, float s,
-                                        uint16_t* __restrict__ dst, int64_t ld) {
+                                        uint16_t* __restrict__ dst, int64_t ld, float* __restrict__ dst32,
+                                        int64_t ld32) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per = (int64_t)M * r;
   if (e >= per * sf.n) return;
@@ -852,7 +1070,9 @@ __global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinis
   const int64_t m = i / r, c = i % r;
   float v = 0.f;
   for (int k = sf.c0[sg]; k < sf.c1[sg]; ++k) v += part[(int64_t)k * per + i];
-  dst[m * ld + sf.col[sg] + c] = f32_to_bf16_bits(s * v);
+  v *= s;
+  dst[m * ld + sf.col[sg] + c] = f32_to_bf16_bits(v);
+  if (dst32) dst32[m * ld32 + sf.col[sg] + c] = v;
 }
 
 // out[i, j] (+)= sum over splits, in split order.  Partials are packed [splits][rows][cols].
@@ -977,7 +1197,12 @@ void launch_fwd(const FwdParams& p, hipStream_t s) {
 template <int BM, int BO, int WGM, int WGN, int WK, int EPI>
 void launch_bwd(const BwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.K + BO - 1) / BO);
+#if LSQ_BWD_PP
+  static_assert(BM == 256 && BO == 256 && WGM * WGN == 8, "ping-pong backward is 256 x 256 with 8 waves");
+  gemm_bwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+#else
   gemm_bwd_kernel<BM, BO, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
+#endif
 }
 
 void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* bias, const float* resid, void* out,
@@ -1047,16 +1272,21 @@ int gemm_fwd_splits(int M, int N, int K) {
                        (double)M * N, 2.0 * kFwdTile[0] * kFwdTile[1] * 64);
 }
 int gemm_bwd_splits(int M, int N, int K, int rr) {
+  const int lora_steps = LSQ_BWD_PP ? 0 : (rr + 63) / 64;   // ping-pong adds the LoRA term after its main loop
   return choose_splits(((M + kBwdTile[0] - 1) / kBwdTile[0]) * ((K + kBwdTile[1] - 1) / kBwdTile[1]),
-                       (N + 63) / 64 + (rr + 63) / 64, (double)M * K, 2.0 * kBwdTile[0] * kBwdTile[1] * 64);
+                       (N + 63) / 64 + lora_steps, (double)M * K, 2.0 * kBwdTile[0] * kBwdTile[1] * 64);
+}
+// Workspace of gemm_bwd: split-K partials, then (ping-pong) the transposed LoRA A.
+static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
+  const int sp = gemm_bwd_splits(M, N, K, rr);
+  return sp > 1 ? ((size_t)sp * M * K * sizeof(float) + 255) / 256 * 256 : 0;
 }
 size_t gemm_fwd_ws_bytes(int M, int N, int K) {
   const int sp = gemm_fwd_splits(M, N, K);
   return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
-  const int sp = gemm_bwd_splits(M, N, K, rr);
-  return sp > 1 ? (size_t)sp * M * K * sizeof(float) : 0;
+  return gemm_bwd_part_bytes(M, N, K, rr) + (LSQ_BWD_PP && rr > 0 ? (size_t)rr * K * 2 : 0);
 }
 
 int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
@@ -1094,11 +1324,20 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
             "gemm_bwd: N=%d and rank %d must be multiples of 8", p.N, p.rr);
   if (p.M == 0 || p.K == 0) return LSQ_OK;
   p.splits = gemm_bwd_splits(p.M, p.N, p.K, p.rr);
-  if (p.splits > 1) {
-    LSQ_CHECK(ws && ws_bytes >= gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr), LSQ_ERR_WORKSPACE,
-              "gemm_bwd: split-K needs %zu bytes of workspace", gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr));
-    p.part = static_cast<float*>(ws);
+  const size_t need = gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr);
+  LSQ_CHECK(need == 0 || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "gemm_bwd: needs %zu bytes of workspace",
+            need);
+  if (p.splits > 1) p.part = static_cast<float*>(ws);
+#if LSQ_BWD_PP
+  if (p.rr > 0) {
+    uint16_t* alt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + gemm_bwd_part_bytes(p.M, p.N, p.K, p.rr));
+    const int64_t nel = (int64_t)p.rr * p.K;
+    int t0 = prof_begin(s);
+    transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, s>>>(p.Al, p.rr, p.K, alt);
+    prof_end(t0, s, PROF_OTHER, 0.0, 4.0 * nel);
+    p.AlT = alt;
   }
+#endif
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
@@ -1120,14 +1359,14 @@ size_t lora_down_ws_bytes(int M, int K, int rr) {
 }
 
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, float* ws, size_t ws_bytes, hipStream_t st) {
+              int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(rr >= 1 && rr <= 64 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr, K);
   if (M == 0) return LSQ_OK;
   LSQ_CHECK(ws && ws_bytes >= lora_down_ws_bytes(M, K, rr), LSQ_ERR_WORKSPACE, "lora_down: workspace too small");
   const int nch = (K + KCHUNK - 1) / KCHUNK;
   int tok = prof_begin(st);
   lora_down_kernel<<<dim3((M + 15) / 16, nch), NTHREADS, 0, st>>>(X, ldx, M, K, A, rr, ws);
-  lora_finish_kernel<<<(M * rr + 255) / 256, 256, 0, st>>>(ws, nch, M, rr, s, U, ldu, 0);
+  lora_finish_kernel<<<(M * rr + 255) / 256, 256, 0, st>>>(ws, nch, M, rr, s, U, ldu, U32, ldu32);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)K * rr, 2.0 * M * (double)K + 2.0 * rr * K + 2.0 * M * rr);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
@@ -1154,7 +1393,7 @@ size_t lora_g_ws_bytes(int M, int N, int r) {
 }
 
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, float* ws, size_t ws_bytes, hipStream_t st) {
+           float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4, LSQ_ERR_SHAPE, "lora_g: bad rank/segments");
   if (M == 0) return LSQ_OK;
   LSQ_CHECK(ws && ws_bytes >= lora_g_ws_bytes(M, N, r), LSQ_ERR_WORKSPACE, "lora_g: workspace too small");
@@ -1179,7 +1418,7 @@ int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int
     c0 = c1;
   }
   const int64_t nfin = (int64_t)M * r * sf.n;
-  lora_finish_segs_kernel<<<(unsigned)((nfin + 255) / 256), 256, 0, st>>>(part, sf, M, r, s, G, ldg);
+  lora_finish_segs_kernel<<<(unsigned)((nfin + 255) / 256), 256, 0, st>>>(part, sf, M, r, s, G, ldg, G32, ldg32);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)N * r, 2.0 * M * (double)N + 4.0 * N * r + 2.0 * M * r * nseg);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
@@ -1192,14 +1431,14 @@ int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream
   double flops = 0, bytes = 0;
   for (int i = 0; i < ntasks; ++i) {
     const TnTask& t = tasks[i];
-    LSQ_CHECK(t.ns >= 8 && t.ns <= 64 && t.ns % 8 == 0 && t.nl % 4 == 0 && t.ldl % 4 == 0 && t.lds % 8 == 0 &&
+    LSQ_CHECK(t.ns >= 8 && t.ns <= 64 && t.ns % 8 == 0 && t.nl % 4 == 0 && t.ldl % 4 == 0 && t.lds % 4 == 0 &&
                   (reinterpret_cast<uintptr_t>(t.S) & 15) == 0 && (reinterpret_cast<uintptr_t>(t.L) & 7) == 0,
               LSQ_ERR_SHAPE, "lora_grads: task %d shape/alignment", i);
     bt.t[i] = t;
     bt.t[i].tile0 = tiles;
     tiles += ((t.nl + 255) / 256) * ((t.ns + 15) / 16);
     flops += 2.0 * M * (double)t.ns * t.nl;
-    bytes += 2.0 * M * (double)(t.ns + t.nl) + 4.0 * t.ns * t.nl;
+    bytes += 4.0 * M * (double)t.ns + 2.0 * M * (double)t.nl + 4.0 * t.ns * t.nl;
   }
   bt.ntasks = ntasks;
   bt.M = M;
@@ -1229,10 +1468,10 @@ size_t lora_tn_ws_bytes(int M, int ns, int nl) {
   return sp > 1 ? (size_t)sp * ns * nl * sizeof(float) : 0;
 }
 
-int lora_tn(const uint16_t* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
+int lora_tn(const float* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
             float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(ns >= 8 && ns <= 64 && ns % 8 == 0, LSQ_ERR_SHAPE, "lora_tn: small dim %d unsupported", ns);
-  LSQ_CHECK(nl % 4 == 0 && ldl % 4 == 0 && lds_ % 8 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0, LSQ_ERR_SHAPE,
+  LSQ_CHECK(nl % 4 == 0 && ldl % 4 == 0 && lds_ % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0, LSQ_ERR_SHAPE,
             "lora_tn: large dim must be a multiple of 4, small rows 16-byte aligned");
   const int splits = tn_splits(M, nl, ns);
   const int rows_per_split = (M + splits - 1) / splits;
@@ -1293,6 +1532,7 @@ extern "C" {
 size_t nf4_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
   const size_t el = dtype == LSQ_F32 ? 4 : 2;
   size_t b = align256(M * r * el) * 2             // U (recomputed or forward scratch) and G
+             + (dtype == LSQ_F32 ? 0 : align256(M * r * 4) * 2)   // their unrounded float32 copies
              + align256(std::max(lora_down_ws_bytes((int)M, (int)K, r), lora_g_ws_bytes((int)M, (int)N, r)));
   b += align256(lora_tn_ws_bytes((int)M, r, (int)K)) + align256(lora_tn_ws_bytes((int)M, r, (int)N));
   b += align256(std::max(gemm_fwd_ws_bytes((int)M, (int)N, (int)K), gemm_bwd_ws_bytes((int)M, (int)N, (int)K, r)));
@@ -1333,7 +1573,7 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
   const size_t lw_off = align256((size_t)Mi * r * 2) * 2;
   const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
   if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale, U,
-                        r, reinterpret_cast<float*>(static_cast<char*>(ws) + lw_off), lw_bytes, s))
+                        r, nullptr, 0, reinterpret_cast<float*>(static_cast<char*>(ws) + lw_off), lw_bytes, s))
     return e;
   const size_t part_off = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype) - 256 -
                           align256(std::max(gemm_fwd_ws_bytes(Mi, w.N, w.K), gemm_bwd_ws_bytes(Mi, w.N, w.K, r)));
@@ -1382,6 +1622,14 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   wsp += align256((size_t)Mi * r * el);
   void* Gw = wsp;
   wsp += align256((size_t)Mi * r * el);
+  float* U32 = nullptr;
+  float* G32 = nullptr;
+  if (dtype != LSQ_F32) {
+    U32 = reinterpret_cast<float*>(wsp);
+    wsp += align256((size_t)Mi * r * 4);
+    G32 = reinterpret_cast<float*>(wsp);
+    wsp += align256((size_t)Mi * r * 4);
+  }
   float* lw = reinterpret_cast<float*>(wsp);
   const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
   wsp += lw_bytes;
@@ -1417,18 +1665,20 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
     LSQ_HIP(hipGetLastError());
     return LSQ_OK;
   }
-  const uint16_t* U = static_cast<const uint16_t*>(U_in);
-  if (!U) {
+  if (U_in) {
+    // the caller's bf16 U: its float32 image feeds dB (no unrounded copy exists)
+    const int64_t nu = (int64_t)Mi * r;
+    if (nu > 0) bf16_to_f32_kernel<<<(unsigned)((nu + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(U_in), nu, U32);
+  } else {
     if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale,
-                          static_cast<uint16_t*>(Uw), r, lw, lw_bytes, s))
+                          static_cast<uint16_t*>(Uw), r, U32, r, lw, lw_bytes, s))
       return e;
-    U = static_cast<const uint16_t*>(Uw);
   }
   uint16_t* G = static_cast<uint16_t*>(Gw);
   SegEnds segs{};
   segs.end[0] = w.N;
   if (int e = lora_g(static_cast<const uint16_t*>(dY), w.N, Mi, w.N, static_cast<const uint16_t*>(B), r, 1, segs,
-                     scale, G, r, lw, lw_bytes, s))
+                     scale, G, r, G32, r, lw, lw_bytes, s))
     return e;
   BwdParams p{};
   p.dY = static_cast<const uint16_t*>(dY);
@@ -1446,9 +1696,10 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   p.out = dX;
   p.ldc = w.K;
   if (int e = gemm_bwd(p, EPI_BF16, s, part, part_bytes)) return e;
-  if (int e = lora_tn(G, r, r, static_cast<const uint16_t*>(X), w.K, w.K, Mi, true, dA, w.K, accumulate, tn1, tn1_b, s))
+  if (int e = lora_tn(G32, r, r, static_cast<const uint16_t*>(X), w.K, w.K, Mi, true, dA, w.K, accumulate, tn1, tn1_b,
+                      s))
     return e;
-  return lora_tn(U, r, r, static_cast<const uint16_t*>(dY), w.N, w.N, Mi, false, dB, r, accumulate, tn2, tn2_b, s);
+  return lora_tn(U32, r, r, static_cast<const uint16_t*>(dY), w.N, w.N, Mi, false, dB, r, accumulate, tn2, tn2_b, s);
 }
 
 }  // extern "C"

@@ -119,6 +119,8 @@ struct LayerWs {
   uint16_t* m;        // [T, I]
   uint16_t* U_d;      // [T, r]
   // backward only
+  float* U32[4];      // unrounded U of each group (adapter-gradient inputs)
+  float* G32;         // [T, 3r] unrounded G
   float* attn_f32;    // [T, Nq] attention output in float32 (recompute pass)
   uint16_t* dy_b;     // [T, H] bf16 copy of an upstream residual gradient
   uint16_t* G;        // [T, 3r]
@@ -196,6 +198,9 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd)
   w.lws_bytes = lws_need(d, (int)T);
   w.lws = static_cast<float*>(take(w.lws_bytes));
   if (bwd) {
+    const int ur[4] = {3, 1, 2, 1};
+    for (int g = 0; g < 4; ++g) w.U32[g] = static_cast<float*>(take(4 * T * ur[g] * d.r));
+    w.G32 = static_cast<float*>(take(4 * T * 3 * d.r));
     w.attn_f32 = static_cast<float*>(take(4 * T * d.Nq));
     w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
     w.G = static_cast<uint16_t*>(take(2 * T * 3 * d.r));
@@ -312,7 +317,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   TRY(rope_table(S, d.hd, c->rope_theta, w.rope, s));
   // attention block
   TRY(rmsnorm_fwd(x_in, bv.norm1, T, d.H, c->rms_eps, w.xn1, nullptr, s));
-  TRY(lora_down(w.xn1, d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.xn1, d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.U32[0], 3 * r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.xn1, T, bv.w[0], w.U_qkv, 3 * r, lv.B[0], r);
     p.nseg = 3;
@@ -331,7 +336,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
                reinterpret_cast<const float2*>(w.rope), w.attn_f32};
     TRY(attention_fwd(a, B, s));
   }
-  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.attn, T, bv.w[1], w.U_o, r, lv.B[1], r);
     p.resid = x_in;
@@ -340,7 +345,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   }
   // MLP block
   TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, nullptr, s));
-  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, s));
   {
     FwdParams p = fwd_params(w.xn2, T, bv.w[2], w.U_gu, 2 * r, lv.B[2], r);
     p.nseg = 2;
@@ -352,7 +357,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   TRY(swiglu_fwd(w.gu, T, d.I, w.m, s));
-  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.U32[3], r, w.lws, w.lws_bytes, s));
   if (x_out) {
     FwdParams p = fwd_params(w.m, T, bv.w[3], w.U_d, r, lv.B[3], r);
     p.resid = w.h;
@@ -363,8 +368,8 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
 }
 
 // dA of the whole stacked group (G^T X, one task) and dB of each segment
-// (dY_seg^T U_seg), in one launch.
-static int adapter_grads(const Dims& d, int T, const uint16_t* G, int ldg, const uint16_t* U, int ldu,
+// (dY_seg^T U_seg), in one launch, from the unrounded float32 G and U.
+static int adapter_grads(const Dims& d, int T, const float* G, int ldg, const float* U, int ldu,
                          const uint16_t* X, int Kx, const uint16_t* dY, int ldy, int nseg, const int* seg_end,
                          float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
   const int r = d.r;
@@ -402,7 +407,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- down projection: out = h + down(m)
   TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[3], r, 1, one, sc, w.G, r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[3], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[3], w.G, r, lv.A[3], r);
     p.out = w.dm;
@@ -410,14 +415,14 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   }
   {
     const int se[1] = {d.H};
-    TRY(adapter_grads(d, T, w.G, r, w.U_d, r, w.m, d.I, w.dy_b, d.H, 1, se, gA[3], gB[3], accumulate, w, s));
+    TRY(adapter_grads(d, T, w.G32, r, w.U32[3], r, w.m, d.I, w.dy_b, d.H, 1, se, gA[3], gB[3], accumulate, w, s));
   }
   // ---- SwiGLU and gate/up
   TRY(swiglu_bwd(w.gu, w.dm, T, d.I, w.dgu, s));
   SegEnds two{};
   two.end[0] = d.I;
   two.end[1] = 2 * d.I;
-  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.B[2], r, 2, two, sc, w.G, 2 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.B[2], r, 2, two, sc, w.G, 2 * r, w.G32, 2 * r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dgu, T, bv.w[2], w.G, 2 * r, lv.A[2], 2 * r);
     p.out = w.dxn;
@@ -425,14 +430,14 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   }
   {
     const int se[2] = {d.I, 2 * d.I};
-    TRY(adapter_grads(d, T, w.G, 2 * r, w.U_gu, 2 * r, w.xn2, d.H, w.dgu, 2 * d.I, 2, se, gA[2], gB[2], accumulate,
+    TRY(adapter_grads(d, T, w.G32, 2 * r, w.U32[2], 2 * r, w.xn2, d.H, w.dgu, 2 * d.I, 2, se, gA[2], gB[2], accumulate,
                       w, s));
   }
   // dh = dout + rmsnorm2'(dxn2)
   TRY(rmsnorm_bwd(w.h, bv.norm2, w.dxn, dx_out, T, d.H, c->rms_eps, w.dh, w.dy_b, s));
   // ---- o projection
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[1], r, 1, one, sc, w.G, r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[1], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[1], w.G, r, lv.A[1], r);
     p.out = w.dattn;
@@ -440,7 +445,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   }
   {
     const int se[1] = {d.H};
-    TRY(adapter_grads(d, T, w.G, r, w.U_o, r, w.attn, d.Nq, w.dy_b, d.H, 1, se, gA[1], gB[1], accumulate, w, s));
+    TRY(adapter_grads(d, T, w.G32, r, w.U32[1], r, w.attn, d.Nq, w.dy_b, d.H, 1, se, gA[1], gB[1], accumulate, w, s));
   }
   // ---- attention (rotary applied inside, in float32)
   {
@@ -453,7 +458,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   three.end[0] = d.Nq;
   three.end[1] = d.Nq + d.Nkv;
   three.end[2] = d.Nqkv;
-  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.B[0], r, 3, three, sc, w.G, 3 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.B[0], r, 3, three, sc, w.G, 3 * r, w.G32, 3 * r, w.lws, w.lws_bytes, s));
   {
     BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], 3 * r);
     p.out = w.dxn;
@@ -461,7 +466,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   }
   {
     const int se[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
-    TRY(adapter_grads(d, T, w.G, 3 * r, w.U_qkv, 3 * r, w.xn1, d.H, w.dqkv, d.Nqkv, 3, se, gA[0], gB[0], accumulate,
+    TRY(adapter_grads(d, T, w.G32, 3 * r, w.U32[0], 3 * r, w.xn1, d.H, w.dqkv, d.Nqkv, 3, se, gA[0], gB[0], accumulate,
                       w, s));
   }
   // dx = dh + rmsnorm1'(dxn1)

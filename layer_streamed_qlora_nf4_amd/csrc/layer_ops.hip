@@ -11,6 +11,8 @@
 #include "common.h"
 #include "layer_ops.h"
 
+#include <cfloat>
+
 namespace lsq {
 namespace {
 
@@ -617,39 +619,70 @@ __global__ void embed_kernel(const int32_t* __restrict__ ids, const uint16_t* __
 // One workgroup per row t of logits [T, V] (float32).  Rows whose position is
 // the last of its sequence have no target: zero loss, zero gradient.
 // loss_rows[t] = lse - logit[target]; dlogits[t] = bf16((softmax - onehot) / count).
-__global__ void __launch_bounds__(256) ce_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
-                                                 int T, int S, int V, float inv_count, float* __restrict__ loss_rows,
-                                                 uint16_t* __restrict__ dlogits, uint16_t* __restrict__ dlogits_lo) {
-  __shared__ float red[4];
+// One row of logits per workgroup (V % 4 == 0).  Pass 1 keeps a running
+// (max, sum of exp) pair per thread over float4 loads and merges the pairs in
+// a fixed order; pass 2 writes dlogits (and its bf16 remainder) four at a time.
+constexpr int kCeThreads = 512;
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+__global__ void __launch_bounds__(kCeThreads) ce_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
+                                                        int T, int S, int V, float inv_count, float* __restrict__ loss_rows,
+                                                        uint16_t* __restrict__ dlogits, uint16_t* __restrict__ dlogits_lo) {
+  constexpr int NW = kCeThreads / 64;
+  __shared__ float red_m[NW], red_s[NW];
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* row = logits + (int64_t)t * V;
-  const bool has_target = (t % S) != S - 1;
-  const int target = has_target ? ids[t + 1] : -1;
-  float mx = -INFINITY;
-  for (int i = tid; i < V; i += 256) mx = fmaxf(mx, row[i]);
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  const int V4 = V / 4;
+  // an out-of-range id (flagged by the embedding kernel) contributes no loss
+  const int nxt = (t % S) != S - 1 ? ids[t + 1] : -1;
+  const bool has_target = nxt >= 0 && nxt < V;
+  const int target = has_target ? nxt : -1;
+  float m = -FLT_MAX, sum = 0.f;
+  for (int i = tid; i < V4; i += kCeThreads) {
+    const float4 x = row4[i];
+    const float mx4 = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+    if (mx4 > m) {
+      sum *= __expf(m - mx4);
+      m = mx4;
+    }
+    sum += ((__expf(x.x - m) + __expf(x.y - m)) + __expf(x.z - m)) + __expf(x.w - m);
+  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) red[w] = mx;
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(sum, o, 64);
+    lse_merge(m, sum, m2, s2);
+  }
+  if (lane == 0) {
+    red_m[w] = m;
+    red_s[w] = sum;
+  }
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float sum = 0.f;
-  for (int i = tid; i < V; i += 256) sum += __expf(row[i] - mx);
-  sum = warp_sum(sum);
-  if (lane == 0) red[w] = sum;
-  __syncthreads();
-  sum = ((red[0] + red[1]) + red[2]) + red[3];
-  const float lse = mx + __logf(sum);
-  uint16_t* drow = dlogits + (int64_t)t * V;
-  uint16_t* lrow = dlogits_lo ? dlogits_lo + (int64_t)t * V : nullptr;
+  m = red_m[0];
+  sum = red_s[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) lse_merge(m, sum, red_m[k], red_s[k]);
+  const float lse = m + __logf(sum);
   const float inv_sum = 1.f / sum;
-  for (int i = tid; i < V; i += 256) {
-    float g = 0.f;
-    if (has_target) g = (__expf(row[i] - mx) * inv_sum - (i == target ? 1.f : 0.f)) * inv_count;
-    const uint16_t hb = f32_to_bf16_bits(g);
-    drow[i] = hb;
-    if (lrow) lrow[i] = f32_to_bf16_bits(g - bf16_bits_to_f32(hb));
+  uint2* drow = reinterpret_cast<uint2*>(dlogits + (int64_t)t * V);
+  uint2* lrow = dlogits_lo ? reinterpret_cast<uint2*>(dlogits_lo + (int64_t)t * V) : nullptr;
+  for (int i = tid; i < V4; i += kCeThreads) {
+    const float4 x = row4[i];
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float g = 0.f;
+      if (has_target) g = (__expf(xv[c] - m) * inv_sum - (4 * i + c == target ? 1.f : 0.f)) * inv_count;
+      hb[c] = f32_to_bf16_bits(g);
+      lb[c] = f32_to_bf16_bits(g - bf16_bits_to_f32(hb[c]));
+    }
+    drow[i] = make_uint2(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16));
+    if (lrow) lrow[i] = make_uint2(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16));
   }
   if (tid == 0) loss_rows[t] = has_target ? lse - row[target] : 0.f;
 }
@@ -811,7 +844,7 @@ int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, 
   const int T = B * S;
   if (T == 0) return LSQ_OK;
   const float inv_count = S > 1 ? 1.f / (float)(B * (S - 1)) : 0.f;
-  ce_kernel<<<T, 256, 0, s>>>(logits, ids, T, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
+  ce_kernel<<<T, kCeThreads, 0, s>>>(logits, ids, T, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
   loss_sum_kernel<<<1, 256, 0, s>>>(loss_rows, T, inv_count, loss);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

@@ -48,7 +48,9 @@ typedef enum {
   LSQ_ERR_HIP = -6,       /* a HIP runtime call failed (message says which) */
   LSQ_ERR_STATE = -7,     /* pool misuse: acquire of a layer never fetched, ... */
   LSQ_ERR_REFUSED = -8,   /* pre-flight: predicted peak exceeds free VRAM */
-  LSQ_ERR_WORKSPACE = -9  /* workspace smaller than the size query returns */
+  LSQ_ERR_WORKSPACE = -9, /* workspace smaller than the size query returns */
+  LSQ_ERR_IO = -10        /* a store file could not be written or read, is not a store,
+                             or fails its checksums                        */
 } lsq_status;
 
 const char* lsq_last_error(void);
@@ -94,8 +96,9 @@ int nf4_dequantize(const void* packed_dev, const float* absmax_dev, int64_t n_ou
  * No gradient for W or the bias: the base is frozen, yet the backward still
  * needs W to push the gradient to X (LS-docs "How it works").
  * Precision: LSQ_BF16 runs bf16 MFMA with float32 accumulation; U and G are
- * rounded to bf16 once.  LSQ_F32 runs float32 end to end (dequantized weights
- * are the exact float32 products).
+ * rounded to bf16 once where they enter an MFMA (Y and dX), while dA and dB
+ * are reduced in float32 from their unrounded values.  LSQ_F32 runs float32
+ * end to end (dequantized weights are the exact float32 products).
  */
 typedef struct {
   int32_t kind;          /* LSQ_W_NF4 or LSQ_W_BF16                          */
@@ -208,6 +211,23 @@ typedef struct {
  * LSQ_ERR_NONFINITE if any weight is NaN/Inf. */
 int shard_store_write_layer(lsq_store* store, int32_t layer, const lsq_layer_src* src,
                             void* staging_dev, size_t staging_bytes, void* stream);
+
+/* Shard cache on disk (LS-docs "Shard cache": the rewrite happens once,
+ * offline, and a cache whose quantisation or shapes differ is re-sharded, not
+ * streamed).  File layout: a 4 KiB header (magic "LSQSTORE", format version,
+ * the blob-shaping fields of the config, blob bytes, layer count), a table of
+ * one 64-bit checksum per layer padded to 4 KiB, then the blobs back to back.
+ * shard_store_save writes path + ".tmp" and renames it over path, so an
+ * interrupted save never leaves a file that loads.  Host-only calls (no GPU
+ * work); LSQ_ERR_IO on any file error. */
+int shard_store_save(const lsq_store* store, const char* path);
+/* Reads a saved store into a new host arena (page-locked per `flags`, as in
+ * shard_store_create).  expect (nullable): the config the caller will stream
+ * with; a file whose hidden, heads, kv heads, head_dim, intermediate, layers,
+ * qkv_bias or weight_kind differ is refused with LSQ_ERR_STATE and a message
+ * naming the first differing field.  A short file, a bad magic, a blob header
+ * that names another layer or a checksum mismatch is LSQ_ERR_IO. */
+int shard_store_load(const char* path, const lsq_model_cfg* expect, int32_t flags, lsq_store** out);
 
 /* ------------------------------------------------------ layer pool (a2, a5)
  * N pre-allocated VRAM slots (2..8, default 2) and a dedicated copy stream:

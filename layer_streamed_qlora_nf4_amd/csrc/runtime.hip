@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <string>
 #include <vector>
 
 #include "common.h"
@@ -88,6 +89,153 @@ void shard_store_destroy(lsq_store* st) {
   else
     free(st->host);
   delete st;
+}
+
+// ------------------------------------------------------------------ shard cache file
+namespace {
+constexpr int32_t kStoreFileVersion = 1;
+struct StoreFileHeader {
+  char magic[8];  // "LSQSTORE"
+  int32_t version;
+  int32_t hidden, n_heads, n_kv_heads, head_dim, intermediate, n_layers, qkv_bias, weight_kind;
+  uint64_t layer_bytes;
+};
+static_assert(sizeof(StoreFileHeader) <= 4096, "store header fits its page");
+
+// 64-bit checksum of a blob: a multiply-xorshift mix over 8-byte words (blob
+// sizes are multiples of 4 KiB), seeded with the layer index.
+uint64_t blob_checksum(const char* p, uint64_t n, int layer) {
+  uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)layer;
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
+  for (uint64_t i = 0; i < n / 8; ++i) {
+    h ^= w[i] + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xBF58476D1CE4E5B9ull;
+  }
+  h ^= h >> 31;
+  return h;
+}
+
+uint64_t table_bytes(int n_layers) { return up(8ull * n_layers, 4096); }
+
+int write_all(FILE* f, const void* p, size_t n) { return fwrite(p, 1, n, f) == n ? 0 : -1; }
+int read_all(FILE* f, void* p, size_t n) { return fread(p, 1, n, f) == n ? 0 : -1; }
+}  // namespace
+
+int shard_store_save(const lsq_store* st, const char* path) {
+  LSQ_CHECK(st && path, LSQ_ERR_INVALID, "shard_store_save: null pointer");
+  const lsq_model_cfg& c = st->cfg;
+  std::vector<char> page(4096, 0);
+  StoreFileHeader hdr{};
+  memcpy(hdr.magic, "LSQSTORE", 8);
+  hdr.version = kStoreFileVersion;
+  hdr.hidden = c.hidden;
+  hdr.n_heads = c.n_heads;
+  hdr.n_kv_heads = c.n_kv_heads;
+  hdr.head_dim = c.head_dim;
+  hdr.intermediate = c.intermediate;
+  hdr.n_layers = c.n_layers;
+  hdr.qkv_bias = c.qkv_bias;
+  hdr.weight_kind = c.weight_kind;
+  hdr.layer_bytes = st->layer_bytes;
+  memcpy(page.data(), &hdr, sizeof(hdr));
+  std::vector<char> table(table_bytes(c.n_layers), 0);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const uint64_t sum = blob_checksum(st->host + (uint64_t)l * st->layer_bytes, st->layer_bytes, l);
+    memcpy(table.data() + 8ull * l, &sum, 8);
+  }
+  std::string tmp = std::string(path) + ".tmp";
+  FILE* f = fopen(tmp.c_str(), "wb");
+  LSQ_CHECK(f, LSQ_ERR_IO, "shard_store_save: cannot create %s", tmp.c_str());
+  bool ok = write_all(f, page.data(), page.size()) == 0 && write_all(f, table.data(), table.size()) == 0 &&
+            write_all(f, st->host, st->layer_bytes * (uint64_t)c.n_layers) == 0;
+  ok = (fclose(f) == 0) && ok;
+  if (!ok) {
+    remove(tmp.c_str());
+    return fail(LSQ_ERR_IO, "shard_store_save: writing %s failed", tmp.c_str());
+  }
+  if (rename(tmp.c_str(), path) != 0) {
+    remove(tmp.c_str());
+    return fail(LSQ_ERR_IO, "shard_store_save: cannot rename %s to %s", tmp.c_str(), path);
+  }
+  return LSQ_OK;
+}
+
+int shard_store_load(const char* path, const lsq_model_cfg* expect, int32_t flags, lsq_store** out) {
+  LSQ_CHECK(path && out, LSQ_ERR_INVALID, "shard_store_load: null pointer");
+  FILE* f = fopen(path, "rb");
+  LSQ_CHECK(f, LSQ_ERR_IO, "shard_store_load: cannot open %s", path);
+  std::vector<char> page(4096);
+  StoreFileHeader hdr{};
+  if (read_all(f, page.data(), page.size()) != 0) {
+    fclose(f);
+    return fail(LSQ_ERR_IO, "shard_store_load: %s is shorter than a store header", path);
+  }
+  memcpy(&hdr, page.data(), sizeof(hdr));
+  if (memcmp(hdr.magic, "LSQSTORE", 8) != 0 || hdr.version != kStoreFileVersion) {
+    fclose(f);
+    return fail(LSQ_ERR_IO, "shard_store_load: %s is not a version-%d shard store", path, kStoreFileVersion);
+  }
+  lsq_model_cfg c{};
+  if (expect) c = *expect;
+  const struct {
+    const char* name;
+    int32_t file, want;
+  } fields[] = {{"hidden", hdr.hidden, c.hidden},           {"n_heads", hdr.n_heads, c.n_heads},
+                {"n_kv_heads", hdr.n_kv_heads, c.n_kv_heads}, {"head_dim", hdr.head_dim, c.head_dim},
+                {"intermediate", hdr.intermediate, c.intermediate}, {"n_layers", hdr.n_layers, c.n_layers},
+                {"qkv_bias", hdr.qkv_bias, c.qkv_bias},     {"weight_kind", hdr.weight_kind, c.weight_kind}};
+  if (expect) {
+    for (const auto& fd : fields) {
+      if (fd.file != fd.want) {
+        fclose(f);
+        return fail(LSQ_ERR_STATE, "shard_store_load: %s was written for %s=%d but the run asks for %d; re-shard",
+                    path, fd.name, fd.file, fd.want);
+      }
+    }
+  } else {
+    // no expectation: take the shape from the file and plausible defaults for the rest
+    c.hidden = hdr.hidden;
+    c.n_heads = hdr.n_heads;
+    c.n_kv_heads = hdr.n_kv_heads;
+    c.head_dim = hdr.head_dim;
+    c.intermediate = hdr.intermediate;
+    c.n_layers = hdr.n_layers;
+    c.qkv_bias = hdr.qkv_bias;
+    c.weight_kind = hdr.weight_kind;
+    c.vocab = 8;
+    c.lora_r = 8;
+    c.rms_eps = 1e-5f;
+    c.rope_theta = 1e4f;
+    c.lora_scale = 1.f;
+  }
+  lsq_store* st = nullptr;
+  if (int e = shard_store_create(&c, flags, &st)) {
+    fclose(f);
+    return e;
+  }
+  auto bad = [&](const char* why, int layer) {
+    fclose(f);
+    shard_store_destroy(st);
+    return fail(LSQ_ERR_IO, "shard_store_load: %s: %s (layer %d)", path, why, layer);
+  };
+  if (hdr.layer_bytes != st->layer_bytes) return bad("blob size differs from this library's layout", -1);
+  std::vector<char> table(table_bytes(c.n_layers));
+  if (read_all(f, table.data(), table.size()) != 0) return bad("truncated checksum table", -1);
+  for (int l = 0; l < c.n_layers; ++l) {
+    char* blob = st->host + (uint64_t)l * st->layer_bytes;
+    if (read_all(f, blob, st->layer_bytes) != 0) return bad("truncated", l);
+    uint64_t want = 0;
+    memcpy(&want, table.data() + 8ull * l, 8);
+    if (blob_checksum(blob, st->layer_bytes, l) != want) return bad("checksum mismatch", l);
+    BlobHeader bh{};
+    memcpy(&bh, blob, sizeof(bh));
+    if (memcmp(bh.magic, "LSQBLOB1", 8) != 0 || bh.layer != l) return bad("blob header names another layer", l);
+  }
+  char extra;
+  if (fread(&extra, 1, 1, f) != 0) return bad("trailing bytes after the last blob", c.n_layers - 1);
+  fclose(f);
+  *out = st;
+  return LSQ_OK;
 }
 
 int32_t shard_store_is_pinned(const lsq_store* st) { return st && st->pinned ? 1 : 0; }

@@ -17,7 +17,8 @@ LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
 LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE = 1, 2
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",
-          -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE"}
+          -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE",
+          -10: "LSQ_ERR_IO"}
 
 
 class LsqError(RuntimeError):
@@ -95,6 +96,8 @@ _SIGS = {
     "shard_store_layer_bytes": (_U64, [_P]),
     "shard_store_layer_host": (_P, [_P, _I32]),
     "shard_store_write_layer": (C.c_int, [_P, _I32, C.POINTER(LayerSrc), _P, _SZ, _P]),
+    "shard_store_save": (C.c_int, [_P, C.c_char_p]),
+    "shard_store_load": (C.c_int, [C.c_char_p, C.POINTER(ModelCfg), _I32, C.POINTER(_P)]),
     "layer_pool_create": (C.c_int, [_P, _I32, _P, _U64, _P, _P, _I32, C.POINTER(_P)]),
     "layer_pool_destroy": (None, [_P]),
     "stream_layer_prefetch": (C.c_int, [_P, _I32]),

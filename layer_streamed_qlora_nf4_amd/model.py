@@ -55,6 +55,22 @@ class Store:
             del dev
         del staging
 
+    @classmethod
+    def load(cls, cfg, path, flags=0):
+        """A store read back from shard_store_save's file (refused if its shape differs from cfg)."""
+        self = cls.__new__(cls)
+        self.cfg = cfg
+        self.ccfg = lib.model_cfg(cfg)
+        h = C.c_void_p()
+        lib.call("shard_store_load", str(path).encode(), C.byref(self.ccfg), flags, C.byref(h))
+        self.handle = h
+        self.layer_bytes = int(lib.raw("shard_store_layer_bytes")(h))
+        self.pinned = bool(lib.raw("shard_store_is_pinned")(h))
+        return self
+
+    def save(self, path):
+        lib.call("shard_store_save", self.handle, str(path).encode())
+
     def host_blob(self, i):
         p = lib.raw("shard_store_layer_host")(self.handle, i)
         return np.ctypeslib.as_array((C.c_uint8 * self.layer_bytes).from_address(p))

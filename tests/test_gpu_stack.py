@@ -156,3 +156,25 @@ def test_step_is_deterministic_and_repeats(gpu):
     # first step copies 2L - N, every later step 2L - 2N (layer 0.. N-1 stay in their slots)
     assert st.copies == (2 * cfg.n_layers - cfg.n_buffers) + 2 * (2 * cfg.n_layers - 2 * cfg.n_buffers)
     r.close()
+
+
+def test_saved_store_reloads_and_streams_identically(gpu, tmp_path):
+    """A store written to disk and read back streams the same bytes: same loss,
+    logits and every adapter gradient, bit for bit."""
+    cfg = configs.TINY.with_(name="tiny-saved", wid=17)
+    print_case(test="store_save_load", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    path = tmp_path / "tiny.lsqstore"
+    store.save(path)
+    loaded = model.Store.load(cfg, path)
+    assert loaded.pinned
+    for i in range(cfg.n_layers):
+        assert np.array_equal(store.host_blob(i), loaded.host_blob(i))
+    a = run(cfg, "streamed", store, res, ids)
+    b = run(cfg, "streamed", loaded, res, ids)
+    exact, total = _compare_bitwise(cfg, a, b)
+    assert exact == total
+    loaded.close()
+    store.close()

@@ -154,3 +154,74 @@ def test_workspace_queries_are_consistent():
         sw = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq)
         assert 0 < lw < sw
         assert lib.raw("decoder_layer_workspace_size")(c, cfg.batch, 2 * cfg.seq) > lw
+
+
+def _fill_store_with_blobs(h, cfg, seed):
+    """Random blob bytes with a valid per-layer header (magic + layer index)."""
+    rng = np.random.default_rng(seed)
+    nbytes = lib.raw("shard_store_layer_bytes")(h)
+    blobs = []
+    for layer in range(cfg.n_layers):
+        p = lib.raw("shard_store_layer_host")(h, layer)
+        arr = np.ctypeslib.as_array((C.c_uint8 * nbytes).from_address(p))
+        arr[:] = rng.integers(0, 256, nbytes, dtype=np.uint8)
+        arr[:8] = np.frombuffer(b"LSQBLOB1", dtype=np.uint8)
+        arr[8:12] = np.frombuffer(np.int32(layer).tobytes(), dtype=np.uint8)
+        blobs.append(arr.copy())
+    return blobs
+
+
+def _store_bytes(h, cfg):
+    nbytes = lib.raw("shard_store_layer_bytes")(h)
+    return [np.ctypeslib.as_array((C.c_uint8 * nbytes).from_address(lib.raw("shard_store_layer_host")(h, l))).copy()
+            for l in range(cfg.n_layers)]
+
+
+def test_shard_store_save_load_roundtrip_and_refusals(tmp_path):
+    cfg = configs.TINY
+    h = C.c_void_p()
+    lib.call("shard_store_create", _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h))
+    blobs = _fill_store_with_blobs(h, cfg, 3)
+    path = str(tmp_path / "tiny.lsqstore")
+    lib.call("shard_store_save", h, path.encode())
+    lib.raw("shard_store_destroy")(h)
+    assert not os.path.exists(path + ".tmp")
+    size = os.path.getsize(path)
+    assert size == 4096 + 4096 + cfg.n_layers * lib.blob_layout(cfg).total_bytes
+
+    h2 = C.c_void_p()
+    lib.call("shard_store_load", path.encode(), _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h2))
+    got = _store_bytes(h2, cfg)
+    lib.raw("shard_store_destroy")(h2)
+    assert all(np.array_equal(a, b) for a, b in zip(blobs, got))
+
+    # a run asking for another shape is told which field differs (re-shard, not stream)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("shard_store_load", path.encode(), _cfg_struct(cfg.with_(intermediate=cfg.intermediate + 64)),
+                 lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h2))
+    assert e.value.status == "LSQ_ERR_STATE" and "intermediate" in str(e.value)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("shard_store_load", path.encode(), _cfg_struct(cfg.with_(quant="bf16")),
+                 lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h2))
+    assert e.value.status == "LSQ_ERR_STATE" and "weight_kind" in str(e.value)
+
+    raw = bytearray(open(path, "rb").read())
+    # one flipped byte inside layer 1's blob fails its checksum
+    bad = bytearray(raw)
+    bad[8192 + lib.blob_layout(cfg).total_bytes + 777] ^= 0x40
+    p_bad = str(tmp_path / "bad.lsqstore")
+    open(p_bad, "wb").write(bytes(bad))
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("shard_store_load", p_bad.encode(), _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h2))
+    assert e.value.status == "LSQ_ERR_IO" and "checksum" in str(e.value) and "layer 1" in str(e.value)
+    # truncated, trailing bytes, not a store
+    for name, data, word in (("short", bytes(raw[:-100]), "truncated"), ("long", bytes(raw) + b"x", "trailing"),
+                             ("magic", b"NOTSTORE" + bytes(raw[8:]), "not a version")):
+        p = str(tmp_path / f"{name}.lsqstore")
+        open(p, "wb").write(data)
+        with pytest.raises(lib.LsqError) as e:
+            lib.call("shard_store_load", p.encode(), _cfg_struct(cfg), lib.LSQ_STORE_FORCE_PAGEABLE, C.byref(h2))
+        assert e.value.status == "LSQ_ERR_IO" and word in str(e.value), (name, str(e.value))
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("shard_store_load", str(tmp_path / "missing").encode(), None, 0, C.byref(h2))
+    assert e.value.status == "LSQ_ERR_IO"

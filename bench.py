@@ -128,6 +128,7 @@ def main():
     ap.add_argument("--workload", default="llama8b-stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers", type=int, default=None)
+    ap.add_argument("--no-variants", action="store_true", help="skip the kept-activations timing")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the data-parallel path is designed "
@@ -150,7 +151,7 @@ def main():
     log(f"store: {cfg.n_layers} x {store.layer_bytes / 1e6:.2f} MB, pinned={store.pinned}, built in "
         f"{time.time() - t0:.0f} s")
     pf = lib.VramBreakdown()
-    lib.call("lsq_preflight", C.byref(lib.model_cfg(cfg)), cfg.batch, cfg.seq, cfg.n_buffers, 0, C.byref(pf))
+    lib.call("lsq_preflight", C.byref(lib.model_cfg(cfg)), cfg.batch, cfg.seq, cfg.n_buffers, 0, 0, C.byref(pf))
     runner = model.Runner(cfg, store, res)
     ids = torch.from_numpy(synth.token_ids(cfg.batch, cfg.seq, cfg.vocab, (cfg.wid, 500, 23))).cuda()
     for _ in range(a.warmup):
@@ -227,6 +228,26 @@ def main():
                                            "h100_median": 113.0}},
     }
     runner.close()
+    # stream_recompute off on the same store: kept activations, no recompute GEMMs
+    if not a.no_variants:
+        pk = lib.VramBreakdown()
+        lib.call("vram_predict_peak", C.byref(lib.model_cfg(cfg)), cfg.batch, cfg.seq, cfg.n_buffers,
+                 lib.LSQ_STEP_KEEP_ACTIVATIONS, C.byref(pk))
+        rk = model.Runner(cfg, store, res, keep_activations=True)
+        for _ in range(2):
+            rk.step(ids)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nk = max(3, a.steps // 2)
+        for _ in range(nk):
+            rk.step(ids)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        out["variants"] = {"keep_activations": {"value": round(cfg.tokens * nk / el, 2), "unit": "tok/s",
+                                                "ms_per_step": round(el / nk * 1e3, 3), "steps": nk,
+                                                "saved_activation_bytes": pk.saved_activations,
+                                                "predicted_bytes": pk.total}}
+        rk.close()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out))

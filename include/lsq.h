@@ -270,7 +270,8 @@ int layer_pool_stats(lsq_pool* pool, int32_t reset, lsq_pool_stats* out);
  * One streamed fwd+bwd step: embedding gather, L layers forward (prefetch one
  * ahead, acquire, layer forward, release), final RMSNorm, head GEMM, mean
  * next-token cross-entropy and its gradient, then L layers backward in reverse
- * with per-layer recompute, writing every adapter gradient.  Embedding, final
+ * with per-layer recompute (or kept activations), writing every adapter
+ * gradient.  Embedding, final
  * norm and head stay resident and get no gradient (LS-docs "How it works").
  * Runs on the pool's compute stream. */
 typedef struct {
@@ -282,13 +283,21 @@ typedef struct {
 } lsq_resident;
 enum {
   LSQ_STEP_FORWARD_ONLY = 1,        /* loss and logits only                      */
-  LSQ_STEP_DEBUG_EARLY_RELEASE = 2  /* control: release each layer's slot after
+  LSQ_STEP_DEBUG_EARLY_RELEASE = 2, /* control: release each layer's slot after
                                        its backward recompute and let the next
                                        copy land before its backward GEMMs, the
                                        aliasing defect the pages describe; must
                                        make gradients differ                    */
+  LSQ_STEP_KEEP_ACTIVATIONS = 4      /* stream_recompute off (LS-docs "How it
+                                       works"): keep each layer's forward
+                                       activations and skip the backward's
+                                       recompute; the backward still re-reads
+                                       every layer's weights.  Needs the larger
+                                       workspace the size query returns for it. */
 };
-size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq);
+/* Workspace of a step run with `flags` (LSQ_STEP_KEEP_ACTIVATIONS adds
+ * n_layers kept-activation regions). */
+size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t flags);
 /* ids_dev int32 [batch, seq]; loss_dev float32 [1]; logits_out float32
  * [batch*seq, vocab] (nullable). */
 int lsq_train_step(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res,
@@ -310,15 +319,17 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
  * activations and logits).  The prediction is the sum of the buffers this
  * library asks the caller to allocate, plus the caller-declared overhead. */
 typedef struct {
-  uint64_t slots, resident, adapters, checkpoints, step_workspace, total;
+  uint64_t slots, resident, adapters, checkpoints, saved_activations, step_workspace, total;
 } lsq_vram_breakdown;
+/* step_flags: the flags the step will run with (kept activations are a term
+ * of their own). */
 int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers,
-                      lsq_vram_breakdown* out);
+                      int32_t step_flags, lsq_vram_breakdown* out);
 /* LSQ_ERR_REFUSED when the prediction exceeds free VRAM.  free_override_bytes
  * > 0 replaces the device's free memory (a capped process cannot see its cap:
  * LS-docs "Run it yourself on a free Colab T4"). */
 int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers,
-                  uint64_t free_override_bytes, lsq_vram_breakdown* out);
+                  int32_t step_flags, uint64_t free_override_bytes, lsq_vram_breakdown* out);
 
 /* ------------------------------------------------------ kernel timing
  * When enabled, every launch of the timed kernel families is bracketed by

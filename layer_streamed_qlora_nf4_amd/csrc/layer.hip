@@ -169,39 +169,55 @@ static size_t lws_need(const Dims& d, int T) {
   return m;
 }
 
-static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd) {
+// The forward activations the backward reads (xn1 .. U_d, the unrounded U and
+// the float32 attention output) come from `acts` when the caller keeps them
+// per layer (no recompute), else from the workspace itself.  keep: a region
+// size query for that split (base and acts may both be null).
+static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd, void* acts = nullptr,
+                     bool keep = false, uint64_t* acts_total = nullptr) {
   const Dims d = dims_of(c);
   const uint64_t T = (uint64_t)B * S;
+  keep = keep || acts != nullptr;
   LayerWs w{};
   char* p = static_cast<char*>(base);
-  uint64_t off = 0;
+  char* pa = static_cast<char*>(acts);
+  uint64_t off = 0, aoff = 0;
   auto take = [&](uint64_t bytes) -> void* {
     void* r = base ? p + off : nullptr;
     off = up(off + std::max<uint64_t>(bytes, 1), 256);
     return r;
   };
+  auto take_act = [&](uint64_t bytes) -> void* {
+    if (!keep) return take(bytes);
+    void* r = acts ? pa + aoff : nullptr;
+    aoff = up(aoff + std::max<uint64_t>(bytes, 1), 256);
+    return r;
+  };
   w.rope = static_cast<float*>(take(8ull * S * (d.hd / 2)));
-  w.xn1 = static_cast<uint16_t*>(take(2 * T * d.H));
-  w.U_qkv = static_cast<uint16_t*>(take(2 * T * 3 * d.r));
-  w.qkv = static_cast<uint16_t*>(take(2 * T * d.Nqkv));
-  w.attn = static_cast<uint16_t*>(take(2 * T * d.Nq));
-  w.lse = static_cast<float*>(take(4ull * B * d.nh * S));
-  w.U_o = static_cast<uint16_t*>(take(2 * T * d.r));
-  w.h = static_cast<float*>(take(4 * T * d.H));
-  w.xn2 = static_cast<uint16_t*>(take(2 * T * d.H));
-  w.U_gu = static_cast<uint16_t*>(take(2 * T * 2 * d.r));
-  w.gu = static_cast<uint16_t*>(take(2 * T * 2 * d.I));
-  w.m = static_cast<uint16_t*>(take(2 * T * d.I));
-  w.U_d = static_cast<uint16_t*>(take(2 * T * d.r));
+  w.xn1 = static_cast<uint16_t*>(take_act(2 * T * d.H));
+  w.U_qkv = static_cast<uint16_t*>(take_act(2 * T * 3 * d.r));
+  w.qkv = static_cast<uint16_t*>(take_act(2 * T * d.Nqkv));
+  w.attn = static_cast<uint16_t*>(take_act(2 * T * d.Nq));
+  w.lse = static_cast<float*>(take_act(4ull * B * d.nh * S));
+  w.U_o = static_cast<uint16_t*>(take_act(2 * T * d.r));
+  w.h = static_cast<float*>(take_act(4 * T * d.H));
+  w.xn2 = static_cast<uint16_t*>(take_act(2 * T * d.H));
+  w.U_gu = static_cast<uint16_t*>(take_act(2 * T * 2 * d.r));
+  w.gu = static_cast<uint16_t*>(take_act(2 * T * 2 * d.I));
+  w.m = static_cast<uint16_t*>(take_act(2 * T * d.I));
+  w.U_d = static_cast<uint16_t*>(take_act(2 * T * d.r));
+  if (bwd || keep) {
+    const int ur[4] = {3, 1, 2, 1};
+    for (int g = 0; g < 4; ++g) w.U32[g] = static_cast<float*>(take_act(4 * T * ur[g] * d.r));
+    w.attn_f32 = static_cast<float*>(take_act(4 * T * d.Nq));
+  }
+  if (acts_total) *acts_total = aoff;
   w.gemm_bytes = gemm_need(d, (int)T);
   w.gemm = take(w.gemm_bytes);
   w.lws_bytes = lws_need(d, (int)T);
   w.lws = static_cast<float*>(take(w.lws_bytes));
   if (bwd) {
-    const int ur[4] = {3, 1, 2, 1};
-    for (int g = 0; g < 4; ++g) w.U32[g] = static_cast<float*>(take(4 * T * ur[g] * d.r));
     w.G32 = static_cast<float*>(take(4 * T * 3 * d.r));
-    w.attn_f32 = static_cast<float*>(take(4 * T * d.Nq));
     w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
     w.G = static_cast<uint16_t*>(take(2 * T * 3 * d.r));
     w.dm = static_cast<uint16_t*>(take(2 * T * d.I));
@@ -220,7 +236,14 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd)
   return w;
 }
 
-size_t layer_ws_bytes(const lsq_model_cfg* c, int B, int S) { return carve(c, B, S, nullptr, true).total; }
+size_t layer_ws_bytes(const lsq_model_cfg* c, int B, int S, bool keep) {
+  return carve(c, B, S, nullptr, true, nullptr, keep).total;
+}
+size_t layer_acts_bytes(const lsq_model_cfg* c, int B, int S) {
+  uint64_t a = 0;
+  carve(c, B, S, nullptr, true, nullptr, true, &a);
+  return a;
+}
 
 struct BlobView {
   WeightRef w[4];
@@ -475,18 +498,23 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
 }
 
 int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, int B, int S,
-              float* x_out, void* ws, hipStream_t s) {
-  LayerWs w = carve(c, B, S, ws, false);
+              float* x_out, void* ws, hipStream_t s, void* acts) {
+  LayerWs w = carve(c, B, S, ws, false, acts);
   return forward_impl(c, view_blob(c, blob), view_lora(c, lora), x_in, B, S, x_out, w, s);
 }
 
 int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, const float* dx_out,
               int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
-              const LayerHook* hook) {
-  LayerWs w = carve(c, B, S, ws, true);
+              const LayerHook* hook, void* acts) {
+  LayerWs w = carve(c, B, S, ws, true, acts);
   const BlobView bv = view_blob(c, blob);
   const LoraView lv = view_lora(c, lora);
-  TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
+  if (acts) {
+    // activations kept from this layer's forward: only the rope table is rebuilt
+    TRY(rope_table(S, dims_of(c).hd, c->rope_theta, w.rope, s));
+  } else {
+    TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
+  }
   if (hook && hook->after_recompute) TRY(hook->after_recompute(hook->ctx));
   return backward_impl(c, bv, lv, x_in, dx_out, B, S, dx_in, grad, accumulate, w, s);
 }
@@ -514,7 +542,7 @@ int lsq_lora_layout_get(const lsq_model_cfg* cfg, lsq_lora_layout* out) {
 
 size_t decoder_layer_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq) {
   if (check_cfg(cfg) || batch < 0 || seq < 0) return 0;
-  return layer_ws_bytes(cfg, batch, seq);
+  return layer_ws_bytes(cfg, batch, seq, false);
 }
 
 static int check_layer_args(const lsq_model_cfg* cfg, const void* blob, const void* lora, const void* x, int B,
@@ -524,8 +552,8 @@ static int check_layer_args(const lsq_model_cfg* cfg, const void* blob, const vo
   LSQ_CHECK(B >= 1 && S >= 1 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "decoder_layer: bad batch/seq");
   LSQ_CHECK(aligned16(blob) && aligned16(lora) && aligned16(x) && aligned16(ws), LSQ_ERR_ALIGN,
             "decoder_layer: unaligned pointer");
-  LSQ_CHECK(ws_bytes >= layer_ws_bytes(cfg, B, S), LSQ_ERR_WORKSPACE, "decoder_layer: workspace %zu < %zu",
-            ws_bytes, layer_ws_bytes(cfg, B, S));
+  LSQ_CHECK(ws_bytes >= layer_ws_bytes(cfg, B, S, false), LSQ_ERR_WORKSPACE, "decoder_layer: workspace %zu < %zu",
+            ws_bytes, layer_ws_bytes(cfg, B, S, false));
   return LSQ_OK;
 }
 
@@ -533,7 +561,7 @@ int decoder_layer_fwd(const lsq_model_cfg* cfg, const void* blob, const void* lo
                       int32_t seq, float* x_out, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_layer_args(cfg, blob, lora, x_in, batch, seq, ws, ws_bytes)) return e;
   LSQ_CHECK(x_out && aligned16(x_out) && x_out != x_in, LSQ_ERR_INVALID, "decoder_layer_fwd: bad x_out");
-  return layer_fwd(cfg, blob, lora, x_in, batch, seq, x_out, ws, as_stream(stream));
+  return layer_fwd(cfg, blob, lora, x_in, batch, seq, x_out, ws, as_stream(stream), nullptr);
 }
 
 int decoder_layer_bwd(const lsq_model_cfg* cfg, const void* blob, const void* lora, const float* x_in_saved,
@@ -543,7 +571,7 @@ int decoder_layer_bwd(const lsq_model_cfg* cfg, const void* blob, const void* lo
   LSQ_CHECK(dx_out && dx_in && lora_grad && aligned16(dx_out) && aligned16(dx_in) && aligned16(lora_grad),
             LSQ_ERR_INVALID, "decoder_layer_bwd: bad gradient pointers");
   return layer_bwd(cfg, blob, lora, x_in_saved, dx_out, batch, seq, dx_in, lora_grad, accumulate, ws,
-                   as_stream(stream), nullptr);
+                   as_stream(stream), nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -505,10 +505,13 @@ struct StepWs {
   size_t gemm_bytes;
   void* layer;       // layer workspace
   size_t layer_bytes;
+  char* acts;        // keep mode: n_layers x acts_bytes of kept forward activations
+  size_t acts_bytes;
   size_t total;
 };
 
-StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base) {
+StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flags) {
+  const bool keep = flags & LSQ_STEP_KEEP_ACTIVATIONS;
   const uint64_t T = (uint64_t)B * S, H = c->hidden, V = c->vocab;
   StepWs w{};
   uint64_t off = 0;
@@ -531,8 +534,12 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base) {
   w.bad = static_cast<int32_t*>(take(4));
   w.gemm_bytes = std::max(gemm_fwd_ws_bytes((int)T, (int)V, (int)H), gemm_bwd_ws_bytes((int)T, (int)V, (int)H, 0));
   w.gemm = take(w.gemm_bytes);
-  w.layer_bytes = layer_ws_bytes(c, B, S);
+  w.layer_bytes = layer_ws_bytes(c, B, S, keep);
   w.layer = take(w.layer_bytes);
+  if (keep) {
+    w.acts_bytes = layer_acts_bytes(c, B, S);
+    w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)c->n_layers));
+  }
   w.total = off;
   return w;
 }
@@ -560,9 +567,9 @@ int early_release_hook(void* vctx) {
 
 extern "C" {
 
-size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq) {
+size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t flags) {
   if (check_cfg(cfg) || batch < 1 || seq < 1) return 0;
-  return carve_step(cfg, batch, seq, nullptr).total;
+  return carve_step(cfg, batch, seq, nullptr, flags).total;
 }
 
 int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
@@ -575,13 +582,17 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
   LSQ_CHECK(B >= 1 && S >= 2 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "lsq_train_step: bad batch/seq");
   LSQ_CHECK(memcmp(cfg, &pool->store->cfg, sizeof(lsq_model_cfg)) == 0, LSQ_ERR_INVALID,
             "lsq_train_step: cfg differs from the store's");
-  const size_t need = carve_step(cfg, B, S, nullptr).total;
-  LSQ_CHECK(ws_bytes >= need, LSQ_ERR_WORKSPACE, "lsq_train_step: workspace %zu < %zu", ws_bytes, need);
+  LSQ_CHECK((flags & ~(LSQ_STEP_FORWARD_ONLY | LSQ_STEP_DEBUG_EARLY_RELEASE | LSQ_STEP_KEEP_ACTIVATIONS)) == 0,
+            LSQ_ERR_INVALID, "lsq_train_step: unknown flags 0x%x", flags);
+  const size_t need = carve_step(cfg, B, S, nullptr, flags).total;
+  LSQ_CHECK(ws_bytes >= need, LSQ_ERR_WORKSPACE, "lsq_train_step: workspace %zu < %zu (flags 0x%x)", ws_bytes, need,
+            flags);
   LSQ_CHECK(!(flags & LSQ_STEP_DEBUG_EARLY_RELEASE) || (cfg->n_layers >= 2 && !pool->resident), LSQ_ERR_INVALID,
             "early-release control needs a streamed pool and >= 2 layers");
   const int L = cfg->n_layers, T = B * S, H = cfg->hidden, V = cfg->vocab;
   hipStream_t s = pool->compute;
-  StepWs w = carve_step(cfg, B, S, ws);
+  StepWs w = carve_step(cfg, B, S, ws, flags);
+  auto acts_at = [&](int i) -> void* { return w.acts ? w.acts + (uint64_t)i * w.acts_bytes : nullptr; };
   lsq_lora_layout LL;
   lora_layout(cfg, &LL);
   const uint16_t* lora = static_cast<const uint16_t*>(res->lora);
@@ -598,7 +609,8 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     if (int e = layer_pool_acquire(pool, i, &blob)) return e;
     if (i + 1 < L)
       if (int e = stream_layer_prefetch(pool, i + 1)) return e;
-    if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s))
+    if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s,
+                          acts_at(i)))
       return e;
     if (int e = layer_pool_release(pool, i)) return e;
   }
@@ -651,7 +663,9 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
   const size_t act = sizeof(float) * (size_t)T * H;
   if (x_trace) LSQ_HIP(hipMemcpyAsync(x_trace, xs, act * (L + 1), hipMemcpyDeviceToDevice, s));
   if (dx_trace) LSQ_HIP(hipMemcpyAsync(dx_trace + (size_t)L * T * H, dcur, act, hipMemcpyDeviceToDevice, s));
-  // ---- backward: the same stream of layers in reverse, recompute inside each layer
+  // ---- backward: the same stream of layers in reverse, recompute inside each
+  // layer unless its forward activations were kept (the weights are re-read
+  // either way: the backward needs W for dX)
   if (int e = stream_layer_prefetch(pool, L - 1)) return e;
   for (int i = L - 1; i >= 0; --i) {
     const void* blob = nullptr;
@@ -663,7 +677,7 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     LayerHook hook{early_release_hook, &actx};
     float* grad = res->lora_grad + (uint64_t)i * LL.layer_elems;
     if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
-                          s, early ? &hook : nullptr))
+                          s, early ? &hook : nullptr, acts_at(i)))
       return e;
     if (!early)
       if (int e = layer_pool_release(pool, i)) return e;
@@ -679,7 +693,7 @@ int lsq_train_step(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident*
 }
 
 // ================================================================== pre-flight
-int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers,
+int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers, int32_t step_flags,
                       lsq_vram_breakdown* out) {
   if (int e = check_cfg(cfg)) return e;
   LSQ_CHECK(out && batch >= 1 && seq >= 2 && n_buffers >= 2, LSQ_ERR_INVALID, "vram_predict_peak: bad arguments");
@@ -692,15 +706,18 @@ int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int3
   out->resident = 2ull * cfg->vocab * H * (cfg->tied ? 1 : 2) + 2 * H;
   out->adapters = LL.layer_elems * (uint64_t)cfg->n_layers * (2 + 4);
   out->checkpoints = 4 * T * H * (cfg->n_layers + 1);
-  out->step_workspace = carve_step(cfg, batch, seq, nullptr).total - out->checkpoints;
-  out->total = out->slots + out->resident + out->adapters + out->checkpoints + out->step_workspace + 4 * T + 64;
+  const StepWs sw = carve_step(cfg, batch, seq, nullptr, step_flags);
+  out->saved_activations = (uint64_t)sw.acts_bytes * cfg->n_layers;
+  out->step_workspace = sw.total - out->checkpoints - out->saved_activations;
+  out->total = out->slots + out->resident + out->adapters + out->checkpoints + out->saved_activations +
+               out->step_workspace + 4 * T + 64;
   return LSQ_OK;
 }
 
-int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers, uint64_t free_override,
-                  lsq_vram_breakdown* out) {
+int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t n_buffers, int32_t step_flags,
+                  uint64_t free_override, lsq_vram_breakdown* out) {
   lsq_vram_breakdown b{};
-  if (int e = vram_predict_peak(cfg, batch, seq, n_buffers, &b)) return e;
+  if (int e = vram_predict_peak(cfg, batch, seq, n_buffers, step_flags, &b)) return e;
   if (out) *out = b;
   uint64_t free_b = free_override;
   if (!free_b) {
@@ -710,9 +727,9 @@ int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t 
   }
   LSQ_CHECK(b.total <= free_b, LSQ_ERR_REFUSED,
             "a streaming step is predicted to need %.2f GB of VRAM but only %.2f GB is free (batch %d x seq %d; "
-            "logits %.2f GB, checkpoints %.2f GB, %d layer buffers %.2f GB)",
+            "logits %.2f GB, checkpoints %.2f GB, kept activations %.2f GB, %d layer buffers %.2f GB)",
             b.total / 1e9, free_b / 1e9, batch, seq, 6.0 * batch * seq * cfg->vocab / 1e9, b.checkpoints / 1e9,
-            n_buffers, b.slots / 1e9);
+            b.saved_activations / 1e9, n_buffers, b.slots / 1e9);
   return LSQ_OK;
 }
 

@@ -142,8 +142,10 @@ class Resident:
 class Runner:
     """A pool over a store plus the step workspace.  mode: 'streamed' or 'resident'."""
 
-    def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda"):
+    def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda",
+                 keep_activations=False):
         self.cfg, self.store, self.res = cfg, store, resident
+        self.step_flags = lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0
         self.ccfg = lib.model_cfg(cfg)
         self.compute = torch.cuda.Stream(device)
         self.copy = torch.cuda.Stream(device)
@@ -156,14 +158,15 @@ class Runner:
                  lib.stream_handle(self.copy), flags, C.byref(h))
         self.pool = h
         self.n_buffers = n
-        self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq))
+        self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq,
+                                                                 self.step_flags))
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.grads = resident.new_grads()
 
     def step(self, ids, forward_only=False, early_release=False, logits=None, x_trace=None, dx_trace=None):
         flags = (lib.LSQ_STEP_FORWARD_ONLY if forward_only else 0) | \
-                (lib.LSQ_STEP_DEBUG_EARLY_RELEASE if early_release else 0)
+                (lib.LSQ_STEP_DEBUG_EARLY_RELEASE if early_release else 0) | self.step_flags
         self.compute.wait_stream(torch.cuda.current_stream())
         rs = self.res.struct(self.grads)
         opt = (lambda t: _ptr(t) if t is not None else None)

@@ -78,7 +78,7 @@ def _cfg_struct(cfg):
 def test_vram_prediction_terms_and_refusal():
     cfg = configs.STACK_8B
     b = lib.VramBreakdown()
-    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, C.byref(b))
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, 0, C.byref(b))
     blob = lib.blob_layout(cfg).total_bytes
     assert b.slots == 2 * blob
     assert b.resident == 2 * 2 * cfg.vocab * cfg.hidden + 2 * cfg.hidden
@@ -86,14 +86,24 @@ def test_vram_prediction_terms_and_refusal():
     assert b.total >= b.slots + b.resident + b.adapters + b.checkpoints + b.step_workspace
     # the logits term scales with batch x seq x vocab: that is what streaming does not bound
     b2 = lib.VramBreakdown()
-    lib.call("vram_predict_peak", _cfg_struct(cfg), 4, 512, 2, C.byref(b2))
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 4, 512, 2, 0, C.byref(b2))
     assert b2.step_workspace - b.step_workspace >= 3 * 512 * cfg.vocab * 6
     # refused before any GPU work when the (overridden) free memory is too small
     with pytest.raises(lib.LsqError) as e:
-        lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, int(b.total) - 1, None)
+        lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, 0, int(b.total) - 1, None)
     assert e.value.status == "LSQ_ERR_REFUSED"
     assert "predicted to need" in str(e.value)
-    lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, int(b.total), None)
+    lib.call("lsq_preflight", _cfg_struct(cfg), 1, 512, 2, 0, int(b.total), None)
+    # kept activations are a term of their own, proportional to layers x tokens
+    k = lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, lib.LSQ_STEP_KEEP_ACTIVATIONS, C.byref(k))
+    assert b.saved_activations == 0 and k.saved_activations > 0
+    per_token_layer = k.saved_activations / (512 * cfg.n_layers)
+    H, I, r = cfg.hidden, cfg.intermediate, cfg.lora_r
+    # the bf16/f32 tensors the backward reads, 256-byte aligned each
+    approx = 2 * H + 2 * 6144 + 2 * 4096 + 4 * 4096 + 4 * 32 + 4 * H + 2 * H + 4 * I + 2 * I + 2 * 7 * r + 4 * 7 * r
+    assert approx <= per_token_layer <= approx * 1.01
+    assert k.total - k.saved_activations < b.total   # the layer scratch no longer holds them
 
 
 def test_store_pageable_fallback_and_refusal(capfd):
@@ -151,8 +161,9 @@ def test_workspace_queries_are_consistent():
     for cfg in (configs.TINY, configs.STACK_8B, configs.STACK_3B_BF16):
         c = _cfg_struct(cfg)
         lw = lib.raw("decoder_layer_workspace_size")(c, cfg.batch, cfg.seq)
-        sw = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq)
+        sw = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, 0)
         assert 0 < lw < sw
+        assert lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, lib.LSQ_STEP_KEEP_ACTIVATIONS) > sw
         assert lib.raw("decoder_layer_workspace_size")(c, cfg.batch, 2 * cfg.seq) > lw
 
 

@@ -53,6 +53,22 @@ def h2d_probe(torch, nbytes=1 << 30, reps=5):
     return best
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this kernel, or None if that summary is missing or was taken
+    from a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def gemm_probe(torch, n=8192, reps=10):
     """Same-session dense bf16 GEMM ceiling: torch.mm (hipBLASLt) at n^3."""
     a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
@@ -69,6 +85,78 @@ def gemm_probe(torch, n=8192, reps=10):
     tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del a, b
     return tflops
+
+
+def linear_gemm_rates(torch, lib, M=2048, r=16, reps=10):
+    """The fused NF4-LoRA linears at the one-layer 8B shapes (T = 2048 tokens):
+    forward and backward tile kernels timed by the library's events, each
+    against the bf16 MFMA peak.  Seeded random NF4 codes and scales."""
+    C_ = C
+    shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gate_up": (28672, 4096), "down": (4096, 14336)}
+    st = lib.stream_handle(torch.cuda.current_stream())
+    P = lambda t: C_.c_void_p(t.data_ptr())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2048)
+    out = {}
+    for name, (N, K) in shapes.items():
+        packed = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+        absmax = torch.rand((N, K // 64), device="cuda", generator=g) * 0.05
+        X = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        A = (torch.randn(r, K, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+        B = (torch.randn(N, r, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+        dY = torch.randn(M, N, device="cuda", generator=g).to(torch.bfloat16)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        U = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dA = torch.empty(r, K, device="cuda")
+        dB = torch.empty(N, r, device="cuda")
+        w = lib.Weight(lib.LSQ_W_NF4, 0, packed.data_ptr(), absmax.data_ptr(), N, K)
+        wsb = lib.raw("nf4_lora_linear_workspace_size")(M, N, K, r, lib.LSQ_BF16)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+        def fwd():
+            lib.call("nf4_lora_linear_fwd", C_.byref(w), None, P(X), M, P(A), P(B), r, 2.0, lib.LSQ_BF16, P(Y), P(U),
+                     P(ws), wsb, st)
+
+        def bwd():
+            lib.call("nf4_lora_linear_bwd", C_.byref(w), P(X), P(U), M, P(A), P(B), r, 2.0, lib.LSQ_BF16, P(dY),
+                     P(dX), P(dA), P(dB), 0, P(ws), wsb, st)
+        for _ in range(3):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        lib.call("lsq_prof_enable", 1)
+        for _ in range(reps):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        entries = (lib.ProfEntry * 8)()
+        n = C_.c_int32()
+        lib.call("lsq_prof_read", entries, 8, C_.byref(n))
+        lib.call("lsq_prof_enable", 0)
+        prof = {e.name.decode(): e for e in entries[:n.value]}
+        row = {}
+        for fam, key in (("gemm_fwd_nf4_lora", "fwd"), ("gemm_bwd_nf4_lora", "bwd")):
+            e = prof[fam]
+            tf = e.flops / (e.ms * 1e-3) / 1e12
+            row[key] = {"TFLOPs": round(tf, 1), "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "avg_launch_us": round(e.ms / max(1, e.launches) * 1e3, 2)}
+        out[f"{name} {N}x{K}"] = row
+        del packed, absmax, X, A, B, dY, Y, U, dX, dA, dB, ws
+    return out
+
+
+def copy_calibration(torch, nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}))
 
 
 def cpu_baseline(cfg):
@@ -129,6 +217,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers", type=int, default=None)
     ap.add_argument("--no-variants", action="store_true", help="skip the kept-activations timing")
+    ap.add_argument("--no-linears", action="store_true", help="skip the one-layer-shape linear GEMM rates")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the data-parallel path is designed "
@@ -136,6 +227,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
     from layer_streamed_qlora_nf4_amd import configs, lib, model, synth
     lib.load()
     cfg = {c.name: c for c in (configs.STACK_8B, configs.STACK_3B_BF16, configs.STACK_72B)}[a.workload]
@@ -174,6 +268,7 @@ def main():
     peak_alloc = torch.cuda.max_memory_allocated()
     # after the peak is read: torch keeps a BLAS workspace allocated once it has run a GEMM
     gprobe = gemm_probe(torch)
+    linears = None if a.no_linears else linear_gemm_rates(torch, lib)
     log(f"bf16 GEMM probe (torch.mm 8192^3): {gprobe:.0f} TFLOP/s")
 
     ms = elapsed / a.steps * 1e3
@@ -208,7 +303,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(dominant, cfg.name),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "frac_of_gemm_probe": round(achieved / gprobe, 4) if peak == MFMA_BF16_PEAK_TFLOPS else None,
                      "gemm_probe_TFLOPs": round(gprobe, 1),
                      "launches": d["launches"], "avg_launch_us": round(d["ms"] / max(1, d["launches"]) * 1e3, 2),
@@ -221,6 +317,7 @@ def main():
         "kernels": {k: {"ms_per_step": round(v["ms"] / a.steps, 3), "launches_per_step": v["launches"] / a.steps,
                         "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None}
                     for k, v in prof.items()},
+        "linear_gemms_T2048": linears,
         "preflight_predicted_bytes": pf.total,
         "peak_allocated_bytes": peak_alloc,
         "loss": loss,

@@ -58,7 +58,7 @@ def measured_traffic(kernel, workload):
     summary of this kernel, or None if that summary is missing or was taken
     from a different kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload.replace('-', '_')}.json")
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()

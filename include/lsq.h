@@ -288,12 +288,21 @@ enum {
                                        copy land before its backward GEMMs, the
                                        aliasing defect the pages describe; must
                                        make gradients differ                    */
-  LSQ_STEP_KEEP_ACTIVATIONS = 4      /* stream_recompute off (LS-docs "How it
+  LSQ_STEP_KEEP_ACTIVATIONS = 4,     /* stream_recompute off (LS-docs "How it
                                        works"): keep each layer's forward
                                        activations and skip the backward's
                                        recompute; the backward still re-reads
                                        every layer's weights.  Needs the larger
                                        workspace the size query returns for it. */
+  LSQ_STEP_REFERENCE_FORWARD = 8     /* preference losses (LS-docs "Preference
+                                       losses over streaming"; Editorial "The
+                                       Honest Cost"): also run the reference
+                                       model, the same streamed base with its
+                                       adapters off, and return its per-token
+                                       negative log-likelihood.  Both forwards
+                                       run on each layer while it is in its
+                                       slot, so the stack is still read twice
+                                       per step.  Needs lsq_step_extra outputs. */
 };
 /* Workspace of a step run with `flags` (LSQ_STEP_KEEP_ACTIVATIONS adds
  * n_layers kept-activation regions). */
@@ -311,6 +320,19 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
                           const int32_t* ids_dev, int32_t batch, int32_t seq, float* loss_dev,
                           float* logits_out, int32_t flags, void* ws, size_t ws_bytes,
                           float* x_trace, float* dx_trace);
+/* Optional step outputs (every pointer nullable, device memory). */
+typedef struct {
+  float* x_trace;       /* as lsq_train_step_traced                               */
+  float* dx_trace;
+  float* ref_nll_rows;  /* LSQ_STEP_REFERENCE_FORWARD: float32 [batch*seq], the
+                           reference model's -log p(next token); 0 at the last
+                           position of each sequence                              */
+  float* ref_loss;      /* float32 [1]: their mean over the batch*(seq-1) targets */
+} lsq_step_extra;
+int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res,
+                      const int32_t* ids_dev, int32_t batch, int32_t seq, float* loss_dev,
+                      float* logits_out, int32_t flags, void* ws, size_t ws_bytes,
+                      const lsq_step_extra* extra);
 
 /* ------------------------------------------------------ VRAM pre-flight
  * Predict the peak device memory of a streamed step for this exact batch and

@@ -507,6 +507,8 @@ struct StepWs {
   size_t layer_bytes;
   char* acts;        // keep mode: n_layers x acts_bytes of kept forward activations
   size_t acts_bytes;
+  float* xr[2];      // reference mode: the adapters-off residual stream, ping-pong [T, H]
+  float* ref_loss_tmp;  // reference mode: its mean loss when the caller wants rows only
   size_t total;
 };
 
@@ -540,6 +542,11 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
     w.acts_bytes = layer_acts_bytes(c, B, S);
     w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)c->n_layers));
   }
+  if (flags & LSQ_STEP_REFERENCE_FORWARD) {
+    w.xr[0] = static_cast<float*>(take(4 * T * H));
+    w.xr[1] = static_cast<float*>(take(4 * T * H));
+    w.ref_loss_tmp = static_cast<float*>(take(4));
+  }
   w.total = off;
   return w;
 }
@@ -572,9 +579,42 @@ size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t 
   return carve_step(cfg, batch, seq, nullptr, flags).total;
 }
 
-int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
-                          int32_t B, int32_t S, float* loss, float* logits_out, int32_t flags, void* ws,
-                          size_t ws_bytes, float* x_trace, float* dx_trace) {
+// The resident head on a final residual x: final RMSNorm, logits (two bf16
+// passes hi + lo into one float32 accumulator), cross-entropy rows and mean.
+static int head_forward(const lsq_model_cfg* cfg, const lsq_resident* res, const StepWs& w, const float* x,
+                        const int32_t* ids, int B, int S, float* logits, float* loss_rows, float* loss, hipStream_t s) {
+  const int T = B * S, H = cfg->hidden, V = cfg->vocab;
+  if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s,
+                          w.xf_lo))
+    return e;
+  for (int pass = 0; pass < 2; ++pass) {
+    FwdParams p{};
+    p.X = pass ? w.xf_lo : w.xf;
+    p.ldx = H;
+    p.kind = LSQ_W_BF16;
+    p.W = res->head;
+    p.M = T;
+    p.N = V;
+    p.K = H;
+    p.r = 0;
+    p.nseg = 1;
+    p.seg_end[0] = V;
+    p.resid = logits;
+    p.out = logits;
+    p.ldc = V;
+    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+  }
+  return cross_entropy(logits, ids, B, S, V, loss_rows, w.dlogits, w.dlogits_lo, loss, s);
+}
+
+int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
+                      int32_t B, int32_t S, float* loss, float* logits_out, int32_t flags, void* ws, size_t ws_bytes,
+                      const lsq_step_extra* extra) {
+  float* x_trace = extra ? extra->x_trace : nullptr;
+  float* dx_trace = extra ? extra->dx_trace : nullptr;
+  const bool ref = flags & LSQ_STEP_REFERENCE_FORWARD;
+  LSQ_CHECK(!ref || (extra && (extra->ref_nll_rows || extra->ref_loss)), LSQ_ERR_INVALID,
+            "lsq_train_step: the reference forward needs ref_nll_rows or ref_loss");
   if (int e = check_cfg(cfg)) return e;
   LSQ_CHECK(pool && res && ids && loss && ws, LSQ_ERR_INVALID, "lsq_train_step: null pointer");
   LSQ_CHECK(res->embed && res->head && res->final_norm && res->lora && (res->lora_grad || (flags & LSQ_STEP_FORWARD_ONLY)),
@@ -582,7 +622,8 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
   LSQ_CHECK(B >= 1 && S >= 2 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "lsq_train_step: bad batch/seq");
   LSQ_CHECK(memcmp(cfg, &pool->store->cfg, sizeof(lsq_model_cfg)) == 0, LSQ_ERR_INVALID,
             "lsq_train_step: cfg differs from the store's");
-  LSQ_CHECK((flags & ~(LSQ_STEP_FORWARD_ONLY | LSQ_STEP_DEBUG_EARLY_RELEASE | LSQ_STEP_KEEP_ACTIVATIONS)) == 0,
+  LSQ_CHECK((flags & ~(LSQ_STEP_FORWARD_ONLY | LSQ_STEP_DEBUG_EARLY_RELEASE | LSQ_STEP_KEEP_ACTIVATIONS |
+                       LSQ_STEP_REFERENCE_FORWARD)) == 0,
             LSQ_ERR_INVALID, "lsq_train_step: unknown flags 0x%x", flags);
   const size_t need = carve_step(cfg, B, S, nullptr, flags).total;
   LSQ_CHECK(ws_bytes >= need, LSQ_ERR_WORKSPACE, "lsq_train_step: workspace %zu < %zu (flags 0x%x)", ws_bytes, need,
@@ -592,6 +633,8 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
   const int L = cfg->n_layers, T = B * S, H = cfg->hidden, V = cfg->vocab;
   hipStream_t s = pool->compute;
   StepWs w = carve_step(cfg, B, S, ws, flags);
+  lsq_model_cfg cfg_ref = *cfg;
+  cfg_ref.lora_scale = 0.f;
   auto acts_at = [&](int i) -> void* { return w.acts ? w.acts + (uint64_t)i * w.acts_bytes : nullptr; };
   lsq_lora_layout LL;
   lora_layout(cfg, &LL);
@@ -612,33 +655,26 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s,
                           acts_at(i)))
       return e;
+    if (ref) {
+      // the reference model on the same bytes while they are in the slot: adapters off (scale 0)
+      const float* xin = i == 0 ? x_at(0) : w.xr[(i - 1) & 1];
+      if (int e = layer_fwd(&cfg_ref, blob, lora + (uint64_t)i * LL.layer_elems, xin, B, S, w.xr[i & 1], w.layer, s,
+                            nullptr))
+        return e;
+    }
     if (int e = layer_pool_release(pool, i)) return e;
+  }
+  if (ref) {
+    if (int e = head_forward(cfg, res, w, w.xr[(L - 1) & 1], ids, B, S, w.logits,
+                             extra->ref_nll_rows ? extra->ref_nll_rows : w.loss_rows,
+                             extra->ref_loss ? extra->ref_loss : w.ref_loss_tmp, s))
+      return e;
   }
   // ---- head and loss (resident).  The head GEMMs take their float32 operand
   // (final-norm output, dlogits) as a bf16 pair hi + lo, two MFMA passes into
   // one float32 accumulator, so the gradient that enters the stack carries
   // no bf16 rounding of its own.
-  if (int e = rmsnorm_fwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s,
-                          w.xf_lo))
-    return e;
-  for (int pass = 0; pass < 2; ++pass) {
-    FwdParams p{};
-    p.X = pass ? w.xf_lo : w.xf;
-    p.ldx = H;
-    p.kind = LSQ_W_BF16;
-    p.W = res->head;
-    p.M = T;
-    p.N = V;
-    p.K = H;
-    p.r = 0;
-    p.nseg = 1;
-    p.seg_end[0] = V;
-    p.resid = logits;
-    p.out = logits;
-    p.ldc = V;
-    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
-  }
-  if (int e = cross_entropy(logits, ids, B, S, V, w.loss_rows, w.dlogits, w.dlogits_lo, loss, s)) return e;
+  if (int e = head_forward(cfg, res, w, x_at(L), ids, B, S, logits, w.loss_rows, loss, s)) return e;
   if (flags & LSQ_STEP_FORWARD_ONLY) return LSQ_OK;
   for (int pass = 0; pass < 2; ++pass) {
     BwdParams p{};
@@ -685,6 +721,15 @@ int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_re
     if (dx_trace) LSQ_HIP(hipMemcpyAsync(dx_trace + (size_t)i * T * H, dcur, act, hipMemcpyDeviceToDevice, s));
   }
   return LSQ_OK;
+}
+
+int lsq_train_step_traced(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
+                          int32_t B, int32_t S, float* loss, float* logits_out, int32_t flags, void* ws,
+                          size_t ws_bytes, float* x_trace, float* dx_trace) {
+  LSQ_CHECK(!(flags & LSQ_STEP_REFERENCE_FORWARD), LSQ_ERR_INVALID,
+            "lsq_train_step_traced: the reference forward needs lsq_train_step_ex");
+  lsq_step_extra ex{x_trace, dx_trace, nullptr, nullptr};
+  return lsq_train_step_ex(cfg, pool, res, ids, B, S, loss, logits_out, flags, ws, ws_bytes, &ex);
 }
 
 int lsq_train_step(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids, int32_t B,

@@ -14,7 +14,7 @@ LSQ_BF16, LSQ_F32 = 0, 1
 LSQ_W_NF4, LSQ_W_BF16 = 0, 1
 LSQ_STORE_ALLOW_PAGEABLE, LSQ_STORE_FORCE_PAGEABLE, LSQ_STORE_FAIL_PIN = 1, 2, 4
 LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
-LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS = 1, 2, 4
+LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS, LSQ_STEP_REFERENCE_FORWARD = 1, 2, 4, 8
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",
           -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE",
@@ -63,6 +63,11 @@ class Resident(C.Structure):
                 ("lora", C.c_void_p), ("lora_grad", C.c_void_p)]
 
 
+class StepExtra(C.Structure):
+    _fields_ = [("x_trace", C.c_void_p), ("dx_trace", C.c_void_p), ("ref_nll_rows", C.c_void_p),
+                ("ref_loss", C.c_void_p)]
+
+
 class VramBreakdown(C.Structure):
     _fields_ = [("slots", C.c_uint64), ("resident", C.c_uint64), ("adapters", C.c_uint64),
                 ("checkpoints", C.c_uint64), ("saved_activations", C.c_uint64), ("step_workspace", C.c_uint64),
@@ -108,6 +113,8 @@ _SIGS = {
     "lsq_step_workspace_size": (_SZ, [C.POINTER(ModelCfg), _I32, _I32, _I32]),
     "lsq_train_step": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32, _P,
                                  _SZ]),
+    "lsq_train_step_ex": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32, _P,
+                                    _SZ, C.POINTER(StepExtra)]),
     "lsq_train_step_traced": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32,
                                         _P, _SZ, _P, _P]),
     "vram_predict_peak": (C.c_int, [C.POINTER(ModelCfg), _I32, _I32, _I32, _I32, C.POINTER(VramBreakdown)]),

@@ -68,6 +68,22 @@ class Store:
         self.pinned = bool(lib.raw("shard_store_is_pinned")(h))
         return self
 
+    @classmethod
+    def copy_of(cls, other, flags):
+        """Another arena (e.g. pageable) holding the same blobs, byte for byte."""
+        self = cls.__new__(cls)
+        self.cfg = other.cfg
+        self.ccfg = lib.model_cfg(other.cfg)
+        h = C.c_void_p()
+        lib.call("shard_store_create", C.byref(self.ccfg), flags, C.byref(h))
+        self.handle = h
+        self.layer_bytes = int(lib.raw("shard_store_layer_bytes")(h))
+        self.pinned = bool(lib.raw("shard_store_is_pinned")(h))
+        for i in range(self.cfg.n_layers):
+            C.memmove(lib.raw("shard_store_layer_host")(h, i), lib.raw("shard_store_layer_host")(other.handle, i),
+                      self.layer_bytes)
+        return self
+
     def save(self, path):
         lib.call("shard_store_save", self.handle, str(path).encode())
 
@@ -143,9 +159,11 @@ class Runner:
     """A pool over a store plus the step workspace.  mode: 'streamed' or 'resident'."""
 
     def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda",
-                 keep_activations=False):
+                 keep_activations=False, reference=False):
         self.cfg, self.store, self.res = cfg, store, resident
         self.step_flags = lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0
+        # the workspace is sized for the reference forward when it may be asked for
+        ws_flags = self.step_flags | (lib.LSQ_STEP_REFERENCE_FORWARD if reference else 0)
         self.ccfg = lib.model_cfg(cfg)
         self.compute = torch.cuda.Stream(device)
         self.copy = torch.cuda.Stream(device)
@@ -158,19 +176,27 @@ class Runner:
                  lib.stream_handle(self.copy), flags, C.byref(h))
         self.pool = h
         self.n_buffers = n
-        self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq,
-                                                                 self.step_flags))
+        self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq, ws_flags))
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         self.grads = resident.new_grads()
 
-    def step(self, ids, forward_only=False, early_release=False, logits=None, x_trace=None, dx_trace=None):
+    def step(self, ids, forward_only=False, early_release=False, logits=None, x_trace=None, dx_trace=None,
+             ref_nll_rows=None, ref_loss=None):
+        """One lsq_train_step.  ref_nll_rows / ref_loss (float32 device tensors)
+        ask for the adapters-off reference forward as well."""
+        reference = ref_nll_rows is not None or ref_loss is not None
         flags = (lib.LSQ_STEP_FORWARD_ONLY if forward_only else 0) | \
-                (lib.LSQ_STEP_DEBUG_EARLY_RELEASE if early_release else 0) | self.step_flags
+                (lib.LSQ_STEP_DEBUG_EARLY_RELEASE if early_release else 0) | self.step_flags | \
+                (lib.LSQ_STEP_REFERENCE_FORWARD if reference else 0)
         self.compute.wait_stream(torch.cuda.current_stream())
         rs = self.res.struct(self.grads)
         opt = (lambda t: _ptr(t) if t is not None else None)
-        if x_trace is None and dx_trace is None:
+        if reference:
+            ex = lib.StepExtra(opt(x_trace), opt(dx_trace), opt(ref_nll_rows), opt(ref_loss))
+            lib.call("lsq_train_step_ex", C.byref(self.ccfg), self.pool, C.byref(rs), _ptr(ids), self.cfg.batch,
+                     self.cfg.seq, _ptr(self.loss), opt(logits), flags, _ptr(self.ws), self.ws_bytes, C.byref(ex))
+        elif x_trace is None and dx_trace is None:
             lib.call("lsq_train_step", C.byref(self.ccfg), self.pool, C.byref(rs), _ptr(ids), self.cfg.batch,
                      self.cfg.seq, _ptr(self.loss), opt(logits), flags, _ptr(self.ws), self.ws_bytes)
         else:

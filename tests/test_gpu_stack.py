@@ -201,3 +201,74 @@ def test_kept_activations_equal_recompute_bit_for_bit(gpu, cfg):
     exact, total = _compare_bitwise(cfg, out[False], out[True])
     assert exact == total == cfg.n_layers * 14
     assert out[True]["stats"].copies == out[False]["stats"].copies == 2 * cfg.n_layers - cfg.n_buffers
+
+
+def test_pageable_store_streams_the_same_bytes(gpu):
+    """The pageable fallback only changes how the copies run (synchronously),
+    never what they carry: gradients equal the pinned store's bit for bit."""
+    cfg = configs.TINY.with_(name="tiny-pageable", wid=19)
+    print_case(test="pageable_store", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    pstore = model.Store.copy_of(store, lib.LSQ_STORE_FORCE_PAGEABLE)
+    assert store.pinned and not pstore.pinned
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    a = run(cfg, "streamed", store, res, ids)
+    b = run(cfg, "streamed", pstore, res, ids)
+    exact, total = _compare_bitwise(cfg, a, b)
+    assert exact == total
+    pstore.close()
+    store.close()
+
+
+def test_reference_forward_rides_the_same_stream(gpu):
+    """The adapters-off reference forward (preference losses) runs on each layer
+    while it is in its slot: the policy step is unchanged bit for bit, no extra
+    layer copies are made, the reference loss equals a step whose adapters
+    contribute nothing (B = 0), and its per-token NLL matches the oracle's
+    adapters-off stack."""
+    cfg = configs.TINY.with_(name="tiny-ref", wid=23)
+    print_case(test="reference_forward", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids_np = ids_for(cfg)
+    ids = torch.from_numpy(ids_np).cuda()
+    base = run(cfg, "streamed", store, res, ids)
+    r = model.Runner(cfg, store, res, reference=True)
+    logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+    rows = torch.empty(cfg.tokens, dtype=torch.float32, device="cuda")
+    rloss = torch.empty(1, dtype=torch.float32, device="cuda")
+    loss = r.step(ids, logits=logits, ref_nll_rows=rows, ref_loss=rloss).item()
+    torch.cuda.synchronize()
+    withref = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy(), stats=r.stats())
+    r.close()
+    exact, total = _compare_bitwise(cfg, base, withref)
+    assert exact == total
+    assert withref["stats"].copies == base["stats"].copies == 2 * cfg.n_layers - cfg.n_buffers
+    # adapters contributing nothing: zero every B block
+    zres = model.Resident(cfg)
+    L = lib.lora_layout(cfg)
+    for g in range(4):
+        nb = sum(cfg.proj_shape(n)[0] for n in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))[g]) * cfg.lora_r
+        zres.lora[:, L.b_off[g]:L.b_off[g] + nb] = 0
+    zero = run(cfg, "streamed", store, zres, ids)
+    assert rloss.item() == zero["loss"]
+    # oracle: the stack with s = 0, per-row NLL
+    rw = synth.resident_weights(cfg, cfg.wid)
+    params = [oracle_layer_params(cfg, i) for i in range(cfg.n_layers)]
+    ref_logits = omodel.stack_fwd(oracle_cfg(cfg), ids_np.astype(np.int64), bits_f64(rw["embed"]),
+                                  lambda i: params[i], cfg.n_layers, bits_f64(rw["final_norm"]),
+                                  bits_f64(rw["head"]), 0.0)
+    B, S, V = cfg.batch, cfg.seq, cfg.vocab
+    lg = ref_logits.reshape(B, S, V)
+    lse = np.log(np.exp(lg - lg.max(-1, keepdims=True)).sum(-1)) + lg.max(-1)
+    nll = np.zeros((B, S))
+    tgt = ids_np.reshape(B, S)
+    for b in range(B):
+        for t in range(S - 1):
+            nll[b, t] = lse[b, t] - lg[b, t, tgt[b, t + 1]]
+    got = rows.cpu().numpy().reshape(B, S)
+    assert rel_err(got, nll) <= TOL
+    assert np.all(got[:, S - 1] == 0)
+    assert abs(rloss.item() - nll[:, :S - 1].mean()) <= TOL * nll[:, :S - 1].mean()
+    store.close()

@@ -136,6 +136,11 @@ typedef struct {
   int32_t weight_kind;   /* LSQ_W_NF4 or LSQ_W_BF16                         */
   int32_t lora_r;
   float rms_eps, rope_theta, lora_scale;
+  int32_t loss_chunk;    /* stream_loss_chunk (LS-docs "Scaling a streaming run",
+                            "Troubleshooting": the logits are usually the whole
+                            story): tokens per head/cross-entropy chunk, which
+                            bounds the logits buffers at loss_chunk x vocab;
+                            0 = all tokens at once                             */
 } lsq_model_cfg;
 
 /* One layer's shard ("blob"): one contiguous, 4 KiB-aligned byte range, so a
@@ -263,6 +268,7 @@ int layer_pool_release(lsq_pool* pool, int32_t layer);
 typedef struct {
   uint64_t copies, copy_bytes, hits;
   double copy_ms;      /* summed copy durations (events on the copy stream); valid after a sync */
+  uint64_t large_copies, large_bytes;   /* head copies of LSQ_STEP_STREAM_LARGE steps */
 } lsq_pool_stats;
 int layer_pool_stats(lsq_pool* pool, int32_t reset, lsq_pool_stats* out);
 
@@ -294,6 +300,18 @@ enum {
                                        recompute; the backward still re-reads
                                        every layer's weights.  Needs the larger
                                        workspace the size query returns for it. */
+  LSQ_STEP_STREAM_LARGE = 16,        /* large-layer streaming of an untied
+                                       embedding and head (LS-docs "Measured
+                                       numbers": they move into the store and
+                                       share one vocabulary-sized buffer):
+                                       res->embed and res->head are then
+                                       page-locked HOST pointers.  The gather
+                                       reads only the batch's embedding rows
+                                       over the link; the head is copied once
+                                       per step into the workspace's head buffer
+                                       on the pool's copy stream, after the last
+                                       layer copy of the forward.  Refused for
+                                       tied models.                              */
   LSQ_STEP_REFERENCE_FORWARD = 8     /* preference losses (LS-docs "Preference
                                        losses over streaming"; Editorial "The
                                        Honest Cost"): also run the reference

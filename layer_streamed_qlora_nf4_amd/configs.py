@@ -24,6 +24,7 @@ class ModelCfg:
     batch: int = 1
     seq: int = 512
     n_buffers: int = 2
+    loss_chunk: int = 0         # tokens per head / cross-entropy chunk (0 = all)
     wid: int = 0                # seed namespace of the workload
 
     @property

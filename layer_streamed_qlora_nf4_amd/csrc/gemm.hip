@@ -423,6 +423,10 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
   fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
 }
 
+template <int TM, int TO, int EPI>
+__device__ __forceinline__ void bwd_store(const BwdParams& p, const f32x4 (&acc)[TM][TO], int r0, int c0, int lane,
+                                          int split);
+
 // =========================================================== backward (NN)
 // C[M, K] = dY[M, N] W[N, K] + G[M, rr] Al[rr, K] (+ resid)
 // The weight slab (64 rows of W) is decoded straight into a transposed LDS

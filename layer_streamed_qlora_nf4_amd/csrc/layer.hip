@@ -32,6 +32,7 @@ int check_cfg(const lsq_model_cfg* c) {
   LSQ_CHECK(c->lora_r >= 8 && c->lora_r <= 64 && c->lora_r % 8 == 0, LSQ_ERR_SHAPE,
             "model cfg: lora_r must be 8..64 and a multiple of 8 (got %d)", c->lora_r);
   LSQ_CHECK(c->rms_eps > 0 && c->rope_theta > 0, LSQ_ERR_INVALID, "model cfg: eps / theta");
+  LSQ_CHECK(c->loss_chunk >= 0, LSQ_ERR_INVALID, "model cfg: loss_chunk must be >= 0 (0 = all tokens)");
   return LSQ_OK;
 }
 

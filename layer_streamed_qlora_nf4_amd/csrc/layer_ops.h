@@ -50,5 +50,11 @@ int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V,
 // dlogits (and, if non-null, dlogits_lo = bf16 of the remainder) for the head backward.
 int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,
                   uint16_t* dlogits_lo, float* loss, hipStream_t s);
+// One chunk of rows [row0, row0 + nrows): logits and dlogits hold just those
+// rows; ids and loss_rows are indexed by the global token.
+int cross_entropy_rows(const float* logits, const int32_t* ids, int B, int S, int V, int row0, int nrows,
+                       float* loss_rows, uint16_t* dlogits, uint16_t* dlogits_lo, hipStream_t s);
+// loss = mean of loss_rows over the B*(S-1) positions that have a target.
+int loss_mean(const float* loss_rows, int B, int S, float* loss, hipStream_t s);
 
 }  // namespace lsq

@@ -629,13 +629,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 __global__ void __launch_bounds__(kCeThreads) ce_kernel(const float* __restrict__ logits, const int32_t* __restrict__ ids,
-                                                        int T, int S, int V, float inv_count, float* __restrict__ loss_rows,
+                                                        int row0, int S, int V, float inv_count, float* __restrict__ loss_rows,
                                                         uint16_t* __restrict__ dlogits, uint16_t* __restrict__ dlogits_lo) {
+  // logits, dlogits: this chunk's rows (chunk-local row blockIdx.x); ids and
+  // loss_rows: global token index t = row0 + blockIdx.x
   constexpr int NW = kCeThreads / 64;
   __shared__ float red_m[NW], red_s[NW];
-  const int t = blockIdx.x;
+  const int lr = blockIdx.x, t = row0 + lr;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* row = logits + (int64_t)t * V;
+  const float* row = logits + (int64_t)lr * V;
   const float4* row4 = reinterpret_cast<const float4*>(row);
   const int V4 = V / 4;
   // an out-of-range id (flagged by the embedding kernel) contributes no loss
@@ -668,8 +670,8 @@ __global__ void __launch_bounds__(kCeThreads) ce_kernel(const float* __restrict_
   for (int k = 1; k < NW; ++k) lse_merge(m, sum, red_m[k], red_s[k]);
   const float lse = m + __logf(sum);
   const float inv_sum = 1.f / sum;
-  uint2* drow = reinterpret_cast<uint2*>(dlogits + (int64_t)t * V);
-  uint2* lrow = dlogits_lo ? reinterpret_cast<uint2*>(dlogits_lo + (int64_t)t * V) : nullptr;
+  uint2* drow = reinterpret_cast<uint2*>(dlogits + (int64_t)lr * V);
+  uint2* lrow = dlogits_lo ? reinterpret_cast<uint2*>(dlogits_lo + (int64_t)lr * V) : nullptr;
   for (int i = tid; i < V4; i += kCeThreads) {
     const float4 x = row4[i];
     const float xv[4] = {x.x, x.y, x.z, x.w};
@@ -839,15 +841,28 @@ int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V,
   return LSQ_OK;
 }
 
-int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,
-                  uint16_t* dlogits_lo, float* loss, hipStream_t s) {
-  const int T = B * S;
-  if (T == 0) return LSQ_OK;
+int cross_entropy_rows(const float* logits, const int32_t* ids, int B, int S, int V, int row0, int nrows,
+                       float* loss_rows, uint16_t* dlogits, uint16_t* dlogits_lo, hipStream_t s) {
+  LSQ_CHECK(V % 4 == 0 && row0 >= 0 && nrows >= 0 && row0 + nrows <= B * S, LSQ_ERR_SHAPE, "cross_entropy: bad rows");
+  if (nrows == 0) return LSQ_OK;
   const float inv_count = S > 1 ? 1.f / (float)(B * (S - 1)) : 0.f;
-  ce_kernel<<<T, kCeThreads, 0, s>>>(logits, ids, T, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
-  loss_sum_kernel<<<1, 256, 0, s>>>(loss_rows, T, inv_count, loss);
+  ce_kernel<<<nrows, kCeThreads, 0, s>>>(logits, ids, row0, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
+}
+
+int loss_mean(const float* loss_rows, int B, int S, float* loss, hipStream_t s) {
+  const float inv_count = S > 1 ? 1.f / (float)(B * (S - 1)) : 0.f;
+  loss_sum_kernel<<<1, 256, 0, s>>>(loss_rows, B * S, inv_count, loss);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,
+                  uint16_t* dlogits_lo, float* loss, hipStream_t s) {
+  if (B * S == 0) return LSQ_OK;
+  if (int e = cross_entropy_rows(logits, ids, B, S, V, 0, B * S, loss_rows, dlogits, dlogits_lo, s)) return e;
+  return loss_mean(loss_rows, B, S, loss, s);
 }
 
 }  // namespace lsq

@@ -344,6 +344,8 @@ struct lsq_pool {
   lsq_pool_stats stats{};
   std::vector<hipEvent_t> tev;  // copy timing pairs (ring)
   int tev_used = 0;
+  hipEvent_t large_ready = nullptr, large_free = nullptr;  // the step's head buffer (LSQ_STEP_STREAM_LARGE)
+  bool large_free_recorded = false;
 };
 
 namespace {
@@ -408,6 +410,8 @@ int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots
     LSQ_HIP(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming));
     LSQ_HIP(hipEventCreateWithFlags(&s.free_ev, hipEventDisableTiming));
   }
+  LSQ_HIP(hipEventCreateWithFlags(&p->large_ready, hipEventDisableTiming));
+  LSQ_HIP(hipEventCreateWithFlags(&p->large_free, hipEventDisableTiming));
   if (resident) {
     for (int i = 0; i < n_buffers; ++i)
       if (int e = copy_into(p, i, i)) return e;
@@ -425,6 +429,8 @@ void layer_pool_destroy(lsq_pool* p) {
     (void)hipEventDestroy(s.ready);
     (void)hipEventDestroy(s.free_ev);
   }
+  if (p->large_ready) (void)hipEventDestroy(p->large_ready);
+  if (p->large_free) (void)hipEventDestroy(p->large_free);
   delete p;
 }
 
@@ -495,9 +501,11 @@ struct StepWs {
   float* dxb;        // [T, H]
   uint16_t* xf;      // [T, H]  final-norm output, bf16
   uint16_t* xf_lo;   // [T, H]  bf16 of its remainder
-  float* logits;     // [T, V]
-  uint16_t* dlogits; // [T, V]
-  uint16_t* dlogits_lo; // [T, V]
+  int chunk;         // tokens per head / cross-entropy chunk
+  float* logits;     // [chunk, V]
+  uint16_t* dlogits; // [chunk, V]
+  uint16_t* dlogits_lo; // [chunk, V]
+  uint16_t* head;    // LSQ_STEP_STREAM_LARGE: the head, copied in each step [V, H]
   float* loss_rows;  // [T]
   float* dxf;        // [T, H]
   int32_t* bad;      // [1]
@@ -528,13 +536,20 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
   w.dxb = static_cast<float*>(take(4 * T * H));
   w.xf = static_cast<uint16_t*>(take(2 * T * H));
   w.xf_lo = static_cast<uint16_t*>(take(2 * T * H));
-  w.logits = static_cast<float*>(take(4 * T * V));
-  w.dlogits = static_cast<uint16_t*>(take(2 * T * V));
-  w.dlogits_lo = static_cast<uint16_t*>(take(2 * T * V));
+  const uint64_t Tc = (c->loss_chunk > 0 && (uint64_t)c->loss_chunk < T) ? (uint64_t)c->loss_chunk : T;
+  w.chunk = (int)Tc;
+  w.logits = static_cast<float*>(take(4 * Tc * V));
+  w.dlogits = static_cast<uint16_t*>(take(2 * Tc * V));
+  w.dlogits_lo = static_cast<uint16_t*>(take(2 * Tc * V));
   w.loss_rows = static_cast<float*>(take(4 * T));
   w.dxf = static_cast<float*>(take(4 * T * H));
   w.bad = static_cast<int32_t*>(take(4));
-  w.gemm_bytes = std::max(gemm_fwd_ws_bytes((int)T, (int)V, (int)H), gemm_bwd_ws_bytes((int)T, (int)V, (int)H, 0));
+  w.gemm_bytes = std::max(gemm_fwd_ws_bytes((int)Tc, (int)V, (int)H), gemm_bwd_ws_bytes((int)Tc, (int)V, (int)H, 0));
+  // a last, shorter chunk can split differently: size for it too
+  if (T % Tc)
+    w.gemm_bytes = std::max(w.gemm_bytes, std::max(gemm_fwd_ws_bytes((int)(T % Tc), (int)V, (int)H),
+                                                   gemm_bwd_ws_bytes((int)(T % Tc), (int)V, (int)H, 0)));
+  if (flags & LSQ_STEP_STREAM_LARGE) w.head = static_cast<uint16_t*>(take(2 * V * H));
   w.gemm = take(w.gemm_bytes);
   w.layer_bytes = layer_ws_bytes(c, B, S, keep);
   w.layer = take(w.layer_bytes);
@@ -579,32 +594,65 @@ size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t 
   return carve_step(cfg, batch, seq, nullptr, flags).total;
 }
 
-// The resident head on a final residual x: final RMSNorm, logits (two bf16
-// passes hi + lo into one float32 accumulator), cross-entropy rows and mean.
-static int head_forward(const lsq_model_cfg* cfg, const lsq_resident* res, const StepWs& w, const float* x,
-                        const int32_t* ids, int B, int S, float* logits, float* loss_rows, float* loss, hipStream_t s) {
+// The head on a final residual x, chunk by chunk of tokens (stream_loss_chunk):
+// final RMSNorm, logits (two bf16 passes hi + lo into one float32
+// accumulator), cross-entropy rows; with dxf, also dlogits -> dxf = dlogits
+// head (again hi + lo).  Rows are independent, so chunking changes no
+// value's definition, only the buffers' size.  logits_out (nullable) receives
+// every row's logits; loss gets the mean.
+static int head_pass(const lsq_model_cfg* cfg, const lsq_resident* res, const void* head, const StepWs& w,
+                     const float* x, const int32_t* ids, int B, int S, float* logits_out, float* loss_rows,
+                     float* loss, float* dxf, hipStream_t s) {
   const int T = B * S, H = cfg->hidden, V = cfg->vocab;
   if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s,
                           w.xf_lo))
     return e;
-  for (int pass = 0; pass < 2; ++pass) {
-    FwdParams p{};
-    p.X = pass ? w.xf_lo : w.xf;
-    p.ldx = H;
-    p.kind = LSQ_W_BF16;
-    p.W = res->head;
-    p.M = T;
-    p.N = V;
-    p.K = H;
-    p.r = 0;
-    p.nseg = 1;
-    p.seg_end[0] = V;
-    p.resid = logits;
-    p.out = logits;
-    p.ldc = V;
-    if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+  for (int r0 = 0; r0 < T; r0 += w.chunk) {
+    const int n = std::min(w.chunk, T - r0);
+    float* logits = logits_out ? logits_out + (int64_t)r0 * V : w.logits;
+    for (int pass = 0; pass < 2; ++pass) {
+      FwdParams p{};
+      p.X = (pass ? w.xf_lo : w.xf) + (int64_t)r0 * H;
+      p.ldx = H;
+      p.kind = LSQ_W_BF16;
+      p.W = head;
+      p.M = n;
+      p.N = V;
+      p.K = H;
+      p.r = 0;
+      p.nseg = 1;
+      p.seg_end[0] = V;
+      p.resid = logits;
+      p.out = logits;
+      p.ldc = V;
+      if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+    }
+    if (int e = cross_entropy_rows(logits, ids, B, S, V, r0, n, loss_rows, w.dlogits, w.dlogits_lo, s)) return e;
+    if (!dxf) continue;
+    for (int pass = 0; pass < 2; ++pass) {
+      BwdParams p{};
+      p.dY = pass ? w.dlogits_lo : w.dlogits;
+      p.ldy = V;
+      p.kind = LSQ_W_BF16;
+      p.W = head;
+      p.M = n;
+      p.N = V;
+      p.K = H;
+      p.rr = 0;
+      p.resid = dxf + (int64_t)r0 * H;
+      p.out = dxf + (int64_t)r0 * H;
+      p.ldc = H;
+      if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+    }
   }
-  return cross_entropy(logits, ids, B, S, V, loss_rows, w.dlogits, w.dlogits_lo, loss, s);
+  return loss_mean(loss_rows, B, S, loss, s);
+}
+
+// Blob-shaping fields only: a store can serve steps that differ in anything else.
+static bool same_store_shape(const lsq_model_cfg* a, const lsq_model_cfg* b) {
+  return a->hidden == b->hidden && a->n_heads == b->n_heads && a->n_kv_heads == b->n_kv_heads &&
+         a->head_dim == b->head_dim && a->intermediate == b->intermediate && a->n_layers == b->n_layers &&
+         a->qkv_bias == b->qkv_bias && a->weight_kind == b->weight_kind;
 }
 
 int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_resident* res, const int32_t* ids,
@@ -620,11 +668,25 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   LSQ_CHECK(res->embed && res->head && res->final_norm && res->lora && (res->lora_grad || (flags & LSQ_STEP_FORWARD_ONLY)),
             LSQ_ERR_INVALID, "lsq_train_step: resident tensors missing");
   LSQ_CHECK(B >= 1 && S >= 2 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "lsq_train_step: bad batch/seq");
-  LSQ_CHECK(memcmp(cfg, &pool->store->cfg, sizeof(lsq_model_cfg)) == 0, LSQ_ERR_INVALID,
-            "lsq_train_step: cfg differs from the store's");
+  LSQ_CHECK(same_store_shape(cfg, &pool->store->cfg), LSQ_ERR_INVALID, "lsq_train_step: cfg differs from the store's");
   LSQ_CHECK((flags & ~(LSQ_STEP_FORWARD_ONLY | LSQ_STEP_DEBUG_EARLY_RELEASE | LSQ_STEP_KEEP_ACTIVATIONS |
-                       LSQ_STEP_REFERENCE_FORWARD)) == 0,
+                       LSQ_STEP_REFERENCE_FORWARD | LSQ_STEP_STREAM_LARGE)) == 0,
             LSQ_ERR_INVALID, "lsq_train_step: unknown flags 0x%x", flags);
+  const bool large = flags & LSQ_STEP_STREAM_LARGE;
+  LSQ_CHECK(!large || !cfg->tied, LSQ_ERR_INVALID,
+            "lsq_train_step: large-layer streaming is for an untied embedding and head (a tied one stays resident)");
+  LSQ_CHECK(!large || !pool->resident, LSQ_ERR_INVALID, "lsq_train_step: large-layer streaming needs a streamed pool");
+  const void* embed = res->embed;
+  const void* head_src = res->head;
+  if (large) {
+    // both live in page-locked host memory; the gather reads the embedding in place
+    void* dev = nullptr;
+    LSQ_CHECK(hipHostGetDevicePointer(&dev, const_cast<void*>(res->embed), 0) == hipSuccess && dev, LSQ_ERR_INVALID,
+              "lsq_train_step: the embedding must be page-locked host memory for large-layer streaming");
+    embed = dev;
+    LSQ_CHECK(hipHostGetDevicePointer(&dev, const_cast<void*>(res->head), 0) == hipSuccess, LSQ_ERR_INVALID,
+              "lsq_train_step: the head must be page-locked host memory for large-layer streaming");
+  }
   const size_t need = carve_step(cfg, B, S, nullptr, flags).total;
   LSQ_CHECK(ws_bytes >= need, LSQ_ERR_WORKSPACE, "lsq_train_step: workspace %zu < %zu (flags 0x%x)", ws_bytes, need,
             flags);
@@ -641,17 +703,31 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   const uint16_t* lora = static_cast<const uint16_t*>(res->lora);
   float* xs = w.xs;
   auto x_at = [&](int i) { return xs + (uint64_t)i * T * H; };
-  float* logits = logits_out ? logits_out : w.logits;
 
   LSQ_HIP(hipMemsetAsync(w.bad, 0, 4, s));
-  if (int e = embed_gather(ids, static_cast<const uint16_t*>(res->embed), T, H, V, x_at(0), w.bad, s)) return e;
+  if (int e = embed_gather(ids, static_cast<const uint16_t*>(embed), T, H, V, x_at(0), w.bad, s)) return e;
+  // the head's copy is queued on the copy stream behind the forward's layer
+  // copies (issued after the prefetch of the last layer) and waited for at the turn
+  auto queue_head_copy = [&]() -> int {
+    lsq_pool* P = pool;
+    if (P->large_free_recorded) LSQ_HIP(hipStreamWaitEvent(P->copy, P->large_free, 0));
+    LSQ_HIP(hipMemcpyAsync(w.head, head_src, (size_t)V * H * 2, hipMemcpyHostToDevice, P->copy));
+    LSQ_HIP(hipEventRecord(P->large_ready, P->copy));
+    P->stats.large_copies += 1;
+    P->stats.large_bytes += (uint64_t)V * H * 2;
+    return LSQ_OK;
+  };
   // ---- forward: prefetch one ahead, acquire, compute, release
   if (int e = stream_layer_prefetch(pool, 0)) return e;
+  if (large && L == 1)
+    if (int e = queue_head_copy()) return e;
   for (int i = 0; i < L; ++i) {
     const void* blob = nullptr;
     if (int e = layer_pool_acquire(pool, i, &blob)) return e;
     if (i + 1 < L)
       if (int e = stream_layer_prefetch(pool, i + 1)) return e;
+    if (large && i + 1 == L - 1)
+      if (int e = queue_head_copy()) return e;
     if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s,
                           acts_at(i)))
       return e;
@@ -664,33 +740,30 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     }
     if (int e = layer_pool_release(pool, i)) return e;
   }
+  const void* head = head_src;
+  if (large) {
+    LSQ_HIP(hipStreamWaitEvent(s, pool->large_ready, 0));
+    head = w.head;
+  }
   if (ref) {
-    if (int e = head_forward(cfg, res, w, w.xr[(L - 1) & 1], ids, B, S, w.logits,
-                             extra->ref_nll_rows ? extra->ref_nll_rows : w.loss_rows,
-                             extra->ref_loss ? extra->ref_loss : w.ref_loss_tmp, s))
+    if (int e = head_pass(cfg, res, head, w, w.xr[(L - 1) & 1], ids, B, S, nullptr,
+                          extra->ref_nll_rows ? extra->ref_nll_rows : w.loss_rows,
+                          extra->ref_loss ? extra->ref_loss : w.ref_loss_tmp, nullptr, s))
       return e;
   }
   // ---- head and loss (resident).  The head GEMMs take their float32 operand
   // (final-norm output, dlogits) as a bf16 pair hi + lo, two MFMA passes into
   // one float32 accumulator, so the gradient that enters the stack carries
   // no bf16 rounding of its own.
-  if (int e = head_forward(cfg, res, w, x_at(L), ids, B, S, logits, w.loss_rows, loss, s)) return e;
-  if (flags & LSQ_STEP_FORWARD_ONLY) return LSQ_OK;
-  for (int pass = 0; pass < 2; ++pass) {
-    BwdParams p{};
-    p.dY = pass ? w.dlogits_lo : w.dlogits;
-    p.ldy = V;
-    p.kind = LSQ_W_BF16;
-    p.W = res->head;
-    p.M = T;
-    p.N = V;
-    p.K = H;
-    p.rr = 0;
-    p.resid = w.dxf;
-    p.out = w.dxf;
-    p.ldc = H;
-    if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+  const bool fwd_only = flags & LSQ_STEP_FORWARD_ONLY;
+  if (int e = head_pass(cfg, res, head, w, x_at(L), ids, B, S, logits_out, w.loss_rows, loss,
+                        fwd_only ? nullptr : w.dxf, s))
+    return e;
+  if (large) {
+    LSQ_HIP(hipEventRecord(pool->large_free, s));
+    pool->large_free_recorded = true;
   }
+  if (fwd_only) return LSQ_OK;
   float* dcur = w.dxa;
   float* dnext = w.dxb;
   if (int e = rmsnorm_bwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), w.dxf, nullptr, T, H, cfg->rms_eps,
@@ -748,7 +821,9 @@ int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int3
   lora_layout(cfg, &LL);
   const uint64_t T = (uint64_t)batch * seq, H = cfg->hidden;
   out->slots = (uint64_t)n_buffers * BL.total_bytes;
-  out->resident = 2ull * cfg->vocab * H * (cfg->tied ? 1 : 2) + 2 * H;
+  // large-layer streaming keeps the embedding and head in host memory (the
+  // head's per-step device copy is part of the step workspace)
+  out->resident = (step_flags & LSQ_STEP_STREAM_LARGE) ? 2 * H : 2ull * cfg->vocab * H * (cfg->tied ? 1 : 2) + 2 * H;
   out->adapters = LL.layer_elems * (uint64_t)cfg->n_layers * (2 + 4);
   out->checkpoints = 4 * T * H * (cfg->n_layers + 1);
   const StepWs sw = carve_step(cfg, batch, seq, nullptr, step_flags);

@@ -15,6 +15,7 @@ LSQ_W_NF4, LSQ_W_BF16 = 0, 1
 LSQ_STORE_ALLOW_PAGEABLE, LSQ_STORE_FORCE_PAGEABLE, LSQ_STORE_FAIL_PIN = 1, 2, 4
 LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
 LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS, LSQ_STEP_REFERENCE_FORWARD = 1, 2, 4, 8
+LSQ_STEP_STREAM_LARGE = 16
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",
           -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE",
@@ -38,7 +39,7 @@ class ModelCfg(C.Structure):
                 ("head_dim", C.c_int32), ("intermediate", C.c_int32), ("vocab", C.c_int32),
                 ("n_layers", C.c_int32), ("qkv_bias", C.c_int32), ("tied", C.c_int32),
                 ("weight_kind", C.c_int32), ("lora_r", C.c_int32), ("rms_eps", C.c_float),
-                ("rope_theta", C.c_float), ("lora_scale", C.c_float)]
+                ("rope_theta", C.c_float), ("lora_scale", C.c_float), ("loss_chunk", C.c_int32)]
 
 
 class BlobLayout(C.Structure):
@@ -55,7 +56,8 @@ class LayerSrc(C.Structure):
 
 
 class PoolStats(C.Structure):
-    _fields_ = [("copies", C.c_uint64), ("copy_bytes", C.c_uint64), ("hits", C.c_uint64), ("copy_ms", C.c_double)]
+    _fields_ = [("copies", C.c_uint64), ("copy_bytes", C.c_uint64), ("hits", C.c_uint64), ("copy_ms", C.c_double),
+                ("large_copies", C.c_uint64), ("large_bytes", C.c_uint64)]
 
 
 class Resident(C.Structure):
@@ -176,7 +178,7 @@ def model_cfg(cfg):
     return ModelCfg(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.vocab,
                     cfg.n_layers, int(cfg.qkv_bias), int(cfg.tied),
                     LSQ_W_NF4 if cfg.quant == "nf4" else LSQ_W_BF16, cfg.lora_r, cfg.eps, cfg.theta,
-                    cfg.lora_scale)
+                    cfg.lora_scale, cfg.loss_chunk)
 
 
 def codebook():

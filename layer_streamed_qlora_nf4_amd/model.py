@@ -138,11 +138,23 @@ def split_lora_grads(cfg, grad_layer):
 
 
 class Resident:
-    def __init__(self, cfg, device="cuda"):
+    """Embedding, final norm, head, adapters.  large_in_host: the untied
+    embedding and head stay in page-locked host memory instead (large-layer
+    streaming: the step reads the batch's embedding rows in place and copies
+    the head in once per step)."""
+
+    def __init__(self, cfg, device="cuda", large_in_host=False):
         self.cfg = cfg
+        self.large_in_host = large_in_host
         rw = synth.resident_weights(cfg, cfg.wid)
-        self.embed = _bits_to_dev(rw["embed"], device)
-        self.head = self.embed if cfg.tied else _bits_to_dev(rw["head"], device)
+        if large_in_host:
+            assert not cfg.tied, "a tied embedding stays resident"
+            host = (lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).pin_memory())
+            self.embed = host(rw["embed"])
+            self.head = host(rw["head"])
+        else:
+            self.embed = _bits_to_dev(rw["embed"], device)
+            self.head = self.embed if cfg.tied else _bits_to_dev(rw["head"], device)
         self.final_norm = _bits_to_dev(rw["final_norm"], device)
         self.lora = _bits_to_dev(lora_arena_host(cfg), device)
         self.layer_elems = self.lora.shape[1]
@@ -161,7 +173,8 @@ class Runner:
     def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda",
                  keep_activations=False, reference=False):
         self.cfg, self.store, self.res = cfg, store, resident
-        self.step_flags = lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0
+        self.step_flags = (lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0) | \
+                          (lib.LSQ_STEP_STREAM_LARGE if resident.large_in_host else 0)
         # the workspace is sized for the reference forward when it may be asked for
         ws_flags = self.step_flags | (lib.LSQ_STEP_REFERENCE_FORWARD if reference else 0)
         self.ccfg = lib.model_cfg(cfg)

@@ -272,3 +272,54 @@ def test_reference_forward_rides_the_same_stream(gpu):
     assert np.all(got[:, S - 1] == 0)
     assert abs(rloss.item() - nll[:, :S - 1].mean()) <= TOL * nll[:, :S - 1].mean()
     store.close()
+
+
+def test_loss_chunk_matches_oracle_and_whole_batch(gpu):
+    """stream_loss_chunk: the head and cross-entropy run chunk by chunk of tokens
+    (48 + 48 + 48 + 16 here); rows are independent, so the loss, logits and
+    every layer still match the oracle, and the whole-batch step to float32
+    rounding of the head GEMM."""
+    cfg = configs.TINY.with_(name="tiny-chunk", wid=29, loss_chunk=48)
+    print_case(test="loss_chunk", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids_np = ids_for(cfg)
+    ids = torch.from_numpy(ids_np).cuda()
+    got = traced_step(cfg, store, res, ids)
+    loss, logits, _ = oracle_step(cfg, ids_np)
+    assert abs(got["loss"] - loss) <= TOL * abs(loss)
+    assert rel_err(got["logits"].reshape(logits.shape), logits) <= TOL
+    check_head_against_oracle(cfg, got, ids_np)
+    check_layers_against_oracle(cfg, got, range(cfg.n_layers))
+    whole = traced_step(cfg.with_(loss_chunk=0), store, res, ids)
+    assert abs(got["loss"] - whole["loss"]) <= 1e-5 * abs(whole["loss"])
+    assert rel_err(got["logits"], whole["logits"].astype(np.float64)) <= 1e-5
+    store.close()
+
+
+def test_large_layer_streaming_is_bit_identical(gpu):
+    """Untied embedding and head in page-locked host memory: the gather reads the
+    batch's rows over the link and the head is copied in once per step; the
+    step is bit for bit the resident one, and the head copy is counted."""
+    cfg = configs.TINY.with_(name="tiny-large", wid=31)
+    print_case(test="stream_large", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    hres = model.Resident(cfg, large_in_host=True)
+    assert not hres.embed.is_cuda and hres.embed.is_pinned()
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    a = run(cfg, "streamed", store, res, ids)
+    r = model.Runner(cfg, store, hres)
+    logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        loss = r.step(ids, logits=logits).item()
+        torch.cuda.synchronize()
+        outs.append(dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy()))
+    st = r.stats()
+    r.close()
+    for b in outs:
+        exact, total = _compare_bitwise(cfg, a, b)
+        assert exact == total
+    assert st.large_copies == 2 and st.large_bytes == 2 * 2 * cfg.vocab * cfg.hidden
+    store.close()

@@ -236,3 +236,24 @@ def test_shard_store_save_load_roundtrip_and_refusals(tmp_path):
     with pytest.raises(lib.LsqError) as e:
         lib.call("shard_store_load", str(tmp_path / "missing").encode(), None, 0, C.byref(h2))
     assert e.value.status == "LSQ_ERR_IO"
+
+
+def test_large_layer_streaming_and_loss_chunk_terms():
+    cfg = configs.STACK_8B
+    V, H, T = cfg.vocab, cfg.hidden, 512
+    base, large = lib.VramBreakdown(), lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, T, 2, 0, C.byref(base))
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, T, 2, lib.LSQ_STEP_STREAM_LARGE, C.byref(large))
+    # embedding and head leave the resident term; one head-sized buffer joins the workspace
+    assert large.resident == 2 * H
+    assert large.step_workspace - base.step_workspace == 2 * V * H
+    assert base.total - large.total == 2 * V * H
+    # stream_loss_chunk bounds the logits buffers at chunk x vocab (fp32 logits + two bf16 dlogits)
+    c1 = cfg.with_(loss_chunk=128)
+    ch = lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(c1), 1, T, 2, 0, C.byref(ch))
+    saved = base.step_workspace - ch.step_workspace
+    assert saved >= (T - 128) * V * 8 - (1 << 20)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("vram_predict_peak", _cfg_struct(cfg.with_(loss_chunk=-1)), 1, T, 2, 0, C.byref(ch))
+    assert e.value.status == "LSQ_ERR_INVALID"

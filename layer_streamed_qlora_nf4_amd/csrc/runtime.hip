@@ -500,11 +500,9 @@ struct StepWs {
   float* dxa;        // [T, H]
   float* dxb;        // [T, H]
   uint16_t* xf;      // [T, H]  final-norm output, bf16
-  uint16_t* xf_lo;   // [T, H]  bf16 of its remainder
   int chunk;         // tokens per head / cross-entropy chunk
   float* logits;     // [chunk, V]
   uint16_t* dlogits; // [chunk, V]
-  uint16_t* dlogits_lo; // [chunk, V]
   uint16_t* head;    // LSQ_STEP_STREAM_LARGE: the head, copied in each step [V, H]
   float* loss_rows;  // [T]
   float* dxf;        // [T, H]
@@ -535,12 +533,10 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
   w.dxa = static_cast<float*>(take(4 * T * H));
   w.dxb = static_cast<float*>(take(4 * T * H));
   w.xf = static_cast<uint16_t*>(take(2 * T * H));
-  w.xf_lo = static_cast<uint16_t*>(take(2 * T * H));
   const uint64_t Tc = (c->loss_chunk > 0 && (uint64_t)c->loss_chunk < T) ? (uint64_t)c->loss_chunk : T;
   w.chunk = (int)Tc;
   w.logits = static_cast<float*>(take(4 * Tc * V));
   w.dlogits = static_cast<uint16_t*>(take(2 * Tc * V));
-  w.dlogits_lo = static_cast<uint16_t*>(take(2 * Tc * V));
   w.loss_rows = static_cast<float*>(take(4 * T));
   w.dxf = static_cast<float*>(take(4 * T * H));
   w.bad = static_cast<int32_t*>(take(4));
@@ -595,24 +591,22 @@ size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t 
 }
 
 // The head on a final residual x, chunk by chunk of tokens (stream_loss_chunk):
-// final RMSNorm, logits (two bf16 passes hi + lo into one float32
-// accumulator), cross-entropy rows; with dxf, also dlogits -> dxf = dlogits
-// head (again hi + lo).  Rows are independent, so chunking changes no
-// value's definition, only the buffers' size.  logits_out (nullable) receives
-// every row's logits; loss gets the mean.
+// final RMSNorm (rounded to bf16 once), logits in float32, cross-entropy rows;
+// with dxf, also dlogits (bf16) -> dxf = dlogits head.  Rows are independent,
+// so chunking changes no value's definition, only the buffers' size.
+// logits_out (nullable) receives every row's logits; loss gets the mean.
 static int head_pass(const lsq_model_cfg* cfg, const lsq_resident* res, const void* head, const StepWs& w,
                      const float* x, const int32_t* ids, int B, int S, float* logits_out, float* loss_rows,
                      float* loss, float* dxf, hipStream_t s) {
   const int T = B * S, H = cfg->hidden, V = cfg->vocab;
-  if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s,
-                          w.xf_lo))
+  if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s))
     return e;
   for (int r0 = 0; r0 < T; r0 += w.chunk) {
     const int n = std::min(w.chunk, T - r0);
     float* logits = logits_out ? logits_out + (int64_t)r0 * V : w.logits;
-    for (int pass = 0; pass < 2; ++pass) {
+    {
       FwdParams p{};
-      p.X = (pass ? w.xf_lo : w.xf) + (int64_t)r0 * H;
+      p.X = w.xf + (int64_t)r0 * H;
       p.ldx = H;
       p.kind = LSQ_W_BF16;
       p.W = head;
@@ -622,16 +616,15 @@ static int head_pass(const lsq_model_cfg* cfg, const lsq_resident* res, const vo
       p.r = 0;
       p.nseg = 1;
       p.seg_end[0] = V;
-      p.resid = logits;
       p.out = logits;
       p.ldc = V;
-      if (int e = gemm_fwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+      if (int e = gemm_fwd(p, EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
     }
-    if (int e = cross_entropy_rows(logits, ids, B, S, V, r0, n, loss_rows, w.dlogits, w.dlogits_lo, s)) return e;
+    if (int e = cross_entropy_rows(logits, ids, B, S, V, r0, n, loss_rows, w.dlogits, nullptr, s)) return e;
     if (!dxf) continue;
-    for (int pass = 0; pass < 2; ++pass) {
+    {
       BwdParams p{};
-      p.dY = pass ? w.dlogits_lo : w.dlogits;
+      p.dY = w.dlogits;
       p.ldy = V;
       p.kind = LSQ_W_BF16;
       p.W = head;
@@ -639,10 +632,9 @@ static int head_pass(const lsq_model_cfg* cfg, const lsq_resident* res, const vo
       p.N = V;
       p.K = H;
       p.rr = 0;
-      p.resid = dxf + (int64_t)r0 * H;
       p.out = dxf + (int64_t)r0 * H;
       p.ldc = H;
-      if (int e = gemm_bwd(p, pass ? EPI_F32_RESID : EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
+      if (int e = gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes)) return e;
     }
   }
   return loss_mean(loss_rows, B, S, loss, s);
@@ -751,10 +743,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
                           extra->ref_loss ? extra->ref_loss : w.ref_loss_tmp, nullptr, s))
       return e;
   }
-  // ---- head and loss (resident).  The head GEMMs take their float32 operand
-  // (final-norm output, dlogits) as a bf16 pair hi + lo, two MFMA passes into
-  // one float32 accumulator, so the gradient that enters the stack carries
-  // no bf16 rounding of its own.
+  // ---- head and loss: resident head, or the copy queued during the forward
   const bool fwd_only = flags & LSQ_STEP_FORWARD_ONLY;
   if (int e = head_pass(cfg, res, head, w, x_at(L), ids, B, S, logits_out, w.loss_rows, loss,
                         fwd_only ? nullptr : w.dxf, s))

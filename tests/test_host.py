@@ -248,12 +248,12 @@ def test_large_layer_streaming_and_loss_chunk_terms():
     assert large.resident == 2 * H
     assert large.step_workspace - base.step_workspace == 2 * V * H
     assert base.total - large.total == 2 * V * H
-    # stream_loss_chunk bounds the logits buffers at chunk x vocab (fp32 logits + two bf16 dlogits)
+    # stream_loss_chunk bounds the logits buffers at chunk x vocab (fp32 logits + bf16 dlogits)
     c1 = cfg.with_(loss_chunk=128)
     ch = lib.VramBreakdown()
     lib.call("vram_predict_peak", _cfg_struct(c1), 1, T, 2, 0, C.byref(ch))
     saved = base.step_workspace - ch.step_workspace
-    assert saved >= (T - 128) * V * 8 - (1 << 20)
+    assert saved >= (T - 128) * V * 6 - (16 << 20)   # less any larger split-K partials of the shorter head GEMMs
     with pytest.raises(lib.LsqError) as e:
         lib.call("vram_predict_peak", _cfg_struct(cfg.with_(loss_chunk=-1)), 1, T, 2, 0, C.byref(ch))
     assert e.value.status == "LSQ_ERR_INVALID"

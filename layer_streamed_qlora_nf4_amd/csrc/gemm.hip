@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_fwd_kernel(FwdParams p
   uint4 ra[A_CHUNKS], rb[B_CHUNKS];
   float rabs[B_CHUNKS];
 
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_fwd_kernel(FwdParams p
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
       int q = tid + i * NT, row = q >> 3, c = q & 7;
@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
   float rabs[B_CH];
   const int arow0 = grp * 128;   // this group's share: rows [arow0, arow0 + 128) of both tiles
 
-  auto load_share = [&](int kt) {
+  auto load_share = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     int gt = gtid;   // opaque copy: addresses are rebuilt per call, not held in registers
     asm volatile("" : "+v"(gt));
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
     }
   };
 
-  auto store_share = [&](int buf) {
+  auto store_share = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7;
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mfma_step = [&](int cur) {
+  auto mfma_step = [&](int cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 af[TM], bfr[TN];
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   // micro-tile coordinates: lanes 8 apart in q, neighbouring rg pairs in a pass
-  auto mt_coords = [&](int i, int& rg, int& q) {
+  auto mt_coords = [&](int i, int& rg, int& q) __attribute__((always_inline)) {
     int u = tid + i * NT;
     q = (u & 7) | (((u >> 4) & ((BO / 8 / 8) - 1)) << 3);
     rg = ((u >> 3) & 1) | ((u >> (4 + __builtin_ctz(BO / 64))) << 1);
@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
   float rabs[MT_PER_THREAD][4];
   uint4 rw[MT_PER_THREAD][4];        // bf16: 4 rows x 16 bytes
 
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
     const bool lora = kt >= nk_main;
     const int r0 = (lora ? kt - nk_main : kt) * BK;   // reduction offset
     const uint16_t* Asrc = lora ? p.G : p.dY;
@@ -508,7 +508,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p
     }
   };
 
-  auto store_tile = [&](int buf, int kt) {
+  auto store_tile = [&](int buf, int kt) __attribute__((always_inline)) {
     const bool lora = kt >= nk_main;
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
@@ -723,7 +723,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
   uint4 ra[A_CH];
   uint32_t rb[RB];   // the micro-tile: NF4 codes + absmax bits, or bf16 rows (see bwd_store_mt)
 
-  auto load_share = [&](int kt) {
+  auto load_share = [&](int kt) __attribute__((always_inline)) {
     const int r0 = kt * BK;
     int gt = gtid, lq = mq, lrg = mrg;   // opaque copies: addresses are rebuilt per call, not held
     asm volatile("" : "+v"(gt), "+v"(lq), "+v"(lrg));
@@ -754,7 +754,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
     }
   };
 
-  auto store_share = [&](int buf) {
+  auto store_share = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int q = gtid + i * GT, row = arow0 + (q >> 3), c = q & 7;
@@ -771,7 +771,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mfma_step = [&](int cur) {
+  auto mfma_step = [&](int cur) __attribute__((always_inline)) {
     // The transposed tile's swizzle differs per 16-row block; recompute its
     // addresses here (an empty asm hides the base from loop-invariant code
     // motion) instead of holding 16 of them in registers across the loop.

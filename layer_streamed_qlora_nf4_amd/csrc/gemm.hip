@@ -423,6 +423,202 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
   fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
 }
 
+// ------------------------------------------------- buffer resources and LDS DMA
+// A raw buffer resource over [base, base + bytes): loads past the end return
+// zeros, which pads ragged tiles without a compare per load.  Offsets are 32-bit
+// bytes, so the host only routes operands below 2 GiB here.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// s_waitcnt vmcnt(N) through the builtin (not inline asm), so that the
+// compiler's own wait insertion sees it and knows which DMA writes are done.
+// gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ lds_ptr_t as_lds(void* p) { return (lds_ptr_t)(p); }
+// Copy 64 lanes x 16 B from the buffer into LDS at lds + 16 * lane (the DMA
+// writes LDS without passing through VGPRs; out-of-range chunks land as zeros).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, as_lds(lds), 16, voff, soff, 0, 0);
+}
+
+// ============================================ forward, NF4, activations by DMA
+// The ping-pong schedule above with the activation tile moved off the VGPR
+// path: each wave copies its group's share of the next k-step's X tile
+// straight into LDS (buffer loads with the LDS modifier, issued as its MFMA
+// half begins and waited for at the end of its decode half), so the decode
+// half only unpacks NF4 codes.  Lane l of a DMA fills LDS bytes 16 l of an
+// 8-row block, i.e. row l / 8, swizzled chunk slot l % 8; it therefore loads
+// logical chunk (l % 8) ^ (row % 8).  The two LDS stages are separate arrays
+// and the k loop is unrolled by two so that every access names its stage
+// statically (the compiler can then tell DMA writes to one stage from reads of
+// the other and does not drain the DMA queue before each fragment read).
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128, TM = WM / 16, TN = WN / 16, GT = 256;
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wig = wave & 3, gtid = tid & (GT - 1);
+  const int wm = grp * 2 + ((wave >> 1) & 1), wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const int K = p.K, nk_all = K / BK;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
+
+  // X rows [m0, M), packed codes and absmax of weight rows [n0, N).
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.X + (int64_t)m0 * p.ldx, (uint32_t)((p.M - m0) * p.ldx * 2));
+  const __amdgpu_buffer_rsrc_t rw =
+      buffer_rsrc(static_cast<const uint8_t*>(p.W) + (int64_t)n0 * (K / 2), (uint32_t)((p.N - n0) * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_rsrc(p.absmax + (int64_t)n0 * (K / 64), (uint32_t)((p.N - n0) * (K / 64) * 4));
+
+  // This wave's four 8-row blocks of its group's 128 X rows.
+  const int xrow0 = grp * 128 + wig * 32;
+  const uint32_t x_voff = (uint32_t)(((xrow0 + (lane >> 3)) * p.ldx + (((lane & 7) ^ (lane >> 3)) * 8)) * 2);
+  const uint32_t x_blk = (uint32_t)(8 * p.ldx * 2);
+  // This thread's 32 codes (row, half of the 64-wide block) and their scale.
+  const int brow = grp * 128 + (gtid >> 1), bh = gtid & 1;
+  const uint32_t w_voff = (uint32_t)(brow * (K / 2) + bh * 16);
+  const uint32_t s_voff = (uint32_t)(brow * (K / 64) * 4);
+
+  auto dma_x = [&](int kt, uint16_t* as) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rx, as + (xrow0 + i * 8) * 64, x_voff, (uint32_t)(kt * 128) + i * x_blk);
+  };
+  // Two register sets for the prefetched codes, by k-step parity, so a decode
+  // half can issue the loads of k-step kt + 2 before it unpacks k-step kt + 1.
+  uint4 rb[2];
+  float rab[2];
+  auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
+    rb[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, (uint32_t)(kt * 32), 0));
+    rab[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)(kt * 4), 0));
+  };
+  auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) {
+    const uint32_t words[4] = {rb[set].x, rb[set].y, rb[set].z, rb[set].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o[4];
+      decode_word(words[w], rab[set], lut, o);
+      *reinterpret_cast<uint4*>(&bs[swz(brow, bh * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_step = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TN];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(as, swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = lds_frag(bs, swz(wn * WN + j * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // The two halves of a k-step on stage (as, bs) while stage (an, bn) receives
+  // k-step kt + 1.  A wave's DMA of X(kt + 1) goes out at the end of its MFMA
+  // half, after the half's fragment reads, and is waited for before the
+  // barrier that closes its decode half, a full MFMA half later; the only
+  // vector-memory operations issued after it are the two B loads of kt + 2.
+  // Each group runs its own loop (group 0: MFMA then decode, group 1 the other
+  // way round) over pairs of k-steps with no branches inside: loads past the
+  // last k-step are clamped to it and land in the stage nobody reads any more.
+  // (Straight-line halves also let the compiler see that every DMA is waited
+  // for before the stage it wrote is read, so it adds no waits of its own.)
+  auto mfma_half = [&](int kt, const uint16_t* as, const uint16_t* bs, uint16_t* an)
+      __attribute__((always_inline)) {
+    mfma_step(as, bs);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_x(min(kt + 1, nk - 1), an);
+    lds_barrier();
+  };
+  // set: register set holding k-step kt's codes (parity relative to kbeg);
+  // k-step kt + 1 is in the other one.
+  auto decode_half = [&](int kt, uint16_t* bn, int set) __attribute__((always_inline)) {
+    load_b(min(kt + 2, nk - 1), set);
+    store_b(bn, set ^ 1);
+    wait_vmcnt<2>();
+    lds_barrier();
+  };
+  // The last k-step of an odd count: no DMA, and the decode half only waits.
+  auto last_mfma = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+    mfma_step(as, bs);
+    lds_barrier();
+  };
+  auto last_wait = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    lds_barrier();
+  };
+
+  // Prologue: stage 0 gets k-step kbeg (X by DMA, codes decoded), registers kbeg + 1.
+  if (kbeg < nk) {
+    dma_x(kbeg, As0);
+    load_b(kbeg, 0);
+  }
+  __syncthreads();  // lut
+  if (kbeg < nk) {
+    load_b(min(kbeg + 1, nk - 1), 1);
+    store_b(Bs0, 0);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  int kt = kbeg;
+  if (grp == 0) {
+    for (; kt + 1 < nk; kt += 2) {
+      mfma_half(kt, As0, Bs0, As1);
+      decode_half(kt, Bs1, 0);
+      mfma_half(kt + 1, As1, Bs1, As0);
+      decode_half(kt + 1, Bs0, 1);
+    }
+    if (kt < nk) {
+      last_mfma(As0, Bs0);
+      last_wait();
+    }
+  } else {
+    for (; kt + 1 < nk; kt += 2) {
+      decode_half(kt, Bs1, 0);
+      mfma_half(kt, As0, Bs0, As1);
+      decode_half(kt + 1, Bs0, 1);
+      mfma_half(kt + 1, As1, Bs1, As0);
+    }
+    if (kt < nk) {
+      last_wait();
+      last_mfma(As0, Bs0);
+    }
+  }
+  wait_vmcnt<0>();   // the clamped DMA / loads of the final pair
+
+  fwd_lora_up<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+  fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+}
+
 template <int TM, int TO, int EPI>
 __device__ __forceinline__ void bwd_store(const BwdParams& p, const f32x4 (&acc)[TM][TO], int r0, int c0, int lane,
                                           int split);
@@ -1187,12 +1383,21 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   }
 }
 
+// The DMA forward addresses its operands with 32-bit byte offsets.
+bool fwd_dma_ok(const FwdParams& p) {
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * (p.K / 2) < lim && p.ldx % 8 == 0;
+}
+
 template <int BM, int BN, int WGM, int WGN, int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
 #if LSQ_FWD_PP
   static_assert(BM == 256 && BN == 256 && WGM * WGN == 8, "ping-pong forward is 256 x 256 with 8 waves");
-  gemm_fwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+  if (WK == LSQ_W_NF4 && fwd_dma_ok(p))
+    gemm_fwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+  else
+    gemm_fwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
 #else
   gemm_fwd_kernel<BM, BN, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
 #endif

@@ -1011,6 +1011,161 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
   bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
 }
 
+// ============================================ backward, NF4, dY tile by DMA
+// The forward DMA kernel's schedule over the NN product dX = dY W: the dY tile
+// reaches LDS by DMA, the weight slab's micro-tiles (4 rows of 8 codes each,
+// per producer thread) come through buffer loads into two register sets and
+// are decoded and written transposed, and the LoRA term G A joins in the
+// epilogue.  Weight rows past N read as zeros, which also cancels the dY
+// columns past N that the DMA brings in on the last reduction step.
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
+  constexpr int BM = 256, BO = 256, WM = 64, WO = 128, TM = WM / 16, TO = WO / 16, GT = 256;
+  static_assert((64 / 4) * (BO / 8) == 2 * GT, "one micro-tile per producer thread");
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bt0[BO * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bt1[BO * 64];
+  __shared__ float lut[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wig = wave & 3, gtid = tid & (GT - 1);
+  const int wm = grp * 2 + ((wave >> 1) & 1), wo = wave & 1;
+  const int tiles_o = (p.K + BO - 1) / BO;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
+  const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
+  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+
+  const int K = p.K;
+  const int nk_all = (p.N + BK - 1) / BK;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
+
+  const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(p.dY + (int64_t)m0 * p.ldy, (uint32_t)((p.M - m0) * p.ldy * 2));
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.W, (uint32_t)((int64_t)p.N * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.absmax, (uint32_t)((int64_t)p.N * (K / 64) * 4));
+
+  const int yrow0 = grp * 128 + wig * 32;
+  const uint32_t y_voff = (uint32_t)(((yrow0 + (lane >> 3)) * p.ldy + (((lane & 7) ^ (lane >> 3)) * 8)) * 2);
+  const uint32_t y_blk = (uint32_t)(8 * p.ldy * 2);
+  int mrg, mq;
+  bwd_mt_coords<BO>(grp * GT + gtid, mrg, mq);
+  const int kcol = o0 + mq * 8;
+  const uint32_t w_voff = (uint32_t)(mrg * 4 * (K / 2) + kcol / 2);
+  const uint32_t s_voff = (uint32_t)((mrg * 4 * (K / 64) + kcol / 64) * 4);
+  const uint32_t w_step = (uint32_t)(64 * (K / 2)), w_row = (uint32_t)(K / 2);
+  const uint32_t s_step = (uint32_t)(64 * (K / 64) * 4), s_row = (uint32_t)((K / 64) * 4);
+
+  auto dma_y = [&](int kt, uint16_t* as) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(ry, as + (yrow0 + i * 8) * 64, y_voff, (uint32_t)(kt * 128) + i * y_blk);
+  };
+  uint32_t rb[2][8];   // per set: codes of the micro-tile's 4 rows, then their absmax bits
+  auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      rb[set][rr] = __builtin_amdgcn_raw_buffer_load_b32(rw, w_voff, (uint32_t)kt * w_step + rr * w_row, 0);
+      rb[set][4 + rr] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)kt * s_step + rr * s_row, 0);
+    }
+  };
+  auto store_b = [&](uint16_t* bt, int set) __attribute__((always_inline)) {
+    int q = mq;
+    asm volatile("" : "+v"(q));
+    bwd_store_mt<true, 8>(bt, mrg, q, rb[set], lut);
+  };
+
+  f32x4 acc[TM][TO];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_step = [&](const uint16_t* as, const uint16_t* bt) __attribute__((always_inline)) {
+    int brow = wo * WO + (lane & 15);
+    asm volatile("" : "+v"(brow));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TO];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(as, swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TO; ++j) bfr[j] = lds_frag(bt, swzt(brow + j * 16, chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TO; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // Same half structure as the forward DMA kernel; eight B loads per decode half.
+  auto mfma_half = [&](int kt, const uint16_t* as, const uint16_t* bt, uint16_t* an)
+      __attribute__((always_inline)) {
+    mfma_step(as, bt);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_y(min(kt + 1, nk - 1), an);
+    lds_barrier();
+  };
+  auto decode_half = [&](int kt, uint16_t* bn, int set) __attribute__((always_inline)) {
+    load_b(min(kt + 2, nk - 1), set);
+    store_b(bn, set ^ 1);
+    wait_vmcnt<8>();
+    lds_barrier();
+  };
+  auto last_mfma = [&](const uint16_t* as, const uint16_t* bt) __attribute__((always_inline)) {
+    mfma_step(as, bt);
+    lds_barrier();
+  };
+  auto last_wait = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    lds_barrier();
+  };
+
+  if (kbeg < nk) {
+    dma_y(kbeg, As0);
+    load_b(kbeg, 0);
+  }
+  __syncthreads();  // lut
+  if (kbeg < nk) {
+    load_b(min(kbeg + 1, nk - 1), 1);
+    store_b(Bt0, 0);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  int kt = kbeg;
+  if (grp == 0) {
+    for (; kt + 1 < nk; kt += 2) {
+      mfma_half(kt, As0, Bt0, As1);
+      decode_half(kt, Bt1, 0);
+      mfma_half(kt + 1, As1, Bt1, As0);
+      decode_half(kt + 1, Bt0, 1);
+    }
+    if (kt < nk) {
+      last_mfma(As0, Bt0);
+      last_wait();
+    }
+  } else {
+    for (; kt + 1 < nk; kt += 2) {
+      decode_half(kt, Bt1, 0);
+      mfma_half(kt, As0, Bt0, As1);
+      decode_half(kt + 1, Bt0, 1);
+      mfma_half(kt + 1, As1, Bt1, As0);
+    }
+    if (kt < nk) {
+      last_wait();
+      last_mfma(As0, Bt0);
+    }
+  }
+  wait_vmcnt<0>();
+
+  bwd_lora_up<TM, TO>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
+  bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
+}
+
 // =========================================================== LoRA down: U = s X A^T
 // Grid (M / 16 row blocks, K / 512 chunks): each workgroup's 4 waves take 128
 // of its chunk's columns each and sum their 16 x rr tiles in wave order; the
@@ -1383,10 +1538,14 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   }
 }
 
-// The DMA forward addresses its operands with 32-bit byte offsets.
+// The DMA kernels address their operands with 32-bit byte offsets.
 bool fwd_dma_ok(const FwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * (p.K / 2) < lim && p.ldx % 8 == 0;
+}
+bool bwd_dma_ok(const BwdParams& p) {
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)p.M * p.ldy * 2 < lim && ((int64_t)p.N + 64) * (p.K / 2) < lim && p.ldy % 8 == 0;
 }
 
 template <int BM, int BN, int WGM, int WGN, int WK, int EPI>
@@ -1408,7 +1567,10 @@ void launch_bwd(const BwdParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.K + BO - 1) / BO);
 #if LSQ_BWD_PP
   static_assert(BM == 256 && BO == 256 && WGM * WGN == 8, "ping-pong backward is 256 x 256 with 8 waves");
-  gemm_bwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+  if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
+    gemm_bwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+  else
+    gemm_bwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
 #else
   gemm_bwd_kernel<BM, BO, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
 #endif

@@ -146,6 +146,69 @@ def linear_gemm_rates(torch, lib, M=2048, r=16, reps=10):
     return out
 
 
+def merge_intervals(iv):
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def covered(merged, a, b):
+    return sum(max(0.0, min(b, y) - max(a, x)) for x, y in merged)
+
+
+def timeline_report(lib, entries, n_layers):
+    """Copy/compute overlap from one pass of steps: per-layer coverage of each
+    compute interval by copy activity, and each step against its copy and
+    compute sums (LS-docs "How it works": layer i+1 arrives while i computes)."""
+    copies = [(a, b) for k, _, a, b in entries if k in (lib.LSQ_TL_COPY, lib.LSQ_TL_LARGE_COPY)]
+    merged = merge_intervals(copies)
+    starts = [a for k, l, a, _ in entries if k == lib.LSQ_TL_FWD and l == 0]
+    fwd_cov = [[] for _ in range(n_layers)]
+    bwd_cov = [[] for _ in range(n_layers)]
+    steps = []
+    for si, t0 in enumerate(starts[:-1]):   # whole steps only: each ends where the next one starts
+        t1 = starts[si + 1]
+        inside = [(k, l, a, b) for k, l, a, b in entries if a >= t0 and a < t1]
+        comp = [(k, l, a, b) for k, l, a, b in inside if k in (lib.LSQ_TL_FWD, lib.LSQ_TL_BWD, lib.LSQ_TL_HEAD)]
+        for k, l, a, b in comp:
+            if b > a and k != lib.LSQ_TL_HEAD:
+                (fwd_cov if k == lib.LSQ_TL_FWD else bwd_cov)[l].append(covered(merged, a, b) / (b - a))
+        cp = [(a, b) for k, l, a, b in inside if k in (lib.LSQ_TL_COPY, lib.LSQ_TL_LARGE_COPY)]
+        sum_copy = sum(b - a for a, b in cp)
+        sum_comp = sum(b - a for _, _, a, b in comp)
+        gaps = []   # copy-stream idle stretches inside the step, with the compute pass running at their start
+        m = merge_intervals([(max(a, t0), min(b, t1)) for a, b in cp] or [(t0, t0)])
+        edges = [(t0, m[0][0])] + [(m[i][1], m[i + 1][0]) for i in range(len(m) - 1)] + [(m[-1][1], t1)]
+        name = lambda k, l: ("fwd" if k == lib.LSQ_TL_FWD else "bwd" if k == lib.LSQ_TL_BWD else "head") + \
+            (f" {l}" if l >= 0 else "")
+        for a, b in edges:
+            if b - a > 0.05:
+                run_ = [name(k, l) for k, l, x, y in comp if x <= a < y]
+                prev = [(y, name(k, l)) for k, l, x, y in comp if y <= a]
+                gaps.append({"ms": round(b - a, 3), "at_ms": round(a - t0, 3),
+                             "during": run_[0] if run_ else "no layer pass (after " +
+                             (max(prev)[1] if prev else "step start") + ")"})
+        steps.append({"step_ms": round(t1 - t0, 3), "sum_copy_ms": round(sum_copy, 3),
+                      "sum_compute_ms": round(sum_comp, 3),
+                      "bound_ms": round(max(sum_copy, sum_comp), 3),
+                      "step_over_bound": round((t1 - t0) / max(sum_copy, sum_comp), 4) if cp else None,
+                      "copy_idle_gaps": gaps})
+    mean = lambda v: round(sum(v) / len(v), 4) if v else None
+    return {
+        "per_layer_fwd_coverage": [mean(v) for v in fwd_cov],
+        "per_layer_bwd_coverage": [mean(v) for v in bwd_cov],
+        "mean_fwd_coverage": mean([x for v in fwd_cov for x in v]),
+        "mean_bwd_coverage": mean([x for v in bwd_cov for x in v]),
+        "steps": steps,
+        "note": "coverage = share of a layer pass's compute interval with a layer copy in flight; a step's copy "
+                "idle gaps name the compute pass running when the link went quiet",
+    }
+
+
 def copy_calibration(torch, nbytes=1 << 30):
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
     WRITE_SIZE counters (run under rocprofv3 --pmc)."""
@@ -254,12 +317,16 @@ def main():
     # timed region: K clean steps (per-launch kernel events cost ~5% of a step,
     # so they run in a second pass of K steps right after, below)
     runner.stats(reset=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     start = time.perf_counter()
-    for _ in range(a.steps):
+    marks[0].record()
+    for k in range(a.steps):
         runner.step(ids)
+        marks[k + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - start
+    step_ms = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(a.steps))
     st = runner.stats(reset=True)
     loss = runner.loss.item()
     # profiled pass: the same K steps with hipEvents around every timed kernel launch
@@ -275,6 +342,17 @@ def main():
     lib.call("lsq_prof_read", entries, 8, C.byref(n))
     lib.call("lsq_prof_enable", 0)
     runner.stats(reset=True)
+    # timeline pass: copy and layer-pass intervals of a few steps (events around each)
+    tl_steps = min(4, a.steps) + 1
+    runner.timeline(tl_steps * (4 * cfg.n_layers + 8))
+    for _ in range(tl_steps):
+        runner.step(ids)
+    torch.cuda.synchronize()
+    tl_entries, tl_dropped = runner.read_timeline()
+    runner.timeline(0)
+    runner.stats(reset=True)
+    overlap = timeline_report(lib, tl_entries, cfg.n_layers)
+    overlap["dropped_records"] = tl_dropped
     peak_alloc = torch.cuda.max_memory_allocated()
     # after the peak is read: torch keeps a BLAS workspace allocated once it has run a GEMM
     gprobe = gemm_probe(torch)
@@ -301,6 +379,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(ms, 3),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 3),
+        "step_ms_slowest": round(step_ms[-1], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -326,6 +406,7 @@ def main():
                 "frac_of_peak": round(h2d_gbps / PCIE_PEAK_GBPS, 4), "probe_GBps": round(probe, 2),
                 "frac_of_probe": round(h2d_gbps / probe, 4) if probe else None,
                 "link_busy_frac_of_step": round(copy_s_per_step / (ms * 1e-3), 4)},
+        "overlap": overlap,
         "kernels": {k: {"ms_per_step": round(v["ms"] / a.steps, 3), "launches_per_step": v["launches"] / a.steps,
                         "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None}
                     for k, v in prof.items()},

@@ -272,6 +272,25 @@ typedef struct {
 } lsq_pool_stats;
 int layer_pool_stats(lsq_pool* pool, int32_t reset, lsq_pool_stats* out);
 
+/* Copy/compute timeline of the steps run on a pool (the evidence for the
+ * pages' overlap claim, LS-docs "How it works": layer i+1's bytes arrive while
+ * layer i computes).  With capacity > 0, every layer copy on the copy stream
+ * and every layer pass on the compute stream (forward, backward, and the head
+ * with its loss) is bracketed by a pair of timing events; capacity 0 turns it
+ * off.  Events are recorded only while enabled and cost a few microseconds per
+ * record, so a timed measurement runs with the timeline off.  Records past the
+ * capacity are dropped (counted in `dropped`).  lsq_timeline_read waits for
+ * the recorded work, writes at most `max` entries in recording order with
+ * times in ms relative to the first entry's start, and clears the timeline. */
+enum { LSQ_TL_COPY = 0, LSQ_TL_FWD = 1, LSQ_TL_BWD = 2, LSQ_TL_HEAD = 3, LSQ_TL_LARGE_COPY = 4 };
+typedef struct {
+  int32_t kind;        /* LSQ_TL_* */
+  int32_t layer;       /* layer index (-1 for the head and its copy) */
+  double start_ms, end_ms;
+} lsq_timeline_entry;
+int lsq_timeline_enable(lsq_pool* pool, int32_t capacity);
+int lsq_timeline_read(lsq_pool* pool, lsq_timeline_entry* out, int32_t max, int32_t* n, int32_t* dropped);
+
 /* --------------------------------------------------- training step (a0..a9)
  * One streamed fwd+bwd step: embedding gather, L layers forward (prefetch one
  * ahead, acquire, layer forward, release), final RMSNorm, head GEMM, mean

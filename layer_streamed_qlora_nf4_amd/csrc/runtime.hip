@@ -346,9 +346,31 @@ struct lsq_pool {
   int tev_used = 0;
   hipEvent_t large_ready = nullptr, large_free = nullptr;  // the step's head buffer (LSQ_STEP_STREAM_LARGE)
   bool large_free_recorded = false;
+  // timeline (lsq_timeline_enable): event pairs and what each one brackets
+  std::vector<hipEvent_t> tl_ev;
+  std::vector<int32_t> tl_kind, tl_layer;
+  int tl_cap = 0, tl_used = 0, tl_dropped = 0;
 };
 
 namespace {
+// Open a timeline record on stream st; returns its index, or -1 when off or full.
+int tl_begin(lsq_pool* p, int kind, int layer, hipStream_t st) {
+  if (p->tl_cap == 0) return -1;
+  if (p->tl_used >= p->tl_cap) {
+    ++p->tl_dropped;
+    return -1;
+  }
+  const int i = p->tl_used++;
+  p->tl_kind[i] = kind;
+  p->tl_layer[i] = layer;
+  if (hipEventRecord(p->tl_ev[2 * i], st) != hipSuccess) return -1;
+  return i;
+}
+int tl_end(lsq_pool* p, int i, hipStream_t st) {
+  if (i >= 0) LSQ_HIP(hipEventRecord(p->tl_ev[2 * i + 1], st));
+  return LSQ_OK;
+}
+
 int find_slot(lsq_pool* p, int layer) {
   for (int i = 0; i < p->n; ++i)
     if (p->slots[i].layer == layer) return i;
@@ -362,8 +384,10 @@ int copy_into(lsq_pool* p, int si, int layer) {
   if (p->flags & LSQ_POOL_POISON) LSQ_HIP(hipMemsetAsync(dst, 0xFF, p->store->layer_bytes, p->copy));
   const bool timed = p->tev_used < kCopyTimers;
   if (timed) LSQ_HIP(hipEventRecord(p->tev[2 * p->tev_used], p->copy));
+  const int tl = p->resident ? -1 : tl_begin(p, LSQ_TL_COPY, layer, p->copy);
   LSQ_HIP(hipMemcpyAsync(dst, shard_store_layer_host(p->store, layer), p->store->layer_bytes, hipMemcpyHostToDevice,
                          p->copy));
+  if (int e = tl_end(p, tl, p->copy)) return e;
   if (timed) {
     LSQ_HIP(hipEventRecord(p->tev[2 * p->tev_used + 1], p->copy));
     ++p->tev_used;
@@ -424,7 +448,9 @@ int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots
 void layer_pool_destroy(lsq_pool* p) {
   if (!p) return;
   (void)hipStreamSynchronize(p->copy);
+  (void)hipStreamSynchronize(p->compute);
   for (auto& e : p->tev) (void)hipEventDestroy(e);
+  for (auto& e : p->tl_ev) (void)hipEventDestroy(e);
   for (auto& s : p->slots) {
     (void)hipEventDestroy(s.ready);
     (void)hipEventDestroy(s.free_ev);
@@ -472,6 +498,37 @@ int layer_pool_release(lsq_pool* p, int32_t layer) {
   LSQ_HIP(hipEventRecord(sl.free_ev, p->compute));
   sl.free_recorded = true;
   sl.held = false;
+  return LSQ_OK;
+}
+
+int lsq_timeline_enable(lsq_pool* p, int32_t capacity) {
+  LSQ_CHECK(p && capacity >= 0 && capacity <= (1 << 20), LSQ_ERR_INVALID, "lsq_timeline_enable: bad capacity %d",
+            capacity);
+  LSQ_HIP(hipStreamSynchronize(p->copy));
+  LSQ_HIP(hipStreamSynchronize(p->compute));
+  for (auto& e : p->tl_ev) LSQ_HIP(hipEventDestroy(e));
+  p->tl_ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& e : p->tl_ev) LSQ_HIP(hipEventCreate(&e));
+  p->tl_kind.assign(capacity, 0);
+  p->tl_layer.assign(capacity, 0);
+  p->tl_cap = capacity;
+  p->tl_used = p->tl_dropped = 0;
+  return LSQ_OK;
+}
+
+int lsq_timeline_read(lsq_pool* p, lsq_timeline_entry* out, int32_t max, int32_t* n, int32_t* dropped) {
+  LSQ_CHECK(p && n && (out || max == 0) && max >= 0, LSQ_ERR_INVALID, "lsq_timeline_read: null pointer");
+  const int cnt = std::min(p->tl_used, (int)max);
+  for (int i = 0; i < cnt; ++i) {
+    LSQ_HIP(hipEventSynchronize(p->tl_ev[2 * i + 1]));
+    float a = 0.f, b = 0.f;
+    LSQ_HIP(hipEventElapsedTime(&a, p->tl_ev[0], p->tl_ev[2 * i]));
+    LSQ_HIP(hipEventElapsedTime(&b, p->tl_ev[0], p->tl_ev[2 * i + 1]));
+    out[i] = lsq_timeline_entry{p->tl_kind[i], p->tl_layer[i], (double)a, (double)b};
+  }
+  *n = cnt;
+  if (dropped) *dropped = p->tl_dropped + (p->tl_used - cnt);
+  p->tl_used = p->tl_dropped = 0;
   return LSQ_OK;
 }
 
@@ -703,7 +760,9 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   auto queue_head_copy = [&]() -> int {
     lsq_pool* P = pool;
     if (P->large_free_recorded) LSQ_HIP(hipStreamWaitEvent(P->copy, P->large_free, 0));
+    const int tl = tl_begin(P, LSQ_TL_LARGE_COPY, -1, P->copy);
     LSQ_HIP(hipMemcpyAsync(w.head, head_src, (size_t)V * H * 2, hipMemcpyHostToDevice, P->copy));
+    if (int e = tl_end(P, tl, P->copy)) return e;
     LSQ_HIP(hipEventRecord(P->large_ready, P->copy));
     P->stats.large_copies += 1;
     P->stats.large_bytes += (uint64_t)V * H * 2;
@@ -720,6 +779,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
       if (int e = stream_layer_prefetch(pool, i + 1)) return e;
     if (large && i + 1 == L - 1)
       if (int e = queue_head_copy()) return e;
+    const int tl = tl_begin(pool, LSQ_TL_FWD, i, s);
     if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s,
                           acts_at(i)))
       return e;
@@ -730,8 +790,10 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
                             nullptr))
         return e;
     }
+    if (int e = tl_end(pool, tl, s)) return e;
     if (int e = layer_pool_release(pool, i)) return e;
   }
+  const int tl_head = tl_begin(pool, LSQ_TL_HEAD, -1, s);
   const void* head = head_src;
   if (large) {
     LSQ_HIP(hipStreamWaitEvent(s, pool->large_ready, 0));
@@ -752,12 +814,13 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     LSQ_HIP(hipEventRecord(pool->large_free, s));
     pool->large_free_recorded = true;
   }
-  if (fwd_only) return LSQ_OK;
+  if (fwd_only) return tl_end(pool, tl_head, s);
   float* dcur = w.dxa;
   float* dnext = w.dxb;
   if (int e = rmsnorm_bwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), w.dxf, nullptr, T, H, cfg->rms_eps,
                           dcur, nullptr, s))
     return e;
+  if (int e = tl_end(pool, tl_head, s)) return e;
   const size_t act = sizeof(float) * (size_t)T * H;
   if (x_trace) LSQ_HIP(hipMemcpyAsync(x_trace, xs, act * (L + 1), hipMemcpyDeviceToDevice, s));
   if (dx_trace) LSQ_HIP(hipMemcpyAsync(dx_trace + (size_t)L * T * H, dcur, act, hipMemcpyDeviceToDevice, s));
@@ -774,9 +837,11 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     AliasCtx actx{pool, i, (i + 1) % L, 0};
     LayerHook hook{early_release_hook, &actx};
     float* grad = res->lora_grad + (uint64_t)i * LL.layer_elems;
+    const int tl = tl_begin(pool, LSQ_TL_BWD, i, s);
     if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
                           s, early ? &hook : nullptr, acts_at(i)))
       return e;
+    if (int e = tl_end(pool, tl, s)) return e;
     if (!early)
       if (int e = layer_pool_release(pool, i)) return e;
     std::swap(dcur, dnext);

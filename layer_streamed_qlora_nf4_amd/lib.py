@@ -16,6 +16,7 @@ LSQ_STORE_ALLOW_PAGEABLE, LSQ_STORE_FORCE_PAGEABLE, LSQ_STORE_FAIL_PIN = 1, 2, 4
 LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
 LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS, LSQ_STEP_REFERENCE_FORWARD = 1, 2, 4, 8
 LSQ_STEP_STREAM_LARGE = 16
+LSQ_TL_COPY, LSQ_TL_FWD, LSQ_TL_BWD, LSQ_TL_HEAD, LSQ_TL_LARGE_COPY = 0, 1, 2, 3, 4
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",
           -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE",
@@ -58,6 +59,10 @@ class LayerSrc(C.Structure):
 class PoolStats(C.Structure):
     _fields_ = [("copies", C.c_uint64), ("copy_bytes", C.c_uint64), ("hits", C.c_uint64), ("copy_ms", C.c_double),
                 ("large_copies", C.c_uint64), ("large_bytes", C.c_uint64)]
+
+
+class TimelineEntry(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("layer", C.c_int32), ("start_ms", C.c_double), ("end_ms", C.c_double)]
 
 
 class Resident(C.Structure):
@@ -112,6 +117,8 @@ _SIGS = {
     "layer_pool_acquire": (C.c_int, [_P, _I32, C.POINTER(_P)]),
     "layer_pool_release": (C.c_int, [_P, _I32]),
     "layer_pool_stats": (C.c_int, [_P, _I32, C.POINTER(PoolStats)]),
+    "lsq_timeline_enable": (C.c_int, [_P, _I32]),
+    "lsq_timeline_read": (C.c_int, [_P, C.POINTER(TimelineEntry), _I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "lsq_step_workspace_size": (_SZ, [C.POINTER(ModelCfg), _I32, _I32, _I32]),
     "lsq_train_step": (C.c_int, [C.POINTER(ModelCfg), _P, C.POINTER(Resident), _P, _I32, _I32, _P, _P, _I32, _P,
                                  _SZ]),

@@ -224,6 +224,19 @@ class Runner:
         lib.call("layer_pool_stats", self.pool, int(reset), C.byref(st))
         return st
 
+    def timeline(self, capacity):
+        """Start recording copy/compute intervals (capacity records; 0 stops)."""
+        lib.call("lsq_timeline_enable", self.pool, int(capacity))
+        self._tl_cap = int(capacity)
+
+    def read_timeline(self):
+        """[(kind, layer, start_ms, end_ms)] since the last read, and the dropped count."""
+        cap = getattr(self, "_tl_cap", 0)
+        buf = (lib.TimelineEntry * max(1, cap))()
+        n, dropped = C.c_int32(), C.c_int32()
+        lib.call("lsq_timeline_read", self.pool, buf, cap, C.byref(n), C.byref(dropped))
+        return [(e.kind, e.layer, e.start_ms, e.end_ms) for e in buf[:n.value]], dropped.value
+
     def close(self):
         if self.pool:
             torch.cuda.synchronize()

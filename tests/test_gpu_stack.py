@@ -323,3 +323,43 @@ def test_large_layer_streaming_is_bit_identical(gpu):
         assert exact == total
     assert st.large_copies == 2 and st.large_bytes == 2 * 2 * cfg.vocab * cfg.hidden
     store.close()
+
+
+def test_timeline_orders_copies_before_their_layer_passes(gpu):
+    """The copy/compute timeline of a 5-layer stack over 2 slots: every layer
+    copy and layer pass is recorded once per step, each interval is well formed,
+    and no layer pass starts before the copy that filled its slot has finished
+    (the pool's ready-event handoff seen from the clock)."""
+    cfg = configs.TINY.with_(name="tiny-5L", n_layers=5, wid=41)
+    print_case(test="timeline", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    r = model.Runner(cfg, store, res)
+    r.step(ids)
+    torch.cuda.synchronize()
+    r.stats(reset=True)
+    steps = 3
+    r.timeline(steps * (3 * cfg.n_layers + 8))
+    for _ in range(steps):
+        r.step(ids)
+    torch.cuda.synchronize()
+    ent, dropped = r.read_timeline()
+    st = r.stats()
+    r.timeline(0)
+    r.close()
+    store.close()
+    assert dropped == 0
+    kinds = [e[0] for e in ent]
+    assert kinds.count(lib.LSQ_TL_COPY) == st.copies
+    assert kinds.count(lib.LSQ_TL_FWD) == steps * cfg.n_layers
+    assert kinds.count(lib.LSQ_TL_BWD) == steps * cfg.n_layers
+    assert kinds.count(lib.LSQ_TL_HEAD) == steps
+    assert all(0.0 <= a <= b for _, _, a, b in ent)
+    last_copy_end = {}
+    eps = 1e-3
+    for k, l, a, b in ent:   # recording order: a layer's copy is queued before the pass that acquires it
+        if k == lib.LSQ_TL_COPY:
+            last_copy_end[l] = b
+        elif k in (lib.LSQ_TL_FWD, lib.LSQ_TL_BWD) and l in last_copy_end:
+            assert a >= last_copy_end[l] - eps, (k, l, a, last_copy_end[l])

@@ -283,6 +283,9 @@ def main():
     ap.add_argument("--no-linears", action="store_true", help="skip the one-layer-shape linear GEMM rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only run forward passes of the stack (for per-dispatch counters of the forward GEMMs) "
+                         "and exit")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the data-parallel path is designed "
@@ -311,6 +314,14 @@ def main():
     lib.call("lsq_preflight", C.byref(lib.model_cfg(cfg)), cfg.batch, cfg.seq, cfg.n_buffers, 0, 0, C.byref(pf))
     runner = model.Runner(cfg, store, res)
     ids = torch.from_numpy(synth.token_ids(cfg.batch, cfg.seq, cfg.vocab, (cfg.wid, 500, 23))).cuda()
+    if a.forward_only:
+        for _ in range(a.warmup + a.steps):
+            runner.step(ids, forward_only=True)
+        torch.cuda.synchronize()
+        print(json.dumps({"forward_only_steps": a.warmup + a.steps, "workload": cfg.name,
+                          "loss": runner.loss.item()}))
+        runner.close()
+        return
     for _ in range(a.warmup):
         runner.step(ids)
     torch.cuda.synchronize()

@@ -472,8 +472,10 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   const int wm = grp * 2 + ((wave >> 1) & 1), wn = wave & 1;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_m = (p.M + BM - 1) / BM;
+  // Column-major tile order: the M tiles that share a weight slab are
+  // neighbours, so remap_tile puts them on one XCD and the slab leaves HBM once.
   const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
-  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
   if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K, nk_all = K / BK;
@@ -1034,8 +1036,8 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   const int wm = grp * 2 + ((wave >> 1) & 1), wo = wave & 1;
   const int tiles_o = (p.K + BO - 1) / BO;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
-  const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);   // column-major, as in the forward
+  const int m0 = (t % tiles_m) * BM, o0 = (t / tiles_m) * BO;
   if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K;

@@ -380,8 +380,10 @@ def main():
     d = prof[dominant]
     peak = peaks[dominant]
     achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
-    h2d_gbps = st.copy_bytes / (st.copy_ms * 1e-3) / 1e9 if st.copy_ms else 0.0
-    copy_s_per_step = st.copy_ms * 1e-3 / a.steps
+    # copy events cover the first 1024 copies between two stats reads: rate from those,
+    # busy time scaled to every copy of the timed steps
+    h2d_gbps = st.timed_bytes / (st.copy_ms * 1e-3) / 1e9 if st.copy_ms else 0.0
+    copy_s_per_step = st.copy_bytes / (h2d_gbps * 1e9) / a.steps if h2d_gbps else 0.0
     out = {
         "metric": "streamed LoRA fwd+bwd tok/s (8B-shape NF4); GEMM MFMA %; H2D GB/s",
         "value": round(tok_s, 2),

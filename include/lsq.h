@@ -267,8 +267,10 @@ int layer_pool_acquire(lsq_pool* pool, int32_t layer, const void** blob_dev);
 int layer_pool_release(lsq_pool* pool, int32_t layer);
 typedef struct {
   uint64_t copies, copy_bytes, hits;
-  double copy_ms;      /* summed copy durations (events on the copy stream); valid after a sync */
+  double copy_ms;      /* summed durations of the timed copies (events on the copy stream) */
   uint64_t large_copies, large_bytes;   /* head copies of LSQ_STEP_STREAM_LARGE steps */
+  uint64_t timed_copies, timed_bytes;   /* the copies copy_ms covers: at most 1024 between two
+                                           layer_pool_stats calls carry events */
 } lsq_pool_stats;
 int layer_pool_stats(lsq_pool* pool, int32_t reset, lsq_pool_stats* out);
 

@@ -391,6 +391,8 @@ int copy_into(lsq_pool* p, int si, int layer) {
   if (timed) {
     LSQ_HIP(hipEventRecord(p->tev[2 * p->tev_used + 1], p->copy));
     ++p->tev_used;
+    p->stats.timed_copies += 1;
+    p->stats.timed_bytes += p->store->layer_bytes;
   }
   LSQ_HIP(hipEventRecord(sl.ready, p->copy));
   sl.ready_recorded = true;

@@ -58,7 +58,8 @@ class LayerSrc(C.Structure):
 
 class PoolStats(C.Structure):
     _fields_ = [("copies", C.c_uint64), ("copy_bytes", C.c_uint64), ("hits", C.c_uint64), ("copy_ms", C.c_double),
-                ("large_copies", C.c_uint64), ("large_bytes", C.c_uint64)]
+                ("large_copies", C.c_uint64), ("large_bytes", C.c_uint64),
+                ("timed_copies", C.c_uint64), ("timed_bytes", C.c_uint64)]
 
 
 class TimelineEntry(C.Structure):

@@ -352,6 +352,7 @@ def test_timeline_orders_copies_before_their_layer_passes(gpu):
     assert dropped == 0
     kinds = [e[0] for e in ent]
     assert kinds.count(lib.LSQ_TL_COPY) == st.copies
+    assert st.timed_copies == st.copies and st.timed_bytes == st.copy_bytes
     assert kinds.count(lib.LSQ_TL_FWD) == steps * cfg.n_layers
     assert kinds.count(lib.LSQ_TL_BWD) == steps * cfg.n_layers
     assert kinds.count(lib.LSQ_TL_HEAD) == steps

@@ -1415,6 +1415,131 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
   }
 }
 
+// The same reductions on the matrix cores.  out[a][b] = sum over tokens of
+// S[m][a] L[m][b] is an MFMA product with the tokens as its reduction: each
+// k-step stages 64 tokens of L (128 columns) and of S (all small indices)
+// in LDS transposed, token-major per column, so a lane's 8 reduction values
+// are contiguous.  S is float32; it enters the bf16 MFMA as a hi/lo pair
+// (hi = bf16(S), lo = bf16(S - hi)), which carries 16 of S's 24 mantissa bits
+// into an exact product with L's bf16 values and float32 accumulation.  Each
+// workgroup owns every small index of 128 columns over all tokens, in a fixed
+// order: no partials, no atomics.
+constexpr int TNM_COLS = 128, TNM_TOK = 64;
+__global__ void __launch_bounds__(NTHREADS) lora_grads_mfma_kernel(TnBatch bt) {
+  __shared__ __attribute__((aligned(16))) uint16_t LT[TNM_COLS][TNM_TOK + 8];   // [column][token], bf16
+  __shared__ __attribute__((aligned(16))) float ST[64][TNM_TOK + 4];            // [small index][token]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  TnTask tk = bt.t[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    if (i < bt.ntasks && (int)blockIdx.x >= bt.t[i].tile0) tk = bt.t[i];
+  const int b0 = (blockIdx.x - tk.tile0) * TNM_COLS;
+  const int ns = tk.ns, M = bt.M;
+  // this thread's L micro-tile (4 tokens x 8 columns) and S row (one token, 16 small indices)
+  const int lr = 4 * (tid >> 4), lc = 8 * (tid & 15);
+  const int scol = b0 + lc;
+  const int sa = 16 * wave;
+  uint4 lv[4];
+  float4 sv[4];
+  auto load = [&](int m0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + lr + i;
+      const uint16_t* row = tk.L + (int64_t)m * tk.ldl + scol;
+      if (m < M && scol + 8 <= tk.nl) {
+        lv[i] = *reinterpret_cast<const uint4*>(row);
+      } else if (m < M && scol + 4 <= tk.nl) {
+        const uint2 h = *reinterpret_cast<const uint2*>(row);
+        lv[i] = make_uint4(h.x, h.y, 0u, 0u);
+      } else {
+        lv[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const int m = m0 + lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = sa + 4 * q;
+      sv[q] = (m < M && a < ns) ? *reinterpret_cast<const float4*>(tk.S + (int64_t)m * tk.lds + a)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&]() __attribute__((always_inline)) {
+    const uint32_t w[4][4] = {{lv[0].x, lv[0].y, lv[0].z, lv[0].w}, {lv[1].x, lv[1].y, lv[1].z, lv[1].w},
+                              {lv[2].x, lv[2].y, lv[2].z, lv[2].w}, {lv[3].x, lv[3].y, lv[3].z, lv[3].w}};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int sel = (c & 1) ? 0x07060302 : 0x05040100;   // high or low bf16 of each token's word
+      const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
+      *reinterpret_cast<u32x2*>(&LT[lc + c][lr]) = u32x2{lo, hi};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ST[sa + 4 * q + 0][lane] = sv[q].x;
+      ST[sa + 4 * q + 1][lane] = sv[q].y;
+      ST[sa + 4 * q + 2][lane] = sv[q].z;
+      ST[sa + 4 * q + 3][lane] = sv[q].w;
+    }
+  };
+  const int J = (ns + 15) / 16;
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int m0 = 0; m0 < M; m0 += TNM_TOK) {
+    __syncthreads();   // the previous k-step's fragment reads are done
+    store();
+    __syncthreads();
+    if (m0 + TNM_TOK < M) load(m0 + TNM_TOK);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int t0 = 32 * kb + 8 * (lane >> 4);
+      bf16x8 bfr[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        bfr[c] = *reinterpret_cast<const bf16x8*>(&LT[32 * wave + 16 * c + (lane & 15)][t0]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g >= J) break;
+        const float* srow = &ST[16 * g + (lane & 15)][t0];
+        const float4 f0 = *reinterpret_cast<const float4*>(srow);
+        const float4 f1 = *reinterpret_cast<const float4*>(srow + 4);
+        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          hw[t] = pack_bf16x2(f[2 * t], f[2 * t + 1]);
+          lw[t] = pack_bf16x2(f[2 * t] - bf_lo(hw[t]), f[2 * t + 1] - bf_hi(hw[t]));
+        }
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          acc[g][c] = mfma16(ahi, bfr[c], acc[g][c]);
+          acc[g][c] = mfma16(alo, bfr[c], acc[g][c]);
+        }
+      }
+    }
+  }
+  // lane holds C[4 (lane >> 4) + v][lane & 15]: small index row, column
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g >= J) break;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int b = b0 + 32 * wave + 16 * c + (lane & 15);
+      if (b >= tk.nl) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int a = 16 * g + 4 * (lane >> 4) + v;
+        if (a >= ns) continue;
+        const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
+        tk.out[o] = bt.accumulate ? tk.out[o] + acc[g][c][v] : acc[g][c][v];
+      }
+    }
+  }
+}
+
 // G finish for several segments at once: segment s sums chunks [c0, c1) of part.
 __global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinish sf, int M, int r, float s,
                                         uint16_t* __restrict__ dst, int64_t ld, float* __restrict__ dst32,
@@ -1800,18 +1925,25 @@ int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int
 int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream_t st) {
   LSQ_CHECK(ntasks >= 1 && ntasks <= 8, LSQ_ERR_INVALID, "lora_grads: 1..8 tasks");
   TnBatch bt{};
-  int tiles = 0;
+  int tiles = 0, mtiles = 0;
+  bool mfma = true;   // every task's large side in 16-byte rows: the matrix-core kernel
   double flops = 0, bytes = 0;
   for (int i = 0; i < ntasks; ++i) {
     const TnTask& t = tasks[i];
     LSQ_CHECK(t.ns >= 8 && t.ns <= 64 && t.ns % 8 == 0 && t.nl % 4 == 0 && t.ldl % 4 == 0 && t.lds % 4 == 0 &&
                   (reinterpret_cast<uintptr_t>(t.S) & 15) == 0 && (reinterpret_cast<uintptr_t>(t.L) & 7) == 0,
               LSQ_ERR_SHAPE, "lora_grads: task %d shape/alignment", i);
+    mfma = mfma && t.ldl % 8 == 0 && (reinterpret_cast<uintptr_t>(t.L) & 15) == 0;
     bt.t[i] = t;
-    bt.t[i].tile0 = tiles;
     tiles += ((t.nl + 255) / 256) * ((t.ns + 15) / 16);
+    mtiles += (t.nl + TNM_COLS - 1) / TNM_COLS;
     flops += 2.0 * M * (double)t.ns * t.nl;
     bytes += 4.0 * M * (double)t.ns + 2.0 * M * (double)t.nl + 4.0 * t.ns * t.nl;
+  }
+  for (int i = 0, acc_t = 0; i < ntasks; ++i) {
+    bt.t[i].tile0 = acc_t;
+    acc_t += mfma ? (tasks[i].nl + TNM_COLS - 1) / TNM_COLS
+                  : ((tasks[i].nl + 255) / 256) * ((tasks[i].ns + 15) / 16);
   }
   bt.ntasks = ntasks;
   bt.M = M;
@@ -1825,7 +1957,10 @@ int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream
     return LSQ_OK;
   }
   int tok = prof_begin(st);
-  lora_grads_kernel<<<tiles, NTHREADS, 0, st>>>(bt);
+  if (mfma)
+    lora_grads_mfma_kernel<<<mtiles, NTHREADS, 0, st>>>(bt);
+  else
+    lora_grads_kernel<<<tiles, NTHREADS, 0, st>>>(bt);
   prof_end(tok, st, PROF_LORA, flops, bytes);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

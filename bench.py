@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
-HBM_PEAK_GBPS = 8000.0
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 PCIE_PEAK_GBPS = 64.0            # PCIe 5.0 x16, one direction, theoretical
 
 
@@ -209,6 +209,30 @@ def timeline_report(lib, entries, n_layers):
     }
 
 
+def dequant_rate(torch, lib, N=28672, K=4096, reps=20):
+    """nf4_dequantize of one 8B gate/up weight (bf16 out), HBM bytes per second:
+    0.5625 B read (codes and scales) + 2 B written per weight."""
+    st = lib.stream_handle(torch.cuda.current_stream())
+    packed = torch.randint(0, 255, (N, K // 2), dtype=torch.uint8, device="cuda")
+    absmax = torch.rand((N, K // 64), device="cuda")
+    out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    P = lambda t: C.c_void_p(t.data_ptr())
+    run = lambda: lib.call("nf4_dequantize", P(packed), P(absmax), N, K, lib.LSQ_BF16, P(out), st)
+    for _ in range(3):
+        run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = 2.5625 * N * K
+    del packed, absmax, out
+    return {"shape": f"{N}x{K}", "avg_launch_us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes_per_launch": nbytes}
+
+
 def copy_calibration(torch, nbytes=1 << 30):
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
     WRITE_SIZE counters (run under rocprofv3 --pmc)."""
@@ -368,6 +392,7 @@ def main():
     # after the peak is read: torch keeps a BLAS workspace allocated once it has run a GEMM
     gprobe = gemm_probe(torch)
     linears = None if a.no_linears else linear_gemm_rates(torch, lib)
+    dequant = dequant_rate(torch, lib)
     log(f"bf16 GEMM probe (torch.mm 8192^3): {gprobe:.0f} TFLOP/s")
 
     ms = elapsed / a.steps * 1e3
@@ -421,8 +446,17 @@ def main():
                 "link_busy_frac_of_step": round(copy_s_per_step / (ms * 1e-3), 4)},
         "overlap": overlap,
         "kernels": {k: {"ms_per_step": round(v["ms"] / a.steps, 3), "launches_per_step": v["launches"] / a.steps,
-                        "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None}
+                        "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None,
+                        "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] and v["bytes"] else None}
                     for k, v in prof.items()},
+        "hbm_bound": {
+            "elementwise": {"GBps": round(prof["elementwise"]["bytes"] / (prof["elementwise"]["ms"] * 1e-3) / 1e9, 1),
+                            "peak_GBps": HBM_PEAK_GBPS,
+                            "frac_of_peak": round(prof["elementwise"]["bytes"] / (prof["elementwise"]["ms"] * 1e-3)
+                                                  / 1e9 / HBM_PEAK_GBPS, 4),
+                            "kernels": "rmsnorm fwd/bwd, swiglu fwd/bwd, embedding gather, cross-entropy rows"}
+            if prof.get("elementwise", {}).get("ms") else None,
+            "nf4_dequantize": dequant},
         "linear_gemms_T2048": linears,
         "preflight_predicted_bytes": pf.total,
         "peak_allocated_bytes": peak_alloc,

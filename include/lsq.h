@@ -396,12 +396,15 @@ int lsq_preflight(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t 
  * When enabled, every launch of the timed kernel families is bracketed by
  * hipEvents on its own stream (library-owned event pool) and credited with its
  * algorithmic flops and bytes.  lsq_prof_read synchronizes the events and
- * fills one entry per family (it needs at least 6 entries):
+ * fills one entry per family (it needs at least 7 entries):
  *   gemm_fwd_nf4_lora, gemm_bwd_nf4_lora  the NF4-weight tile kernels alone
  *   lora_skinny        rank-r down-projection, G and adapter-gradient kernels
  *   attention          attention forward and backward kernels
- *   other              split-K reductions
+ *   other              split-K reductions, transposes of the adapters
  *   gemm_bf16_weights  tile kernels over bf16 weights (bf16 base, the head)
+ *   elementwise        RMSNorm forward and backward, SwiGLU forward and
+ *                      backward, the embedding gather and the cross-entropy
+ *                      rows: bytes = each operand read once and written once
  * Enabling resets the counts. */
 typedef struct {
   char name[48];

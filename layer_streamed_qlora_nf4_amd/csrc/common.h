@@ -62,7 +62,8 @@ enum ProfKind {
   PROF_ATTN = 3,
   PROF_OTHER = 4,
   PROF_GEMM_BF16 = 5,  // bf16-weight tile kernels (bf16 base, the head), both directions
-  PROF_N = 6
+  PROF_ELEM = 6,       // HBM-bound row and elementwise kernels (norms, SwiGLU, gather, cross-entropy)
+  PROF_N = 7
 };
 bool prof_on();
 // Returns an opaque token; prof_end credits flops/bytes to the family.

@@ -46,7 +46,7 @@ struct Prof {
   int dropped = 0;
 } g_prof;
 const char* kNames[PROF_N] = {"gemm_fwd_nf4_lora", "gemm_bwd_nf4_lora", "lora_skinny", "attention", "other",
-                              "gemm_bf16_weights"};
+                              "gemm_bf16_weights", "elementwise"};
 }  // namespace
 
 bool prof_on() { return g_prof.on; }

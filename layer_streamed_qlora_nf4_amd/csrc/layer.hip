@@ -28,6 +28,8 @@ int check_cfg(const lsq_model_cfg* c) {
             LSQ_ERR_SHAPE,
             "model cfg: need hidden, intermediate multiples of 64, head_dim 64/128, heads divisible, vocab %% 8 == 0");
   LSQ_CHECK((c->n_heads * c->head_dim) % 64 == 0, LSQ_ERR_SHAPE, "model cfg: n_heads*head_dim %% 64 != 0");
+  LSQ_CHECK(c->hidden <= 8192, LSQ_ERR_SHAPE, "model cfg: hidden %d above 8192 (RMSNorm keeps a row in registers)",
+            c->hidden);
   LSQ_CHECK(c->weight_kind == LSQ_W_NF4 || c->weight_kind == LSQ_W_BF16, LSQ_ERR_INVALID, "model cfg: weight_kind");
   LSQ_CHECK(c->lora_r >= 8 && c->lora_r <= 64 && c->lora_r % 8 == 0, LSQ_ERR_SHAPE,
             "model cfg: lora_r must be 8..64 and a multiple of 8 (got %d)", c->lora_r);

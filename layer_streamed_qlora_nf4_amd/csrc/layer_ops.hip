@@ -23,32 +23,50 @@ __device__ __forceinline__ float warp_sum(float v) {
 }
 
 // ------------------------------------------------------------------ RMSNorm
-// One wave per row: y = bf16(w * x / sqrt(mean(x^2) + eps)); rstd saved.
-// With y_lo, the output is also written as the bf16 rounding of its own
-// remainder (y ~ y + y_lo to about 16 bits), for GEMMs run as two bf16 passes.
+// One workgroup (4 waves) per row, the row held in registers: each thread
+// owns float4 groups tid, tid + 256, ... (up to 8, i.e. H <= 8192), so the row
+// is read from HBM once and 256 threads keep loads in flight.  The sums meet
+// in a fixed order (wave shuffles, then the 4 wave totals in LDS in wave order).
+constexpr int kNormMaxV = 8;
+__device__ __forceinline__ float block4_sum(float v, float* red) {
+  v = warp_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();   // red is reused by the next call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// y = bf16(w * x / sqrt(mean(x^2) + eps)); rstd saved.  With y_lo, the output
+// is also written as the bf16 rounding of its own remainder (y ~ y + y_lo to
+// about 16 bits), for GEMMs run as two bf16 passes.
 __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
                                                           int T, int H, float eps, uint16_t* __restrict__ y,
                                                           float* __restrict__ rstd, uint16_t* __restrict__ y_lo) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= T) return;
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
   const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
+  float4 v[kNormMaxV];
   float ss = 0.f;
-  for (int i = lane; i < H / 4; i += 64) {
-    float4 v = xr[i];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int k = 0; k < kNormMaxV; ++k) {
+    const int i = tid + 256 * k;
+    v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
-  ss = warp_sum(ss);
+  ss = block4_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if (rstd && lane == 0) rstd[row] = r;
+  if (rstd && tid == 0) rstd[row] = r;
   const uint2* wr = reinterpret_cast<const uint2*>(w);
   uint2* yr = reinterpret_cast<uint2*>(y + (int64_t)row * H);
   uint2* lr = y_lo ? reinterpret_cast<uint2*>(y_lo + (int64_t)row * H) : nullptr;
-  for (int i = lane; i < H / 4; i += 64) {
-    float4 v = xr[i];
-    uint2 ww = wr[i];
-    const float o0 = bf_lo(ww.x) * (v.x * r), o1 = bf_hi(ww.x) * (v.y * r);
-    const float o2 = bf_lo(ww.y) * (v.z * r), o3 = bf_hi(ww.y) * (v.w * r);
+#pragma unroll
+  for (int k = 0; k < kNormMaxV; ++k) {
+    const int i = tid + 256 * k;
+    if (i >= n4) continue;
+    const uint2 ww = wr[i];
+    const float o0 = bf_lo(ww.x) * (v[k].x * r), o1 = bf_hi(ww.x) * (v[k].y * r);
+    const float o2 = bf_lo(ww.y) * (v[k].z * r), o3 = bf_hi(ww.y) * (v[k].w * r);
     const uint2 hi = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
     yr[i] = hi;
     if (lr)
@@ -61,36 +79,43 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
                                                           const float* __restrict__ dy, const float* __restrict__ gres,
                                                           int T, int H, float eps, float* __restrict__ dx,
                                                           uint16_t* __restrict__ dx_b) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= T) return;
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
   const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
   const float4* dr = reinterpret_cast<const float4*>(dy + (int64_t)row * H);
   const uint2* wr = reinterpret_cast<const uint2*>(w);
+  float4 v[kNormMaxV], d[kNormMaxV];
   float ss = 0.f, dot = 0.f;
-  for (int i = lane; i < H / 4; i += 64) {
-    float4 v = xr[i], d = dr[i];
-    uint2 ww = wr[i];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    dot += bf_lo(ww.x) * d.x * v.x + bf_hi(ww.x) * d.y * v.y + bf_lo(ww.y) * d.z * v.z + bf_hi(ww.y) * d.w * v.w;
+#pragma unroll
+  for (int k = 0; k < kNormMaxV; ++k) {
+    const int i = tid + 256 * k;
+    const bool ok = i < n4;
+    v[k] = ok ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    d[k] = ok ? dr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint2 ww = ok ? wr[i] : make_uint2(0u, 0u);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    dot += bf_lo(ww.x) * d[k].x * v[k].x + bf_hi(ww.x) * d[k].y * v[k].y + bf_lo(ww.y) * d[k].z * v[k].z +
+           bf_hi(ww.y) * d[k].w * v[k].w;
   }
-  ss = warp_sum(ss);
-  dot = warp_sum(dot);
+  ss = block4_sum(ss, red);
+  dot = block4_sum(dot, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
   const float c = r * r * r * dot / (float)H;
   float4* outr = reinterpret_cast<float4*>(dx + (int64_t)row * H);
   const float4* gr = gres ? reinterpret_cast<const float4*>(gres + (int64_t)row * H) : nullptr;
   uint2* ob = dx_b ? reinterpret_cast<uint2*>(dx_b + (int64_t)row * H) : nullptr;
-  for (int i = lane; i < H / 4; i += 64) {
-    float4 v = xr[i], d = dr[i];
-    uint2 ww = wr[i];
+#pragma unroll
+  for (int k = 0; k < kNormMaxV; ++k) {
+    const int i = tid + 256 * k;
+    if (i >= n4) continue;
+    const uint2 ww = wr[i];
     float4 o;
-    o.x = r * bf_lo(ww.x) * d.x - v.x * c;
-    o.y = r * bf_hi(ww.x) * d.y - v.y * c;
-    o.z = r * bf_lo(ww.y) * d.z - v.z * c;
-    o.w = r * bf_hi(ww.y) * d.w - v.w * c;
+    o.x = r * bf_lo(ww.x) * d[k].x - v[k].x * c;
+    o.y = r * bf_hi(ww.x) * d[k].y - v[k].y * c;
+    o.z = r * bf_lo(ww.y) * d[k].z - v[k].z * c;
+    o.w = r * bf_hi(ww.y) * d[k].w - v[k].w * c;
     if (gr) {
-      float4 g = gr[i];
+      const float4 g = gr[i];
       o.x += g.x;
       o.y += g.y;
       o.z += g.z;
@@ -712,17 +737,25 @@ size_t attn_bwd_smem() { return sizeof(AttnBwdSmem<HD>); }
 // ================================================================== launchers
 int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
                 uint16_t* y_lo) {
-  LSQ_CHECK(H % 4 == 0, LSQ_ERR_SHAPE, "rmsnorm: hidden %d must be a multiple of 4", H);
+  LSQ_CHECK(H % 4 == 0 && H <= 4 * 256 * kNormMaxV, LSQ_ERR_SHAPE,
+            "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
   if (T == 0) return LSQ_OK;
-  rmsnorm_fwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, w, T, H, eps, y, rstd, y_lo);
+  const int tok = prof_begin(s);
+  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(x, w, T, H, eps, y, rstd, y_lo);
+  prof_end(tok, s, PROF_ELEM, 0.0, (4.0 + 2.0 + (y_lo ? 2.0 : 0.0)) * T * (double)H + 2.0 * H + (rstd ? 4.0 * T : 0.0));
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
 int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
                 float* dx, uint16_t* dx_b, hipStream_t s) {
+  LSQ_CHECK(H % 4 == 0 && H <= 4 * 256 * kNormMaxV, LSQ_ERR_SHAPE,
+            "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
   if (T == 0) return LSQ_OK;
-  rmsnorm_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, w, dy, gres, T, H, eps, dx, dx_b);
+  const int tok = prof_begin(s);
+  rmsnorm_bwd_kernel<<<T, 256, 0, s>>>(x, w, dy, gres, T, H, eps, dx, dx_b);
+  prof_end(tok, s, PROF_ELEM, 0.0,
+           (4.0 + 4.0 + 4.0 + (gres ? 4.0 : 0.0) + (dx_b ? 2.0 : 0.0)) * T * (double)H + 2.0 * H);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -819,7 +852,9 @@ int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s) {
   LSQ_CHECK(I % 2 == 0, LSQ_ERR_SHAPE, "swiglu: odd intermediate");
   const int64_t n = (int64_t)T * I / 2;
   if (n == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
   swiglu_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, T, I, m);
+  prof_end(tok, s, PROF_ELEM, 0.0, 6.0 * T * (double)I);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -827,7 +862,9 @@ int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s) {
 int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* dgu, hipStream_t s) {
   const int64_t n = (int64_t)T * I / 2;
   if (n == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
   swiglu_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, dm, T, I, dgu);
+  prof_end(tok, s, PROF_ELEM, 0.0, 10.0 * T * (double)I);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -836,7 +873,9 @@ int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V,
   LSQ_CHECK(H % 4 == 0, LSQ_ERR_SHAPE, "embed: hidden %% 4 != 0");
   const int64_t n = (int64_t)T * H / 4;
   if (n == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
   embed_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ids, table, T, H, V, x, bad);
+  prof_end(tok, s, PROF_ELEM, 0.0, 6.0 * T * (double)H + 4.0 * T);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -846,7 +885,10 @@ int cross_entropy_rows(const float* logits, const int32_t* ids, int B, int S, in
   LSQ_CHECK(V % 4 == 0 && row0 >= 0 && nrows >= 0 && row0 + nrows <= B * S, LSQ_ERR_SHAPE, "cross_entropy: bad rows");
   if (nrows == 0) return LSQ_OK;
   const float inv_count = S > 1 ? 1.f / (float)(B * (S - 1)) : 0.f;
+  const int tok = prof_begin(s);
   ce_kernel<<<nrows, kCeThreads, 0, s>>>(logits, ids, row0, S, V, inv_count, loss_rows, dlogits, dlogits_lo);
+  prof_end(tok, s, PROF_ELEM, 0.0,
+           (4.0 + (dlogits ? 2.0 : 0.0) + (dlogits_lo ? 2.0 : 0.0)) * nrows * (double)V + 8.0 * nrows);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }

@@ -85,36 +85,38 @@ __global__ void __launch_bounds__(256) nf4_quantize_kernel(const uint16_t* __res
   absmax[b] = a;
 }
 
-// One thread per 8 packed bytes (16 weights, inside one block).
+// One thread per 16 packed bytes (32 weights, half of one 64-weight block):
+// one 16-byte load, the 16 levels from LDS, 64 (bf16) or 128 (fp32) bytes out.
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ packed,
                                                           const float* __restrict__ absmax, int64_t n_chunks,
                                                           void* __restrict__ out) {
-  int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = lsq::kNF4LevelsDev[threadIdx.x];
+  __syncthreads();
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (c >= n_chunks) return;
-  u32x2 p = *reinterpret_cast<const u32x2*>(packed + c * 8);
-  float a = absmax[c >> 2];
-  float vals[16];
+  const uint4 p = *reinterpret_cast<const uint4*>(packed + c * 16);
+  const float a = absmax[c >> 1];
+  const uint32_t words[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-  for (int w = 0; w < 2; ++w) {
+  for (int w = 0; w < 4; ++w) {
+    float vals[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t byte = (p[w] >> (8 * j)) & 0xFF;
-      vals[w * 8 + 2 * j] = lsq::kNF4LevelsDev[byte >> 4] * a;
-      vals[w * 8 + 2 * j + 1] = lsq::kNF4LevelsDev[byte & 15] * a;
+      const uint32_t byte = (words[w] >> (8 * j)) & 0xFF;
+      vals[2 * j] = lut[byte >> 4] * a;
+      vals[2 * j + 1] = lut[byte & 15] * a;
     }
-  }
-  if (OUT_F32) {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + c * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = make_float4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]);
-  } else {
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(vals[2 * i], vals[2 * i + 1]);
-    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + c * 16);
-    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if (OUT_F32) {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + c * 32 + w * 8);
+      o[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
+      o[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
+    } else {
+      uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + c * 32 + w * 8);
+      *o = make_uint4(pack_bf16x2(vals[0], vals[1]), pack_bf16x2(vals[2], vals[3]), pack_bf16x2(vals[4], vals[5]),
+                      pack_bf16x2(vals[6], vals[7]));
+    }
   }
 }
 
@@ -158,7 +160,7 @@ int nf4_dequantize(const void* packed_dev, const float* absmax_dev, int64_t n_ou
             "nf4_dequantize: n_in must be a multiple of 64");
   LSQ_CHECK(lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev) && lsq::aligned16(w_out_dev), LSQ_ERR_ALIGN,
             "nf4_dequantize: pointers must be 16-byte aligned");
-  int64_t n_chunks = n_out * n_in / 16;
+  int64_t n_chunks = n_out * n_in / 32;
   if (n_chunks == 0) return LSQ_OK;
   dim3 grid(static_cast<unsigned>((n_chunks + 255) / 256));
   hipStream_t s = lsq::as_stream(stream);

@@ -87,7 +87,7 @@ def gemm_probe(torch, n=8192, reps=10):
     return tflops
 
 
-def linear_gemm_rates(torch, lib, M=2048, r=16, reps=10):
+def linear_gemm_rates(torch, lib, M=2048, r=16, reps=10, only=None):
     """The fused NF4-LoRA linears at the one-layer 8B shapes (T = 2048 tokens):
     forward and backward tile kernels timed by the library's events, each
     against the bf16 MFMA peak.  Seeded random NF4 codes and scales."""
@@ -99,6 +99,8 @@ def linear_gemm_rates(torch, lib, M=2048, r=16, reps=10):
     g.manual_seed(2048)
     out = {}
     for name, (N, K) in shapes.items():
+        if only and name != only:
+            continue
         packed = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
         absmax = torch.rand((N, K // 64), device="cuda", generator=g) * 0.05
         X = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
@@ -307,6 +309,11 @@ def main():
     ap.add_argument("--no-linears", action="store_true", help="skip the one-layer-shape linear GEMM rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--linear", default=None, metavar="NAME",
+                    help="only time one fused linear of the 8B layer at 2048 tokens (qkv, o, gate_up or down), "
+                         "forward and backward, print its rates and exit (for per-kernel counters)")
+    ap.add_argument("--mm-probe", action="store_true",
+                    help="only run the torch.mm bf16 8192^3 probe, print it and exit (for counters)")
     ap.add_argument("--forward-only", action="store_true",
                     help="only run forward passes of the stack (for per-dispatch counters of the forward GEMMs) "
                          "and exit")
@@ -319,6 +326,14 @@ def main():
     import torch
     if a.copy_calibration:
         copy_calibration(torch)
+        return
+    if a.mm_probe:
+        print(json.dumps({"torch_mm_bf16_8192_TFLOPs": round(gemm_probe(torch), 1)}))
+        return
+    if a.linear:
+        from layer_streamed_qlora_nf4_amd import lib as lib_
+        lib_.load()
+        print(json.dumps(linear_gemm_rates(torch, lib_, only=a.linear)))
         return
     from layer_streamed_qlora_nf4_amd import configs, lib, model, synth
     lib.load()

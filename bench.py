@@ -272,11 +272,19 @@ def cpu_baseline(cfg):
             W[k] = f64(w[k])
     ad = {n: (f64(a), f64(b)) for n, (a, b) in synth.layer_lora(cfg, cfg.wid, 0).items()}
     del w
-    t0 = time.perf_counter()
-    out = olayer.layer_fwd(oc, x, W, ad, cfg.lora_scale)
-    t1 = time.perf_counter()
-    olayer.layer_bwd(oc, x, W, ad, cfg.lora_scale, out)
-    t2 = time.perf_counter()
+    # repeat the layer (fresh inputs each time) until about 8 s of CPU work
+    fwd_s = bwd_s = 0.0
+    reps = 0
+    while reps < 12 and (reps == 0 or fwd_s + bwd_s < 8.0):
+        xr = x if reps == 0 else f64(synth.normal_bf16((B, S, H), 0, 1, (7, 7, 7 + reps)))
+        t0 = time.perf_counter()
+        out = olayer.layer_fwd(oc, xr, W, ad, cfg.lora_scale)
+        t1 = time.perf_counter()
+        olayer.layer_bwd(oc, xr, W, ad, cfg.lora_scale, out)
+        t2 = time.perf_counter()
+        fwd_s += t1 - t0
+        bwd_s += t2 - t1
+        reps += 1
     rw = synth.resident_weights(cfg.with_(vocab=cfg.vocab), cfg.wid)
     head = synth.bits_to_f32(rw["head"]).astype(np.float64)
     ids = synth.token_ids(B, S, cfg.vocab, (1, 2, 3)).astype(np.int64)
@@ -285,16 +293,17 @@ def cpu_baseline(cfg):
     _, dl = omodel.ce_loss_and_grad(logits, ids)
     dl.reshape(-1, cfg.vocab) @ head
     t4 = time.perf_counter()
-    step_s = cfg.n_layers * ((t1 - t0) + (t2 - t1)) + (t4 - t3)
+    step_s = cfg.n_layers * (fwd_s + bwd_s) / reps + (t4 - t3)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(cfg.tokens / step_s, 3), "unit": "tok/s", "cores": min(cores, threads), "kind": "oracle",
-            "sample": (f"one {cfg.name} decoder layer forward ({t1 - t0:.1f} s) and backward with recompute "
-                       f"({t2 - t1:.1f} s) in float64 at {B}x{S} tokens, times {cfg.n_layers} layers, plus the "
-                       f"head and cross-entropy ({t4 - t3:.1f} s); {t4 - t0:.0f} s of CPU work")}
+            "sample": (f"one {cfg.name} decoder layer forward ({fwd_s / reps:.2f} s) and backward with recompute "
+                       f"({bwd_s / reps:.2f} s) in float64 at {B}x{S} tokens, averaged over {reps} runs and "
+                       f"times {cfg.n_layers} layers, plus the head and cross-entropy ({t4 - t3:.1f} s); "
+                       f"{fwd_s + bwd_s + t4 - t3:.0f} s of CPU work")}
 
 
 def main():

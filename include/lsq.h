@@ -333,6 +333,18 @@ enum {
                                        on the pool's copy stream, after the last
                                        layer copy of the forward.  Refused for
                                        tied models.                              */
+  LSQ_STEP_RECOMPUTE_ALL = 32,       /* recompute every layer in the backward.
+                                       Without it (and without
+                                       LSQ_STEP_KEEP_ACTIVATIONS) a step keeps
+                                       the forward activations of layers L-1, 1
+                                       and 0: their backward passes run while
+                                       both slots hold layers still needed and
+                                       the copy stream has nothing to do (the
+                                       forward/backward turn and the step's
+                                       tail), so their recompute would sit on
+                                       the step's critical path.  Every other
+                                       layer is recomputed under its copy.
+                                       Results are bit-identical either way. */
   LSQ_STEP_REFERENCE_FORWARD = 8     /* preference losses (LS-docs "Preference
                                        losses over streaming"; Editorial "The
                                        Honest Cost"): also run the reference
@@ -344,7 +356,8 @@ enum {
                                        per step.  Needs lsq_step_extra outputs. */
 };
 /* Workspace of a step run with `flags` (LSQ_STEP_KEEP_ACTIVATIONS adds
- * n_layers kept-activation regions). */
+ * n_layers kept-activation regions, the default min(n_layers, 3), and
+ * LSQ_STEP_RECOMPUTE_ALL none). */
 size_t lsq_step_workspace_size(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int32_t flags);
 /* ids_dev int32 [batch, seq]; loss_dev float32 [1]; logits_out float32
  * [batch*seq, vocab] (nullable). */

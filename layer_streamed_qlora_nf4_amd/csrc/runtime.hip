@@ -570,15 +570,35 @@ struct StepWs {
   size_t gemm_bytes;
   void* layer;       // layer workspace
   size_t layer_bytes;
-  char* acts;        // keep mode: n_layers x acts_bytes of kept forward activations
+  char* acts;        // n_kept x acts_bytes of kept forward activations
   size_t acts_bytes;
+  int n_kept;
   float* xr[2];      // reference mode: the adapters-off residual stream, ping-pong [T, H]
   float* ref_loss_tmp;  // reference mode: its mean loss when the caller wants rows only
   size_t total;
 };
 
+// Layers whose forward activations a step keeps: all of them under
+// LSQ_STEP_KEEP_ACTIVATIONS, none under LSQ_STEP_RECOMPUTE_ALL, else the ones
+// whose backward runs while the copy stream idles (L-1 at the turn, 1 and 0 at
+// the tail).  Returns the count; slot[i] = the layer's region index or -1.
+int kept_layers(const lsq_model_cfg* c, int32_t flags, std::vector<int>* slot_out) {
+  const int L = c->n_layers;
+  std::vector<int> slot(L, -1);
+  int n = 0;
+  if (flags & LSQ_STEP_KEEP_ACTIVATIONS) {
+    for (int i = 0; i < L; ++i) slot[i] = n++;
+  } else if (!(flags & (LSQ_STEP_RECOMPUTE_ALL | LSQ_STEP_FORWARD_ONLY))) {
+    for (int i : {L - 1, 1, 0})
+      if (i >= 0 && i < L && slot[i] < 0) slot[i] = n++;
+  }
+  if (slot_out) *slot_out = std::move(slot);
+  return n;
+}
+
 StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flags) {
   const bool keep = flags & LSQ_STEP_KEEP_ACTIVATIONS;
+  const int n_kept = kept_layers(c, flags, nullptr);
   const uint64_t T = (uint64_t)B * S, H = c->hidden, V = c->vocab;
   StepWs w{};
   uint64_t off = 0;
@@ -608,10 +628,11 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
   w.gemm = take(w.gemm_bytes);
   w.layer_bytes = layer_ws_bytes(c, B, S, keep);
   w.layer = take(w.layer_bytes);
-  if (keep) {
+  if (n_kept > 0) {
     w.acts_bytes = layer_acts_bytes(c, B, S);
-    w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)c->n_layers));
+    w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)n_kept));
   }
+  w.n_kept = n_kept;
   if (flags & LSQ_STEP_REFERENCE_FORWARD) {
     w.xr[0] = static_cast<float*>(take(4 * T * H));
     w.xr[1] = static_cast<float*>(take(4 * T * H));
@@ -721,8 +742,10 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   LSQ_CHECK(B >= 1 && S >= 2 && (int64_t)B * S < (1 << 24), LSQ_ERR_SHAPE, "lsq_train_step: bad batch/seq");
   LSQ_CHECK(same_store_shape(cfg, &pool->store->cfg), LSQ_ERR_INVALID, "lsq_train_step: cfg differs from the store's");
   LSQ_CHECK((flags & ~(LSQ_STEP_FORWARD_ONLY | LSQ_STEP_DEBUG_EARLY_RELEASE | LSQ_STEP_KEEP_ACTIVATIONS |
-                       LSQ_STEP_REFERENCE_FORWARD | LSQ_STEP_STREAM_LARGE)) == 0,
+                       LSQ_STEP_REFERENCE_FORWARD | LSQ_STEP_STREAM_LARGE | LSQ_STEP_RECOMPUTE_ALL)) == 0,
             LSQ_ERR_INVALID, "lsq_train_step: unknown flags 0x%x", flags);
+  LSQ_CHECK(!((flags & LSQ_STEP_KEEP_ACTIVATIONS) && (flags & LSQ_STEP_RECOMPUTE_ALL)), LSQ_ERR_INVALID,
+            "lsq_train_step: LSQ_STEP_KEEP_ACTIVATIONS and LSQ_STEP_RECOMPUTE_ALL contradict each other");
   const bool large = flags & LSQ_STEP_STREAM_LARGE;
   LSQ_CHECK(!large || !cfg->tied, LSQ_ERR_INVALID,
             "lsq_train_step: large-layer streaming is for an untied embedding and head (a tied one stays resident)");
@@ -748,7 +771,11 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   StepWs w = carve_step(cfg, B, S, ws, flags);
   lsq_model_cfg cfg_ref = *cfg;
   cfg_ref.lora_scale = 0.f;
-  auto acts_at = [&](int i) -> void* { return w.acts ? w.acts + (uint64_t)i * w.acts_bytes : nullptr; };
+  std::vector<int> kslot;
+  kept_layers(cfg, flags, &kslot);
+  auto acts_at = [&](int i) -> void* {
+    return (w.acts && kslot[i] >= 0) ? w.acts + (uint64_t)kslot[i] * w.acts_bytes : nullptr;
+  };
   lsq_lora_layout LL;
   lora_layout(cfg, &LL);
   const uint16_t* lora = static_cast<const uint16_t*>(res->lora);
@@ -883,7 +910,7 @@ int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int3
   out->adapters = LL.layer_elems * (uint64_t)cfg->n_layers * (2 + 4);
   out->checkpoints = 4 * T * H * (cfg->n_layers + 1);
   const StepWs sw = carve_step(cfg, batch, seq, nullptr, step_flags);
-  out->saved_activations = (uint64_t)sw.acts_bytes * cfg->n_layers;
+  out->saved_activations = (uint64_t)sw.acts_bytes * sw.n_kept;
   out->step_workspace = sw.total - out->checkpoints - out->saved_activations;
   out->total = out->slots + out->resident + out->adapters + out->checkpoints + out->saved_activations +
                out->step_workspace + 4 * T + 64;

@@ -15,7 +15,7 @@ LSQ_W_NF4, LSQ_W_BF16 = 0, 1
 LSQ_STORE_ALLOW_PAGEABLE, LSQ_STORE_FORCE_PAGEABLE, LSQ_STORE_FAIL_PIN = 1, 2, 4
 LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
 LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS, LSQ_STEP_REFERENCE_FORWARD = 1, 2, 4, 8
-LSQ_STEP_STREAM_LARGE = 16
+LSQ_STEP_STREAM_LARGE, LSQ_STEP_RECOMPUTE_ALL = 16, 32
 LSQ_TL_COPY, LSQ_TL_FWD, LSQ_TL_BWD, LSQ_TL_HEAD, LSQ_TL_LARGE_COPY = 0, 1, 2, 3, 4
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",

@@ -171,9 +171,10 @@ class Runner:
     """A pool over a store plus the step workspace.  mode: 'streamed' or 'resident'."""
 
     def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda",
-                 keep_activations=False, reference=False):
+                 keep_activations=False, reference=False, recompute_all=False):
         self.cfg, self.store, self.res = cfg, store, resident
         self.step_flags = (lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0) | \
+                          (lib.LSQ_STEP_RECOMPUTE_ALL if recompute_all else 0) | \
                           (lib.LSQ_STEP_STREAM_LARGE if resident.large_in_host else 0)
         # the workspace is sized for the reference forward when it may be asked for
         ws_flags = self.step_flags | (lib.LSQ_STEP_REFERENCE_FORWARD if reference else 0)

@@ -183,24 +183,26 @@ def test_saved_store_reloads_and_streams_identically(gpu, tmp_path):
 @pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_QWEN])
 def test_kept_activations_equal_recompute_bit_for_bit(gpu, cfg):
     """stream_recompute off: the backward reads the forward's kept activations
-    instead of recomputing them.  Recompute is deterministic, so both modes must
-    give the same loss, logits and adapter gradients bit for bit, and both still
+    instead of recomputing them.  Recompute is deterministic, so every policy
+    (recompute all, the default that keeps layers L-1, 1 and 0, keep all) must
+    give the same loss, logits and adapter gradients bit for bit, and all still
     re-read every layer's weights (same copy count)."""
     print_case(test="keep_vs_recompute", cfg=cfg.name)
     store = model.Store(cfg)
     res = model.Resident(cfg)
     ids = torch.from_numpy(ids_for(cfg)).cuda()
     out = {}
-    for keep in (False, True):
-        r = model.Runner(cfg, store, res, keep_activations=keep)
+    for mode in ("recompute_all", "default", "keep_all"):
+        r = model.Runner(cfg, store, res, keep_activations=mode == "keep_all", recompute_all=mode == "recompute_all")
         logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
         loss = r.step(ids, logits=logits).item()
         torch.cuda.synchronize()
-        out[keep] = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy(), stats=r.stats())
+        out[mode] = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy(), stats=r.stats())
         r.close()
-    exact, total = _compare_bitwise(cfg, out[False], out[True])
-    assert exact == total == cfg.n_layers * 14
-    assert out[True]["stats"].copies == out[False]["stats"].copies == 2 * cfg.n_layers - cfg.n_buffers
+    for mode in ("default", "keep_all"):
+        exact, total = _compare_bitwise(cfg, out["recompute_all"], out[mode])
+        assert exact == total == cfg.n_layers * 14, mode
+        assert out[mode]["stats"].copies == out["recompute_all"]["stats"].copies == 2 * cfg.n_layers - cfg.n_buffers
 
 
 def test_pageable_store_streams_the_same_bytes(gpu):

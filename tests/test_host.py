@@ -97,13 +97,18 @@ def test_vram_prediction_terms_and_refusal():
     # kept activations are a term of their own, proportional to layers x tokens
     k = lib.VramBreakdown()
     lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, lib.LSQ_STEP_KEEP_ACTIVATIONS, C.byref(k))
-    assert b.saved_activations == 0 and k.saved_activations > 0
+    rc = lib.VramBreakdown()
+    lib.call("vram_predict_peak", _cfg_struct(cfg), 1, 512, 2, lib.LSQ_STEP_RECOMPUTE_ALL, C.byref(rc))
+    # the default keeps the three layers whose backward runs with the link idle (L-1, 1, 0)
+    assert rc.saved_activations == 0 and k.saved_activations > 0
+    assert b.saved_activations * cfg.n_layers == 3 * k.saved_activations
+    assert b.total - rc.total == b.saved_activations
     per_token_layer = k.saved_activations / (512 * cfg.n_layers)
     H, I, r = cfg.hidden, cfg.intermediate, cfg.lora_r
     # the bf16/f32 tensors the backward reads, 256-byte aligned each
     approx = 2 * H + 2 * 6144 + 2 * 4096 + 4 * 4096 + 4 * 32 + 4 * H + 2 * H + 4 * I + 2 * I + 2 * 7 * r + 4 * 7 * r
     assert approx <= per_token_layer <= approx * 1.01
-    assert k.total - k.saved_activations < b.total   # the layer scratch no longer holds them
+    assert k.total - k.saved_activations < rc.total   # the layer scratch no longer holds them
 
 
 def test_store_pageable_fallback_and_refusal(capfd):
@@ -162,8 +167,9 @@ def test_workspace_queries_are_consistent():
         c = _cfg_struct(cfg)
         lw = lib.raw("decoder_layer_workspace_size")(c, cfg.batch, cfg.seq)
         sw = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, 0)
-        assert 0 < lw < sw
-        assert lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, lib.LSQ_STEP_KEEP_ACTIVATIONS) > sw
+        sr = lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, lib.LSQ_STEP_RECOMPUTE_ALL)
+        assert 0 < lw < sr < sw
+        assert lib.raw("lsq_step_workspace_size")(c, cfg.batch, cfg.seq, lib.LSQ_STEP_KEEP_ACTIVATIONS) > sr
         assert lib.raw("decoder_layer_workspace_size")(c, cfg.batch, 2 * cfg.seq) > lw
 
 

@@ -452,6 +452,8 @@ def main():
         "config": {"workload": cfg.name, "layers": cfg.n_layers, "batch": cfg.batch, "seq": cfg.seq,
                    "quant": cfg.quant, "layer_buffers": cfg.n_buffers, "lora_r": cfg.lora_r,
                    "lora_targets": "q,k,v,o,gate,up,down", "vocab": cfg.vocab, "tied": cfg.tied,
+                   "recompute": "per layer in the backward, except layers L-1, 1 and 0 whose backward runs with "
+                                "the link idle (their forward activations are kept; results bit-identical)",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
@@ -509,6 +511,19 @@ def main():
                                                 "saved_activation_bytes": pk.saved_activations,
                                                 "predicted_bytes": pk.total}}
         rk.close()
+        # every layer recomputed (the plain stream_recompute policy)
+        ra = model.Runner(cfg, store, res, recompute_all=True)
+        for _ in range(2):
+            ra.step(ids)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(nk):
+            ra.step(ids)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        out["variants"]["recompute_all"] = {"value": round(cfg.tokens * nk / el, 2), "unit": "tok/s",
+                                            "ms_per_step": round(el / nk * 1e3, 3), "steps": nk}
+        ra.close()
         # preference-loss reference forward (adapters off) fused into the same layer stream
         rr = model.Runner(cfg, store, res, reference=True)
         rows = torch.empty(cfg.tokens, dtype=torch.float32, device="cuda")

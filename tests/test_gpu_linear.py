@@ -124,6 +124,11 @@ LINEAR_CASES = [
     (77, 320, 200, 16),
     (300, 1024, 656, 32),
     (1, 64, 16, 8),
+    # an odd number of 64-deep reduction steps split several ways (the last
+    # split shorter or empty), and a one-row M tail with an odd step count
+    (64, 1600, 520, 16),
+    (64, 1344, 264, 8),
+    (513, 192, 264, 8),
 ]
 
 

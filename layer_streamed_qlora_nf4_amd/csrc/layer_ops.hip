@@ -330,6 +330,224 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------ attention on bf16 MFMA
+// The float32 operands (rotated q and k, the probabilities P) enter the bf16
+// matrix cores as hi/lo pairs: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
+// which carries 16 of float32's 24 mantissa bits.  Q K^T takes the three
+// products hi.hi + hi.lo + lo.hi (the lo.lo term is below 2^-17 of the
+// result); P V takes P's two halves against V's exact bf16 values.
+// Accumulation is float32 throughout.
+__device__ __forceinline__ bf16x8 mfma_a8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 8 floats -> bf16 hi and lo halves, as MFMA operands
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    h[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
+    l[t] = pack_bf16x2(x[2 * t] - bf_lo(h[t]), x[2 * t + 1] - bf_hi(h[t]));
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+__device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
+  x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
+  x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
+}
+// Rotate-half RoPE of 8 consecutive pair indices i .. i+7 at position pos:
+// (x1, x2) -> (x1 c - x2 s, x2 c + x1 s), table[pos][i] = (c, s).
+__device__ __forceinline__ void rope8(float (&x1)[8], float (&x2)[8], const float2* __restrict__ tab) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float2 cs = tab[t];
+    const float a = x1[t], b = x2[t];
+    x1[t] = a * cs.x - b * cs.y;
+    x2[t] = b * cs.x + a * cs.y;
+  }
+}
+__device__ __forceinline__ void store_hilo8(uint16_t* hi, uint16_t* lo, const float (&x)[8]) {
+  bf16x8 h, l;
+  split8(x, h, l);
+  *reinterpret_cast<bf16x8*>(hi) = h;
+  *reinterpret_cast<bf16x8*>(lo) = l;
+}
+
+template <int HD>
+struct AttnF16Smem {
+  uint16_t kh[AT][HD + 8];     // rotated K, bf16 hi  [key][d]
+  uint16_t kl[AT][HD + 8];     // rotated K, bf16 lo
+  uint16_t vt[HD][AT + 8];     // V transposed [d][key]
+  uint16_t ph[4][16][AT + 8];  // per-wave P hi [query][key]
+  uint16_t pl[4][16][AT + 8];  // per-wave P lo
+};
+
+// Stage one 64-key block: K rotated and split into kh/kl, V transposed into vt.
+template <int HD>
+__device__ __forceinline__ void stage_kv(AttnF16Smem<HD>& sm, const uint16_t* Kp, const uint16_t* Vp, int64_t ld,
+                                         int k0, int nk, const float2* __restrict__ rope) {
+  constexpr int HALF = HD / 2, NCH = HALF / 32;   // 8-pair chunks per thread: 2 (hd 128) or 1 (hd 64)
+  const int tid = threadIdx.x;
+  {
+    const int r = tid >> 2, q = tid & 3;   // row, quarter of the pair range
+    const bool ok = r < nk;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int i0 = (q * NCH + c) * 8;   // first pair index of this chunk
+      float x1[8], x2[8];
+      const uint16_t* row = Kp + (int64_t)(k0 + r) * ld;
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+      if (ok) rope8(x1, x2, rope + (int64_t)(k0 + r) * HALF + i0);
+      store_hilo8(&sm.kh[r][i0], &sm.kl[r][i0], x1);
+      store_hilo8(&sm.kh[r][HALF + i0], &sm.kl[r][HALF + i0], x2);
+    }
+  }
+  // V: micro-tiles of 4 keys x 8 dims, transposed in registers
+  constexpr int NMT = AT / 4 * (HD / 8);
+  if (tid < NMT) {
+    const int kg = tid / (HD / 8), dg = tid % (HD / 8);
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 4 * kg + i;
+      const uint4 v = key < nk ? *reinterpret_cast<const uint4*>(Vp + (int64_t)(k0 + key) * ld + 8 * dg)
+                               : make_uint4(0u, 0u, 0u, 0u);
+      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int sel = (c & 1) ? 0x07060302 : 0x05040100;
+      const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
+      *reinterpret_cast<u32x2*>(&sm.vt[8 * dg + c][4 * kg]) = u32x2{lo, hi};
+    }
+  }
+}
+
+// Forward: one workgroup per (query block of 64, head, batch), the heaviest
+// query blocks first; wave w owns queries 16w .. 16w+15 and keeps its rotated q
+// as MFMA operands in registers.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnF16Smem<HD>& sm = *reinterpret_cast<AttnF16Smem<HD>*>(smem_raw);
+  constexpr int DC = HD / 32, DT = HD / 16, HALF = HD / 2;
+  const int nqb = gridDim.x;
+  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.nh / a.nkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q0 = qb * AT;
+  const int64_t rowbase = (int64_t)b * a.S;
+  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
+  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
+  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
+  // this lane's query row, its 8-wide d slices 32c + 8 lg .. +8, rotated and split
+  bf16x8 qh[DC], ql[DC];
+  {
+    const int qi = q0 + 16 * w + lr;
+    const bool ok = qi < a.S;
+    const uint16_t* row = Q + (int64_t)qi * a.ld;
+#pragma unroll
+    for (int c = 0; c < DC / 2; ++c) {
+      const int i0 = 32 * c + 8 * lg;
+      float x1[8], x2[8];
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+      if (ok) rope8(x1, x2, a.rope + (int64_t)qi * HALF + i0);
+      split8(x1, qh[c], ql[c]);
+      split8(x2, qh[c + DC / 2], ql[c + DC / 2]);
+    }
+  }
+  const float sc = a.scale * kLog2e;
+  float m[4], l[4];
+  f32x4 o[DT];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * AT;
+    const int nk = min(AT, a.S - k0);
+    __syncthreads();   // the previous block's kh/kl/vt reads are done
+    stage_kv<HD>(sm, Kp, Vp, a.ld, k0, nk, a.rope);
+    __syncthreads();
+    f32x4 st[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
+        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
+        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
+        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = q0 + 16 * w + 4 * lg + v;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int kj = k0 + 16 * jt + lr;
+        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
+        mx = fmaxf(mx, st[jt][v]);
+      }
+      mx = group16_max(mx);
+      const float mn = fmaxf(m[v], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
+        const uint16_t ph = f32_to_bf16_bits(pv);
+        sm.ph[w][4 * lg + v][16 * jt + lr] = ph;
+        sm.pl[w][4 * lg + v][16 * jt + lr] = f32_to_bf16_bits(pv - bf16_bits_to_f32(ph));
+        rs += pv;
+      }
+      rs = group16_sum(rs);
+      l[v] = l[v] * alpha + rs;
+      m[v] = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
+    }
+    // P is wave-private: this wave's LDS writes are done before its reads below
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 pal = mfma_a8(&sm.pl[w][lr][32 * kc + 8 * lg]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vb = mfma_a8(&sm.vt[16 * dt + lr][32 * kc + 8 * lg]);
+        o[dt] = mfma_bf16(pah, vb, o[dt]);
+        o[dt] = mfma_bf16(pal, vb, o[dt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
+    if (qi >= a.S) continue;
+    const float inv = 1.f / l[v];
+    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
+    if (a.out_f32) {
+      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
+    }
+    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
+  }
+}
+
 // D[t][h] = sum_d dO[t, h, d] * O[t, h, d], with the float32 O of the forward:
 // D must equal sum_j P_j dP_j, and a rounded O breaks that identity exactly
 // where attention is peaked and dP_j - D cancels.
@@ -799,17 +1017,17 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   LSQ_CHECK(a.nkv > 0 && a.nh % a.nkv == 0, LSQ_ERR_SHAPE, "attention: n_heads %% n_kv_heads != 0");
   if (B == 0 || a.S == 0) return LSQ_OK;
   static int init = [] {
-    int e = allow_smem(attn_fwd_kernel<128>, attn_fwd_smem<128>());
-    return e ? e : allow_smem(attn_fwd_kernel<64>, attn_fwd_smem<64>());
+    int e = allow_smem(attn_fwd_bf16_kernel<128>, sizeof(AttnF16Smem<128>));
+    return e ? e : allow_smem(attn_fwd_bf16_kernel<64>, sizeof(AttnF16Smem<64>));
   }();
   if (init) return init;
   dim3 grid((a.S + AT - 1) / AT, a.nh, B);
   const double flops = 2.0 * 2.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
   int tok = prof_begin(s);
   if (a.hd == 128)
-    attn_fwd_kernel<128><<<grid, 256, attn_fwd_smem<128>(), s>>>(a);
+    attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a);
   else
-    attn_fwd_kernel<64><<<grid, 256, attn_fwd_smem<64>(), s>>>(a);
+    attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a);
   prof_end(tok, s, PROF_ATTN, flops, 0.0);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

@@ -165,43 +165,10 @@ __global__ void rope_kernel(uint16_t* __restrict__ buf, int64_t ld, int T, int S
 
 // ------------------------------------------------------------------ attention
 // Causal GQA attention on 64-query x 64-key tiles (one workgroup per (query
-// block, head, batch)), staged in LDS as float32; scores are kept in base 2:
-// s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
+// block, head, batch) forward and for dQ, per (key block, head) for dK and dV);
+// scores are kept in base 2: s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
 constexpr int AT = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-
-template <int HD>
-__device__ __forceinline__ void load_rows(float (*dst)[HD + 4], const uint16_t* src, int64_t ld, int row0, int nrows_valid) {
-  // 64 rows x HD bf16 -> float; 8 elements per thread-iteration
-  for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
-    const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nrows_valid) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * ld + c);
-    dst[r][c + 0] = bf_lo(v.x);
-    dst[r][c + 1] = bf_hi(v.x);
-    dst[r][c + 2] = bf_lo(v.y);
-    dst[r][c + 3] = bf_hi(v.y);
-    dst[r][c + 4] = bf_lo(v.z);
-    dst[r][c + 5] = bf_hi(v.z);
-    dst[r][c + 6] = bf_lo(v.w);
-    dst[r][c + 7] = bf_hi(v.w);
-  }
-}
-
-// Rotary embedding applied in float32 to rows already staged in LDS (position
-// pos0 + r for row r), so q and k are rounded to bf16 only once, by the GEMM.
-template <int HD>
-__device__ __forceinline__ void rope_rows(float (*x)[HD + 4], int pos0, int nvalid, const float2* __restrict__ table) {
-  constexpr int HALF = HD / 2;
-  for (int e = threadIdx.x; e < AT * HALF; e += 256) {
-    const int r = e / HALF, i = e % HALF;
-    if (r >= nvalid) continue;
-    const float2 cs = table[(int64_t)(pos0 + r) * HALF + i];
-    const float x1 = x[r][i], x2 = x[r][i + HALF];
-    x[r][i] = x1 * cs.x - x2 * cs.y;
-    x[r][i + HALF] = x2 * cs.x + x1 * cs.y;
-  }
-}
 
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
@@ -212,122 +179,6 @@ __device__ __forceinline__ float group16_sum(float v) {
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
-}
-
-// float32 MFMA 16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
-// D[4 (l / 16) + v][l % 16] comes back in element v.  Attention runs on these
-// so every operand (rotated q and k, P, dS) stays in float32.
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <int HD>
-struct AttnSmem {
-  float q[AT][HD + 4];
-  float k[AT][HD + 4];
-  float v[AT][HD + 4];
-  float p[4][16][AT + 4];   // per-wave P tile, row = query
-};
-
-// Forward: one workgroup per (query block of 64, head, batch); wave w owns
-// queries 16w .. 16w+15 and keeps its rotated q rows in registers.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  AttnSmem<HD>& sm = *reinterpret_cast<AttnSmem<HD>*>(smem_raw);
-  constexpr int KS = HD / 4, DT = HD / 16;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.nh / a.nkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = qb * AT;
-  const int nq_valid = min(AT, a.S - q0);
-  const int64_t rowbase = (int64_t)b * a.S;
-  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
-  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
-  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
-  load_rows<HD>(sm.q, Q, a.ld, q0, nq_valid);
-  __syncthreads();
-  rope_rows<HD>(sm.q, q0, nq_valid, a.rope);
-  __syncthreads();
-  float qa[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qa[ks] = sm.q[16 * w + lr][4 * ks + lg];
-  const float sc = a.scale * kLog2e;
-  float m[4], l[4];
-  f32x4 o[DT];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * AT;
-    const int nk_valid = min(AT, a.S - k0);
-    __syncthreads();
-    load_rows<HD>(sm.k, Kp, a.ld, k0, nk_valid);
-    load_rows<HD>(sm.v, Vp, a.ld, k0, nk_valid);
-    __syncthreads();
-    rope_rows<HD>(sm.k, k0, nk_valid, a.rope);
-    __syncthreads();
-    f32x4 st[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) st[jt] = mfma_f32(qa[ks], sm.k[16 * jt + lr][4 * ks + lg], st[jt]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = q0 + 16 * w + 4 * lg + v;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int kj = k0 + 16 * jt + lr;
-        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
-        mx = fmaxf(mx, st[jt][v]);
-      }
-      mx = group16_max(mx);
-      const float mn = fmaxf(m[v], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
-      float rs = 0.f;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
-        sm.p[w][4 * lg + v][16 * jt + lr] = pv;
-        rs += pv;
-      }
-      rs = group16_sum(rs);
-      l[v] = l[v] * alpha + rs;
-      m[v] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int ks = 0; ks < AT / 4; ++ks) {
-      const float pa = sm.p[w][lr][4 * ks + lg];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_f32(pa, sm.v[4 * ks + lg][16 * dt + lr], o[dt]);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int qi = q0 + 16 * w + 4 * lg + v;
-    if (qi >= a.S) continue;
-    const float inv = 1.f / l[v];
-    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
-    if (a.out_f32) {
-      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
-    }
-    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
-  }
 }
 
 // ------------------------------------------------ attention on bf16 MFMA
@@ -548,6 +399,334 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
+// ---- backward on bf16 MFMA: staging helpers (64-row blocks, 256 threads)
+// Write a 4-row x 8-column bf16 micro-tile transposed: dst[c][r0 .. r0+4] for
+// its 8 columns c (two v_perm per column pair).
+template <int PITCH>
+__device__ __forceinline__ void put_mt_t(uint16_t (*dst)[PITCH], int c0, int r0, const uint4 (&rows)[4]) {
+  const uint32_t w[4][4] = {{rows[0].x, rows[0].y, rows[0].z, rows[0].w}, {rows[1].x, rows[1].y, rows[1].z, rows[1].w},
+                            {rows[2].x, rows[2].y, rows[2].z, rows[2].w}, {rows[3].x, rows[3].y, rows[3].z, rows[3].w}};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int sel = (c & 1) ? 0x07060302 : 0x05040100;
+    const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
+    *reinterpret_cast<u32x2*>(&dst[c0 + c][r0]) = u32x2{lo, hi};
+  }
+}
+// Rows [row0, row0 + 64) of a bf16 matrix, rotated (RoPE at positions
+// row0 + r) and split into hi/lo, row-major.  Rows at or past n read as zero.
+template <int HD>
+__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)[HD + 8], const uint16_t* src,
+                                          int64_t ld, int row0, int n, const float2* __restrict__ rope) {
+  constexpr int HALF = HD / 2, NCH = HALF / 32;
+  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const bool ok = r < n;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int i0 = (q * NCH + c) * 8;
+    float x1[8], x2[8];
+    const uint16_t* row = src + (int64_t)(row0 + r) * ld;
+    unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
+    unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+    if (ok) rope8(x1, x2, rope + (int64_t)(row0 + r) * HALF + i0);
+    store_hilo8(&hi[r][i0], &lo[r][i0], x1);
+    store_hilo8(&hi[r][HALF + i0], &lo[r][HALF + i0], x2);
+  }
+}
+// Rows [row0, row0 + 64) copied row-major (zero past n).
+template <int HD>
+__device__ __forceinline__ void stage_rows(uint16_t (*dst)[HD + 8], const uint16_t* src, int64_t ld, int row0, int n) {
+  for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
+    const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
+    *reinterpret_cast<uint4*>(&dst[r][c]) =
+        r < n ? *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * ld + c) : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+// A staged row-major [64][HD] tile transposed into [HD][64] (call after a barrier).
+template <int HD>
+__device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + 8], const uint16_t (*src)[HD + 8]) {
+  constexpr int NMT = AT / 4 * (HD / 8);
+  for (int t = threadIdx.x; t < NMT; t += 256) {
+    const int rg = t / (HD / 8), cg = t % (HD / 8);
+    uint4 rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rows[i] = *reinterpret_cast<const uint4*>(&src[4 * rg + i][8 * cg]);
+    put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
+  }
+}
+// Rows [row0, row0 + 64) of a bf16 matrix straight into [HD][64] (zero past n).
+template <int HD>
+__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const uint16_t* src, int64_t ld, int row0,
+                                             int n) {
+  constexpr int NMT = AT / 4 * (HD / 8);
+  for (int t = threadIdx.x; t < NMT; t += 256) {
+    const int rg = t / (HD / 8), cg = t % (HD / 8);
+    uint4 rows[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * rg + i;
+      rows[i] = r < n ? *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * ld + 8 * cg)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+    put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
+  }
+}
+// One lane's rotated row slices as MFMA A operands (hi/lo), d slices 32c + 8 lg.
+template <int HD>
+__device__ __forceinline__ void load_rot_frags(const uint16_t* row, bool ok, int pos, const float2* __restrict__ rope,
+                                               int lg, bf16x8 (&fh)[HD / 32], bf16x8 (&fl)[HD / 32]) {
+  constexpr int DC = HD / 32, HALF = HD / 2;
+#pragma unroll
+  for (int c = 0; c < DC / 2; ++c) {
+    const int i0 = 32 * c + 8 * lg;
+    float x1[8], x2[8];
+    unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
+    unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+    if (ok) rope8(x1, x2, rope + (int64_t)pos * HALF + i0);
+    split8(x1, fh[c], fl[c]);
+    split8(x2, fh[c + DC / 2], fl[c + DC / 2]);
+  }
+}
+template <int HD>
+__device__ __forceinline__ void load_frags(const uint16_t* row, bool ok, int lg, bf16x8 (&f)[HD / 32]) {
+#pragma unroll
+  for (int c = 0; c < HD / 32; ++c)
+    f[c] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const uint4*>(row + 32 * c + 8 * lg)
+                                         : make_uint4(0u, 0u, 0u, 0u));
+}
+__device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, float x) {
+  const uint16_t h = f32_to_bf16_bits(x);
+  *hi = h;
+  *lo = f32_to_bf16_bits(x - bf16_bits_to_f32(h));
+}
+
+template <int HD>
+struct AttnDqSmem {
+  uint16_t kh[AT][HD + 8], kl[AT][HD + 8];   // rotated K [key][d]
+  uint16_t th[HD][AT + 8], tl[HD][AT + 8];   // the same transposed [d][key]
+  uint16_t v[AT][HD + 8];                    // V [key][d]
+  uint16_t sh[4][16][AT + 8], sl[4][16][AT + 8];   // per-wave dS [query][key]
+};
+
+// dQ for one query block of one head; wave w owns queries 16w .. 16w+15.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(AttnBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnDqSmem<HD>& sm = *reinterpret_cast<AttnDqSmem<HD>*>(smem_raw);
+  constexpr int DC = HD / 32, DT = HD / 16;
+  const int nqb = gridDim.x;
+  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.nh / a.nkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q0 = qb * AT;
+  const int64_t rowbase = (int64_t)b * a.S;
+  const float sc = a.scale * kLog2e;
+  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
+  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
+  bf16x8 qh[DC], ql[DC], od[DC];
+  {
+    const int qi = q0 + 16 * w + lr;
+    const bool ok = qi < a.S;
+    load_rot_frags<HD>(a.qkv + (rowbase + qi) * a.ld + (int64_t)h * HD, ok, qi, a.rope, lg, qh, ql);
+    load_frags<HD>(a.dO + (rowbase + qi) * a.ldo + (int64_t)h * HD, ok, lg, od);
+  }
+  float lse_r[4], dd_r[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
+    const bool ok = qi < a.S;
+    lse_r[v] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + qi] : 0.f;
+    dd_r[v] = ok ? a.D[(rowbase + qi) * a.nh + h] : 0.f;
+  }
+  f32x4 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * AT;
+    const int nk = min(AT, a.S - k0);
+    __syncthreads();
+    stage_rot<HD>(sm.kh, sm.kl, Kp, a.ld, k0, nk, a.rope);
+    stage_rows<HD>(sm.v, Vp, a.ld, k0, nk);
+    __syncthreads();
+    lds_transpose<HD>(sm.th, sm.kh);
+    lds_transpose<HD>(sm.tl, sm.kl);
+    f32x4 st[4], dpt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 vv = mfma_a8(&sm.v[16 * jt + lr][32 * c + 8 * lg]);
+        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
+        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
+        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
+        dpt[jt] = mfma_bf16(od[c], vv, dpt[jt]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = q0 + 16 * w + 4 * lg + v;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int kj = k0 + 16 * jt + lr;
+        const bool ok = kj <= qi && qi < a.S && kj < a.S;
+        const float pv = ok ? exp2f(st[jt][v] * sc - lse_r[v]) : 0.f;
+        put_hilo(&sm.sh[w][4 * lg + v][16 * jt + lr], &sm.sl[w][4 * lg + v][16 * jt + lr],
+                 pv * (dpt[jt][v] - dd_r[v]));
+      }
+    }
+    __syncthreads();   // the transposed K tiles are complete
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 dh = mfma_a8(&sm.sh[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 dl = mfma_a8(&sm.sl[w][lr][32 * kc + 8 * lg]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 th = mfma_a8(&sm.th[16 * dt + lr][32 * kc + 8 * lg]);
+        const bf16x8 tl = mfma_a8(&sm.tl[16 * dt + lr][32 * kc + 8 * lg]);
+        dq[dt] = mfma_bf16(dh, th, dq[dt]);
+        dq[dt] = mfma_bf16(dh, tl, dq[dt]);
+        dq[dt] = mfma_bf16(dl, th, dq[dt]);
+      }
+    }
+  }
+  constexpr int HALF_T = DT / 2;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
+    if (qi >= a.S) continue;
+    uint16_t* dqp = a.dqkv + (rowbase + qi) * a.ld + (int64_t)h * HD;
+#pragma unroll
+    for (int dt = 0; dt < HALF_T; ++dt) {
+      const int i = 16 * dt + lr;
+      const float2 cs = a.rope[(int64_t)qi * (HD / 2) + i];
+      const float g1 = dq[dt][v] * a.scale, g2 = dq[dt + HALF_T][v] * a.scale;
+      dqp[i] = f32_to_bf16_bits(g1 * cs.x + g2 * cs.y);
+      dqp[i + HD / 2] = f32_to_bf16_bits(g2 * cs.x - g1 * cs.y);
+    }
+  }
+}
+
+template <int HD>
+struct AttnDkdvSmem {
+  uint16_t qh[AT][HD + 8], ql[AT][HD + 8];   // rotated Q [query][d]
+  uint16_t th[HD][AT + 8], tl[HD][AT + 8];   // the same transposed [d][query]
+  uint16_t o[AT][HD + 8];                    // dO [query][d]
+  uint16_t ot[HD][AT + 8];                   // dO transposed [d][query]
+  uint16_t ph[4][16][AT + 8], pl[4][16][AT + 8];   // per-wave P^T [key][query]
+  uint16_t sh[4][16][AT + 8], sl[4][16][AT + 8];   // per-wave dS^T
+  float lse[AT], dd[AT];
+};
+
+// One query head's contribution to dK and dV of one key block, over the query
+// blocks at or after it, as float32 partials (summed over the group's heads in
+// head order by attn_dkdv_reduce_kernel).  Wave w owns keys 16w .. 16w+15;
+// scores are formed transposed (S^T = K Q^T) so P^T and dS^T come out key-major.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnDkdvSmem<HD>& sm = *reinterpret_cast<AttnDkdvSmem<HD>*>(smem_raw);
+  constexpr int DC = HD / 32, DT = HD / 16;
+  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int k0 = kb * AT;
+  const int g = h / (a.nh / a.nkv);
+  const int64_t rowbase = (int64_t)b * a.S;
+  const float sc = a.scale * kLog2e;
+  bf16x8 kh[DC], kl[DC], vv[DC];
+  {
+    const int kj = k0 + 16 * w + lr;
+    const bool ok = kj < a.S;
+    load_rot_frags<HD>(a.qkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + g) * HD, ok, kj, a.rope, lg, kh, kl);
+    load_frags<HD>(a.qkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, ok, lg, vv);
+  }
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nqb = (a.S + AT - 1) / AT;
+  const uint16_t* Qp = a.qkv + rowbase * a.ld + (int64_t)h * HD;
+  const uint16_t* Op = a.dO + rowbase * a.ldo + (int64_t)h * HD;
+  for (int qb = kb; qb < nqb; ++qb) {
+    const int q0 = qb * AT;
+    const int nq = min(AT, a.S - q0);
+    __syncthreads();
+    stage_rot<HD>(sm.qh, sm.ql, Qp, a.ld, q0, nq, a.rope);
+    stage_rows<HD>(sm.o, Op, a.ldo, q0, nq);
+    stage_rows_t<HD>(sm.ot, Op, a.ldo, q0, nq);
+    if (tid < AT) {
+      const bool ok = tid < nq;
+      sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
+      sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
+    }
+    __syncthreads();
+    lds_transpose<HD>(sm.th, sm.qh);
+    lds_transpose<HD>(sm.tl, sm.ql);
+    f32x4 st[4], dpt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 qhf = mfma_a8(&sm.qh[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 qlf = mfma_a8(&sm.ql[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 of = mfma_a8(&sm.o[16 * jt + lr][32 * c + 8 * lg]);
+        st[jt] = mfma_bf16(kh[c], qhf, st[jt]);
+        st[jt] = mfma_bf16(kh[c], qlf, st[jt]);
+        st[jt] = mfma_bf16(kl[c], qhf, st[jt]);
+        dpt[jt] = mfma_bf16(vv[c], of, dpt[jt]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int kj = k0 + 16 * w + 4 * lg + v;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int qi = q0 + 16 * jt + lr;
+        const bool ok = kj <= qi && qi < a.S && kj < a.S;
+        const float pv = ok ? exp2f(st[jt][v] * sc - sm.lse[16 * jt + lr]) : 0.f;
+        put_hilo(&sm.ph[w][4 * lg + v][16 * jt + lr], &sm.pl[w][4 * lg + v][16 * jt + lr], pv);
+        put_hilo(&sm.sh[w][4 * lg + v][16 * jt + lr], &sm.sl[w][4 * lg + v][16 * jt + lr],
+                 pv * (dpt[jt][v] - sm.dd[16 * jt + lr]));
+      }
+    }
+    __syncthreads();   // the transposed Q tile is complete
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 pal = mfma_a8(&sm.pl[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 sah = mfma_a8(&sm.sh[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 sal = mfma_a8(&sm.sl[w][lr][32 * kc + 8 * lg]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 ob = mfma_a8(&sm.ot[16 * dt + lr][32 * kc + 8 * lg]);
+        dv[dt] = mfma_bf16(pah, ob, dv[dt]);
+        dv[dt] = mfma_bf16(pal, ob, dv[dt]);
+        const bf16x8 th = mfma_a8(&sm.th[16 * dt + lr][32 * kc + 8 * lg]);
+        const bf16x8 tl = mfma_a8(&sm.tl[16 * dt + lr][32 * kc + 8 * lg]);
+        dk[dt] = mfma_bf16(sah, th, dk[dt]);
+        dk[dt] = mfma_bf16(sah, tl, dk[dt]);
+        dk[dt] = mfma_bf16(sal, th, dk[dt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int kj = k0 + 16 * w + 4 * lg + v;
+    if (kj >= a.S) continue;
+    const int64_t o = (((int64_t)b * a.nh + h) * a.S + kj) * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      a.dk_part[o + 16 * dt + lr] = dk[dt][v];
+      a.dv_part[o + 16 * dt + lr] = dv[dt][v];
+    }
+  }
+}
+
 // D[t][h] = sum_d dO[t, h, d] * O[t, h, d], with the float32 O of the forward:
 // D must equal sum_j P_j dP_j, and a rounded O breaks that identity exactly
 // where attention is peaked and dP_j - D cancels.
@@ -563,125 +742,6 @@ __global__ void attn_dot_kernel(const uint16_t* __restrict__ dO, const float* __
   for (int d = lane; d < hd; d += 64) s += bf16_bits_to_f32(x[d]) * y[d];
   s = warp_sum(s);
   if (lane == 0) D[row] = s;
-}
-
-template <int HD>
-struct AttnBwdSmem {
-  float a[AT][HD + 4];      // Q rows (rotated)
-  float b[AT][HD + 4];      // dO rows
-  float k[AT][HD + 4];      // K rows (rotated)
-  float v[AT][HD + 4];      // V rows
-  float p[4][16][AT + 4];   // per-wave transposition tile
-  float lse[AT];
-  float dd[AT];
-};
-
-// One query head's contribution to dK and dV of one key block, over the query
-// blocks at or after it, as float32 partials; attn_dkdv_reduce_kernel sums the
-// group's heads in head order.  Wave w owns keys 16w .. 16w+15.  Scores are
-// formed transposed (S^T = K Q^T) so P^T and dS^T come out key-major.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(AttnBwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
-  constexpr int KS = HD / 4, DT = HD / 16;
-  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int k0 = kb * AT;
-  const int group = a.nh / a.nkv;
-  const int g = h / group;
-  const int64_t rowbase = (int64_t)b * a.S;
-  const float sc = a.scale * kLog2e;
-  const int nk_valid = min(AT, a.S - k0);
-  load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, nk_valid);
-  load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, nk_valid);
-  __syncthreads();
-  rope_rows<HD>(sm.k, k0, nk_valid, a.rope);
-  __syncthreads();
-  float ka[KS], va[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    ka[ks] = sm.k[16 * w + lr][4 * ks + lg];
-    va[ks] = sm.v[16 * w + lr][4 * ks + lg];
-  }
-  f32x4 dk[DT], dv[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nqb = (a.S + AT - 1) / AT;
-  for (int qb = kb; qb < nqb; ++qb) {
-    const int q0 = qb * AT;
-    const int nqv = min(AT, a.S - q0);
-    __syncthreads();
-    load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);
-    load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);
-    if (tid < AT) {
-      const bool ok = tid < nqv;
-      sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
-      sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
-    }
-    __syncthreads();
-    rope_rows<HD>(sm.a, q0, nqv, a.rope);
-    __syncthreads();
-    // S^T[k][q] and dP^T[k][q] for the wave's 16 keys x 64 queries
-    f32x4 st[4], dpt[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        st[jt] = mfma_f32(ka[ks], sm.a[16 * jt + lr][4 * ks + lg], st[jt]);
-        dpt[jt] = mfma_f32(va[ks], sm.b[16 * jt + lr][4 * ks + lg], dpt[jt]);
-      }
-    // P^T, written key-major into the wave's tile
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int kj = k0 + 16 * w + 4 * lg + v;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int qi = q0 + 16 * jt + lr;
-        const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float pv = ok ? exp2f(st[jt][v] * sc - sm.lse[16 * jt + lr]) : 0.f;
-        st[jt][v] = pv;
-        sm.p[w][4 * lg + v][16 * jt + lr] = pv;
-      }
-    }
-    __syncthreads();
-    // dV[k][d] += sum_q P^T[k][q] dO[q][d]
-#pragma unroll 4
-    for (int ks = 0; ks < AT / 4; ++ks) {
-      const float pa = sm.p[w][lr][4 * ks + lg];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dv[dt] = mfma_f32(pa, sm.b[4 * ks + lg][16 * dt + lr], dv[dt]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-        sm.p[w][4 * lg + v][16 * jt + lr] = st[jt][v] * (dpt[jt][v] - sm.dd[16 * jt + lr]);   // dS^T
-    __syncthreads();
-    // dK[k][d] += sum_q dS^T[k][q] Q[q][d]
-#pragma unroll 4
-    for (int ks = 0; ks < AT / 4; ++ks) {
-      const float da = sm.p[w][lr][4 * ks + lg];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dk[dt] = mfma_f32(da, sm.a[4 * ks + lg][16 * dt + lr], dk[dt]);
-    }
-  }
-  // partials [b][h][s][HD], float32; scale and rotation applied by the reduce
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int kj = k0 + 16 * w + 4 * lg + v;
-    if (kj >= a.S) continue;
-    const int64_t o = (((int64_t)b * a.nh + h) * a.S + kj) * HD;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      a.dk_part[o + 16 * dt + lr] = dk[dt][v];
-      a.dv_part[o + 16 * dt + lr] = dv[dt][v];
-    }
-  }
 }
 
 // dK, dV of each KV head = sum of its query heads' partials (head order); dK
@@ -712,101 +772,6 @@ __global__ void attn_dkdv_reduce_kernel(AttnBwdArgs a, int B) {
   row[(int64_t)(a.nh + g) * a.hd + i + half] = f32_to_bf16_bits(k2 * cs.x - k1 * cs.y);
   row[(int64_t)(a.nh + a.nkv + g) * a.hd + i] = f32_to_bf16_bits(v1);
   row[(int64_t)(a.nh + a.nkv + g) * a.hd + i + half] = f32_to_bf16_bits(v2);
-}
-
-// dQ for one query block of one head; wave w owns queries 16w .. 16w+15.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  AttnBwdSmem<HD>& sm = *reinterpret_cast<AttnBwdSmem<HD>*>(smem_raw);
-  constexpr int KS = HD / 4, DT = HD / 16;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.nh / a.nkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = qb * AT;
-  const int nqv = min(AT, a.S - q0);
-  const int64_t rowbase = (int64_t)b * a.S;
-  const float sc = a.scale * kLog2e;
-  load_rows<HD>(sm.a, a.qkv + rowbase * a.ld + (int64_t)h * HD, a.ld, q0, nqv);      // Q
-  load_rows<HD>(sm.b, a.dO + rowbase * a.ldo + (int64_t)h * HD, a.ldo, q0, nqv);     // dO
-  if (tid < AT) {
-    const bool ok = tid < nqv;
-    sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
-    sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
-  }
-  __syncthreads();
-  rope_rows<HD>(sm.a, q0, nqv, a.rope);
-  __syncthreads();
-  float qa[KS], oa[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qa[ks] = sm.a[16 * w + lr][4 * ks + lg];
-    oa[ks] = sm.b[16 * w + lr][4 * ks + lg];
-  }
-  float lse_r[4], dd_r[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    lse_r[v] = sm.lse[16 * w + 4 * lg + v];
-    dd_r[v] = sm.dd[16 * w + 4 * lg + v];
-  }
-  f32x4 dq[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * AT;
-    const int nkv = min(AT, a.S - k0);
-    __syncthreads();
-    load_rows<HD>(sm.k, a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD, a.ld, k0, nkv);          // K
-    load_rows<HD>(sm.v, a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, a.ld, k0, nkv);  // V
-    __syncthreads();
-    rope_rows<HD>(sm.k, k0, nkv, a.rope);
-    __syncthreads();
-    f32x4 st[4], dpt[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) st[jt] = dpt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        st[jt] = mfma_f32(qa[ks], sm.k[16 * jt + lr][4 * ks + lg], st[jt]);
-        dpt[jt] = mfma_f32(oa[ks], sm.v[16 * jt + lr][4 * ks + lg], dpt[jt]);
-      }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = q0 + 16 * w + 4 * lg + v;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int kj = k0 + 16 * jt + lr;
-        const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float pv = ok ? exp2f(st[jt][v] * sc - lse_r[v]) : 0.f;
-        sm.p[w][4 * lg + v][16 * jt + lr] = pv * (dpt[jt][v] - dd_r[v]);   // dS
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int ks = 0; ks < AT / 4; ++ks) {
-      const float da = sm.p[w][lr][4 * ks + lg];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dq[dt] = mfma_f32(da, sm.k[4 * ks + lg][16 * dt + lr], dq[dt]);
-    }
-  }
-  // scale, then back through the rotation: dims d and d + HD/2 sit in tiles dt and dt + DT/2
-  constexpr int HALF_T = DT / 2;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int qi = q0 + 16 * w + 4 * lg + v;
-    if (qi >= a.S) continue;
-    uint16_t* dqp = a.dqkv + (rowbase + qi) * a.ld + (int64_t)h * HD;
-#pragma unroll
-    for (int dt = 0; dt < HALF_T; ++dt) {
-      const int i = 16 * dt + lr;
-      const float2 cs = a.rope[(int64_t)qi * (HD / 2) + i];
-      const float g1 = dq[dt][v] * a.scale, g2 = dq[dt + HALF_T][v] * a.scale;
-      dqp[i] = f32_to_bf16_bits(g1 * cs.x + g2 * cs.y);
-      dqp[i + HD / 2] = f32_to_bf16_bits(g2 * cs.x - g1 * cs.y);
-    }
-  }
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -945,11 +910,6 @@ __global__ void __launch_bounds__(256) loss_sum_kernel(const float* __restrict__
   if (tid == 0) *loss = (((red[0] + red[1]) + red[2]) + red[3]) * inv_count;
 }
 
-template <int HD>
-size_t attn_fwd_smem() { return sizeof(AttnSmem<HD>); }
-template <int HD>
-size_t attn_bwd_smem() { return sizeof(AttnBwdSmem<HD>); }
-
 }  // namespace
 
 // ================================================================== launchers
@@ -1037,10 +997,10 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   LSQ_CHECK(a.hd == 64 || a.hd == 128, LSQ_ERR_SHAPE, "attention: head_dim %d unsupported", a.hd);
   if (B == 0 || a.S == 0) return LSQ_OK;
   static int init = [] {
-    int e = allow_smem(attn_bwd_dkdv_kernel<128>, attn_bwd_smem<128>());
-    if (!e) e = allow_smem(attn_bwd_dq_kernel<128>, attn_bwd_smem<128>());
-    if (!e) e = allow_smem(attn_bwd_dkdv_kernel<64>, attn_bwd_smem<64>());
-    if (!e) e = allow_smem(attn_bwd_dq_kernel<64>, attn_bwd_smem<64>());
+    int e = allow_smem(attn_bwd_dkdv_bf16_kernel<128>, sizeof(AttnDkdvSmem<128>));
+    if (!e) e = allow_smem(attn_bwd_dq_bf16_kernel<128>, sizeof(AttnDqSmem<128>));
+    if (!e) e = allow_smem(attn_bwd_dkdv_bf16_kernel<64>, sizeof(AttnDkdvSmem<64>));
+    if (!e) e = allow_smem(attn_bwd_dq_bf16_kernel<64>, sizeof(AttnDqSmem<64>));
     return e;
   }();
   if (init) return init;
@@ -1053,11 +1013,11 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   LSQ_CHECK(a.dk_part && a.dv_part, LSQ_ERR_WORKSPACE, "attention_bwd: partial buffers missing");
   dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
   if (a.hd == 128) {
-    attn_bwd_dkdv_kernel<128><<<g1, 256, attn_bwd_smem<128>(), s>>>(b);
-    attn_bwd_dq_kernel<128><<<g2, 256, attn_bwd_smem<128>(), s>>>(b);
+    attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b);
+    attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b);
   } else {
-    attn_bwd_dkdv_kernel<64><<<g1, 256, attn_bwd_smem<64>(), s>>>(b);
-    attn_bwd_dq_kernel<64><<<g2, 256, attn_bwd_smem<64>(), s>>>(b);
+    attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b);
+    attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b);
   }
   const int64_t nred = (int64_t)B * a.S * a.nkv * (a.hd / 2);
   attn_dkdv_reduce_kernel<<<(unsigned)((nred + 255) / 256), 256, 0, s>>>(b, B);

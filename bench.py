@@ -200,7 +200,20 @@ def timeline_report(lib, entries, n_layers):
                       "step_over_bound": round((t1 - t0) / max(sum_copy, sum_comp), 4) if cp else None,
                       "copy_idle_gaps": gaps})
     mean = lambda v: round(sum(v) / len(v), 4) if v else None
+    # compute time per pass (ms): forward layers, backward layers (recompute or kept), the head
+    durs = {"fwd": [], "bwd": [], "head": []}
+    for k, l, a, b in entries:
+        key = {lib.LSQ_TL_FWD: "fwd", lib.LSQ_TL_BWD: "bwd", lib.LSQ_TL_HEAD: "head"}.get(k)
+        if key:
+            durs[key].append((l, b - a))
+    per_bwd = {}
+    for l, d in durs["bwd"]:
+        per_bwd.setdefault(l, []).append(d)
+    pass_ms = {"fwd_layer_mean": mean([d for _, d in durs["fwd"]]), "head_mean": mean([d for _, d in durs["head"]]),
+               "bwd_layer_mean": mean([d for _, d in durs["bwd"]]),
+               "bwd_by_layer": {str(l): mean(v) for l, v in sorted(per_bwd.items())}}
     return {
+        "pass_ms": pass_ms,
         "per_layer_fwd_coverage": [mean(v) for v in fwd_cov],
         "per_layer_bwd_coverage": [mean(v) for v in bwd_cov],
         "mean_fwd_coverage": mean([x for v in fwd_cov for x in v]),

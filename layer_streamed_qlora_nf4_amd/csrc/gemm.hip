@@ -20,19 +20,11 @@
 #include "gemm.h"
 #include "nf4_levels.h"
 
-// Forward schedule: 1 = ping-pong wave groups (gemm_fwd_pp_kernel), 0 = the
-// plain double-buffered kernel of any tile shape.
-#ifndef LSQ_FWD_PP
-#define LSQ_FWD_PP 1
-#endif
-#ifndef LSQ_BWD_PP
-#define LSQ_BWD_PP 1
-#endif
-
 namespace lsq {
 namespace {
 
 constexpr int BK = 64;          // reduction step = one NF4 block
+constexpr int kTile = 256;      // output tile edge of every GEMM kernel (256 x 256, 8 waves)
 constexpr int NTHREADS = 256;   // 4 waves
 
 // ------------------------------------------------------------------ LDS tiles
@@ -160,131 +152,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // =========================================================== forward (NT)
 // C[M, N] = X[M, K] W[N, K]^T + U_seg[M, r] Bl[N, r]^T (+ bias) (+ resid)
-template <int BM, int BN, int WGM, int WGN, int WKIND, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_fwd_kernel(FwdParams p) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;
-  constexpr int A_TOTAL = BM * 8;                                                // 16-B chunks of the A tile
-  constexpr int B_TOTAL = (WKIND == LSQ_W_NF4) ? BN * 2 : BN * 8;
-  constexpr int A_CHUNKS = (A_TOTAL + NT - 1) / NT, B_CHUNKS = (B_TOTAL + NT - 1) / NT;
-  static_assert(TM >= 1 && TN >= 1 && A_TOTAL % NT == 0, "bad tile");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
-  __shared__ float lut[16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int tiles_n = (p.N + BN - 1) / BN;
-  const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
-  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
-  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
-
-  const uint16_t* __restrict__ X = p.X;
-  const int K = p.K, nk_all = K / BK;
-  const int split = blockIdx.y;
-  const int per = (nk_all + p.splits - 1) / p.splits;
-  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
-
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  float rabs[B_CHUNKS];
-
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NT, row = q >> 3, c = q & 7;
-      int m = m0 + row;
-      ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(X + (int64_t)m * p.ldx + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (WKIND == LSQ_W_NF4) {
-      const uint8_t* W = static_cast<const uint8_t*>(p.W);
-#pragma unroll
-      for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NT, row = q >> 1, h = q & 1;
-        int n = n0 + row;
-        if (q < B_TOTAL && n < p.N) {
-          rb[i] = *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16);
-          rabs[i] = p.absmax[(int64_t)n * (K / 64) + kt];
-        } else {
-          rb[i] = make_uint4(0, 0, 0, 0);
-          rabs[i] = 0.f;
-        }
-      }
-    } else {
-      const uint16_t* W = static_cast<const uint16_t*>(p.W);
-#pragma unroll
-      for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NT, row = q >> 3, c = q & 7;
-        int n = n0 + row;
-        rb[i] = (q < B_TOTAL && n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NT, row = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
-    }
-    if (WKIND == LSQ_W_NF4) {
-#pragma unroll
-      for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NT, row = q >> 1, h = q & 1;
-        if (q >= B_TOTAL) break;
-        uint32_t words[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t o[4];
-          decode_word(words[w], rabs[i], lut, o);
-          *reinterpret_cast<uint4*>(&Bs[buf][swz(row, h * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_CHUNKS; ++i) {
-        int q = tid + i * NT, row = q >> 3, c = q & 7;
-        if (q >= B_TOTAL) break;
-        *reinterpret_cast<uint4*>(&Bs[buf][swz(row, c)]) = rb[i];
-      }
-    }
-  };
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (kbeg < nk) load_tile(kbeg);
-  __syncthreads();  // lut
-  if (kbeg < nk) store_tile(0);
-  __syncthreads();
-
-  for (int kt = kbeg; kt < nk; ++kt) {
-    const int cur = (kt - kbeg) & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[TM], bfr[TN];
-      const int chunk = ks * 4 + (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = lds_frag(Bs[cur], swz(wn * WN + j * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
-    __syncthreads();
-  }
-
-  fwd_lora_up<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
-  fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
-}
 
 // Ping-pong forward: 256 x 256 tile, 8 waves in two groups of 4 (one wave
 // per SIMD in each).  Group g owns tile rows [128 g, 128 g + 128) and loads /
@@ -629,155 +496,6 @@ __device__ __forceinline__ void bwd_store(const BwdParams& p, const f32x4 (&acc)
 // C[M, K] = dY[M, N] W[N, K] + G[M, rr] Al[rr, K] (+ resid)
 // The weight slab (64 rows of W) is decoded straight into a transposed LDS
 // tile Bt[k][n] so that each lane's 8 reduction values are contiguous.
-template <int BM, int BO, int WGM, int WGN, int WKIND, int EPI>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_bwd_kernel(BwdParams p) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int WM = BM / WGM, WO = BO / WGN, TM = WM / 16, TO = WO / 16;
-  constexpr int A_TOTAL = BM * 8;
-  constexpr int A_CHUNKS = (A_TOTAL + NT - 1) / NT;
-  // Transposing loads: each thread owns a 4 (rows n) x 8 (cols k) micro-tile.
-  constexpr int MT_TOTAL = (64 / 4) * (BO / 8);
-  constexpr int MT_PER_THREAD = (MT_TOTAL + NT - 1) / NT;
-  static_assert(TM >= 1 && TO >= 1 && A_TOTAL % NT == 0 && BO >= 128, "bad tile");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Bt[2][BO * 64];
-  __shared__ float lut[16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wo = wave % WGN;
-  const int tiles_o = (p.K + BO - 1) / BO;
-  const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
-  const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
-  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
-
-  const int K = p.K;
-  const int nk_main = (p.N + BK - 1) / BK;
-  const int nk_lora = (p.rr + BK - 1) / BK;
-  const int nk_all = nk_main + nk_lora;
-  const int split = blockIdx.y;
-  const int per = (nk_all + p.splits - 1) / p.splits;
-  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
-
-  // micro-tile coordinates: lanes 8 apart in q, neighbouring rg pairs in a pass
-  auto mt_coords = [&](int i, int& rg, int& q) __attribute__((always_inline)) {
-    int u = tid + i * NT;
-    q = (u & 7) | (((u >> 4) & ((BO / 8 / 8) - 1)) << 3);
-    rg = ((u >> 3) & 1) | ((u >> (4 + __builtin_ctz(BO / 64))) << 1);
-  };
-
-  uint4 ra[A_CHUNKS];
-  uint32_t rq[MT_PER_THREAD][4];     // NF4: 4 rows x 4 bytes
-  float rabs[MT_PER_THREAD][4];
-  uint4 rw[MT_PER_THREAD][4];        // bf16: 4 rows x 16 bytes
-
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
-    const bool lora = kt >= nk_main;
-    const int r0 = (lora ? kt - nk_main : kt) * BK;   // reduction offset
-    const uint16_t* Asrc = lora ? p.G : p.dY;
-    const int64_t lda = lora ? p.ldg : p.ldy;
-    const int red_lim = lora ? p.rr : p.N;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NT, row = q >> 3, c = q & 7;
-      int m = m0 + row, rcol = r0 + c * 8;
-      ra[i] = (m < p.M && rcol < red_lim) ? *reinterpret_cast<const uint4*>(Asrc + (int64_t)m * lda + rcol)
-                                          : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < MT_PER_THREAD; ++i) {
-      if (tid + i * NT >= MT_TOTAL) break;
-      int rg, q;
-      mt_coords(i, rg, q);
-      const int kcol = o0 + q * 8;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int n = r0 + rg * 4 + rr;
-        const bool ok = n < red_lim && kcol < K;
-        if (!lora && WKIND == LSQ_W_NF4) {
-          const uint8_t* W = static_cast<const uint8_t*>(p.W);
-          rq[i][rr] = ok ? *reinterpret_cast<const uint32_t*>(W + (int64_t)n * (K / 2) + kcol / 2) : 0u;
-          rabs[i][rr] = ok ? p.absmax[(int64_t)n * (K / 64) + kcol / 64] : 0.f;
-        } else {
-          const uint16_t* W = lora ? p.Al : static_cast<const uint16_t*>(p.W);
-          rw[i][rr] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + kcol) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf, int kt) __attribute__((always_inline)) {
-    const bool lora = kt >= nk_main;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      int q = tid + i * NT, row = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(&As[buf][swz(row, c)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < MT_PER_THREAD; ++i) {
-      if (tid + i * NT >= MT_TOTAL) break;
-      int rg, q;
-      mt_coords(i, rg, q);
-      // vals[rr][c]: weight (row rg*4+rr, column q*8+c) as bf16 bits
-      uint32_t pairs[4][4];  // pairs[rr][j] = (col 2j, col 2j+1) of row rr
-      if (!lora && WKIND == LSQ_W_NF4) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) decode_word(rq[i][rr], rabs[i][rr], lut, pairs[rr]);
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          pairs[rr][0] = rw[i][rr].x;
-          pairs[rr][1] = rw[i][rr].y;
-          pairs[rr][2] = rw[i][rr].z;
-          pairs[rr][3] = rw[i][rr].w;
-        }
-      }
-      // Column c of the micro-tile -> 4 consecutive reduction values (rows) = 8 bytes.
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int sel = (c & 1) ? 0x07060302 : 0x05040100;  // pick high or low halves
-        uint32_t lo = __builtin_amdgcn_perm(pairs[1][c >> 1], pairs[0][c >> 1], sel);
-        uint32_t hi = __builtin_amdgcn_perm(pairs[3][c >> 1], pairs[2][c >> 1], sel);
-        const int krow = q * 8 + c;
-        const int nbase = rg * 4;   // 0..60, chunk nbase/8, half (nbase%8)/4
-        uint16_t* dst = &Bt[buf][swzt(krow, nbase >> 3) + (nbase & 7)];
-        *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-      }
-    }
-  };
-
-  f32x4 acc[TM][TO];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TO; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (kbeg < nk) load_tile(kbeg);
-  __syncthreads();
-  if (kbeg < nk) store_tile(0, kbeg);
-  __syncthreads();
-  for (int kt = kbeg; kt < nk; ++kt) {
-    const int cur = (kt - kbeg) & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[TM], bfr[TO];
-      const int chunk = ks * 4 + (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = lds_frag(As[cur], swz(wm * WM + i * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int j = 0; j < TO; ++j) bfr[j] = lds_frag(Bt[cur], swzt(wo * WO + j * 16 + (lane & 15), chunk));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TO; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) store_tile(cur ^ 1, kt + 1);
-    __syncthreads();
-  }
-
-  bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
-}
 
 // Backward epilogue (lane layout as in fwd_store); columns are the weight's
 // input dimension K.
@@ -1675,32 +1393,24 @@ bool bwd_dma_ok(const BwdParams& p) {
   return (int64_t)p.M * p.ldy * 2 < lim && ((int64_t)p.N + 64) * (p.K / 2) < lim && p.ldy % 8 == 0;
 }
 
-template <int BM, int BN, int WGM, int WGN, int WK, int EPI>
+// The NF4 kernels take activations by DMA when their operands fit 32-bit
+// offsets; bf16 weights (and larger operands) use the register-path kernels.
+template <int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-#if LSQ_FWD_PP
-  static_assert(BM == 256 && BN == 256 && WGM * WGN == 8, "ping-pong forward is 256 x 256 with 8 waves");
+  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile);
   if (WK == LSQ_W_NF4 && fwd_dma_ok(p))
     gemm_fwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
   else
     gemm_fwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
-#else
-  gemm_fwd_kernel<BM, BN, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
-#endif
 }
 
-template <int BM, int BO, int WGM, int WGN, int WK, int EPI>
+template <int WK, int EPI>
 void launch_bwd(const BwdParams& p, hipStream_t s) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.K + BO - 1) / BO);
-#if LSQ_BWD_PP
-  static_assert(BM == 256 && BO == 256 && WGM * WGN == 8, "ping-pong backward is 256 x 256 with 8 waves");
+  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.K + kTile - 1) / kTile);
   if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
     gemm_bwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
   else
     gemm_bwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
-#else
-  gemm_bwd_kernel<BM, BO, WGM, WGN, WK, EPI><<<dim3(tiles, p.splits), 64 * WGM * WGN, 0, s>>>(p);
-#endif
 }
 
 void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* bias, const float* resid, void* out,
@@ -1737,42 +1447,31 @@ int choose_splits(int tiles, int ksteps, double out_elems, double tile_flops_per
   return best;
 }
 
-template <int BM, int BN, int WGM, int WGN, int WK>
+template <int WK>
 void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_fwd<BM, BN, WGM, WGN, WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_fwd<BM, BN, WGM, WGN, WK, EPI_F32>(p, s);
-  else launch_fwd<BM, BN, WGM, WGN, WK, EPI_F32_RESID>(p, s);
+  if (epi == EPI_BF16) launch_fwd<WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_fwd<WK, EPI_F32>(p, s);
+  else launch_fwd<WK, EPI_F32_RESID>(p, s);
 }
 
-template <int BM, int BO, int WGM, int WGN, int WK>
+template <int WK>
 void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_bwd<BM, BO, WGM, WGN, WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_bwd<BM, BO, WGM, WGN, WK, EPI_F32>(p, s);
-  else launch_bwd<BM, BO, WGM, WGN, WK, EPI_F32_RESID>(p, s);
+  if (epi == EPI_BF16) launch_bwd<WK, EPI_BF16>(p, s);
+  else if (epi == EPI_F32) launch_bwd<WK, EPI_F32>(p, s);
+  else launch_bwd<WK, EPI_F32_RESID>(p, s);
 }
-
-// Tile shape of each direction (compile-time; tuned on gfx950).  Kernel
-// choice is a pure function of the shape, never of where the weights live.
-#ifndef LSQ_FWD_TILE
-#define LSQ_FWD_TILE 256, 256, 4, 2
-#endif
-#ifndef LSQ_BWD_TILE
-#define LSQ_BWD_TILE 256, 256, 4, 2
-#endif
-constexpr int kFwdTile[4] = {LSQ_FWD_TILE};
-constexpr int kBwdTile[4] = {LSQ_BWD_TILE};
 
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
 int gemm_fwd_splits(int M, int N, int K) {
-  return choose_splits(((M + kFwdTile[0] - 1) / kFwdTile[0]) * ((N + kFwdTile[1] - 1) / kFwdTile[1]), K / 64,
-                       (double)M * N, 2.0 * kFwdTile[0] * kFwdTile[1] * 64);
+  return choose_splits(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile), K / 64, (double)M * N,
+                       2.0 * kTile * kTile * 64);
 }
 int gemm_bwd_splits(int M, int N, int K, int rr) {
-  const int lora_steps = LSQ_BWD_PP ? 0 : (rr + 63) / 64;   // ping-pong adds the LoRA term after its main loop
-  return choose_splits(((M + kBwdTile[0] - 1) / kBwdTile[0]) * ((K + kBwdTile[1] - 1) / kBwdTile[1]),
-                       (N + 63) / 64 + lora_steps, (double)M * K, 2.0 * kBwdTile[0] * kBwdTile[1] * 64);
+  (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
+  return choose_splits(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile), (N + 63) / 64, (double)M * K,
+                       2.0 * kTile * kTile * 64);
 }
 // Workspace of gemm_bwd: split-K partials, then (ping-pong) the transposed LoRA A.
 static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
@@ -1784,7 +1483,7 @@ size_t gemm_fwd_ws_bytes(int M, int N, int K) {
   return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
-  return gemm_bwd_part_bytes(M, N, K, rr) + (LSQ_BWD_PP && rr > 0 ? (size_t)rr * K * 2 : 0);
+  return gemm_bwd_part_bytes(M, N, K, rr) + (rr > 0 ? (size_t)rr * K * 2 : 0);
 }
 
 int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
@@ -1803,8 +1502,8 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
   // The profiler brackets the tile kernel alone; a split-K reduction is credited separately.
   int tok = prof_begin(s);
-  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_NF4>(p, epi, s);
-  else dispatch_fwd_epi<LSQ_FWD_TILE, LSQ_W_BF16>(p, epi, s);
+  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_W_NF4>(p, epi, s);
+  else dispatch_fwd_epi<LSQ_W_BF16>(p, epi, s);
   prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_FWD : PROF_GEMM_BF16, flops, bytes);
   if (p.splits > 1) {
     tok = prof_begin(s);
@@ -1826,7 +1525,6 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   LSQ_CHECK(need == 0 || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "gemm_bwd: needs %zu bytes of workspace",
             need);
   if (p.splits > 1) p.part = static_cast<float*>(ws);
-#if LSQ_BWD_PP
   if (p.rr > 0) {
     uint16_t* alt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + gemm_bwd_part_bytes(p.M, p.N, p.K, p.rr));
     const int64_t nel = (int64_t)p.rr * p.K;
@@ -1835,13 +1533,12 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
     prof_end(t0, s, PROF_OTHER, 0.0, 4.0 * nel);
     p.AlT = alt;
   }
-#endif
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
   int tok = prof_begin(s);
-  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_NF4>(p, epi, s);
-  else dispatch_bwd_epi<LSQ_BWD_TILE, LSQ_W_BF16>(p, epi, s);
+  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_W_NF4>(p, epi, s);
+  else dispatch_bwd_epi<LSQ_W_BF16>(p, epi, s);
   prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_BWD : PROF_GEMM_BF16, flops, bytes);
   if (p.splits > 1) {
     tok = prof_begin(s);

@@ -39,6 +39,7 @@ struct FwdParams {
   int64_t ldc;
   float* part;           // split-K partials [splits, M, N] (workspace); set by gemm_fwd
   int splits;
+  int bn;                // tile width in output columns; set by gemm_fwd
 };
 
 // Backward: out[M, K] = dY[M, N] W + G[M, rr] Al[rr, K] (+ resid).
@@ -64,7 +65,14 @@ struct BwdParams {
 // Split-K: a launch with fewer tiles than the chip has CUs splits its
 // reduction into a fixed number of ranges (a pure function of the shape),
 // writes float32 partials and sums them in split order in a second kernel.
-int gemm_fwd_splits(int M, int N, int K);
+// Forward plan: tile width (256, or 192 for the NF4 DMA kernels when 256-wide
+// tiles would leave a quarter of the CUs idle) and split count.  narrow: the
+// launch can take the narrower tile (NF4 weights, operands within 32-bit
+// offsets).  The split count does not depend on narrow.
+struct GemmPlan {
+  int bn, splits;
+};
+GemmPlan gemm_fwd_plan(int M, int N, int K, bool narrow);
 int gemm_bwd_splits(int M, int N, int K, int rr);
 size_t gemm_fwd_ws_bytes(int M, int N, int K);
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr);

@@ -324,9 +324,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // and the k loop is unrolled by two so that every access names its stage
 // statically (the compiler can then tell DMA writes to one stage from reads of
 // the other and does not drain the DMA queue before each fragment read).
-template <int EPI>
+//
+// BN is the tile's width in output columns (256, or 192 where 256-wide tiles
+// would leave a quarter of the CUs idle: N = 6144 at 2048 rows gives 192
+// tiles of 256 but 256 of 192).  Each group decodes BN / 2 weight rows; the
+// spare threads of the narrower tile load a duplicate row and skip the store.
+template <int EPI, int BN>
 __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
-  constexpr int BM = 256, BN = 256, WM = 64, WN = 128, TM = WM / 16, TN = WN / 16, GT = 256;
+  static_assert(BN % 32 == 0 && BN <= 256, "two 16-column-aligned wave columns per tile");
+  constexpr int BM = 256, WM = 64, WN = BN / 2, TM = WM / 16, TN = WN / 16, GT = 256;
   __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * 64];
@@ -362,7 +368,8 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   const uint32_t x_voff = (uint32_t)(((xrow0 + (lane >> 3)) * p.ldx + (((lane & 7) ^ (lane >> 3)) * 8)) * 2);
   const uint32_t x_blk = (uint32_t)(8 * p.ldx * 2);
   // This thread's 32 codes (row, half of the 64-wide block) and their scale.
-  const int brow = grp * 128 + (gtid >> 1), bh = gtid & 1;
+  const bool bact = BN == 256 || gtid < BN;
+  const int brow = grp * WN + (bact ? (gtid >> 1) : WN - 1), bh = gtid & 1;
   const uint32_t w_voff = (uint32_t)(brow * (K / 2) + bh * 16);
   const uint32_t s_voff = (uint32_t)(brow * (K / 64) * 4);
 
@@ -380,6 +387,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   };
   auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) {
     const uint32_t words[4] = {rb[set].x, rb[set].y, rb[set].z, rb[set].w};
+    if (!bact) return;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t o[4];
@@ -1397,11 +1405,11 @@ bool bwd_dma_ok(const BwdParams& p) {
 // offsets; bf16 weights (and larger operands) use the register-path kernels.
 template <int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s) {
-  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + kTile - 1) / kTile);
-  if (WK == LSQ_W_NF4 && fwd_dma_ok(p))
-    gemm_fwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
-  else
-    gemm_fwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + p.bn - 1) / p.bn);
+  const dim3 grid(tiles, p.splits);
+  if (WK != LSQ_W_NF4 || !fwd_dma_ok(p)) gemm_fwd_pp_kernel<WK, EPI><<<grid, 512, 0, s>>>(p);
+  else if (p.bn == 192) gemm_fwd_nf4_dma_kernel<EPI, 192><<<grid, 512, 0, s>>>(p);
+  else gemm_fwd_nf4_dma_kernel<EPI, 256><<<grid, 512, 0, s>>>(p);
 }
 
 template <int WK, int EPI>
@@ -1430,8 +1438,11 @@ void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* 
 // reduction steps; every extra split writes and re-reads an fp32 partial of the
 // whole output.  Per-step time is the tile's flops at ~40% of one CU's MFMA
 // peak; partial traffic is priced at 4 TB/s.
-int choose_splits(int tiles, int ksteps, double out_elems, double tile_flops_per_step) {
-  const double step_us = tile_flops_per_step / (0.4 * 2.5e15 / 256) * 1e6;
+// Split count of a launch of 256 x 256 tiles: modelled time = whole rounds of
+// 256 workgroups x k-steps per split at 40% of the per-CU MFMA peak, plus the
+// fp32 partials of a split written and read back at 4 TB/s.
+int choose_splits(int tiles, int ksteps, double out_elems) {
+  const double step_us = 2.0 * kTile * kTile * BK / (0.4 * 2.5e15 / 256) * 1e6;
   int best = 1;
   double best_t = 1e30;
   for (int sp = 1; sp <= 8; ++sp) {
@@ -1464,14 +1475,21 @@ void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
-int gemm_fwd_splits(int M, int N, int K) {
-  return choose_splits(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile), K / 64, (double)M * N,
-                       2.0 * kTile * kTile * 64);
+GemmPlan gemm_fwd_plan(int M, int N, int K, bool narrow) {
+  const int tm = (M + kTile - 1) / kTile;
+  const int tiles = tm * ((N + kTile - 1) / kTile);
+  const int sp = choose_splits(tiles, K / 64, (double)M * N);
+  // One round that leaves a quarter of the CUs idle: 192-wide tiles, same
+  // split count, when they still fit one round.  (Measured on gfx950: 10%
+  // faster for N = 6144 at 2048 rows; a narrower tile does not pay where the
+  // wide plan is nearly full, the chip's clock rises when CUs idle.)
+  const int wgs = tiles * sp, wgs192 = tm * ((N + 191) / 192) * sp;
+  if (narrow && wgs <= 192 && wgs192 > wgs && wgs192 <= 256) return GemmPlan{192, sp};
+  return GemmPlan{kTile, sp};
 }
 int gemm_bwd_splits(int M, int N, int K, int rr) {
   (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
-  return choose_splits(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile), (N + 63) / 64, (double)M * K,
-                       2.0 * kTile * kTile * 64);
+  return choose_splits(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile), (N + 63) / 64, (double)M * K);
 }
 // Workspace of gemm_bwd: split-K partials, then (ping-pong) the transposed LoRA A.
 static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
@@ -1479,7 +1497,7 @@ static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
   return sp > 1 ? ((size_t)sp * M * K * sizeof(float) + 255) / 256 * 256 : 0;
 }
 size_t gemm_fwd_ws_bytes(int M, int N, int K) {
-  const int sp = gemm_fwd_splits(M, N, K);
+  const int sp = gemm_fwd_plan(M, N, K, true).splits;   // the tile width never changes the split count
   return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
@@ -1491,7 +1509,9 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
   LSQ_CHECK(p.r == 0 || (p.r % 8 == 0 && p.ldu % 8 == 0), LSQ_ERR_SHAPE, "gemm: LoRA rank must be a multiple of 8");
   if (p.M == 0 || p.N == 0) return LSQ_OK;
-  p.splits = gemm_fwd_splits(p.M, p.N, p.K);
+  const GemmPlan plan = gemm_fwd_plan(p.M, p.N, p.K, p.kind == LSQ_W_NF4 && fwd_dma_ok(p));
+  p.bn = plan.bn;
+  p.splits = plan.splits;
   if (p.splits > 1) {
     LSQ_CHECK(ws && ws_bytes >= gemm_fwd_ws_bytes(p.M, p.N, p.K) && p.N % 4 == 0, LSQ_ERR_WORKSPACE,
               "gemm_fwd: split-K needs %zu bytes of workspace", gemm_fwd_ws_bytes(p.M, p.N, p.K));

@@ -129,6 +129,10 @@ LINEAR_CASES = [
     (64, 1600, 520, 16),
     (64, 1344, 264, 8),
     (513, 192, 264, 8),
+    # ragged last column tiles of many-tile launches: 192-wide tiles split
+    # four ways, 256-wide unsplit
+    (200, 1024, 7600, 16),
+    (300, 256, 28680, 8),
 ]
 
 

@@ -85,37 +85,48 @@ __global__ void __launch_bounds__(256) nf4_quantize_kernel(const uint16_t* __res
   absmax[b] = a;
 }
 
-// One thread per 16 packed bytes (32 weights, half of one 64-weight block):
-// one 16-byte load, the 16 levels from LDS, 64 (bf16) or 128 (fp32) bytes out.
+// Each wave dequantizes one 2048-weight segment in four passes; in pass q,
+// lane l takes the 8 weights [512 q + 8 l, + 8) of the segment: one 4-byte
+// load of packed codes and its block's absmax, one 16-byte (bf16) or two
+// 16-byte (fp32) stores.  Every load and store instruction of a wave covers a
+// contiguous range (256 B of codes in, 1 KiB or 2 KiB out).  n_w is a multiple
+// of 64, so a lane's 8 weights are all in range or all out.
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ packed,
-                                                          const float* __restrict__ absmax, int64_t n_chunks,
+                                                          const float* __restrict__ absmax, int64_t n_w,
                                                           void* __restrict__ out) {
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = lsq::kNF4LevelsDev[threadIdx.x];
   __syncthreads();
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= n_chunks) return;
-  const uint4 p = *reinterpret_cast<const uint4*>(packed + c * 16);
-  const float a = absmax[c >> 1];
-  const uint32_t words[4] = {p.x, p.y, p.z, p.w};
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2048 + lane * 8;
+  uint32_t word[4];
+  float a[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    float vals[8];
+  for (int q = 0; q < 4; ++q) {
+    const int64_t e = w0 + q * 512;
+    const bool ok = e < n_w;
+    word[q] = ok ? *reinterpret_cast<const uint32_t*>(packed + e / 2) : 0u;
+    a[q] = ok ? absmax[e >> 6] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t e = w0 + q * 512;
+    if (e >= n_w) break;
+    float v[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = (words[w] >> (8 * j)) & 0xFF;
-      vals[2 * j] = lut[byte >> 4] * a;
-      vals[2 * j + 1] = lut[byte & 15] * a;
+      const uint32_t byte = (word[q] >> (8 * j)) & 0xFF;
+      v[2 * j] = lut[byte >> 4] * a[q];
+      v[2 * j + 1] = lut[byte & 15] * a[q];
     }
     if (OUT_F32) {
-      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + c * 32 + w * 8);
-      o[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
-      o[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + e);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
     } else {
-      uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + c * 32 + w * 8);
-      *o = make_uint4(pack_bf16x2(vals[0], vals[1]), pack_bf16x2(vals[2], vals[3]), pack_bf16x2(vals[4], vals[5]),
-                      pack_bf16x2(vals[6], vals[7]));
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e) =
+          make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
     }
   }
 }
@@ -160,16 +171,14 @@ int nf4_dequantize(const void* packed_dev, const float* absmax_dev, int64_t n_ou
             "nf4_dequantize: n_in must be a multiple of 64");
   LSQ_CHECK(lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev) && lsq::aligned16(w_out_dev), LSQ_ERR_ALIGN,
             "nf4_dequantize: pointers must be 16-byte aligned");
-  int64_t n_chunks = n_out * n_in / 32;
-  if (n_chunks == 0) return LSQ_OK;
-  dim3 grid(static_cast<unsigned>((n_chunks + 255) / 256));
+  const int64_t n_w = n_out * n_in;
+  if (n_w == 0) return LSQ_OK;
+  dim3 grid(static_cast<unsigned>((n_w + 8191) / 8192));   // 4 waves x 2048 weights per block
   hipStream_t s = lsq::as_stream(stream);
   if (out_dtype == LSQ_F32)
-    nf4_dequant_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_chunks,
-                                                  w_out_dev);
+    nf4_dequant_kernel<true><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_w, w_out_dev);
   else
-    nf4_dequant_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_chunks,
-                                                   w_out_dev);
+    nf4_dequant_kernel<false><<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(packed_dev), absmax_dev, n_w, w_out_dev);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }

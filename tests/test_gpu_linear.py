@@ -62,19 +62,24 @@ def test_nf4_shape_errors_enqueue_nothing(gpu):
     assert e.value.status == "LSQ_ERR_SHAPE"
 
 
-@pytest.mark.parametrize("shape", [(1024, 512), (40, 320)])
+# whole and partial 2048-weight wave segments, down to a single 64-block
+@pytest.mark.parametrize("shape", [(1024, 512), (40, 320), (1, 64), (7, 4416)])
 def test_nf4_dequantize_bit_exact(gpu, shape):
     print_case(test="nf4_dequantize", shape=shape)
     w = synth.normal_bf16(shape, 0.0, 0.02, (80, shape[0]))
     rp, ra = onf4.quantize(w)
     packed, absmax = dev(rp), dev(ra)
-    out_b = torch.empty(shape, dtype=torch.int16, device="cuda")
-    out_f = torch.empty(shape, dtype=torch.float32, device="cuda")
+    n = shape[0] * shape[1]
+    # 8192 guard elements after the output must keep their fill
+    out_b = torch.full((n + 8192,), 0x5A5A, dtype=torch.int16, device="cuda")
+    out_f = torch.full((n + 8192,), 7.0, dtype=torch.float32, device="cuda")
     lib.call("nf4_dequantize", ptr(packed), ptr(absmax), shape[0], shape[1], lib.LSQ_BF16, ptr(out_b), stream())
     lib.call("nf4_dequantize", ptr(packed), ptr(absmax), shape[0], shape[1], lib.LSQ_F32, ptr(out_f), stream())
     torch.cuda.synchronize()
-    assert np.array_equal(host_bits(out_b), onf4.dequantize_bf16_bits(rp, ra))
-    assert np.array_equal(out_f.cpu().numpy().view(np.uint32), onf4.dequantize_f32(rp, ra).view(np.uint32))
+    assert np.array_equal(host_bits(out_b[:n].view(shape)), onf4.dequantize_bf16_bits(rp, ra))
+    assert np.array_equal(out_f[:n].view(shape).cpu().numpy().view(np.uint32),
+                          onf4.dequantize_f32(rp, ra).view(np.uint32))
+    assert bool((out_b[n:] == 0x5A5A).all()) and bool((out_f[n:] == 7.0).all())
 
 
 # ------------------------------------------------------------------ linear

@@ -11,6 +11,7 @@
 #include "common.h"
 #include "layer_ops.h"
 
+#include <algorithm>
 #include <cfloat>
 
 namespace lsq {
@@ -775,37 +776,56 @@ __global__ void attn_dkdv_reduce_kernel(AttnBwdArgs a, int B) {
 }
 
 // ------------------------------------------------------------------ SwiGLU
-// gu [T, 2I] (gate | up) -> m [T, I] = bf16(silu(g) * u)
-__global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ m) {
-  int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
-  if (e >= (int64_t)T * I) return;
-  const int64_t t = e / I, i = e % I;
-  const uint32_t gw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + i);
-  const uint32_t uw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + I + i);
-  float g0 = bf_lo(gw), g1 = bf_hi(gw), u0 = bf_lo(uw), u1 = bf_hi(uw);
-  float s0 = g0 / (1.f + __expf(-g0)), s1 = g1 / (1.f + __expf(-g1));
-  *reinterpret_cast<uint32_t*>(m + e) = pack_bf16x2(s0 * u0, s1 * u1);
+// gu [T, 2I] (gate | up) -> m [T, I] = bf16(silu(g) * u).
+// Rows t = blockIdx.y, + gridDim.y, ...; this thread's 8 intermediate columns start at i.
+__global__ void __launch_bounds__(256) swiglu_fwd_kernel(const uint16_t* __restrict__ gu, int T, int I,
+                                                         uint16_t* __restrict__ m) {
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= I) return;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    const uint4 gv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + i);
+    const uint4 uv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float g0 = bf_lo(gw[q]), g1 = bf_hi(gw[q]), u0 = bf_lo(uw[q]), u1 = bf_hi(uw[q]);
+      const float s0 = g0 / (1.f + __expf(-g0)), s1 = g1 / (1.f + __expf(-g1));
+      o[q] = pack_bf16x2(s0 * u0, s1 * u1);
+    }
+    *reinterpret_cast<uint4*>(m + t * I + i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // dgu [T, 2I]: dg = dm u sig(g) (1 + g (1 - sig(g))), du = dm silu(g)
-__global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ gu, const uint16_t* __restrict__ dm, int T, int I,
-                                  uint16_t* __restrict__ dgu) {
-  int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
-  if (e >= (int64_t)T * I) return;
-  const int64_t t = e / I, i = e % I;
-  const uint32_t gw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + i);
-  const uint32_t uw = *reinterpret_cast<const uint32_t*>(gu + t * 2 * I + I + i);
-  const uint32_t dw = *reinterpret_cast<const uint32_t*>(dm + e);
-  float g[2] = {bf_lo(gw), bf_hi(gw)}, u[2] = {bf_lo(uw), bf_hi(uw)}, d[2] = {bf_lo(dw), bf_hi(dw)};
-  float dg[2], du[2];
+__global__ void __launch_bounds__(256) swiglu_bwd_kernel(const uint16_t* __restrict__ gu,
+                                                         const uint16_t* __restrict__ dm, int T, int I,
+                                                         uint16_t* __restrict__ dgu) {
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= I) return;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    const uint4 gv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + i);
+    const uint4 uv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dm + t * I + i);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
+    uint32_t og[4], ou[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float sg = 1.f / (1.f + __expf(-g[j]));
-    dg[j] = d[j] * u[j] * sg * (1.f + g[j] * (1.f - sg));
-    du[j] = d[j] * g[j] * sg;
+    for (int q = 0; q < 4; ++q) {
+      const float g[2] = {bf_lo(gw[q]), bf_hi(gw[q])}, u[2] = {bf_lo(uw[q]), bf_hi(uw[q])},
+                  d[2] = {bf_lo(dw[q]), bf_hi(dw[q])};
+      float dg[2], du[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sg = 1.f / (1.f + __expf(-g[j]));
+        dg[j] = d[j] * u[j] * sg * (1.f + g[j] * (1.f - sg));
+        du[j] = d[j] * g[j] * sg;
+      }
+      og[q] = pack_bf16x2(dg[0], dg[1]);
+      ou[q] = pack_bf16x2(du[0], du[1]);
+    }
+    *reinterpret_cast<uint4*>(dgu + t * 2 * I + i) = make_uint4(og[0], og[1], og[2], og[3]);
+    *reinterpret_cast<uint4*>(dgu + t * 2 * I + I + i) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
   }
-  *reinterpret_cast<uint32_t*>(dgu + t * 2 * I + i) = pack_bf16x2(dg[0], dg[1]);
-  *reinterpret_cast<uint32_t*>(dgu + t * 2 * I + I + i) = pack_bf16x2(du[0], du[1]);
 }
 
 // ------------------------------------------------------------------ embedding
@@ -1027,21 +1047,21 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
 }
 
 int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s) {
-  LSQ_CHECK(I % 2 == 0, LSQ_ERR_SHAPE, "swiglu: odd intermediate");
-  const int64_t n = (int64_t)T * I / 2;
-  if (n == 0) return LSQ_OK;
+  LSQ_CHECK(I % 8 == 0, LSQ_ERR_SHAPE, "swiglu: intermediate %d must be a multiple of 8", I);
+  if ((int64_t)T * I == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  swiglu_fwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, T, I, m);
+  swiglu_fwd_kernel<<<dim3((unsigned)((I / 8 + 255) / 256), (unsigned)std::min(T, 65535)), 256, 0, s>>>(gu, T, I, m);
   prof_end(tok, s, PROF_ELEM, 0.0, 6.0 * T * (double)I);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
 
 int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* dgu, hipStream_t s) {
-  const int64_t n = (int64_t)T * I / 2;
-  if (n == 0) return LSQ_OK;
+  LSQ_CHECK(I % 8 == 0, LSQ_ERR_SHAPE, "swiglu: intermediate %d must be a multiple of 8", I);
+  if ((int64_t)T * I == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  swiglu_bwd_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, dm, T, I, dgu);
+  swiglu_bwd_kernel<<<dim3((unsigned)((I / 8 + 255) / 256), (unsigned)std::min(T, 65535)), 256, 0, s>>>(gu, dm, T, I,
+                                                                                                  dgu);
   prof_end(tok, s, PROF_ELEM, 0.0, 10.0 * T * (double)I);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

@@ -322,8 +322,9 @@ def cpu_baseline(cfg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the pages' protocol: 50 steps after 10 warm-up steps, median and slowest step reported
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b-stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--buffers", type=int, default=None)

@@ -70,7 +70,12 @@ def inputs(cfg, seq=None):
 
 
 @pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_QWEN,
-                                 configs.TINY.with_(name="tiny-b1-s200", batch=1, seq=200, wid=11)])
+                                 configs.TINY.with_(name="tiny-b1-s200", batch=1, seq=200, wid=11),
+                                 # one-token sequences; head_dim 128 with one kv head per two query
+                                 # heads and a sequence one past a whole query block
+                                 configs.TINY.with_(name="tiny-s1", batch=3, seq=1, wid=13),
+                                 configs.TINY.with_(name="tiny-hd128", n_heads=2, n_kv_heads=1, head_dim=128,
+                                                    batch=2, seq=129, wid=14)])
 def test_decoder_layer_matches_oracle(gpu, cfg):
     print_case(test="decoder_layer", cfg=cfg.name, B=cfg.batch, S=cfg.seq)
     x_bits, dout = inputs(cfg)
@@ -83,9 +88,17 @@ def test_decoder_layer_matches_oracle(gpu, cfg):
     assert rel_err(got["x_out"].reshape(ref_out.shape), ref_out) <= TOL
     assert rel_err(got["dx_in"].reshape(ref_dx.shape), ref_dx) <= TOL
     g = model.split_lora_grads(cfg, got["grad"])
+    # With one-token sequences the softmax has a single key, so q and k get no
+    # gradient at all: their references are exactly zero and the GPU's rounding
+    # noise is measured against the layer's largest adapter gradient instead.
+    scale = max(float(np.abs(ref_g[n][w]).max()) for n in model.PROJ for w in (0, 1))
     for name in model.PROJ:
         for which in (0, 1):
-            e = rel_err(g[name][which], ref_g[name][which])
+            ref = ref_g[name][which]
+            if np.abs(ref).max() == 0.0:
+                e = float(np.abs(g[name][which]).max()) / scale
+            else:
+                e = rel_err(g[name][which], ref)
             assert e <= TOL, f"{name} d{'AB'[which]}: {e:.3e}"
 
 

@@ -244,6 +244,33 @@ def test_layer_merged_lora_and_identity_special_cases():
     assert np.allclose(L.layer_fwd(CFG, x, ident, zero, S_SCALE), x)
 
 
+def test_single_token_sequences_give_q_and_k_no_gradient():
+    """With one key the attention output is that key's value whatever the
+    scores, so the loss does not depend on q or k: their adapter gradients are
+    zero, while v, o and the MLP adapters still receive gradient (checked by
+    finite differences on v)."""
+    Wn, adn = _layer_params(CFG, 18)
+    g = np.random.default_rng(19)
+    x = g.standard_normal((3, 1, CFG.hidden))
+    dout = g.standard_normal((3, 1, CFG.hidden))
+    _, grads = L.layer_bwd(CFG, x, Wn, adn, S_SCALE, dout)
+    for n in ("q", "k"):
+        assert np.abs(grads[n][0]).max() <= 1e-12 and np.abs(grads[n][1]).max() <= 1e-12, n
+    for n in ("v", "o", "gate", "up", "down"):
+        assert np.abs(grads[n][0]).max() > 1e-3 and np.abs(grads[n][1]).max() > 1e-3, n
+
+    def f(ad_):
+        return float(np.sum(L.layer_fwd(CFG, x, Wn, ad_, S_SCALE) * dout))
+
+    eps = 1e-6
+    pa = {k: (a.copy(), b.copy()) for k, (a, b) in adn.items()}
+    ma = {k: (a.copy(), b.copy()) for k, (a, b) in adn.items()}
+    pa["v"][1][2, 1] += eps
+    ma["v"][1][2, 1] -= eps
+    num = (f(pa) - f(ma)) / (2 * eps)
+    assert abs(num - grads["v"][1][2, 1]) < 1e-6 * max(1, abs(num))
+
+
 def test_gqa_equals_repeated_kv_heads():
     Wn, adn = _layer_params(CFG, 16)
     x = np.random.default_rng(17).standard_normal((1, 6, CFG.hidden))

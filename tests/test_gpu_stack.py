@@ -140,6 +140,30 @@ def test_streamed_equals_resident_and_control_breaks_it(gpu, cfg):
     assert exact_bad < total
 
 
+@pytest.mark.parametrize("n_layers", [1, 2])
+def test_short_stacks_match_oracle_and_resident(gpu, n_layers):
+    """Stacks no longer than the pool: every layer stays in a slot across the
+    turn, one copy per layer on the first step, and the results still match
+    the oracle and the resident run."""
+    cfg = configs.TINY.with_(name=f"tiny-{n_layers}L", n_layers=n_layers, wid=20 + n_layers)
+    print_case(test="short_stack", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids_np = ids_for(cfg)
+    ids = torch.from_numpy(ids_np).cuda()
+    got = traced_step(cfg, store, res, ids)
+    loss, logits, _ = oracle_step(cfg, ids_np)
+    assert abs(got["loss"] - loss) <= TOL * abs(loss)
+    assert rel_err(got["logits"].reshape(logits.shape), logits) <= TOL
+    check_head_against_oracle(cfg, got, ids_np)
+    check_layers_against_oracle(cfg, got, range(cfg.n_layers))
+    resident = run(cfg, "resident", store, res, ids)
+    streamed = run(cfg, "streamed", store, res, ids)
+    exact, total = _compare_bitwise(cfg, resident, streamed)
+    assert exact == total == cfg.n_layers * 14
+    assert streamed["stats"].copies == 2 * cfg.n_layers - min(cfg.n_buffers, cfg.n_layers) == n_layers
+
+
 def test_step_is_deterministic_and_repeats(gpu):
     cfg = configs.TINY
     store = model.Store(cfg)

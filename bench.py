@@ -1,6 +1,6 @@
 """Streamed LoRA fwd+bwd throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama8b-stack]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload llama8b-stack]
 
 A step is one lsq_train_step over the whole hot path: embedding, 32 streamed
 NF4 decoder layers forward (two VRAM slots, prefetch one ahead on a dedicated
@@ -248,6 +248,64 @@ def dequant_rate(torch, lib, N=28672, K=4096, reps=20):
             "frac_of_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBPS, 4), "bytes_per_launch": nbytes}
 
 
+def layer_rates(torch, lib, model, configs, reps=5):
+    """One Llama-3.1-8B-shaped decoder layer (1 x 2048 tokens, the blob resident
+    in HBM) forward and backward through decoder_layer_fwd / decoder_layer_bwd:
+    the time of the pair and, per kernel family, its time, TFLOP/s and GB/s
+    from the library's events.  At 2048 tokens the elementwise kernels move
+    4x the bytes per launch of the 512-token stack."""
+    cfg = configs.LAYER_8B
+    B, S, H = cfg.batch, cfg.seq, cfg.hidden
+    st = lib.stream_handle(torch.cuda.current_stream())
+    P = lambda t: C.c_void_p(t.data_ptr())
+    store = model.Store(cfg)
+    blob = torch.from_numpy(store.host_blob(0).copy()).cuda()
+    store.close()
+    lora = torch.from_numpy(model.lora_arena_host(cfg)[0].view(np.int16)).cuda()
+    ccfg = lib.model_cfg(cfg)
+    wsb = lib.raw("decoder_layer_workspace_size")(C.byref(ccfg), B, S)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2049)
+    x = torch.randn(B * S, H, device="cuda", generator=g).to(torch.bfloat16).float()
+    dxo = torch.randn(B * S, H, device="cuda", generator=g).to(torch.bfloat16).float()
+    xo, dxi = torch.empty_like(x), torch.empty_like(x)
+    grad = torch.zeros(lora.numel(), dtype=torch.float32, device="cuda")
+
+    def pair():
+        lib.call("decoder_layer_fwd", C.byref(ccfg), P(blob), P(lora), P(x), B, S, P(xo), P(ws), wsb, st)
+        lib.call("decoder_layer_bwd", C.byref(ccfg), P(blob), P(lora), P(x), P(dxo), B, S, P(dxi), P(grad), 0,
+                 P(ws), wsb, st)
+    for _ in range(2):
+        pair()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pair()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    lib.call("lsq_prof_enable", 1)
+    for _ in range(reps):
+        pair()
+    torch.cuda.synchronize()
+    entries = (lib.ProfEntry * 8)()
+    n = C.c_int32()
+    lib.call("lsq_prof_read", entries, 8, C.byref(n))
+    lib.call("lsq_prof_enable", 0)
+    fams = {}
+    for e in entries[:n.value]:
+        fams[e.name.decode()] = {
+            "ms": round(e.ms / reps, 3), "launches": e.launches // reps,
+            "TFLOPs": round(e.flops / (e.ms * 1e-3) / 1e12, 1) if e.ms and e.flops else None,
+            "GBps": round(e.bytes / (e.ms * 1e-3) / 1e9, 1) if e.ms and e.bytes else None}
+    del blob, lora, ws, x, dxo, xo, dxi, grad
+    return {"workload": cfg.name, "tokens": B * S, "fwd_bwd_ms": round(ms, 3),
+            "tok_s": round(B * S / (ms * 1e-3), 1), "families": fams,
+            "note": "backward includes the layer's recompute; blob resident, no copies"}
+
+
 def copy_calibration(torch, nbytes=1 << 30):
     """A plain device-to-device copy of known size, for scaling FETCH_SIZE /
     WRITE_SIZE counters (run under rocprofv3 --pmc)."""
@@ -430,6 +488,7 @@ def main():
     # after the peak is read: torch keeps a BLAS workspace allocated once it has run a GEMM
     gprobe = gemm_probe(torch)
     linears = None if a.no_linears else linear_gemm_rates(torch, lib)
+    layer2048 = None if a.no_linears else layer_rates(torch, lib, model, configs)
     dequant = dequant_rate(torch, lib)
     log(f"bf16 GEMM probe (torch.mm 8192^3): {gprobe:.0f} TFLOP/s")
 
@@ -498,6 +557,7 @@ def main():
             if prof.get("elementwise", {}).get("ms") else None,
             "nf4_dequantize": dequant},
         "linear_gemms_T2048": linears,
+        "layer_T2048": layer2048,
         "preflight_predicted_bytes": pf.total,
         "peak_allocated_bytes": peak_alloc,
         "loss": loss,

@@ -136,6 +136,7 @@ struct LayerWs {
   uint16_t* dqkv;     // [T, Nqkv]
   float* dk_part;     // [T, nh, hd] per-query-head dK, dV partials
   float* dv_part;
+  uint16_t* aprep;    // attention operands prepared once per call
   float* lws;         // scratch of the LoRA down / G kernels
   size_t lws_bytes;
   float* tn;          // token-reduction partials
@@ -219,6 +220,7 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
   w.gemm = take(w.gemm_bytes);
   w.lws_bytes = lws_need(d, (int)T);
   w.lws = static_cast<float*>(take(w.lws_bytes));
+  w.aprep = static_cast<uint16_t*>(take(attention_prep_bytes(B, S, d.nh, d.nkv, d.hd, bwd)));
   if (bwd) {
     w.G32 = static_cast<float*>(take(4 * T * 3 * d.r));
     w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
@@ -359,7 +361,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   }
   {
     AttnArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, d.Nq, w.lse,
-               reinterpret_cast<const float2*>(w.rope), w.attn_f32};
+               reinterpret_cast<const float2*>(w.rope), w.attn_f32, w.aprep};
     TRY(attention_fwd(a, B, s));
   }
   TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, s));
@@ -476,7 +478,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- attention (rotary applied inside, in float32)
   {
     AttnBwdArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, w.attn_f32, w.dattn, d.Nq,
-                  w.lse, nullptr, w.dqkv, reinterpret_cast<const float2*>(w.rope), w.dk_part, w.dv_part};
+                  w.lse, nullptr, w.dqkv, reinterpret_cast<const float2*>(w.rope), w.dk_part, w.dv_part, w.aprep};
     TRY(attention_bwd(a, B, w.D, s));
   }
   // ---- q, k, v projections

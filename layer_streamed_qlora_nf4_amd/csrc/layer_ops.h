@@ -15,6 +15,7 @@ struct AttnArgs {
   float* lse;       // [B, nh, S], base-2 log-sum-exp of the scaled scores
   const float2* rope;  // [S, hd/2] (cos, sin); q and k are rotated on load
   float* out_f32;      // nullable: the same output in float32 (kept for the backward)
+  uint16_t* prep;      // attention_prep_bytes(.., false) of workspace
 };
 
 struct AttnBwdArgs {
@@ -32,7 +33,13 @@ struct AttnBwdArgs {
   const float2* rope;
   float* dk_part;       // [B, nh, S, hd] per-query-head partials (workspace)
   float* dv_part;
+  uint16_t* prep;       // attention_prep_bytes(.., true) of workspace
 };
+
+// Workspace of the operands each attention call prepares once (rotated and
+// split into bf16 hi/lo, or transposed, rows padded with zeros to a multiple
+// of 64): K and V^T for the forward; K, K^T, Q, Q^T and dO^T too for the backward.
+size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd);
 
 int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
                 uint16_t* y_lo = nullptr);

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cfloat>
+#include <utility>
 
 namespace lsq {
 namespace {
@@ -226,180 +227,6 @@ __device__ __forceinline__ void store_hilo8(uint16_t* hi, uint16_t* lo, const fl
   *reinterpret_cast<bf16x8*>(lo) = l;
 }
 
-template <int HD>
-struct AttnF16Smem {
-  uint16_t kh[AT][HD + 8];     // rotated K, bf16 hi  [key][d]
-  uint16_t kl[AT][HD + 8];     // rotated K, bf16 lo
-  uint16_t vt[HD][AT + 8];     // V transposed [d][key]
-  uint16_t ph[4][16][AT + 8];  // per-wave P hi [query][key]
-  uint16_t pl[4][16][AT + 8];  // per-wave P lo
-};
-
-// Stage one 64-key block: K rotated and split into kh/kl, V transposed into vt.
-template <int HD>
-__device__ __forceinline__ void stage_kv(AttnF16Smem<HD>& sm, const uint16_t* Kp, const uint16_t* Vp, int64_t ld,
-                                         int k0, int nk, const float2* __restrict__ rope) {
-  constexpr int HALF = HD / 2, NCH = HALF / 32;   // 8-pair chunks per thread: 2 (hd 128) or 1 (hd 64)
-  const int tid = threadIdx.x;
-  {
-    const int r = tid >> 2, q = tid & 3;   // row, quarter of the pair range
-    const bool ok = r < nk;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int i0 = (q * NCH + c) * 8;   // first pair index of this chunk
-      float x1[8], x2[8];
-      const uint16_t* row = Kp + (int64_t)(k0 + r) * ld;
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
-      if (ok) rope8(x1, x2, rope + (int64_t)(k0 + r) * HALF + i0);
-      store_hilo8(&sm.kh[r][i0], &sm.kl[r][i0], x1);
-      store_hilo8(&sm.kh[r][HALF + i0], &sm.kl[r][HALF + i0], x2);
-    }
-  }
-  // V: micro-tiles of 4 keys x 8 dims, transposed in registers
-  constexpr int NMT = AT / 4 * (HD / 8);
-  if (tid < NMT) {
-    const int kg = tid / (HD / 8), dg = tid % (HD / 8);
-    uint32_t w[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 4 * kg + i;
-      const uint4 v = key < nk ? *reinterpret_cast<const uint4*>(Vp + (int64_t)(k0 + key) * ld + 8 * dg)
-                               : make_uint4(0u, 0u, 0u, 0u);
-      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int sel = (c & 1) ? 0x07060302 : 0x05040100;
-      const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
-      *reinterpret_cast<u32x2*>(&sm.vt[8 * dg + c][4 * kg]) = u32x2{lo, hi};
-    }
-  }
-}
-
-// Forward: one workgroup per (query block of 64, head, batch), the heaviest
-// query blocks first; wave w owns queries 16w .. 16w+15 and keeps its rotated q
-// as MFMA operands in registers.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  AttnF16Smem<HD>& sm = *reinterpret_cast<AttnF16Smem<HD>*>(smem_raw);
-  constexpr int DC = HD / 32, DT = HD / 16, HALF = HD / 2;
-  const int nqb = gridDim.x;
-  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (a.nh / a.nkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int q0 = qb * AT;
-  const int64_t rowbase = (int64_t)b * a.S;
-  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
-  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
-  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
-  // this lane's query row, its 8-wide d slices 32c + 8 lg .. +8, rotated and split
-  bf16x8 qh[DC], ql[DC];
-  {
-    const int qi = q0 + 16 * w + lr;
-    const bool ok = qi < a.S;
-    const uint16_t* row = Q + (int64_t)qi * a.ld;
-#pragma unroll
-    for (int c = 0; c < DC / 2; ++c) {
-      const int i0 = 32 * c + 8 * lg;
-      float x1[8], x2[8];
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
-      if (ok) rope8(x1, x2, a.rope + (int64_t)qi * HALF + i0);
-      split8(x1, qh[c], ql[c]);
-      split8(x2, qh[c + DC / 2], ql[c + DC / 2]);
-    }
-  }
-  const float sc = a.scale * kLog2e;
-  float m[4], l[4];
-  f32x4 o[DT];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb <= qb; ++kb) {
-    const int k0 = kb * AT;
-    const int nk = min(AT, a.S - k0);
-    __syncthreads();   // the previous block's kh/kl/vt reads are done
-    stage_kv<HD>(sm, Kp, Vp, a.ld, k0, nk, a.rope);
-    __syncthreads();
-    f32x4 st[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
-        const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
-        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
-        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
-        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = q0 + 16 * w + 4 * lg + v;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int kj = k0 + 16 * jt + lr;
-        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
-        mx = fmaxf(mx, st[jt][v]);
-      }
-      mx = group16_max(mx);
-      const float mn = fmaxf(m[v], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
-      float rs = 0.f;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
-        const uint16_t ph = f32_to_bf16_bits(pv);
-        sm.ph[w][4 * lg + v][16 * jt + lr] = ph;
-        sm.pl[w][4 * lg + v][16 * jt + lr] = f32_to_bf16_bits(pv - bf16_bits_to_f32(ph));
-        rs += pv;
-      }
-      rs = group16_sum(rs);
-      l[v] = l[v] * alpha + rs;
-      m[v] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
-    }
-    // P is wave-private: this wave's LDS writes are done before its reads below
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
-      const bf16x8 pal = mfma_a8(&sm.pl[w][lr][32 * kc + 8 * lg]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 vb = mfma_a8(&sm.vt[16 * dt + lr][32 * kc + 8 * lg]);
-        o[dt] = mfma_bf16(pah, vb, o[dt]);
-        o[dt] = mfma_bf16(pal, vb, o[dt]);
-      }
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int qi = q0 + 16 * w + 4 * lg + v;
-    if (qi >= a.S) continue;
-    const float inv = 1.f / l[v];
-    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
-    if (a.out_f32) {
-      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
-    }
-    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
-  }
-}
-
 // ---- backward on bf16 MFMA: staging helpers (64-row blocks, 256 threads)
 // Write a 4-row x 8-column bf16 micro-tile transposed: dst[c][r0 .. r0+4] for
 // its 8 columns c (two v_perm per column pair).
@@ -473,6 +300,151 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const uint
     put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
   }
 }
+// ---- operands prepared once per attention call
+// Every key/query block of 64 rows is staged by many workgroups (one per
+// query/key block after it), so the rotation, the hi/lo split and the
+// transposes run once per call in the prep kernels below and the attention
+// kernels stage plain copies.  Layouts, bf16, rows padded with zeros to Sp, a
+// multiple of 64: rows [b][head][Sp][HD], transposed [b][head][HD][Sp].
+struct PrepPtrs {
+  uint16_t *kh, *kl, *vt;               // forward and backward
+  uint16_t *kht, *klt, *qh, *ql, *qht, *qlt, *ot;   // backward only
+  int Sp;
+};
+PrepPtrs prep_ptrs(uint16_t* base, int B, int S, int nh, int nkv, int hd, bool bwd) {
+  PrepPtrs p{};
+  p.Sp = (S + AT - 1) / AT * AT;
+  const int64_t ekv = (int64_t)B * nkv * p.Sp * hd, eq = (int64_t)B * nh * p.Sp * hd;
+  uint16_t* c = base;
+  auto take = [&](int64_t n) {
+    uint16_t* r = base ? c : nullptr;
+    c += n;
+    return r;
+  };
+  p.kh = take(ekv);
+  p.kl = take(ekv);
+  p.vt = take(ekv);
+  if (bwd) {
+    p.kht = take(ekv);
+    p.klt = take(ekv);
+    p.qh = take(eq);
+    p.ql = take(eq);
+    p.qht = take(eq);
+    p.qlt = take(eq);
+    p.ot = take(eq);
+  }
+  return p;
+}
+
+// One thread's share of a 64 x HD (or HD x 64) bf16 tile: the staging loads of
+// a block are all issued into registers before any is stored to LDS, so a
+// block costs one memory round trip, and the kernels issue the next block's
+// loads before the current block's MFMAs (register prefetch; the last block's
+// prefetch is clamped to a block in range and never stored).
+template <int HD>
+struct Chunks {
+  static constexpr int N = AT * HD / 8 / 256;
+  uint4 v[N];
+};
+// f(integral_constant<int, I>) for I = 0 .. N-1, with the index a constant from
+// the start (so the register arrays indexed by it never need memory).
+template <typename F, int... I>
+__device__ __forceinline__ void each_chunk(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void each_chunk(F&& f) {
+  each_chunk(f, std::make_integer_sequence<int, N>{});
+}
+// A tile of ROWS rows x COLS bf16 from rows of pitch ld (rows at or past n read
+// as zero) into registers, and out to an LDS tile with rows of COLS + 8.
+template <int ROWS, int COLS>
+__device__ __forceinline__ void ld_tile(Chunks<ROWS * COLS / AT>& c, const uint16_t* __restrict__ src, int64_t ld,
+                                        int n) {
+  each_chunk<Chunks<ROWS * COLS / AT>::N>([&](auto i) __attribute__((always_inline)) {
+    const int e = threadIdx.x + 256 * i.value, r = e / (COLS / 8), k = (e % (COLS / 8)) * 8;
+    c.v[i.value] = r < n ? *reinterpret_cast<const uint4*>(src + r * ld + k) : make_uint4(0u, 0u, 0u, 0u);
+  });
+}
+template <int ROWS, int COLS>
+__device__ __forceinline__ void st_tile(uint16_t (*dst)[COLS + 8], const Chunks<ROWS * COLS / AT>& c) {
+  each_chunk<Chunks<ROWS * COLS / AT>::N>([&](auto i) __attribute__((always_inline)) {
+    const int e = threadIdx.x + 256 * i.value, r = e / (COLS / 8), k = (e % (COLS / 8)) * 8;
+    *reinterpret_cast<uint4*>(&dst[r][k]) = c.v[i.value];
+  });
+}
+template <int HD>
+__device__ __forceinline__ void ld_rows(Chunks<HD>& c, const uint16_t* __restrict__ src, int64_t ld, int n) {
+  ld_tile<AT, HD>(c, src, ld, n);
+}
+template <int HD>
+__device__ __forceinline__ void st_rows(uint16_t (*dst)[HD + 8], const Chunks<HD>& c) {
+  st_tile<AT, HD>(dst, c);
+}
+template <int HD>
+__device__ __forceinline__ void ld_cols(Chunks<HD>& c, const uint16_t* __restrict__ src, int Sp) {
+  ld_tile<HD, AT>(c, src, Sp, HD);
+}
+template <int HD>
+__device__ __forceinline__ void st_cols(uint16_t (*dst)[AT + 8], const Chunks<HD>& c) {
+  st_tile<HD, AT>(dst, c);
+}
+// [64][HD] and [HD][64] LDS tiles out to the prepared layouts.
+template <int HD>
+__device__ __forceinline__ void put_rows(uint16_t* __restrict__ dst, const uint16_t (*src)[HD + 8]) {
+  for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
+    const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
+    *reinterpret_cast<uint4*>(dst + r * HD + c) = *reinterpret_cast<const uint4*>(&src[r][c]);
+  }
+}
+template <int HD>
+__device__ __forceinline__ void put_cols(uint16_t* __restrict__ dst, const uint16_t (*src)[AT + 8], int Sp) {
+  for (int e = threadIdx.x; e < HD * AT / 8; e += 256) {
+    const int d = e / (AT / 8), c = (e % (AT / 8)) * 8;
+    *reinterpret_cast<uint4*>(dst + (int64_t)d * Sp + c) = *reinterpret_cast<const uint4*>(&src[d][c]);
+  }
+}
+
+template <int HD>
+struct PrepRotSmem {
+  uint16_t h[AT][HD + 8], l[AT][HD + 8];
+  uint16_t t[HD][AT + 8];
+};
+// Heads [col0, col0 + nheads) of the qkv rows (head columns of width HD),
+// rows [64 blockIdx.x, + 64) of batch blockIdx.z, head blockIdx.y: rotated in
+// float32 and split into hi/lo rows; with hiT, also transposed.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_prep_rot_kernel(const uint16_t* __restrict__ qkv, int64_t ld, int S, int Sp,
+                                                           int col0, int nheads, const float2* __restrict__ rope,
+                                                           uint16_t* hi, uint16_t* lo, uint16_t* hiT, uint16_t* loT) {
+  __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
+  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
+  const uint16_t* src = qkv + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
+  stage_rot<HD>(sm.h, sm.l, src, ld, row0, S - row0, rope);
+  __syncthreads();
+  const int64_t hb = (int64_t)b * nheads + hh;
+  put_rows<HD>(hi + (hb * Sp + row0) * HD, sm.h);
+  put_rows<HD>(lo + (hb * Sp + row0) * HD, sm.l);
+  if (!hiT) return;
+  lds_transpose<HD>(sm.t, sm.h);
+  __syncthreads();
+  put_cols<HD>(hiT + hb * HD * Sp + row0, sm.t, Sp);
+  __syncthreads();
+  lds_transpose<HD>(sm.t, sm.l);
+  __syncthreads();
+  put_cols<HD>(loT + hb * HD * Sp + row0, sm.t, Sp);
+}
+// The same blocks of a plain bf16 operand (V, dO), transposed.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_prep_t_kernel(const uint16_t* __restrict__ src, int64_t ld, int S, int Sp,
+                                                         int col0, int nheads, uint16_t* dstT) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[HD][AT + 8];
+  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
+  stage_rows_t<HD>(t, src + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD, ld, row0, S - row0);
+  __syncthreads();
+  put_cols<HD>(dstT + ((int64_t)b * nheads + hh) * HD * Sp + row0, t, Sp);
+}
+
 // One lane's rotated row slices as MFMA A operands (hi/lo), d slices 32c + 8 lg.
 template <int HD>
 __device__ __forceinline__ void load_rot_frags(const uint16_t* row, bool ok, int pos, const float2* __restrict__ rope,
@@ -503,6 +475,150 @@ __device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, float x) {
 }
 
 template <int HD>
+struct AttnF16Smem {
+  uint16_t kh[AT][HD + 8];     // rotated K, bf16 hi  [key][d]
+  uint16_t kl[AT][HD + 8];     // rotated K, bf16 lo
+  uint16_t vt[HD][AT + 8];     // V transposed [d][key]
+  uint16_t ph[4][16][AT + 8];  // per-wave P hi [query][key]
+  uint16_t pl[4][16][AT + 8];  // per-wave P lo
+};
+
+// Forward: one workgroup per (query block of 64, head, batch), the heaviest
+// query blocks first; wave w owns queries 16w .. 16w+15 and keeps its rotated q
+// as MFMA operands in registers.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs pp) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnF16Smem<HD>& sm = *reinterpret_cast<AttnF16Smem<HD>*>(smem_raw);
+  constexpr int DC = HD / 32, DT = HD / 16, HALF = HD / 2;
+  const int nqb = gridDim.x;
+  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (a.nh / a.nkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q0 = qb * AT;
+  const int64_t rowbase = (int64_t)b * a.S;
+  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
+  const int64_t kvh = (int64_t)b * a.nkv + g;
+  const uint16_t* Kh = pp.kh + kvh * pp.Sp * HD;
+  const uint16_t* Kl = pp.kl + kvh * pp.Sp * HD;
+  const uint16_t* Vt = pp.vt + kvh * HD * pp.Sp;
+  // this lane's query row, its 8-wide d slices 32c + 8 lg .. +8, rotated and split
+  bf16x8 qh[DC], ql[DC];
+  {
+    const int qi = q0 + 16 * w + lr;
+    const bool ok = qi < a.S;
+    const uint16_t* row = Q + (int64_t)qi * a.ld;
+#pragma unroll
+    for (int c = 0; c < DC / 2; ++c) {
+      const int i0 = 32 * c + 8 * lg;
+      float x1[8], x2[8];
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
+      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+      if (ok) rope8(x1, x2, a.rope + (int64_t)qi * HALF + i0);
+      split8(x1, qh[c], ql[c]);
+      split8(x2, qh[c + DC / 2], ql[c + DC / 2]);
+    }
+  }
+  const float sc = a.scale * kLog2e;
+  float m[4], l[4];
+  f32x4 o[DT];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Chunks<HD> ckh, ckl, cvt;
+  ld_rows<HD>(ckh, Kh, HD, AT);
+  ld_rows<HD>(ckl, Kl, HD, AT);
+  ld_cols<HD>(cvt, Vt, pp.Sp);
+  for (int kb = 0; kb <= qb; ++kb) {
+    const int k0 = kb * AT;
+    __syncthreads();   // the previous block's kh/kl/vt reads are done
+    st_rows<HD>(sm.kh, ckh);
+    st_rows<HD>(sm.kl, ckl);
+    st_cols<HD>(sm.vt, cvt);
+    __syncthreads();
+    {
+      const int kn = min(kb + 1, qb) * AT;
+      ld_rows<HD>(ckh, Kh + (int64_t)kn * HD, HD, AT);
+      ld_rows<HD>(ckl, Kl + (int64_t)kn * HD, HD, AT);
+      ld_cols<HD>(cvt, Vt + kn, pp.Sp);
+    }
+    f32x4 st[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      st[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
+        const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
+        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
+        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
+        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = q0 + 16 * w + 4 * lg + v;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int kj = k0 + 16 * jt + lr;
+        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
+        mx = fmaxf(mx, st[jt][v]);
+      }
+      mx = group16_max(mx);
+      const float mn = fmaxf(m[v], mx);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
+        const uint16_t ph = f32_to_bf16_bits(pv);
+        sm.ph[w][4 * lg + v][16 * jt + lr] = ph;
+        sm.pl[w][4 * lg + v][16 * jt + lr] = f32_to_bf16_bits(pv - bf16_bits_to_f32(ph));
+        rs += pv;
+      }
+      rs = group16_sum(rs);
+      l[v] = l[v] * alpha + rs;
+      m[v] = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
+    }
+    // P is wave-private: this wave's LDS writes are done before its reads below
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
+      const bf16x8 pal = mfma_a8(&sm.pl[w][lr][32 * kc + 8 * lg]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vb = mfma_a8(&sm.vt[16 * dt + lr][32 * kc + 8 * lg]);
+        o[dt] = mfma_bf16(pah, vb, o[dt]);
+        o[dt] = mfma_bf16(pal, vb, o[dt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int qi = q0 + 16 * w + 4 * lg + v;
+    if (qi >= a.S) continue;
+    const float inv = 1.f / l[v];
+    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
+    if (a.out_f32) {
+      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
+    }
+    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
+  }
+}
+
+template <int HD>
 struct AttnDqSmem {
   uint16_t kh[AT][HD + 8], kl[AT][HD + 8];   // rotated K [key][d]
   uint16_t th[HD][AT + 8], tl[HD][AT + 8];   // the same transposed [d][key]
@@ -512,7 +628,7 @@ struct AttnDqSmem {
 
 // dQ for one query block of one head; wave w owns queries 16w .. 16w+15.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) attn_bwd_dq_bf16_kernel(AttnBwdArgs a, PrepPtrs pp) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnDqSmem<HD>& sm = *reinterpret_cast<AttnDqSmem<HD>*>(smem_raw);
   constexpr int DC = HD / 32, DT = HD / 16;
@@ -524,8 +640,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(AttnBwdArgs a) {
   const int q0 = qb * AT;
   const int64_t rowbase = (int64_t)b * a.S;
   const float sc = a.scale * kLog2e;
-  const uint16_t* Kp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + g) * HD;
   const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
+  const int64_t kvh = (int64_t)b * a.nkv + g;
+  const uint16_t* Kh = pp.kh + kvh * pp.Sp * HD;
+  const uint16_t* Kl = pp.kl + kvh * pp.Sp * HD;
+  const uint16_t* Kht = pp.kht + kvh * HD * pp.Sp;
+  const uint16_t* Klt = pp.klt + kvh * HD * pp.Sp;
   bf16x8 qh[DC], ql[DC], od[DC];
   {
     const int qi = q0 + 16 * w + lr;
@@ -544,15 +664,32 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(AttnBwdArgs a) {
   f32x4 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // kh, kl and v of the next block are prefetched across this block's MFMAs;
+  // the transposed tiles are loaded as a block begins (in flight during its barrier)
+  Chunks<HD> ckh, ckl, cv;
+  ld_rows<HD>(ckh, Kh, HD, AT);
+  ld_rows<HD>(ckl, Kl, HD, AT);
+  ld_rows<HD>(cv, Vp, a.ld, a.S);
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * AT;
-    const int nk = min(AT, a.S - k0);
+    {
+      Chunks<HD> cth, ctl;
+      ld_cols<HD>(cth, Kht + k0, pp.Sp);
+      ld_cols<HD>(ctl, Klt + k0, pp.Sp);
+      __syncthreads();
+      st_rows<HD>(sm.kh, ckh);
+      st_rows<HD>(sm.kl, ckl);
+      st_rows<HD>(sm.v, cv);
+      st_cols<HD>(sm.th, cth);
+      st_cols<HD>(sm.tl, ctl);
+    }
     __syncthreads();
-    stage_rot<HD>(sm.kh, sm.kl, Kp, a.ld, k0, nk, a.rope);
-    stage_rows<HD>(sm.v, Vp, a.ld, k0, nk);
-    __syncthreads();
-    lds_transpose<HD>(sm.th, sm.kh);
-    lds_transpose<HD>(sm.tl, sm.kl);
+    {
+      const int kn = min(kb + 1, qb) * AT;
+      ld_rows<HD>(ckh, Kh + (int64_t)kn * HD, HD, AT);
+      ld_rows<HD>(ckl, Kl + (int64_t)kn * HD, HD, AT);
+      ld_rows<HD>(cv, Vp + (int64_t)kn * a.ld, a.ld, a.S - kn);
+    }
     f32x4 st[4], dpt[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -580,7 +717,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(AttnBwdArgs a) {
                  pv * (dpt[jt][v] - dd_r[v]));
       }
     }
-    __syncthreads();   // the transposed K tiles are complete
+    // dS is wave-private: this wave's LDS writes are done before its reads below
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const bf16x8 dh = mfma_a8(&sm.sh[w][lr][32 * kc + 8 * lg]);
@@ -628,7 +765,7 @@ struct AttnDkdvSmem {
 // head order by attn_dkdv_reduce_kernel).  Wave w owns keys 16w .. 16w+15;
 // scores are formed transposed (S^T = K Q^T) so P^T and dS^T come out key-major.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a, PrepPtrs pp) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnDkdvSmem<HD>& sm = *reinterpret_cast<AttnDkdvSmem<HD>*>(smem_raw);
   constexpr int DC = HD / 32, DT = HD / 16;
@@ -650,23 +787,52 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a) 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nqb = (a.S + AT - 1) / AT;
-  const uint16_t* Qp = a.qkv + rowbase * a.ld + (int64_t)h * HD;
+  const int64_t qh_ = (int64_t)b * a.nh + h;
+  const uint16_t* Qh = pp.qh + qh_ * pp.Sp * HD;
+  const uint16_t* Ql = pp.ql + qh_ * pp.Sp * HD;
+  const uint16_t* Qht = pp.qht + qh_ * HD * pp.Sp;
+  const uint16_t* Qlt = pp.qlt + qh_ * HD * pp.Sp;
+  const uint16_t* Ot = pp.ot + qh_ * HD * pp.Sp;
   const uint16_t* Op = a.dO + rowbase * a.ldo + (int64_t)h * HD;
+  Chunks<HD> cqh, cql, co;
+  float clse = 0.f, cdd = 0.f;
+  // the blocks' loads, as a macro so that the register arrays stay plain locals
+  // qh, ql, dO and the row statistics of the next block are prefetched across
+  // this block's MFMAs; the transposed tiles are loaded as a block begins
+#define LSQ_DKDV_LOAD(q0)                                                      \
+  do {                                                                         \
+    ld_rows<HD>(cqh, Qh + (int64_t)(q0) * HD, HD, AT);                         \
+    ld_rows<HD>(cql, Ql + (int64_t)(q0) * HD, HD, AT);                         \
+    ld_rows<HD>(co, Op + (int64_t)(q0) * a.ldo, a.ldo, a.S - (q0));            \
+    const bool ok_ = tid < AT && (q0) + tid < a.S;                             \
+    clse = ok_ ? a.lse[((int64_t)b * a.nh + h) * a.S + (q0) + tid] : 0.f;      \
+    cdd = ok_ ? a.D[(rowbase + (q0) + tid) * a.nh + h] : 0.f;                  \
+  } while (0)
+  LSQ_DKDV_LOAD(kb * AT);
   for (int qb = kb; qb < nqb; ++qb) {
     const int q0 = qb * AT;
-    const int nq = min(AT, a.S - q0);
-    __syncthreads();
-    stage_rot<HD>(sm.qh, sm.ql, Qp, a.ld, q0, nq, a.rope);
-    stage_rows<HD>(sm.o, Op, a.ldo, q0, nq);
-    stage_rows_t<HD>(sm.ot, Op, a.ldo, q0, nq);
-    if (tid < AT) {
-      const bool ok = tid < nq;
-      sm.lse[tid] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + q0 + tid] : 0.f;
-      sm.dd[tid] = ok ? a.D[(rowbase + q0 + tid) * a.nh + h] : 0.f;
+    {
+      Chunks<HD> cot, cth, ctl;
+      ld_cols<HD>(cot, Ot + q0, pp.Sp);
+      ld_cols<HD>(cth, Qht + q0, pp.Sp);
+      ld_cols<HD>(ctl, Qlt + q0, pp.Sp);
+      __syncthreads();
+      st_rows<HD>(sm.qh, cqh);
+      st_rows<HD>(sm.ql, cql);
+      st_rows<HD>(sm.o, co);
+      st_cols<HD>(sm.ot, cot);
+      st_cols<HD>(sm.th, cth);
+      st_cols<HD>(sm.tl, ctl);
+      if (tid < AT) {
+        sm.lse[tid] = clse;
+        sm.dd[tid] = cdd;
+      }
     }
     __syncthreads();
-    lds_transpose<HD>(sm.th, sm.qh);
-    lds_transpose<HD>(sm.tl, sm.ql);
+    {
+      const int qn = min(qb + 1, nqb - 1) * AT;
+      LSQ_DKDV_LOAD(qn);
+    }
     f32x4 st[4], dpt[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -695,7 +861,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a) 
                  pv * (dpt[jt][v] - sm.dd[16 * jt + lr]));
       }
     }
-    __syncthreads();   // the transposed Q tile is complete
+    // P^T and dS^T are wave-private: this wave's LDS writes are done before its reads below
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
@@ -727,6 +893,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(AttnBwdArgs a) 
     }
   }
 }
+#undef LSQ_DKDV_LOAD
 
 // D[t][h] = sum_d dO[t, h, d] * O[t, h, d], with the float32 O of the forward:
 // D must equal sum_j P_j dP_j, and a rounded O breaks that identity exactly
@@ -992,6 +1159,22 @@ int allow_smem(K* kernel, size_t bytes) {
   return LSQ_OK;
 }
 
+size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd) {
+  const PrepPtrs p = prep_ptrs(nullptr, B, S, nh, nkv, hd, bwd);
+  const int64_t ekv = (int64_t)B * nkv * p.Sp * hd, eq = (int64_t)B * nh * p.Sp * hd;
+  return (size_t)(2 * (bwd ? 5 * ekv + 5 * eq : 3 * ekv));
+}
+
+// K rotated and split (and, for the backward, transposed) and V^T.
+template <int HD>
+void launch_prep_kv(const uint16_t* qkv, int64_t ld, int B, int S, int nh, int nkv, const float2* rope,
+                    const PrepPtrs& p, bool bwd, hipStream_t s) {
+  const dim3 grid(p.Sp / AT, nkv, B);
+  attn_prep_rot_kernel<HD><<<grid, 256, 0, s>>>(qkv, ld, S, p.Sp, nh, nkv, rope, p.kh, p.kl, bwd ? p.kht : nullptr,
+                                                bwd ? p.klt : nullptr);
+  if (!bwd) attn_prep_t_kernel<HD><<<grid, 256, 0, s>>>(qkv, ld, S, p.Sp, nh + nkv, nkv, p.vt);
+}
+
 int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   LSQ_CHECK(a.hd == 64 || a.hd == 128, LSQ_ERR_SHAPE, "attention: head_dim %d unsupported (64 or 128)", a.hd);
   LSQ_CHECK(a.nkv > 0 && a.nh % a.nkv == 0, LSQ_ERR_SHAPE, "attention: n_heads %% n_kv_heads != 0");
@@ -1001,13 +1184,18 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
     return e ? e : allow_smem(attn_fwd_bf16_kernel<64>, sizeof(AttnF16Smem<64>));
   }();
   if (init) return init;
+  LSQ_CHECK(a.prep, LSQ_ERR_WORKSPACE, "attention_fwd: prepared-operand workspace missing");
+  const PrepPtrs pp = prep_ptrs(a.prep, B, a.S, a.nh, a.nkv, a.hd, false);
   dim3 grid((a.S + AT - 1) / AT, a.nh, B);
   const double flops = 2.0 * 2.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
   int tok = prof_begin(s);
-  if (a.hd == 128)
-    attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a);
-  else
-    attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a);
+  if (a.hd == 128) {
+    launch_prep_kv<128>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, false, s);
+    attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a, pp);
+  } else {
+    launch_prep_kv<64>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, false, s);
+    attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a, pp);
+  }
   prof_end(tok, s, PROF_ATTN, flops, 0.0);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
@@ -1030,14 +1218,22 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   attn_dot_kernel<<<(unsigned)(((int64_t)T * a.nh + 3) / 4), 256, 0, s>>>(a.dO, a.O_f32, a.ldo, T, a.nh, a.hd, D);
   AttnBwdArgs b = a;
   b.D = D;
-  LSQ_CHECK(a.dk_part && a.dv_part, LSQ_ERR_WORKSPACE, "attention_bwd: partial buffers missing");
+  LSQ_CHECK(a.dk_part && a.dv_part && a.prep, LSQ_ERR_WORKSPACE, "attention_bwd: workspace buffers missing");
+  const PrepPtrs pp = prep_ptrs(a.prep, B, a.S, a.nh, a.nkv, a.hd, true);
   dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
+  const dim3 gq(pp.Sp / AT, a.nh, B);
   if (a.hd == 128) {
-    attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b);
-    attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b);
+    launch_prep_kv<128>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, true, s);
+    attn_prep_rot_kernel<128><<<gq, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.rope, pp.qh, pp.ql, pp.qht, pp.qlt);
+    attn_prep_t_kernel<128><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b, pp);
+    attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b, pp);
   } else {
-    attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b);
-    attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b);
+    launch_prep_kv<64>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, true, s);
+    attn_prep_rot_kernel<64><<<gq, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.rope, pp.qh, pp.ql, pp.qht, pp.qlt);
+    attn_prep_t_kernel<64><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b, pp);
+    attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b, pp);
   }
   const int64_t nred = (int64_t)B * a.S * a.nkv * (a.hd / 2);
   attn_dkdv_reduce_kernel<<<(unsigned)((nred + 255) / 256), 256, 0, s>>>(b, B);

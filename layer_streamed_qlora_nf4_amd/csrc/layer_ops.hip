@@ -666,29 +666,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // kh, kl and v of the next block are prefetched across this block's MFMAs;
   // the transposed tiles are loaded as a block begins (in flight during its barrier)
-  Chunks<HD> ckh, ckl, cv;
+  Chunks<HD> ckh, ckl, cv, cth, ctl;
   ld_rows<HD>(ckh, Kh, HD, AT);
   ld_rows<HD>(ckl, Kl, HD, AT);
   ld_rows<HD>(cv, Vp, a.ld, a.S);
+  ld_cols<HD>(cth, Kht, pp.Sp);
+  ld_cols<HD>(ctl, Klt, pp.Sp);
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * AT;
-    {
-      Chunks<HD> cth, ctl;
-      ld_cols<HD>(cth, Kht + k0, pp.Sp);
-      ld_cols<HD>(ctl, Klt + k0, pp.Sp);
-      __syncthreads();
-      st_rows<HD>(sm.kh, ckh);
-      st_rows<HD>(sm.kl, ckl);
-      st_rows<HD>(sm.v, cv);
-      st_cols<HD>(sm.th, cth);
-      st_cols<HD>(sm.tl, ctl);
-    }
+    __syncthreads();
+    st_rows<HD>(sm.kh, ckh);
+    st_rows<HD>(sm.kl, ckl);
+    st_rows<HD>(sm.v, cv);
+    st_cols<HD>(sm.th, cth);
+    st_cols<HD>(sm.tl, ctl);
     __syncthreads();
     {
       const int kn = min(kb + 1, qb) * AT;
       ld_rows<HD>(ckh, Kh + (int64_t)kn * HD, HD, AT);
       ld_rows<HD>(ckl, Kl + (int64_t)kn * HD, HD, AT);
       ld_rows<HD>(cv, Vp + (int64_t)kn * a.ld, a.ld, a.S - kn);
+      ld_cols<HD>(cth, Kht + kn, pp.Sp);
+      ld_cols<HD>(ctl, Klt + kn, pp.Sp);
     }
     f32x4 st[4], dpt[4];
 #pragma unroll
@@ -794,7 +793,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* Qlt = pp.qlt + qh_ * HD * pp.Sp;
   const uint16_t* Ot = pp.ot + qh_ * HD * pp.Sp;
   const uint16_t* Op = a.dO + rowbase * a.ldo + (int64_t)h * HD;
-  Chunks<HD> cqh, cql, co;
+  Chunks<HD> cqh, cql, co, cot, cth, ctl;
   float clse = 0.f, cdd = 0.f;
   // the blocks' loads, as a macro so that the register arrays stay plain locals
   // qh, ql, dO and the row statistics of the next block are prefetched across
@@ -804,6 +803,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     ld_rows<HD>(cqh, Qh + (int64_t)(q0) * HD, HD, AT);                         \
     ld_rows<HD>(cql, Ql + (int64_t)(q0) * HD, HD, AT);                         \
     ld_rows<HD>(co, Op + (int64_t)(q0) * a.ldo, a.ldo, a.S - (q0));            \
+    ld_cols<HD>(cot, Ot + (q0), pp.Sp);                                        \
+    ld_cols<HD>(cth, Qht + (q0), pp.Sp);                                       \
+    ld_cols<HD>(ctl, Qlt + (q0), pp.Sp);                                       \
     const bool ok_ = tid < AT && (q0) + tid < a.S;                             \
     clse = ok_ ? a.lse[((int64_t)b * a.nh + h) * a.S + (q0) + tid] : 0.f;      \
     cdd = ok_ ? a.D[(rowbase + (q0) + tid) * a.nh + h] : 0.f;                  \
@@ -811,22 +813,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   LSQ_DKDV_LOAD(kb * AT);
   for (int qb = kb; qb < nqb; ++qb) {
     const int q0 = qb * AT;
-    {
-      Chunks<HD> cot, cth, ctl;
-      ld_cols<HD>(cot, Ot + q0, pp.Sp);
-      ld_cols<HD>(cth, Qht + q0, pp.Sp);
-      ld_cols<HD>(ctl, Qlt + q0, pp.Sp);
-      __syncthreads();
-      st_rows<HD>(sm.qh, cqh);
-      st_rows<HD>(sm.ql, cql);
-      st_rows<HD>(sm.o, co);
-      st_cols<HD>(sm.ot, cot);
-      st_cols<HD>(sm.th, cth);
-      st_cols<HD>(sm.tl, ctl);
-      if (tid < AT) {
-        sm.lse[tid] = clse;
-        sm.dd[tid] = cdd;
-      }
+    __syncthreads();
+    st_rows<HD>(sm.qh, cqh);
+    st_rows<HD>(sm.ql, cql);
+    st_rows<HD>(sm.o, co);
+    st_cols<HD>(sm.ot, cot);
+    st_cols<HD>(sm.th, cth);
+    st_cols<HD>(sm.tl, ctl);
+    if (tid < AT) {
+      sm.lse[tid] = clse;
+      sm.dd[tid] = cdd;
     }
     __syncthreads();
     {

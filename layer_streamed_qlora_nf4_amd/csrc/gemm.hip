@@ -910,15 +910,17 @@ __global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __r
   f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
   const int row = m0 + (lane & 15);
   const int g = lane >> 4;
-#pragma unroll 4
-  for (int k = kb; k < ke; k += 32) {
-    const int kk = k + 8 * g;
-    uint4 av = (row < M && kk < K) ? *reinterpret_cast<const uint4*>(X + (int64_t)row * ldx + kk) : make_uint4(0, 0, 0, 0);
+  // four 32-wide steps per wave; steps past this wave's range read zeros
+#pragma unroll
+  for (int i = 0; i < KCHUNK / 4 / 32; ++i) {
+    const int kk = kb + 32 * i + 8 * g;
+    const bool kin = kk < ke;
+    uint4 av = (row < M && kin) ? *reinterpret_cast<const uint4*>(X + (int64_t)row * ldx + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
       const int c = ct * 16 + (lane & 15);
-      uint4 bv = (c < rr && kk < K) ? *reinterpret_cast<const uint4*>(A + (int64_t)c * K + kk) : make_uint4(0, 0, 0, 0);
+      uint4 bv = (c < rr && kin) ? *reinterpret_cast<const uint4*>(A + (int64_t)c * K + kk) : make_uint4(0, 0, 0, 0);
       acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
     }
   }
@@ -976,15 +978,16 @@ __global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __rest
   const int cb = ch.begin[chunk], ce = ch.end[chunk];
   const int kb = cb + wave * (KCHUNK / 4), ke = min(ce, kb + KCHUNK / 4);
   f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-#pragma unroll 4
-  for (int k = kb; k < ke; k += 32) {
-    const int kk = k + 8 * g;
-    uint4 av = (row < M && kk < ce) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < KCHUNK / 4 / 32; ++i) {
+    const int kk = kb + 32 * i + 8 * g;
+    const bool kin = kk < ke;
+    uint4 av = (row < M && kin) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
       const int c = ct * 16 + (lane & 15);
-      uint4 bv = (c < r && kk < ce) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
+      uint4 bv = (c < r && kin) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
       acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
     }
   }

@@ -18,10 +18,34 @@
 namespace lsq {
 namespace {
 
+// Reductions over the 16 lanes of a DPP row (lanes 16 g .. 16 g + 15): the
+// value rotated within the row by 8, 4, 2 and 1 lanes (DPP row_ror, a VALU
+// operand modifier, no LDS round trip).  At each step lane i and the lane it
+// reads hold the same two partial sums, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kRowRor2 = 0x122, kRowRor1 = 0x121;
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, dpp_row<kRowRor8>(v));
+  v = fmaxf(v, dpp_row<kRowRor4>(v));
+  v = fmaxf(v, dpp_row<kRowRor2>(v));
+  return fmaxf(v, dpp_row<kRowRor1>(v));
+}
+__device__ __forceinline__ float group16_sum(float v) {
+  v += dpp_row<kRowRor8>(v);
+  v += dpp_row<kRowRor4>(v);
+  v += dpp_row<kRowRor2>(v);
+  return v + dpp_row<kRowRor1>(v);
+}
+
+// Sum over the wave: within each 16-lane row by DPP, then across the four
+// rows by two lane swaps (every lane ends with the same bits).
 __device__ __forceinline__ float warp_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = group16_sum(v);
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
 }
 
 // ------------------------------------------------------------------ RMSNorm
@@ -171,17 +195,6 @@ __global__ void rope_kernel(uint16_t* __restrict__ buf, int64_t ld, int T, int S
 // scores are kept in base 2: s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
 constexpr int AT = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // ------------------------------------------------ attention on bf16 MFMA
 // The float32 operands (rotated q and k, the probabilities P) enter the bf16

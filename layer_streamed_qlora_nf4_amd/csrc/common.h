@@ -69,4 +69,9 @@ bool prof_on();
 // Returns an opaque token; prof_end credits flops/bytes to the family.
 int prof_begin(hipStream_t s);
 void prof_end(int token, hipStream_t s, ProfKind kind, double flops, double bytes);
+// For one kernel launched with hipExtLaunchKernelGGL: the pair's events are
+// handed out unrecorded (null when timing is off) and the launch attaches them
+// to its dispatch, so they time the kernel's own execution.
+int prof_begin_kernel(hipEvent_t* start, hipEvent_t* stop);
+void prof_end_kernel(int token, ProfKind kind, double flops, double bytes);
 }  // namespace lsq

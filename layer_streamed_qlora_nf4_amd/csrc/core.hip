@@ -70,6 +70,26 @@ void prof_end(int token, hipStream_t s, ProfKind kind, double flops, double byte
   g_prof.rec[token] = ProfRec{kind, flops, bytes};
 }
 
+int prof_begin_kernel(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (!g_prof.on) return -1;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (g_prof.used >= kPoolPairs) {
+    ++g_prof.dropped;
+    return -1;
+  }
+  const int t = g_prof.used++;
+  *start = g_prof.ev[2 * t];
+  *stop = g_prof.ev[2 * t + 1];
+  return t;
+}
+
+void prof_end_kernel(int token, ProfKind kind, double flops, double bytes) {
+  if (token < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.rec[token] = ProfRec{kind, flops, bytes};
+}
+
 }  // namespace lsq
 
 extern "C" {

@@ -16,6 +16,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "gemm.h"
 #include "nf4_levels.h"
@@ -1406,22 +1408,27 @@ bool bwd_dma_ok(const BwdParams& p) {
 
 // The NF4 kernels take activations by DMA when their operands fit 32-bit
 // offsets; bf16 weights (and larger operands) use the register-path kernels.
+// e0, e1: the timing events attached to the dispatch (null when timing is off).
 template <int WK, int EPI>
-void launch_fwd(const FwdParams& p, hipStream_t s) {
+void launch_fwd(const FwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + p.bn - 1) / p.bn);
-  const dim3 grid(tiles, p.splits);
-  if (WK != LSQ_W_NF4 || !fwd_dma_ok(p)) gemm_fwd_pp_kernel<WK, EPI><<<grid, 512, 0, s>>>(p);
-  else if (p.bn == 192) gemm_fwd_nf4_dma_kernel<EPI, 192><<<grid, 512, 0, s>>>(p);
-  else gemm_fwd_nf4_dma_kernel<EPI, 256><<<grid, 512, 0, s>>>(p);
+  const dim3 grid(tiles, p.splits), block(512);
+  if (WK != LSQ_W_NF4 || !fwd_dma_ok(p))
+    hipExtLaunchKernelGGL(gemm_fwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
+  else if (p.bn == 192)
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 192>, grid, block, 0, s, e0, e1, 0, p);
+  else
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 256>, grid, block, 0, s, e0, e1, 0, p);
 }
 
 template <int WK, int EPI>
-void launch_bwd(const BwdParams& p, hipStream_t s) {
+void launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((p.M + kTile - 1) / kTile) * ((p.K + kTile - 1) / kTile);
+  const dim3 grid(tiles, p.splits), block(512);
   if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
-    gemm_bwd_nf4_dma_kernel<EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+    hipExtLaunchKernelGGL(gemm_bwd_nf4_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
   else
-    gemm_bwd_pp_kernel<WK, EPI><<<dim3(tiles, p.splits), 512, 0, s>>>(p);
+    hipExtLaunchKernelGGL(gemm_bwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
 }
 
 void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* bias, const float* resid, void* out,
@@ -1462,17 +1469,17 @@ int choose_splits(int tiles, int ksteps, double out_elems) {
 }
 
 template <int WK>
-void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_fwd<WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_fwd<WK, EPI_F32>(p, s);
-  else launch_fwd<WK, EPI_F32_RESID>(p, s);
+void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (epi == EPI_BF16) launch_fwd<WK, EPI_BF16>(p, s, e0, e1);
+  else if (epi == EPI_F32) launch_fwd<WK, EPI_F32>(p, s, e0, e1);
+  else launch_fwd<WK, EPI_F32_RESID>(p, s, e0, e1);
 }
 
 template <int WK>
-void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s) {
-  if (epi == EPI_BF16) launch_bwd<WK, EPI_BF16>(p, s);
-  else if (epi == EPI_F32) launch_bwd<WK, EPI_F32>(p, s);
-  else launch_bwd<WK, EPI_F32_RESID>(p, s);
+void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (epi == EPI_BF16) launch_bwd<WK, EPI_BF16>(p, s, e0, e1);
+  else if (epi == EPI_F32) launch_bwd<WK, EPI_F32>(p, s, e0, e1);
+  else launch_bwd<WK, EPI_F32_RESID>(p, s, e0, e1);
 }
 
 }  // namespace
@@ -1523,11 +1530,13 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.N * p.r;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
-  // The profiler brackets the tile kernel alone; a split-K reduction is credited separately.
-  int tok = prof_begin(s);
-  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_W_NF4>(p, epi, s);
-  else dispatch_fwd_epi<LSQ_W_BF16>(p, epi, s);
-  prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_FWD : PROF_GEMM_BF16, flops, bytes);
+  // The profiler times the tile kernel alone (events on its dispatch); a split-K
+  // reduction is credited separately.
+  hipEvent_t e0, e1;
+  int tok = prof_begin_kernel(&e0, &e1);
+  if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_W_NF4>(p, epi, s, e0, e1);
+  else dispatch_fwd_epi<LSQ_W_BF16>(p, epi, s, e0, e1);
+  prof_end_kernel(tok, p.kind == LSQ_W_NF4 ? PROF_GEMM_FWD : PROF_GEMM_BF16, flops, bytes);
   if (p.splits > 1) {
     tok = prof_begin(s);
     launch_reduce(p.part, p.splits, p.M, p.N, p.bias, p.resid, p.out, p.ldc, epi, s);
@@ -1559,10 +1568,11 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
-  int tok = prof_begin(s);
-  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_W_NF4>(p, epi, s);
-  else dispatch_bwd_epi<LSQ_W_BF16>(p, epi, s);
-  prof_end(tok, s, p.kind == LSQ_W_NF4 ? PROF_GEMM_BWD : PROF_GEMM_BF16, flops, bytes);
+  hipEvent_t e0, e1;
+  int tok = prof_begin_kernel(&e0, &e1);
+  if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_W_NF4>(p, epi, s, e0, e1);
+  else dispatch_bwd_epi<LSQ_W_BF16>(p, epi, s, e0, e1);
+  prof_end_kernel(tok, p.kind == LSQ_W_NF4 ? PROF_GEMM_BWD : PROF_GEMM_BF16, flops, bytes);
   if (p.splits > 1) {
     tok = prof_begin(s);
     launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);

@@ -481,6 +481,14 @@ __device__ __forceinline__ void load_frags(const uint16_t* row, bool ok, int lg,
     f[c] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const uint4*>(row + 32 * c + 8 * lg)
                                          : make_uint4(0u, 0u, 0u, 0u));
 }
+// Four consecutive values as bf16 hi/lo quads, one 8-byte store each.
+__device__ __forceinline__ void put_hilo4(uint16_t* hi, uint16_t* lo, const float (&x)[4]) {
+  const uint32_t h0 = pack_bf16x2(x[0], x[1]), h1 = pack_bf16x2(x[2], x[3]);
+  const uint32_t l0 = pack_bf16x2(x[0] - bf_lo(h0), x[1] - bf_hi(h0));
+  const uint32_t l1 = pack_bf16x2(x[2] - bf_lo(h1), x[3] - bf_hi(h1));
+  *reinterpret_cast<u32x2*>(hi) = u32x2{h0, h1};
+  *reinterpret_cast<u32x2*>(lo) = u32x2{l0, l1};
+}
 __device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, float x) {
   const uint16_t h = f32_to_bf16_bits(x);
   *hi = h;
@@ -666,14 +674,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     load_rot_frags<HD>(a.qkv + (rowbase + qi) * a.ld + (int64_t)h * HD, ok, qi, a.rope, lg, qh, ql);
     load_frags<HD>(a.dO + (rowbase + qi) * a.ldo + (int64_t)h * HD, ok, lg, od);
   }
-  float lse_r[4], dd_r[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int qi = q0 + 16 * w + 4 * lg + v;
-    const bool ok = qi < a.S;
-    lse_r[v] = ok ? a.lse[((int64_t)b * a.nh + h) * a.S + qi] : 0.f;
-    dd_r[v] = ok ? a.D[(rowbase + qi) * a.nh + h] : 0.f;
-  }
+  // this lane's query for the scores (formed transposed: lane = query, its 4 values = 4 keys)
+  const int qi = q0 + 16 * w + lr;
+  const float lse_q = qi < a.S ? a.lse[((int64_t)b * a.nh + h) * a.S + qi] : 0.f;
+  const float dd_q = qi < a.S ? a.D[(rowbase + qi) * a.nh + h] : 0.f;
   f32x4 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -711,23 +715,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
         const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
         const bf16x8 vv = mfma_a8(&sm.v[16 * jt + lr][32 * c + 8 * lg]);
-        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
-        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
-        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
-        dpt[jt] = mfma_bf16(od[c], vv, dpt[jt]);
+        st[jt] = mfma_bf16(kh, qh[c], st[jt]);   // S^T: C[key 16 jt + 4 lg + v][query lr]
+        st[jt] = mfma_bf16(kl, qh[c], st[jt]);
+        st[jt] = mfma_bf16(kh, ql[c], st[jt]);
+        dpt[jt] = mfma_bf16(vv, od[c], dpt[jt]);
       }
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = q0 + 16 * w + 4 * lg + v;
+    for (int jt = 0; jt < 4; ++jt) {
+      float ds[4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int kj = k0 + 16 * jt + lr;
+      for (int v = 0; v < 4; ++v) {
+        const int kj = k0 + 16 * jt + 4 * lg + v;
         const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float pv = ok ? exp2f(st[jt][v] * sc - lse_r[v]) : 0.f;
-        put_hilo(&sm.sh[w][4 * lg + v][16 * jt + lr], &sm.sl[w][4 * lg + v][16 * jt + lr],
-                 pv * (dpt[jt][v] - dd_r[v]));
+        const float pv = ok ? exp2f(st[jt][v] * sc - lse_q) : 0.f;
+        ds[v] = pv * (dpt[jt][v] - dd_q);
       }
+      put_hilo4(&sm.sh[w][lr][16 * jt + 4 * lg], &sm.sl[w][lr][16 * jt + 4 * lg], ds);
     }
     // dS is wave-private: this wave's LDS writes are done before its reads below
 #pragma unroll
@@ -851,23 +855,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         const bf16x8 qhf = mfma_a8(&sm.qh[16 * jt + lr][32 * c + 8 * lg]);
         const bf16x8 qlf = mfma_a8(&sm.ql[16 * jt + lr][32 * c + 8 * lg]);
         const bf16x8 of = mfma_a8(&sm.o[16 * jt + lr][32 * c + 8 * lg]);
-        st[jt] = mfma_bf16(kh[c], qhf, st[jt]);
-        st[jt] = mfma_bf16(kh[c], qlf, st[jt]);
-        st[jt] = mfma_bf16(kl[c], qhf, st[jt]);
-        dpt[jt] = mfma_bf16(vv[c], of, dpt[jt]);
+        st[jt] = mfma_bf16(qhf, kh[c], st[jt]);   // S: C[query 16 jt + 4 lg + v][key lr]
+        st[jt] = mfma_bf16(qlf, kh[c], st[jt]);
+        st[jt] = mfma_bf16(qhf, kl[c], st[jt]);
+        dpt[jt] = mfma_bf16(of, vv[c], dpt[jt]);
       }
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int kj = k0 + 16 * w + 4 * lg + v;
+    {
+      const int kj = k0 + 16 * w + lr;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const int qi = q0 + 16 * jt + lr;
-        const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float pv = ok ? exp2f(st[jt][v] * sc - sm.lse[16 * jt + lr]) : 0.f;
-        put_hilo(&sm.ph[w][4 * lg + v][16 * jt + lr], &sm.pl[w][4 * lg + v][16 * jt + lr], pv);
-        put_hilo(&sm.sh[w][4 * lg + v][16 * jt + lr], &sm.sl[w][4 * lg + v][16 * jt + lr],
-                 pv * (dpt[jt][v] - sm.dd[16 * jt + lr]));
+        float pv[4], ds[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int qr = 16 * jt + 4 * lg + v, qi = q0 + qr;
+          const bool ok = kj <= qi && qi < a.S && kj < a.S;
+          pv[v] = ok ? exp2f(st[jt][v] * sc - sm.lse[qr]) : 0.f;
+          ds[v] = pv[v] * (dpt[jt][v] - sm.dd[qr]);
+        }
+        put_hilo4(&sm.ph[w][lr][16 * jt + 4 * lg], &sm.pl[w][lr][16 * jt + 4 * lg], pv);
+        put_hilo4(&sm.sh[w][lr][16 * jt + 4 * lg], &sm.sl[w][lr][16 * jt + 4 * lg], ds);
       }
     }
     // P^T and dS^T are wave-private: this wave's LDS writes are done before its reads below

@@ -27,12 +27,6 @@ __device__ __forceinline__ float dpp_row(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kRowRor2 = 0x122, kRowRor1 = 0x121;
-__device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, dpp_row<kRowRor8>(v));
-  v = fmaxf(v, dpp_row<kRowRor4>(v));
-  v = fmaxf(v, dpp_row<kRowRor2>(v));
-  return fmaxf(v, dpp_row<kRowRor1>(v));
-}
 __device__ __forceinline__ float group16_sum(float v) {
   v += dpp_row<kRowRor8>(v);
   v += dpp_row<kRowRor4>(v);
@@ -502,6 +496,7 @@ struct AttnF16Smem {
   uint16_t vt[HD][AT + 8];     // V transposed [d][key]
   uint16_t ph[4][16][AT + 8];  // per-wave P hi [query][key]
   uint16_t pl[4][16][AT + 8];  // per-wave P lo
+  float al[4][16];             // per-wave row factors (rescale, then 1 / sum) by query
 };
 
 // Forward: one workgroup per (query block of 64, head, batch), the heaviest
@@ -542,13 +537,14 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
     }
   }
   const float sc = a.scale * kLog2e;
-  float m[4], l[4];
+  // Scores are formed transposed (S^T = K Q^T): lane (lr, lg) holds keys
+  // 16 jt + 4 lg + v of query 16 w + lr, so its P values go to LDS as four
+  // 8-byte stores and the softmax state of its query (m_q, l_q) is shared by
+  // the four lanes lg.  The output rows (queries 4 lg + v) take their factors
+  // from the lanes that own those queries through sm.al.
+  const int qi = q0 + 16 * w + lr;
+  float m_q = -INFINITY, l_q = 0.f;
   f32x4 o[DT];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   Chunks<HD> ckh, ckl, cvt;
@@ -576,38 +572,50 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
       for (int c = 0; c < DC; ++c) {
         const bf16x8 kh = mfma_a8(&sm.kh[16 * jt + lr][32 * c + 8 * lg]);
         const bf16x8 kl = mfma_a8(&sm.kl[16 * jt + lr][32 * c + 8 * lg]);
-        st[jt] = mfma_bf16(qh[c], kh, st[jt]);
-        st[jt] = mfma_bf16(qh[c], kl, st[jt]);
-        st[jt] = mfma_bf16(ql[c], kh, st[jt]);
+        st[jt] = mfma_bf16(kh, qh[c], st[jt]);
+        st[jt] = mfma_bf16(kl, qh[c], st[jt]);
+        st[jt] = mfma_bf16(kh, ql[c], st[jt]);
       }
     }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = q0 + 16 * w + 4 * lg + v;
-      float mx = -INFINITY;
+    for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int kj = k0 + 16 * jt + lr;
+      for (int v = 0; v < 4; ++v) {
+        const int kj = k0 + 16 * jt + 4 * lg + v;
         st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
         mx = fmaxf(mx, st[jt][v]);
       }
-      mx = group16_max(mx);
-      const float mn = fmaxf(m[v], mx);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[v] - mn);
-      float rs = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m_q, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m_q - mn);
+    float rs = 0.f;
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const float pv = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
-        const uint16_t ph = f32_to_bf16_bits(pv);
-        sm.ph[w][4 * lg + v][16 * jt + lr] = ph;
-        sm.pl[w][4 * lg + v][16 * jt + lr] = f32_to_bf16_bits(pv - bf16_bits_to_f32(ph));
-        rs += pv;
+    for (int jt = 0; jt < 4; ++jt) {
+      float pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[v] = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
+        rs += pv[v];
       }
-      rs = group16_sum(rs);
-      l[v] = l[v] * alpha + rs;
-      m[v] = mn;
+      put_hilo4(&sm.ph[w][lr][16 * jt + 4 * lg], &sm.pl[w][lr][16 * jt + 4 * lg], pv);
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    l_q = l_q * alpha + rs;
+    m_q = mn;
+    // sm.al is wave-private: this wave's write lands before its read below
+    if (lg == 0) sm.al[w][lr] = alpha;
+    {
+      const float4 a4 = *reinterpret_cast<const float4*>(&sm.al[w][4 * lg]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][v] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt][0] *= a4.x;
+        o[dt][1] *= a4.y;
+        o[dt][2] *= a4.z;
+        o[dt][3] *= a4.w;
+      }
     }
     // P is wave-private: this wave's LDS writes are done before its reads below
 #pragma unroll
@@ -622,20 +630,25 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
       }
     }
   }
+  if (lg == 0) {
+    sm.al[w][lr] = l_q;
+    if (qi < a.S) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m_q + log2f(l_q);
+  }
+  const float4 l4 = *reinterpret_cast<const float4*>(&sm.al[w][4 * lg]);
+  const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int qi = q0 + 16 * w + 4 * lg + v;
-    if (qi >= a.S) continue;
-    const float inv = 1.f / l[v];
-    uint16_t* out = a.out + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+    const int qo = q0 + 16 * w + 4 * lg + v;
+    if (qo >= a.S) continue;
+    const float inv = 1.f / lv[v];
+    uint16_t* out = a.out + (rowbase + qo) * a.ldo + (int64_t)h * HD;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) out[16 * dt + lr] = f32_to_bf16_bits(o[dt][v] * inv);
     if (a.out_f32) {
-      float* of = a.out_f32 + (rowbase + qi) * a.ldo + (int64_t)h * HD;
+      float* of = a.out_f32 + (rowbase + qo) * a.ldo + (int64_t)h * HD;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) of[16 * dt + lr] = o[dt][v] * inv;
     }
-    if (lr == 0) a.lse[((int64_t)b * a.nh + h) * a.S + qi] = m[v] + log2f(l[v]);
   }
 }
 

@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "layer_ops.h"
 #include "nf4_levels.h"
 
 namespace lsq {
@@ -1681,8 +1682,7 @@ int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream
   if (M == 0 && !accumulate) {
     for (int i = 0; i < ntasks; ++i) {
       const TnTask& t = tasks[i];
-      for (int r = 0; r < (t.small_rows ? t.ns : t.nl); ++r)
-        LSQ_HIP(hipMemsetAsync(t.out + (int64_t)r * t.ldo, 0, sizeof(float) * (t.small_rows ? t.nl : t.ns), st));
+      if (int e = zero_words(t.out, t.ldo, t.small_rows ? t.ns : t.nl, t.small_rows ? t.nl : t.ns, st)) return e;
     }
     return LSQ_OK;
   }
@@ -1717,8 +1717,7 @@ int lora_tn(const float* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl
   LSQ_CHECK(direct || (ws && ws_bytes >= lora_tn_ws_bytes(M, ns, nl)), LSQ_ERR_WORKSPACE, "lora_tn: workspace too small");
   if (M == 0) {
     if (!accumulate) {
-      for (int i = 0; i < (small_rows ? ns : nl); ++i)
-        LSQ_HIP(hipMemsetAsync(out + (int64_t)i * ldo, 0, sizeof(float) * (small_rows ? nl : ns), st));
+      if (int e = zero_words(out, ldo, small_rows ? ns : nl, small_rows ? nl : ns, st)) return e;
     }
     return LSQ_OK;
   }
@@ -1792,6 +1791,7 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
   LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
   hipStream_t s = as_stream(stream);
   const WeightRef w = ref_of(W);
+  if (M == 0) return LSQ_OK;   // no tokens: nothing to write
   const int Mi = (int)M;
   if (dtype == LSQ_F32) {
     float* U = U_out ? static_cast<float*>(U_out) : static_cast<float*>(ws);
@@ -1853,6 +1853,11 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_bwd: workspace %zu < %zu", ws_bytes, need);
   hipStream_t s = as_stream(stream);
   const WeightRef w = ref_of(W);
+  if (M == 0) {   // no tokens: zero adapter gradients, or leave them when accumulating
+    if (accumulate) return LSQ_OK;
+    if (int e = zero_words(dA, w.K, r, w.K, s)) return e;
+    return zero_words(dB, r, w.N, r, s);
+  }
   const int Mi = (int)M;
   char* wsp = static_cast<char*>(ws);
   const size_t el = dtype == LSQ_F32 ? 4 : 2;

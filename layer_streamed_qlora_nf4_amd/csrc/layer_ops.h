@@ -46,6 +46,8 @@ int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint
 int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
                 float* dx, uint16_t* dx_b, hipStream_t s);
 int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+// Zero rows x cols 32-bit words, row pitch ld words (a kernel, safe under graph capture).
+int zero_words(void* dst, int64_t ld, int rows, int cols, hipStream_t s);
 int rope_table(int S, int head_dim, float theta, float* table, hipStream_t s);
 int rope_apply(uint16_t* buf, int64_t ld, int T, int S, int n_rot_heads, int head_dim, const float* table, int inverse,
                hipStream_t s);

@@ -1154,6 +1154,23 @@ int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float*
   return LSQ_OK;
 }
 
+// Zero rows x cols 32-bit words at a row pitch of ld words, with a kernel
+// rather than hipMemsetAsync so that the clear stays correct inside a captured
+// HIP graph replayed several times.
+__global__ void zero_words_kernel(uint32_t* __restrict__ dst, int64_t ld, int rows, int cols) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)rows * cols) return;
+  dst[(e / cols) * ld + e % cols] = 0u;
+}
+
+int zero_words(void* dst, int64_t ld, int rows, int cols, hipStream_t s) {
+  const int64_t n = (int64_t)rows * cols;
+  if (n == 0) return LSQ_OK;
+  zero_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<uint32_t*>(dst), ld, rows, cols);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
 int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
   LSQ_CHECK(n % 4 == 0, LSQ_ERR_SHAPE, "to_bf16: n %% 4 != 0");
   if (n == 0) return LSQ_OK;

@@ -782,7 +782,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   float* xs = w.xs;
   auto x_at = [&](int i) { return xs + (uint64_t)i * T * H; };
 
-  LSQ_HIP(hipMemsetAsync(w.bad, 0, 4, s));
+  if (int e = zero_words(w.bad, 1, 1, 1, s)) return e;
   if (int e = embed_gather(ids, static_cast<const uint16_t*>(embed), T, H, V, x_at(0), w.bad, s)) return e;
   // the head's copy is queued on the copy stream behind the forward's layer
   // copies (issued after the prefetch of the last layer) and waited for at the turn

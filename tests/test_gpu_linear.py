@@ -161,6 +161,31 @@ def test_nf4_lora_linear_matches_oracle(gpu, M, K, N, r, dtype):
         assert e <= tol, f"{name}: {e:.3e} > {tol}"
 
 
+def test_linear_bwd_with_no_tokens_clears_or_keeps_the_adapter_grads(gpu):
+    """M = 0: dA and dB are zero (accumulate = 0) or left as they were (accumulate = 1)."""
+    K, N, r = 256, 320, 8
+    print_case(test="linear_bwd_empty", K=K, N=N, r=r)
+    w = synth.normal_bf16((N, K), 0.0, 0.02, (130, 0))
+    packed, absmax = (dev(a) for a in onf4.quantize(w))
+    weight = lib.Weight(lib.LSQ_W_NF4, 0, packed.data_ptr(), absmax.data_ptr(), N, K)
+    A = torch.zeros((r, K), dtype=torch.int16, device="cuda")
+    B = torch.zeros((N, r), dtype=torch.int16, device="cuda")
+    dummy = torch.zeros(64, dtype=torch.int16, device="cuda")
+    wsb = lib.raw("nf4_lora_linear_workspace_size")(0, N, K, r, lib.LSQ_BF16)
+    ws = empty_bytes(max(wsb, 256))
+    for dtype in (lib.LSQ_BF16, lib.LSQ_F32):
+        lib.call("nf4_lora_linear_fwd", C.byref(weight), None, ptr(dummy), 0, ptr(A), ptr(B), r, 2.0, dtype,
+                 ptr(dummy), ptr(dummy), ptr(ws), wsb, stream())
+        for accumulate in (1, 0):
+            dA = torch.full((r, K), 7.0, dtype=torch.float32, device="cuda")
+            dB = torch.full((N, r), 7.0, dtype=torch.float32, device="cuda")
+            lib.call("nf4_lora_linear_bwd", C.byref(weight), ptr(dummy), ptr(dummy), 0, ptr(A), ptr(B), r, 2.0,
+                     dtype, ptr(dummy), ptr(dummy), ptr(dA), ptr(dB), accumulate, ptr(ws), wsb, stream())
+            torch.cuda.synchronize()
+            want = 7.0 if accumulate else 0.0
+            assert bool((dA == want).all()) and bool((dB == want).all()), (dtype, accumulate)
+
+
 def test_bf16_base_linear_matches_oracle(gpu):
     M, K, N, r, s = 96, 256, 320, 16, 2.0
     X, W, A, B, dY = _linear_inputs(M, K, N, r, 120)

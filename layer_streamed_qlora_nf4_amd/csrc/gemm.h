@@ -110,17 +110,23 @@ struct TnTask {
   int64_t ldo;
   int small_rows;
   int tile0;          // set by lora_grads
+  int64_t part_off;   // set by lora_grads: this task's float32 partials in the workspace
 };
 struct TnBatch {
   TnTask t[8];
   int ntasks, M, accumulate;
+  int splits, per;    // token ranges of `per` tokens (a multiple of 64); splits > 1 writes partials
+  float* part;
 };
 struct SegFinish {
   int c0[4], c1[4], col[4];
   int n;
 };
-// Every task of one group in one launch, no partials (fixed token order per output).
-int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream_t st);
+// Every task of one group in one launch.  Launches with few column tiles
+// split the tokens into ranges whose float32 partials are summed in range
+// order by a second kernel (a pure function of the shapes; fixed order).
+size_t lora_grads_ws_bytes(const TnTask* tasks, int ntasks, int M);
+int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, float* ws, size_t ws_bytes, hipStream_t st);
 
 // Token-dimension reduction C = S^T L (small_rows: [ns, nl]; else [nl, ns]).
 size_t lora_tn_ws_bytes(int M, int ns, int nl);

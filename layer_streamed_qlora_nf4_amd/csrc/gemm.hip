@@ -1166,7 +1166,9 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_mfma_kernel(TnBatch bt) {
   for (int i = 1; i < 8; ++i)
     if (i < bt.ntasks && (int)blockIdx.x >= bt.t[i].tile0) tk = bt.t[i];
   const int b0 = (blockIdx.x - tk.tile0) * TNM_COLS;
-  const int ns = tk.ns, M = bt.M;
+  const int ns = tk.ns;
+  const int m_hi = min(bt.M, (int)(blockIdx.y + 1) * bt.per);   // this block's tokens end here
+  const int M = m_hi;
   // this thread's L micro-tile (4 tokens x 8 columns) and S row (one token, 16 small indices)
   const int lr = 4 * (tid >> 4), lc = 8 * (tid & 15);
   const int scol = b0 + lc;
@@ -1217,12 +1219,13 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_mfma_kernel(TnBatch bt) {
   f32x4 acc[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load(0);
-  for (int m0 = 0; m0 < M; m0 += TNM_TOK) {
+  const int m_lo = blockIdx.y * bt.per;
+  load(m_lo);
+  for (int m0 = m_lo; m0 < m_hi; m0 += TNM_TOK) {
     __syncthreads();   // the previous k-step's fragment reads are done
     store();
     __syncthreads();
-    if (m0 + TNM_TOK < M) load(m0 + TNM_TOK);
+    if (m0 + TNM_TOK < m_hi) load(m0 + TNM_TOK);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int t0 = 32 * kb + 8 * (lane >> 4);
@@ -1265,11 +1268,34 @@ __global__ void __launch_bounds__(NTHREADS) lora_grads_mfma_kernel(TnBatch bt) {
       for (int v = 0; v < 4; ++v) {
         const int a = 16 * g + 4 * (lane >> 4) + v;
         if (a >= ns) continue;
+        if (bt.splits > 1) {
+          bt.part[tk.part_off + ((int64_t)blockIdx.y * ns + a) * tk.nl + b] = acc[g][c][v];
+          continue;
+        }
         const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
         tk.out[o] = bt.accumulate ? tk.out[o] + acc[g][c][v] : acc[g][c][v];
       }
     }
   }
+}
+
+// The token-range partials of every task of a lora_grads launch summed in
+// range order, then stored (or added) in the task's output layout.
+__global__ void lora_grads_reduce_kernel(TnBatch bt, int64_t total) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  int i = 0;
+  while (i + 1 < bt.ntasks && e >= (int64_t)bt.t[i].ns * bt.t[i].nl) {
+    e -= (int64_t)bt.t[i].ns * bt.t[i].nl;
+    ++i;
+  }
+  const TnTask& tk = bt.t[i];
+  const int a = (int)(e / tk.nl), b = (int)(e % tk.nl);
+  const int64_t plane = (int64_t)tk.ns * tk.nl;
+  float v = 0.f;
+  for (int sp = 0; sp < bt.splits; ++sp) v += bt.part[tk.part_off + sp * plane + e];
+  const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
+  tk.out[o] = bt.accumulate ? tk.out[o] + v : v;
 }
 
 // G finish for several segments at once: segment s sums chunks [c0, c1) of part.
@@ -1653,7 +1679,26 @@ int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int
   return LSQ_OK;
 }
 
-int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream_t st) {
+// Token ranges of a matrix-core lora_grads launch: enough column-tile x range
+// workgroups to keep about four per CU loading (each walks its range 64 tokens
+// at a time), at least 128 tokens per range, at most 8 ranges.
+static int lora_grads_splits(int mtiles, int M) {
+  return std::max(1, std::min({8, (1024 + mtiles - 1) / mtiles, M / 128}));
+}
+static int lora_grads_mtiles(const TnTask* tasks, int ntasks) {
+  int mt = 0;
+  for (int i = 0; i < ntasks; ++i) mt += (tasks[i].nl + TNM_COLS - 1) / TNM_COLS;
+  return mt;
+}
+size_t lora_grads_ws_bytes(const TnTask* tasks, int ntasks, int M) {
+  const int sp = lora_grads_splits(lora_grads_mtiles(tasks, ntasks), M);
+  if (sp <= 1) return 0;
+  size_t n = 0;
+  for (int i = 0; i < ntasks; ++i) n += (size_t)tasks[i].ns * tasks[i].nl;
+  return n * sp * sizeof(float);
+}
+
+int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
   LSQ_CHECK(ntasks >= 1 && ntasks <= 8, LSQ_ERR_INVALID, "lora_grads: 1..8 tasks");
   TnBatch bt{};
   int tiles = 0, mtiles = 0;
@@ -1686,11 +1731,33 @@ int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, hipStream
     }
     return LSQ_OK;
   }
+  bt.splits = 1;
+  bt.per = M;
+  if (mfma) {
+    bt.splits = lora_grads_splits(mtiles, M);
+    if (bt.splits > 1) {
+      const size_t need = lora_grads_ws_bytes(tasks, ntasks, M);
+      LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "lora_grads: needs %zu bytes of workspace", need);
+      bt.per = ((M + bt.splits - 1) / bt.splits + TNM_TOK - 1) / TNM_TOK * TNM_TOK;
+      bt.part = ws;
+      int64_t off = 0;
+      for (int i = 0; i < ntasks; ++i) {
+        bt.t[i].part_off = off;
+        off += (int64_t)bt.splits * tasks[i].ns * tasks[i].nl;
+      }
+    }
+  }
   int tok = prof_begin(st);
-  if (mfma)
-    lora_grads_mfma_kernel<<<mtiles, NTHREADS, 0, st>>>(bt);
-  else
+  if (mfma) {
+    lora_grads_mfma_kernel<<<dim3(mtiles, bt.splits), NTHREADS, 0, st>>>(bt);
+    if (bt.splits > 1) {
+      int64_t total = 0;
+      for (int i = 0; i < ntasks; ++i) total += (int64_t)tasks[i].ns * tasks[i].nl;
+      lora_grads_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(bt, total);
+    }
+  } else {
     lora_grads_kernel<<<tiles, NTHREADS, 0, st>>>(bt);
+  }
   prof_end(tok, st, PROF_LORA, flops, bytes);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

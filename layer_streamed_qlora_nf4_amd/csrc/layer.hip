@@ -156,10 +156,27 @@ static size_t gemm_need(const Dims& d, int T) {
   return m;
 }
 
+static int grad_tasks(const Dims& d, const float* G, int ldg, const float* U, int ldu, const uint16_t* X, int Kx,
+                      const uint16_t* dY, int ldy, int nseg, const int* seg_end, float* gA, float* gB,
+                      TnTask (&tasks)[8]);
+
+// Token-reduction partials: the adapter-gradient launches of the four groups
+// (shapes only; the pointers are not used for sizing).
 static size_t tn_need(const Dims& d, int T) {
   size_t m = 0;
-  const int nls[] = {d.H, d.I, d.Nq, d.Nkv, d.Nqkv, 2 * d.I};
-  for (int nl : nls) m = std::max(m, lora_tn_ws_bytes(T, d.r, nl));
+  const int r = d.r;
+  const int se3[1] = {d.H}, se2[2] = {d.I, 2 * d.I}, se1[1] = {d.H}, se0[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
+  const struct {
+    int rr, Kx, ldy, nseg;
+    const int* se;
+  } groups[4] = {{3 * r, d.H, d.Nqkv, 3, se0}, {r, d.Nq, d.H, 1, se1}, {2 * r, d.H, 2 * d.I, 2, se2},
+                 {r, d.I, d.H, 1, se3}};
+  for (const auto& g : groups) {
+    TnTask tasks[8];
+    const int n = grad_tasks(d, nullptr, g.rr, nullptr, g.rr, nullptr, g.Kx, nullptr, g.ldy, g.nseg, g.se, nullptr,
+                             nullptr, tasks);
+    m = std::max(m, lora_grads_ws_bytes(tasks, n, T));
+  }
   return m;
 }
 
@@ -397,24 +414,32 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
 
 // dA of the whole stacked group (G^T X, one task) and dB of each segment
 // (dY_seg^T U_seg), in one launch, from the unrounded float32 G and U.
-static int adapter_grads(const Dims& d, int T, const float* G, int ldg, const float* U, int ldu,
-                         const uint16_t* X, int Kx, const uint16_t* dY, int ldy, int nseg, const int* seg_end,
-                         float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
+// The dA and dB tasks of one group (segments of a stacked group are separate
+// dB tasks; dA stays one task while the stacked rank fits 64).
+static int grad_tasks(const Dims& d, const float* G, int ldg, const float* U, int ldu, const uint16_t* X, int Kx,
+                      const uint16_t* dY, int ldy, int nseg, const int* seg_end, float* gA, float* gB,
+                      TnTask (&tasks)[8]) {
   const int r = d.r;
-  TnTask tasks[8];
   int n = 0;
   if (nseg * r <= 64) {
-    tasks[n++] = TnTask{G, ldg, nseg * r, X, Kx, Kx, gA, Kx, 1, 0};
+    tasks[n++] = TnTask{G, ldg, nseg * r, X, Kx, Kx, gA, Kx, 1, 0, 0};
   } else {
     for (int sg = 0; sg < nseg; ++sg)
-      tasks[n++] = TnTask{G + sg * r, ldg, r, X, Kx, Kx, gA + (int64_t)sg * r * Kx, Kx, 1, 0};
+      tasks[n++] = TnTask{G + sg * r, ldg, r, X, Kx, Kx, gA + (int64_t)sg * r * Kx, Kx, 1, 0, 0};
   }
   for (int sg = 0; sg < nseg; ++sg) {
     const int nb = sg == 0 ? 0 : seg_end[sg - 1], ne = seg_end[sg];
-    tasks[n++] = TnTask{U + sg * r, ldu, r, dY + nb, ldy, ne - nb, gB + (int64_t)nb * r, r, 0, 0};
+    tasks[n++] = TnTask{U + sg * r, ldu, r, dY + nb, ldy, ne - nb, gB + (int64_t)nb * r, r, 0, 0, 0};
   }
-  (void)w;
-  return lora_grads(tasks, n, T, accumulate, s);
+  return n;
+}
+
+static int adapter_grads(const Dims& d, int T, const float* G, int ldg, const float* U, int ldu,
+                         const uint16_t* X, int Kx, const uint16_t* dY, int ldy, int nseg, const int* seg_end,
+                         float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
+  TnTask tasks[8];
+  const int n = grad_tasks(d, G, ldg, U, ldu, X, Kx, dY, ldy, nseg, seg_end, gA, gB, tasks);
+  return lora_grads(tasks, n, T, accumulate, w.tn, w.tn_bytes, s);
 }
 
 static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraView& lv, const float* x_in,

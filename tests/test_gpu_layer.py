@@ -75,7 +75,9 @@ def inputs(cfg, seq=None):
                                  # heads and a sequence one past a whole query block
                                  configs.TINY.with_(name="tiny-s1", batch=3, seq=1, wid=13),
                                  configs.TINY.with_(name="tiny-hd128", n_heads=2, n_kv_heads=1, head_dim=128,
-                                                    batch=2, seq=129, wid=14)])
+                                                    batch=2, seq=129, wid=14),
+                                 # 1000 tokens: the adapter-gradient token reduction split 7 ways, the last range short
+                                 configs.TINY.with_(name="tiny-t1000", batch=2, seq=500, wid=15)])
 def test_decoder_layer_matches_oracle(gpu, cfg):
     print_case(test="decoder_layer", cfg=cfg.name, B=cfg.batch, S=cfg.seq)
     x_bits, dout = inputs(cfg)

@@ -7,7 +7,9 @@
 // two claims, not one"; "v0.76.0 changes the code").  Here both directions
 // decode NF4 inside the GEMM: packed codes and float32 absmax stream from HBM
 // (0.5625 B per weight), each workgroup decodes its weight tile once into LDS
-// as bf16 through a 16-entry level table, and bf16 MFMA 16x16x32 tiles with
+// as bf16 (the forward's main kernel looks levels up with byte permutes of a
+// per-row table in registers, the others through a 16-entry table in LDS),
+// and bf16 MFMA 16x16x32 tiles with
 // float32 accumulation consume it.  The LoRA up-projection U B^T (forward) and
 // G A (backward) ride in the same accumulators.  The kernel chosen depends on
 // (M, N, K, r) only, so resident and streamed runs execute identical code.
@@ -69,6 +71,46 @@ __device__ __forceinline__ void decode_word(uint32_t w, float a, const float* lu
     float v1 = lut[byte & 15u] * a;
     out[j] = pack_bf16x2(v0, v1);
   }
+}
+
+// The same decode with the level table in registers: the 16 levels times one
+// absmax, rounded to bf16, split into byte planes (the low bytes of levels
+// 4g..4g+3 in lo[g], their high bytes in hi[g]).  A code then becomes its bf16
+// value through byte permutes (v_perm_b32: selector byte s < 8 takes byte s of
+// {src0, src1}, src1 the low word), with no LDS reads; the values are the same
+// fp32 products rounded once to bf16 as decode_word gives.
+struct NF4Planes {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ NF4Planes nf4_planes(float a) {
+  NF4Planes p;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t d0 = pack_bf16x2(kNF4LevelsDev[4 * g] * a, kNF4LevelsDev[4 * g + 1] * a);
+    const uint32_t d1 = pack_bf16x2(kNF4LevelsDev[4 * g + 2] * a, kNF4LevelsDev[4 * g + 3] * a);
+    p.lo[g] = __builtin_amdgcn_perm(d1, d0, 0x06040200u);
+    p.hi[g] = __builtin_amdgcn_perm(d1, d0, 0x07050301u);
+  }
+  return p;
+}
+// Four codes, one per byte of x, to bf16 pairs (code of byte 0, byte 1) and
+// (byte 2, byte 3): each plane is looked up in levels 0-7 and 8-15 with the
+// code's low 3 bits, and bit 3 picks which of the two bytes is kept.
+__device__ __forceinline__ void nf4_lookup4(const NF4Planes& p, uint32_t x, uint32_t& o01, uint32_t& o23) {
+  const uint32_t s = x & 0x07070707u;
+  const uint32_t pick = ((x >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(p.lo[3], p.lo[2], s),
+                                            __builtin_amdgcn_perm(p.lo[1], p.lo[0], s), pick);
+  const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(p.hi[3], p.hi[2], s),
+                                            __builtin_amdgcn_perm(p.hi[1], p.hi[0], s), pick);
+  o01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+// decode_word's output (4 bf16 pairs in element order) from the planes.
+__device__ __forceinline__ void decode_word_regs(uint32_t w, const NF4Planes& p, uint32_t out[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;   // odd, even elements
+  nf4_lookup4(p, __builtin_amdgcn_perm(hi, lo, 0x01050004u), out[0], out[1]);
+  nf4_lookup4(p, __builtin_amdgcn_perm(hi, lo, 0x03070206u), out[2], out[3]);
 }
 
 // LoRA up-projection folded into the tile: acc += U_seg B^T, one or more
@@ -321,8 +363,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // path: each wave copies its group's share of the next k-step's X tile
 // straight into LDS (buffer loads with the LDS modifier, issued as its MFMA
 // half begins and waited for at the end of its decode half), so the decode
-// half only unpacks NF4 codes.  Lane l of a DMA fills LDS bytes 16 l of an
-// 8-row block, i.e. row l / 8, swizzled chunk slot l % 8; it therefore loads
+// half only unpacks NF4 codes.  It does so from registers (nf4_planes, one
+// table per thread and k-step: a thread's 32 codes share one absmax), which
+// leaves LDS to the fragment reads, the decoded tile and the DMA; the level
+// table lookups were half of this kernel's LDS instructions.  Lane l of a
+// DMA fills LDS bytes 16 l of an 8-row block, i.e. row l / 8, swizzled chunk
+// slot l % 8; it therefore loads
 // logical chunk (l % 8) ^ (row % 8).  The two LDS stages are separate arrays
 // and the k loop is unrolled by two so that every access names its stage
 // statically (the compiler can then tell DMA writes to one stage from reads of
@@ -340,7 +386,6 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * 64];
-  __shared__ float lut[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -352,7 +397,6 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   // neighbours, so remap_tile puts them on one XCD and the slab leaves HBM once.
   const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
   const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
-  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K, nk_all = K / BK;
   const int split = blockIdx.y;
@@ -391,10 +435,11 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) {
     const uint32_t words[4] = {rb[set].x, rb[set].y, rb[set].z, rb[set].w};
     if (!bact) return;
+    const NF4Planes pl = nf4_planes(rab[set]);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t o[4];
-      decode_word(words[w], rab[set], lut, o);
+      decode_word_regs(words[w], pl, o);
       *reinterpret_cast<uint4*>(&bs[swz(brow, bh * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
@@ -461,7 +506,6 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
     dma_x(kbeg, As0);
     load_b(kbeg, 0);
   }
-  __syncthreads();  // lut
   if (kbeg < nk) {
     load_b(min(kbeg + 1, nk - 1), 1);
     store_b(Bs0, 0);

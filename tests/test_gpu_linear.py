@@ -186,6 +186,48 @@ def test_linear_bwd_with_no_tokens_clears_or_keeps_the_adapter_grads(gpu):
             assert bool((dA == want).all()) and bool((dB == want).all()), (dtype, accumulate)
 
 
+IDENTITY_CASES = [
+    # (M, K, N): 256-wide tiles with several row tiles; a ragged N with an odd
+    # number of k-steps; the 192-wide forward tile (N = 6144 at 512 rows); a
+    # forward split four or more ways over its k-steps
+    (1024, 512, 1024),
+    (600, 320, 600),
+    (512, 512, 6144),
+    (2048, 2048, 256),
+]
+
+
+@pytest.mark.parametrize("M,K,N", IDENTITY_CASES)
+@pytest.mark.parametrize("dtype", [lib.LSQ_BF16, lib.LSQ_F32])
+def test_in_gemm_decode_is_the_dequantized_weight(gpu, M, K, N, dtype):
+    """With X = I the forward's output is W^T, and with dY = I (and B = 0) the
+    backward's dX is W: each output is one product with 1.0 accumulated in
+    float32, so it must equal the oracle's dequantized weight exactly (bf16
+    bits, or the float32 product, compared as values so that +0 and -0 of an
+    all-zero block agree).  Random codes cover all 16 levels; the absmax values
+    span 1e-30 to 1e30 and include zero blocks."""
+    print_case(test="in_gemm_decode", M=M, K=K, N=N, dtype=dtype)
+    rng = np.random.default_rng(7000 + M + K + N)
+    packed = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    mag = 10.0 ** rng.choice([-30, -12, -3, -1, 0, 2, 12, 30], size=(N, K // 64))
+    absmax = (mag * rng.uniform(0.5, 1.0, size=mag.shape)).astype(np.float32)
+    absmax[rng.random(absmax.shape) < 0.02] = 0.0
+    one = np.uint16(0x3F80)
+    X = np.zeros((M, K), dtype=np.uint16)
+    X[np.arange(min(M, K)), np.arange(min(M, K))] = one
+    dY = np.zeros((M, N), dtype=np.uint16)
+    dY[np.arange(min(M, N)), np.arange(min(M, N))] = one
+    r = 8
+    A = synth.normal_bf16((r, K), 0.0, 0.01, (140, 0))
+    B = np.zeros((N, r), dtype=np.uint16)
+    Y, _, dX, _, _ = _run_linear(X, packed, absmax, A, B, dY, M, K, N, r, 2.0, dtype)
+    Wd = onf4.dequantize_bf16_f64(packed, absmax) if dtype == lib.LSQ_BF16 else \
+        onf4.dequantize_f32(packed, absmax).astype(np.float64)
+    kk, nn = min(M, K), min(M, N)
+    assert np.array_equal(Y[:kk], Wd.T[:kk]) and not Y[kk:].any()
+    assert np.array_equal(dX[:nn], Wd[:nn]) and not dX[nn:].any()
+
+
 def test_bf16_base_linear_matches_oracle(gpu):
     M, K, N, r, s = 96, 256, 320, 16, 2.0
     X, W, A, B, dY = _linear_inputs(M, K, N, r, 120)

@@ -111,7 +111,9 @@ typedef struct {
 size_t nf4_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype);
 
 /* X [M, K], A [r, K], B [N, r], bias [N] (nullable, bf16) in `dtype`;
- * Y [M, N] in `dtype`; U_out [M, r] in `dtype` (nullable). */
+ * Y [M, N] in `dtype`; U_out [M, r] in `dtype` (nullable).
+ * Shapes: K % 64 == 0, r in {8, 16, ..., 64}, and N % 8 == 0 for LSQ_BF16
+ * (LSQ_ERR_SHAPE otherwise, checked before anything is enqueued). */
 int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, int64_t M,
                         const void* A, const void* B, int32_t r, float scale, int32_t dtype,
                         void* Y, void* U_out, void* ws, size_t ws_bytes, void* stream);

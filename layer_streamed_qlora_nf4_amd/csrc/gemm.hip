@@ -941,6 +941,21 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
 }
 
+// v + p[k0 * stride] + ... + p[(k1 - 1) * stride], added in k order.  The
+// loads go out eight at a time before any add: a loop with a run-time bound
+// otherwise waits for each load before issuing the next.
+__device__ __forceinline__ float ordered_sum(float v, const float* __restrict__ p, int64_t stride, int k0, int k1) {
+  for (int kb = k0; kb < k1; kb += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = (kb + j < k1) ? p[(int64_t)(kb + j) * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (kb + j < k1) v += t[j];
+  }
+  return v;
+}
+
 // =========================================================== LoRA down: U = s X A^T
 // Grid (M / 16 row blocks, K / 512 chunks): each workgroup's 4 waves take 128
 // of its chunk's columns each and sum their 16 x rr tiles in wave order; the
@@ -957,20 +972,33 @@ __global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __r
   f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
   const int row = m0 + (lane & 15);
   const int g = lane >> 4;
-  // four 32-wide steps per wave; steps past this wave's range read zeros
+  // four 32-wide steps per wave; steps past this wave's range read zeros.
+  // Every load of the wave is issued before the first MFMA (addresses are
+  // clamped into the operands and the values masked afterwards).
+  constexpr int NS = KCHUNK / 4 / 32;
+  uint4 av[NS], bv[NS][4];
+  const int rowc = min(row, M - 1);
 #pragma unroll
-  for (int i = 0; i < KCHUNK / 4 / 32; ++i) {
-    const int kk = kb + 32 * i + 8 * g;
+  for (int i = 0; i < NS; ++i) {
+    const int kk = kb + 32 * i + 8 * g, kkc = min(kk, K - 8);
     const bool kin = kk < ke;
-    uint4 av = (row < M && kin) ? *reinterpret_cast<const uint4*>(X + (int64_t)row * ldx + kk) : make_uint4(0, 0, 0, 0);
+    const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)rowc * ldx + kkc);
+    av[i] = (row < M && kin) ? x : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
       const int c = ct * 16 + (lane & 15);
-      uint4 bv = (c < rr && kin) ? *reinterpret_cast<const uint4*>(A + (int64_t)c * K + kk) : make_uint4(0, 0, 0, 0);
-      acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
+      const uint4 a = *reinterpret_cast<const uint4*>(A + (int64_t)min(c, rr - 1) * K + kkc);
+      bv[i][ct] = (c < rr && kin) ? a : make_uint4(0, 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nct) break;
+      acc[ct] = mfma16(u4_as_frag(av[i]), u4_as_frag(bv[i][ct]), acc[ct]);
+    }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     if (ct >= nct) break;
@@ -992,8 +1020,7 @@ __global__ void lora_finish_kernel(const float* __restrict__ part, int nchunks, 
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (int64_t)M * w) return;
   const int64_t m = e / w, c = e % w;
-  float v = 0.f;
-  for (int k = 0; k < nchunks; ++k) v += part[(int64_t)k * M * w + e];
+  float v = ordered_sum(0.f, part + e, (int64_t)M * w, 0, nchunks);
   v *= s;
   dst[m * ld + c] = f32_to_bf16_bits(v);
   if (dst32) dst32[m * ld32 + c] = v;
@@ -1004,12 +1031,14 @@ __global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, int64_t n, 
   if (e < n) dst[e] = bf16_bits_to_f32(src[e]);
 }
 
-// B [N, r] -> Bt [r, N] (bf16), so the G kernel reads 8 reduction values contiguously.
+// B [N, r] -> Bt [r, N] (bf16), so the G kernel reads 8 reduction values
+// contiguously.  One thread per output element: the writes are coalesced and
+// the strided reads of the (small) source come from cache.
 __global__ void transpose_rows_kernel(const uint16_t* __restrict__ B, int N, int r, uint16_t* __restrict__ Bt) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (int64_t)N * r) return;
-  int n = e / r, j = e % r;
-  Bt[(int64_t)j * N + n] = B[e];
+  const int64_t j = e / N, n = e % N;
+  Bt[e] = B[n * r + j];
 }
 
 // =========================================================== LoRA G = s dY_seg B_seg
@@ -1025,19 +1054,31 @@ __global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __rest
   const int cb = ch.begin[chunk], ce = ch.end[chunk];
   const int kb = cb + wave * (KCHUNK / 4), ke = min(ce, kb + KCHUNK / 4);
   f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  // all loads first, as in lora_down_kernel
+  constexpr int NS = KCHUNK / 4 / 32;
+  uint4 av[NS], bv[NS][4];
+  const int rowc = min(row, M - 1);
 #pragma unroll
-  for (int i = 0; i < KCHUNK / 4 / 32; ++i) {
-    const int kk = kb + 32 * i + 8 * g;
+  for (int i = 0; i < NS; ++i) {
+    const int kk = kb + 32 * i + 8 * g, kkc = min(kk, N - 8);
     const bool kin = kk < ke;
-    uint4 av = (row < M && kin) ? *reinterpret_cast<const uint4*>(dY + (int64_t)row * ldy + kk) : make_uint4(0, 0, 0, 0);
+    const uint4 y = *reinterpret_cast<const uint4*>(dY + (int64_t)rowc * ldy + kkc);
+    av[i] = (row < M && kin) ? y : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
       const int c = ct * 16 + (lane & 15);
-      uint4 bv = (c < r && kin) ? *reinterpret_cast<const uint4*>(Bt + (int64_t)c * N + kk) : make_uint4(0, 0, 0, 0);
-      acc[ct] = mfma16(u4_as_frag(av), u4_as_frag(bv), acc[ct]);
+      const uint4 b = *reinterpret_cast<const uint4*>(Bt + (int64_t)min(c, r - 1) * N + kkc);
+      bv[i][ct] = (c < r && kin) ? b : make_uint4(0, 0, 0, 0);
     }
   }
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nct) break;
+      acc[ct] = mfma16(u4_as_frag(av[i]), u4_as_frag(bv[i][ct]), acc[ct]);
+    }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     if (ct >= nct) break;
@@ -1336,8 +1377,7 @@ __global__ void lora_grads_reduce_kernel(TnBatch bt, int64_t total) {
   const TnTask& tk = bt.t[i];
   const int a = (int)(e / tk.nl), b = (int)(e % tk.nl);
   const int64_t plane = (int64_t)tk.ns * tk.nl;
-  float v = 0.f;
-  for (int sp = 0; sp < bt.splits; ++sp) v += bt.part[tk.part_off + sp * plane + e];
+  const float v = ordered_sum(0.f, bt.part + tk.part_off + e, plane, 0, bt.splits);
   const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
   tk.out[o] = bt.accumulate ? tk.out[o] + v : v;
 }
@@ -1352,8 +1392,7 @@ __global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinis
   const int sg = e / per;
   const int64_t i = e % per;
   const int64_t m = i / r, c = i % r;
-  float v = 0.f;
-  for (int k = sf.c0[sg]; k < sf.c1[sg]; ++k) v += part[(int64_t)k * per + i];
+  float v = ordered_sum(0.f, part + i, per, sf.c0[sg], sf.c1[sg]);
   v *= s;
   dst[m * ld + sf.col[sg] + c] = f32_to_bf16_bits(v);
   if (dst32) dst32[m * ld32 + sf.col[sg] + c] = v;
@@ -1365,8 +1404,7 @@ __global__ void reduce_splits_kernel(const float* __restrict__ part, int splits,
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)rows * cols;
   if (e >= n) return;
-  float v = 0.f;
-  for (int sp = 0; sp < splits; ++sp) v += part[sp * n + e];
+  const float v = ordered_sum(0.f, part + e, n, 0, splits);
   const int64_t o = (e / cols) * ldo + (e % cols);
   out[o] = accumulate ? out[o] + v : v;
 }
@@ -1444,13 +1482,22 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   const int64_t total = (int64_t)M * N;
   if (e >= total) return;
+  // Partials added in split order; the loads go out four splits at a time.
   float4 v = *reinterpret_cast<const float4*>(part + e);
-  for (int sp = 1; sp < splits; ++sp) {
-    const float4 w = *reinterpret_cast<const float4*>(part + (int64_t)sp * total + e);
-    v.x += w.x;
-    v.y += w.y;
-    v.z += w.z;
-    v.w += w.w;
+  for (int sb = 1; sb < splits; sb += 4) {
+    float4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (sb + j < splits) ? *reinterpret_cast<const float4*>(part + (int64_t)(sb + j) * total + e)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sb + j < splits) {
+        v.x += w[j].x;
+        v.y += w[j].y;
+        v.z += w[j].z;
+        v.w += w[j].w;
+      }
   }
   const int64_t row = e / N, col = e % N;
   float r[4] = {v.x, v.y, v.z, v.w};
@@ -1659,7 +1706,8 @@ size_t lora_down_ws_bytes(int M, int K, int rr) {
 
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
               int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(rr >= 1 && rr <= 64 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr, K);
+  LSQ_CHECK(rr >= 1 && rr <= 64 && K >= 32 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr,
+            K);
   if (M == 0) return LSQ_OK;
   LSQ_CHECK(ws && ws_bytes >= lora_down_ws_bytes(M, K, rr), LSQ_ERR_WORKSPACE, "lora_down: workspace too small");
   const int nch = (K + KCHUNK - 1) / KCHUNK;
@@ -1693,7 +1741,8 @@ size_t lora_g_ws_bytes(int M, int N, int r) {
 
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
            float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4, LSQ_ERR_SHAPE, "lora_g: bad rank/segments");
+  LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4 && N >= 8 && N % 8 == 0, LSQ_ERR_SHAPE,
+            "lora_g: bad rank/segments/N");
   if (M == 0) return LSQ_OK;
   LSQ_CHECK(ws && ws_bytes >= lora_g_ws_bytes(M, N, r), LSQ_ERR_WORKSPACE, "lora_g: workspace too small");
   int seg_of[128];
@@ -1891,6 +1940,8 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
                         const void* B, int32_t r, float scale, int32_t dtype, void* Y, void* U_out, void* ws,
                         size_t ws_bytes, void* stream) {
   if (int e = check_weight(W)) return e;
+  LSQ_CHECK(dtype == LSQ_F32 || W->n_out % 8 == 0, LSQ_ERR_SHAPE,
+            "linear: the bf16 kernels need n_out to be a multiple of 8 (got %lld)", (long long)W->n_out);
   LSQ_CHECK(X && A && B && Y, LSQ_ERR_INVALID, "linear_fwd: null pointer");
   LSQ_CHECK(dtype == LSQ_BF16 || dtype == LSQ_F32, LSQ_ERR_INVALID, "linear_fwd: bad dtype");
   LSQ_CHECK(M >= 0 && M < (1 << 30) && r >= 8 && r <= 64 && r % 8 == 0, LSQ_ERR_SHAPE,
@@ -1954,6 +2005,8 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
                         const void* B, int32_t r, float scale, int32_t dtype, const void* dY, void* dX, float* dA,
                         float* dB, int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_weight(W)) return e;
+  LSQ_CHECK(dtype == LSQ_F32 || W->n_out % 8 == 0, LSQ_ERR_SHAPE,
+            "linear: the bf16 kernels need n_out to be a multiple of 8 (got %lld)", (long long)W->n_out);
   LSQ_CHECK(X && A && B && dY && dX && dA && dB, LSQ_ERR_INVALID, "linear_bwd: null pointer");
   LSQ_CHECK(dtype == LSQ_BF16 || dtype == LSQ_F32, LSQ_ERR_INVALID, "linear_bwd: bad dtype");
   LSQ_CHECK(M >= 0 && M < (1 << 30) && r >= 8 && r <= 64 && r % 8 == 0, LSQ_ERR_SHAPE, "linear_bwd: bad M or r");

@@ -62,6 +62,20 @@ def test_nf4_shape_errors_enqueue_nothing(gpu):
     assert e.value.status == "LSQ_ERR_SHAPE"
 
 
+def test_bf16_linear_rejects_n_out_not_a_multiple_of_8(gpu):
+    """The bf16 kernels read rows of dY and B in 8-element chunks: n_out % 8 != 0
+    is refused before anything is enqueued (the float32 tier takes any n_out)."""
+    fake = C.c_void_p(256)
+    w = lib.Weight(lib.LSQ_W_NF4, 0, 256, 256, 12, 64)
+    for name, args in (("nf4_lora_linear_fwd", (None, fake, 4, fake, fake, 8, 2.0, lib.LSQ_BF16, fake, None,
+                                                  fake, 1 << 20, None)),
+                       ("nf4_lora_linear_bwd", (fake, None, 4, fake, fake, 8, 2.0, lib.LSQ_BF16, fake, fake, fake,
+                                                  fake, 0, fake, 1 << 20, None))):
+        with pytest.raises(lib.LsqError) as e:
+            lib.call(name, C.byref(w), *args)
+        assert e.value.status == "LSQ_ERR_SHAPE", name
+
+
 # whole and partial 2048-weight wave segments, down to a single 64-block
 @pytest.mark.parametrize("shape", [(1024, 512), (40, 320), (1, 64), (7, 4416)])
 def test_nf4_dequantize_bit_exact(gpu, shape):

@@ -543,6 +543,101 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
 }
 
+// ==================================== forward, bf16 weights, both operands by DMA
+// With nothing to decode there is no second half to ping-pong against: all
+// eight waves run MFMAs on the 256 x 256 tile (a 64 x 128 wave tile each), and
+// each wave copies 32 rows of both the X and the W tile of the next k-step
+// into the other LDS stage by DMA while it computes on the current one, with
+// one barrier per k-step.  The DMA lane mapping and swizzle are those of the
+// NF4 kernel above; the stages are again separate arrays named statically.
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_fwd_bf16_dma_kernel(FwdParams p) {
+  constexpr int BM = 256, BN = 256, WM = 64, WN = 128, TM = WM / 16, TN = WN / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+
+  const int K = p.K, nk_all = K / BK;
+  const int split = blockIdx.y;
+  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
+
+  // X rows [m0, M) and W rows [n0, N): rows past the end read as zeros.
+  const uint16_t* W = static_cast<const uint16_t*>(p.W);
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.X + (int64_t)m0 * p.ldx, (uint32_t)((p.M - m0) * p.ldx * 2));
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * K, (uint32_t)((int64_t)(p.N - n0) * K * 2));
+  // This wave's four 8-row blocks of each tile: rows [32 wave, 32 wave + 32).
+  const int row0 = wave * 32;
+  const int lchunk = ((lane & 7) ^ (lane >> 3)) * 8;
+  const uint32_t x_voff = (uint32_t)(((row0 + (lane >> 3)) * p.ldx + lchunk) * 2);
+  const uint32_t x_blk = (uint32_t)(8 * p.ldx * 2);
+  const uint32_t w_voff = (uint32_t)(((row0 + (lane >> 3)) * K + lchunk) * 2);
+  const uint32_t w_blk = (uint32_t)(8 * K * 2);
+  auto dma = [&](int kt, uint16_t* as, uint16_t* bs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rx, as + (row0 + i * 8) * 64, x_voff, (uint32_t)(kt * 128) + i * x_blk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rw, bs + (row0 + i * 8) * 64, w_voff, (uint32_t)(kt * 128) + i * w_blk);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mfma_step = [&](const uint16_t* as, const uint16_t* bs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[TM], bfr[TN];
+      const int chunk = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = lds_frag(as, swz(wm * WM + i * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = lds_frag(bs, swz(wn * WN + j * 16 + (lane & 15), chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // Stage 0 holds k-step kt at the top of each pair; the DMA into a stage is
+  // issued only after the barrier that closed the last reads of it.  A DMA
+  // past the last k-step is clamped to it and lands in a stage nobody reads.
+  if (kbeg < nk) dma(kbeg, As0, Bs0);
+  wait_vmcnt<0>();
+  lds_barrier();
+  int kt = kbeg;
+  // (sched_barrier keeps the compiler from sinking the DMA issue to the end
+  // of the MFMAs, right before its wait.)
+  for (; kt + 1 < nk; kt += 2) {
+    dma(kt + 1, As1, Bs1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(As0, Bs0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    dma(min(kt + 2, nk - 1), As0, Bs0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(As1, Bs1);
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+  if (kt < nk) mfma_step(As0, Bs0);
+
+  fwd_lora_up<TM, TN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+  fwd_store<TM, TN, EPI>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, split);
+}
+
 template <int TM, int TO, int EPI>
 __device__ __forceinline__ void bwd_store(const BwdParams& p, const f32x4 (&acc)[TM][TO], int r0, int c0, int lane,
                                           int split);
@@ -1519,19 +1614,26 @@ bool fwd_dma_ok(const FwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * (p.K / 2) < lim && p.ldx % 8 == 0;
 }
+bool fwd_bf16_dma_ok(const FwdParams& p) {
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * p.K * 2 < lim && p.ldx % 8 == 0;
+}
 bool bwd_dma_ok(const BwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
   return (int64_t)p.M * p.ldy * 2 < lim && ((int64_t)p.N + 64) * (p.K / 2) < lim && p.ldy % 8 == 0;
 }
 
-// The NF4 kernels take activations by DMA when their operands fit 32-bit
-// offsets; bf16 weights (and larger operands) use the register-path kernels.
+// The forward kernels take their operands by DMA when they fit 32-bit offsets
+// (the NF4 one its activations, the bf16 one both operands); larger operands
+// and the backward's bf16 weights use the register-path kernels.
 // e0, e1: the timing events attached to the dispatch (null when timing is off).
 template <int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + p.bn - 1) / p.bn);
   const dim3 grid(tiles, p.splits), block(512);
-  if (WK != LSQ_W_NF4 || !fwd_dma_ok(p))
+  if (WK == LSQ_W_BF16 && fwd_bf16_dma_ok(p))
+    hipExtLaunchKernelGGL(gemm_fwd_bf16_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
+  else if (WK != LSQ_W_NF4 || !fwd_dma_ok(p))
     hipExtLaunchKernelGGL(gemm_fwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
   else if (p.bn == 192)
     hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 192>, grid, block, 0, s, e0, e1, 0, p);

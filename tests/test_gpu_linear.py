@@ -242,9 +242,14 @@ def test_in_gemm_decode_is_the_dequantized_weight(gpu, M, K, N, dtype):
     assert np.array_equal(dX[:nn], Wd[:nn]) and not dX[nn:].any()
 
 
-def test_bf16_base_linear_matches_oracle(gpu):
-    M, K, N, r, s = 96, 256, 320, 16, 2.0
-    X, W, A, B, dY = _linear_inputs(M, K, N, r, 120)
+@pytest.mark.parametrize("M,K,N", [
+    # one tile; ragged rows and columns over several tiles; a reduction split
+    # several ways with an odd step count; a one-row M tail
+    (96, 256, 320), (300, 1024, 656), (64, 1600, 520), (513, 192, 264)])
+def test_bf16_base_linear_matches_oracle(gpu, M, K, N):
+    print_case(test="bf16_linear", M=M, K=K, N=N)
+    r, s = 16, 2.0
+    X, W, A, B, dY = _linear_inputs(M, K, N, r, 120 + M)
     Y, U, dX, dA, dB = _run_linear(X, None, None, A, B, dY, M, K, N, r, s, lib.LSQ_BF16, kind=lib.LSQ_W_BF16, wbf16=W)
     Wf, Xf, Af, Bf, dYf = (bits_f64(a) for a in (W, X, A, B, dY))
     rY, _ = olora.linear_fwd(Xf, Wf, Af, Bf, s)

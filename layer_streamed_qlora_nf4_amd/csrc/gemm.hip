@@ -888,8 +888,9 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
 // are decoded and written transposed, and the LoRA term G A joins in the
 // epilogue.  Weight rows past N read as zeros, which also cancels the dY
 // columns past N that the DMA brings in on the last reduction step.
-template <int EPI>
-__global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
+template <int WK, int EPI>
+__device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
+  constexpr bool NF4 = WK == LSQ_W_NF4;
   constexpr int BM = 256, BO = 256, WM = 64, WO = 128, TM = WM / 16, TO = WO / 16, GT = 256;
   static_assert((64 / 4) * (BO / 8) == 2 * GT, "one micro-tile per producer thread");
   __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
@@ -906,7 +907,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);   // column-major, as in the forward
   const int m0 = (t % tiles_m) * BM, o0 = (t / tiles_m) * BO;
-  if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
+  if (NF4 && tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K;
   const int nk_all = (p.N + BK - 1) / BK;
@@ -915,7 +916,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   const __amdgpu_buffer_rsrc_t ry = buffer_rsrc(p.dY + (int64_t)m0 * p.ldy, (uint32_t)((p.M - m0) * p.ldy * 2));
-  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.W, (uint32_t)((int64_t)p.N * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.W, (uint32_t)((int64_t)p.N * (NF4 ? K / 2 : 2 * K)));
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.absmax, (uint32_t)((int64_t)p.N * (K / 64) * 4));
 
   const int yrow0 = grp * 128 + wig * 32;
@@ -924,27 +925,39 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   int mrg, mq;
   bwd_mt_coords<BO>(grp * GT + gtid, mrg, mq);
   const int kcol = o0 + mq * 8;
-  const uint32_t w_voff = (uint32_t)(mrg * 4 * (K / 2) + kcol / 2);
+  const uint32_t w_voff = NF4 ? (uint32_t)(mrg * 4 * (K / 2) + kcol / 2) : (uint32_t)((mrg * 4 * K + kcol) * 2);
   const uint32_t s_voff = (uint32_t)((mrg * 4 * (K / 64) + kcol / 64) * 4);
-  const uint32_t w_step = (uint32_t)(64 * (K / 2)), w_row = (uint32_t)(K / 2);
+  const uint32_t w_row = NF4 ? (uint32_t)(K / 2) : (uint32_t)(2 * K), w_step = 64 * w_row;
   const uint32_t s_step = (uint32_t)(64 * (K / 64) * 4), s_row = (uint32_t)((K / 64) * 4);
 
   auto dma_y = [&](int kt, uint16_t* as) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(ry, as + (yrow0 + i * 8) * 64, y_voff, (uint32_t)(kt * 128) + i * y_blk);
   };
-  uint32_t rb[2][8];   // per set: codes of the micro-tile's 4 rows, then their absmax bits
+  // Per set: NF4, the codes of the micro-tile's 4 rows, then their absmax
+  // bits (8 loads); bf16, the 4 rows of 8 values (4 loads of 16 bytes).
+  constexpr int RB = NF4 ? 8 : 16, NLOAD = NF4 ? 8 : 4;
+  uint32_t rb[2][RB];
   auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      rb[set][rr] = __builtin_amdgcn_raw_buffer_load_b32(rw, w_voff, (uint32_t)kt * w_step + rr * w_row, 0);
-      rb[set][4 + rr] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)kt * s_step + rr * s_row, 0);
+      if constexpr (NF4) {
+        rb[set][rr] = __builtin_amdgcn_raw_buffer_load_b32(rw, w_voff, (uint32_t)kt * w_step + rr * w_row, 0);
+        rb[set][4 + rr] = __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)kt * s_step + rr * s_row, 0);
+      } else {
+        const uint4 v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, (uint32_t)kt * w_step + rr * w_row, 0));
+        rb[set][4 * rr] = v.x;
+        rb[set][4 * rr + 1] = v.y;
+        rb[set][4 * rr + 2] = v.z;
+        rb[set][4 * rr + 3] = v.w;
+      }
     }
   };
   auto store_b = [&](uint16_t* bt, int set) __attribute__((always_inline)) {
     int q = mq;
     asm volatile("" : "+v"(q));
-    bwd_store_mt<true, 8>(bt, mrg, q, rb[set], lut);
+    bwd_store_mt<NF4, RB>(bt, mrg, q, rb[set], lut);
   };
 
   f32x4 acc[TM][TO];
@@ -982,7 +995,7 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
   auto decode_half = [&](int kt, uint16_t* bn, int set) __attribute__((always_inline)) {
     load_b(min(kt + 2, nk - 1), set);
     store_b(bn, set ^ 1);
-    wait_vmcnt<8>();
+    wait_vmcnt<NLOAD>();
     lds_barrier();
   };
   auto last_mfma = [&](const uint16_t* as, const uint16_t* bt) __attribute__((always_inline)) {
@@ -1034,6 +1047,17 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
 
   bwd_lora_up<TM, TO>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
   bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
+  gemm_bwd_dma_body<LSQ_W_NF4, EPI>(p);
+}
+// The same schedule over bf16 weights: each producer thread copies (instead
+// of decoding) its 4 x 8 micro-tile and writes it transposed.
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) gemm_bwd_bf16_dma_kernel(BwdParams p) {
+  gemm_bwd_dma_body<LSQ_W_BF16, EPI>(p);
 }
 
 // v + p[k0 * stride] + ... + p[(k1 - 1) * stride], added in k order.  The
@@ -1620,7 +1644,8 @@ bool fwd_bf16_dma_ok(const FwdParams& p) {
 }
 bool bwd_dma_ok(const BwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
-  return (int64_t)p.M * p.ldy * 2 < lim && ((int64_t)p.N + 64) * (p.K / 2) < lim && p.ldy % 8 == 0;
+  const int64_t row_bytes = p.kind == LSQ_W_NF4 ? p.K / 2 : 2 * (int64_t)p.K;
+  return (int64_t)p.M * p.ldy * 2 < lim && ((int64_t)p.N + 64) * row_bytes < lim && p.ldy % 8 == 0;
 }
 
 // The forward kernels take their operands by DMA when they fit 32-bit offsets
@@ -1647,6 +1672,8 @@ void launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
   const dim3 grid(tiles, p.splits), block(512);
   if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
     hipExtLaunchKernelGGL(gemm_bwd_nf4_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
+  else if (WK == LSQ_W_BF16 && bwd_dma_ok(p))
+    hipExtLaunchKernelGGL(gemm_bwd_bf16_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
   else
     hipExtLaunchKernelGGL(gemm_bwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
 }

@@ -319,6 +319,19 @@ def copy_calibration(torch, nbytes=1 << 30):
     print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}))
 
 
+def blas_info():
+    """The BLAS library NumPy calls and the threads it runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        for pool in threadpool_info():
+            if pool.get("user_api") == "blas":
+                return {"library": pool.get("internal_api"), "version": pool.get("version"),
+                        "threads": pool.get("num_threads")}
+    except Exception as e:   # report, never fail the bench over it
+        return {"library": None, "error": str(e)}
+    return {"library": None}
+
+
 def cpu_baseline(cfg):
     """The oracle timed on this host: one decoder layer forward plus its
     backward (with recompute) at the workload's token count, scaled to the
@@ -366,11 +379,14 @@ def cpu_baseline(cfg):
     t4 = time.perf_counter()
     step_s = cfg.n_layers * (fwd_s + bwd_s) / reps + (t4 - t3)
     try:
-        cores = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(cfg.tokens / step_s, 3), "unit": "tok/s", "cores": min(cores, threads), "kind": "oracle",
+        host_cores = os.cpu_count()
+    blas = blas_info()
+    # the oracle's time is NumPy's BLAS calls: the threads they ran on are the cores it used
+    used = min(host_cores, blas["threads"]) if blas.get("threads") else host_cores
+    return {"value": round(cfg.tokens / step_s, 3), "unit": "tok/s", "cores": used, "host_cores": host_cores,
+            "blas": blas, "kind": "oracle",
             "sample": (f"one {cfg.name} decoder layer forward ({fwd_s / reps:.2f} s) and backward with recompute "
                        f"({bwd_s / reps:.2f} s) in float64 at {B}x{S} tokens, averaged over {reps} runs and "
                        f"times {cfg.n_layers} layers, plus the head and cross-entropy ({t4 - t3:.1f} s); "
@@ -497,7 +513,10 @@ def main():
     prof = {e.name.decode(): dict(launches=e.launches, ms=e.ms, flops=e.flops, bytes=e.bytes) for e in entries[:n.value]}
     # the dominant MFMA-bound family by time, priced at the peak of the MFMA type it runs on
     peaks = {"gemm_fwd_nf4_lora": MFMA_BF16_PEAK_TFLOPS, "gemm_bwd_nf4_lora": MFMA_BF16_PEAK_TFLOPS,
-             "gemm_bf16_weights": MFMA_BF16_PEAK_TFLOPS, "attention": MFMA_F32_PEAK_TFLOPS}
+             "gemm_bf16_weights": MFMA_BF16_PEAK_TFLOPS,
+             # attention runs on bf16 MFMAs; its flops are the algorithmic ones
+             # (the hi/lo operand passes are extra work, not credited)
+             "attention": MFMA_BF16_PEAK_TFLOPS}
     dominant = max(peaks, key=lambda k: prof[k]["ms"])
     d = prof[dominant]
     peak = peaks[dominant]

@@ -393,9 +393,17 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
  * sequence length and refuse before any GPU work if it does not fit (LS-docs
  * "Turn it on"; "Troubleshooting": the terms streaming does not bound are the
  * activations and logits).  The prediction is the sum of the buffers this
- * library asks the caller to allocate, plus the caller-declared overhead. */
+ * library asks the caller to allocate (the pool's slots at their 4 KiB stride,
+ * the resident tensors, adapters and their gradients, the step workspace), the
+ * caller's own step tensors, and a margin, so that it errs high like the
+ * pages' pre-flight (LS-docs "Run it yourself on a free Colab T4": 3.02 GB
+ * predicted against 2.91 GB measured). */
 typedef struct {
-  uint64_t slots, resident, adapters, checkpoints, saved_activations, step_workspace, total;
+  uint64_t slots, resident, adapters, checkpoints, saved_activations, step_workspace;
+  uint64_t caller;   /* the token ids and the loss scalar, plus up to 511 bytes of
+                        allocator rounding for each of the step's 16 buffers     */
+  uint64_t margin;   /* 1% of the sum above (at least 1 MiB): allocator slack     */
+  uint64_t total;
 } lsq_vram_breakdown;
 /* step_flags: the flags the step will run with (kept activations are a term
  * of their own). */

@@ -903,7 +903,7 @@ int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int3
   lsq_lora_layout LL;
   lora_layout(cfg, &LL);
   const uint64_t T = (uint64_t)batch * seq, H = cfg->hidden;
-  out->slots = (uint64_t)n_buffers * BL.total_bytes;
+  out->slots = (uint64_t)n_buffers * up(BL.total_bytes, 4096);   // layer_pool_create's slot stride
   // large-layer streaming keeps the embedding and head in host memory (the
   // head's per-step device copy is part of the step workspace)
   out->resident = (step_flags & LSQ_STEP_STREAM_LARGE) ? 2 * H : 2ull * cfg->vocab * H * (cfg->tied ? 1 : 2) + 2 * H;
@@ -912,8 +912,14 @@ int vram_predict_peak(const lsq_model_cfg* cfg, int32_t batch, int32_t seq, int3
   const StepWs sw = carve_step(cfg, batch, seq, nullptr, step_flags);
   out->saved_activations = (uint64_t)sw.acts_bytes * sw.n_kept;
   out->step_workspace = sw.total - out->checkpoints - out->saved_activations;
-  out->total = out->slots + out->resident + out->adapters + out->checkpoints + out->saved_activations +
-               out->step_workspace + 4 * T + 64;
+  // token ids and the loss scalar; each of the step's buffers (slots, embedding,
+  // head, final norm, adapters, gradients, workspace, ids, loss and a few more
+  // of the caller's) may be rounded up by the allocator, at most 511 bytes each
+  out->caller = 4 * T + 4 + 16 * 511;
+  const uint64_t sum = out->slots + out->resident + out->adapters + out->checkpoints + out->saved_activations +
+                       out->step_workspace + out->caller;
+  out->margin = std::max<uint64_t>(sum / 100, 1ull << 20);
+  out->total = sum + out->margin;
   return LSQ_OK;
 }
 

@@ -79,7 +79,7 @@ class StepExtra(C.Structure):
 class VramBreakdown(C.Structure):
     _fields_ = [("slots", C.c_uint64), ("resident", C.c_uint64), ("adapters", C.c_uint64),
                 ("checkpoints", C.c_uint64), ("saved_activations", C.c_uint64), ("step_workspace", C.c_uint64),
-                ("total", C.c_uint64)]
+                ("caller", C.c_uint64), ("margin", C.c_uint64), ("total", C.c_uint64)]
 
 
 class ProfEntry(C.Structure):

@@ -69,6 +69,23 @@ class Store:
         return self
 
     @classmethod
+    def blank(cls, cfg, flags=0):
+        """A store of the right shape whose blobs are all zero bytes (weights of
+        zero): a step over it allocates and launches exactly what a step over
+        real weights does, without the cost of drawing and quantizing them."""
+        self = cls.__new__(cls)
+        self.cfg = cfg
+        self.ccfg = lib.model_cfg(cfg)
+        h = C.c_void_p()
+        lib.call("shard_store_create", C.byref(self.ccfg), flags, C.byref(h))
+        self.handle = h
+        self.layer_bytes = int(lib.raw("shard_store_layer_bytes")(h))
+        self.pinned = bool(lib.raw("shard_store_is_pinned")(h))
+        for i in range(cfg.n_layers):
+            C.memset(lib.raw("shard_store_layer_host")(h, i), 0, self.layer_bytes)
+        return self
+
+    @classmethod
     def copy_of(cls, other, flags):
         """Another arena (e.g. pageable) holding the same blobs, byte for byte."""
         self = cls.__new__(cls)
@@ -143,9 +160,17 @@ class Resident:
     streaming: the step reads the batch's embedding rows in place and copies
     the head in once per step)."""
 
-    def __init__(self, cfg, device="cuda", large_in_host=False):
+    def __init__(self, cfg, device="cuda", large_in_host=False, blank=False):
         self.cfg = cfg
         self.large_in_host = large_in_host
+        if blank:   # zeros of the same shapes (memory and launch tests)
+            z = (lambda *shape: torch.zeros(shape, dtype=torch.int16, device=device))
+            self.embed = z(cfg.vocab, cfg.hidden)
+            self.head = self.embed if cfg.tied else z(cfg.vocab, cfg.hidden)
+            self.final_norm = z(cfg.hidden)
+            self.lora = z(cfg.n_layers, lib.lora_layout(cfg).layer_elems)
+            self.layer_elems = self.lora.shape[1]
+            return
         rw = synth.resident_weights(cfg, cfg.wid)
         if large_in_host:
             assert not cfg.tied, "a tied embedding stays resident"

@@ -1,5 +1,6 @@
 """Helpers for the GPU parity tests: device buffers from seeded host arrays."""
 import ctypes as C
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -43,3 +44,18 @@ def rel_err(got, ref):
 
 def print_case(**kw):
     print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def row_blocks(fn, *arrays, threads=16):
+    """fn applied to row blocks of the arrays on a thread pool, results stacked
+    by rows.  Quantizing and dequantizing are row-local (a 64-block never
+    crosses a row), so this is the same result as one call on the whole
+    arrays; it only spreads the oracle's work over the host's cores."""
+    n = arrays[0].shape[0]
+    step = max(1, -(-n // (4 * threads)))
+    starts = list(range(0, n, step))
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda r0: fn(*(a[r0:r0 + step] for a in arrays)), starts))
+    if isinstance(parts[0], tuple):
+        return tuple(np.concatenate([p[i] for p in parts]) for i in range(len(parts[0])))
+    return np.concatenate(parts)

@@ -390,3 +390,28 @@ def test_timeline_orders_copies_before_their_layer_passes(gpu):
             last_copy_end[l] = b
         elif k in (lib.LSQ_TL_FWD, lib.LSQ_TL_BWD) and l in last_copy_end:
             assert a >= last_copy_end[l] - eps, (k, l, a, last_copy_end[l])
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY.with_(name="tiny-5L-3buf", n_layers=5, n_buffers=3,
+                                                                   wid=13)])
+def test_poisoned_slots_stream_identically(gpu, cfg):
+    """LSQ_POOL_POISON fills a slot with 0xFF bytes (NaN absmax, NaN bf16)
+    before each refill: any read of a slot before its copy lands would turn
+    into NaNs.  Two steps over poisoned slots equal the resident run bit for
+    bit, and every refill was poisoned (the copy count)."""
+    print_case(test="poisoned_slots", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    resident = run(cfg, "resident", store, res, ids)
+    r = model.Runner(cfg, store, res, pool_flags=lib.LSQ_POOL_POISON)
+    logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        loss = r.step(ids, logits=logits).item()
+        torch.cuda.synchronize()
+        got = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy())
+        exact, total = _compare_bitwise(cfg, resident, got)
+        assert exact == total == cfg.n_layers * 14
+    assert r.stats().copies == (2 * cfg.n_layers - cfg.n_buffers) + (2 * cfg.n_layers - 2 * cfg.n_buffers)
+    r.close()
+    store.close()

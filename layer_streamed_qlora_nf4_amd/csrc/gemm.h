@@ -25,7 +25,10 @@ struct FwdParams {
   int kind;
   const void* W;
   const float* absmax;
-  int M, N, K;
+  int M, N, K;           // K: the reduction length over X's columns
+  int Kw;                // the weight's columns: K, or K / 2 for X = [X_hi | X_lo], whose
+                         // reduction steps past Kw read the weight again from column 0
+                         // (Y = X_hi W^T + X_lo W^T); 0 means K
   const uint16_t* U;     // scaled down-projection, bf16 [M, ldu]; unused when r == 0
   int ldu;
   const uint16_t* Bl;    // [N, r]
@@ -54,7 +57,7 @@ struct BwdParams {
   int64_t ldg;
   const uint16_t* Al;    // stacked A, bf16 [rr, K]
   int rr;
-  const uint16_t* AlT;   // Al transposed [K, rr] (workspace; set by gemm_bwd)
+  const uint16_t* AlT;   // Al transposed [K, rr]: the LoRA term's operand (required when rr > 0)
   const float* resid;
   void* out;
   int64_t ldc;
@@ -80,57 +83,50 @@ size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr);
 // ws: split-K partial buffer (>= the *_ws_bytes query), may be null when that is 0.
 int gemm_fwd(const FwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
 int gemm_bwd(const BwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
-// Reduction chunks of lora_g, each inside one segment.
-struct GChunks {
-  int begin[128], end[128];
-  int n;
-};
+// ------------------------------------------------------------ rank-r kernels (lora.hip)
+// Each product is one launch; where its reduction is split over workgroups,
+// the last workgroup of a group to arrive sums the group's float32 partials
+// in a fixed order.  cnt: that launch's arrival counters, which must be zero
+// when it starts and are zero again when it ends (zero_counters once per
+// workspace use; every launch leaves them as it found them).
+size_t counters_bytes(int n);
+int zero_counters(int* cnt, int n, hipStream_t s);
 
-// U[M, rr] = bf16(s X A^T), A = stacked [rr, K]; ws holds the chunk partials.
-// U32 (nullable, ld ldu32) receives the same values before the bf16 rounding.
+// U[M, rr] = bf16(s X A^T), A = stacked [rr, K]; U32 (nullable, ld ldu32)
+// receives the same values before the bf16 rounding.
+int lora_down_counters(int M);
 size_t lora_down_ws_bytes(int M, int K, int rr);
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, hipStream_t st);
-// G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]); ws holds B transposed and partials.
+              int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, int* cnt, hipStream_t st);
+// G[M, s*r .. s*r + r) = bf16(s dY[:, seg s] B[seg s rows]) from Bt = B^T [r, N];
 // G32 (nullable, ld ldg32) receives the unrounded values.
+int lora_g_counters(int M, int nseg);
 size_t lora_g_ws_bytes(int M, int N, int r);
-int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, hipStream_t st);
-// One reduction over the token dimension, C = S^T L: S [M, ns] float32 (ns <=
-// 64, a multiple of 8), L [M, nl] bf16; small_rows: out [ns, nl] (dA); else
-// out [nl, ns] (dB).  The small side is the unrounded U or G.
-struct TnTask {
-  const float* S;
-  int64_t lds;
-  int ns;
-  const uint16_t* L;
-  int64_t ldl;
-  int nl;
-  float* out;
-  int64_t ldo;
-  int small_rows;
-  int tile0;          // set by lora_grads
-  int64_t part_off;   // set by lora_grads: this task's float32 partials in the workspace
+int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* Bt, int r, int nseg, const SegEnds& segs,
+           float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, int* cnt,
+           hipStream_t st);
+// The adapter gradients of one linear group over the token dimension, from
+// the unrounded float32 G and U: dA [nseg r, Kx] = G^T X (rows of the stacked
+// group) and, per segment s of dY's columns, dB[seg rows] = dY_seg^T U_seg.
+struct GradGroup {
+  const float* G;
+  int64_t ldg;
+  const float* U;
+  int64_t ldu;
+  const uint16_t* X;
+  int64_t ldx;
+  const uint16_t* dY;
+  int64_t ldy;
+  int Kx, r, nseg;
+  int seg_end[3];
+  float* gA;
+  float* gB;
 };
-struct TnBatch {
-  TnTask t[8];
-  int ntasks, M, accumulate;
-  int splits, per;    // token ranges of `per` tokens (a multiple of 64); splits > 1 writes partials
-  float* part;
-};
-struct SegFinish {
-  int c0[4], c1[4], col[4];
-  int n;
-};
-// Every task of one group in one launch.  Launches with few column tiles
-// split the tokens into ranges whose float32 partials are summed in range
-// order by a second kernel (a pure function of the shapes; fixed order).
-size_t lora_grads_ws_bytes(const TnTask* tasks, int ntasks, int M);
-int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, float* ws, size_t ws_bytes, hipStream_t st);
-
-// Token-dimension reduction C = S^T L (small_rows: [ns, nl]; else [nl, ns]).
-size_t lora_tn_ws_bytes(int M, int ns, int nl);
-int lora_tn(const float* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
-            float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st);
+int lora_grads_counters(int Kx, int r, int nseg, const int* seg_end);
+size_t lora_grads_ws_bytes(int Kx, int r, int nseg, const int* seg_end, int M);
+int lora_grads(const GradGroup& g, int M, int accumulate, float* ws, size_t ws_bytes, int* cnt, hipStream_t st);
+// The adapters of n_layers consecutive layers transposed block by block
+// (A [rr, K] -> [K, rr], B [N, r] -> [r, N]) into the same offsets of lora_t.
+int adapter_transpose(const lsq_model_cfg* c, const uint16_t* lora, uint16_t* lora_t, int n_layers, hipStream_t st);
 
 }  // namespace lsq

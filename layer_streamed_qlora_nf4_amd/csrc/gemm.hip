@@ -53,12 +53,22 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// XCD-aware tile order: consecutive workgroup ids go to different XCDs, so
-// hand each XCD a contiguous range of tiles (row-major over M tiles): the
-// tiles one XCD runs together share their activation rows in its L2.
-__device__ __forceinline__ int remap_tile(int g, int total) {
-  if ((total & 7) != 0) return g;
-  return (g & 7) * (total >> 3) + (g >> 3);
+// XCD-aware work order.  Workgroups are handed to the 8 XCDs round-robin in
+// dispatch order (x fastest), and each XCD has its own L2.  A launch of
+// `tiles` output tiles x `splits` reduction ranges is therefore renumbered so
+// that each XCD receives one contiguous run of (split, tile) pairs in
+// split-major order: with one range, a run of neighbouring tiles (column-major,
+// so the tiles that share a weight slab read it into one L2); with several,
+// the tiles of one reduction range, whose activation and weight columns then
+// leave HBM once instead of once per XCD.
+struct TileSplit {
+  int tile, split;
+};
+__device__ __forceinline__ TileSplit xcd_order(int tiles, int splits) {
+  const int g = blockIdx.x + blockIdx.y * gridDim.x;
+  const int total = tiles * splits;
+  const int v = (total & 7) ? g : (g & 7) * (total >> 3) + (g >> 3);
+  return TileSplit{v % tiles, v / tiles};
 }
 
 // Decode 8 packed bytes' worth... one 32-bit word = 8 NF4 codes (bytes in
@@ -219,12 +229,13 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
   const int wm = grp * 2 + ((wave >> 1) & 1), wn = wave & 1;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const TileSplit ts = xcd_order(tiles_m * tiles_n, p.splits);
+  const int t = ts.tile;
   const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
   if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
-  const int K = p.K, nk_all = K / BK;
-  const int split = blockIdx.y;
+  const int K = p.K, nk_all = K / BK, Kw = p.Kw, nkw = Kw / BK;
+  const int split = ts.split;
   const int per = (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
@@ -242,21 +253,23 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_pp_kernel(FwdParams p) {
       ra[i] = (m < p.M) ? *reinterpret_cast<const uint4*>(p.X + (int64_t)m * p.ldx + k0 + c * 8)
                         : make_uint4(0, 0, 0, 0);
     }
+    const int kq = kt - (kt >= nkw ? nkw : 0), kq0 = kq * BK;   // the weight's reduction step
     if (WKIND == LSQ_W_NF4) {
       const uint8_t* W = static_cast<const uint8_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
         const int q = gt + i * GT, n = n0 + arow0 + (q >> 1), h = q & 1;
         const bool ok = n < p.N;
-        rb[i] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * (K / 2) + k0 / 2 + h * 16) : make_uint4(0, 0, 0, 0);
-        rabs[i] = ok ? p.absmax[(int64_t)n * (K / 64) + kt] : 0.f;
+        rb[i] = ok ? *reinterpret_cast<const uint4*>(W + (int64_t)n * (Kw / 2) + kq0 / 2 + h * 16)
+                   : make_uint4(0, 0, 0, 0);
+        rabs[i] = ok ? p.absmax[(int64_t)n * (Kw / 64) + kq] : 0.f;
       }
     } else {
       const uint16_t* W = static_cast<const uint16_t*>(p.W);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
         const int q = gt + i * GT, n = n0 + arow0 + (q >> 3), c = q & 7;
-        rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * K + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+        rb[i] = (n < p.N) ? *reinterpret_cast<const uint4*>(W + (int64_t)n * Kw + kq0 + c * 8) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -394,21 +407,22 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_m = (p.M + BM - 1) / BM;
   // Column-major tile order: the M tiles that share a weight slab are
-  // neighbours, so remap_tile puts them on one XCD and the slab leaves HBM once.
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  // neighbours, so xcd_order puts them on one XCD and the slab leaves HBM once.
+  const TileSplit ts = xcd_order(tiles_m * tiles_n, p.splits);
+  const int t = ts.tile;
   const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
 
-  const int K = p.K, nk_all = K / BK;
-  const int split = blockIdx.y;
+  const int K = p.K, nk_all = K / BK, Kw = p.Kw, nkw = Kw / BK;
+  const int split = ts.split;
   const int per = (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   // X rows [m0, M), packed codes and absmax of weight rows [n0, N).
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.X + (int64_t)m0 * p.ldx, (uint32_t)((p.M - m0) * p.ldx * 2));
   const __amdgpu_buffer_rsrc_t rw =
-      buffer_rsrc(static_cast<const uint8_t*>(p.W) + (int64_t)n0 * (K / 2), (uint32_t)((p.N - n0) * (K / 2)));
+      buffer_rsrc(static_cast<const uint8_t*>(p.W) + (int64_t)n0 * (Kw / 2), (uint32_t)((p.N - n0) * (Kw / 2)));
   const __amdgpu_buffer_rsrc_t rs =
-      buffer_rsrc(p.absmax + (int64_t)n0 * (K / 64), (uint32_t)((p.N - n0) * (K / 64) * 4));
+      buffer_rsrc(p.absmax + (int64_t)n0 * (Kw / 64), (uint32_t)((p.N - n0) * (Kw / 64) * 4));
 
   // This wave's four 8-row blocks of its group's 128 X rows.
   const int xrow0 = grp * 128 + wig * 32;
@@ -417,8 +431,8 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   // This thread's 32 codes (row, half of the 64-wide block) and their scale.
   const bool bact = BN == 256 || gtid < BN;
   const int brow = grp * WN + (bact ? (gtid >> 1) : WN - 1), bh = gtid & 1;
-  const uint32_t w_voff = (uint32_t)(brow * (K / 2) + bh * 16);
-  const uint32_t s_voff = (uint32_t)(brow * (K / 64) * 4);
+  const uint32_t w_voff = (uint32_t)(brow * (Kw / 2) + bh * 16);
+  const uint32_t s_voff = (uint32_t)(brow * (Kw / 64) * 4);
 
   auto dma_x = [&](int kt, uint16_t* as) __attribute__((always_inline)) {
 #pragma unroll
@@ -429,8 +443,9 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   uint4 rb[2];
   float rab[2];
   auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
-    rb[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, (uint32_t)(kt * 32), 0));
-    rab[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)(kt * 4), 0));
+    const int kq = kt - (kt >= nkw ? nkw : 0);   // the weight's reduction step
+    rb[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, (uint32_t)(kq * 32), 0));
+    rab[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)(kq * 4), 0));
   };
   auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) {
     const uint32_t words[4] = {rb[set].x, rb[set].y, rb[set].z, rb[set].w};
@@ -563,30 +578,32 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_bf16_dma_kernel(FwdParams p) 
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_n);
+  const TileSplit ts = xcd_order(tiles_m * tiles_n, p.splits);
+  const int t = ts.tile;
   const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
 
-  const int K = p.K, nk_all = K / BK;
-  const int split = blockIdx.y;
+  const int K = p.K, nk_all = K / BK, Kw = p.Kw, nkw = Kw / BK;
+  const int split = ts.split;
   const int per = (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   // X rows [m0, M) and W rows [n0, N): rows past the end read as zeros.
   const uint16_t* W = static_cast<const uint16_t*>(p.W);
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.X + (int64_t)m0 * p.ldx, (uint32_t)((p.M - m0) * p.ldx * 2));
-  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * K, (uint32_t)((int64_t)(p.N - n0) * K * 2));
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W + (int64_t)n0 * Kw, (uint32_t)((int64_t)(p.N - n0) * Kw * 2));
   // This wave's four 8-row blocks of each tile: rows [32 wave, 32 wave + 32).
   const int row0 = wave * 32;
   const int lchunk = ((lane & 7) ^ (lane >> 3)) * 8;
   const uint32_t x_voff = (uint32_t)(((row0 + (lane >> 3)) * p.ldx + lchunk) * 2);
   const uint32_t x_blk = (uint32_t)(8 * p.ldx * 2);
-  const uint32_t w_voff = (uint32_t)(((row0 + (lane >> 3)) * K + lchunk) * 2);
-  const uint32_t w_blk = (uint32_t)(8 * K * 2);
+  const uint32_t w_voff = (uint32_t)(((row0 + (lane >> 3)) * Kw + lchunk) * 2);
+  const uint32_t w_blk = (uint32_t)(8 * Kw * 2);
   auto dma = [&](int kt, uint16_t* as, uint16_t* bs) __attribute__((always_inline)) {
+    const int kq = kt - (kt >= nkw ? nkw : 0);   // the weight's reduction step
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(rx, as + (row0 + i * 8) * 64, x_voff, (uint32_t)(kt * 128) + i * x_blk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rw, bs + (row0 + i * 8) * 64, w_voff, (uint32_t)(kt * 128) + i * w_blk);
+    for (int i = 0; i < 4; ++i) dma16(rw, bs + (row0 + i * 8) * 64, w_voff, (uint32_t)(kq * 128) + i * w_blk);
   };
 
   f32x4 acc[TM][TN];
@@ -772,13 +789,14 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
   const int wm = grp * 2 + ((wave >> 1) & 1), wo = wave & 1;
   const int tiles_o = (p.K + BO - 1) / BO;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);
+  const TileSplit ts = xcd_order(tiles_m * tiles_o, p.splits);
+  const int t = ts.tile;
   const int m0 = (t / tiles_o) * BM, o0 = (t % tiles_o) * BO;
   if (tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K;
   const int nk_all = (p.N + BK - 1) / BK;   // the LoRA term is added after the main loop
-  const int split = blockIdx.y;
+  const int split = ts.split;
   const int per = (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
@@ -905,13 +923,14 @@ __device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
   const int wm = grp * 2 + ((wave >> 1) & 1), wo = wave & 1;
   const int tiles_o = (p.K + BO - 1) / BO;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int t = remap_tile(blockIdx.x, tiles_m * tiles_o);   // column-major, as in the forward
+  const TileSplit ts = xcd_order(tiles_m * tiles_o, p.splits);
+  const int t = ts.tile;   // column-major, as in the forward
   const int m0 = (t % tiles_m) * BM, o0 = (t / tiles_m) * BO;
   if (NF4 && tid < 16) lut[tid] = kNF4LevelsDev[tid];
 
   const int K = p.K;
   const int nk_all = (p.N + BK - 1) / BK;
-  const int split = blockIdx.y;
+  const int split = ts.split;
   const int per = (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
@@ -1060,91 +1079,6 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_bf16_dma_kernel(BwdParams p) 
   gemm_bwd_dma_body<LSQ_W_BF16, EPI>(p);
 }
 
-// v + p[k0 * stride] + ... + p[(k1 - 1) * stride], added in k order.  The
-// loads go out eight at a time before any add: a loop with a run-time bound
-// otherwise waits for each load before issuing the next.
-__device__ __forceinline__ float ordered_sum(float v, const float* __restrict__ p, int64_t stride, int k0, int k1) {
-  for (int kb = k0; kb < k1; kb += 8) {
-    float t[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = (kb + j < k1) ? p[(int64_t)(kb + j) * stride] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (kb + j < k1) v += t[j];
-  }
-  return v;
-}
-
-// =========================================================== LoRA down: U = s X A^T
-// Grid (M / 16 row blocks, K / 512 chunks): each workgroup's 4 waves take 128
-// of its chunk's columns each and sum their 16 x rr tiles in wave order; the
-// chunk partials are then summed in chunk order by lora_finish_kernel.
-constexpr int KCHUNK = 512;
-__global__ void __launch_bounds__(NTHREADS) lora_down_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M, int K,
-                                                             const uint16_t* __restrict__ A, int rr,
-                                                             float* __restrict__ part) {
-  __shared__ float red[4][16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 16, chunk = blockIdx.y;
-  const int nct = (rr + 15) / 16;
-  const int kb = chunk * KCHUNK + wave * (KCHUNK / 4), ke = min(K, kb + KCHUNK / 4);
-  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-  const int row = m0 + (lane & 15);
-  const int g = lane >> 4;
-  // four 32-wide steps per wave; steps past this wave's range read zeros.
-  // Every load of the wave is issued before the first MFMA (addresses are
-  // clamped into the operands and the values masked afterwards).
-  constexpr int NS = KCHUNK / 4 / 32;
-  uint4 av[NS], bv[NS][4];
-  const int rowc = min(row, M - 1);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int kk = kb + 32 * i + 8 * g, kkc = min(kk, K - 8);
-    const bool kin = kk < ke;
-    const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)rowc * ldx + kkc);
-    av[i] = (row < M && kin) ? x : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= nct) break;
-      const int c = ct * 16 + (lane & 15);
-      const uint4 a = *reinterpret_cast<const uint4*>(A + (int64_t)min(c, rr - 1) * K + kkc);
-      bv[i][ct] = (c < rr && kin) ? a : make_uint4(0, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= nct) break;
-      acc[ct] = mfma16(u4_as_frag(av[i]), u4_as_frag(bv[i][ct]), acc[ct]);
-    }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct >= nct) break;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
-  }
-  __syncthreads();
-  float* out = part + (int64_t)chunk * M * rr;
-  for (int e = tid; e < 16 * rr; e += NTHREADS) {
-    const int r = e / rr, c = e % rr;
-    if (m0 + r >= M) continue;
-    out[(int64_t)(m0 + r) * rr + c] = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
-  }
-}
-
-// dst[m, col0 + c] = bf16(s * sum over chunks of part[chunk, m, c]) for c < w
-__global__ void lora_finish_kernel(const float* __restrict__ part, int nchunks, int M, int w, float s,
-                                   uint16_t* __restrict__ dst, int64_t ld, float* __restrict__ dst32, int64_t ld32) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)M * w) return;
-  const int64_t m = e / w, c = e % w;
-  float v = ordered_sum(0.f, part + e, (int64_t)M * w, 0, nchunks);
-  v *= s;
-  dst[m * ld + c] = f32_to_bf16_bits(v);
-  if (dst32) dst32[m * ld32 + c] = v;
-}
-
 __global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, int64_t n, float* __restrict__ dst) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e < n) dst[e] = bf16_bits_to_f32(src[e]);
@@ -1160,373 +1094,6 @@ __global__ void transpose_rows_kernel(const uint16_t* __restrict__ B, int N, int
   Bt[e] = B[n * r + j];
 }
 
-// =========================================================== LoRA G = s dY_seg B_seg
-// Grid (M / 16 row blocks, chunks of 512 reduction columns within one segment).
-__global__ void __launch_bounds__(NTHREADS) lora_g_kernel(const uint16_t* __restrict__ dY, int64_t ldy, int M, int N,
-                                                          const uint16_t* __restrict__ Bt, int r, GChunks ch,
-                                                          float* __restrict__ part) {
-  __shared__ float red[4][16][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.x * 16, chunk = blockIdx.y;
-  const int row = m0 + (lane & 15), g = lane >> 4;
-  const int nct = (r + 15) / 16;
-  const int cb = ch.begin[chunk], ce = ch.end[chunk];
-  const int kb = cb + wave * (KCHUNK / 4), ke = min(ce, kb + KCHUNK / 4);
-  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-  // all loads first, as in lora_down_kernel
-  constexpr int NS = KCHUNK / 4 / 32;
-  uint4 av[NS], bv[NS][4];
-  const int rowc = min(row, M - 1);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int kk = kb + 32 * i + 8 * g, kkc = min(kk, N - 8);
-    const bool kin = kk < ke;
-    const uint4 y = *reinterpret_cast<const uint4*>(dY + (int64_t)rowc * ldy + kkc);
-    av[i] = (row < M && kin) ? y : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= nct) break;
-      const int c = ct * 16 + (lane & 15);
-      const uint4 b = *reinterpret_cast<const uint4*>(Bt + (int64_t)min(c, r - 1) * N + kkc);
-      bv[i][ct] = (c < r && kin) ? b : make_uint4(0, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= nct) break;
-      acc[ct] = mfma16(u4_as_frag(av[i]), u4_as_frag(bv[i][ct]), acc[ct]);
-    }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct >= nct) break;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
-  }
-  __syncthreads();
-  float* out = part + (int64_t)chunk * M * r;
-  for (int e = tid; e < 16 * r; e += NTHREADS) {
-    const int rr = e / r, c = e % r;
-    if (m0 + rr >= M) continue;
-    out[(int64_t)(m0 + rr) * r + c] = ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c];
-  }
-}
-
-// =========================================================== LoRA weight grads
-// C = S^T L over the token dimension M: S [M, ns], L [M, nl] (bf16).
-// SMALL_ROWS: C[ns, nl] row-major (dA = G^T X);  else C[nl, ns] (dB = dY^T U).
-// Grid (nl / 256 column tiles, token splits, ns / 16 slices).  A thread owns 4
-// adjacent columns x 16 small indices (64 accumulators) and walks its wave's
-// tokens reading L straight from HBM (coalesced) and S as wave-uniform loads;
-// the 4 waves' sums meet in LDS in wave order.  With splits > 1 the partials
-// go to ws and reduce_splits adds them in split order.
-// 8 or 16 float32 small-side values of one token: wave-uniform 16-byte loads.
-__device__ __forceinline__ void load_small16(const float* row, bool wide, float (&sv)[16]) {
-  const float4* p = reinterpret_cast<const float4*>(row);
-  const float4 a = p[0], b = p[1];
-  const float4 c = wide ? p[2] : make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4 d = wide ? p[3] : make_float4(0.f, 0.f, 0.f, 0.f);
-  sv[0] = a.x; sv[1] = a.y; sv[2] = a.z; sv[3] = a.w;
-  sv[4] = b.x; sv[5] = b.y; sv[6] = b.z; sv[7] = b.w;
-  sv[8] = c.x; sv[9] = c.y; sv[10] = c.z; sv[11] = c.w;
-  sv[12] = d.x; sv[13] = d.y; sv[14] = d.z; sv[15] = d.w;
-}
-
-template <bool SMALL_ROWS>
-__global__ void __launch_bounds__(NTHREADS) lora_tn_kernel(const float* __restrict__ S, int64_t lds_, int ns,
-                                                           const uint16_t* __restrict__ Lm, int64_t ldl, int nl, int M,
-                                                           int rows_per_split, float* __restrict__ out,
-                                                           int64_t ldo, int accumulate, int direct) {
-  __shared__ float red[3][64][65];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = blockIdx.x * 256 + lane * 4;
-  const int split = blockIdx.y;
-  const int j0 = blockIdx.z * 16;
-  const int nj = min(16, ns - j0);
-  const int mb = split * rows_per_split, me = min(M, mb + rows_per_split);
-  float acc[16][4];
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
-  const bool colok = col < nl;
-  const bool wide = nj > 8;
-#pragma unroll 4
-  for (int m = mb + wave; m < me; m += 4) {
-    const uint2 lv = colok ? *reinterpret_cast<const uint2*>(Lm + (int64_t)m * ldl + col) : make_uint2(0, 0);
-    const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
-    float sv[16];
-    load_small16(S + (int64_t)m * lds_ + j0, wide, sv);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv[j], l4[c], acc[j][c]);
-  }
-  // waves 1..3 park their sums; wave 0 adds them in order
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (wave > 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave - 1][lane][j * 4 + c] = acc[j][c];
-    }
-  }
-  __syncthreads();
-  if (wave != 0 || !colok) return;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j >= nj) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
-      const int a = j0 + j, b = col + c;
-      if (b >= nl) continue;
-      if (direct) {
-        const int64_t o = SMALL_ROWS ? (int64_t)a * ldo + b : (int64_t)b * ldo + a;
-        out[o] = accumulate ? out[o] + v : v;
-      } else {
-        out[(int64_t)split * ((int64_t)ns * nl) + (SMALL_ROWS ? (int64_t)a * nl + b : (int64_t)b * ns + a)] = v;
-      }
-    }
-  }
-}
-
-// All adapter-gradient reductions of one linear group in one launch: one
-// dA task (the group's stacked G^T X) and one dB task per segment (dY_seg^T
-// U_seg).  Each workgroup owns 256 output columns x 16 small indices over all
-// tokens (the 4 waves interleave tokens and meet in LDS in wave order), so no
-// partials and no second pass.
-__global__ void __launch_bounds__(NTHREADS) lora_grads_kernel(TnBatch bt) {
-  __shared__ float red[3][64][65];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Pick this workgroup's task with constant indices only: a dynamically
-  // indexed kernel-argument array would be copied to scratch memory.
-  TnTask tk = bt.t[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i)
-    if (i < bt.ntasks && (int)blockIdx.x >= bt.t[i].tile0) tk = bt.t[i];
-  const int local = blockIdx.x - tk.tile0;
-  const int ncol = (tk.nl + 255) / 256;
-  const int col = (local % ncol) * 256 + lane * 4;
-  const int j0 = (local / ncol) * 16;
-  const int nj = min(16, tk.ns - j0);
-  float acc[16][4];
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
-  const bool colok = col < tk.nl;
-  const bool wide = nj > 8;
-#pragma unroll 4
-  for (int m = wave; m < bt.M; m += 4) {
-    const uint2 lv = colok ? *reinterpret_cast<const uint2*>(tk.L + (int64_t)m * tk.ldl + col) : make_uint2(0, 0);
-    const float l4[4] = {bf_lo(lv.x), bf_hi(lv.x), bf_lo(lv.y), bf_hi(lv.y)};
-    float sv[16];
-    load_small16(tk.S + (int64_t)m * tk.lds + j0, wide, sv);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(sv[j], l4[c], acc[j][c]);
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (wave > 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) red[wave - 1][lane][j * 4 + c] = acc[j][c];
-    }
-  }
-  __syncthreads();
-  if (wave != 0 || !colok) return;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j >= nj) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float v = ((acc[j][c] + red[0][lane][j * 4 + c]) + red[1][lane][j * 4 + c]) + red[2][lane][j * 4 + c];
-      const int a = j0 + j, b = col + c;
-      if (b >= tk.nl) continue;
-      const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
-      tk.out[o] = bt.accumulate ? tk.out[o] + v : v;
-    }
-  }
-}
-
-// The same reductions on the matrix cores.  out[a][b] = sum over tokens of
-// S[m][a] L[m][b] is an MFMA product with the tokens as its reduction: each
-// k-step stages 64 tokens of L (128 columns) and of S (all small indices)
-// in LDS transposed, token-major per column, so a lane's 8 reduction values
-// are contiguous.  S is float32; it enters the bf16 MFMA as a hi/lo pair
-// (hi = bf16(S), lo = bf16(S - hi)), which carries 16 of S's 24 mantissa bits
-// into an exact product with L's bf16 values and float32 accumulation.  Each
-// workgroup owns every small index of 128 columns over all tokens, in a fixed
-// order: no partials, no atomics.
-constexpr int TNM_COLS = 128, TNM_TOK = 64;
-__global__ void __launch_bounds__(NTHREADS) lora_grads_mfma_kernel(TnBatch bt) {
-  __shared__ __attribute__((aligned(16))) uint16_t LT[TNM_COLS][TNM_TOK + 8];   // [column][token], bf16
-  __shared__ __attribute__((aligned(16))) float ST[64][TNM_TOK + 4];            // [small index][token]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  TnTask tk = bt.t[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i)
-    if (i < bt.ntasks && (int)blockIdx.x >= bt.t[i].tile0) tk = bt.t[i];
-  const int b0 = (blockIdx.x - tk.tile0) * TNM_COLS;
-  const int ns = tk.ns;
-  const int m_hi = min(bt.M, (int)(blockIdx.y + 1) * bt.per);   // this block's tokens end here
-  const int M = m_hi;
-  // this thread's L micro-tile (4 tokens x 8 columns) and S row (one token, 16 small indices)
-  const int lr = 4 * (tid >> 4), lc = 8 * (tid & 15);
-  const int scol = b0 + lc;
-  const int sa = 16 * wave;
-  uint4 lv[4];
-  float4 sv[4];
-  auto load = [&](int m0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + lr + i;
-      const uint16_t* row = tk.L + (int64_t)m * tk.ldl + scol;
-      if (m < M && scol + 8 <= tk.nl) {
-        lv[i] = *reinterpret_cast<const uint4*>(row);
-      } else if (m < M && scol + 4 <= tk.nl) {
-        const uint2 h = *reinterpret_cast<const uint2*>(row);
-        lv[i] = make_uint4(h.x, h.y, 0u, 0u);
-      } else {
-        lv[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    const int m = m0 + lane;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int a = sa + 4 * q;
-      sv[q] = (m < M && a < ns) ? *reinterpret_cast<const float4*>(tk.S + (int64_t)m * tk.lds + a)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto store = [&]() __attribute__((always_inline)) {
-    const uint32_t w[4][4] = {{lv[0].x, lv[0].y, lv[0].z, lv[0].w}, {lv[1].x, lv[1].y, lv[1].z, lv[1].w},
-                              {lv[2].x, lv[2].y, lv[2].z, lv[2].w}, {lv[3].x, lv[3].y, lv[3].z, lv[3].w}};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int sel = (c & 1) ? 0x07060302 : 0x05040100;   // high or low bf16 of each token's word
-      const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
-      *reinterpret_cast<u32x2*>(&LT[lc + c][lr]) = u32x2{lo, hi};
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ST[sa + 4 * q + 0][lane] = sv[q].x;
-      ST[sa + 4 * q + 1][lane] = sv[q].y;
-      ST[sa + 4 * q + 2][lane] = sv[q].z;
-      ST[sa + 4 * q + 3][lane] = sv[q].w;
-    }
-  };
-  const int J = (ns + 15) / 16;
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int m_lo = blockIdx.y * bt.per;
-  load(m_lo);
-  for (int m0 = m_lo; m0 < m_hi; m0 += TNM_TOK) {
-    __syncthreads();   // the previous k-step's fragment reads are done
-    store();
-    __syncthreads();
-    if (m0 + TNM_TOK < m_hi) load(m0 + TNM_TOK);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int t0 = 32 * kb + 8 * (lane >> 4);
-      bf16x8 bfr[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        bfr[c] = *reinterpret_cast<const bf16x8*>(&LT[32 * wave + 16 * c + (lane & 15)][t0]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g >= J) break;
-        const float* srow = &ST[16 * g + (lane & 15)][t0];
-        const float4 f0 = *reinterpret_cast<const float4*>(srow);
-        const float4 f1 = *reinterpret_cast<const float4*>(srow + 4);
-        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          hw[t] = pack_bf16x2(f[2 * t], f[2 * t + 1]);
-          lw[t] = pack_bf16x2(f[2 * t] - bf_lo(hw[t]), f[2 * t + 1] - bf_hi(hw[t]));
-        }
-        const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          acc[g][c] = mfma16(ahi, bfr[c], acc[g][c]);
-          acc[g][c] = mfma16(alo, bfr[c], acc[g][c]);
-        }
-      }
-    }
-  }
-  // lane holds C[4 (lane >> 4) + v][lane & 15]: small index row, column
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    if (g >= J) break;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int b = b0 + 32 * wave + 16 * c + (lane & 15);
-      if (b >= tk.nl) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int a = 16 * g + 4 * (lane >> 4) + v;
-        if (a >= ns) continue;
-        if (bt.splits > 1) {
-          bt.part[tk.part_off + ((int64_t)blockIdx.y * ns + a) * tk.nl + b] = acc[g][c][v];
-          continue;
-        }
-        const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
-        tk.out[o] = bt.accumulate ? tk.out[o] + acc[g][c][v] : acc[g][c][v];
-      }
-    }
-  }
-}
-
-// The token-range partials of every task of a lora_grads launch summed in
-// range order, then stored (or added) in the task's output layout.
-__global__ void lora_grads_reduce_kernel(TnBatch bt, int64_t total) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  int i = 0;
-  while (i + 1 < bt.ntasks && e >= (int64_t)bt.t[i].ns * bt.t[i].nl) {
-    e -= (int64_t)bt.t[i].ns * bt.t[i].nl;
-    ++i;
-  }
-  const TnTask& tk = bt.t[i];
-  const int a = (int)(e / tk.nl), b = (int)(e % tk.nl);
-  const int64_t plane = (int64_t)tk.ns * tk.nl;
-  const float v = ordered_sum(0.f, bt.part + tk.part_off + e, plane, 0, bt.splits);
-  const int64_t o = tk.small_rows ? (int64_t)a * tk.ldo + b : (int64_t)b * tk.ldo + a;
-  tk.out[o] = bt.accumulate ? tk.out[o] + v : v;
-}
-
-// G finish for several segments at once: segment s sums chunks [c0, c1) of part.
-__global__ void lora_finish_segs_kernel(const float* __restrict__ part, SegFinish sf, int M, int r, float s,
-                                        uint16_t* __restrict__ dst, int64_t ld, float* __restrict__ dst32,
-                                        int64_t ld32) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per = (int64_t)M * r;
-  if (e >= per * sf.n) return;
-  const int sg = e / per;
-  const int64_t i = e % per;
-  const int64_t m = i / r, c = i % r;
-  float v = ordered_sum(0.f, part + i, per, sf.c0[sg], sf.c1[sg]);
-  v *= s;
-  dst[m * ld + sf.col[sg] + c] = f32_to_bf16_bits(v);
-  if (dst32) dst32[m * ld32 + sf.col[sg] + c] = v;
-}
-
-// out[i, j] (+)= sum over splits, in split order.  Partials are packed [splits][rows][cols].
-__global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int rows, int cols,
-                                     float* __restrict__ out, int64_t ldo, int accumulate) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)rows * cols;
-  if (e >= n) return;
-  const float v = ordered_sum(0.f, part + e, n, 0, splits);
-  const int64_t o = (e / cols) * ldo + (e % cols);
-  out[o] = accumulate ? out[o] + v : v;
-}
 
 // =========================================================== float32 variants
 // The float32 tier: dequantized weights are the exact float32 products and
@@ -1636,11 +1203,11 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 // The DMA kernels address their operands with 32-bit byte offsets.
 bool fwd_dma_ok(const FwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
-  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * (p.K / 2) < lim && p.ldx % 8 == 0;
+  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * (p.Kw / 2) < lim && p.ldx % 8 == 0;
 }
 bool fwd_bf16_dma_ok(const FwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
-  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * p.K * 2 < lim && p.ldx % 8 == 0;
+  return (int64_t)p.M * p.ldx * 2 < lim && (int64_t)p.N * p.Kw * 2 < lim && p.ldx % 8 == 0;
 }
 bool bwd_dma_ok(const BwdParams& p) {
   const int64_t lim = int64_t(1) << 31;
@@ -1748,7 +1315,7 @@ int gemm_bwd_splits(int M, int N, int K, int rr) {
   (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
   return choose_splits(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile), (N + 63) / 64, (double)M * K);
 }
-// Workspace of gemm_bwd: split-K partials, then (ping-pong) the transposed LoRA A.
+// Workspace of gemm_bwd: the split-K partials.
 static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
   const int sp = gemm_bwd_splits(M, N, K, rr);
   return sp > 1 ? ((size_t)sp * M * K * sizeof(float) + 255) / 256 * 256 : 0;
@@ -1757,13 +1324,13 @@ size_t gemm_fwd_ws_bytes(int M, int N, int K) {
   const int sp = gemm_fwd_plan(M, N, K, true).splits;   // the tile width never changes the split count
   return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
-size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
-  return gemm_bwd_part_bytes(M, N, K, rr) + (rr > 0 ? (size_t)rr * K * 2 : 0);
-}
+size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) { return gemm_bwd_part_bytes(M, N, K, rr); }
 
 int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
   FwdParams p = p_in;
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
+  if (p.Kw == 0) p.Kw = p.K;
+  LSQ_CHECK(p.Kw == p.K || 2 * p.Kw == p.K, LSQ_ERR_SHAPE, "gemm: the weight is read once or twice along K");
   LSQ_CHECK(p.r == 0 || (p.r % 8 == 0 && p.ldu % 8 == 0), LSQ_ERR_SHAPE, "gemm: LoRA rank must be a multiple of 8");
   if (p.M == 0 || p.N == 0) return LSQ_OK;
   const GemmPlan plan = gemm_fwd_plan(p.M, p.N, p.K, p.kind == LSQ_W_NF4 && fwd_dma_ok(p));
@@ -1774,8 +1341,9 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
               "gemm_fwd: split-K needs %zu bytes of workspace", gemm_fwd_ws_bytes(p.M, p.N, p.K));
     p.part = static_cast<float*>(ws);
   }
-  const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.N * p.r;
-  const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
+  // algorithmic work of the product itself (a hi/lo input is two passes over one product)
+  const double flops = 2.0 * p.M * p.N * (double)p.Kw + 2.0 * p.M * (double)p.N * p.r;
+  const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.Kw;
   const double bytes = wbytes + 2.0 * p.M * p.K + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.N;
   // The profiler times the tile kernel alone (events on its dispatch); a split-K
   // reduction is credited separately.
@@ -1803,15 +1371,8 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   const size_t need = gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr);
   LSQ_CHECK(need == 0 || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "gemm_bwd: needs %zu bytes of workspace",
             need);
+  LSQ_CHECK(p.rr == 0 || p.AlT, LSQ_ERR_INVALID, "gemm_bwd: the LoRA term needs the transposed A");
   if (p.splits > 1) p.part = static_cast<float*>(ws);
-  if (p.rr > 0) {
-    uint16_t* alt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + gemm_bwd_part_bytes(p.M, p.N, p.K, p.rr));
-    const int64_t nel = (int64_t)p.rr * p.K;
-    int t0 = prof_begin(s);
-    transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, s>>>(p.Al, p.rr, p.K, alt);
-    prof_end(t0, s, PROF_OTHER, 0.0, 4.0 * nel);
-    p.AlT = alt;
-  }
   const double flops = 2.0 * p.M * p.N * (double)p.K + 2.0 * p.M * (double)p.rr * p.K;
   const double wbytes = (p.kind == LSQ_W_NF4 ? 0.5625 : 2.0) * p.N * (double)p.K;
   const double bytes = wbytes + 2.0 * p.M * p.N + (epi == EPI_BF16 ? 2.0 : (epi == EPI_F32 ? 4.0 : 8.0)) * p.M * (double)p.K;
@@ -1825,205 +1386,6 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
     launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);
     prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * p.splits * p.M * (double)p.K + 2.0 * p.M * (double)p.K);
   }
-  LSQ_HIP(hipGetLastError());
-  return LSQ_OK;
-}
-
-size_t lora_down_ws_bytes(int M, int K, int rr) {
-  return (size_t)((K + KCHUNK - 1) / KCHUNK) * M * rr * sizeof(float);
-}
-
-int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
-              int64_t ldu, float* U32, int64_t ldu32, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(rr >= 1 && rr <= 64 && K >= 32 && K % 32 == 0, LSQ_ERR_SHAPE, "lora_down: rank %d / K %d unsupported", rr,
-            K);
-  if (M == 0) return LSQ_OK;
-  LSQ_CHECK(ws && ws_bytes >= lora_down_ws_bytes(M, K, rr), LSQ_ERR_WORKSPACE, "lora_down: workspace too small");
-  const int nch = (K + KCHUNK - 1) / KCHUNK;
-  int tok = prof_begin(st);
-  lora_down_kernel<<<dim3((M + 15) / 16, nch), NTHREADS, 0, st>>>(X, ldx, M, K, A, rr, ws);
-  lora_finish_kernel<<<(M * rr + 255) / 256, 256, 0, st>>>(ws, nch, M, rr, s, U, ldu, U32, ldu32);
-  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)K * rr, 2.0 * M * (double)K + 2.0 * rr * K + 2.0 * M * rr);
-  LSQ_HIP(hipGetLastError());
-  return LSQ_OK;
-}
-
-static GChunks g_chunks(int N, int nseg, const SegEnds& segs, int seg_of[128]) {
-  GChunks ch{};
-  ch.n = 0;
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int nb = sg == 0 ? 0 : segs.end[sg - 1], ne = segs.end[sg];
-    for (int b = nb; b < ne; b += KCHUNK) {
-      ch.begin[ch.n] = b;
-      ch.end[ch.n] = std::min(ne, b + KCHUNK);
-      seg_of[ch.n] = sg;
-      ++ch.n;
-    }
-  }
-  return ch;
-}
-
-size_t lora_g_ws_bytes(int M, int N, int r) {
-  // chunks <= N / KCHUNK + one partial chunk per segment (at most 4)
-  return (size_t)((N + KCHUNK - 1) / KCHUNK + 4) * M * r * sizeof(float) + (size_t)N * r * 2 + 256;
-}
-
-int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* B, int r, int nseg, const SegEnds& segs,
-           float s, uint16_t* G, int64_t ldg, float* G32, int64_t ldg32, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(r >= 1 && r <= 64 && r % 8 == 0 && nseg >= 1 && nseg <= 4 && N >= 8 && N % 8 == 0, LSQ_ERR_SHAPE,
-            "lora_g: bad rank/segments/N");
-  if (M == 0) return LSQ_OK;
-  LSQ_CHECK(ws && ws_bytes >= lora_g_ws_bytes(M, N, r), LSQ_ERR_WORKSPACE, "lora_g: workspace too small");
-  int seg_of[128];
-  LSQ_CHECK((N + KCHUNK - 1) / KCHUNK + nseg <= 128, LSQ_ERR_SHAPE, "lora_g: too many reduction chunks (N=%d)", N);
-  GChunks ch = g_chunks(N, nseg, segs, seg_of);
-  uint16_t* bt = reinterpret_cast<uint16_t*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (((size_t)N * r * 2 + 255) & ~size_t(255)));
-  int tok = prof_begin(st);
-  const int64_t nel = (int64_t)N * r;
-  transpose_rows_kernel<<<(unsigned)((nel + 255) / 256), 256, 0, st>>>(B, N, r, bt);
-  lora_g_kernel<<<dim3((M + 15) / 16, ch.n), NTHREADS, 0, st>>>(dY, ldy, M, N, bt, r, ch, part);
-  // each segment's chunks are consecutive: sum them in order into its G columns
-  SegFinish sf{};
-  for (int c0 = 0; c0 < ch.n;) {
-    int c1 = c0;
-    while (c1 < ch.n && seg_of[c1] == seg_of[c0]) ++c1;
-    sf.c0[sf.n] = c0;
-    sf.c1[sf.n] = c1;
-    sf.col[sf.n] = seg_of[c0] * r;
-    ++sf.n;
-    c0 = c1;
-  }
-  const int64_t nfin = (int64_t)M * r * sf.n;
-  lora_finish_segs_kernel<<<(unsigned)((nfin + 255) / 256), 256, 0, st>>>(part, sf, M, r, s, G, ldg, G32, ldg32);
-  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)N * r, 2.0 * M * (double)N + 4.0 * N * r + 2.0 * M * r * nseg);
-  LSQ_HIP(hipGetLastError());
-  return LSQ_OK;
-}
-
-// Token ranges of a matrix-core lora_grads launch: enough column-tile x range
-// workgroups to keep about four per CU loading (each walks its range 64 tokens
-// at a time), at least 128 tokens per range, at most 8 ranges.
-static int lora_grads_splits(int mtiles, int M) {
-  return std::max(1, std::min({8, (1024 + mtiles - 1) / mtiles, M / 128}));
-}
-static int lora_grads_mtiles(const TnTask* tasks, int ntasks) {
-  int mt = 0;
-  for (int i = 0; i < ntasks; ++i) mt += (tasks[i].nl + TNM_COLS - 1) / TNM_COLS;
-  return mt;
-}
-size_t lora_grads_ws_bytes(const TnTask* tasks, int ntasks, int M) {
-  const int sp = lora_grads_splits(lora_grads_mtiles(tasks, ntasks), M);
-  if (sp <= 1) return 0;
-  size_t n = 0;
-  for (int i = 0; i < ntasks; ++i) n += (size_t)tasks[i].ns * tasks[i].nl;
-  return n * sp * sizeof(float);
-}
-
-int lora_grads(const TnTask* tasks, int ntasks, int M, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(ntasks >= 1 && ntasks <= 8, LSQ_ERR_INVALID, "lora_grads: 1..8 tasks");
-  TnBatch bt{};
-  int tiles = 0, mtiles = 0;
-  bool mfma = true;   // every task's large side in 16-byte rows: the matrix-core kernel
-  double flops = 0, bytes = 0;
-  for (int i = 0; i < ntasks; ++i) {
-    const TnTask& t = tasks[i];
-    LSQ_CHECK(t.ns >= 8 && t.ns <= 64 && t.ns % 8 == 0 && t.nl % 4 == 0 && t.ldl % 4 == 0 && t.lds % 4 == 0 &&
-                  (reinterpret_cast<uintptr_t>(t.S) & 15) == 0 && (reinterpret_cast<uintptr_t>(t.L) & 7) == 0,
-              LSQ_ERR_SHAPE, "lora_grads: task %d shape/alignment", i);
-    mfma = mfma && t.ldl % 8 == 0 && (reinterpret_cast<uintptr_t>(t.L) & 15) == 0;
-    bt.t[i] = t;
-    tiles += ((t.nl + 255) / 256) * ((t.ns + 15) / 16);
-    mtiles += (t.nl + TNM_COLS - 1) / TNM_COLS;
-    flops += 2.0 * M * (double)t.ns * t.nl;
-    bytes += 4.0 * M * (double)t.ns + 2.0 * M * (double)t.nl + 4.0 * t.ns * t.nl;
-  }
-  for (int i = 0, acc_t = 0; i < ntasks; ++i) {
-    bt.t[i].tile0 = acc_t;
-    acc_t += mfma ? (tasks[i].nl + TNM_COLS - 1) / TNM_COLS
-                  : ((tasks[i].nl + 255) / 256) * ((tasks[i].ns + 15) / 16);
-  }
-  bt.ntasks = ntasks;
-  bt.M = M;
-  bt.accumulate = accumulate;
-  if (M == 0 && !accumulate) {
-    for (int i = 0; i < ntasks; ++i) {
-      const TnTask& t = tasks[i];
-      if (int e = zero_words(t.out, t.ldo, t.small_rows ? t.ns : t.nl, t.small_rows ? t.nl : t.ns, st)) return e;
-    }
-    return LSQ_OK;
-  }
-  bt.splits = 1;
-  bt.per = M;
-  if (mfma) {
-    bt.splits = lora_grads_splits(mtiles, M);
-    if (bt.splits > 1) {
-      const size_t need = lora_grads_ws_bytes(tasks, ntasks, M);
-      LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "lora_grads: needs %zu bytes of workspace", need);
-      bt.per = ((M + bt.splits - 1) / bt.splits + TNM_TOK - 1) / TNM_TOK * TNM_TOK;
-      bt.part = ws;
-      int64_t off = 0;
-      for (int i = 0; i < ntasks; ++i) {
-        bt.t[i].part_off = off;
-        off += (int64_t)bt.splits * tasks[i].ns * tasks[i].nl;
-      }
-    }
-  }
-  int tok = prof_begin(st);
-  if (mfma) {
-    lora_grads_mfma_kernel<<<dim3(mtiles, bt.splits), NTHREADS, 0, st>>>(bt);
-    if (bt.splits > 1) {
-      int64_t total = 0;
-      for (int i = 0; i < ntasks; ++i) total += (int64_t)tasks[i].ns * tasks[i].nl;
-      lora_grads_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(bt, total);
-    }
-  } else {
-    lora_grads_kernel<<<tiles, NTHREADS, 0, st>>>(bt);
-  }
-  prof_end(tok, st, PROF_LORA, flops, bytes);
-  LSQ_HIP(hipGetLastError());
-  return LSQ_OK;
-}
-
-static int tn_splits(int M, int nl, int ns) {
-  const int tiles = ((nl + 255) / 256) * ((ns + 15) / 16);
-  return std::max(1, std::min(std::max(1, M / 64), (512 + tiles - 1) / tiles));
-}
-
-size_t lora_tn_ws_bytes(int M, int ns, int nl) {
-  const int sp = tn_splits(M, nl, ns);
-  return sp > 1 ? (size_t)sp * ns * nl * sizeof(float) : 0;
-}
-
-int lora_tn(const float* S, int64_t lds_, int ns, const uint16_t* L, int64_t ldl, int nl, int M, bool small_rows,
-            float* out, int64_t ldo, int accumulate, float* ws, size_t ws_bytes, hipStream_t st) {
-  LSQ_CHECK(ns >= 8 && ns <= 64 && ns % 8 == 0, LSQ_ERR_SHAPE, "lora_tn: small dim %d unsupported", ns);
-  LSQ_CHECK(nl % 4 == 0 && ldl % 4 == 0 && lds_ % 4 == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0, LSQ_ERR_SHAPE,
-            "lora_tn: large dim must be a multiple of 4, small rows 16-byte aligned");
-  const int splits = tn_splits(M, nl, ns);
-  const int rows_per_split = (M + splits - 1) / splits;
-  const bool direct = splits == 1;
-  LSQ_CHECK(direct || (ws && ws_bytes >= lora_tn_ws_bytes(M, ns, nl)), LSQ_ERR_WORKSPACE, "lora_tn: workspace too small");
-  if (M == 0) {
-    if (!accumulate) {
-      if (int e = zero_words(out, ldo, small_rows ? ns : nl, small_rows ? nl : ns, st)) return e;
-    }
-    return LSQ_OK;
-  }
-  int tok = prof_begin(st);
-  dim3 grid((nl + 255) / 256, splits, (ns + 15) / 16);
-  if (small_rows)
-    lora_tn_kernel<true><<<grid, NTHREADS, 0, st>>>(S, lds_, ns, L, ldl, nl, M, rows_per_split, direct ? out : ws, ldo,
-                                                    accumulate, direct ? 1 : 0);
-  else
-    lora_tn_kernel<false><<<grid, NTHREADS, 0, st>>>(S, lds_, ns, L, ldl, nl, M, rows_per_split, direct ? out : ws, ldo,
-                                                     accumulate, direct ? 1 : 0);
-  if (!direct) {
-    const int rows = small_rows ? ns : nl, cols = small_rows ? nl : ns;
-    const int64_t n = (int64_t)rows * cols;
-    reduce_splits_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(ws, splits, rows, cols, out, ldo, accumulate);
-  }
-  prof_end(tok, st, PROF_LORA, 2.0 * M * (double)ns * nl, 2.0 * M * (double)(ns + nl) + 4.0 * ns * nl);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -2051,18 +1413,61 @@ WeightRef ref_of(const lsq_weight* W) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace of one linear call, carved in a fixed order (base null: sizes only).
+struct LinWs {
+  void* U;            // [M, r] in dtype: U (recomputed or forward scratch)
+  void* G;            // [M, r] in dtype
+  float* U32;         // [M, r] float32 (bf16 dtype): the unrounded U and G
+  float* G32;
+  float* lw;          // partials of the down / G projections
+  size_t lw_bytes;
+  float* gw;          // partials of the adapter-gradient reduction
+  size_t gw_bytes;
+  uint16_t* Bt;       // B^T [r, N]
+  uint16_t* At;       // A^T [K, r]
+  int* cnt;           // arrival counters
+  int ncnt;
+  void* part;         // split-K partials of the GEMM
+  size_t part_bytes;
+  size_t total;
+};
+LinWs carve_lin(void* base, int M, int N, int K, int r, int dtype) {
+  LinWs w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* q = base ? p + off : nullptr;
+    off += align256(std::max<size_t>(bytes, 1));
+    return q;
+  };
+  const size_t el = dtype == LSQ_F32 ? 4 : 2;
+  w.U = take((size_t)M * r * el);
+  w.G = take((size_t)M * r * el);
+  if (dtype != LSQ_F32) {
+    w.U32 = static_cast<float*>(take((size_t)M * r * 4));
+    w.G32 = static_cast<float*>(take((size_t)M * r * 4));
+    w.lw_bytes = std::max(lora_down_ws_bytes(M, K, r), lora_g_ws_bytes(M, N, r));
+    w.lw = static_cast<float*>(take(w.lw_bytes));
+    const int se[1] = {N};
+    w.gw_bytes = lora_grads_ws_bytes(K, r, 1, se, M);
+    w.gw = static_cast<float*>(take(w.gw_bytes));
+    w.Bt = static_cast<uint16_t*>(take((size_t)N * r * 2));
+    w.At = static_cast<uint16_t*>(take((size_t)K * r * 2));
+    w.ncnt = std::max({lora_down_counters(M), lora_g_counters(M, 1), lora_grads_counters(K, r, 1, se)});
+    w.cnt = static_cast<int*>(take(counters_bytes(w.ncnt)));
+  }
+  w.part_bytes = std::max(gemm_fwd_ws_bytes(M, N, K), gemm_bwd_ws_bytes(M, N, K, r));
+  w.part = take(w.part_bytes);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t nf4_lora_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
-  const size_t el = dtype == LSQ_F32 ? 4 : 2;
-  size_t b = align256(M * r * el) * 2             // U (recomputed or forward scratch) and G
-             + (dtype == LSQ_F32 ? 0 : align256(M * r * 4) * 2)   // their unrounded float32 copies
-             + align256(std::max(lora_down_ws_bytes((int)M, (int)K, r), lora_g_ws_bytes((int)M, (int)N, r)));
-  b += align256(lora_tn_ws_bytes((int)M, r, (int)K)) + align256(lora_tn_ws_bytes((int)M, r, (int)N));
-  b += align256(std::max(gemm_fwd_ws_bytes((int)M, (int)N, (int)K), gemm_bwd_ws_bytes((int)M, (int)N, (int)K, r)));
-  return b + 256;
+  return carve_lin(nullptr, (int)M, (int)N, (int)K, r, dtype).total + 256;
 }
 
 int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, int64_t M, const void* A,
@@ -2097,17 +1502,12 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
     LSQ_HIP(hipGetLastError());
     return LSQ_OK;
   }
-  uint16_t* U = U_out ? static_cast<uint16_t*>(U_out) : static_cast<uint16_t*>(ws);
-  LSQ_CHECK(ws && ws_bytes >= need, LSQ_ERR_WORKSPACE, "linear_fwd: workspace too small");
-  const size_t lw_off = align256((size_t)Mi * r * 2) * 2;
-  const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
+  const LinWs lw = carve_lin(ws, Mi, w.N, w.K, r, dtype);
+  uint16_t* U = U_out ? static_cast<uint16_t*>(U_out) : static_cast<uint16_t*>(lw.U);
+  if (int e = zero_counters(lw.cnt, lw.ncnt, s)) return e;
   if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale, U,
-                        r, nullptr, 0, reinterpret_cast<float*>(static_cast<char*>(ws) + lw_off), lw_bytes, s))
+                        r, nullptr, 0, lw.lw, lw.lw_bytes, lw.cnt, s))
     return e;
-  const size_t part_off = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype) - 256 -
-                          align256(std::max(gemm_fwd_ws_bytes(Mi, w.N, w.K), gemm_bwd_ws_bytes(Mi, w.N, w.K, r)));
-  void* part = ws ? static_cast<char*>(ws) + part_off : nullptr;
-  const size_t part_bytes = ws && ws_bytes > part_off ? ws_bytes - part_off : 0;
   FwdParams p{};
   p.X = static_cast<const uint16_t*>(X);
   p.ldx = w.K;
@@ -2127,7 +1527,7 @@ int nf4_lora_linear_fwd(const lsq_weight* W, const void* bias, const void* X, in
   p.bias = static_cast<const uint16_t*>(bias);
   p.out = Y;
   p.ldc = w.N;
-  return gemm_fwd(p, EPI_BF16, s, part, part_bytes);
+  return gemm_fwd(p, EPI_BF16, s, lw.part, lw.part_bytes);
 }
 
 int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, int64_t M, const void* A,
@@ -2152,31 +1552,11 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
     return zero_words(dB, r, w.N, r, s);
   }
   const int Mi = (int)M;
-  char* wsp = static_cast<char*>(ws);
-  const size_t el = dtype == LSQ_F32 ? 4 : 2;
-  void* Uw = wsp;
-  wsp += align256((size_t)Mi * r * el);
-  void* Gw = wsp;
-  wsp += align256((size_t)Mi * r * el);
-  float* U32 = nullptr;
-  float* G32 = nullptr;
-  if (dtype != LSQ_F32) {
-    U32 = reinterpret_cast<float*>(wsp);
-    wsp += align256((size_t)Mi * r * 4);
-    G32 = reinterpret_cast<float*>(wsp);
-    wsp += align256((size_t)Mi * r * 4);
-  }
-  float* lw = reinterpret_cast<float*>(wsp);
-  const size_t lw_bytes = align256(std::max(lora_down_ws_bytes(Mi, w.K, r), lora_g_ws_bytes(Mi, w.N, r)));
-  wsp += lw_bytes;
-  float* tn1 = reinterpret_cast<float*>(wsp);
-  const size_t tn1_b = align256(lora_tn_ws_bytes(Mi, r, w.K));
-  wsp += tn1_b;
-  float* tn2 = reinterpret_cast<float*>(wsp);
-  const size_t tn2_b = align256(lora_tn_ws_bytes(Mi, r, w.N));
-  wsp += tn2_b;
-  void* part = wsp;
-  const size_t part_bytes = align256(std::max(gemm_fwd_ws_bytes(Mi, w.N, w.K), gemm_bwd_ws_bytes(Mi, w.N, w.K, r)));
+  const LinWs lw = carve_lin(ws, Mi, w.N, w.K, r, dtype);
+  void* Uw = lw.U;
+  void* Gw = lw.G;
+  float* U32 = lw.U32;
+  float* G32 = lw.G32;
 
   if (dtype == LSQ_F32) {
     const float* U = static_cast<const float*>(U_in);
@@ -2201,20 +1581,28 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
     LSQ_HIP(hipGetLastError());
     return LSQ_OK;
   }
+  if (int e = zero_counters(lw.cnt, lw.ncnt, s)) return e;
+  {   // B^T [r, N] for the G projection and A^T [K, r] for the LoRA term of dX
+    const int64_t nb = (int64_t)w.N * r, na = (int64_t)r * w.K;
+    int tok = prof_begin(s);
+    transpose_rows_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(B), w.N, r, lw.Bt);
+    transpose_rows_kernel<<<(unsigned)((na + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(A), r, w.K, lw.At);
+    prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * (nb + na));
+  }
   if (U_in) {
     // the caller's bf16 U: its float32 image feeds dB (no unrounded copy exists)
     const int64_t nu = (int64_t)Mi * r;
     if (nu > 0) bf16_to_f32_kernel<<<(unsigned)((nu + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(U_in), nu, U32);
   } else {
     if (int e = lora_down(static_cast<const uint16_t*>(X), w.K, Mi, w.K, static_cast<const uint16_t*>(A), r, scale,
-                          static_cast<uint16_t*>(Uw), r, U32, r, lw, lw_bytes, s))
+                          static_cast<uint16_t*>(Uw), r, U32, r, lw.lw, lw.lw_bytes, lw.cnt, s))
       return e;
   }
   uint16_t* G = static_cast<uint16_t*>(Gw);
   SegEnds segs{};
   segs.end[0] = w.N;
-  if (int e = lora_g(static_cast<const uint16_t*>(dY), w.N, Mi, w.N, static_cast<const uint16_t*>(B), r, 1, segs,
-                     scale, G, r, G32, r, lw, lw_bytes, s))
+  if (int e = lora_g(static_cast<const uint16_t*>(dY), w.N, Mi, w.N, lw.Bt, r, 1, segs, scale, G, r, G32, r, lw.lw,
+                     lw.lw_bytes, lw.cnt, s))
     return e;
   BwdParams p{};
   p.dY = static_cast<const uint16_t*>(dY);
@@ -2228,14 +1616,27 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   p.G = G;
   p.ldg = r;
   p.Al = static_cast<const uint16_t*>(A);
+  p.AlT = lw.At;
   p.rr = r;
   p.out = dX;
   p.ldc = w.K;
-  if (int e = gemm_bwd(p, EPI_BF16, s, part, part_bytes)) return e;
-  if (int e = lora_tn(G32, r, r, static_cast<const uint16_t*>(X), w.K, w.K, Mi, true, dA, w.K, accumulate, tn1, tn1_b,
-                      s))
-    return e;
-  return lora_tn(U32, r, r, static_cast<const uint16_t*>(dY), w.N, w.N, Mi, false, dB, r, accumulate, tn2, tn2_b, s);
+  if (int e = gemm_bwd(p, EPI_BF16, s, lw.part, lw.part_bytes)) return e;
+  GradGroup g{};
+  g.G = G32;
+  g.ldg = r;
+  g.U = U32;
+  g.ldu = r;
+  g.X = static_cast<const uint16_t*>(X);
+  g.ldx = w.K;
+  g.dY = static_cast<const uint16_t*>(dY);
+  g.ldy = w.N;
+  g.Kx = w.K;
+  g.r = r;
+  g.nseg = 1;
+  g.seg_end[0] = w.N;
+  g.gA = dA;
+  g.gB = dB;
+  return lora_grads(g, Mi, accumulate, lw.gw, lw.gw_bytes, lw.cnt, s);
 }
 
 }  // extern "C"

@@ -27,12 +27,17 @@ struct LayerHook {
   void* ctx;
 };
 
+// Once per workspace use, before the first layer pass on it: the rotary
+// table and the rank-r launches' arrival counters (zeroed).
+int layer_prepare(const lsq_model_cfg* c, int B, int S, void* ws, hipStream_t s);
 // acts (nullable): this layer's kept-activation region.  layer_fwd fills it;
-// layer_bwd then reads it instead of recomputing the forward.
+// layer_bwd then reads it instead of recomputing the forward.  lora_t
+// (nullable): the layer's adapters transposed block by block
+// (adapter_transpose); null transposes them into the workspace first.
 int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, int B, int S,
               float* x_out, void* ws, hipStream_t s, void* acts);
-int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, const float* dx_out,
-              int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
+int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const void* lora_t, const float* x_in,
+              const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
               const LayerHook* hook, void* acts);
 
 }  // namespace lsq

@@ -109,9 +109,10 @@ void lora_layout(const lsq_model_cfg* c, lsq_lora_layout* L) {
 // Buffers of one layer pass, carved from the caller's workspace in a fixed order.
 struct LayerWs {
   float* rope;        // [S, hd/2] (cos, sin)
-  uint16_t* xn1;      // [T, H]
+  uint16_t* xn1;      // [T, 2H]: the normed input as bf16 (columns [0, H)) and the
+                      // bf16 rounding of its remainder (columns [H, 2H))
   uint16_t* U_qkv;    // [T, 3r]
-  uint16_t* qkv;      // [T, Nqkv]
+  float* qkv;         // [T, Nqkv] float32
   uint16_t* attn;     // [T, Nq]
   float* lse;         // [B, nh, S]
   uint16_t* U_o;      // [T, r]
@@ -137,10 +138,13 @@ struct LayerWs {
   float* dk_part;     // [T, nh, hd] per-query-head dK, dV partials
   float* dv_part;
   uint16_t* aprep;    // attention operands prepared once per call
-  float* lws;         // scratch of the LoRA down / G kernels
+  float* lws;         // partials of the LoRA down / G projections
   size_t lws_bytes;
-  float* tn;          // token-reduction partials
+  float* tn;          // partials of the adapter-gradient token reduction
   size_t tn_bytes;
+  int* cnt;           // arrival counters of the rank-r launches
+  int ncnt;
+  uint16_t* lora_t;   // backward: this layer's adapters transposed (when the caller has none)
   void* gemm;         // split-K partials of the layer's GEMMs
   size_t gemm_bytes;
   size_t total;
@@ -150,34 +154,41 @@ static size_t gemm_need(const Dims& d, int T) {
   size_t m = 0;
   for (int g = 0; g < 4; ++g) {
     const int rr = (g == 0 ? 3 : g == 2 ? 2 : 1) * d.r;
-    m = std::max(m, gemm_fwd_ws_bytes(T, d.gN[g], d.gK[g]));
+    // the q/k/v group reduces over its input's bf16 hi and lo halves (2H)
+    m = std::max(m, gemm_fwd_ws_bytes(T, d.gN[g], g == 0 ? 2 * d.gK[g] : d.gK[g]));
     m = std::max(m, gemm_bwd_ws_bytes(T, d.gN[g], d.gK[g], rr));
   }
   return m;
 }
 
-static int grad_tasks(const Dims& d, const float* G, int ldg, const float* U, int ldu, const uint16_t* X, int Kx,
-                      const uint16_t* dY, int ldy, int nseg, const int* seg_end, float* gA, float* gB,
-                      TnTask (&tasks)[8]);
+// The four groups' adapter-gradient reductions: (stacked rank segments, input
+// width, segment ends of the output columns).
+struct GroupShape {
+  int nseg, Kx;
+  int seg_end[3];
+};
+static void group_shapes(const Dims& d, GroupShape (&g)[4]) {
+  g[0] = GroupShape{3, d.H, {d.Nq, d.Nq + d.Nkv, d.Nqkv}};
+  g[1] = GroupShape{1, d.Nq, {d.H, 0, 0}};
+  g[2] = GroupShape{2, d.H, {d.I, 2 * d.I, 0}};
+  g[3] = GroupShape{1, d.I, {d.H, 0, 0}};
+}
 
-// Token-reduction partials: the adapter-gradient launches of the four groups
-// (shapes only; the pointers are not used for sizing).
 static size_t tn_need(const Dims& d, int T) {
+  GroupShape g[4];
+  group_shapes(d, g);
   size_t m = 0;
-  const int r = d.r;
-  const int se3[1] = {d.H}, se2[2] = {d.I, 2 * d.I}, se1[1] = {d.H}, se0[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
-  const struct {
-    int rr, Kx, ldy, nseg;
-    const int* se;
-  } groups[4] = {{3 * r, d.H, d.Nqkv, 3, se0}, {r, d.Nq, d.H, 1, se1}, {2 * r, d.H, 2 * d.I, 2, se2},
-                 {r, d.I, d.H, 1, se3}};
-  for (const auto& g : groups) {
-    TnTask tasks[8];
-    const int n = grad_tasks(d, nullptr, g.rr, nullptr, g.rr, nullptr, g.Kx, nullptr, g.ldy, g.nseg, g.se, nullptr,
-                             nullptr, tasks);
-    m = std::max(m, lora_grads_ws_bytes(tasks, n, T));
-  }
+  for (const auto& x : g) m = std::max(m, lora_grads_ws_bytes(x.Kx, d.r, x.nseg, x.seg_end, T));
   return m;
+}
+
+// Arrival counters: the most any one rank-r launch of the layer uses.
+static int counters_need(const Dims& d, int T) {
+  GroupShape g[4];
+  group_shapes(d, g);
+  int n = std::max(lora_down_counters(T), lora_g_counters(T, 3));
+  for (const auto& x : g) n = std::max(n, lora_grads_counters(x.Kx, d.r, x.nseg, x.seg_end));
+  return n;
 }
 
 static size_t lws_need(const Dims& d, int T) {
@@ -214,10 +225,15 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
     aoff = up(aoff + std::max<uint64_t>(bytes, 1), 256);
     return r;
   };
+  // rope and the counters first: the same addresses in every carve of one
+  // workspace (forward or backward, kept activations or not), so one
+  // layer_prepare serves every pass
   w.rope = static_cast<float*>(take(8ull * S * (d.hd / 2)));
-  w.xn1 = static_cast<uint16_t*>(take_act(2 * T * d.H));
+  w.ncnt = counters_need(d, (int)T);
+  w.cnt = static_cast<int*>(take(counters_bytes(w.ncnt)));
+  w.xn1 = static_cast<uint16_t*>(take_act(2 * T * 2 * d.H));
   w.U_qkv = static_cast<uint16_t*>(take_act(2 * T * 3 * d.r));
-  w.qkv = static_cast<uint16_t*>(take_act(2 * T * d.Nqkv));
+  w.qkv = static_cast<float*>(take_act(4 * T * d.Nqkv));
   w.attn = static_cast<uint16_t*>(take_act(2 * T * d.Nq));
   w.lse = static_cast<float*>(take_act(4ull * B * d.nh * S));
   w.U_o = static_cast<uint16_t*>(take_act(2 * T * d.r));
@@ -253,6 +269,9 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
     w.dv_part = static_cast<float*>(take(4 * T * d.nh * d.hd));
     w.tn_bytes = tn_need(d, (int)T);
     w.tn = static_cast<float*>(take(w.tn_bytes));
+    lsq_lora_layout LL;
+    lora_layout(c, &LL);
+    w.lora_t = static_cast<uint16_t*>(take(2 * LL.layer_elems));
   }
   w.total = off;
   return w;
@@ -290,18 +309,27 @@ static BlobView view_blob(const lsq_model_cfg* c, const void* blob) {
   return v;
 }
 
+// A layer's adapters (A [rr, K], B [N, r] per group) and, for the backward,
+// their transposed copies (A^T [K, rr], B^T [r, N]) at the same offsets.
 struct LoraView {
   const uint16_t* A[4];
   const uint16_t* B[4];
+  const uint16_t* AT[4];
+  const uint16_t* BT[4];
 };
-static LoraView view_lora(const lsq_model_cfg* c, const void* lora) {
+static LoraView view_lora(const lsq_model_cfg* c, const void* lora, const void* lora_t = nullptr) {
   lsq_lora_layout L;
   lora_layout(c, &L);
   const uint16_t* p = static_cast<const uint16_t*>(lora);
-  LoraView v;
+  const uint16_t* t = static_cast<const uint16_t*>(lora_t);
+  LoraView v{};
   for (int g = 0; g < 4; ++g) {
     v.A[g] = p + L.a_off[g];
     v.B[g] = p + L.b_off[g];
+    if (t) {
+      v.AT[g] = t + L.a_off[g];
+      v.BT[g] = t + L.b_off[g];
+    }
   }
   return v;
 }
@@ -329,7 +357,7 @@ static FwdParams fwd_params(const uint16_t* X, int T, const WeightRef& w, const 
 }
 
 static BwdParams bwd_params(const uint16_t* dY, int T, const WeightRef& w, const uint16_t* G, int ldg,
-                            const uint16_t* Al, int rr) {
+                            const uint16_t* Al, const uint16_t* AlT, int rr) {
   BwdParams p{};
   p.dY = dY;
   p.ldy = w.N;
@@ -342,6 +370,7 @@ static BwdParams bwd_params(const uint16_t* dY, int T, const WeightRef& w, const
   p.G = G;
   p.ldg = ldg;
   p.Al = Al;
+  p.AlT = AlT;
   p.rr = rr;
   p.ldc = w.K;
   return p;
@@ -359,12 +388,18 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   const Dims d = dims_of(c);
   const int T = B * S, r = d.r;
   const float sc = c->lora_scale;
-  TRY(rope_table(S, d.hd, c->rope_theta, w.rope, s));
-  // attention block
-  TRY(rmsnorm_fwd(x_in, bv.norm1, T, d.H, c->rms_eps, w.xn1, nullptr, s));
-  TRY(lora_down(w.xn1, d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.U32[0], 3 * r, w.lws, w.lws_bytes, s));
+  // attention block.  q and k decide the attention weights, whose error grows
+  // with the scores' magnitude: the q/k/v product takes the normed input as a
+  // bf16 hi/lo pair (two passes over one weight) and keeps its output in
+  // float32.  The adapters' down-projection and gradient read the hi half.
+  TRY(rmsnorm_fwd(x_in, bv.norm1, T, d.H, c->rms_eps, w.xn1, 2 * d.H, nullptr, s, w.xn1 + d.H));
+  TRY(lora_down(w.xn1, 2 * d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.U32[0], 3 * r, w.lws, w.lws_bytes,
+                w.cnt, s));
   {
     FwdParams p = fwd_params(w.xn1, T, bv.w[0], w.U_qkv, 3 * r, lv.B[0], r);
+    p.ldx = 2 * d.H;
+    p.K = 2 * d.H;
+    p.Kw = d.H;
     p.nseg = 3;
     p.seg_end[0] = d.Nq;
     p.seg_end[1] = d.Nq + d.Nkv;
@@ -374,14 +409,14 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     p.seg_ucol[2] = 2 * r;
     p.bias = bv.bias;
     p.out = w.qkv;
-    TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
+    TRY(gemm_fwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
   }
   {
     AttnArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, d.Nq, w.lse,
                reinterpret_cast<const float2*>(w.rope), w.attn_f32, w.aprep};
     TRY(attention_fwd(a, B, s));
   }
-  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, w.cnt, s));
   {
     FwdParams p = fwd_params(w.attn, T, bv.w[1], w.U_o, r, lv.B[1], r);
     p.resid = x_in;
@@ -389,8 +424,8 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     TRY(gemm_fwd(p, EPI_F32_RESID, s, w.gemm, w.gemm_bytes));
   }
   // MLP block
-  TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, nullptr, s));
-  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, s));
+  TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, d.H, nullptr, s));
+  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, w.cnt, s));
   {
     FwdParams p = fwd_params(w.xn2, T, bv.w[2], w.U_gu, 2 * r, lv.B[2], r);
     p.nseg = 2;
@@ -402,7 +437,7 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   TRY(swiglu_fwd(w.gu, T, d.I, w.m, s));
-  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.U32[3], r, w.lws, w.lws_bytes, s));
+  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.U32[3], r, w.lws, w.lws_bytes, w.cnt, s));
   if (x_out) {
     FwdParams p = fwd_params(w.m, T, bv.w[3], w.U_d, r, lv.B[3], r);
     p.resid = w.h;
@@ -412,34 +447,27 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   return LSQ_OK;
 }
 
-// dA of the whole stacked group (G^T X, one task) and dB of each segment
-// (dY_seg^T U_seg), in one launch, from the unrounded float32 G and U.
-// The dA and dB tasks of one group (segments of a stacked group are separate
-// dB tasks; dA stays one task while the stacked rank fits 64).
-static int grad_tasks(const Dims& d, const float* G, int ldg, const float* U, int ldu, const uint16_t* X, int Kx,
-                      const uint16_t* dY, int ldy, int nseg, const int* seg_end, float* gA, float* gB,
-                      TnTask (&tasks)[8]) {
-  const int r = d.r;
-  int n = 0;
-  if (nseg * r <= 64) {
-    tasks[n++] = TnTask{G, ldg, nseg * r, X, Kx, Kx, gA, Kx, 1, 0, 0};
-  } else {
-    for (int sg = 0; sg < nseg; ++sg)
-      tasks[n++] = TnTask{G + sg * r, ldg, r, X, Kx, Kx, gA + (int64_t)sg * r * Kx, Kx, 1, 0, 0};
-  }
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int nb = sg == 0 ? 0 : seg_end[sg - 1], ne = seg_end[sg];
-    tasks[n++] = TnTask{U + sg * r, ldu, r, dY + nb, ldy, ne - nb, gB + (int64_t)nb * r, r, 0, 0, 0};
-  }
-  return n;
-}
-
+// dA of the stacked group (G^T X) and dB of each segment (dY_seg^T U_seg), in
+// one launch, from the unrounded float32 G and U.
 static int adapter_grads(const Dims& d, int T, const float* G, int ldg, const float* U, int ldu,
-                         const uint16_t* X, int Kx, const uint16_t* dY, int ldy, int nseg, const int* seg_end,
-                         float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
-  TnTask tasks[8];
-  const int n = grad_tasks(d, G, ldg, U, ldu, X, Kx, dY, ldy, nseg, seg_end, gA, gB, tasks);
-  return lora_grads(tasks, n, T, accumulate, w.tn, w.tn_bytes, s);
+                         const uint16_t* X, int64_t ldx, int Kx, const uint16_t* dY, int ldy, int nseg,
+                         const int* seg_end, float* gA, float* gB, int accumulate, const LayerWs& w, hipStream_t s) {
+  GradGroup g{};
+  g.G = G;
+  g.ldg = ldg;
+  g.U = U;
+  g.ldu = ldu;
+  g.X = X;
+  g.ldx = ldx;
+  g.dY = dY;
+  g.ldy = ldy;
+  g.Kx = Kx;
+  g.r = d.r;
+  g.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) g.seg_end[i] = seg_end[i];
+  g.gA = gA;
+  g.gB = gB;
+  return lora_grads(g, T, accumulate, w.tn, w.tn_bytes, w.cnt, s);
 }
 
 static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraView& lv, const float* x_in,
@@ -460,45 +488,46 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- down projection: out = h + down(m)
   TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[3], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[3], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
   {
-    BwdParams p = bwd_params(w.dy_b, T, bv.w[3], w.G, r, lv.A[3], r);
+    BwdParams p = bwd_params(w.dy_b, T, bv.w[3], w.G, r, lv.A[3], lv.AT[3], r);
     p.out = w.dm;
     TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[1] = {d.H};
-    TRY(adapter_grads(d, T, w.G32, r, w.U32[3], r, w.m, d.I, w.dy_b, d.H, 1, se, gA[3], gB[3], accumulate, w, s));
+    TRY(adapter_grads(d, T, w.G32, r, w.U32[3], r, w.m, d.I, d.I, w.dy_b, d.H, 1, se, gA[3], gB[3], accumulate, w, s));
   }
   // ---- SwiGLU and gate/up
   TRY(swiglu_bwd(w.gu, w.dm, T, d.I, w.dgu, s));
   SegEnds two{};
   two.end[0] = d.I;
   two.end[1] = 2 * d.I;
-  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.B[2], r, 2, two, sc, w.G, 2 * r, w.G32, 2 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.BT[2], r, 2, two, sc, w.G, 2 * r, w.G32, 2 * r, w.lws, w.lws_bytes,
+             w.cnt, s));
   {
-    BwdParams p = bwd_params(w.dgu, T, bv.w[2], w.G, 2 * r, lv.A[2], 2 * r);
+    BwdParams p = bwd_params(w.dgu, T, bv.w[2], w.G, 2 * r, lv.A[2], lv.AT[2], 2 * r);
     p.out = w.dxn;
     TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[2] = {d.I, 2 * d.I};
-    TRY(adapter_grads(d, T, w.G32, 2 * r, w.U32[2], 2 * r, w.xn2, d.H, w.dgu, 2 * d.I, 2, se, gA[2], gB[2], accumulate,
+    TRY(adapter_grads(d, T, w.G32, 2 * r, w.U32[2], 2 * r, w.xn2, d.H, d.H, w.dgu, 2 * d.I, 2, se, gA[2], gB[2], accumulate,
                       w, s));
   }
   // dh = dout + rmsnorm2'(dxn2)
   TRY(rmsnorm_bwd(w.h, bv.norm2, w.dxn, dx_out, T, d.H, c->rms_eps, w.dh, w.dy_b, s));
   // ---- o projection
   one.end[0] = d.H;
-  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.B[1], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[1], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
   {
-    BwdParams p = bwd_params(w.dy_b, T, bv.w[1], w.G, r, lv.A[1], r);
+    BwdParams p = bwd_params(w.dy_b, T, bv.w[1], w.G, r, lv.A[1], lv.AT[1], r);
     p.out = w.dattn;
     TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[1] = {d.H};
-    TRY(adapter_grads(d, T, w.G32, r, w.U32[1], r, w.attn, d.Nq, w.dy_b, d.H, 1, se, gA[1], gB[1], accumulate, w, s));
+    TRY(adapter_grads(d, T, w.G32, r, w.U32[1], r, w.attn, d.Nq, d.Nq, w.dy_b, d.H, 1, se, gA[1], gB[1], accumulate, w, s));
   }
   // ---- attention (rotary applied inside, in float32)
   {
@@ -511,20 +540,30 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   three.end[0] = d.Nq;
   three.end[1] = d.Nq + d.Nkv;
   three.end[2] = d.Nqkv;
-  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.B[0], r, 3, three, sc, w.G, 3 * r, w.G32, 3 * r, w.lws, w.lws_bytes, s));
+  TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.BT[0], r, 3, three, sc, w.G, 3 * r, w.G32, 3 * r, w.lws,
+             w.lws_bytes, w.cnt, s));
   {
-    BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], 3 * r);
+    BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], lv.AT[0], 3 * r);
     p.out = w.dxn;
     TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
   }
   {
     const int se[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
-    TRY(adapter_grads(d, T, w.G32, 3 * r, w.U32[0], 3 * r, w.xn1, d.H, w.dqkv, d.Nqkv, 3, se, gA[0], gB[0], accumulate,
+    TRY(adapter_grads(d, T, w.G32, 3 * r, w.U32[0], 3 * r, w.xn1, 2 * d.H, d.H, w.dqkv, d.Nqkv, 3, se, gA[0], gB[0], accumulate,
                       w, s));
   }
   // dx = dh + rmsnorm1'(dxn1)
   TRY(rmsnorm_bwd(x_in, bv.norm1, w.dxn, w.dh, T, d.H, c->rms_eps, dx_in, nullptr, s));
   return LSQ_OK;
+}
+
+// The per-call preparation a layer pass needs: the rotary table, and zeroed
+// arrival counters.  A step does it once for all of its layer passes (they
+// share one workspace and every rank-r launch leaves the counters at zero).
+int layer_prepare(const lsq_model_cfg* c, int B, int S, void* ws, hipStream_t s) {
+  const LayerWs w = carve(c, B, S, ws, true);
+  TRY(rope_table(S, dims_of(c).hd, c->rope_theta, w.rope, s));
+  return zero_counters(w.cnt, w.ncnt, s);
 }
 
 int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, int B, int S,
@@ -533,18 +572,17 @@ int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const 
   return forward_impl(c, view_blob(c, blob), view_lora(c, lora), x_in, B, S, x_out, w, s);
 }
 
-int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, const float* dx_out,
-              int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
+int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const void* lora_t, const float* x_in,
+              const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
               const LayerHook* hook, void* acts) {
   LayerWs w = carve(c, B, S, ws, true, acts);
-  const BlobView bv = view_blob(c, blob);
-  const LoraView lv = view_lora(c, lora);
-  if (acts) {
-    // activations kept from this layer's forward: only the rope table is rebuilt
-    TRY(rope_table(S, dims_of(c).hd, c->rope_theta, w.rope, s));
-  } else {
-    TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
+  if (!lora_t) {
+    TRY(adapter_transpose(c, static_cast<const uint16_t*>(lora), w.lora_t, 1, s));
+    lora_t = w.lora_t;
   }
+  const BlobView bv = view_blob(c, blob);
+  const LoraView lv = view_lora(c, lora, lora_t);
+  if (!acts) TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
   if (hook && hook->after_recompute) TRY(hook->after_recompute(hook->ctx));
   return backward_impl(c, bv, lv, x_in, dx_out, B, S, dx_in, grad, accumulate, w, s);
 }
@@ -591,6 +629,7 @@ int decoder_layer_fwd(const lsq_model_cfg* cfg, const void* blob, const void* lo
                       int32_t seq, float* x_out, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_layer_args(cfg, blob, lora, x_in, batch, seq, ws, ws_bytes)) return e;
   LSQ_CHECK(x_out && aligned16(x_out) && x_out != x_in, LSQ_ERR_INVALID, "decoder_layer_fwd: bad x_out");
+  if (int e = layer_prepare(cfg, batch, seq, ws, as_stream(stream))) return e;
   return layer_fwd(cfg, blob, lora, x_in, batch, seq, x_out, ws, as_stream(stream), nullptr);
 }
 
@@ -600,7 +639,8 @@ int decoder_layer_bwd(const lsq_model_cfg* cfg, const void* blob, const void* lo
   if (int e = check_layer_args(cfg, blob, lora, x_in_saved, batch, seq, ws, ws_bytes)) return e;
   LSQ_CHECK(dx_out && dx_in && lora_grad && aligned16(dx_out) && aligned16(dx_in) && aligned16(lora_grad),
             LSQ_ERR_INVALID, "decoder_layer_bwd: bad gradient pointers");
-  return layer_bwd(cfg, blob, lora, x_in_saved, dx_out, batch, seq, dx_in, lora_grad, accumulate, ws,
+  if (int e = layer_prepare(cfg, batch, seq, ws, as_stream(stream))) return e;
+  return layer_bwd(cfg, blob, lora, nullptr, x_in_saved, dx_out, batch, seq, dx_in, lora_grad, accumulate, ws,
                    as_stream(stream), nullptr, nullptr);
 }
 

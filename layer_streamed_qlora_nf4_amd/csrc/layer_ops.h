@@ -4,9 +4,11 @@
 
 namespace lsq {
 
-// qkv: bf16 [B*S, ld] with q heads | k heads | v heads per token row.
+// qkv: float32 [B*S, ld] with q heads | k heads | v heads per token row (q
+// and k are rotated and split into bf16 hi/lo pairs once, by the prep
+// kernels; v enters its products rounded to bf16).
 struct AttnArgs {
-  const uint16_t* qkv;
+  const float* qkv;
   int64_t ld;
   int S, nh, nkv, hd;
   float scale;
@@ -19,7 +21,7 @@ struct AttnArgs {
 };
 
 struct AttnBwdArgs {
-  const uint16_t* qkv;
+  const float* qkv;
   int64_t ld;
   int S, nh, nkv, hd;
   float scale;
@@ -38,11 +40,13 @@ struct AttnBwdArgs {
 
 // Workspace of the operands each attention call prepares once (rotated and
 // split into bf16 hi/lo, or transposed, rows padded with zeros to a multiple
-// of 64): K and V^T for the forward; K, K^T, Q, Q^T and dO^T too for the backward.
+// of 64): Q, K and V^T for the forward; Q, K, their transposes, V and dO^T for
+// the backward.
 size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd);
 
-int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
-                uint16_t* y_lo = nullptr);
+// y [T, ldy] bf16 (and, with y_lo, the bf16 remainder at the same row pitch).
+int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, int64_t ldy, float* rstd,
+                hipStream_t s, uint16_t* y_lo = nullptr);
 int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
                 float* dx, uint16_t* dx_b, hipStream_t s);
 int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);

@@ -57,12 +57,13 @@ __device__ __forceinline__ float block4_sum(float v, float* red) {
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
-// y = bf16(w * x / sqrt(mean(x^2) + eps)); rstd saved.  With y_lo, the output
-// is also written as the bf16 rounding of its own remainder (y ~ y + y_lo to
-// about 16 bits), for GEMMs run as two bf16 passes.
+// y = bf16(w * x / sqrt(mean(x^2) + eps)), rows ldy apart; rstd saved.  With
+// y_lo, the output is also written as the bf16 rounding of its own remainder
+// (y + y_lo carries about 16 bits), for GEMMs run as two bf16 passes.
 __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
                                                           int T, int H, float eps, uint16_t* __restrict__ y,
-                                                          float* __restrict__ rstd, uint16_t* __restrict__ y_lo) {
+                                                          int64_t ldy, float* __restrict__ rstd,
+                                                          uint16_t* __restrict__ y_lo) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
   const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
@@ -78,8 +79,8 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
   if (rstd && tid == 0) rstd[row] = r;
   const uint2* wr = reinterpret_cast<const uint2*>(w);
-  uint2* yr = reinterpret_cast<uint2*>(y + (int64_t)row * H);
-  uint2* lr = y_lo ? reinterpret_cast<uint2*>(y_lo + (int64_t)row * H) : nullptr;
+  uint2* yr = reinterpret_cast<uint2*>(y + (int64_t)row * ldy);
+  uint2* lr = y_lo ? reinterpret_cast<uint2*>(y_lo + (int64_t)row * ldy) : nullptr;
 #pragma unroll
   for (int k = 0; k < kNormMaxV; ++k) {
     const int i = tid + 256 * k;
@@ -216,6 +217,23 @@ __device__ __forceinline__ void unpack8(uint4 v, float (&x)[8]) {
   x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
   x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
 }
+// 8 consecutive values of a float32 row (zeros when !ok).
+__device__ __forceinline__ void load8(const float* p, bool ok, float (&x)[8]) {
+  const float4 a = ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 b = ok ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+// 8 consecutive values of a bf16 row, or of a float32 row rounded to bf16, as one uint4 (zeros when !ok).
+__device__ __forceinline__ uint4 load8_bf16(const uint16_t* p, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+}
+__device__ __forceinline__ uint4 load8_bf16(const float* p, bool ok) {
+  float x[8];
+  load8(p, ok, x);
+  return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7]));
+}
 // Rotate-half RoPE of 8 consecutive pair indices i .. i+7 at position pos:
 // (x1, x2) -> (x1 c - x2 s, x2 c + x1 s), table[pos][i] = (c, s).
 __device__ __forceinline__ void rope8(float (&x1)[8], float (&x2)[8], const float2* __restrict__ tab) {
@@ -252,7 +270,7 @@ __device__ __forceinline__ void put_mt_t(uint16_t (*dst)[PITCH], int c0, int r0,
 // Rows [row0, row0 + 64) of a bf16 matrix, rotated (RoPE at positions
 // row0 + r) and split into hi/lo, row-major.  Rows at or past n read as zero.
 template <int HD>
-__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)[HD + 8], const uint16_t* src,
+__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)[HD + 8], const float* src,
                                           int64_t ld, int row0, int n, const float2* __restrict__ rope) {
   constexpr int HALF = HD / 2, NCH = HALF / 32;
   const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
@@ -261,9 +279,9 @@ __device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)
   for (int c = 0; c < NCH; ++c) {
     const int i0 = (q * NCH + c) * 8;
     float x1[8], x2[8];
-    const uint16_t* row = src + (int64_t)(row0 + r) * ld;
-    unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
-    unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
+    const float* row = src + (int64_t)(row0 + r) * ld;
+    load8(row + i0, ok, x1);
+    load8(row + HALF + i0, ok, x2);
     if (ok) rope8(x1, x2, rope + (int64_t)(row0 + r) * HALF + i0);
     store_hilo8(&hi[r][i0], &lo[r][i0], x1);
     store_hilo8(&hi[r][HALF + i0], &lo[r][HALF + i0], x2);
@@ -291,8 +309,8 @@ __device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + 8], const uin
   }
 }
 // Rows [row0, row0 + 64) of a bf16 matrix straight into [HD][64] (zero past n).
-template <int HD>
-__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const uint16_t* src, int64_t ld, int row0,
+template <int HD, typename SrcT>
+__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const SrcT* src, int64_t ld, int row0,
                                              int n) {
   constexpr int NMT = AT / 4 * (HD / 8);
   for (int t = threadIdx.x; t < NMT; t += 256) {
@@ -301,8 +319,7 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const uint
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * rg + i;
-      rows[i] = r < n ? *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + r) * ld + 8 * cg)
-                      : make_uint4(0u, 0u, 0u, 0u);
+      rows[i] = load8_bf16(src + (int64_t)(row0 + r) * ld + 8 * cg, r < n);
     }
     put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
   }
@@ -314,8 +331,9 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const uint
 // kernels stage plain copies.  Layouts, bf16, rows padded with zeros to Sp, a
 // multiple of 64: rows [b][head][Sp][HD], transposed [b][head][HD][Sp].
 struct PrepPtrs {
-  uint16_t *kh, *kl, *vt;               // forward and backward
-  uint16_t *kht, *klt, *qh, *ql, *qht, *qlt, *ot;   // backward only
+  uint16_t *kh, *kl, *qh, *ql;          // rotated K and Q, bf16 hi/lo rows
+  uint16_t* vt;                         // forward: V^T
+  uint16_t *kht, *klt, *qht, *qlt, *ot, *vr;   // backward: K^T, Q^T, dO^T, V rows
   int Sp;
 };
 PrepPtrs prep_ptrs(uint16_t* base, int B, int S, int nh, int nkv, int hd, bool bwd) {
@@ -330,15 +348,17 @@ PrepPtrs prep_ptrs(uint16_t* base, int B, int S, int nh, int nkv, int hd, bool b
   };
   p.kh = take(ekv);
   p.kl = take(ekv);
-  p.vt = take(ekv);
+  p.qh = take(eq);
+  p.ql = take(eq);
   if (bwd) {
     p.kht = take(ekv);
     p.klt = take(ekv);
-    p.qh = take(eq);
-    p.ql = take(eq);
+    p.vr = take(ekv);
     p.qht = take(eq);
     p.qlt = take(eq);
     p.ot = take(eq);
+  } else {
+    p.vt = take(ekv);
   }
   return p;
 }
@@ -417,33 +437,41 @@ struct PrepRotSmem {
   uint16_t h[AT][HD + 8], l[AT][HD + 8];
   uint16_t t[HD][AT + 8];
 };
-// Heads [col0, col0 + nheads) of the qkv rows (head columns of width HD),
-// rows [64 blockIdx.x, + 64) of batch blockIdx.z, head blockIdx.y: rotated in
-// float32 and split into hi/lo rows; with hiT, also transposed.
+// Where the rotated rows of one set of heads go (hiT/loT null: no transposes).
+struct RotOut {
+  uint16_t *hi, *lo, *hiT, *loT;
+};
+// Rows [64 blockIdx.x, + 64) of batch blockIdx.z, qkv head column col0 +
+// blockIdx.y, rotated in float32 and split into bf16 hi/lo rows, and
+// transposed where the set asks for it: heads below nA (the queries) go to
+// set A, the rest (the keys) to set B.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_prep_rot_kernel(const uint16_t* __restrict__ qkv, int64_t ld, int S, int Sp,
-                                                           int col0, int nheads, const float2* __restrict__ rope,
-                                                           uint16_t* hi, uint16_t* lo, uint16_t* hiT, uint16_t* loT) {
+__global__ void __launch_bounds__(256) attn_prep_rot_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
+                                                           int col0, int nA, int nB, const float2* __restrict__ rope,
+                                                           RotOut A, RotOut Bo) {
   __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
   const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
-  const uint16_t* src = qkv + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
+  const bool in_a = hh < nA;
+  const RotOut o = in_a ? A : Bo;
+  const int nheads = in_a ? nA : nB, hl = in_a ? hh : hh - nA;
+  const float* src = qkv + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
   stage_rot<HD>(sm.h, sm.l, src, ld, row0, S - row0, rope);
   __syncthreads();
-  const int64_t hb = (int64_t)b * nheads + hh;
-  put_rows<HD>(hi + (hb * Sp + row0) * HD, sm.h);
-  put_rows<HD>(lo + (hb * Sp + row0) * HD, sm.l);
-  if (!hiT) return;
+  const int64_t hb = (int64_t)b * nheads + hl;
+  put_rows<HD>(o.hi + (hb * Sp + row0) * HD, sm.h);
+  put_rows<HD>(o.lo + (hb * Sp + row0) * HD, sm.l);
+  if (!o.hiT) return;   // uniform over the workgroup
   lds_transpose<HD>(sm.t, sm.h);
   __syncthreads();
-  put_cols<HD>(hiT + hb * HD * Sp + row0, sm.t, Sp);
+  put_cols<HD>(o.hiT + hb * HD * Sp + row0, sm.t, Sp);
   __syncthreads();
   lds_transpose<HD>(sm.t, sm.l);
   __syncthreads();
-  put_cols<HD>(loT + hb * HD * Sp + row0, sm.t, Sp);
+  put_cols<HD>(o.loT + hb * HD * Sp + row0, sm.t, Sp);
 }
-// The same blocks of a plain bf16 operand (V, dO), transposed.
-template <int HD>
-__global__ void __launch_bounds__(256) attn_prep_t_kernel(const uint16_t* __restrict__ src, int64_t ld, int S, int Sp,
+// The same blocks of a plain operand (V from the float32 qkv, dO in bf16), transposed, in bf16.
+template <int HD, typename SrcT>
+__global__ void __launch_bounds__(256) attn_prep_t_kernel(const SrcT* __restrict__ src, int64_t ld, int S, int Sp,
                                                          int col0, int nheads, uint16_t* dstT) {
   __shared__ __attribute__((aligned(16))) uint16_t t[HD][AT + 8];
   const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
@@ -451,23 +479,19 @@ __global__ void __launch_bounds__(256) attn_prep_t_kernel(const uint16_t* __rest
   __syncthreads();
   put_cols<HD>(dstT + ((int64_t)b * nheads + hh) * HD * Sp + row0, t, Sp);
 }
-
-// One lane's rotated row slices as MFMA A operands (hi/lo), d slices 32c + 8 lg.
+// V rows of the float32 qkv rounded to bf16 rows [b][head][Sp][HD] (zero past S).
 template <int HD>
-__device__ __forceinline__ void load_rot_frags(const uint16_t* row, bool ok, int pos, const float2* __restrict__ rope,
-                                               int lg, bf16x8 (&fh)[HD / 32], bf16x8 (&fl)[HD / 32]) {
-  constexpr int DC = HD / 32, HALF = HD / 2;
-#pragma unroll
-  for (int c = 0; c < DC / 2; ++c) {
-    const int i0 = 32 * c + 8 * lg;
-    float x1[8], x2[8];
-    unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
-    unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
-    if (ok) rope8(x1, x2, rope + (int64_t)pos * HALF + i0);
-    split8(x1, fh[c], fl[c]);
-    split8(x2, fh[c + DC / 2], fl[c + DC / 2]);
+__global__ void __launch_bounds__(256) attn_prep_rows_kernel(const float* __restrict__ src, int64_t ld, int S, int Sp,
+                                                            int col0, int nheads, uint16_t* dst) {
+  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
+  const float* base = src + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
+  uint16_t* out = dst + (((int64_t)b * nheads + hh) * Sp + row0) * HD;
+  for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
+    const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
+    *reinterpret_cast<uint4*>(out + r * HD + c) = load8_bf16(base + (int64_t)(row0 + r) * ld + c, row0 + r < S);
   }
 }
+
 template <int HD>
 __device__ __forceinline__ void load_frags(const uint16_t* row, bool ok, int lg, bf16x8 (&f)[HD / 32]) {
 #pragma unroll
@@ -506,7 +530,7 @@ template <int HD>
 __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs pp) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnF16Smem<HD>& sm = *reinterpret_cast<AttnF16Smem<HD>*>(smem_raw);
-  constexpr int DC = HD / 32, DT = HD / 16, HALF = HD / 2;
+  constexpr int DC = HD / 32, DT = HD / 16;
   const int nqb = gridDim.x;
   const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = h / (a.nh / a.nkv);
@@ -514,27 +538,16 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
   const int lr = lane & 15, lg = lane >> 4;
   const int q0 = qb * AT;
   const int64_t rowbase = (int64_t)b * a.S;
-  const uint16_t* Q = a.qkv + rowbase * a.ld + (int64_t)h * HD;
   const int64_t kvh = (int64_t)b * a.nkv + g;
   const uint16_t* Kh = pp.kh + kvh * pp.Sp * HD;
   const uint16_t* Kl = pp.kl + kvh * pp.Sp * HD;
   const uint16_t* Vt = pp.vt + kvh * HD * pp.Sp;
-  // this lane's query row, its 8-wide d slices 32c + 8 lg .. +8, rotated and split
+  // this lane's query row (rotated, hi/lo; zero rows past S), its 8-wide d slices 32c + 8 lg .. +8
   bf16x8 qh[DC], ql[DC];
   {
-    const int qi = q0 + 16 * w + lr;
-    const bool ok = qi < a.S;
-    const uint16_t* row = Q + (int64_t)qi * a.ld;
-#pragma unroll
-    for (int c = 0; c < DC / 2; ++c) {
-      const int i0 = 32 * c + 8 * lg;
-      float x1[8], x2[8];
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + i0) : make_uint4(0u, 0u, 0u, 0u), x1);
-      unpack8(ok ? *reinterpret_cast<const uint4*>(row + HALF + i0) : make_uint4(0u, 0u, 0u, 0u), x2);
-      if (ok) rope8(x1, x2, a.rope + (int64_t)qi * HALF + i0);
-      split8(x1, qh[c], ql[c]);
-      split8(x2, qh[c + DC / 2], ql[c + DC / 2]);
-    }
+    const int64_t qrow = (((int64_t)b * a.nh + h) * pp.Sp + q0 + 16 * w + lr) * HD;
+    load_frags<HD>(pp.qh + qrow, true, lg, qh);
+    load_frags<HD>(pp.ql + qrow, true, lg, ql);
   }
   const float sc = a.scale * kLog2e;
   // Scores are formed transposed (S^T = K Q^T): lane (lr, lg) holds keys
@@ -674,8 +687,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int q0 = qb * AT;
   const int64_t rowbase = (int64_t)b * a.S;
   const float sc = a.scale * kLog2e;
-  const uint16_t* Vp = a.qkv + rowbase * a.ld + (int64_t)(a.nh + a.nkv + g) * HD;
   const int64_t kvh = (int64_t)b * a.nkv + g;
+  const uint16_t* Vp = pp.vr + kvh * pp.Sp * HD;
   const uint16_t* Kh = pp.kh + kvh * pp.Sp * HD;
   const uint16_t* Kl = pp.kl + kvh * pp.Sp * HD;
   const uint16_t* Kht = pp.kht + kvh * HD * pp.Sp;
@@ -684,7 +697,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   {
     const int qi = q0 + 16 * w + lr;
     const bool ok = qi < a.S;
-    load_rot_frags<HD>(a.qkv + (rowbase + qi) * a.ld + (int64_t)h * HD, ok, qi, a.rope, lg, qh, ql);
+    const int64_t qrow = (((int64_t)b * a.nh + h) * pp.Sp + qi) * HD;
+    load_frags<HD>(pp.qh + qrow, true, lg, qh);
+    load_frags<HD>(pp.ql + qrow, true, lg, ql);
     load_frags<HD>(a.dO + (rowbase + qi) * a.ldo + (int64_t)h * HD, ok, lg, od);
   }
   // this lane's query for the scores (formed transposed: lane = query, its 4 values = 4 keys)
@@ -699,7 +714,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   Chunks<HD> ckh, ckl, cv, cth, ctl;
   ld_rows<HD>(ckh, Kh, HD, AT);
   ld_rows<HD>(ckl, Kl, HD, AT);
-  ld_rows<HD>(cv, Vp, a.ld, a.S);
+  ld_rows<HD>(cv, Vp, HD, AT);
   ld_cols<HD>(cth, Kht, pp.Sp);
   ld_cols<HD>(ctl, Klt, pp.Sp);
   for (int kb = 0; kb <= qb; ++kb) {
@@ -715,7 +730,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       const int kn = min(kb + 1, qb) * AT;
       ld_rows<HD>(ckh, Kh + (int64_t)kn * HD, HD, AT);
       ld_rows<HD>(ckl, Kl + (int64_t)kn * HD, HD, AT);
-      ld_rows<HD>(cv, Vp + (int64_t)kn * a.ld, a.ld, a.S - kn);
+      ld_rows<HD>(cv, Vp + (int64_t)kn * HD, HD, AT);
       ld_cols<HD>(cth, Kht + kn, pp.Sp);
       ld_cols<HD>(ctl, Klt + kn, pp.Sp);
     }
@@ -806,11 +821,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t rowbase = (int64_t)b * a.S;
   const float sc = a.scale * kLog2e;
   bf16x8 kh[DC], kl[DC], vv[DC];
-  {
-    const int kj = k0 + 16 * w + lr;
-    const bool ok = kj < a.S;
-    load_rot_frags<HD>(a.qkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + g) * HD, ok, kj, a.rope, lg, kh, kl);
-    load_frags<HD>(a.qkv + (rowbase + kj) * a.ld + (int64_t)(a.nh + a.nkv + g) * HD, ok, lg, vv);
+  {   // this lane's key row: rotated K hi/lo and V, prepared rows (zero past S)
+    const int64_t krow = (((int64_t)b * a.nkv + g) * pp.Sp + k0 + 16 * w + lr) * HD;
+    load_frags<HD>(pp.kh + krow, true, lg, kh);
+    load_frags<HD>(pp.kl + krow, true, lg, kl);
+    load_frags<HD>(pp.vr + krow, true, lg, vv);
   }
   f32x4 dk[DT], dv[DT];
 #pragma unroll
@@ -1129,13 +1144,13 @@ __global__ void __launch_bounds__(256) loss_sum_kernel(const float* __restrict__
 }  // namespace
 
 // ================================================================== launchers
-int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, float* rstd, hipStream_t s,
-                uint16_t* y_lo) {
+int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint16_t* y, int64_t ldy, float* rstd,
+                hipStream_t s, uint16_t* y_lo) {
   LSQ_CHECK(H % 4 == 0 && H <= 4 * 256 * kNormMaxV, LSQ_ERR_SHAPE,
             "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
   if (T == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(x, w, T, H, eps, y, rstd, y_lo);
+  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(x, w, T, H, eps, y, ldy, rstd, y_lo);
   prof_end(tok, s, PROF_ELEM, 0.0, (4.0 + 2.0 + (y_lo ? 2.0 : 0.0)) * T * (double)H + 2.0 * H + (rstd ? 4.0 * T : 0.0));
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
@@ -1208,17 +1223,7 @@ int allow_smem(K* kernel, size_t bytes) {
 size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd) {
   const PrepPtrs p = prep_ptrs(nullptr, B, S, nh, nkv, hd, bwd);
   const int64_t ekv = (int64_t)B * nkv * p.Sp * hd, eq = (int64_t)B * nh * p.Sp * hd;
-  return (size_t)(2 * (bwd ? 5 * ekv + 5 * eq : 3 * ekv));
-}
-
-// K rotated and split (and, for the backward, transposed) and V^T.
-template <int HD>
-void launch_prep_kv(const uint16_t* qkv, int64_t ld, int B, int S, int nh, int nkv, const float2* rope,
-                    const PrepPtrs& p, bool bwd, hipStream_t s) {
-  const dim3 grid(p.Sp / AT, nkv, B);
-  attn_prep_rot_kernel<HD><<<grid, 256, 0, s>>>(qkv, ld, S, p.Sp, nh, nkv, rope, p.kh, p.kl, bwd ? p.kht : nullptr,
-                                                bwd ? p.klt : nullptr);
-  if (!bwd) attn_prep_t_kernel<HD><<<grid, 256, 0, s>>>(qkv, ld, S, p.Sp, nh + nkv, nkv, p.vt);
+  return (size_t)(2 * (bwd ? 5 * ekv + 5 * eq : 3 * ekv + 2 * eq));
 }
 
 int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
@@ -1235,11 +1240,16 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   dim3 grid((a.S + AT - 1) / AT, a.nh, B);
   const double flops = 2.0 * 2.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
   int tok = prof_begin(s);
+  // Q and K rotated and split into hi/lo rows (one launch), V^T
+  const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B);
+  const RotOut oq{pp.qh, pp.ql, nullptr, nullptr}, ok{pp.kh, pp.kl, nullptr, nullptr};
   if (a.hd == 128) {
-    launch_prep_kv<128>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, false, s);
+    attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
+    attn_prep_t_kernel<128, float><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vt);
     attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a, pp);
   } else {
-    launch_prep_kv<64>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, false, s);
+    attn_prep_rot_kernel<64><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
+    attn_prep_t_kernel<64, float><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vt);
     attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a, pp);
   }
   prof_end(tok, s, PROF_ATTN, flops, 0.0);
@@ -1267,17 +1277,19 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   LSQ_CHECK(a.dk_part && a.dv_part && a.prep, LSQ_ERR_WORKSPACE, "attention_bwd: workspace buffers missing");
   const PrepPtrs pp = prep_ptrs(a.prep, B, a.S, a.nh, a.nkv, a.hd, true);
   dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
-  const dim3 gq(pp.Sp / AT, a.nh, B);
+  // Q and K rotated, split and transposed (one launch), V rows, dO^T
+  const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B), gq(pp.Sp / AT, a.nh, B);
+  const RotOut oq{pp.qh, pp.ql, pp.qht, pp.qlt}, ok{pp.kh, pp.kl, pp.kht, pp.klt};
   if (a.hd == 128) {
-    launch_prep_kv<128>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, true, s);
-    attn_prep_rot_kernel<128><<<gq, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.rope, pp.qh, pp.ql, pp.qht, pp.qlt);
-    attn_prep_t_kernel<128><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
+    attn_prep_rows_kernel<128><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vr);
+    attn_prep_t_kernel<128, uint16_t><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
     attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b, pp);
   } else {
-    launch_prep_kv<64>(a.qkv, a.ld, B, a.S, a.nh, a.nkv, a.rope, pp, true, s);
-    attn_prep_rot_kernel<64><<<gq, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.rope, pp.qh, pp.ql, pp.qht, pp.qlt);
-    attn_prep_t_kernel<64><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_prep_rot_kernel<64><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
+    attn_prep_rows_kernel<64><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vr);
+    attn_prep_t_kernel<64, uint16_t><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
     attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b, pp);
   }

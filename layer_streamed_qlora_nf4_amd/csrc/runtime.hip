@@ -573,6 +573,7 @@ struct StepWs {
   char* acts;        // n_kept x acts_bytes of kept forward activations
   size_t acts_bytes;
   int n_kept;
+  uint16_t* lora_t;  // every layer's adapters transposed block by block, once per step
   float* xr[2];      // reference mode: the adapters-off residual stream, ping-pong [T, H]
   float* ref_loss_tmp;  // reference mode: its mean loss when the caller wants rows only
   size_t total;
@@ -628,6 +629,11 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
   w.gemm = take(w.gemm_bytes);
   w.layer_bytes = layer_ws_bytes(c, B, S, keep);
   w.layer = take(w.layer_bytes);
+  {
+    lsq_lora_layout LL;
+    lora_layout(c, &LL);
+    w.lora_t = static_cast<uint16_t*>(take(2 * LL.layer_elems * (uint64_t)c->n_layers));
+  }
   if (n_kept > 0) {
     w.acts_bytes = layer_acts_bytes(c, B, S);
     w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)n_kept));
@@ -679,7 +685,7 @@ static int head_pass(const lsq_model_cfg* cfg, const lsq_resident* res, const vo
                      const float* x, const int32_t* ids, int B, int S, float* logits_out, float* loss_rows,
                      float* loss, float* dxf, hipStream_t s) {
   const int T = B * S, H = cfg->hidden, V = cfg->vocab;
-  if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, nullptr, s))
+  if (int e = rmsnorm_fwd(x, static_cast<const uint16_t*>(res->final_norm), T, H, cfg->rms_eps, w.xf, H, nullptr, s))
     return e;
   for (int r0 = 0; r0 < T; r0 += w.chunk) {
     const int n = std::min(w.chunk, T - r0);
@@ -783,6 +789,11 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   auto x_at = [&](int i) { return xs + (uint64_t)i * T * H; };
 
   if (int e = zero_words(w.bad, 1, 1, 1, s)) return e;
+  // once per step: the rotary table and zeroed counters of the layer
+  // workspace, and the adapters transposed for the backward's products
+  if (int e = layer_prepare(cfg, B, S, w.layer, s)) return e;
+  if (!(flags & LSQ_STEP_FORWARD_ONLY))
+    if (int e = adapter_transpose(cfg, lora, w.lora_t, L, s)) return e;
   if (int e = embed_gather(ids, static_cast<const uint16_t*>(embed), T, H, V, x_at(0), w.bad, s)) return e;
   // the head's copy is queued on the copy stream behind the forward's layer
   // copies (issued after the prefetch of the last layer) and waited for at the turn
@@ -867,7 +878,8 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     LayerHook hook{early_release_hook, &actx};
     float* grad = res->lora_grad + (uint64_t)i * LL.layer_elems;
     const int tl = tl_begin(pool, LSQ_TL_BWD, i, s);
-    if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
+    if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, w.lora_t + (uint64_t)i * LL.layer_elems,
+                          x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
                           s, early ? &hook : nullptr, acts_at(i)))
       return e;
     if (int e = tl_end(pool, tl, s)) return e;

@@ -110,8 +110,11 @@ def test_vram_prediction_terms_and_refusal():
     assert (b.total - b.margin) - (rc.total - rc.margin) == b.saved_activations
     per_token_layer = k.saved_activations / (512 * cfg.n_layers)
     H, I, r = cfg.hidden, cfg.intermediate, cfg.lora_r
-    # the bf16/f32 tensors the backward reads, 256-byte aligned each
-    approx = 2 * H + 2 * 6144 + 2 * 4096 + 4 * 4096 + 4 * 32 + 4 * H + 2 * H + 4 * I + 2 * I + 2 * 7 * r + 4 * 7 * r
+    # the bf16/f32 tensors the backward reads, 256-byte aligned each: the normed
+    # input as a bf16 hi/lo pair, q/k/v in float32, the attention output (bf16,
+    # f32), the log-sum-exp, the mid residual, its norm, gate/up, the SwiGLU
+    # product, and every U in bf16 and f32
+    approx = 4 * H + 4 * 6144 + 2 * 4096 + 4 * 4096 + 4 * 32 + 4 * H + 2 * H + 4 * I + 2 * I + 2 * 7 * r + 4 * 7 * r
     assert approx <= per_token_layer <= approx * 1.01
     assert k.total - k.saved_activations < rc.total   # the layer scratch no longer holds them
 

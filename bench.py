@@ -53,20 +53,121 @@ def h2d_probe(torch, nbytes=1 << 30, reps=5):
     return best
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary of this kernel, or None if that summary is missing or was taken
-    from a different kernel source."""
+# Kernel families, as the library's timing hooks credit them, by kernel name
+# (rocprofv3 prints demangled names) and the source file that holds them.
+FAMILY_KERNELS = [
+    ("gemm_fwd_nf4_lora", ("gemm_fwd_nf4_dma_kernel", "gemm_fwd_pp_kernel<0,"), "gemm.hip"),
+    ("gemm_bwd_nf4_lora", ("gemm_bwd_nf4_dma_kernel", "gemm_bwd_pp_kernel<0,"), "gemm.hip"),
+    ("gemm_bf16_weights", ("gemm_fwd_bf16_dma_kernel", "gemm_bwd_bf16_dma_kernel", "gemm_fwd_pp_kernel<1,",
+                           "gemm_bwd_pp_kernel<1,"), "gemm.hip"),
+    ("lora_skinny", ("lora_down_kernel", "lora_g_kernel", "lora_grads_kernel"), "lora.hip"),
+    ("attention", ("attn_",), "layer_ops.hip"),
+    ("elementwise", ("rmsnorm_fwd_kernel", "rmsnorm_bwd_kernel", "swiglu_fwd_kernel", "swiglu_bwd_kernel",
+                     "embed_kernel", "ce_kernel", "ce_grad_kernel", "loss_sum_kernel"), "layer_ops.hip"),
+    ("other", ("splitk_reduce_kernel", "adapter_transpose_kernel", "transpose_rows_kernel"), "gemm.hip"),
+]
+
+
+def family_of(kernel_name):
+    base = kernel_name.split("(")[0]
+    for fam, keys, _ in FAMILY_KERNELS:
+        if any(k in base for k in keys):
+            return fam
+    return None
+
+
+def source_sha(fname):
     import hashlib
+    return hashlib.sha256(open(os.path.join(ROOT, "layer_streamed_qlora_nf4_amd", "csrc", fname), "rb").read()).hexdigest()
+
+
+def _read_csvs(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _counter_by_dispatch(directory):
+    """{dispatch id: (kernel name, counter value)} of a single-counter rocprofv3 --pmc run."""
+    out = {}
+    for r in _read_csvs(directory, "counter_collection.csv"):
+        out[(r.get("Dispatch_Id"), r.get("Correlation_Id"))] = (r["Kernel_Name"], float(r["Counter_Value"]))
+    return out
+
+
+def summarize_profiles(directory, workload):
+    """rocprofv3 outputs under directory -> profiles/ records and markdown tables.
+
+    kernels/      rocprofv3 --kernel-trace --stats of the bench command
+    fetch/ write/ rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE) of bench.py --counters
+    calib_fetch/ calib_write/  the same counters of bench.py --copy-calibration
+    counters.json the stdout of bench.py --counters (the library's algorithmic work)
+    Counter values are KiB per dispatch; each is scaled by what it reads for a
+    plain device copy of known size (copy bytes / counter bytes)."""
+    wl = workload.replace("-", "_")
+    # per-family kernel durations from the kernel trace
+    durs = {}
+    for r in _read_csvs(os.path.join(directory, "kernels"), "kernel_trace.csv"):
+        fam = family_of(r["Kernel_Name"])
+        if fam:
+            durs.setdefault(fam, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # copy calibration: the copy kernel of bench.py --copy-calibration moves 1 GiB per dispatch
+    def scale(sub):
+        vals = [v for (name, v) in _counter_by_dispatch(os.path.join(directory, sub)).values() if "copyBuffer" in name]
+        return (1 << 30) / (sum(vals) / len(vals) * 1024.0) if vals else None
+    f_fetch, f_write = scale("calib_fetch"), scale("calib_write")
+    fetch = _counter_by_dispatch(os.path.join(directory, "fetch"))
+    write = _counter_by_dispatch(os.path.join(directory, "write"))
+    algo = json.load(open(os.path.join(directory, "counters.json")))["families"]
+    fams = {}
+    for fam, _, src in FAMILY_KERNELS:
+        fv = [v for name, v in fetch.values() if family_of(name) == fam]
+        wv = [v for name, v in write.values() if family_of(name) == fam]
+        a = algo.get(fam, {})
+        rec = {"family": fam, "workload": workload, "source": f"layer_streamed_qlora_nf4_amd/csrc/{src}",
+               "source_sha256": source_sha(src)}
+        if durs.get(fam):
+            rec["rocprof_calls"] = len(durs[fam])
+            rec["rocprof_avg_us"] = sum(durs[fam]) / len(durs[fam])
+        if a.get("launches"):
+            rec["algorithmic_flops_per_launch"] = a["flops"] / a["launches"]
+            rec["algorithmic_bytes_per_launch"] = a["bytes"] / a["launches"]
+        if fv and wv and f_fetch and f_write:
+            rec["dispatches_counted"] = len(fv)
+            rec["fetch_scale"], rec["write_scale"] = round(f_fetch, 4), round(f_write, 4)
+            rec["fetch_bytes_per_launch"] = sum(fv) / len(fv) * 1024.0 * f_fetch
+            rec["write_bytes_per_launch"] = sum(wv) / len(wv) * 1024.0 * f_write
+            rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        fams[fam] = rec
+        with open(os.path.join(ROOT, "profiles", f"traffic_{fam}_{wl}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print(f"| family | rocprof calls | avg us | algorithmic MB / launch | FETCH MB | WRITE MB | traffic / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    for fam, r in fams.items():
+        am = r.get("algorithmic_bytes_per_launch")
+        tr = r.get("traffic_bytes_per_launch")
+        print(f"| {fam} | {r.get('rocprof_calls', '-')} | {r.get('rocprof_avg_us', float('nan')):.1f} | "
+              f"{(am or float('nan')) / 1e6:.2f} | {r.get('fetch_bytes_per_launch', float('nan')) / 1e6:.2f} | "
+              f"{r.get('write_bytes_per_launch', float('nan')) / 1e6:.2f} | "
+              f"{(tr / am) if (tr and am) else float('nan'):.2f} |")
+    print(f"\ncopy calibration: FETCH_SIZE x {f_fetch}, WRITE_SIZE x {f_write}")
+
+
+def profile_record(kernel, workload):
+    """The committed rocprofv3 record of one kernel family on a workload, or
+    None if it is missing or was taken from a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload.replace('-', '_')}.json")
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if source_sha(os.path.basename(rec["source"])) != rec.get("source_sha256"):
+            return None
+        return rec
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
-        return None
-    return rec["traffic_bytes_per_launch"]
 
 
 def gemm_probe(torch, n=8192, reps=10):
@@ -414,7 +515,18 @@ def main():
     ap.add_argument("--forward-only", action="store_true",
                     help="only run forward passes of the stack (for per-dispatch counters of the forward GEMMs) "
                          "and exit")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run --warmup + --steps full training steps of the stack (for per-dispatch "
+                         "rocprofv3 counters and kernel traces), print the library's algorithmic work per kernel "
+                         "family over the --steps steps, and exit")
+    ap.add_argument("--summarize-profiles", default=None, metavar="DIR",
+                    help="read the rocprofv3 CSV outputs under DIR (subdirectories kernels/, fetch/, write/, "
+                         "calib_fetch/, calib_write/ and the --counters JSON as counters.json), write the "
+                         "per-family records under profiles/ and print them as markdown; no GPU needed")
     a = ap.parse_args()
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles, a.workload)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the data-parallel path is designed "
               f"but not implemented, so there is no multi-GPU figure to report", file=sys.stderr)
@@ -456,6 +568,24 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"forward_only_steps": a.warmup + a.steps, "workload": cfg.name,
                           "loss": runner.loss.item()}))
+        runner.close()
+        return
+    if a.counters:
+        for _ in range(a.warmup):
+            runner.step(ids)
+        torch.cuda.synchronize()
+        lib.call("lsq_prof_enable", 1)
+        for _ in range(a.steps):
+            runner.step(ids)
+        torch.cuda.synchronize()
+        entries = (lib.ProfEntry * 8)()
+        n = C.c_int32()
+        lib.call("lsq_prof_read", entries, 8, C.byref(n))
+        lib.call("lsq_prof_enable", 0)
+        print(json.dumps({"counter_steps": a.steps, "warmup": a.warmup, "workload": cfg.name,
+                          "loss": runner.loss.item(),
+                          "families": {e.name.decode(): {"launches": e.launches, "flops": e.flops, "bytes": e.bytes}
+                                       for e in entries[:n.value]}}))
         runner.close()
         return
     for _ in range(a.warmup):
@@ -521,6 +651,7 @@ def main():
     d = prof[dominant]
     peak = peaks[dominant]
     achieved = d["flops"] / (d["ms"] * 1e-3) / 1e12
+    rec_dom = profile_record(dominant, cfg.name)
     # copy events cover the first 1024 copies between two stats reads: rate from those,
     # busy time scaled to every copy of the timed steps
     h2d_gbps = st.timed_bytes / (st.copy_ms * 1e-3) / 1e9 if st.copy_ms else 0.0
@@ -549,8 +680,13 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(dominant, cfg.name),
+                     "frac": round(achieved / peak, 4),
+                     "traffic": (rec_dom or {}).get("traffic_bytes_per_launch"),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": d["bytes"] / max(1, d["launches"]),
+                     "rocprof_avg_launch_us": (rec_dom or {}).get("rocprof_avg_us"),
+                     "frac_rocprof": (round(d["flops"] / max(1, d["launches"]) / (rec_dom["rocprof_avg_us"] * 1e-6)
+                                            / 1e12 / peak, 4) if rec_dom and rec_dom.get("rocprof_avg_us") else None),
                      "frac_of_gemm_probe": round(achieved / gprobe, 4) if peak == MFMA_BF16_PEAK_TFLOPS else None,
                      "gemm_probe_TFLOPs": round(gprobe, 1),
                      "launches": d["launches"], "avg_launch_us": round(d["ms"] / max(1, d["launches"]) * 1e3, 2),
@@ -565,7 +701,9 @@ def main():
         "overlap": overlap,
         "kernels": {k: {"ms_per_step": round(v["ms"] / a.steps, 3), "launches_per_step": v["launches"] / a.steps,
                         "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None,
-                        "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] and v["bytes"] else None}
+                        "GBps": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] and v["bytes"] else None,
+                        "algorithmic_bytes_per_launch": v["bytes"] / v["launches"] if v["launches"] else None,
+                        "traffic_bytes_per_launch": (profile_record(k, cfg.name) or {}).get("traffic_bytes_per_launch")}
                     for k, v in prof.items()},
         "hbm_bound": {
             "elementwise": {"GBps": round(prof["elementwise"]["bytes"] / (prof["elementwise"]["ms"] * 1e-3) / 1e9, 1),

@@ -127,6 +127,22 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U, int64
                         const void* dY, void* dX, float* dA, float* dB, int32_t accumulate,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* nf4_lora_linear_bwd with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Its scratch is a static device array of
+ * LSQ_NOALLOC_SCRATCH_BYTES per GPU, created with the library's code on each
+ * device and held until the process ends; the call itself allocates nothing.
+ * A shape whose nf4_lora_linear_workspace_size exceeds that size is refused
+ * with LSQ_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialized by the caller.  The arguments and
+ * results are those of nf4_lora_linear_bwd, bit for bit. */
+#define LSQ_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int nf4_lora_linear_bwd_noalloc(const lsq_weight* W, const void* X, const void* U, int64_t M,
+                                const void* A, const void* B, int32_t r, float scale, int32_t dtype,
+                                const void* dY, void* dX, float* dA, float* dB, int32_t accumulate,
+                                void* stream);
+
 /* ---------------------------------------------------------------- model shape
  * A Llama / Qwen2 decoder stack (LS-docs "How it works": transformers' own
  * classes).  weight_kind selects the streamed base format (LS-docs "Turn it

@@ -17,6 +17,8 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include <hip/hip_ext.h>
 
@@ -1637,6 +1639,48 @@ int nf4_lora_linear_bwd(const lsq_weight* W, const void* X, const void* U_in, in
   g.gA = dA;
   g.gB = dB;
   return lora_grads(g, Mi, accumulate, lw.gw, lw.gw_bytes, lw.cnt, s);
+}
+
+// ------------------------------------------------------------ without a workspace
+// The scratch of nf4_lora_linear_bwd_noalloc: one static array per GPU (each
+// device holds its own copy from module load until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, taken once per device on the
+// first call there (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[LSQ_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;   // per device
+  int dev = 0;
+  LSQ_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    LSQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    LSQ_CHECK(p, LSQ_ERR_HIP, "nf4_lora_linear_bwd_noalloc: no device address for the scratch array");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LSQ_OK;
+}
+
+int nf4_lora_linear_bwd_noalloc(const lsq_weight* W, const void* X, const void* U, int64_t M, const void* A,
+                                const void* B, int32_t r, float scale, int32_t dtype, const void* dY, void* dX,
+                                float* dA, float* dB, int32_t accumulate, void* stream) {
+  if (int e = check_weight(W)) return e;
+  LSQ_CHECK(M >= 0 && M < (1 << 30) && r >= 8 && r <= 64 && r % 8 == 0, LSQ_ERR_SHAPE,
+            "linear_bwd_noalloc: bad M or r");
+  const size_t need = nf4_lora_linear_workspace_size(M, W->n_out, W->n_in, r, dtype);
+  LSQ_CHECK(need <= LSQ_NOALLOC_SCRATCH_BYTES, LSQ_ERR_WORKSPACE,
+            "linear_bwd_noalloc: this shape needs %zu bytes of scratch, above the static %llu (use "
+            "nf4_lora_linear_bwd with a workspace)", need, (unsigned long long)LSQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int e = scratch_address(&ws)) return e;
+  // the arrival counters in it are zeroed by a kernel inside the call; nothing else must start at zero
+  return nf4_lora_linear_bwd(W, X, U, M, A, B, r, scale, dtype, dY, dX, dA, dB, accumulate, ws,
+                             LSQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

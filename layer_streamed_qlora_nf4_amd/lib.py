@@ -17,6 +17,7 @@ LSQ_POOL_RESIDENT, LSQ_POOL_POISON = 1, 2
 LSQ_STEP_FORWARD_ONLY, LSQ_STEP_DEBUG_EARLY_RELEASE, LSQ_STEP_KEEP_ACTIVATIONS, LSQ_STEP_REFERENCE_FORWARD = 1, 2, 4, 8
 LSQ_STEP_STREAM_LARGE, LSQ_STEP_RECOMPUTE_ALL = 16, 32
 LSQ_TL_COPY, LSQ_TL_FWD, LSQ_TL_BWD, LSQ_TL_HEAD, LSQ_TL_LARGE_COPY = 0, 1, 2, 3, 4
+LSQ_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 STATUS = {0: "LSQ_OK", -1: "LSQ_ERR_INVALID", -2: "LSQ_ERR_SHAPE", -3: "LSQ_ERR_ALIGN", -4: "LSQ_ERR_NONFINITE",
           -5: "LSQ_ERR_OOM", -6: "LSQ_ERR_HIP", -7: "LSQ_ERR_STATE", -8: "LSQ_ERR_REFUSED", -9: "LSQ_ERR_WORKSPACE",
@@ -99,6 +100,8 @@ _SIGS = {
     "nf4_lora_linear_fwd": (C.c_int, [C.POINTER(Weight), _P, _P, _I64, _P, _P, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
     "nf4_lora_linear_bwd": (C.c_int, [C.POINTER(Weight), _P, _P, _I64, _P, _P, _I32, _F, _I32, _P, _P, _P, _P, _I32,
                                       _P, _SZ, _P]),
+    "nf4_lora_linear_bwd_noalloc": (C.c_int, [C.POINTER(Weight), _P, _P, _I64, _P, _P, _I32, _F, _I32, _P, _P, _P,
+                                              _P, _I32, _P]),
     "lsq_blob_layout_get": (C.c_int, [C.POINTER(ModelCfg), C.POINTER(BlobLayout)]),
     "lsq_lora_layout_get": (C.c_int, [C.POINTER(ModelCfg), C.POINTER(LoraLayout)]),
     "decoder_layer_workspace_size": (_SZ, [C.POINTER(ModelCfg), _I32, _I32]),

@@ -53,26 +53,44 @@ def h2d_probe(torch, nbytes=1 << 30, reps=5):
     return best
 
 
-# Kernel families, as the library's timing hooks credit them, by kernel name
-# (rocprofv3 prints demangled names) and the source file that holds them.
+# Kernel families, as the library's timing hooks credit them: kernel
+# identifiers (rocprofv3 prints demangled names), the first template argument
+# where it decides the family (the weight kind of the register-path GEMMs),
+# and the source file that holds them.
 FAMILY_KERNELS = [
-    ("gemm_fwd_nf4_lora", ("gemm_fwd_nf4_dma_kernel", "gemm_fwd_pp_kernel<0,"), "gemm.hip"),
-    ("gemm_bwd_nf4_lora", ("gemm_bwd_nf4_dma_kernel", "gemm_bwd_pp_kernel<0,"), "gemm.hip"),
-    ("gemm_bf16_weights", ("gemm_fwd_bf16_dma_kernel", "gemm_bwd_bf16_dma_kernel", "gemm_fwd_pp_kernel<1,",
-                           "gemm_bwd_pp_kernel<1,"), "gemm.hip"),
+    ("gemm_fwd_nf4_lora", ("gemm_fwd_nf4_dma_kernel", "gemm_fwd_pp_kernel<0"), "gemm.hip"),
+    ("gemm_bwd_nf4_lora", ("gemm_bwd_nf4_dma_kernel", "gemm_bwd_pp_kernel<0"), "gemm.hip"),
+    ("gemm_bf16_weights", ("gemm_fwd_bf16_dma_kernel", "gemm_bwd_bf16_dma_kernel", "gemm_fwd_pp_kernel<1",
+                           "gemm_bwd_pp_kernel<1"), "gemm.hip"),
     ("lora_skinny", ("lora_down_kernel", "lora_g_kernel", "lora_grads_kernel"), "lora.hip"),
-    ("attention", ("attn_",), "layer_ops.hip"),
+    ("attention", ("attn_prep_rot_kernel", "attn_prep_t_kernel", "attn_prep_rows_kernel", "attn_fwd_bf16_kernel",
+                   "attn_dot_kernel", "attn_bwd_dq_bf16_kernel", "attn_bwd_dkdv_bf16_kernel",
+                   "attn_dkdv_reduce_kernel"), "layer_ops.hip"),
     ("elementwise", ("rmsnorm_fwd_kernel", "rmsnorm_bwd_kernel", "swiglu_fwd_kernel", "swiglu_bwd_kernel",
-                     "embed_kernel", "ce_kernel", "ce_grad_kernel", "loss_sum_kernel"), "layer_ops.hip"),
+                     "embed_kernel", "ce_kernel", "loss_sum_kernel"), "layer_ops.hip"),
     ("other", ("splitk_reduce_kernel", "adapter_transpose_kernel", "transpose_rows_kernel"), "gemm.hip"),
 ]
 
 
 def family_of(kernel_name):
-    base = kernel_name.split("(")[0]
+    """The family of a demangled kernel name: its identifier (the last name
+    before the argument list, with its first template argument) matched exactly."""
+    head = kernel_name.strip()
+    if head.endswith(")"):                            # drop the argument list: the last balanced (...)
+        depth = 0
+        for i in range(len(head) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(head[i], 0)
+            if depth == 0:
+                head = head[:i]
+                break
+    ident = head.split("::")[-1].strip()             # e.g. gemm_fwd_pp_kernel<0, 1>
+    name, _, targs = ident.partition("<")
+    first = targs.split(",")[0].rstrip(">").strip()
     for fam, keys, _ in FAMILY_KERNELS:
-        if any(k in base for k in keys):
-            return fam
+        for k in keys:
+            kname, _, karg = k.partition("<")
+            if name == kname and (not karg or karg == first):
+                return fam
     return None
 
 

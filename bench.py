@@ -530,6 +530,9 @@ def main():
                          "forward and backward, print its rates and exit (for per-kernel counters)")
     ap.add_argument("--mm-probe", action="store_true",
                     help="only run the torch.mm bf16 8192^3 probe, print it and exit (for counters)")
+    ap.add_argument("--layer", action="store_true",
+                    help="only time one 8B-shaped decoder layer at 2048 tokens (forward + backward with its "
+                         "recompute), print its per-family rates and exit (for per-kernel traces)")
     ap.add_argument("--forward-only", action="store_true",
                     help="only run forward passes of the stack (for per-dispatch counters of the forward GEMMs) "
                          "and exit")
@@ -556,6 +559,11 @@ def main():
         return
     if a.mm_probe:
         print(json.dumps({"torch_mm_bf16_8192_TFLOPs": round(gemm_probe(torch), 1)}))
+        return
+    if a.layer:
+        from layer_streamed_qlora_nf4_amd import configs as configs_, lib as lib_, model as model_
+        lib_.load()
+        print(json.dumps(layer_rates(torch, lib_, model_, configs_)))
         return
     if a.linear:
         from layer_streamed_qlora_nf4_amd import lib as lib_

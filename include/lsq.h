@@ -265,7 +265,17 @@ int shard_store_load(const char* path, const lsq_model_cfg* expect, int32_t flag
  * layer once at create and never again: the acceptance partner of a streamed
  * run, same kernels, same bytes (LS-docs "Bit-exact is two claims, not one").
  * dev_slots: n_buffers * slot_stride bytes of device memory owned by the
- * caller; slot_stride >= shard_store_layer_bytes() and a multiple of 4096. */
+ * caller; slot_stride >= shard_store_layer_bytes() and a multiple of 4096.
+ * copy_stream: the caller's stream for the layer copies, or NULL.  The overlap
+ * needs the copy stream to run while the compute stream is busy, which HIP
+ * does not promise: streams share a few hardware queues (GPU_MAX_HW_QUEUES),
+ * and two streams on one queue run in submission order.  So a streaming pool
+ * checks at create (a kernel on the compute stream waits, at most 20 ms, for a
+ * flag set by a kernel on the copy stream, using slot 0's first bytes) and, if
+ * the copy stream is NULL, the compute stream itself, or fails the check,
+ * copies on a stream of its own that passes it (destroyed with the pool; a
+ * message on stderr if none does).  layer_pool_copy_stream names the stream in
+ * use.  A resident pool copies once, on copy_stream or else compute_stream. */
 typedef struct lsq_pool lsq_pool;
 enum {
   LSQ_POOL_RESIDENT = 1,
@@ -274,6 +284,9 @@ enum {
 int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots, uint64_t slot_stride,
                       void* compute_stream, void* copy_stream, int32_t flags, lsq_pool** out);
 void layer_pool_destroy(lsq_pool* pool);
+/* The stream the pool's layer copies run on (*stream; the pool's own when it
+ * replaced or was not given one). */
+int layer_pool_copy_stream(const lsq_pool* pool, void** stream);
 /* Enqueue the copy of `layer` into a free slot on the copy stream; no-op if it
  * is already in a slot.  LSQ_ERR_STATE if every slot is held. */
 int stream_layer_prefetch(lsq_pool* pool, int32_t layer);

@@ -337,6 +337,7 @@ struct lsq_pool {
   char* dev;
   uint64_t stride;
   hipStream_t compute, copy;
+  hipStream_t own_copy = nullptr;   // a copy stream the pool created (see copy_stream_runs_beside)
   int flags;
   bool resident;
   std::vector<Slot> slots;
@@ -402,6 +403,86 @@ int copy_into(lsq_pool* p, int si, int layer) {
   p->stats.copy_bytes += p->store->layer_bytes;
   return LSQ_OK;
 }
+// ---- can the copy stream run while the compute stream is busy?
+// HIP places streams on a few hardware queues (GPU_MAX_HW_QUEUES, 4 by
+// default); once there are more streams than queues, a new stream shares the
+// queue of an existing one, and work on two streams of one queue runs in
+// submission order.  A copy stream on the compute stream's queue waits behind
+// every kernel enqueued before each copy, so the copies stop overlapping
+// compute (a step of the 8B-shaped stack went from 142 to 197 ms when the
+// caller had created two other streams first).  The check: a kernel on the
+// compute stream waits, for at most kProbeMs, for a flag that a kernel on the
+// copy stream sets.  Both loops end on their own: the wait by time and by an
+// iteration cap, whatever the other stream does.
+constexpr int kProbeMs = 20;
+__global__ void pool_probe_clear_kernel(int* w) {
+  if (threadIdx.x < 2) w[threadIdx.x] = 0;
+}
+__global__ void pool_probe_set_kernel(int* w) { __hip_atomic_store(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__global__ void pool_probe_wait_kernel(int* w, long long ticks, int max_iter) {
+  const long long t0 = wall_clock64();
+  int seen = 0;
+  for (int i = 0; i < max_iter; ++i) {
+    seen = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (seen || wall_clock64() - t0 > ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  w[1] = seen;
+}
+
+// *ok: a kernel on `copy` ran while the compute stream was busy.  Uses the
+// first 8 bytes of slot 0, which holds nothing before the first copy.
+int copy_stream_runs_beside(lsq_pool* p, hipStream_t copy, bool* ok) {
+  int dev = 0, khz = 0;
+  LSQ_HIP(hipGetDevice(&dev));
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+  int* w = reinterpret_cast<int*>(p->dev);
+  hipEvent_t cleared;
+  LSQ_HIP(hipEventCreateWithFlags(&cleared, hipEventDisableTiming));
+  pool_probe_clear_kernel<<<1, 64, 0, p->compute>>>(w);
+  LSQ_HIP(hipEventRecord(cleared, p->compute));
+  pool_probe_wait_kernel<<<1, 64, 0, p->compute>>>(w, (long long)khz * kProbeMs, 1 << 20);
+  LSQ_HIP(hipStreamWaitEvent(copy, cleared, 0));
+  pool_probe_set_kernel<<<1, 64, 0, copy>>>(w);
+  int res[2] = {0, 0};
+  LSQ_HIP(hipMemcpyAsync(res, w, sizeof(res), hipMemcpyDeviceToHost, p->compute));
+  LSQ_HIP(hipStreamSynchronize(copy));
+  LSQ_HIP(hipStreamSynchronize(p->compute));
+  LSQ_HIP(hipGetLastError());
+  LSQ_HIP(hipEventDestroy(cleared));
+  *ok = res[1] != 0;
+  return LSQ_OK;
+}
+
+// Keep the caller's copy stream if it runs beside the compute stream, else
+// create streams until one does (each new stream goes to the least used
+// queue, so a few tries reach a queue of its own).
+int choose_copy_stream(lsq_pool* p) {
+  bool ok = false;
+  if (p->copy && p->copy != p->compute)
+    if (int e = copy_stream_runs_beside(p, p->copy, &ok)) return e;
+  std::vector<hipStream_t> tried;
+  for (int t = 0; !ok && t < 4; ++t) {
+    hipStream_t s = nullptr;
+    LSQ_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+    tried.push_back(s);
+    if (int e = copy_stream_runs_beside(p, s, &ok)) return e;
+    if (ok) {
+      p->own_copy = s;
+      p->copy = s;
+      tried.pop_back();
+    }
+  }
+  for (hipStream_t s : tried) LSQ_HIP(hipStreamDestroy(s));
+  if (!ok && !p->copy) {
+    LSQ_HIP(hipStreamCreateWithFlags(&p->own_copy, hipStreamNonBlocking));
+    p->copy = p->own_copy;
+  }
+  if (!ok)
+    fprintf(stderr, "layer_pool_create: no copy stream found that runs beside the compute stream; layer copies "
+                    "will serialize with compute\n");
+  return LSQ_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -417,8 +498,6 @@ int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots
               "stream_buffers must be in [2, 8] (got %d): a refusal, not a clamp", n_buffers);
   LSQ_CHECK(slot_stride >= store->layer_bytes && slot_stride % 4096 == 0 && aligned16(dev_slots), LSQ_ERR_ALIGN,
             "layer_pool_create: slot stride must cover a blob and be a multiple of 4096");
-  LSQ_CHECK(compute_stream != copy_stream || resident, LSQ_ERR_INVALID,
-            "layer_pool_create: the copy stream must differ from the compute stream");
   lsq_pool* p = new (std::nothrow) lsq_pool();
   LSQ_CHECK(p, LSQ_ERR_OOM, "layer_pool_create: out of memory");
   p->store = store;
@@ -439,9 +518,13 @@ int layer_pool_create(const lsq_store* store, int32_t n_buffers, void* dev_slots
   LSQ_HIP(hipEventCreateWithFlags(&p->large_ready, hipEventDisableTiming));
   LSQ_HIP(hipEventCreateWithFlags(&p->large_free, hipEventDisableTiming));
   if (resident) {
+    if (!p->copy) p->copy = p->compute;   // copies once, at create
     for (int i = 0; i < n_buffers; ++i)
       if (int e = copy_into(p, i, i)) return e;
     LSQ_HIP(hipStreamSynchronize(p->copy));
+  } else if (int e = choose_copy_stream(p)) {
+    layer_pool_destroy(p);
+    return e;
   }
   *out = p;
   return LSQ_OK;
@@ -459,7 +542,14 @@ void layer_pool_destroy(lsq_pool* p) {
   }
   if (p->large_ready) (void)hipEventDestroy(p->large_ready);
   if (p->large_free) (void)hipEventDestroy(p->large_free);
+  if (p->own_copy) (void)hipStreamDestroy(p->own_copy);
   delete p;
+}
+
+int layer_pool_copy_stream(const lsq_pool* p, void** stream) {
+  LSQ_CHECK(p && stream, LSQ_ERR_INVALID, "layer_pool_copy_stream: null pointer");
+  *stream = p->copy;
+  return LSQ_OK;
 }
 
 int stream_layer_prefetch(lsq_pool* p, int32_t layer) {

@@ -117,6 +117,7 @@ _SIGS = {
     "shard_store_load": (C.c_int, [C.c_char_p, C.POINTER(ModelCfg), _I32, C.POINTER(_P)]),
     "layer_pool_create": (C.c_int, [_P, _I32, _P, _U64, _P, _P, _I32, C.POINTER(_P)]),
     "layer_pool_destroy": (None, [_P]),
+    "layer_pool_copy_stream": (C.c_int, [_P, C.POINTER(_P)]),
     "stream_layer_prefetch": (C.c_int, [_P, _I32]),
     "layer_pool_acquire": (C.c_int, [_P, _I32, C.POINTER(_P)]),
     "layer_pool_release": (C.c_int, [_P, _I32]),

@@ -196,7 +196,9 @@ class Runner:
     """A pool over a store plus the step workspace.  mode: 'streamed' or 'resident'."""
 
     def __init__(self, cfg, store, resident, mode="streamed", n_buffers=None, pool_flags=0, device="cuda",
-                 keep_activations=False, reference=False, recompute_all=False):
+                 keep_activations=False, reference=False, recompute_all=False, copy_on_compute=False):
+        """copy_on_compute: hand the pool the compute stream as its copy stream
+        (the pool must then copy on a stream of its own)."""
         self.cfg, self.store, self.res = cfg, store, resident
         self.step_flags = (lib.LSQ_STEP_KEEP_ACTIVATIONS if keep_activations else 0) | \
                           (lib.LSQ_STEP_RECOMPUTE_ALL if recompute_all else 0) | \
@@ -212,7 +214,7 @@ class Runner:
         self.slots = torch.empty(n * stride, dtype=torch.uint8, device=device)
         h = C.c_void_p()
         lib.call("layer_pool_create", store.handle, n, _ptr(self.slots), stride, lib.stream_handle(self.compute),
-                 lib.stream_handle(self.copy), flags, C.byref(h))
+                 lib.stream_handle(self.compute if copy_on_compute else self.copy), flags, C.byref(h))
         self.pool = h
         self.n_buffers = n
         self.ws_bytes = int(lib.raw("lsq_step_workspace_size")(C.byref(self.ccfg), cfg.batch, cfg.seq, ws_flags))
@@ -244,6 +246,12 @@ class Runner:
                      opt(x_trace), opt(dx_trace))
         torch.cuda.current_stream().wait_stream(self.compute)
         return self.loss
+
+    def copy_stream_handle(self):
+        """The stream the pool copies layers on (an int handle)."""
+        sp = C.c_void_p()
+        lib.call("layer_pool_copy_stream", self.pool, C.byref(sp))
+        return sp.value or 0
 
     def stats(self, reset=False):
         st = lib.PoolStats()

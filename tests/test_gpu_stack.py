@@ -415,3 +415,30 @@ def test_poisoned_slots_stream_identically(gpu, cfg):
     assert r.stats().copies == (2 * cfg.n_layers - cfg.n_buffers) + (2 * cfg.n_layers - 2 * cfg.n_buffers)
     r.close()
     store.close()
+
+
+def test_pool_copies_on_a_stream_that_runs_beside_compute(gpu):
+    """HIP maps streams onto a few hardware queues, and two streams on one
+    queue run in order, which would serialize the layer copies with compute.
+    Handed the compute stream itself as its copy stream, the pool must find a
+    stream of its own that runs beside it, and the step must still equal the
+    resident run bit for bit; a normal runner's copy stream is never the
+    compute stream either."""
+    cfg = configs.TINY
+    print_case(test="copy_stream_beside_compute", cfg=cfg.name)
+    store = model.Store(cfg)
+    res = model.Resident(cfg)
+    ids = torch.from_numpy(ids_for(cfg)).cuda()
+    resident = run(cfg, "resident", store, res, ids)
+    for on_compute in (True, False):
+        r = model.Runner(cfg, store, res, copy_on_compute=on_compute)
+        used = r.copy_stream_handle()
+        assert used not in (0, r.compute.cuda_stream)
+        logits = torch.empty((cfg.tokens, cfg.vocab), dtype=torch.float32, device="cuda")
+        loss = r.step(ids, logits=logits).item()
+        torch.cuda.synchronize()
+        got = dict(loss=loss, logits=logits.cpu().numpy(), grads=r.grads.cpu().numpy())
+        exact, total = _compare_bitwise(cfg, resident, got)
+        assert exact == total == cfg.n_layers * 14
+        r.close()
+    store.close()

@@ -40,8 +40,8 @@ struct AttnBwdArgs {
 
 // Workspace of the operands each attention call prepares once (rotated and
 // split into bf16 hi/lo, or transposed, rows padded with zeros to a multiple
-// of 64): Q, K and V^T for the forward; Q, K, their transposes, V and dO^T for
-// the backward.
+// of 64): Q, K and V^T for the forward; Q, K, the transposes of their bf16
+// values, V and dO^T for the backward.
 size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd);
 
 // y [T, ldy] bf16 (and, with y_lo, the bf16 remainder at the same row pitch).

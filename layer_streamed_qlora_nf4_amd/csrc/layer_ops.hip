@@ -333,7 +333,7 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const SrcT
 struct PrepPtrs {
   uint16_t *kh, *kl, *qh, *ql;          // rotated K and Q, bf16 hi/lo rows
   uint16_t* vt;                         // forward: V^T
-  uint16_t *kht, *klt, *qht, *qlt, *ot, *vr;   // backward: K^T, Q^T, dO^T, V rows
+  uint16_t *kht, *qht, *ot, *vr;   // backward: K^T and Q^T (bf16 of the rotated values), dO^T, V rows
   int Sp;
 };
 PrepPtrs prep_ptrs(uint16_t* base, int B, int S, int nh, int nkv, int hd, bool bwd) {
@@ -352,10 +352,8 @@ PrepPtrs prep_ptrs(uint16_t* base, int B, int S, int nh, int nkv, int hd, bool b
   p.ql = take(eq);
   if (bwd) {
     p.kht = take(ekv);
-    p.klt = take(ekv);
     p.vr = take(ekv);
     p.qht = take(eq);
-    p.qlt = take(eq);
     p.ot = take(eq);
   } else {
     p.vt = take(ekv);
@@ -437,14 +435,14 @@ struct PrepRotSmem {
   uint16_t h[AT][HD + 8], l[AT][HD + 8];
   uint16_t t[HD][AT + 8];
 };
-// Where the rotated rows of one set of heads go (hiT/loT null: no transposes).
+// Where the rotated rows of one set of heads go (hiT null: no transpose).
 struct RotOut {
-  uint16_t *hi, *lo, *hiT, *loT;
+  uint16_t *hi, *lo, *hiT;
 };
 // Rows [64 blockIdx.x, + 64) of batch blockIdx.z, qkv head column col0 +
 // blockIdx.y, rotated in float32 and split into bf16 hi/lo rows, and
-// transposed where the set asks for it: heads below nA (the queries) go to
-// set A, the rest (the keys) to set B.
+// the hi rows transposed where the set asks for it: heads below nA (the
+// queries) go to set A, the rest (the keys) to set B.
 template <int HD>
 __global__ void __launch_bounds__(256) attn_prep_rot_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
                                                            int col0, int nA, int nB, const float2* __restrict__ rope,
@@ -464,10 +462,6 @@ __global__ void __launch_bounds__(256) attn_prep_rot_kernel(const float* __restr
   lds_transpose<HD>(sm.t, sm.h);
   __syncthreads();
   put_cols<HD>(o.hiT + hb * HD * Sp + row0, sm.t, Sp);
-  __syncthreads();
-  lds_transpose<HD>(sm.t, sm.l);
-  __syncthreads();
-  put_cols<HD>(o.loT + hb * HD * Sp + row0, sm.t, Sp);
 }
 // The same blocks of a plain operand (V from the float32 qkv, dO in bf16), transposed, in bf16.
 template <int HD, typename SrcT>
@@ -507,10 +501,41 @@ __device__ __forceinline__ void put_hilo4(uint16_t* hi, uint16_t* lo, const floa
   *reinterpret_cast<u32x2*>(hi) = u32x2{h0, h1};
   *reinterpret_cast<u32x2*>(lo) = u32x2{l0, l1};
 }
+// 2^x on the hardware's exponential unit (no denormal-range rescaling; the
+// tiny results it would keep only matter far below the softmax's precision).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Four consecutive values rounded to bf16, one 8-byte store.
+__device__ __forceinline__ void put_bf16x4(uint16_t* dst, const float (&x)[4]) {
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
 __device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, float x) {
   const uint16_t h = f32_to_bf16_bits(x);
   *hi = h;
   *lo = f32_to_bf16_bits(x - bf16_bits_to_f32(h));
+}
+
+// XCD-aware order of attention work items (a query or key block of one head
+// of one batch row; the grid is (blocks, heads, batch)).  Workgroups reach the
+// 8 XCDs round-robin and each XCD has its own L2, while every item of one KV
+// head group reads the same K and V.  So, when the item count is a multiple
+// of 8, each XCD takes one contiguous run of the item list ordered group by
+// group (batch-major), and within a group by block, heaviest first, then
+// head: one group's K/V stays in one L2.  Otherwise the plain order: blocks
+// along x (heaviest first), heads along y.  desc: the heaviest block is the
+// last one (causal queries), else the first (keys).
+struct AttnItem {
+  int blk, h, b;
+};
+__device__ __forceinline__ AttnItem attn_item(int nh, int nkv, bool desc) {
+  const int nblk = gridDim.x;
+  const int total = nblk * nh * gridDim.z;
+  if (total & 7) return AttnItem{desc ? nblk - 1 - (int)blockIdx.x : (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  const int g = blockIdx.x + nblk * (blockIdx.y + nh * blockIdx.z);
+  const int v = (g & 7) * (total >> 3) + (g >> 3);
+  const int hpg = nh / nkv, per_group = nblk * hpg;
+  const int gi = v / per_group, rem = v - gi * per_group;
+  const int k = rem / hpg, hh = rem - k * hpg;
+  return AttnItem{desc ? nblk - 1 - k : k, (gi % nkv) * hpg + hh, gi / nkv};
 }
 
 template <int HD>
@@ -532,7 +557,8 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
   AttnF16Smem<HD>& sm = *reinterpret_cast<AttnF16Smem<HD>*>(smem_raw);
   constexpr int DC = HD / 32, DT = HD / 16;
   const int nqb = gridDim.x;
-  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const AttnItem it = attn_item(a.nh, a.nkv, true);
+  const int qb = it.blk, h = it.h, b = it.b;
   const int g = h / (a.nh / a.nkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -590,26 +616,33 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
         st[jt] = mfma_bf16(kh, ql[c], st[jt]);
       }
     }
+    // Only the diagonal block needs the causal mask: every key of an earlier
+    // block precedes every query of this one.  Key and query rows past S are
+    // zero (prepared so) and only reach outputs that are never written.
+    if (kb == qb) {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (16 * jt + 4 * lg + v > 16 * w + lr) st[jt][v] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kj = k0 + 16 * jt + 4 * lg + v;
-        st[jt][v] = (kj <= qi && kj < a.S) ? st[jt][v] * sc : -INFINITY;
-        mx = fmaxf(mx, st[jt][v]);
-      }
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, st[jt][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m_q, mx);
-    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m_q - mn);
+    // finite: key 0 is in every query's first block
+    const float mn = fmaxf(m_q, mx * sc);
+    const float alpha = fast_exp2(m_q - mn);
     float rs = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       float pv[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        pv[v] = (st[jt][v] == -INFINITY) ? 0.f : exp2f(st[jt][v] - mn);
+        pv[v] = fast_exp2(fmaf(st[jt][v], sc, -mn));
         rs += pv[v];
       }
       put_hilo4(&sm.ph[w][lr][16 * jt + 4 * lg], &sm.pl[w][lr][16 * jt + 4 * lg], pv);
@@ -668,7 +701,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
 template <int HD>
 struct AttnDqSmem {
   uint16_t kh[AT][HD + 8], kl[AT][HD + 8];   // rotated K [key][d]
-  uint16_t th[HD][AT + 8], tl[HD][AT + 8];   // the same transposed [d][key]
+  uint16_t th[HD][AT + 8];                   // its bf16 value transposed [d][key]
   uint16_t v[AT][HD + 8];                    // V [key][d]
   uint16_t sh[4][16][AT + 8], sl[4][16][AT + 8];   // per-wave dS [query][key]
 };
@@ -680,7 +713,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   AttnDqSmem<HD>& sm = *reinterpret_cast<AttnDqSmem<HD>*>(smem_raw);
   constexpr int DC = HD / 32, DT = HD / 16;
   const int nqb = gridDim.x;
-  const int qb = nqb - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const AttnItem it = attn_item(a.nh, a.nkv, true);
+  const int qb = it.blk, h = it.h, b = it.b;
   const int g = h / (a.nh / a.nkv);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -692,7 +726,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* Kh = pp.kh + kvh * pp.Sp * HD;
   const uint16_t* Kl = pp.kl + kvh * pp.Sp * HD;
   const uint16_t* Kht = pp.kht + kvh * HD * pp.Sp;
-  const uint16_t* Klt = pp.klt + kvh * HD * pp.Sp;
   bf16x8 qh[DC], ql[DC], od[DC];
   {
     const int qi = q0 + 16 * w + lr;
@@ -711,12 +744,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // kh, kl and v of the next block are prefetched across this block's MFMAs;
   // the transposed tiles are loaded as a block begins (in flight during its barrier)
-  Chunks<HD> ckh, ckl, cv, cth, ctl;
+  Chunks<HD> ckh, ckl, cv, cth;
   ld_rows<HD>(ckh, Kh, HD, AT);
   ld_rows<HD>(ckl, Kl, HD, AT);
   ld_rows<HD>(cv, Vp, HD, AT);
   ld_cols<HD>(cth, Kht, pp.Sp);
-  ld_cols<HD>(ctl, Klt, pp.Sp);
   for (int kb = 0; kb <= qb; ++kb) {
     const int k0 = kb * AT;
     __syncthreads();
@@ -724,7 +756,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     st_rows<HD>(sm.kl, ckl);
     st_rows<HD>(sm.v, cv);
     st_cols<HD>(sm.th, cth);
-    st_cols<HD>(sm.tl, ctl);
     __syncthreads();
     {
       const int kn = min(kb + 1, qb) * AT;
@@ -732,7 +763,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       ld_rows<HD>(ckl, Kl + (int64_t)kn * HD, HD, AT);
       ld_rows<HD>(cv, Vp + (int64_t)kn * HD, HD, AT);
       ld_cols<HD>(cth, Kht + kn, pp.Sp);
-      ld_cols<HD>(ctl, Klt + kn, pp.Sp);
     }
     f32x4 st[4], dpt[4];
 #pragma unroll
@@ -754,14 +784,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       float ds[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kj = k0 + 16 * jt + 4 * lg + v;
-        const bool ok = kj <= qi && qi < a.S && kj < a.S;
-        const float pv = ok ? exp2f(st[jt][v] * sc - lse_q) : 0.f;
+        // the causal mask on the diagonal block only (rows past S are zero)
+        const bool ok = kb != qb || 16 * jt + 4 * lg + v <= 16 * w + lr;
+        const float pv = ok ? fast_exp2(fmaf(st[jt][v], sc, -lse_q)) : 0.f;
         ds[v] = pv * (dpt[jt][v] - dd_q);
       }
       put_hilo4(&sm.sh[w][lr][16 * jt + 4 * lg], &sm.sl[w][lr][16 * jt + 4 * lg], ds);
     }
-    // dS is wave-private: this wave's LDS writes are done before its reads below
+    // dS is wave-private: this wave's LDS writes are done before its reads below.
+    // dQ = dS K takes dS as a hi/lo pair and K as its bf16 value.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const bf16x8 dh = mfma_a8(&sm.sh[w][lr][32 * kc + 8 * lg]);
@@ -769,9 +800,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 th = mfma_a8(&sm.th[16 * dt + lr][32 * kc + 8 * lg]);
-        const bf16x8 tl = mfma_a8(&sm.tl[16 * dt + lr][32 * kc + 8 * lg]);
         dq[dt] = mfma_bf16(dh, th, dq[dt]);
-        dq[dt] = mfma_bf16(dh, tl, dq[dt]);
         dq[dt] = mfma_bf16(dl, th, dq[dt]);
       }
     }
@@ -796,11 +825,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 template <int HD>
 struct AttnDkdvSmem {
   uint16_t qh[AT][HD + 8], ql[AT][HD + 8];   // rotated Q [query][d]
-  uint16_t th[HD][AT + 8], tl[HD][AT + 8];   // the same transposed [d][query]
+  uint16_t th[HD][AT + 8];                   // its bf16 value transposed [d][query]
   uint16_t o[AT][HD + 8];                    // dO [query][d]
   uint16_t ot[HD][AT + 8];                   // dO transposed [d][query]
   uint16_t ph[4][16][AT + 8], pl[4][16][AT + 8];   // per-wave P^T [key][query]
-  uint16_t sh[4][16][AT + 8], sl[4][16][AT + 8];   // per-wave dS^T
+  uint16_t sh[4][16][AT + 8];                      // per-wave dS^T in bf16
   float lse[AT], dd[AT];
 };
 
@@ -813,7 +842,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnDkdvSmem<HD>& sm = *reinterpret_cast<AttnDkdvSmem<HD>*>(smem_raw);
   constexpr int DC = HD / 32, DT = HD / 16;
-  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const AttnItem it = attn_item(a.nh, a.nkv, false);
+  const int kb = it.blk, h = it.h, b = it.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int k0 = kb * AT;
@@ -835,10 +865,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint16_t* Qh = pp.qh + qh_ * pp.Sp * HD;
   const uint16_t* Ql = pp.ql + qh_ * pp.Sp * HD;
   const uint16_t* Qht = pp.qht + qh_ * HD * pp.Sp;
-  const uint16_t* Qlt = pp.qlt + qh_ * HD * pp.Sp;
   const uint16_t* Ot = pp.ot + qh_ * HD * pp.Sp;
   const uint16_t* Op = a.dO + rowbase * a.ldo + (int64_t)h * HD;
-  Chunks<HD> cqh, cql, co, cot, cth, ctl;
+  Chunks<HD> cqh, cql, co, cot, cth;
   float clse = 0.f, cdd = 0.f;
   // the blocks' loads, as a macro so that the register arrays stay plain locals
   // qh, ql, dO and the row statistics of the next block are prefetched across
@@ -850,7 +879,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     ld_rows<HD>(co, Op + (int64_t)(q0) * a.ldo, a.ldo, a.S - (q0));            \
     ld_cols<HD>(cot, Ot + (q0), pp.Sp);                                        \
     ld_cols<HD>(cth, Qht + (q0), pp.Sp);                                       \
-    ld_cols<HD>(ctl, Qlt + (q0), pp.Sp);                                       \
     const bool ok_ = tid < AT && (q0) + tid < a.S;                             \
     clse = ok_ ? a.lse[((int64_t)b * a.nh + h) * a.S + (q0) + tid] : 0.f;      \
     cdd = ok_ ? a.D[(rowbase + (q0) + tid) * a.nh + h] : 0.f;                  \
@@ -864,7 +892,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     st_rows<HD>(sm.o, co);
     st_cols<HD>(sm.ot, cot);
     st_cols<HD>(sm.th, cth);
-    st_cols<HD>(sm.tl, ctl);
     if (tid < AT) {
       sm.lse[tid] = clse;
       sm.dd[tid] = cdd;
@@ -890,38 +917,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     {
-      const int kj = k0 + 16 * w + lr;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
         float pv[4], ds[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int qr = 16 * jt + 4 * lg + v, qi = q0 + qr;
-          const bool ok = kj <= qi && qi < a.S && kj < a.S;
-          pv[v] = ok ? exp2f(st[jt][v] * sc - sm.lse[qr]) : 0.f;
+          // the causal mask on the diagonal block only (rows past S are zero)
+          const int qr = 16 * jt + 4 * lg + v;
+          const bool ok = qb != kb || 16 * w + lr <= qr;
+          pv[v] = ok ? fast_exp2(fmaf(st[jt][v], sc, -sm.lse[qr])) : 0.f;
           ds[v] = pv[v] * (dpt[jt][v] - sm.dd[qr]);
         }
         put_hilo4(&sm.ph[w][lr][16 * jt + 4 * lg], &sm.pl[w][lr][16 * jt + 4 * lg], pv);
-        put_hilo4(&sm.sh[w][lr][16 * jt + 4 * lg], &sm.sl[w][lr][16 * jt + 4 * lg], ds);
+        put_bf16x4(&sm.sh[w][lr][16 * jt + 4 * lg], ds);
       }
     }
-    // P^T and dS^T are wave-private: this wave's LDS writes are done before its reads below
+    // P^T and dS^T are wave-private: this wave's LDS writes are done before its
+    // reads below.  dV = P^T dO takes P^T as a hi/lo pair; dK = dS^T Q takes
+    // both dS and Q as their bf16 values.
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const bf16x8 pah = mfma_a8(&sm.ph[w][lr][32 * kc + 8 * lg]);
       const bf16x8 pal = mfma_a8(&sm.pl[w][lr][32 * kc + 8 * lg]);
       const bf16x8 sah = mfma_a8(&sm.sh[w][lr][32 * kc + 8 * lg]);
-      const bf16x8 sal = mfma_a8(&sm.sl[w][lr][32 * kc + 8 * lg]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 ob = mfma_a8(&sm.ot[16 * dt + lr][32 * kc + 8 * lg]);
         dv[dt] = mfma_bf16(pah, ob, dv[dt]);
         dv[dt] = mfma_bf16(pal, ob, dv[dt]);
         const bf16x8 th = mfma_a8(&sm.th[16 * dt + lr][32 * kc + 8 * lg]);
-        const bf16x8 tl = mfma_a8(&sm.tl[16 * dt + lr][32 * kc + 8 * lg]);
         dk[dt] = mfma_bf16(sah, th, dk[dt]);
-        dk[dt] = mfma_bf16(sah, tl, dk[dt]);
-        dk[dt] = mfma_bf16(sal, th, dk[dt]);
       }
     }
   }
@@ -1223,7 +1248,7 @@ int allow_smem(K* kernel, size_t bytes) {
 size_t attention_prep_bytes(int B, int S, int nh, int nkv, int hd, bool bwd) {
   const PrepPtrs p = prep_ptrs(nullptr, B, S, nh, nkv, hd, bwd);
   const int64_t ekv = (int64_t)B * nkv * p.Sp * hd, eq = (int64_t)B * nh * p.Sp * hd;
-  return (size_t)(2 * (bwd ? 5 * ekv + 5 * eq : 3 * ekv + 2 * eq));
+  return (size_t)(2 * (bwd ? 4 * ekv + 4 * eq : 3 * ekv + 2 * eq));
 }
 
 int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
@@ -1242,7 +1267,7 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   int tok = prof_begin(s);
   // Q and K rotated and split into hi/lo rows (one launch), V^T
   const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B);
-  const RotOut oq{pp.qh, pp.ql, nullptr, nullptr}, ok{pp.kh, pp.kl, nullptr, nullptr};
+  const RotOut oq{pp.qh, pp.ql, nullptr}, ok{pp.kh, pp.kl, nullptr};
   if (a.hd == 128) {
     attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
     attn_prep_t_kernel<128, float><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vt);
@@ -1279,7 +1304,7 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
   // Q and K rotated, split and transposed (one launch), V rows, dO^T
   const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B), gq(pp.Sp / AT, a.nh, B);
-  const RotOut oq{pp.qh, pp.ql, pp.qht, pp.qlt}, ok{pp.kh, pp.kl, pp.kht, pp.klt};
+  const RotOut oq{pp.qh, pp.ql, pp.qht}, ok{pp.kh, pp.kl, pp.kht};
   if (a.hd == 128) {
     attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
     attn_prep_rows_kernel<128><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vr);

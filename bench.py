@@ -63,9 +63,9 @@ FAMILY_KERNELS = [
     ("gemm_bf16_weights", ("gemm_fwd_bf16_dma_kernel", "gemm_bwd_bf16_dma_kernel", "gemm_fwd_pp_kernel<1",
                            "gemm_bwd_pp_kernel<1"), "gemm.hip"),
     ("lora_skinny", ("lora_down_kernel", "lora_g_kernel", "lora_grads_kernel"), "lora.hip"),
-    ("attention", ("attn_prep_rot_kernel", "attn_prep_t_kernel", "attn_prep_rows_kernel", "attn_fwd_bf16_kernel",
-                   "attn_dot_kernel", "attn_bwd_dq_bf16_kernel", "attn_bwd_dkdv_bf16_kernel",
-                   "attn_dkdv_reduce_kernel"), "layer_ops.hip"),
+    ("attention", ("attn_prep_fwd_kernel", "attn_prep_bwd_kernel", "attn_fwd_bf16_kernel",
+                   "attn_bwd_dq_bf16_kernel", "attn_bwd_dkdv_bf16_kernel", "attn_dkdv_reduce_kernel"),
+     "layer_ops.hip"),
     ("elementwise", ("rmsnorm_fwd_kernel", "rmsnorm_bwd_kernel", "swiglu_fwd_kernel", "swiglu_bwd_kernel",
                      "embed_kernel", "ce_kernel", "loss_sum_kernel"), "layer_ops.hip"),
     ("other", ("splitk_reduce_kernel", "adapter_transpose_kernel", "transpose_rows_kernel"), "gemm.hip"),

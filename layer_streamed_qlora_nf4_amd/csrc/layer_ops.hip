@@ -439,20 +439,17 @@ struct PrepRotSmem {
 struct RotOut {
   uint16_t *hi, *lo, *hiT;
 };
-// Rows [64 blockIdx.x, + 64) of batch blockIdx.z, qkv head column col0 +
-// blockIdx.y, rotated in float32 and split into bf16 hi/lo rows, and
-// the hi rows transposed where the set asks for it: heads below nA (the
-// queries) go to set A, the rest (the keys) to set B.
+// Rows [row0, row0 + 64) of batch b, qkv head column hh (hh < nA: a query
+// head, set A; else key head hh - nA, set B), rotated in float32 and split
+// into bf16 hi/lo rows, and the hi rows transposed where the set asks for it.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_prep_rot_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
-                                                           int col0, int nA, int nB, const float2* __restrict__ rope,
-                                                           RotOut A, RotOut Bo) {
-  __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
-  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const float* __restrict__ qkv, int64_t ld, int S,
+                                               int Sp, int row0, int hh, int b, int nA, int nB,
+                                               const float2* __restrict__ rope, const RotOut& A, const RotOut& Bo) {
   const bool in_a = hh < nA;
   const RotOut o = in_a ? A : Bo;
   const int nheads = in_a ? nA : nB, hl = in_a ? hh : hh - nA;
-  const float* src = qkv + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
+  const float* src = qkv + (int64_t)b * S * ld + (int64_t)hh * HD;
   stage_rot<HD>(sm.h, sm.l, src, ld, row0, S - row0, rope);
   __syncthreads();
   const int64_t hb = (int64_t)b * nheads + hl;
@@ -463,26 +460,94 @@ __global__ void __launch_bounds__(256) attn_prep_rot_kernel(const float* __restr
   __syncthreads();
   put_cols<HD>(o.hiT + hb * HD * Sp + row0, sm.t, Sp);
 }
-// The same blocks of a plain operand (V from the float32 qkv, dO in bf16), transposed, in bf16.
+// The same rows of a plain operand (V from the float32 qkv, dO in bf16) at
+// column head `col`, transposed into head hh of dstT, in bf16.
 template <int HD, typename SrcT>
-__global__ void __launch_bounds__(256) attn_prep_t_kernel(const SrcT* __restrict__ src, int64_t ld, int S, int Sp,
-                                                         int col0, int nheads, uint16_t* dstT) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[HD][AT + 8];
-  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
-  stage_rows_t<HD>(t, src + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD, ld, row0, S - row0);
+__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + 8], const SrcT* __restrict__ src, int64_t ld, int S,
+                                             int Sp, int row0, int col, int hh, int b, int nheads, uint16_t* dstT) {
+  stage_rows_t<HD>(t, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);
   __syncthreads();
   put_cols<HD>(dstT + ((int64_t)b * nheads + hh) * HD * Sp + row0, t, Sp);
 }
 // V rows of the float32 qkv rounded to bf16 rows [b][head][Sp][HD] (zero past S).
 template <int HD>
-__global__ void __launch_bounds__(256) attn_prep_rows_kernel(const float* __restrict__ src, int64_t ld, int S, int Sp,
-                                                            int col0, int nheads, uint16_t* dst) {
-  const int row0 = blockIdx.x * AT, hh = blockIdx.y, b = blockIdx.z;
-  const float* base = src + (int64_t)b * S * ld + (int64_t)(col0 + hh) * HD;
+__device__ __forceinline__ void prep_rows_block(const float* __restrict__ src, int64_t ld, int S, int Sp, int row0,
+                                                int col, int hh, int b, int nheads, uint16_t* dst) {
+  const float* base = src + (int64_t)b * S * ld + (int64_t)col * HD;
   uint16_t* out = dst + (((int64_t)b * nheads + hh) * Sp + row0) * HD;
   for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
     const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
     *reinterpret_cast<uint4*>(out + r * HD + c) = load8_bf16(base + (int64_t)(row0 + r) * ld + c, row0 + r < S);
+  }
+}
+// D[b*S + t][h] = sum_d dO[t, h, d] * O[t, h, d] for rows [row0, row0 + 64),
+// with the float32 O of the forward: D must equal sum_j P_j dP_j, and a
+// rounded O breaks that identity exactly where attention is peaked and
+// dP_j - D cancels.  Four lanes per row, each a quarter of d in order, then
+// summed in a fixed order.
+template <int HD>
+__device__ __forceinline__ void dot_rows_block(const uint16_t* __restrict__ dO, const float* __restrict__ O,
+                                               int64_t ldo, int S, int row0, int h, int b, int nh,
+                                               float* __restrict__ D) {
+  constexpr int Q = HD / 4;
+  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int t = row0 + r;
+  float acc = 0.f;
+  if (t < S) {
+    const int64_t off = ((int64_t)b * S + t) * ldo + (int64_t)h * HD + part * Q;
+#pragma unroll
+    for (int d = 0; d < Q; d += 8) {
+      float x[8], y[8];
+      load8(O + off + d, true, y);
+      const uint4 xb = *reinterpret_cast<const uint4*>(dO + off + d);
+      const uint32_t xw[4] = {xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf_lo(xw[j]);
+        x[2 * j + 1] = bf_hi(xw[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += x[j] * y[j];
+    }
+  }
+  const float s1 = acc + __shfl_xor(acc, 1, 64);
+  const float s2 = s1 + __shfl_xor(s1, 2, 64);
+  if (part == 0 && t < S) D[((int64_t)b * S + t) * nh + h] = s2;
+}
+
+// Every operand the forward prepares, one launch: workgroups (row block x,
+// y, batch z); y < nh + nkv rotates and splits Q and K, the rest transpose V.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_prep_fwd_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
+                                                           int nh, int nkv, const float2* __restrict__ rope,
+                                                           RotOut Qo, RotOut Ko, uint16_t* vt) {
+  __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
+  const int row0 = blockIdx.x * AT, y = blockIdx.y, b = blockIdx.z;
+  if (y < nh + nkv)
+    prep_rot_block<HD>(sm, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
+  else
+    prep_t_block<HD, float>(sm.t, qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vt);
+}
+// Every operand the backward prepares, one launch: y < nh + nkv rotates and
+// splits Q and K (with the transposes of their bf16 values), the next nkv
+// round V rows to bf16, the last nh transpose dO and form D for their rows.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
+                                                           int nh, int nkv, const float2* __restrict__ rope,
+                                                           RotOut Qo, RotOut Ko, uint16_t* vr,
+                                                           const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ O, int64_t ldo, uint16_t* ot,
+                                                           float* __restrict__ D) {
+  __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
+  const int row0 = blockIdx.x * AT, y = blockIdx.y, b = blockIdx.z;
+  if (y < nh + nkv) {
+    prep_rot_block<HD>(sm, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
+  } else if (y < nh + 2 * nkv) {
+    prep_rows_block<HD>(qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vr);
+  } else {
+    const int h = y - nh - 2 * nkv;
+    prep_t_block<HD, uint16_t>(sm.t, dO, ldo, S, Sp, row0, h, h, b, nh, ot);
+    dot_rows_block<HD>(dO, O, ldo, S, row0, h, b, nh, D);
   }
 }
 
@@ -964,23 +1029,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 #undef LSQ_DKDV_LOAD
 
-// D[t][h] = sum_d dO[t, h, d] * O[t, h, d], with the float32 O of the forward:
-// D must equal sum_j P_j dP_j, and a rounded O breaks that identity exactly
-// where attention is peaked and dP_j - D cancels.
-__global__ void attn_dot_kernel(const uint16_t* __restrict__ dO, const float* __restrict__ O, int64_t ldo, int T,
-                                int nh, int hd, float* __restrict__ D) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t, h)
-  if (row >= (int64_t)T * nh) return;
-  const int t = row / nh, h = row % nh;
-  const uint16_t* x = dO + (int64_t)t * ldo + (int64_t)h * hd;
-  const float* y = O + (int64_t)t * ldo + (int64_t)h * hd;
-  float s = 0.f;
-  for (int d = lane; d < hd; d += 64) s += bf16_bits_to_f32(x[d]) * y[d];
-  s = warp_sum(s);
-  if (lane == 0) D[row] = s;
-}
-
 // dK, dV of each KV head = sum of its query heads' partials (head order); dK
 // is scaled and taken back through the rotation, both rounded once to bf16.
 __global__ void attn_dkdv_reduce_kernel(AttnBwdArgs a, int B) {
@@ -1265,16 +1313,14 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   dim3 grid((a.S + AT - 1) / AT, a.nh, B);
   const double flops = 2.0 * 2.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
   int tok = prof_begin(s);
-  // Q and K rotated and split into hi/lo rows (one launch), V^T
-  const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B);
+  // Q and K rotated and split into hi/lo rows, and V^T: one launch
+  const dim3 gp(pp.Sp / AT, a.nh + 2 * a.nkv, B);
   const RotOut oq{pp.qh, pp.ql, nullptr}, ok{pp.kh, pp.kl, nullptr};
   if (a.hd == 128) {
-    attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
-    attn_prep_t_kernel<128, float><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vt);
+    attn_prep_fwd_kernel<128><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
     attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a, pp);
   } else {
-    attn_prep_rot_kernel<64><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
-    attn_prep_t_kernel<64, float><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vt);
+    attn_prep_fwd_kernel<64><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
     attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a, pp);
   }
   prof_end(tok, s, PROF_ATTN, flops, 0.0);
@@ -1293,28 +1339,24 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
     return e;
   }();
   if (init) return init;
-  const int T = B * a.S;
   const double flops = 2.0 * 5.0 * B * a.nh * (double)a.S * (a.S + 1) / 2.0 * a.hd;
   int tok = prof_begin(s);
-  attn_dot_kernel<<<(unsigned)(((int64_t)T * a.nh + 3) / 4), 256, 0, s>>>(a.dO, a.O_f32, a.ldo, T, a.nh, a.hd, D);
   AttnBwdArgs b = a;
   b.D = D;
   LSQ_CHECK(a.dk_part && a.dv_part && a.prep, LSQ_ERR_WORKSPACE, "attention_bwd: workspace buffers missing");
   const PrepPtrs pp = prep_ptrs(a.prep, B, a.S, a.nh, a.nkv, a.hd, true);
   dim3 g1((a.S + AT - 1) / AT, a.nh, B), g2((a.S + AT - 1) / AT, a.nh, B);
-  // Q and K rotated, split and transposed (one launch), V rows, dO^T
-  const dim3 gqk(pp.Sp / AT, a.nh + a.nkv, B), gkv(pp.Sp / AT, a.nkv, B), gq(pp.Sp / AT, a.nh, B);
+  // Q and K rotated, split and transposed, V rows, dO^T and D: one launch
+  const dim3 gp(pp.Sp / AT, 2 * a.nh + 2 * a.nkv, B);
   const RotOut oq{pp.qh, pp.ql, pp.qht}, ok{pp.kh, pp.kl, pp.kht};
   if (a.hd == 128) {
-    attn_prep_rot_kernel<128><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
-    attn_prep_rows_kernel<128><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vr);
-    attn_prep_t_kernel<128, uint16_t><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_prep_bwd_kernel<128><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, a.dO,
+                                                 a.O_f32, a.ldo, pp.ot, D);
     attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b, pp);
   } else {
-    attn_prep_rot_kernel<64><<<gqk, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, 0, a.nh, a.nkv, a.rope, oq, ok);
-    attn_prep_rows_kernel<64><<<gkv, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh + a.nkv, a.nkv, pp.vr);
-    attn_prep_t_kernel<64, uint16_t><<<gq, 256, 0, s>>>(a.dO, a.ldo, a.S, pp.Sp, 0, a.nh, pp.ot);
+    attn_prep_bwd_kernel<64><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, a.dO,
+                                                a.O_f32, a.ldo, pp.ot, D);
     attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b, pp);
   }

@@ -189,6 +189,9 @@ __global__ void rope_kernel(uint16_t* __restrict__ buf, int64_t ld, int T, int S
 // block, head, batch) forward and for dQ, per (key block, head) for dK and dV);
 // scores are kept in base 2: s2 = q.k * scale * log2(e), lse2 = max + log2(sum).
 constexpr int AT = 64;
+// bf16 elements of padding after every row of an attention LDS tile (keeps the
+// rows of one 16-lane fragment read in distinct banks)
+constexpr int PAD = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------ attention on bf16 MFMA
@@ -270,7 +273,7 @@ __device__ __forceinline__ void put_mt_t(uint16_t (*dst)[PITCH], int c0, int r0,
 // Rows [row0, row0 + 64) of a bf16 matrix, rotated (RoPE at positions
 // row0 + r) and split into hi/lo, row-major.  Rows at or past n read as zero.
 template <int HD>
-__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)[HD + 8], const float* src,
+__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + PAD], uint16_t (*lo)[HD + PAD], const float* src,
                                           int64_t ld, int row0, int n, const float2* __restrict__ rope) {
   constexpr int HALF = HD / 2, NCH = HALF / 32;
   const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
@@ -289,7 +292,7 @@ __device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + 8], uint16_t (*lo)
 }
 // Rows [row0, row0 + 64) copied row-major (zero past n).
 template <int HD>
-__device__ __forceinline__ void stage_rows(uint16_t (*dst)[HD + 8], const uint16_t* src, int64_t ld, int row0, int n) {
+__device__ __forceinline__ void stage_rows(uint16_t (*dst)[HD + PAD], const uint16_t* src, int64_t ld, int row0, int n) {
   for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
     const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
     *reinterpret_cast<uint4*>(&dst[r][c]) =
@@ -298,19 +301,19 @@ __device__ __forceinline__ void stage_rows(uint16_t (*dst)[HD + 8], const uint16
 }
 // A staged row-major [64][HD] tile transposed into [HD][64] (call after a barrier).
 template <int HD>
-__device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + 8], const uint16_t (*src)[HD + 8]) {
+__device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + PAD], const uint16_t (*src)[HD + PAD]) {
   constexpr int NMT = AT / 4 * (HD / 8);
   for (int t = threadIdx.x; t < NMT; t += 256) {
     const int rg = t / (HD / 8), cg = t % (HD / 8);
     uint4 rows[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) rows[i] = *reinterpret_cast<const uint4*>(&src[4 * rg + i][8 * cg]);
-    put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
+    put_mt_t<AT + PAD>(dst, 8 * cg, 4 * rg, rows);
   }
 }
 // Rows [row0, row0 + 64) of a bf16 matrix straight into [HD][64] (zero past n).
 template <int HD, typename SrcT>
-__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const SrcT* src, int64_t ld, int row0,
+__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const SrcT* src, int64_t ld, int row0,
                                              int n) {
   constexpr int NMT = AT / 4 * (HD / 8);
   for (int t = threadIdx.x; t < NMT; t += 256) {
@@ -321,7 +324,7 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + 8], const SrcT
       const int r = 4 * rg + i;
       rows[i] = load8_bf16(src + (int64_t)(row0 + r) * ld + 8 * cg, r < n);
     }
-    put_mt_t<AT + 8>(dst, 8 * cg, 4 * rg, rows);
+    put_mt_t<AT + PAD>(dst, 8 * cg, 4 * rg, rows);
   }
 }
 // ---- operands prepared once per attention call
@@ -382,7 +385,7 @@ __device__ __forceinline__ void each_chunk(F&& f) {
   each_chunk(f, std::make_integer_sequence<int, N>{});
 }
 // A tile of ROWS rows x COLS bf16 from rows of pitch ld (rows at or past n read
-// as zero) into registers, and out to an LDS tile with rows of COLS + 8.
+// as zero) into registers, and out to an LDS tile with rows of COLS + PAD.
 template <int ROWS, int COLS>
 __device__ __forceinline__ void ld_tile(Chunks<ROWS * COLS / AT>& c, const uint16_t* __restrict__ src, int64_t ld,
                                         int n) {
@@ -392,7 +395,7 @@ __device__ __forceinline__ void ld_tile(Chunks<ROWS * COLS / AT>& c, const uint1
   });
 }
 template <int ROWS, int COLS>
-__device__ __forceinline__ void st_tile(uint16_t (*dst)[COLS + 8], const Chunks<ROWS * COLS / AT>& c) {
+__device__ __forceinline__ void st_tile(uint16_t (*dst)[COLS + PAD], const Chunks<ROWS * COLS / AT>& c) {
   each_chunk<Chunks<ROWS * COLS / AT>::N>([&](auto i) __attribute__((always_inline)) {
     const int e = threadIdx.x + 256 * i.value, r = e / (COLS / 8), k = (e % (COLS / 8)) * 8;
     *reinterpret_cast<uint4*>(&dst[r][k]) = c.v[i.value];
@@ -403,7 +406,7 @@ __device__ __forceinline__ void ld_rows(Chunks<HD>& c, const uint16_t* __restric
   ld_tile<AT, HD>(c, src, ld, n);
 }
 template <int HD>
-__device__ __forceinline__ void st_rows(uint16_t (*dst)[HD + 8], const Chunks<HD>& c) {
+__device__ __forceinline__ void st_rows(uint16_t (*dst)[HD + PAD], const Chunks<HD>& c) {
   st_tile<AT, HD>(dst, c);
 }
 template <int HD>
@@ -411,19 +414,19 @@ __device__ __forceinline__ void ld_cols(Chunks<HD>& c, const uint16_t* __restric
   ld_tile<HD, AT>(c, src, Sp, HD);
 }
 template <int HD>
-__device__ __forceinline__ void st_cols(uint16_t (*dst)[AT + 8], const Chunks<HD>& c) {
+__device__ __forceinline__ void st_cols(uint16_t (*dst)[AT + PAD], const Chunks<HD>& c) {
   st_tile<HD, AT>(dst, c);
 }
 // [64][HD] and [HD][64] LDS tiles out to the prepared layouts.
 template <int HD>
-__device__ __forceinline__ void put_rows(uint16_t* __restrict__ dst, const uint16_t (*src)[HD + 8]) {
+__device__ __forceinline__ void put_rows(uint16_t* __restrict__ dst, const uint16_t (*src)[HD + PAD]) {
   for (int e = threadIdx.x; e < AT * HD / 8; e += 256) {
     const int r = e / (HD / 8), c = (e % (HD / 8)) * 8;
     *reinterpret_cast<uint4*>(dst + r * HD + c) = *reinterpret_cast<const uint4*>(&src[r][c]);
   }
 }
 template <int HD>
-__device__ __forceinline__ void put_cols(uint16_t* __restrict__ dst, const uint16_t (*src)[AT + 8], int Sp) {
+__device__ __forceinline__ void put_cols(uint16_t* __restrict__ dst, const uint16_t (*src)[AT + PAD], int Sp) {
   for (int e = threadIdx.x; e < HD * AT / 8; e += 256) {
     const int d = e / (AT / 8), c = (e % (AT / 8)) * 8;
     *reinterpret_cast<uint4*>(dst + (int64_t)d * Sp + c) = *reinterpret_cast<const uint4*>(&src[d][c]);
@@ -432,8 +435,8 @@ __device__ __forceinline__ void put_cols(uint16_t* __restrict__ dst, const uint1
 
 template <int HD>
 struct PrepRotSmem {
-  uint16_t h[AT][HD + 8], l[AT][HD + 8];
-  uint16_t t[HD][AT + 8];
+  uint16_t h[AT][HD + PAD], l[AT][HD + PAD];
+  uint16_t t[HD][AT + PAD];
 };
 // Where the rotated rows of one set of heads go (hiT null: no transpose).
 struct RotOut {
@@ -463,7 +466,7 @@ __device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const float*
 // The same rows of a plain operand (V from the float32 qkv, dO in bf16) at
 // column head `col`, transposed into head hh of dstT, in bf16.
 template <int HD, typename SrcT>
-__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + 8], const SrcT* __restrict__ src, int64_t ld, int S,
+__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const SrcT* __restrict__ src, int64_t ld, int S,
                                              int Sp, int row0, int col, int hh, int b, int nheads, uint16_t* dstT) {
   stage_rows_t<HD>(t, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);
   __syncthreads();
@@ -605,11 +608,11 @@ __device__ __forceinline__ AttnItem attn_item(int nh, int nkv, bool desc) {
 
 template <int HD>
 struct AttnF16Smem {
-  uint16_t kh[AT][HD + 8];     // rotated K, bf16 hi  [key][d]
-  uint16_t kl[AT][HD + 8];     // rotated K, bf16 lo
-  uint16_t vt[HD][AT + 8];     // V transposed [d][key]
-  uint16_t ph[4][16][AT + 8];  // per-wave P hi [query][key]
-  uint16_t pl[4][16][AT + 8];  // per-wave P lo
+  uint16_t kh[AT][HD + PAD];     // rotated K, bf16 hi  [key][d]
+  uint16_t kl[AT][HD + PAD];     // rotated K, bf16 lo
+  uint16_t vt[HD][AT + PAD];     // V transposed [d][key]
+  uint16_t ph[4][16][AT + PAD];  // per-wave P hi [query][key]
+  uint16_t pl[4][16][AT + PAD];  // per-wave P lo
   float al[4][16];             // per-wave row factors (rescale, then 1 / sum) by query
 };
 
@@ -765,10 +768,10 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a, PrepPtrs
 
 template <int HD>
 struct AttnDqSmem {
-  uint16_t kh[AT][HD + 8], kl[AT][HD + 8];   // rotated K [key][d]
-  uint16_t th[HD][AT + 8];                   // its bf16 value transposed [d][key]
-  uint16_t v[AT][HD + 8];                    // V [key][d]
-  uint16_t sh[4][16][AT + 8], sl[4][16][AT + 8];   // per-wave dS [query][key]
+  uint16_t kh[AT][HD + PAD], kl[AT][HD + PAD];   // rotated K [key][d]
+  uint16_t th[HD][AT + PAD];                   // its bf16 value transposed [d][key]
+  uint16_t v[AT][HD + PAD];                    // V [key][d]
+  uint16_t sh[4][16][AT + PAD], sl[4][16][AT + PAD];   // per-wave dS [query][key]
 };
 
 // dQ for one query block of one head; wave w owns queries 16w .. 16w+15.
@@ -889,12 +892,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 template <int HD>
 struct AttnDkdvSmem {
-  uint16_t qh[AT][HD + 8], ql[AT][HD + 8];   // rotated Q [query][d]
-  uint16_t th[HD][AT + 8];                   // its bf16 value transposed [d][query]
-  uint16_t o[AT][HD + 8];                    // dO [query][d]
-  uint16_t ot[HD][AT + 8];                   // dO transposed [d][query]
-  uint16_t ph[4][16][AT + 8], pl[4][16][AT + 8];   // per-wave P^T [key][query]
-  uint16_t sh[4][16][AT + 8];                      // per-wave dS^T in bf16
+  uint16_t qh[AT][HD + PAD], ql[AT][HD + PAD];   // rotated Q [query][d]
+  uint16_t th[HD][AT + PAD];                   // its bf16 value transposed [d][query]
+  uint16_t o[AT][HD + PAD];                    // dO [query][d]
+  uint16_t ot[HD][AT + PAD];                   // dO transposed [d][query]
+  uint16_t ph[4][16][AT + PAD], pl[4][16][AT + PAD];   // per-wave P^T [key][query]
+  uint16_t sh[4][16][AT + PAD];                      // per-wave dS^T in bf16
   float lse[AT], dd[AT];
 };
 

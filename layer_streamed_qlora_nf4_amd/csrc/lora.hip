@@ -41,17 +41,31 @@ __device__ __forceinline__ void put_partial(float* p, float v) {
 __device__ __forceinline__ float get_partial(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// v + p[k0 * stride] + ... + p[(k1 - 1) * stride] over partials, in k order.
-__device__ __forceinline__ float ordered_partial_sum(float v, const float* p, int64_t stride, int k0, int k1) {
-  for (int kb = k0; kb < k1; kb += 8) {
-    float t[8];
+// v[i] = 0 + p[e_i] + p[e_i + stride] + ... + p[e_i + (count - 1) stride] over
+// partials, in k order, for the E elements e_i = e0 + i step below n (v[i] = 0
+// past n).  The loads of E elements x 8 partials are all issued before the
+// first sum, so a last workgroup's reduction costs count / 8 memory round
+// trips per E elements rather than one per element.
+template <int E>
+__device__ __forceinline__ void ordered_partial_sums(float (&v)[E], const float* p, int64_t stride, int e0, int step,
+                                                     int n, int count) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = (kb + j < k1) ? get_partial(p + (int64_t)(kb + j) * stride) : 0.f;
+  for (int i = 0; i < E; ++i) v[i] = 0.f;
+  for (int kb = 0; kb < count; kb += 8) {
+    float t[E][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (kb + j < k1) v += t[j];
+    for (int i = 0; i < E; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + i * step;
+        t[i][j] = (kb + j < count && e < n) ? get_partial(p + e + (int64_t)(kb + j) * stride) : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (kb + j < count) v[i] += t[i][j];
   }
-  return v;
 }
 
 // Call after this workgroup's put_partial stores: true, in every thread, for
@@ -159,8 +173,14 @@ __global__ void __launch_bounds__(NT) lora_down_kernel(DownArgs a) {
     put_partial(base + (int64_t)chunk * n + e, ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c]);
   }
   if (!last_arriver(a.cnt + rb, a.nch)) return;
-  for (int e = tid; e < n; e += NT)
-    if (m0 + e / a.rr < a.M) finish(e, ordered_partial_sum(0.f, base + e, n, 0, a.nch));
+  constexpr int E = 4;   // n <= 16 * 64 = 4 NT
+  float v[E];
+  ordered_partial_sums<E>(v, base, n, tid, NT, n, a.nch);
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = tid + i * NT;
+    if (e < n && m0 + e / a.rr < a.M) finish(e, v[i]);
+  }
 }
 
 // ------------------------------------------------------------- G = s dY_seg B_seg
@@ -227,8 +247,14 @@ __global__ void __launch_bounds__(NT) lora_g_kernel(GArgs a) {
                 ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c]);
   }
   if (!last_arriver(a.cnt + rb * a.nseg + sg, nsc)) return;
-  for (int e = tid; e < n; e += NT)
-    if (m0 + e / a.r < a.M) finish(e, ordered_partial_sum(0.f, base + e, n, 0, nsc));
+  constexpr int E = 4;   // n <= 16 * 64 = 4 NT
+  float v[E];
+  ordered_partial_sums<E>(v, base, n, tid, NT, n, nsc);
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int e = tid + i * NT;
+    if (e < n && m0 + e / a.r < a.M) finish(e, v[i]);
+  }
 }
 
 // ------------------------------------------------------------- dA = G^T X, dB = dY^T U
@@ -461,9 +487,18 @@ __global__ void __launch_bounds__(NT) lora_grads_kernel(GradsArgs a) {
     }
   }
   if (!last_arriver(a.cnt + blockIdx.x, a.splits)) return;
-  for (int e = tid; e < ns * TNM_COLS; e += NT) {
-    const int aa = e / TNM_COLS, bl = e % TNM_COLS;
-    if (b0 + bl < tk.nl) put(aa, b0 + bl, ordered_partial_sum(0.f, base + e, PT, 0, a.splits));
+  constexpr int E = 8;
+  const int n = ns * TNM_COLS;
+  for (int e0 = tid; e0 < n; e0 += E * NT) {
+    float v[E];
+    ordered_partial_sums<E>(v, base, PT, e0, NT, n, a.splits);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i * NT;
+      if (e >= n) break;
+      const int aa = e / TNM_COLS, bl = e % TNM_COLS;
+      if (b0 + bl < tk.nl) put(aa, b0 + bl, v[i]);
+    }
   }
 }
 

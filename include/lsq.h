@@ -72,11 +72,16 @@ enum { LSQ_W_NF4 = 0, LSQ_W_BF16 = 1 };   /* streamed base weight kinds  */
  * level), and two codes per byte with the even element in the high nibble.
  */
 
-/* w_bf16_dev [n_out, n_in] bf16 -> packed_dev uint8 [n_out, n_in/2] and
- * absmax_dev float32 [n_out, n_in/64].  flag_dev (device int32, nullable) is
- * set to 1 if any input is NaN or Inf (the outputs of such a block are then
- * unspecified); it is never cleared by the call. */
-int nf4_quantize(const void* w_bf16_dev, int64_t n_out, int64_t n_in,
+/* w_dev [n_out, n_in] of dtype LSQ_BF16 or LSQ_F32 -> packed_dev uint8
+ * [n_out, n_in/2] and absmax_dev float32 [n_out, n_in/64].  blocksize must be
+ * 64 (the store format; others are LSQ_ERR_SHAPE).  A NaN or Inf input leaves
+ * its block's outputs unspecified and is reported in one of two ways:
+ * flag_dev (device int32, nullable) non-null: the call is stream-ordered and
+ * sets *flag_dev to 1 (never clears it);
+ * flag_dev null: the call waits for the stream and returns LSQ_ERR_NONFINITE
+ * (such calls use one library-owned device word per GPU and are serialized by
+ * the library). */
+int nf4_quantize(const void* w_dev, int32_t dtype, int64_t n_out, int64_t n_in, int32_t blocksize,
                  void* packed_dev, float* absmax_dev, int32_t* flag_dev, void* stream);
 
 /* Inverse map: w = bf16(fp32(level[code] * absmax)) (out_dtype LSQ_BF16) or the

@@ -10,6 +10,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "nf4_levels.h"
 
@@ -42,24 +45,47 @@ __device__ __forceinline__ uint32_t code_of(float n, const Thresholds& th) {
   return c;
 }
 
-// One thread per 64-element block.
-__global__ void __launch_bounds__(256) nf4_quantize_kernel(const uint16_t* __restrict__ w, int64_t n_blocks,
+// The 64 elements of block b as float32 (exact for bf16 input).
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ w, int64_t b, float (&x)[64]) {
+  const uint4* src = reinterpret_cast<const uint4*>(w + b * 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = src[i];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = bf_lo(u[j]);       // the even element is the low half of its word
+      x[8 * i + 2 * j + 1] = bf_hi(u[j]);
+    }
+  }
+}
+__device__ __forceinline__ void load_block(const float* __restrict__ w, int64_t b, float (&x)[64]) {
+  const float4* src = reinterpret_cast<const float4*>(w + b * 64);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 v = src[i];
+    x[4 * i] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+}
+
+// One thread per 64-element block of bf16 or float32 input.
+template <typename T>
+__global__ void __launch_bounds__(256) nf4_quantize_kernel(const T* __restrict__ w, int64_t n_blocks,
                                                            uint8_t* __restrict__ packed, float* __restrict__ absmax,
                                                            int32_t* __restrict__ flag, Thresholds th) {
   int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (b >= n_blocks) return;
-  const uint4* src = reinterpret_cast<const uint4*>(w + b * 64);
-  uint4 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = src[i];
-  const uint32_t* u = reinterpret_cast<const uint32_t*>(v);
+  float x[64];
+  load_block(w, b, x);
   float a = 0.f;
   bool finite = true;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float lo = bf_lo(u[i]), hi = bf_hi(u[i]);
-    finite = finite && isfinite(lo) && isfinite(hi);
-    a = fmaxf(a, fmaxf(fabsf(lo), fabsf(hi)));
+  for (int i = 0; i < 64; ++i) {
+    finite = finite && isfinite(x[i]);
+    a = fmaxf(a, fabsf(x[i]));
   }
   if (!finite && flag) atomicOr(flag, 1);
   uint32_t out[8];
@@ -68,8 +94,7 @@ __global__ void __launch_bounds__(256) nf4_quantize_kernel(const uint16_t* __res
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t pair = u[i * 4 + j];  // elements 2(4i+j) (low half) and 2(4i+j)+1 (high half)
-      float e0 = bf_lo(pair), e1 = bf_hi(pair);
+      const float e0 = x[8 * i + 2 * j], e1 = x[8 * i + 2 * j + 1];   // elements 2(4i+j) and 2(4i+j)+1
       uint32_t c0 = 7, c1 = 7;
       if (a > 0.f) {
         c0 = code_of(e0 / a, th);
@@ -131,17 +156,42 @@ __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restr
   }
 }
 
+// A word of device memory per GPU for the non-finite flag of calls that bring
+// none (see nf4_quantize); its address is taken once per device.
+__device__ int32_t g_nonfinite;
+__global__ void clear_word_kernel(int32_t* w) { *w = 0; }
+
+std::mutex g_flag_mu;   // such calls wait for their stream, so they are serialized
+std::vector<int32_t*> g_flag_addr;
+
+int nonfinite_word(int32_t** out) {
+  int dev = 0;
+  LSQ_HIP(hipGetDevice(&dev));
+  if ((int)g_flag_addr.size() <= dev) g_flag_addr.resize(dev + 1, nullptr);
+  if (!g_flag_addr[dev]) {
+    void* p = nullptr;
+    LSQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(g_nonfinite)));
+    g_flag_addr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_flag_addr[dev];
+  return LSQ_OK;
+}
+
 }  // namespace
 
 namespace lsq {
-int launch_nf4_quantize(const void* w, int64_t n_out, int64_t n_in, void* packed, float* absmax, int32_t* flag,
-                        hipStream_t s) {
+int launch_nf4_quantize(const void* w, int32_t dtype, int64_t n_out, int64_t n_in, void* packed, float* absmax,
+                        int32_t* flag, hipStream_t s) {
   static const Thresholds th = make_thresholds();
   int64_t n_blocks = n_out * (n_in / 64);
   if (n_blocks == 0) return LSQ_OK;
   dim3 grid(static_cast<unsigned>((n_blocks + 255) / 256));
-  nf4_quantize_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(w), n_blocks, static_cast<uint8_t*>(packed),
-                                           absmax, flag, th);
+  if (dtype == LSQ_F32)
+    nf4_quantize_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(w), n_blocks,
+                                                    static_cast<uint8_t*>(packed), absmax, flag, th);
+  else
+    nf4_quantize_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(w), n_blocks,
+                                                       static_cast<uint8_t*>(packed), absmax, flag, th);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -153,14 +203,29 @@ void lsq_nf4_codebook(float out[16]) {
   for (int i = 0; i < 16; ++i) out[i] = lsq::kNF4Levels[i];
 }
 
-int nf4_quantize(const void* w_bf16_dev, int64_t n_out, int64_t n_in, void* packed_dev, float* absmax_dev,
-                 int32_t* flag_dev, void* stream) {
-  LSQ_CHECK(w_bf16_dev && packed_dev && absmax_dev, LSQ_ERR_INVALID, "nf4_quantize: null pointer");
+int nf4_quantize(const void* w_dev, int32_t dtype, int64_t n_out, int64_t n_in, int32_t blocksize, void* packed_dev,
+                 float* absmax_dev, int32_t* flag_dev, void* stream) {
+  LSQ_CHECK(w_dev && packed_dev && absmax_dev, LSQ_ERR_INVALID, "nf4_quantize: null pointer");
+  LSQ_CHECK(dtype == LSQ_BF16 || dtype == LSQ_F32, LSQ_ERR_INVALID, "nf4_quantize: input dtype %d unsupported", dtype);
+  LSQ_CHECK(blocksize == 64, LSQ_ERR_SHAPE, "nf4_quantize: blocksize %d unsupported (the store format uses 64)",
+            blocksize);
   LSQ_CHECK(n_out >= 0 && n_in >= 0 && n_in % 64 == 0, LSQ_ERR_SHAPE,
             "nf4_quantize: n_in must be a multiple of 64 (got %lld x %lld)", (long long)n_out, (long long)n_in);
-  LSQ_CHECK(lsq::aligned16(w_bf16_dev) && lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev), LSQ_ERR_ALIGN,
+  LSQ_CHECK(lsq::aligned16(w_dev) && lsq::aligned16(packed_dev) && lsq::aligned16(absmax_dev), LSQ_ERR_ALIGN,
             "nf4_quantize: pointers must be 16-byte aligned");
-  return lsq::launch_nf4_quantize(w_bf16_dev, n_out, n_in, packed_dev, absmax_dev, flag_dev, lsq::as_stream(stream));
+  hipStream_t s = lsq::as_stream(stream);
+  if (flag_dev) return lsq::launch_nf4_quantize(w_dev, dtype, n_out, n_in, packed_dev, absmax_dev, flag_dev, s);
+  std::lock_guard<std::mutex> lock(g_flag_mu);
+  int32_t* word = nullptr;
+  if (int e = nonfinite_word(&word)) return e;
+  clear_word_kernel<<<1, 1, 0, s>>>(word);
+  LSQ_HIP(hipGetLastError());
+  if (int e = lsq::launch_nf4_quantize(w_dev, dtype, n_out, n_in, packed_dev, absmax_dev, word, s)) return e;
+  int32_t seen = 0;
+  LSQ_HIP(hipMemcpyAsync(&seen, word, sizeof(seen), hipMemcpyDeviceToHost, s));
+  LSQ_HIP(hipStreamSynchronize(s));
+  LSQ_CHECK(seen == 0, LSQ_ERR_NONFINITE, "nf4_quantize: NaN or Inf in the input");
+  return LSQ_OK;
 }
 
 int nf4_dequantize(const void* packed_dev, const float* absmax_dev, int64_t n_out, int64_t n_in, int32_t out_dtype,

@@ -293,7 +293,7 @@ int shard_store_write_layer(lsq_store* st, int32_t layer, const lsq_layer_src* s
     if (c->weight_kind == LSQ_W_NF4) {
       void* packed = blob + L.w_off[g] + (uint64_t)row_off[i] * (K / 2);
       float* absmax = reinterpret_cast<float*>(blob + L.absmax_off[g] + (uint64_t)row_off[i] * (K / 64) * 4);
-      if (int e = nf4_quantize(src->w[i], rows_of[i], K, packed, absmax, flag, stream)) return e;
+      if (int e = nf4_quantize(src->w[i], LSQ_BF16, rows_of[i], K, 64, packed, absmax, flag, stream)) return e;
     } else {
       LSQ_HIP(hipMemcpyAsync(blob + L.w_off[g] + (uint64_t)row_off[i] * K * 2, src->w[i], (size_t)rows_of[i] * K * 2,
                              hipMemcpyDeviceToDevice, s));

@@ -94,7 +94,7 @@ _SIGS = {
     "lsq_last_error": (C.c_char_p, []),
     "lsq_version": (_I32, []),
     "lsq_nf4_codebook": (None, [_P]),
-    "nf4_quantize": (C.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "nf4_quantize": (C.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _P, _P]),
     "nf4_dequantize": (C.c_int, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "nf4_lora_linear_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32]),
     "nf4_lora_linear_fwd": (C.c_int, [C.POINTER(Weight), _P, _P, _I64, _P, _P, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),

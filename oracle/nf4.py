@@ -62,13 +62,25 @@ def quantize(w_bits):
     Raises ValueError on a non-finite input or a bad shape.
     """
     w_bits = np.asarray(w_bits, dtype=np.uint16)
-    n_out, n_in = w_bits.shape
+    return _quantize_rows(w_bits, bf16_bits_to_f32)
+
+
+def quantize_f32(w):
+    """A float32 weight [n_out, n_in] -> (packed, absmax), by the same readings
+    2-4 applied to its float32 values (a float32 holding a bf16 value gives the
+    bf16 result)."""
+    w = np.asarray(w, dtype=np.float32)
+    return _quantize_rows(w, lambda x: x)
+
+
+def _quantize_rows(w, to_f32):
+    n_out, n_in = w.shape
     _check_shape(n_out, n_in)
     packed = np.empty((n_out, n_in // 2), dtype=np.uint8)
     absmax = np.empty((n_out, n_in // BLOCK), dtype=np.float32)
     rows = max(1, (1 << 20) // max(1, n_in))          # bound the [.., 16] distance tensor
     for r0 in range(0, n_out, rows):
-        x = bf16_bits_to_f32(w_bits[r0:r0 + rows]).reshape(-1, n_in // BLOCK, BLOCK)
+        x = to_f32(w[r0:r0 + rows]).reshape(-1, n_in // BLOCK, BLOCK)
         if not np.isfinite(x).all():
             raise ValueError("non-finite value in NF4 quantize input")
         a = np.max(np.abs(x), axis=-1)                           # exact in float32

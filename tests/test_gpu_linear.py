@@ -18,13 +18,15 @@ BF16_TOL = 1e-2
 F32_TOL = 1e-5
 
 
-def _quantize_gpu(w_bits):
-    n, k = w_bits.shape
-    w = dev_bits(w_bits)
+def _quantize_gpu(w_bits, f32=None):
+    """bf16 bits (or, with f32, that float32 array) through nf4_quantize with a device flag."""
+    n, k = w_bits.shape if f32 is None else f32.shape
+    w = dev_bits(w_bits) if f32 is None else dev(f32)
     packed = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
     absmax = torch.empty((n, k // 64), dtype=torch.float32, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    lib.call("nf4_quantize", ptr(w), n, k, ptr(packed), ptr(absmax), ptr(flag), stream())
+    lib.call("nf4_quantize", ptr(w), lib.LSQ_BF16 if f32 is None else lib.LSQ_F32, n, k, 64, ptr(packed),
+             ptr(absmax), ptr(flag), stream())
     torch.cuda.synchronize()
     return packed, absmax, flag
 
@@ -49,6 +51,44 @@ def test_nf4_quantize_flags_nonfinite(gpu):
     w[2, 70] = 0x7F80   # +inf
     _, _, flag = _quantize_gpu(w)
     assert flag.item() == 1
+
+
+def test_nf4_quantize_f32_input_bit_exact(gpu):
+    """float32 weights (values no bf16 holds, tiny blocks, an all-zero block and
+    exact level midpoints, which only a float32 input can reach)."""
+    print_case(test="nf4_quantize_f32", shape=(96, 320))
+    x = (synth.normal_bf16((96, 320), 0.0, 0.02, (91,)).astype(np.uint32) << 16).view(np.float32)
+    x = x * np.float32(1.0 + 2.0 ** -12)               # off the bf16 grid
+    x[0, :64] = 0
+    x[1, :64] *= np.float32(1e-30)
+    c = onf4.codebook().astype(np.float64)
+    mids = [np.float32((c[j] + c[j + 1]) / 2) for j in range(15)
+            if float(np.float32((c[j] + c[j + 1]) / 2)) == (c[j] + c[j + 1]) / 2]
+    x[2, :64] = 0
+    x[2, 0] = 1.0
+    x[2, 1:1 + len(mids)] = mids
+    packed, absmax, flag = _quantize_gpu(None, f32=x)
+    rp, ra = onf4.quantize_f32(x)
+    assert np.array_equal(packed.cpu().numpy(), rp)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    assert flag.item() == 0
+
+
+def test_nf4_quantize_without_flag_returns_nonfinite(gpu):
+    """Called without a device flag, the call waits and returns the status itself,
+    and a finite input after a refused one still succeeds."""
+    w = synth.normal_bf16((4, 128), 0.0, 0.02, (92,))
+    bad = w.copy()
+    bad[1, 5] = 0x7FC0   # NaN
+    out_p = torch.empty((4, 64), dtype=torch.uint8, device="cuda")
+    out_a = torch.empty((4, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("nf4_quantize", ptr(dev_bits(bad)), lib.LSQ_BF16, 4, 128, 64, ptr(out_p), ptr(out_a), None,
+                 stream())
+    assert e.value.status == "LSQ_ERR_NONFINITE"
+    lib.call("nf4_quantize", ptr(dev_bits(w)), lib.LSQ_BF16, 4, 128, 64, ptr(out_p), ptr(out_a), None, stream())
+    rp, ra = onf4.quantize(w)
+    assert np.array_equal(out_p.cpu().numpy(), rp) and np.array_equal(out_a.cpu().numpy(), ra)
 
 
 # whole and partial 2048-weight wave segments, down to a single 64-block

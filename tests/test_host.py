@@ -277,9 +277,13 @@ def test_large_layer_streaming_and_loss_chunk_terms():
 # memory at all: every check runs before the first HIP call, so nothing is
 # ever dereferenced or launched, and they run without a GPU.
 def test_nf4_shape_errors_enqueue_nothing():
-    with pytest.raises(lib.LsqError) as e:
-        lib.call("nf4_quantize", C.c_void_p(16), 4, 96, C.c_void_p(16), C.c_void_p(16), None, None)
-    assert e.value.status == "LSQ_ERR_SHAPE"
+    fake = C.c_void_p(16)
+    for args, status in (((lib.LSQ_BF16, 4, 96, 64), "LSQ_ERR_SHAPE"),      # n_in % 64 != 0
+                         ((lib.LSQ_BF16, 4, 128, 32), "LSQ_ERR_SHAPE"),     # the store format's block is 64
+                         ((7, 4, 128, 64), "LSQ_ERR_INVALID")):             # not bf16 or float32 input
+        with pytest.raises(lib.LsqError) as e:
+            lib.call("nf4_quantize", fake, *args, fake, fake, None, None)
+        assert e.value.status == status, args
 
 
 def test_bf16_linear_rejects_n_out_not_a_multiple_of_8():

@@ -109,6 +109,46 @@ def test_quantize_is_nearest_code_brute_force():
             assert codes[r, k] == best
 
 
+def test_quantize_f32_is_nearest_code_brute_force():
+    """The float32 entry, on values no bf16 can hold: every element against all
+    16 levels in plain Python floats."""
+    g = np.random.default_rng(41)
+    x = (g.standard_normal((3, 128)) * 0.02).astype(np.float32)
+    assert not np.array_equal(bf16.bf16_bits_to_f32(bf16.f32_to_bf16_bits(x)), x)
+    packed, absmax = nf4.quantize_f32(x)
+    codes = nf4.unpack_codes(packed)
+    c = [float(v) for v in nf4.codebook()]
+    for r in range(3):
+        for k in range(128):
+            a = max(abs(float(v)) for v in x[r, (k // 64) * 64:(k // 64 + 1) * 64])
+            assert absmax[r, k // 64] == np.float32(a)
+            n = float(np.float32(x[r, k]) / np.float32(a))
+            best = min(range(16), key=lambda j: (abs(n - c[j]), j))
+            assert codes[r, k] == best
+
+
+def test_quantize_f32_of_bf16_values_equals_the_bf16_entry():
+    g = np.random.default_rng(42)
+    w = _bits(g.standard_normal((5, 192)) * 0.02)
+    p1, a1 = nf4.quantize(w)
+    p2, a2 = nf4.quantize_f32(bf16.bf16_bits_to_f32(w))
+    assert np.array_equal(p1, p2) and np.array_equal(a1.view(np.uint32), a2.view(np.uint32))
+
+
+def test_quantize_f32_exact_midpoint_goes_to_lower_code():
+    """A float32 input can sit exactly on a level midpoint (x / 1.0 = x): the
+    lower level wins, the next float32 up takes the upper one."""
+    c = nf4.codebook().astype(np.float64)
+    j = next(j for j in range(8, 15) if float(np.float32((c[j] + c[j + 1]) / 2)) == (c[j] + c[j + 1]) / 2)
+    m = np.float32((c[j] + c[j + 1]) / 2)
+    row = np.zeros(64, dtype=np.float32)
+    row[0] = 1.0                       # absmax 1: the quotient is the value itself
+    row[1] = m
+    row[2] = np.nextafter(m, np.float32(2))
+    codes = nf4.unpack_codes(nf4.quantize_f32(row[None, :])[0])[0]
+    assert codes[0] == 15 and codes[1] == j and codes[2] == j + 1
+
+
 def test_quantize_monotone_within_block():
     g = np.random.default_rng(5)
     x = np.sort(g.standard_normal(64)).astype(np.float32)

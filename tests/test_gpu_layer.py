@@ -135,6 +135,8 @@ def layer_errors(cfg, got, x_bits, dout):
 WORKLOAD_LAYERS = [
     configs.LAYER_8B.with_(name="llama8b-layer-s100", seq=100, wid=12),
     configs.LAYER_8B,
+    # ragged length (not a multiple of 64 or 128) in the 128-query attention blocks
+    configs.LAYER_8B.with_(name="llama8b-layer-s1000", seq=1000, wid=14),
     configs.STACK_3B_BF16.with_(name="qwen3b-bf16-layer", n_layers=1, batch=2, seq=200, wid=42),
     configs.STACK_72B.with_(name="qwen72b-layer", n_layers=1, batch=1, seq=100, wid=43),
 ]

@@ -307,3 +307,29 @@ def test_layer_rejects_bad_arguments():
         lib.call("decoder_layer_fwd", C.byref(ccfg), C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1, 8,
                  C.c_void_p(512), C.c_void_p(1024), 16, None)
     assert e.value.status == "LSQ_ERR_WORKSPACE"
+
+
+def test_bench_kernel_family_mapping_and_profile_records():
+    """bench.py's attribution of rocprofv3 kernel names to the library's
+    families (exact identifiers: "ce_kernel" must not catch
+    splitk_reduce_kernel, and the first template argument splits the
+    register-path GEMMs by weight kind), and the committed per-family traffic
+    records are current for the sources they name."""
+    import bench
+    cases = {
+        "void lsq::(anonymous namespace)::gemm_fwd_nf4_dma_kernel<0, 256>(lsq::FwdParams)": "gemm_fwd_nf4_lora",
+        "void lsq::(anonymous namespace)::gemm_fwd_pp_kernel<1, 2>(lsq::FwdParams)": "gemm_bf16_weights",
+        "void lsq::(anonymous namespace)::gemm_fwd_pp_kernel<0, 2>(lsq::FwdParams)": "gemm_fwd_nf4_lora",
+        "void lsq::(anonymous namespace)::splitk_reduce_kernel<1>(float const*, int, int, int)": "other",
+        "lsq::(anonymous namespace)::ce_kernel(float const*, int const*, int, int)": "elementwise",
+        "void lsq::(anonymous namespace)::attn_prep_bwd_kernel<128>(float const*, long)": "attention",
+        "lsq::(anonymous namespace)::lora_grads_kernel(lsq::(anonymous namespace)::GradsArgs)": "lora_skinny",
+        "Cijk_Ailk_Bljk_BBS_BH_Bias_HA_S_SAV_UserArgs_MT256x256x64_MI16x16x1_SN": None,
+        "__amd_rocclr_copyBuffer": None,
+    }
+    for name, fam in cases.items():
+        assert bench.family_of(name) == fam, name
+    # the dominant family's committed counters were taken on the current source
+    rec = bench.profile_record("gemm_fwd_nf4_lora", "llama8b-stack")
+    assert rec is not None and rec["source"].endswith("gemm.hip")
+    assert rec["traffic_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"] > 0

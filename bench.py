@@ -819,6 +819,25 @@ def main():
             "frac_of_pinned_rate": round((cfg.tokens * nk / el) / tok_s, 4)}
         rp.close()
         pstore.close()
+        # more layer buffers (the pages allow 2..8): the turn and the step boundary reuse more slots
+        for nb in (3, 4):
+            pb = lib.VramBreakdown()
+            lib.call("vram_predict_peak", C.byref(lib.model_cfg(cfg)), cfg.batch, cfg.seq, nb, 0, C.byref(pb))
+            rb = model.Runner(cfg, store, res, n_buffers=nb)
+            for _ in range(2):
+                rb.step(ids)
+            torch.cuda.synchronize()
+            rb.stats(reset=True)
+            t0 = time.perf_counter()
+            for _ in range(nk):
+                rb.step(ids)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            sb = rb.stats(reset=True)
+            out["variants"][f"layer_buffers_{nb}"] = {
+                "value": round(cfg.tokens * nk / el, 2), "unit": "tok/s", "ms_per_step": round(el / nk * 1e3, 3),
+                "steps": nk, "copies_per_step": round(sb.copies / nk, 2), "predicted_bytes": pb.total}
+            rb.close()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out))

@@ -88,27 +88,39 @@ __device__ __forceinline__ bool last_arriver(int* counter, int n) {
   return s_last != 0;
 }
 
-// A 16-row block of S = X W^T for a skinny W [nw, K] (nw <= 64) over the
+// RT 16-row tiles of S = X W^T for a skinny W [nw, K] (nw <= 64) over the
 // reduction columns [kb0, kb0 + KCHUNK): the 4 waves take 128 columns each
-// (4 MFMA steps of 32, every load issued before the first MFMA; addresses
-// clamped into the operands, values masked) and meet in red[wave] [16][64].
+// (4 MFMA steps of 32; every load issued before the first MFMA; addresses
+// clamped into the operands, values masked) and meet in red[wave] [16 RT][64].
+// A wave loads its W fragments once for all RT row tiles, so W's bytes per
+// workgroup are spread over 16 RT rows of X.  Each row tile's accumulation
+// (k order inside the wave, then the four waves in order) does not depend on
+// RT.
+template <int RT>
 __device__ __forceinline__ void skinny_block(const uint16_t* __restrict__ X, int64_t ldx, int M, int m0, int K,
                                              int kb0, int kend, const uint16_t* __restrict__ W, int64_t ldw, int nw,
-                                             float (&red)[4][16][64]) {
+                                             float (&red)[4][16 * RT][64]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nct = (nw + 15) / 16;
   const int kb = kb0 + wave * (KCHUNK / 4), ke = min(kend, kb + KCHUNK / 4);
-  const int row = m0 + (lane & 15), g = lane >> 4;
+  const int g = lane >> 4;
   constexpr int NS = KCHUNK / 4 / 32;
-  f32x4 acc[4] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-  uint4 av[NS], bv[NS][4];
-  const int rowc = min(row, M - 1);
+  f32x4 acc[RT][4];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = f32x4{0, 0, 0, 0};
+  uint4 av[RT][NS], bv[NS][4];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int kk = kb + 32 * i + 8 * g, kkc = min(kk, K - 8);
     const bool kin = kk < ke;
-    const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)rowc * ldx + kkc);
-    av[i] = (row < M && kin) ? x : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int row = m0 + 16 * t + (lane & 15);
+      const uint4 x = *reinterpret_cast<const uint4*>(X + (int64_t)min(row, M - 1) * ldx + kkc);
+      av[t][i] = (row < M && kin) ? x : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
@@ -122,14 +134,17 @@ __device__ __forceinline__ void skinny_block(const uint16_t* __restrict__ X, int
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       if (ct >= nct) break;
-      acc[ct] = mfma(as_frag(av[i]), as_frag(bv[i][ct]), acc[ct]);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t][ct] = mfma(as_frag(av[t][i]), as_frag(bv[i][ct]), acc[t][ct]);
     }
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct >= nct) break;
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][ct * 16 + (lane & 15)] = acc[ct][v];
-  }
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nct) break;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][16 * t + 4 * g + v][ct * 16 + (lane & 15)] = acc[t][ct][v];
+    }
   __syncthreads();
 }
 
@@ -144,16 +159,17 @@ struct DownArgs {
   int64_t ldu;
   float* U32;          // [M, ldu32] float32 (nullable)
   int64_t ldu32;
-  float* part;         // [row blocks][nch][16][rr]
+  float* part;         // [row blocks][nch][16 RT][rr]
   int* cnt;            // one per row block
 };
 
-// Grid (row blocks of 16, chunks of KCHUNK input columns).
+// Grid (row blocks of 16 RT, chunks of KCHUNK input columns).
+template <int RT>
 __global__ void __launch_bounds__(NT) lora_down_kernel(DownArgs a) {
-  __shared__ float red[4][16][64];
-  const int rb = blockIdx.x, chunk = blockIdx.y, m0 = rb * 16, tid = threadIdx.x;
-  skinny_block(a.X, a.ldx, a.M, m0, a.K, chunk * KCHUNK, a.K, a.A, a.K, a.rr, red);
-  const int n = 16 * a.rr;
+  __shared__ float red[4][16 * RT][64];
+  const int rb = blockIdx.x, chunk = blockIdx.y, m0 = rb * 16 * RT, tid = threadIdx.x;
+  skinny_block<RT>(a.X, a.ldx, a.M, m0, a.K, chunk * KCHUNK, a.K, a.A, a.K, a.rr, red);
+  const int n = 16 * RT * a.rr;
   auto finish = [&](int e, float v) {
     const int r = e / a.rr, c = e % a.rr;
     v *= a.s;
@@ -173,13 +189,15 @@ __global__ void __launch_bounds__(NT) lora_down_kernel(DownArgs a) {
     put_partial(base + (int64_t)chunk * n + e, ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c]);
   }
   if (!last_arriver(a.cnt + rb, a.nch)) return;
-  constexpr int E = 4;   // n <= 16 * 64 = 4 NT
-  float v[E];
-  ordered_partial_sums<E>(v, base, n, tid, NT, n, a.nch);
+  constexpr int E = 4;
+  for (int e0 = tid; e0 < n; e0 += E * NT) {
+    float v[E];
+    ordered_partial_sums<E>(v, base, n, e0, NT, n, a.nch);
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int e = tid + i * NT;
-    if (e < n && m0 + e / a.rr < a.M) finish(e, v[i]);
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i * NT;
+      if (e < n && m0 + e / a.rr < a.M) finish(e, v[i]);
+    }
   }
 }
 
@@ -197,17 +215,18 @@ struct GArgs {
   int64_t ldg;
   float* G32;          // [M, ldg32] (nullable)
   int64_t ldg32;
-  float* part;         // [row blocks][total chunks][16][r]
+  float* part;         // [row blocks][total chunks][16 RT][r]
   int* cnt;            // [row blocks][nseg]
   int nch;             // total chunks
 };
 
 __device__ __forceinline__ int seg_chunks(int len) { return (len + KCHUNK - 1) / KCHUNK; }
 
-// Grid (row blocks of 16, chunks).
+// Grid (row blocks of 16 RT, chunks).
+template <int RT>
 __global__ void __launch_bounds__(NT) lora_g_kernel(GArgs a) {
-  __shared__ float red[4][16][64];
-  const int rb = blockIdx.x, chunk = blockIdx.y, m0 = rb * 16, tid = threadIdx.x;
+  __shared__ float red[4][16 * RT][64];
+  const int rb = blockIdx.x, chunk = blockIdx.y, m0 = rb * 16 * RT, tid = threadIdx.x;
   // this chunk's segment, its column range and the segment's first chunk
   int sg = 0, c0 = 0, nb = 0, ne = a.seg_end[0];
   int first = 0, begin = 0;
@@ -225,8 +244,8 @@ __global__ void __launch_bounds__(NT) lora_g_kernel(GArgs a) {
     begin = end;
   }
   const int nsc = seg_chunks(ne - nb);
-  skinny_block(a.dY, a.ldy, a.M, m0, a.N, nb + (chunk - c0) * KCHUNK, ne, a.Bt, a.N, a.r, red);
-  const int n = 16 * a.r;
+  skinny_block<RT>(a.dY, a.ldy, a.M, m0, a.N, nb + (chunk - c0) * KCHUNK, ne, a.Bt, a.N, a.r, red);
+  const int n = 16 * RT * a.r;
   auto finish = [&](int e, float v) {
     const int rr = e / a.r, c = e % a.r;
     v *= a.s;
@@ -247,13 +266,15 @@ __global__ void __launch_bounds__(NT) lora_g_kernel(GArgs a) {
                 ((red[0][rr][c] + red[1][rr][c]) + red[2][rr][c]) + red[3][rr][c]);
   }
   if (!last_arriver(a.cnt + rb * a.nseg + sg, nsc)) return;
-  constexpr int E = 4;   // n <= 16 * 64 = 4 NT
-  float v[E];
-  ordered_partial_sums<E>(v, base, n, tid, NT, n, nsc);
+  constexpr int E = 4;
+  for (int e0 = tid; e0 < n; e0 += E * NT) {
+    float v[E];
+    ordered_partial_sums<E>(v, base, n, e0, NT, n, nsc);
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int e = tid + i * NT;
-    if (e < n && m0 + e / a.r < a.M) finish(e, v[i]);
+    for (int i = 0; i < E; ++i) {
+      const int e = e0 + i * NT;
+      if (e < n && m0 + e / a.r < a.M) finish(e, v[i]);
+    }
   }
 }
 
@@ -291,6 +312,20 @@ struct GradsArgs {
   int* cnt;             // one per column tile
 };
 constexpr int TNM_COLS = 128, TNM_TOK = 64;
+// Element offset of (column, token) in the staged L tile: unpadded 128-byte
+// column rows whose 16-byte chunks of 8 tokens are permuted per column (chunk
+// index XOR (col ^ 5 (col >> 3)) & 7), and of (small index, token) in the
+// staged S tile: 256-byte rows of 16 chunks of 4 tokens, chunk index XOR
+// row & 15.  Measured on gfx950 (SQ_LDS_BANK_CONFLICT): the fragment reads of
+// both tiles are conflict-free, and the L staging writes (one thread: 8
+// columns 8 apart, 4 tokens) cost 4 conflict cycles each instead of the 60
+// of rows padded to 144 bytes; the S reads cost 4 in rows padded to 272 bytes.
+__device__ __forceinline__ int lt_off(int col, int tok) {
+  return col * TNM_TOK + ((((tok >> 3) ^ col ^ (5 * (col >> 3))) & 7) << 3) + (tok & 7);
+}
+__device__ __forceinline__ int st_off(int row, int tok) {
+  return row * TNM_TOK + ((((tok >> 2) ^ row) & 15) << 2) + (tok & 3);
+}
 
 struct Task {
   const float* S;
@@ -354,8 +389,8 @@ __device__ __forceinline__ Task grads_task(const GradsArgs& a, int tile) {
 }
 
 __global__ void __launch_bounds__(NT) lora_grads_kernel(GradsArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t LT[TNM_COLS][TNM_TOK + 8];   // [column][token], bf16
-  __shared__ __attribute__((aligned(16))) float ST[64][TNM_TOK + 4];            // [small index][token]
+  __shared__ __attribute__((aligned(16))) uint16_t LT[TNM_COLS * TNM_TOK];   // [column][token] by lt_off, bf16
+  __shared__ __attribute__((aligned(16))) float ST[64 * TNM_TOK];               // [small index][token] by st_off
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const Task tk = grads_task(a, blockIdx.x);
   const int b0 = (blockIdx.x - tk.tile0) * TNM_COLS;
@@ -366,71 +401,71 @@ __global__ void __launch_bounds__(NT) lora_grads_kernel(GradsArgs a) {
   const int lr = 4 * (tid >> 4), lc = 8 * (tid & 15);
   const int scol = b0 + lc;
   const int sa = 16 * wave;
-  uint4 lv[4];
-  float4 sv[4];
-  auto load = [&](int m0) __attribute__((always_inline)) {
+  // Two register sets of staged operands, by k-step parity: the loads of
+  // k-step k + 2 go out while k-step k + 1 waits in the other set, so two
+  // k-steps of each workgroup are in flight while it computes.
+  uint4 lv[2][4];
+  float4 sv[2][4];
+  auto load = [&](int m0, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + lr + i;
       const uint16_t* row = tk.L + (int64_t)m * tk.ldl + scol;
       if (m < m_hi && scol + 8 <= tk.nl) {
-        lv[i] = *reinterpret_cast<const uint4*>(row);
+        lv[set][i] = *reinterpret_cast<const uint4*>(row);
       } else if (m < m_hi && scol + 4 <= tk.nl) {
         const uint2 h = *reinterpret_cast<const uint2*>(row);
-        lv[i] = make_uint4(h.x, h.y, 0u, 0u);
+        lv[set][i] = make_uint4(h.x, h.y, 0u, 0u);
       } else {
-        lv[i] = make_uint4(0u, 0u, 0u, 0u);
+        lv[set][i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
     const int m = m0 + lane;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int aa = sa + 4 * q;
-      sv[q] = (m < m_hi && aa < ns) ? *reinterpret_cast<const float4*>(tk.S + (int64_t)m * tk.lds + aa)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      sv[set][q] = (m < m_hi && aa < ns) ? *reinterpret_cast<const float4*>(tk.S + (int64_t)m * tk.lds + aa)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto store = [&]() __attribute__((always_inline)) {
-    const uint32_t w[4][4] = {{lv[0].x, lv[0].y, lv[0].z, lv[0].w}, {lv[1].x, lv[1].y, lv[1].z, lv[1].w},
-                              {lv[2].x, lv[2].y, lv[2].z, lv[2].w}, {lv[3].x, lv[3].y, lv[3].z, lv[3].w}};
+  auto store = [&](int set) __attribute__((always_inline)) {
+    const uint4(&l)[4] = lv[set];
+    const uint32_t w[4][4] = {{l[0].x, l[0].y, l[0].z, l[0].w}, {l[1].x, l[1].y, l[1].z, l[1].w},
+                              {l[2].x, l[2].y, l[2].z, l[2].w}, {l[3].x, l[3].y, l[3].z, l[3].w}};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int sel = (c & 1) ? 0x07060302 : 0x05040100;   // high or low bf16 of each token's word
       const uint32_t lo = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
       const uint32_t hi = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
-      *reinterpret_cast<u32x2*>(&LT[lc + c][lr]) = u32x2{lo, hi};
+      *reinterpret_cast<u32x2*>(&LT[lt_off(lc + c, lr)]) = u32x2{lo, hi};
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ST[sa + 4 * q + 0][lane] = sv[q].x;
-      ST[sa + 4 * q + 1][lane] = sv[q].y;
-      ST[sa + 4 * q + 2][lane] = sv[q].z;
-      ST[sa + 4 * q + 3][lane] = sv[q].w;
+      ST[st_off(sa + 4 * q + 0, lane)] = sv[set][q].x;
+      ST[st_off(sa + 4 * q + 1, lane)] = sv[set][q].y;
+      ST[st_off(sa + 4 * q + 2, lane)] = sv[set][q].z;
+      ST[st_off(sa + 4 * q + 3, lane)] = sv[set][q].w;
     }
   };
   const int J = (ns + 15) / 16;
   f32x4 acc[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load(m_lo);
-  for (int m0 = m_lo; m0 < m_hi; m0 += TNM_TOK) {
-    __syncthreads();   // the previous k-step's fragment reads are done
-    store();
-    __syncthreads();
-    if (m0 + TNM_TOK < m_hi) load(m0 + TNM_TOK);
+  // The tokens' products in k-step order, one k-step staged in LDS at a time.
+  auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int t0 = 32 * kb + 8 * (lane >> 4);
       bf16x8 bfr[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        bfr[c] = *reinterpret_cast<const bf16x8*>(&LT[32 * wave + 16 * c + (lane & 15)][t0]);
+        bfr[c] = *reinterpret_cast<const bf16x8*>(&LT[lt_off(32 * wave + 16 * c + (lane & 15), t0)]);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (g >= J) break;
-        const float* srow = &ST[16 * g + (lane & 15)][t0];
-        const float4 f0 = *reinterpret_cast<const float4*>(srow);
-        const float4 f1 = *reinterpret_cast<const float4*>(srow + 4);
+        const int srow = 16 * g + (lane & 15);
+        const float4 f0 = *reinterpret_cast<const float4*>(&ST[st_off(srow, t0)]);
+        const float4 f1 = *reinterpret_cast<const float4*>(&ST[st_off(srow, t0 + 4)]);
         const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
         uint32_t hw[4], lw[4];
 #pragma unroll
@@ -447,6 +482,20 @@ __global__ void __launch_bounds__(NT) lora_grads_kernel(GradsArgs a) {
         }
       }
     }
+  };
+  auto step = [&](int m0, int set) __attribute__((always_inline)) {
+    __syncthreads();   // the previous k-step's fragment reads are done
+    store(set);
+    __syncthreads();
+    if (m0 + 2 * TNM_TOK < m_hi) load(m0 + 2 * TNM_TOK, set);
+    compute();
+  };
+  load(m_lo, 0);
+  if (m_lo + TNM_TOK < m_hi) load(m_lo + TNM_TOK, 1);
+  for (int m0 = m_lo; m0 < m_hi; m0 += 2 * TNM_TOK) {
+    step(m0, 0);
+    if (m0 + TNM_TOK >= m_hi) break;
+    step(m0 + TNM_TOK, 1);
   }
   // lane holds C[4 (lane >> 4) + v][lane & 15]: small index row, column
   auto put = [&](int aa, int b, float v) {
@@ -544,10 +593,23 @@ size_t counters_bytes(int n) { return ((size_t)std::max(n, 1) * sizeof(int) + 25
 
 int zero_counters(int* cnt, int n, hipStream_t s) { return zero_words(cnt, n, 1, n, s); }
 
+// Row tiles per workgroup of the down and G projections: the largest of 4, 2
+// and 1 that still gives the launch kSkinnyBlocks workgroups (about two per
+// CU), so that small launches keep every CU loading and large ones read the
+// skinny operand once per 64 or 32 rows instead of once per 16.
+constexpr int kSkinnyBlocks = 512;
+static int skinny_rt(int M, int nch) {
+  for (int rt = 4; rt > 1; rt /= 2)
+    if ((int64_t)((M + 16 * rt - 1) / (16 * rt)) * nch >= kSkinnyBlocks) return rt;
+  return 1;
+}
+// Partial rows of a split launch: M rounded up to 64 covers every row tiling.
+static int64_t skinny_part_rows(int M) { return ((int64_t)M + 63) / 64 * 64; }
+
 int lora_down_counters(int M) { return (M + 15) / 16; }
 size_t lora_down_ws_bytes(int M, int K, int rr) {
   const int nch = (K + KCHUNK - 1) / KCHUNK;
-  return nch > 1 ? (size_t)lora_down_counters(M) * nch * 16 * rr * sizeof(float) : 0;
+  return nch > 1 ? (size_t)skinny_part_rows(M) * nch * rr * sizeof(float) : 0;
 }
 
 int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, int rr, float s, uint16_t* U,
@@ -559,8 +621,12 @@ int lora_down(const uint16_t* X, int64_t ldx, int M, int K, const uint16_t* A, i
   LSQ_CHECK(nch == 1 || (ws && ws_bytes >= lora_down_ws_bytes(M, K, rr) && cnt), LSQ_ERR_WORKSPACE,
             "lora_down: workspace too small");
   DownArgs a{X, ldx, M, K, rr, nch, A, s, U, ldu, U32, ldu32, ws, cnt};
+  const int rt = skinny_rt(M, nch);
+  const dim3 grid((M + 16 * rt - 1) / (16 * rt), nch);
   int tok = prof_begin(st);
-  lora_down_kernel<<<dim3(lora_down_counters(M), nch), NT, 0, st>>>(a);
+  if (rt == 4) lora_down_kernel<4><<<grid, NT, 0, st>>>(a);
+  else if (rt == 2) lora_down_kernel<2><<<grid, NT, 0, st>>>(a);
+  else lora_down_kernel<1><<<grid, NT, 0, st>>>(a);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)K * rr, 2.0 * M * (double)K + 2.0 * rr * K + 2.0 * M * rr);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
@@ -574,7 +640,7 @@ static int g_total_chunks(int nseg, const SegEnds& segs) {
 int lora_g_counters(int M, int nseg) { return (M + 15) / 16 * nseg; }
 size_t lora_g_ws_bytes(int M, int N, int r) {
   // chunks <= N / KCHUNK + one partial chunk per segment (at most 4)
-  return (size_t)((M + 15) / 16) * ((N + KCHUNK - 1) / KCHUNK + 4) * 16 * r * sizeof(float);
+  return (size_t)skinny_part_rows(M) * ((N + KCHUNK - 1) / KCHUNK + 4) * r * sizeof(float);
 }
 
 int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* Bt, int r, int nseg, const SegEnds& segs,
@@ -605,8 +671,12 @@ int lora_g(const uint16_t* dY, int64_t ldy, int M, int N, const uint16_t* Bt, in
   a.part = ws;
   a.cnt = cnt;
   a.nch = g_total_chunks(nseg, segs);
+  const int rt = skinny_rt(M, a.nch);
+  const dim3 grid((M + 16 * rt - 1) / (16 * rt), a.nch);
   int tok = prof_begin(st);
-  lora_g_kernel<<<dim3((M + 15) / 16, a.nch), NT, 0, st>>>(a);
+  if (rt == 4) lora_g_kernel<4><<<grid, NT, 0, st>>>(a);
+  else if (rt == 2) lora_g_kernel<2><<<grid, NT, 0, st>>>(a);
+  else lora_g_kernel<1><<<grid, NT, 0, st>>>(a);
   prof_end(tok, st, PROF_LORA, 2.0 * M * (double)N * r, 2.0 * M * (double)N + 2.0 * N * r + 2.0 * M * r * nseg);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;

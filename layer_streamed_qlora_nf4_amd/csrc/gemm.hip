@@ -40,10 +40,13 @@ constexpr int NTHREADS = 256;   // 4 waves
 // 128-bit LDS pass read 8 different bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 // Transposed weight tile (backward): row = output column k, 64 reduction values.
-// The swizzle also folds in k >> 3 so the transposing writes (rows 8 apart)
-// spread over banks too.
+// The swizzle also folds in 5 (k >> 3) so the transposing writes (rows 8
+// apart) spread over banks too.  Measured on gfx950 with
+// SQ_LDS_BANK_CONFLICT, both the fragment reads (16 consecutive rows) and the
+// transposing 8-byte writes are conflict-free with this form; folding in
+// k >> 3 unmultiplied cost 4 conflict cycles per fragment read.
 __device__ __forceinline__ int swzt(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 3);
+  return row * 64 + ((chunk ^ ((row ^ (5 * (row >> 3))) & 7)) << 3);
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* base, int idx) {

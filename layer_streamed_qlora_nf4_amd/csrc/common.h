@@ -52,6 +52,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Sum over splits of a split-K launch's float32 partials part[s][e .. e + 3]
+// (total elements per split apart), in split order; the loads go out four
+// splits at a time.  Every kernel that consumes split-K partials sums them
+// through this, so a fused consumer gives the same bits as the plain
+// reduction.
+__device__ __forceinline__ float4 split_sum4(const float* __restrict__ part, int splits, int64_t total, int64_t e) {
+  float4 v = *reinterpret_cast<const float4*>(part + e);
+  for (int sb = 1; sb < splits; sb += 4) {
+    float4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (sb + j < splits) ? *reinterpret_cast<const float4*>(part + (int64_t)(sb + j) * total + e)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sb + j < splits) {
+        v.x += w[j].x;
+        v.y += w[j].y;
+        v.z += w[j].z;
+        v.w += w[j].w;
+      }
+  }
+  return v;
+}
+
 // ------------------------------------------------------------------ timing hooks
 namespace lsq {
 // Kernel families credited by the profiler (lsq_prof_*).

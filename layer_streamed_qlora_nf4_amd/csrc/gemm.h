@@ -81,8 +81,14 @@ size_t gemm_fwd_ws_bytes(int M, int N, int K);
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr);
 
 // ws: split-K partial buffer (>= the *_ws_bytes query), may be null when that is 0.
-int gemm_fwd(const FwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
-int gemm_bwd(const BwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0);
+// With deferred_splits, a split-K launch leaves its float32 partials at the
+// start of ws ([splits][M][out width]) for the caller to reduce (split_sum4
+// order) and stores the split count there; 1 means the tile kernel wrote the
+// output itself.
+int gemm_fwd(const FwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0,
+             int* deferred_splits = nullptr);
+int gemm_bwd(const BwdParams& p, int epi, hipStream_t s, void* ws = nullptr, size_t ws_bytes = 0,
+             int* deferred_splits = nullptr);
 // ------------------------------------------------------------ rank-r kernels (lora.hip)
 // Each product is one launch; where its reduction is split over workgroups,
 // the last workgroup of a group to arrive sums the group's float32 partials

@@ -1173,23 +1173,7 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   const int64_t e = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   const int64_t total = (int64_t)M * N;
   if (e >= total) return;
-  // Partials added in split order; the loads go out four splits at a time.
-  float4 v = *reinterpret_cast<const float4*>(part + e);
-  for (int sb = 1; sb < splits; sb += 4) {
-    float4 w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (sb + j < splits) ? *reinterpret_cast<const float4*>(part + (int64_t)(sb + j) * total + e)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (sb + j < splits) {
-        v.x += w[j].x;
-        v.y += w[j].y;
-        v.z += w[j].z;
-        v.w += w[j].w;
-      }
-  }
+  const float4 v = split_sum4(part, splits, total, e);
   const int64_t row = e / N, col = e % N;
   float r[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1331,7 +1315,7 @@ size_t gemm_fwd_ws_bytes(int M, int N, int K) {
 }
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) { return gemm_bwd_part_bytes(M, N, K, rr); }
 
-int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
+int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes, int* deferred_splits) {
   FwdParams p = p_in;
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
   if (p.Kw == 0) p.Kw = p.K;
@@ -1357,7 +1341,8 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   if (p.kind == LSQ_W_NF4) dispatch_fwd_epi<LSQ_W_NF4>(p, epi, s, e0, e1);
   else dispatch_fwd_epi<LSQ_W_BF16>(p, epi, s, e0, e1);
   prof_end_kernel(tok, p.kind == LSQ_W_NF4 ? PROF_GEMM_FWD : PROF_GEMM_BF16, flops, bytes);
-  if (p.splits > 1) {
+  if (deferred_splits) *deferred_splits = p.splits;
+  if (p.splits > 1 && !deferred_splits) {
     tok = prof_begin(s);
     launch_reduce(p.part, p.splits, p.M, p.N, p.bias, p.resid, p.out, p.ldc, epi, s);
     prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * p.splits * p.M * (double)p.N + 2.0 * p.M * (double)p.N);
@@ -1366,7 +1351,7 @@ int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   return LSQ_OK;
 }
 
-int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes) {
+int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes, int* deferred_splits) {
   BwdParams p = p_in;
   LSQ_CHECK(p.K % 64 == 0, LSQ_ERR_SHAPE, "gemm: K=%d must be a multiple of 64", p.K);
   LSQ_CHECK(p.N % 8 == 0 && p.rr % 8 == 0 && p.ldy % 8 == 0 && p.ldg % 8 == 0, LSQ_ERR_SHAPE,
@@ -1386,7 +1371,8 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   if (p.kind == LSQ_W_NF4) dispatch_bwd_epi<LSQ_W_NF4>(p, epi, s, e0, e1);
   else dispatch_bwd_epi<LSQ_W_BF16>(p, epi, s, e0, e1);
   prof_end_kernel(tok, p.kind == LSQ_W_NF4 ? PROF_GEMM_BWD : PROF_GEMM_BF16, flops, bytes);
-  if (p.splits > 1) {
+  if (deferred_splits) *deferred_splits = p.splits;
+  if (p.splits > 1 && !deferred_splits) {
     tok = prof_begin(s);
     launch_reduce(p.part, p.splits, p.M, p.K, nullptr, p.resid, p.out, p.ldc, epi, s);
     prof_end(tok, s, PROF_OTHER, 0.0, 4.0 * p.splits * p.M * (double)p.K + 2.0 * p.M * (double)p.K);

@@ -417,14 +417,21 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     TRY(attention_fwd(a, B, s));
   }
   TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, w.cnt, s));
+  // h = x + o(attn) and the MLP's RMSNorm; a split-K o projection leaves its
+  // partials to the norm kernel, which sums them (and writes h) on the way in
   {
     FwdParams p = fwd_params(w.attn, T, bv.w[1], w.U_o, r, lv.B[1], r);
     p.resid = x_in;
     p.out = w.h;
-    TRY(gemm_fwd(p, EPI_F32_RESID, s, w.gemm, w.gemm_bytes));
+    int sp = 1;
+    TRY(gemm_fwd(p, EPI_F32_RESID, s, w.gemm, w.gemm_bytes, &sp));
+    if (sp > 1)
+      TRY(splitk_resid_rmsnorm_fwd(static_cast<const float*>(w.gemm), sp, x_in, w.h, bv.norm2, T, d.H, c->rms_eps,
+                                   w.xn2, d.H, s));
+    else
+      TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, d.H, nullptr, s));
   }
   // MLP block
-  TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, d.H, nullptr, s));
   TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, w.cnt, s));
   {
     FwdParams p = fwd_params(w.xn2, T, bv.w[2], w.U_gu, 2 * r, lv.B[2], r);
@@ -489,34 +496,45 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
   one.end[0] = d.H;
   TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[3], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
+  // dm, and through SwiGLU dgu; a split-K launch leaves dm's partials to the
+  // SwiGLU kernel
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[3], w.G, r, lv.A[3], lv.AT[3], r);
     p.out = w.dm;
-    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
+    int sp = 1;
+    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes, &sp));
+    if (sp > 1)
+      TRY(splitk_swiglu_bwd(w.gu, static_cast<const float*>(w.gemm), sp, T, d.I, w.dgu, s));
+    else
+      TRY(swiglu_bwd(w.gu, w.dm, T, d.I, w.dgu, s));
   }
   {
     const int se[1] = {d.H};
     TRY(adapter_grads(d, T, w.G32, r, w.U32[3], r, w.m, d.I, d.I, w.dy_b, d.H, 1, se, gA[3], gB[3], accumulate, w, s));
   }
-  // ---- SwiGLU and gate/up
-  TRY(swiglu_bwd(w.gu, w.dm, T, d.I, w.dgu, s));
+  // ---- gate/up
   SegEnds two{};
   two.end[0] = d.I;
   two.end[1] = 2 * d.I;
   TRY(lora_g(w.dgu, 2 * d.I, T, 2 * d.I, lv.BT[2], r, 2, two, sc, w.G, 2 * r, w.G32, 2 * r, w.lws, w.lws_bytes,
              w.cnt, s));
+  // dxn2, then dh = dout + rmsnorm2'(dxn2) (from the partials of a split-K launch)
   {
     BwdParams p = bwd_params(w.dgu, T, bv.w[2], w.G, 2 * r, lv.A[2], lv.AT[2], 2 * r);
     p.out = w.dxn;
-    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
+    int sp = 1;
+    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes, &sp));
+    if (sp > 1)
+      TRY(splitk_rmsnorm_bwd(w.h, bv.norm2, static_cast<const float*>(w.gemm), sp, dx_out, T, d.H, c->rms_eps, w.dh,
+                             w.dy_b, s));
+    else
+      TRY(rmsnorm_bwd(w.h, bv.norm2, w.dxn, dx_out, T, d.H, c->rms_eps, w.dh, w.dy_b, s));
   }
   {
     const int se[2] = {d.I, 2 * d.I};
     TRY(adapter_grads(d, T, w.G32, 2 * r, w.U32[2], 2 * r, w.xn2, d.H, d.H, w.dgu, 2 * d.I, 2, se, gA[2], gB[2], accumulate,
                       w, s));
   }
-  // dh = dout + rmsnorm2'(dxn2)
-  TRY(rmsnorm_bwd(w.h, bv.norm2, w.dxn, dx_out, T, d.H, c->rms_eps, w.dh, w.dy_b, s));
   // ---- o projection
   one.end[0] = d.H;
   TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[1], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
@@ -542,18 +560,23 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   three.end[2] = d.Nqkv;
   TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.BT[0], r, 3, three, sc, w.G, 3 * r, w.G32, 3 * r, w.lws,
              w.lws_bytes, w.cnt, s));
+  // dxn1, then dx = dh + rmsnorm1'(dxn1) (from the partials of a split-K launch)
   {
     BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], lv.AT[0], 3 * r);
     p.out = w.dxn;
-    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
+    int sp = 1;
+    TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes, &sp));
+    if (sp > 1)
+      TRY(splitk_rmsnorm_bwd(x_in, bv.norm1, static_cast<const float*>(w.gemm), sp, w.dh, T, d.H, c->rms_eps, dx_in,
+                             nullptr, s));
+    else
+      TRY(rmsnorm_bwd(x_in, bv.norm1, w.dxn, w.dh, T, d.H, c->rms_eps, dx_in, nullptr, s));
   }
   {
     const int se[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
     TRY(adapter_grads(d, T, w.G32, 3 * r, w.U32[0], 3 * r, w.xn1, 2 * d.H, d.H, w.dqkv, d.Nqkv, 3, se, gA[0], gB[0], accumulate,
                       w, s));
   }
-  // dx = dh + rmsnorm1'(dxn1)
-  TRY(rmsnorm_bwd(x_in, bv.norm1, w.dxn, w.dh, T, d.H, c->rms_eps, dx_in, nullptr, s));
   return LSQ_OK;
 }
 

@@ -49,6 +49,14 @@ int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint
                 hipStream_t s, uint16_t* y_lo = nullptr);
 int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float* gres, int T, int H, float eps,
                 float* dx, uint16_t* dx_b, hipStream_t s);
+// The same row kernels fed by a GEMM's deferred split-K partials ([splits][T][H],
+// summed in split order): h = resid + sum (stored), then y = rmsnorm(h); and
+// the backward with dy = sum.  Bit-identical to the reduction followed by the
+// plain kernel.
+int splitk_resid_rmsnorm_fwd(const float* part, int splits, const float* resid, float* h, const uint16_t* w, int T,
+                             int H, float eps, uint16_t* y, int64_t ldy, hipStream_t s);
+int splitk_rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy_part, int splits, const float* gres, int T,
+                       int H, float eps, float* dx, uint16_t* dx_b, hipStream_t s);
 int to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 // Zero rows x cols 32-bit words, row pitch ld words (a kernel, safe under graph capture).
 int zero_words(void* dst, int64_t ld, int rows, int cols, hipStream_t s);
@@ -59,6 +67,9 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s);
 int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s);
 int swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* m, hipStream_t s);
 int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* dgu, hipStream_t s);
+// dm = bf16(sum of a GEMM's deferred split-K partials [splits][T][I]).
+int splitk_swiglu_bwd(const uint16_t* gu, const float* dm_part, int splits, int T, int I, uint16_t* dgu,
+                      hipStream_t s);
 int embed_gather(const int32_t* ids, const uint16_t* table, int T, int H, int V, float* x, int32_t* bad, hipStream_t s);
 // dlogits (and, if non-null, dlogits_lo = bf16 of the remainder) for the head backward.
 int cross_entropy(const float* logits, const int32_t* ids, int B, int S, int V, float* loss_rows, uint16_t* dlogits,

@@ -57,22 +57,44 @@ __device__ __forceinline__ float block4_sum(float v, float* red) {
   return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// Where a row kernel's float32 input comes from: an array, or the split-K
+// partials of the GEMM that produces it, summed in split order (split_sum4,
+// the order of the plain reduction) plus an optional float32 residual, the
+// summed row also stored when out is set.  Fusing the reduction into its
+// consumer this way gives the same bits as the separate reduction kernel.
+struct RowSrc {
+  const float* x;       // [T][H], or null for partials
+  const float* part;    // [splits][T][H]
+  int splits;
+  const float* resid;   // [T][H] (nullable)
+  float* out;           // [T][H] (nullable)
+};
+__device__ __forceinline__ float4 row_load4(const RowSrc& s, int64_t e, int64_t total) {
+  if (s.x) return *reinterpret_cast<const float4*>(s.x + e);
+  float4 v = split_sum4(s.part, s.splits, total, e);
+  if (s.resid) {
+    const float4 r = *reinterpret_cast<const float4*>(s.resid + e);
+    v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+  }
+  if (s.out) *reinterpret_cast<float4*>(s.out + e) = v;
+  return v;
+}
+
 // y = bf16(w * x / sqrt(mean(x^2) + eps)), rows ldy apart; rstd saved.  With
 // y_lo, the output is also written as the bf16 rounding of its own remainder
 // (y + y_lo carries about 16 bits), for GEMMs run as two bf16 passes.
-__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          int T, int H, float eps, uint16_t* __restrict__ y,
-                                                          int64_t ldy, float* __restrict__ rstd,
-                                                          uint16_t* __restrict__ y_lo) {
+__global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(RowSrc x, const uint16_t* __restrict__ w, int T, int H,
+                                                          float eps, uint16_t* __restrict__ y, int64_t ldy,
+                                                          float* __restrict__ rstd, uint16_t* __restrict__ y_lo) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
+  const int64_t r0 = (int64_t)row * H, total = (int64_t)T * H;
   float4 v[kNormMaxV];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kNormMaxV; ++k) {
     const int i = tid + 256 * k;
-    v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[k] = i < n4 ? row_load4(x, r0 + 4 * i, total) : make_float4(0.f, 0.f, 0.f, 0.f);
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   ss = block4_sum(ss, red);
@@ -97,13 +119,13 @@ __global__ void __launch_bounds__(256) rmsnorm_fwd_kernel(const float* __restric
 
 // dx = gres + r (w dy) - x r^3 sum(w dy x) / H ; also a bf16 copy of dx.
 __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          const float* __restrict__ dy, const float* __restrict__ gres,
-                                                          int T, int H, float eps, float* __restrict__ dx,
+                                                          RowSrc dy, const float* __restrict__ gres, int T, int H,
+                                                          float eps, float* __restrict__ dx,
                                                           uint16_t* __restrict__ dx_b) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
-  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)row * H);
-  const float4* dr = reinterpret_cast<const float4*>(dy + (int64_t)row * H);
+  const int64_t r0 = (int64_t)row * H, total = (int64_t)T * H;
+  const float4* xr = reinterpret_cast<const float4*>(x + r0);
   const uint2* wr = reinterpret_cast<const uint2*>(w);
   float4 v[kNormMaxV], d[kNormMaxV];
   float ss = 0.f, dot = 0.f;
@@ -112,7 +134,7 @@ __global__ void __launch_bounds__(256) rmsnorm_bwd_kernel(const float* __restric
     const int i = tid + 256 * k;
     const bool ok = i < n4;
     v[k] = ok ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    d[k] = ok ? dr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    d[k] = ok ? row_load4(dy, r0 + 4 * i, total) : make_float4(0.f, 0.f, 0.f, 0.f);
     const uint2 ww = ok ? wr[i] : make_uint2(0u, 0u);
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     dot += bf_lo(ww.x) * d[k].x * v[k].x + bf_hi(ww.x) * d[k].y * v[k].y + bf_lo(ww.y) * d[k].z * v[k].z +
@@ -1085,15 +1107,30 @@ __global__ void __launch_bounds__(256) swiglu_fwd_kernel(const uint16_t* __restr
 }
 
 // dgu [T, 2I]: dg = dm u sig(g) (1 + g (1 - sig(g))), du = dm silu(g)
+// dm comes from a bf16 array, or (dm null) from the split-K partials of the
+// GEMM that produces it, summed in split order and rounded to bf16 as the
+// plain reduction would store it.
 __global__ void __launch_bounds__(256) swiglu_bwd_kernel(const uint16_t* __restrict__ gu,
-                                                         const uint16_t* __restrict__ dm, int T, int I,
+                                                         const uint16_t* __restrict__ dm,
+                                                         const float* __restrict__ dm_part, int splits, int T, int I,
                                                          uint16_t* __restrict__ dgu) {
   const int i = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= I) return;
   for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
     const uint4 gv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + i);
     const uint4 uv = *reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i);
-    const uint4 dv = *reinterpret_cast<const uint4*>(dm + t * I + i);
+    uint4 dv;
+    if (dm) {
+      dv = *reinterpret_cast<const uint4*>(dm + t * I + i);
+    } else {
+      const int64_t total = (int64_t)T * I;
+      const float4 a = split_sum4(dm_part, splits, total, t * I + i);
+      const float4 b = split_sum4(dm_part, splits, total, t * I + i + 4);
+      auto bits2 = [](float lo, float hi) {
+        return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+      };
+      dv = make_uint4(bits2(a.x, a.y), bits2(a.z, a.w), bits2(b.x, b.y), bits2(b.z, b.w));
+    }
     const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
     uint32_t og[4], ou[4];
 #pragma unroll
@@ -1226,8 +1263,21 @@ int rmsnorm_fwd(const float* x, const uint16_t* w, int T, int H, float eps, uint
             "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
   if (T == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(x, w, T, H, eps, y, ldy, rstd, y_lo);
+  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(RowSrc{x, nullptr, 0, nullptr, nullptr}, w, T, H, eps, y, ldy, rstd, y_lo);
   prof_end(tok, s, PROF_ELEM, 0.0, (4.0 + 2.0 + (y_lo ? 2.0 : 0.0)) * T * (double)H + 2.0 * H + (rstd ? 4.0 * T : 0.0));
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int splitk_resid_rmsnorm_fwd(const float* part, int splits, const float* resid, float* h, const uint16_t* w, int T,
+                             int H, float eps, uint16_t* y, int64_t ldy, hipStream_t s) {
+  LSQ_CHECK(H % 4 == 0 && H <= 4 * 256 * kNormMaxV && splits >= 1, LSQ_ERR_SHAPE,
+            "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
+  if (T == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
+  rmsnorm_fwd_kernel<<<T, 256, 0, s>>>(RowSrc{nullptr, part, splits, resid, h}, w, T, H, eps, y, ldy, nullptr,
+                                       nullptr);
+  prof_end(tok, s, PROF_ELEM, 0.0, (4.0 * splits + (resid ? 4.0 : 0.0) + 4.0 + 2.0) * T * (double)H + 2.0 * H);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -1238,9 +1288,23 @@ int rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy, const float*
             "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
   if (T == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  rmsnorm_bwd_kernel<<<T, 256, 0, s>>>(x, w, dy, gres, T, H, eps, dx, dx_b);
+  rmsnorm_bwd_kernel<<<T, 256, 0, s>>>(x, w, RowSrc{dy, nullptr, 0, nullptr, nullptr}, gres, T, H, eps, dx, dx_b);
   prof_end(tok, s, PROF_ELEM, 0.0,
            (4.0 + 4.0 + 4.0 + (gres ? 4.0 : 0.0) + (dx_b ? 2.0 : 0.0)) * T * (double)H + 2.0 * H);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int splitk_rmsnorm_bwd(const float* x, const uint16_t* w, const float* dy_part, int splits, const float* gres, int T,
+                       int H, float eps, float* dx, uint16_t* dx_b, hipStream_t s) {
+  LSQ_CHECK(H % 4 == 0 && H <= 4 * 256 * kNormMaxV && splits >= 1, LSQ_ERR_SHAPE,
+            "rmsnorm: hidden %d must be a multiple of 4 and at most %d", H, 4 * 256 * kNormMaxV);
+  if (T == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
+  rmsnorm_bwd_kernel<<<T, 256, 0, s>>>(x, w, RowSrc{nullptr, dy_part, splits, nullptr, nullptr}, gres, T, H, eps, dx,
+                                       dx_b);
+  prof_end(tok, s, PROF_ELEM, 0.0,
+           (4.0 + 4.0 * splits + 4.0 + (gres ? 4.0 : 0.0) + (dx_b ? 2.0 : 0.0)) * T * (double)H + 2.0 * H);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }
@@ -1384,9 +1448,21 @@ int swiglu_bwd(const uint16_t* gu, const uint16_t* dm, int T, int I, uint16_t* d
   LSQ_CHECK(I % 8 == 0, LSQ_ERR_SHAPE, "swiglu: intermediate %d must be a multiple of 8", I);
   if ((int64_t)T * I == 0) return LSQ_OK;
   const int tok = prof_begin(s);
-  swiglu_bwd_kernel<<<dim3((unsigned)((I / 8 + 255) / 256), (unsigned)std::min(T, 65535)), 256, 0, s>>>(gu, dm, T, I,
-                                                                                                  dgu);
+  swiglu_bwd_kernel<<<dim3((unsigned)((I / 8 + 255) / 256), (unsigned)std::min(T, 65535)), 256, 0, s>>>(
+      gu, dm, nullptr, 0, T, I, dgu);
   prof_end(tok, s, PROF_ELEM, 0.0, 10.0 * T * (double)I);
+  LSQ_HIP(hipGetLastError());
+  return LSQ_OK;
+}
+
+int splitk_swiglu_bwd(const uint16_t* gu, const float* dm_part, int splits, int T, int I, uint16_t* dgu,
+                      hipStream_t s) {
+  LSQ_CHECK(I % 8 == 0 && splits >= 1, LSQ_ERR_SHAPE, "swiglu: intermediate %d must be a multiple of 8", I);
+  if ((int64_t)T * I == 0) return LSQ_OK;
+  const int tok = prof_begin(s);
+  swiglu_bwd_kernel<<<dim3((unsigned)((I / 8 + 255) / 256), (unsigned)std::min(T, 65535)), 256, 0, s>>>(
+      gu, nullptr, dm_part, splits, T, I, dgu);
+  prof_end(tok, s, PROF_ELEM, 0.0, (8.0 + 4.0 * splits) * T * (double)I);
   LSQ_HIP(hipGetLastError());
   return LSQ_OK;
 }

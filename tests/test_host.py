@@ -300,6 +300,20 @@ def test_bf16_linear_rejects_n_out_not_a_multiple_of_8():
         assert e.value.status == "LSQ_ERR_SHAPE", name
 
 
+def test_noalloc_backward_refuses_a_shape_beyond_its_scratch():
+    """nf4_lora_linear_bwd_noalloc checks the shape's scratch need against its
+    static array before it looks up the array's device address."""
+    M, N, K, r = 3072, 4096, 14336, 16   # its split-K partials alone pass the array
+    need = lib.raw("nf4_lora_linear_workspace_size")(M, N, K, r, lib.LSQ_BF16)
+    assert need > lib.LSQ_NOALLOC_SCRATCH_BYTES
+    weight = lib.Weight(lib.LSQ_W_NF4, 0, 4096, 8192, N, K)
+    fake = C.c_void_p(4096)
+    with pytest.raises(lib.LsqError) as e:
+        lib.call("nf4_lora_linear_bwd_noalloc", C.byref(weight), fake, None, M, fake, fake, r, 2.0, lib.LSQ_BF16,
+                 fake, fake, fake, fake, 0, None)
+    assert e.value.status == "LSQ_ERR_WORKSPACE"
+
+
 def test_layer_rejects_bad_arguments():
     cfg = configs.TINY.with_(n_layers=1)
     ccfg = lib.model_cfg(cfg)

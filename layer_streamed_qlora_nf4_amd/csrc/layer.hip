@@ -409,11 +409,17 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     p.seg_ucol[2] = 2 * r;
     p.bias = bv.bias;
     p.out = w.qkv;
-    TRY(gemm_fwd(p, EPI_F32, s, w.gemm, w.gemm_bytes));
-  }
-  {
+    // a split-K launch leaves its partials to the attention's operand
+    // preparation, which sums them (plus the bias) and writes q/k/v on the way
+    int sp = 1;
+    TRY(gemm_fwd(p, EPI_F32, s, w.gemm, w.gemm_bytes, &sp));
     AttnArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, d.Nq, w.lse,
                reinterpret_cast<const float2*>(w.rope), w.attn_f32, w.aprep};
+    if (sp > 1) {
+      a.qkv_part = static_cast<const float*>(w.gemm);
+      a.qkv_splits = sp;
+      a.qkv_bias = bv.bias;
+    }
     TRY(attention_fwd(a, B, s));
   }
   TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, w.cnt, s));

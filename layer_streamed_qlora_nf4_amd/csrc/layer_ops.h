@@ -18,6 +18,13 @@ struct AttnArgs {
   const float2* rope;  // [S, hd/2] (cos, sin); q and k are rotated on load
   float* out_f32;      // nullable: the same output in float32 (kept for the backward)
   uint16_t* prep;      // attention_prep_bytes(.., false) of workspace
+  // Optional: q/k/v not yet reduced.  With qkv_part set, the preparation sums
+  // the q/k/v product's split-K partials [qkv_splits][B*S][ld] in split order,
+  // adds qkv_bias (bf16, nullable) and stores the result into qkv, as the
+  // plain reduction would, before using it.
+  const float* qkv_part = nullptr;
+  int qkv_splits = 0;
+  const uint16_t* qkv_bias = nullptr;
 };
 
 struct AttnBwdArgs {

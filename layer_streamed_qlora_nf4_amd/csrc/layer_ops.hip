@@ -259,6 +259,43 @@ __device__ __forceinline__ uint4 load8_bf16(const float* p, bool ok) {
   return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                     pack_bf16x2(x[6], x[7]));
 }
+// Where the attention preparation reads the float32 q/k/v from: the array
+// itself, or (part set) the split-K partials of the q/k/v product, summed in
+// split order plus the bias and stored into the array on the way, exactly as
+// the plain reduction would write them.
+struct QkvSrc {
+  float* base;            // the q/k/v array [B*S][ld]
+  const float* part;      // [splits][B*S][ld], or null
+  int splits;
+  int64_t total;          // B*S*ld
+  int64_t ld;
+  const uint16_t* bias;   // [ld] bf16 (nullable)
+};
+__device__ __forceinline__ void load8(const QkvSrc& q, const float* p, bool ok, float (&x)[8]) {
+  if (!q.part || !ok) {
+    load8(p, ok, x);
+    return;
+  }
+  const int64_t e = p - q.base;
+  const float4 a = split_sum4(q.part, q.splits, q.total, e), b = split_sum4(q.part, q.splits, q.total, e + 4);
+  float r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if (q.bias) {
+    const int64_t col = e % q.ld;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] += bf16_bits_to_f32(q.bias[col + j]);
+  }
+  *reinterpret_cast<float4*>(q.base + e) = make_float4(r[0], r[1], r[2], r[3]);
+  *reinterpret_cast<float4*>(q.base + e + 4) = make_float4(r[4], r[5], r[6], r[7]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = r[j];
+}
+__device__ __forceinline__ uint4 load8_bf16(const QkvSrc& q, const float* p, bool ok) {
+  float x[8];
+  load8(q, p, ok, x);
+  return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7]));
+}
+__device__ __forceinline__ uint4 load8_bf16(const QkvSrc&, const uint16_t* p, bool ok) { return load8_bf16(p, ok); }
 // Rotate-half RoPE of 8 consecutive pair indices i .. i+7 at position pos:
 // (x1, x2) -> (x1 c - x2 s, x2 c + x1 s), table[pos][i] = (c, s).
 __device__ __forceinline__ void rope8(float (&x1)[8], float (&x2)[8], const float2* __restrict__ tab) {
@@ -295,8 +332,9 @@ __device__ __forceinline__ void put_mt_t(uint16_t (*dst)[PITCH], int c0, int r0,
 // Rows [row0, row0 + 64) of a bf16 matrix, rotated (RoPE at positions
 // row0 + r) and split into hi/lo, row-major.  Rows at or past n read as zero.
 template <int HD>
-__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + PAD], uint16_t (*lo)[HD + PAD], const float* src,
-                                          int64_t ld, int row0, int n, const float2* __restrict__ rope) {
+__device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + PAD], uint16_t (*lo)[HD + PAD], const QkvSrc& qs,
+                                          const float* src, int64_t ld, int row0, int n,
+                                          const float2* __restrict__ rope) {
   constexpr int HALF = HD / 2, NCH = HALF / 32;
   const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
   const bool ok = r < n;
@@ -305,8 +343,8 @@ __device__ __forceinline__ void stage_rot(uint16_t (*hi)[HD + PAD], uint16_t (*l
     const int i0 = (q * NCH + c) * 8;
     float x1[8], x2[8];
     const float* row = src + (int64_t)(row0 + r) * ld;
-    load8(row + i0, ok, x1);
-    load8(row + HALF + i0, ok, x2);
+    load8(qs, row + i0, ok, x1);
+    load8(qs, row + HALF + i0, ok, x2);
     if (ok) rope8(x1, x2, rope + (int64_t)(row0 + r) * HALF + i0);
     store_hilo8(&hi[r][i0], &lo[r][i0], x1);
     store_hilo8(&hi[r][HALF + i0], &lo[r][HALF + i0], x2);
@@ -335,8 +373,8 @@ __device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + PAD], const u
 }
 // Rows [row0, row0 + 64) of a bf16 matrix straight into [HD][64] (zero past n).
 template <int HD, typename SrcT>
-__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const SrcT* src, int64_t ld, int row0,
-                                             int n) {
+__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const QkvSrc& qs, const SrcT* src, int64_t ld,
+                                             int row0, int n) {
   constexpr int NMT = AT / 4 * (HD / 8);
   for (int t = threadIdx.x; t < NMT; t += 256) {
     const int rg = t / (HD / 8), cg = t % (HD / 8);
@@ -344,7 +382,7 @@ __device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const Sr
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * rg + i;
-      rows[i] = load8_bf16(src + (int64_t)(row0 + r) * ld + 8 * cg, r < n);
+      rows[i] = load8_bf16(qs, src + (int64_t)(row0 + r) * ld + 8 * cg, r < n);
     }
     put_mt_t<AT + PAD>(dst, 8 * cg, 4 * rg, rows);
   }
@@ -468,14 +506,14 @@ struct RotOut {
 // head, set A; else key head hh - nA, set B), rotated in float32 and split
 // into bf16 hi/lo rows, and the hi rows transposed where the set asks for it.
 template <int HD>
-__device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const float* __restrict__ qkv, int64_t ld, int S,
-                                               int Sp, int row0, int hh, int b, int nA, int nB,
+__device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const QkvSrc& qs, const float* __restrict__ qkv,
+                                               int64_t ld, int S, int Sp, int row0, int hh, int b, int nA, int nB,
                                                const float2* __restrict__ rope, const RotOut& A, const RotOut& Bo) {
   const bool in_a = hh < nA;
   const RotOut o = in_a ? A : Bo;
   const int nheads = in_a ? nA : nB, hl = in_a ? hh : hh - nA;
   const float* src = qkv + (int64_t)b * S * ld + (int64_t)hh * HD;
-  stage_rot<HD>(sm.h, sm.l, src, ld, row0, S - row0, rope);
+  stage_rot<HD>(sm.h, sm.l, qs, src, ld, row0, S - row0, rope);
   __syncthreads();
   const int64_t hb = (int64_t)b * nheads + hl;
   put_rows<HD>(o.hi + (hb * Sp + row0) * HD, sm.h);
@@ -488,9 +526,10 @@ __device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const float*
 // The same rows of a plain operand (V from the float32 qkv, dO in bf16) at
 // column head `col`, transposed into head hh of dstT, in bf16.
 template <int HD, typename SrcT>
-__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const SrcT* __restrict__ src, int64_t ld, int S,
-                                             int Sp, int row0, int col, int hh, int b, int nheads, uint16_t* dstT) {
-  stage_rows_t<HD>(t, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);
+__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const QkvSrc& qs, const SrcT* __restrict__ src,
+                                             int64_t ld, int S, int Sp, int row0, int col, int hh, int b, int nheads,
+                                             uint16_t* dstT) {
+  stage_rows_t<HD>(t, qs, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);
   __syncthreads();
   put_cols<HD>(dstT + ((int64_t)b * nheads + hh) * HD * Sp + row0, t, Sp);
 }
@@ -542,16 +581,19 @@ __device__ __forceinline__ void dot_rows_block(const uint16_t* __restrict__ dO, 
 
 // Every operand the forward prepares, one launch: workgroups (row block x,
 // y, batch z); y < nh + nkv rotates and splits Q and K, the rest transpose V.
+// With qs.part set, every q/k/v value is summed from the product's split-K
+// partials (each by the one workgroup that reads it) and stored on the way.
 template <int HD>
-__global__ void __launch_bounds__(256) attn_prep_fwd_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
-                                                           int nh, int nkv, const float2* __restrict__ rope,
-                                                           RotOut Qo, RotOut Ko, uint16_t* vt) {
+__global__ void __launch_bounds__(256) attn_prep_fwd_kernel(QkvSrc qs, int64_t ld, int S, int Sp, int nh, int nkv,
+                                                           const float2* __restrict__ rope, RotOut Qo, RotOut Ko,
+                                                           uint16_t* vt) {
   __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
   const int row0 = blockIdx.x * AT, y = blockIdx.y, b = blockIdx.z;
+  const float* qkv = qs.base;
   if (y < nh + nkv)
-    prep_rot_block<HD>(sm, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
+    prep_rot_block<HD>(sm, qs, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
   else
-    prep_t_block<HD, float>(sm.t, qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vt);
+    prep_t_block<HD, float>(sm.t, qs, qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vt);
 }
 // Every operand the backward prepares, one launch: y < nh + nkv rotates and
 // splits Q and K (with the transposes of their bf16 values), the next nkv
@@ -566,12 +608,13 @@ __global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* __restr
   __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
   const int row0 = blockIdx.x * AT, y = blockIdx.y, b = blockIdx.z;
   if (y < nh + nkv) {
-    prep_rot_block<HD>(sm, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
+    prep_rot_block<HD>(sm, QkvSrc{const_cast<float*>(qkv), nullptr, 0, 0, ld, nullptr}, qkv, ld, S, Sp, row0, y, b,
+                       nh, nkv, rope, Qo, Ko);
   } else if (y < nh + 2 * nkv) {
     prep_rows_block<HD>(qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vr);
   } else {
     const int h = y - nh - 2 * nkv;
-    prep_t_block<HD, uint16_t>(sm.t, dO, ldo, S, Sp, row0, h, h, b, nh, ot);
+    prep_t_block<HD, uint16_t>(sm.t, QkvSrc{}, dO, ldo, S, Sp, row0, h, h, b, nh, ot);
     dot_rows_block<HD>(dO, O, ldo, S, row0, h, b, nh, D);
   }
 }
@@ -1383,11 +1426,12 @@ int attention_fwd(const AttnArgs& a, int B, hipStream_t s) {
   // Q and K rotated and split into hi/lo rows, and V^T: one launch
   const dim3 gp(pp.Sp / AT, a.nh + 2 * a.nkv, B);
   const RotOut oq{pp.qh, pp.ql, nullptr}, ok{pp.kh, pp.kl, nullptr};
+  const QkvSrc qs{const_cast<float*>(a.qkv), a.qkv_part, a.qkv_splits, (int64_t)B * a.S * a.ld, a.ld, a.qkv_bias};
   if (a.hd == 128) {
-    attn_prep_fwd_kernel<128><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
+    attn_prep_fwd_kernel<128><<<gp, 256, 0, s>>>(qs, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
     attn_fwd_bf16_kernel<128><<<grid, 256, sizeof(AttnF16Smem<128>), s>>>(a, pp);
   } else {
-    attn_prep_fwd_kernel<64><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
+    attn_prep_fwd_kernel<64><<<gp, 256, 0, s>>>(qs, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vt);
     attn_fwd_bf16_kernel<64><<<grid, 256, sizeof(AttnF16Smem<64>), s>>>(a, pp);
   }
   prof_end(tok, s, PROF_ATTN, flops, 0.0);

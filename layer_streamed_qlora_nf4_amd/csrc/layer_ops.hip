@@ -506,7 +506,7 @@ struct RotOut {
 // head, set A; else key head hh - nA, set B), rotated in float32 and split
 // into bf16 hi/lo rows, and the hi rows transposed where the set asks for it.
 template <int HD>
-__device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const QkvSrc& qs, const float* __restrict__ qkv,
+__device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const QkvSrc& qs, const float* qkv,
                                                int64_t ld, int S, int Sp, int row0, int hh, int b, int nA, int nB,
                                                const float2* __restrict__ rope, const RotOut& A, const RotOut& Bo) {
   const bool in_a = hh < nA;
@@ -526,7 +526,7 @@ __device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const QkvSrc
 // The same rows of a plain operand (V from the float32 qkv, dO in bf16) at
 // column head `col`, transposed into head hh of dstT, in bf16.
 template <int HD, typename SrcT>
-__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const QkvSrc& qs, const SrcT* __restrict__ src,
+__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const QkvSrc& qs, const SrcT* src,
                                              int64_t ld, int S, int Sp, int row0, int col, int hh, int b, int nheads,
                                              uint16_t* dstT) {
   stage_rows_t<HD>(t, qs, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);

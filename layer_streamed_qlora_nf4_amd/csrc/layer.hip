@@ -544,10 +544,13 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   // ---- o projection
   one.end[0] = d.H;
   TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[1], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
+  // d_attn; a split-K launch leaves its partials to the attention backward's
+  // operand preparation, which sums and stores them on the way
+  int sp_o = 1;
   {
     BwdParams p = bwd_params(w.dy_b, T, bv.w[1], w.G, r, lv.A[1], lv.AT[1], r);
     p.out = w.dattn;
-    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
+    TRY(gemm_bwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes, &sp_o));
   }
   {
     const int se[1] = {d.H};
@@ -557,6 +560,10 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   {
     AttnBwdArgs a{w.qkv, d.Nqkv, S, d.nh, d.nkv, d.hd, 1.0f / sqrtf((float)d.hd), w.attn, w.attn_f32, w.dattn, d.Nq,
                   w.lse, nullptr, w.dqkv, reinterpret_cast<const float2*>(w.rope), w.dk_part, w.dv_part, w.aprep};
+    if (sp_o > 1) {
+      a.dO_part = static_cast<const float*>(w.gemm);
+      a.dO_splits = sp_o;
+    }
     TRY(attention_bwd(a, B, w.D, s));
   }
   // ---- q, k, v projections

@@ -43,6 +43,12 @@ struct AttnBwdArgs {
   float* dk_part;       // [B, nh, S, hd] per-query-head partials (workspace)
   float* dv_part;
   uint16_t* prep;       // attention_prep_bytes(.., true) of workspace
+  // Optional: dO not yet reduced.  With dO_part set, the preparation sums the
+  // split-K partials [dO_splits][B*S][ldo] of the product that makes dO in
+  // split order, rounds them to bf16 and stores them into dO, as the plain
+  // reduction would, before anything reads dO.
+  const float* dO_part = nullptr;
+  int dO_splits = 0;
 };
 
 // Workspace of the operands each attention call prepares once (rotated and

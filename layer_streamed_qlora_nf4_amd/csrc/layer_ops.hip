@@ -296,6 +296,27 @@ __device__ __forceinline__ uint4 load8_bf16(const QkvSrc& q, const float* p, boo
                     pack_bf16x2(x[6], x[7]));
 }
 __device__ __forceinline__ uint4 load8_bf16(const QkvSrc&, const uint16_t* p, bool ok) { return load8_bf16(p, ok); }
+// The same for a bf16 operand (the attention output's gradient): the array, or
+// (part set) the split-K partials of the product that makes it, summed in
+// split order, rounded to bf16 and stored into the array on the way, as the
+// plain reduction would store them.
+struct Bf16Src {
+  uint16_t* base;         // the bf16 array [rows][ld]
+  const float* part;      // [splits][rows][ld], or null
+  int splits;
+  int64_t total;          // rows * ld
+};
+__device__ __forceinline__ uint4 load8_bf16(const Bf16Src& q, const uint16_t* p, bool ok) {
+  if (!q.part || !ok) return load8_bf16(p, ok);
+  const int64_t e = p - q.base;
+  const float4 a = split_sum4(q.part, q.splits, q.total, e), b = split_sum4(q.part, q.splits, q.total, e + 4);
+  auto bits2 = [](float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  };
+  const uint4 v = make_uint4(bits2(a.x, a.y), bits2(a.z, a.w), bits2(b.x, b.y), bits2(b.z, b.w));
+  *reinterpret_cast<uint4*>(q.base + e) = v;
+  return v;
+}
 // Rotate-half RoPE of 8 consecutive pair indices i .. i+7 at position pos:
 // (x1, x2) -> (x1 c - x2 s, x2 c + x1 s), table[pos][i] = (c, s).
 __device__ __forceinline__ void rope8(float (&x1)[8], float (&x2)[8], const float2* __restrict__ tab) {
@@ -372,8 +393,8 @@ __device__ __forceinline__ void lds_transpose(uint16_t (*dst)[AT + PAD], const u
   }
 }
 // Rows [row0, row0 + 64) of a bf16 matrix straight into [HD][64] (zero past n).
-template <int HD, typename SrcT>
-__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const QkvSrc& qs, const SrcT* src, int64_t ld,
+template <int HD, typename SrcT, typename Q>
+__device__ __forceinline__ void stage_rows_t(uint16_t (*dst)[AT + PAD], const Q& qs, const SrcT* src, int64_t ld,
                                              int row0, int n) {
   constexpr int NMT = AT / 4 * (HD / 8);
   for (int t = threadIdx.x; t < NMT; t += 256) {
@@ -525,8 +546,8 @@ __device__ __forceinline__ void prep_rot_block(PrepRotSmem<HD>& sm, const QkvSrc
 }
 // The same rows of a plain operand (V from the float32 qkv, dO in bf16) at
 // column head `col`, transposed into head hh of dstT, in bf16.
-template <int HD, typename SrcT>
-__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const QkvSrc& qs, const SrcT* src,
+template <int HD, typename SrcT, typename Q>
+__device__ __forceinline__ void prep_t_block(uint16_t (*t)[AT + PAD], const Q& qs, const SrcT* src,
                                              int64_t ld, int S, int Sp, int row0, int col, int hh, int b, int nheads,
                                              uint16_t* dstT) {
   stage_rows_t<HD>(t, qs, src + (int64_t)b * S * ld + (int64_t)col * HD, ld, row0, S - row0);
@@ -593,7 +614,7 @@ __global__ void __launch_bounds__(256) attn_prep_fwd_kernel(QkvSrc qs, int64_t l
   if (y < nh + nkv)
     prep_rot_block<HD>(sm, qs, qkv, ld, S, Sp, row0, y, b, nh, nkv, rope, Qo, Ko);
   else
-    prep_t_block<HD, float>(sm.t, qs, qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vt);
+    prep_t_block<HD, float, QkvSrc>(sm.t, qs, qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vt);
 }
 // Every operand the backward prepares, one launch: y < nh + nkv rotates and
 // splits Q and K (with the transposes of their bf16 values), the next nkv
@@ -601,10 +622,10 @@ __global__ void __launch_bounds__(256) attn_prep_fwd_kernel(QkvSrc qs, int64_t l
 template <int HD>
 __global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* __restrict__ qkv, int64_t ld, int S, int Sp,
                                                            int nh, int nkv, const float2* __restrict__ rope,
-                                                           RotOut Qo, RotOut Ko, uint16_t* vr,
-                                                           const uint16_t* __restrict__ dO,
+                                                           RotOut Qo, RotOut Ko, uint16_t* vr, Bf16Src dos,
                                                            const float* __restrict__ O, int64_t ldo, uint16_t* ot,
                                                            float* __restrict__ D) {
+  const uint16_t* dO = dos.base;
   __shared__ __attribute__((aligned(16))) PrepRotSmem<HD> sm;
   const int row0 = blockIdx.x * AT, y = blockIdx.y, b = blockIdx.z;
   if (y < nh + nkv) {
@@ -614,7 +635,9 @@ __global__ void __launch_bounds__(256) attn_prep_bwd_kernel(const float* __restr
     prep_rows_block<HD>(qkv, ld, S, Sp, row0, y, y - nh - nkv, b, nkv, vr);
   } else {
     const int h = y - nh - 2 * nkv;
-    prep_t_block<HD, uint16_t>(sm.t, QkvSrc{}, dO, ldo, S, Sp, row0, h, h, b, nh, ot);
+    // dO summed from its product's partials is stored before the barrier
+    // inside prep_t_block, so the dot below reads the stored values
+    prep_t_block<HD, uint16_t, Bf16Src>(sm.t, dos, dO, ldo, S, Sp, row0, h, h, b, nh, ot);
     dot_rows_block<HD>(dO, O, ldo, S, row0, h, b, nh, D);
   }
 }
@@ -1460,13 +1483,14 @@ int attention_bwd(const AttnBwdArgs& a, int B, float* D, hipStream_t s) {
   // Q and K rotated, split and transposed, V rows, dO^T and D: one launch
   const dim3 gp(pp.Sp / AT, 2 * a.nh + 2 * a.nkv, B);
   const RotOut oq{pp.qh, pp.ql, pp.qht}, ok{pp.kh, pp.kl, pp.kht};
+  const Bf16Src dos{const_cast<uint16_t*>(a.dO), a.dO_part, a.dO_splits, (int64_t)B * a.S * a.ldo};
   if (a.hd == 128) {
-    attn_prep_bwd_kernel<128><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, a.dO,
+    attn_prep_bwd_kernel<128><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, dos,
                                                  a.O_f32, a.ldo, pp.ot, D);
     attn_bwd_dkdv_bf16_kernel<128><<<g1, 256, sizeof(AttnDkdvSmem<128>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<128><<<g2, 256, sizeof(AttnDqSmem<128>), s>>>(b, pp);
   } else {
-    attn_prep_bwd_kernel<64><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, a.dO,
+    attn_prep_bwd_kernel<64><<<gp, 256, 0, s>>>(a.qkv, a.ld, a.S, pp.Sp, a.nh, a.nkv, a.rope, oq, ok, pp.vr, dos,
                                                 a.O_f32, a.ldo, pp.ot, D);
     attn_bwd_dkdv_bf16_kernel<64><<<g1, 256, sizeof(AttnDkdvSmem<64>), s>>>(b, pp);
     attn_bwd_dq_bf16_kernel<64><<<g2, 256, sizeof(AttnDqSmem<64>), s>>>(b, pp);

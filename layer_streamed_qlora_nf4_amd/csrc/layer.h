@@ -36,8 +36,13 @@ int layer_prepare(const lsq_model_cfg* c, int B, int S, void* ws, hipStream_t s)
 // (adapter_transpose); null transposes them into the workspace first.
 int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, int B, int S,
               float* x_out, void* ws, hipStream_t s, void* acts);
+// Every layer_bwd leaves bf16(dx_in) in the workspace's bf16 gradient buffer
+// (layer_bwd_dy_b: the same address in every backward carve of one
+// workspace), which is the bf16 copy of dx_out the layer below starts from:
+// with dy_b_ready, layer_bwd takes it as bf16(dx_out) instead of converting.
 int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const void* lora_t, const float* x_in,
               const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
-              const LayerHook* hook, void* acts);
+              const LayerHook* hook, void* acts, bool dy_b_ready = false);
+uint16_t* layer_bwd_dy_b(const lsq_model_cfg* c, int B, int S, void* ws);
 
 }  // namespace lsq

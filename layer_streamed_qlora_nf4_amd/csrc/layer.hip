@@ -231,6 +231,9 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
   w.rope = static_cast<float*>(take(8ull * S * (d.hd / 2)));
   w.ncnt = counters_need(d, (int)T);
   w.cnt = static_cast<int*>(take(counters_bytes(w.ncnt)));
+  // the backward's bf16 upstream gradient next, so that it too has one
+  // address in every backward carve and one layer can hand it to the next
+  if (bwd) w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
   w.xn1 = static_cast<uint16_t*>(take_act(2 * T * 2 * d.H));
   w.U_qkv = static_cast<uint16_t*>(take_act(2 * T * 3 * d.r));
   w.qkv = static_cast<float*>(take_act(4 * T * d.Nqkv));
@@ -256,7 +259,6 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
   w.aprep = static_cast<uint16_t*>(take(attention_prep_bytes(B, S, d.nh, d.nkv, d.hd, bwd)));
   if (bwd) {
     w.G32 = static_cast<float*>(take(4 * T * 3 * d.r));
-    w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
     w.G = static_cast<uint16_t*>(take(2 * T * 3 * d.r));
     w.dm = static_cast<uint16_t*>(take(2 * T * d.I));
     w.dgu = static_cast<uint16_t*>(take(2 * T * 2 * d.I));
@@ -485,7 +487,7 @@ static int adapter_grads(const Dims& d, int T, const float* G, int ldg, const fl
 
 static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraView& lv, const float* x_in,
                          const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate,
-                         const LayerWs& w, hipStream_t s) {
+                         const LayerWs& w, hipStream_t s, bool dy_b_ready) {
   const Dims d = dims_of(c);
   const int T = B * S, r = d.r;
   const float sc = c->lora_scale;
@@ -499,7 +501,7 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   }
   SegEnds one{};
   // ---- down projection: out = h + down(m)
-  TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
+  if (!dy_b_ready) TRY(to_bf16(dx_out, (int64_t)T * d.H, w.dy_b, s));
   one.end[0] = d.H;
   TRY(lora_g(w.dy_b, d.H, T, d.H, lv.BT[3], r, 1, one, sc, w.G, r, w.G32, r, w.lws, w.lws_bytes, w.cnt, s));
   // dm, and through SwiGLU dgu; a split-K launch leaves dm's partials to the
@@ -573,7 +575,8 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
   three.end[2] = d.Nqkv;
   TRY(lora_g(w.dqkv, d.Nqkv, T, d.Nqkv, lv.BT[0], r, 3, three, sc, w.G, 3 * r, w.G32, 3 * r, w.lws,
              w.lws_bytes, w.cnt, s));
-  // dxn1, then dx = dh + rmsnorm1'(dxn1) (from the partials of a split-K launch)
+  // dxn1, then dx = dh + rmsnorm1'(dxn1) (from the partials of a split-K
+  // launch), with its bf16 copy in dy_b for the layer below (layer_bwd_dy_b)
   {
     BwdParams p = bwd_params(w.dqkv, T, bv.w[0], w.G, 3 * r, lv.A[0], lv.AT[0], 3 * r);
     p.out = w.dxn;
@@ -581,9 +584,9 @@ static int backward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraV
     TRY(gemm_bwd(p, EPI_F32, s, w.gemm, w.gemm_bytes, &sp));
     if (sp > 1)
       TRY(splitk_rmsnorm_bwd(x_in, bv.norm1, static_cast<const float*>(w.gemm), sp, w.dh, T, d.H, c->rms_eps, dx_in,
-                             nullptr, s));
+                             w.dy_b, s));
     else
-      TRY(rmsnorm_bwd(x_in, bv.norm1, w.dxn, w.dh, T, d.H, c->rms_eps, dx_in, nullptr, s));
+      TRY(rmsnorm_bwd(x_in, bv.norm1, w.dxn, w.dh, T, d.H, c->rms_eps, dx_in, w.dy_b, s));
   }
   {
     const int se[3] = {d.Nq, d.Nq + d.Nkv, d.Nqkv};
@@ -608,9 +611,11 @@ int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const 
   return forward_impl(c, view_blob(c, blob), view_lora(c, lora), x_in, B, S, x_out, w, s);
 }
 
+uint16_t* layer_bwd_dy_b(const lsq_model_cfg* c, int B, int S, void* ws) { return carve(c, B, S, ws, true).dy_b; }
+
 int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const void* lora_t, const float* x_in,
               const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
-              const LayerHook* hook, void* acts) {
+              const LayerHook* hook, void* acts, bool dy_b_ready) {
   LayerWs w = carve(c, B, S, ws, true, acts);
   if (!lora_t) {
     TRY(adapter_transpose(c, static_cast<const uint16_t*>(lora), w.lora_t, 1, s));
@@ -620,7 +625,7 @@ int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const 
   const LoraView lv = view_lora(c, lora, lora_t);
   if (!acts) TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
   if (hook && hook->after_recompute) TRY(hook->after_recompute(hook->ctx));
-  return backward_impl(c, bv, lv, x_in, dx_out, B, S, dx_in, grad, accumulate, w, s);
+  return backward_impl(c, bv, lv, x_in, dx_out, B, S, dx_in, grad, accumulate, w, s, dy_b_ready);
 }
 
 }  // namespace lsq

@@ -947,8 +947,9 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   if (fwd_only) return tl_end(pool, tl_head, s);
   float* dcur = w.dxa;
   float* dnext = w.dxb;
+  // dh of the last layer, and its bf16 copy where that layer's backward looks for it
   if (int e = rmsnorm_bwd(x_at(L), static_cast<const uint16_t*>(res->final_norm), w.dxf, nullptr, T, H, cfg->rms_eps,
-                          dcur, nullptr, s))
+                          dcur, layer_bwd_dy_b(cfg, B, S, w.layer), s))
     return e;
   if (int e = tl_end(pool, tl_head, s)) return e;
   const size_t act = sizeof(float) * (size_t)T * H;
@@ -970,7 +971,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     const int tl = tl_begin(pool, LSQ_TL_BWD, i, s);
     if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, w.lora_t + (uint64_t)i * LL.layer_elems,
                           x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
-                          s, early ? &hook : nullptr, acts_at(i)))
+                          s, early ? &hook : nullptr, acts_at(i), /*dy_b_ready=*/true))
       return e;
     if (int e = tl_end(pool, tl, s)) return e;
     if (!early)

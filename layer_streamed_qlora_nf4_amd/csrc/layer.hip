@@ -205,8 +205,12 @@ static size_t lws_need(const Dims& d, int T) {
 // the float32 attention output) come from `acts` when the caller keeps them
 // per layer (no recompute), else from the workspace itself.  keep: a region
 // size query for that split (base and acts may both be null).
+// ustore (nullable): the layer's rank-r inputs U (bf16) and U32 (float32),
+// kept from its forward for the backward's recompute, which then skips the
+// down projections (layer_ustore_bytes).
 static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd, void* acts = nullptr,
-                     bool keep = false, uint64_t* acts_total = nullptr) {
+                     bool keep = false, uint64_t* acts_total = nullptr, void* ustore = nullptr,
+                     uint64_t* ustore_total = nullptr) {
   const Dims d = dims_of(c);
   const uint64_t T = (uint64_t)B * S;
   keep = keep || acts != nullptr;
@@ -225,6 +229,14 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
     aoff = up(aoff + std::max<uint64_t>(bytes, 1), 256);
     return r;
   };
+  char* pu = static_cast<char*>(ustore);
+  uint64_t uoff = 0;
+  auto take_u = [&](uint64_t bytes) -> void* {
+    if (!ustore) return take_act(bytes);
+    void* r = pu + uoff;
+    uoff = up(uoff + std::max<uint64_t>(bytes, 1), 256);
+    return r;
+  };
   // rope and the counters first: the same addresses in every carve of one
   // workspace (forward or backward, kept activations or not), so one
   // layer_prepare serves every pass
@@ -235,23 +247,24 @@ static LayerWs carve(const lsq_model_cfg* c, int B, int S, void* base, bool bwd,
   // address in every backward carve and one layer can hand it to the next
   if (bwd) w.dy_b = static_cast<uint16_t*>(take(2 * T * d.H));
   w.xn1 = static_cast<uint16_t*>(take_act(2 * T * 2 * d.H));
-  w.U_qkv = static_cast<uint16_t*>(take_act(2 * T * 3 * d.r));
+  w.U_qkv = static_cast<uint16_t*>(take_u(2 * T * 3 * d.r));
   w.qkv = static_cast<float*>(take_act(4 * T * d.Nqkv));
   w.attn = static_cast<uint16_t*>(take_act(2 * T * d.Nq));
   w.lse = static_cast<float*>(take_act(4ull * B * d.nh * S));
-  w.U_o = static_cast<uint16_t*>(take_act(2 * T * d.r));
+  w.U_o = static_cast<uint16_t*>(take_u(2 * T * d.r));
   w.h = static_cast<float*>(take_act(4 * T * d.H));
   w.xn2 = static_cast<uint16_t*>(take_act(2 * T * d.H));
-  w.U_gu = static_cast<uint16_t*>(take_act(2 * T * 2 * d.r));
+  w.U_gu = static_cast<uint16_t*>(take_u(2 * T * 2 * d.r));
   w.gu = static_cast<uint16_t*>(take_act(2 * T * 2 * d.I));
   w.m = static_cast<uint16_t*>(take_act(2 * T * d.I));
-  w.U_d = static_cast<uint16_t*>(take_act(2 * T * d.r));
-  if (bwd || keep) {
+  w.U_d = static_cast<uint16_t*>(take_u(2 * T * d.r));
+  if (bwd || keep || ustore) {
     const int ur[4] = {3, 1, 2, 1};
-    for (int g = 0; g < 4; ++g) w.U32[g] = static_cast<float*>(take_act(4 * T * ur[g] * d.r));
-    w.attn_f32 = static_cast<float*>(take_act(4 * T * d.Nq));
+    for (int g = 0; g < 4; ++g) w.U32[g] = static_cast<float*>(take_u(4 * T * ur[g] * d.r));
   }
+  if (bwd || keep) w.attn_f32 = static_cast<float*>(take_act(4 * T * d.Nq));
   if (acts_total) *acts_total = aoff;
+  if (ustore_total) *ustore_total = uoff;
   w.gemm_bytes = gemm_need(d, (int)T);
   w.gemm = take(w.gemm_bytes);
   w.lws_bytes = lws_need(d, (int)T);
@@ -286,6 +299,12 @@ size_t layer_acts_bytes(const lsq_model_cfg* c, int B, int S) {
   uint64_t a = 0;
   carve(c, B, S, nullptr, true, nullptr, true, &a);
   return a;
+}
+size_t layer_ustore_bytes(const lsq_model_cfg* c, int B, int S) {
+  uint64_t u = 0;
+  char probe;   // any non-null address: only the offsets are used
+  carve(c, B, S, nullptr, true, nullptr, false, nullptr, &probe, &u);
+  return u;
 }
 
 struct BlobView {
@@ -385,8 +404,11 @@ static BwdParams bwd_params(const uint16_t* dY, int T, const WeightRef& w, const
 
 // Forward through the layer.  x_out == nullptr stops after the MLP activation
 // and its down-projection input U_d (the part of the forward the backward reads).
+// u_ready: U and U32 already hold this layer's down projections (kept from
+// its forward in the layer's rank-r store), so the recompute skips them; the
+// kernels are deterministic, so the values are the ones it would recompute.
 static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraView& lv, const float* x_in, int B,
-                        int S, float* x_out, const LayerWs& w, hipStream_t s) {
+                        int S, float* x_out, const LayerWs& w, hipStream_t s, bool u_ready = false) {
   const Dims d = dims_of(c);
   const int T = B * S, r = d.r;
   const float sc = c->lora_scale;
@@ -395,8 +417,9 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
   // bf16 hi/lo pair (two passes over one weight) and keeps its output in
   // float32.  The adapters' down-projection and gradient read the hi half.
   TRY(rmsnorm_fwd(x_in, bv.norm1, T, d.H, c->rms_eps, w.xn1, 2 * d.H, nullptr, s, w.xn1 + d.H));
-  TRY(lora_down(w.xn1, 2 * d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.U32[0], 3 * r, w.lws, w.lws_bytes,
-                w.cnt, s));
+  if (!u_ready)
+    TRY(lora_down(w.xn1, 2 * d.H, T, d.H, lv.A[0], 3 * r, sc, w.U_qkv, 3 * r, w.U32[0], 3 * r, w.lws, w.lws_bytes,
+                  w.cnt, s));
   {
     FwdParams p = fwd_params(w.xn1, T, bv.w[0], w.U_qkv, 3 * r, lv.B[0], r);
     p.ldx = 2 * d.H;
@@ -424,7 +447,8 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     }
     TRY(attention_fwd(a, B, s));
   }
-  TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, w.cnt, s));
+  if (!u_ready)
+    TRY(lora_down(w.attn, d.Nq, T, d.Nq, lv.A[1], r, sc, w.U_o, r, w.U32[1], r, w.lws, w.lws_bytes, w.cnt, s));
   // h = x + o(attn) and the MLP's RMSNorm; a split-K o projection leaves its
   // partials to the norm kernel, which sums them (and writes h) on the way in
   {
@@ -440,7 +464,9 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
       TRY(rmsnorm_fwd(w.h, bv.norm2, T, d.H, c->rms_eps, w.xn2, d.H, nullptr, s));
   }
   // MLP block
-  TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, w.cnt, s));
+  if (!u_ready)
+    TRY(lora_down(w.xn2, d.H, T, d.H, lv.A[2], 2 * r, sc, w.U_gu, 2 * r, w.U32[2], 2 * r, w.lws, w.lws_bytes, w.cnt,
+                  s));
   {
     FwdParams p = fwd_params(w.xn2, T, bv.w[2], w.U_gu, 2 * r, lv.B[2], r);
     p.nseg = 2;
@@ -452,7 +478,8 @@ static int forward_impl(const lsq_model_cfg* c, const BlobView& bv, const LoraVi
     TRY(gemm_fwd(p, EPI_BF16, s, w.gemm, w.gemm_bytes));
   }
   TRY(swiglu_fwd(w.gu, T, d.I, w.m, s));
-  TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.U32[3], r, w.lws, w.lws_bytes, w.cnt, s));
+  if (!u_ready)
+    TRY(lora_down(w.m, d.I, T, d.I, lv.A[3], r, sc, w.U_d, r, w.U32[3], r, w.lws, w.lws_bytes, w.cnt, s));
   if (x_out) {
     FwdParams p = fwd_params(w.m, T, bv.w[3], w.U_d, r, lv.B[3], r);
     p.resid = w.h;
@@ -606,8 +633,8 @@ int layer_prepare(const lsq_model_cfg* c, int B, int S, void* ws, hipStream_t s)
 }
 
 int layer_fwd(const lsq_model_cfg* c, const void* blob, const void* lora, const float* x_in, int B, int S,
-              float* x_out, void* ws, hipStream_t s, void* acts) {
-  LayerWs w = carve(c, B, S, ws, false, acts);
+              float* x_out, void* ws, hipStream_t s, void* acts, void* ustore) {
+  LayerWs w = carve(c, B, S, ws, false, acts, false, nullptr, ustore);
   return forward_impl(c, view_blob(c, blob), view_lora(c, lora), x_in, B, S, x_out, w, s);
 }
 
@@ -615,15 +642,15 @@ uint16_t* layer_bwd_dy_b(const lsq_model_cfg* c, int B, int S, void* ws) { retur
 
 int layer_bwd(const lsq_model_cfg* c, const void* blob, const void* lora, const void* lora_t, const float* x_in,
               const float* dx_out, int B, int S, float* dx_in, float* grad, int accumulate, void* ws, hipStream_t s,
-              const LayerHook* hook, void* acts, bool dy_b_ready) {
-  LayerWs w = carve(c, B, S, ws, true, acts);
+              const LayerHook* hook, void* acts, bool dy_b_ready, void* ustore) {
+  LayerWs w = carve(c, B, S, ws, true, acts, false, nullptr, ustore);
   if (!lora_t) {
     TRY(adapter_transpose(c, static_cast<const uint16_t*>(lora), w.lora_t, 1, s));
     lora_t = w.lora_t;
   }
   const BlobView bv = view_blob(c, blob);
   const LoraView lv = view_lora(c, lora, lora_t);
-  if (!acts) TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s));
+  if (!acts) TRY(forward_impl(c, bv, lv, x_in, B, S, nullptr, w, s, ustore != nullptr));
   if (hook && hook->after_recompute) TRY(hook->after_recompute(hook->ctx));
   return backward_impl(c, bv, lv, x_in, dx_out, B, S, dx_in, grad, accumulate, w, s, dy_b_ready);
 }

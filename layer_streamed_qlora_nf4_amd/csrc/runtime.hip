@@ -663,6 +663,8 @@ struct StepWs {
   char* acts;        // n_kept x acts_bytes of kept forward activations
   size_t acts_bytes;
   int n_kept;
+  char* ustore;      // n_layers x ustore_bytes: each layer's rank-r store (U, U32) for its recompute
+  size_t ustore_bytes;
   uint16_t* lora_t;  // every layer's adapters transposed block by block, once per step
   float* xr[2];      // reference mode: the adapters-off residual stream, ping-pong [T, H]
   float* ref_loss_tmp;  // reference mode: its mean loss when the caller wants rows only
@@ -729,6 +731,10 @@ StepWs carve_step(const lsq_model_cfg* c, int B, int S, void* base, int32_t flag
     w.acts = static_cast<char*>(take(w.acts_bytes * (uint64_t)n_kept));
   }
   w.n_kept = n_kept;
+  if (!(flags & LSQ_STEP_FORWARD_ONLY)) {
+    w.ustore_bytes = layer_ustore_bytes(c, B, S);
+    w.ustore = static_cast<char*>(take(w.ustore_bytes * (uint64_t)c->n_layers));
+  }
   if (flags & LSQ_STEP_REFERENCE_FORWARD) {
     w.xr[0] = static_cast<float*>(take(4 * T * H));
     w.xr[1] = static_cast<float*>(take(4 * T * H));
@@ -872,6 +878,10 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
   auto acts_at = [&](int i) -> void* {
     return (w.acts && kslot[i] >= 0) ? w.acts + (uint64_t)kslot[i] * w.acts_bytes : nullptr;
   };
+  // a recomputed layer keeps its down projections from the forward for the recompute
+  auto ustore_at = [&](int i) -> void* {
+    return (w.ustore && kslot[i] < 0) ? w.ustore + (uint64_t)i * w.ustore_bytes : nullptr;
+  };
   lsq_lora_layout LL;
   lora_layout(cfg, &LL);
   const uint16_t* lora = static_cast<const uint16_t*>(res->lora);
@@ -911,7 +921,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
       if (int e = queue_head_copy()) return e;
     const int tl = tl_begin(pool, LSQ_TL_FWD, i, s);
     if (int e = layer_fwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, x_at(i), B, S, x_at(i + 1), w.layer, s,
-                          acts_at(i)))
+                          acts_at(i), ustore_at(i)))
       return e;
     if (ref) {
       // the reference model on the same bytes while they are in the slot: adapters off (scale 0)
@@ -971,7 +981,7 @@ int lsq_train_step_ex(const lsq_model_cfg* cfg, lsq_pool* pool, const lsq_reside
     const int tl = tl_begin(pool, LSQ_TL_BWD, i, s);
     if (int e = layer_bwd(cfg, blob, lora + (uint64_t)i * LL.layer_elems, w.lora_t + (uint64_t)i * LL.layer_elems,
                           x_at(i), dcur, B, S, dnext, grad, 0, w.layer,
-                          s, early ? &hook : nullptr, acts_at(i), /*dy_b_ready=*/true))
+                          s, early ? &hook : nullptr, acts_at(i), /*dy_b_ready=*/true, ustore_at(i)))
       return e;
     if (int e = tl_end(pool, tl, s)) return e;
     if (!early)

@@ -63,15 +63,16 @@ struct BwdParams {
   int64_t ldc;
   float* part;           // split-K partials [splits, M, K] (workspace); set by gemm_bwd
   int splits;
+  int bo;                // tile width in output columns; set by gemm_bwd
 };
 
 // Split-K: a launch with fewer tiles than the chip has CUs splits its
 // reduction into a fixed number of ranges (a pure function of the shape),
 // writes float32 partials and sums them in split order in a second kernel.
-// Forward plan: tile width (256, or 192 for the NF4 DMA kernels when 256-wide
-// tiles would leave a quarter of the CUs idle) and split count.  narrow: the
-// launch can take the narrower tile (NF4 weights, operands within 32-bit
-// offsets).  The split count does not depend on narrow.
+// Forward plan: tile width (256, or 224 or 192 for the NF4 DMA kernels when
+// 256-wide tiles would leave part of a round of workgroups idle) and split
+// count.  narrow: the launch can take a narrower tile (NF4 weights, operands
+// within 32-bit offsets).  The split count does not depend on narrow.
 struct GemmPlan {
   int bn, splits;
 };

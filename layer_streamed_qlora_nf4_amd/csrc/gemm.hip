@@ -392,10 +392,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // statically (the compiler can then tell DMA writes to one stage from reads of
 // the other and does not drain the DMA queue before each fragment read).
 //
-// BN is the tile's width in output columns (256, or 192 where 256-wide tiles
-// would leave a quarter of the CUs idle: N = 6144 at 2048 rows gives 192
-// tiles of 256 but 256 of 192).  Each group decodes BN / 2 weight rows; the
-// spare threads of the narrower tile load a duplicate row and skip the store.
+// BN is the tile's width in output columns (256, or 224 or 192 where 256-wide
+// tiles would leave part of a round of 256 workgroups idle, e.g. N = 6144 at
+// 2048 rows gives 192 tiles of 256 but 256 of 192).  Each group decodes BN / 2
+// weight rows; the spare threads of a narrower tile load a duplicate row and
+// skip the store.
 template <int EPI, int BN>
 __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   static_assert(BN % 32 == 0 && BN <= 256, "two 16-column-aligned wave columns per tile");
@@ -911,11 +912,19 @@ __global__ void __launch_bounds__(512, 1) gemm_bwd_pp_kernel(BwdParams p) {
 // are decoded and written transposed, and the LoRA term G A joins in the
 // epilogue.  Weight rows past N read as zeros, which also cancels the dY
 // columns past N that the DMA brings in on the last reduction step.
-template <int WK, int EPI>
+//
+// BO is the tile's width in output columns: 256, or 224 where 256-wide tiles
+// would leave part of a round of workgroups idle (K = 14336 at 2048 rows: 448
+// tiles of 256, two rounds of 256 workgroups with a quarter idle, but 512 of
+// 224).  The producer threads keep the 256-wide micro-tile map; those whose
+// micro-tile column falls past a narrower tile load a duplicate and skip the
+// store.
+template <int WK, int EPI, int BO>
 __device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
   constexpr bool NF4 = WK == LSQ_W_NF4;
-  constexpr int BM = 256, BO = 256, WM = 64, WO = 128, TM = WM / 16, TO = WO / 16, GT = 256;
-  static_assert((64 / 4) * (BO / 8) == 2 * GT, "one micro-tile per producer thread");
+  constexpr int BM = 256, WM = 64, WO = BO / 2, TM = WM / 16, TO = WO / 16, GT = 256;
+  static_assert(BO % 32 == 0 && BO <= 256, "two 16-column-aligned wave columns per tile");
+  static_assert((64 / 4) * (256 / 8) == 2 * GT, "one micro-tile per producer thread at the full width");
   __shared__ __attribute__((aligned(16))) uint16_t As0[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t As1[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Bt0[BO * 64];
@@ -947,7 +956,9 @@ __device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
   const uint32_t y_voff = (uint32_t)(((yrow0 + (lane >> 3)) * p.ldy + (((lane & 7) ^ (lane >> 3)) * 8)) * 2);
   const uint32_t y_blk = (uint32_t)(8 * p.ldy * 2);
   int mrg, mq;
-  bwd_mt_coords<BO>(grp * GT + gtid, mrg, mq);
+  bwd_mt_coords<256>(grp * GT + gtid, mrg, mq);
+  const bool mact = BO == 256 || mq < BO / 8;
+  if (!mact) mq = BO / 8 - 1;
   const int kcol = o0 + mq * 8;
   const uint32_t w_voff = NF4 ? (uint32_t)(mrg * 4 * (K / 2) + kcol / 2) : (uint32_t)((mrg * 4 * K + kcol) * 2);
   const uint32_t s_voff = (uint32_t)((mrg * 4 * (K / 64) + kcol / 64) * 4);
@@ -981,7 +992,7 @@ __device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
   auto store_b = [&](uint16_t* bt, int set) __attribute__((always_inline)) {
     int q = mq;
     asm volatile("" : "+v"(q));
-    bwd_store_mt<NF4, RB>(bt, mrg, q, rb[set], lut);
+    if (mact) bwd_store_mt<NF4, RB>(bt, mrg, q, rb[set], lut);
   };
 
   f32x4 acc[TM][TO];
@@ -1073,15 +1084,15 @@ __device__ __forceinline__ void gemm_bwd_dma_body(const BwdParams& p) {
   bwd_store<TM, TO, EPI>(p, acc, m0 + wm * WM, o0 + wo * WO, lane, split);
 }
 
-template <int EPI>
+template <int EPI, int BO>
 __global__ void __launch_bounds__(512, 1) gemm_bwd_nf4_dma_kernel(BwdParams p) {
-  gemm_bwd_dma_body<LSQ_W_NF4, EPI>(p);
+  gemm_bwd_dma_body<LSQ_W_NF4, EPI, BO>(p);
 }
 // The same schedule over bf16 weights: each producer thread copies (instead
 // of decoding) its 4 x 8 micro-tile and writes it transposed.
 template <int EPI>
 __global__ void __launch_bounds__(512, 1) gemm_bwd_bf16_dma_kernel(BwdParams p) {
-  gemm_bwd_dma_body<LSQ_W_BF16, EPI>(p);
+  gemm_bwd_dma_body<LSQ_W_BF16, EPI, 256>(p);
 }
 
 __global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, int64_t n, float* __restrict__ dst) {
@@ -1218,16 +1229,20 @@ void launch_fwd(const FwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
     hipExtLaunchKernelGGL(gemm_fwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
   else if (p.bn == 192)
     hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 192>, grid, block, 0, s, e0, e1, 0, p);
+  else if (p.bn == 224)
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 224>, grid, block, 0, s, e0, e1, 0, p);
   else
     hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 256>, grid, block, 0, s, e0, e1, 0, p);
 }
 
 template <int WK, int EPI>
 void launch_bwd(const BwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.K + kTile - 1) / kTile);
+  const int tiles = ((p.M + kTile - 1) / kTile) * ((p.K + p.bo - 1) / p.bo);
   const dim3 grid(tiles, p.splits), block(512);
-  if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
-    hipExtLaunchKernelGGL(gemm_bwd_nf4_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
+  if (WK == LSQ_W_NF4 && bwd_dma_ok(p) && p.bo == 224)
+    hipExtLaunchKernelGGL(gemm_bwd_nf4_dma_kernel<EPI, 224>, grid, block, 0, s, e0, e1, 0, p);
+  else if (WK == LSQ_W_NF4 && bwd_dma_ok(p))
+    hipExtLaunchKernelGGL(gemm_bwd_nf4_dma_kernel<EPI, 256>, grid, block, 0, s, e0, e1, 0, p);
   else if (WK == LSQ_W_BF16 && bwd_dma_ok(p))
     hipExtLaunchKernelGGL(gemm_bwd_bf16_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
   else
@@ -1288,17 +1303,41 @@ void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s, hipEvent_t e0,
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+// Tile width along the output columns (n_cols of them) for tm row tiles and
+// sp splits: 256, or down to `narrowest` (224, 192) when a narrower tile
+// fills the rounds of 256 workgroups better.  Modelled time = rounds x the
+// tile's work per k-step, of which the activation DMA (about 15%) does not
+// shrink with the width; a narrower tile must win by 5% (on gfx950 the clock
+// rises a little when CUs idle in a partly filled round).  Every output
+// element sums the same products in the same order whatever the width, so
+// the choice never changes a result.
+static int tile_width(int tm, int n_cols, int sp, int narrowest) {
+  auto cost = [&](int w) {
+    const int wgs = tm * ((n_cols + w - 1) / w) * sp;
+    return (double)((wgs + 255) / 256) * (0.15 + 0.85 * w / 256.0);
+  };
+  int best = kTile;
+  double best_c = cost(kTile);
+  for (int w : {224, 192}) {
+    if (w < narrowest) break;
+    const double c = cost(w);
+    if (c < 0.95 * best_c) {
+      best_c = c;
+      best = w;
+    }
+  }
+  return best;
+}
+
 GemmPlan gemm_fwd_plan(int M, int N, int K, bool narrow) {
   const int tm = (M + kTile - 1) / kTile;
   const int tiles = tm * ((N + kTile - 1) / kTile);
   const int sp = choose_splits(tiles, K / 64, (double)M * N);
-  // One round that leaves a quarter of the CUs idle: 192-wide tiles, same
-  // split count, when they still fit one round.  (Measured on gfx950: 10%
-  // faster for N = 6144 at 2048 rows; a narrower tile does not pay where the
-  // wide plan is nearly full, the chip's clock rises when CUs idle.)
-  const int wgs = tiles * sp, wgs192 = tm * ((N + 191) / 192) * sp;
-  if (narrow && wgs <= 192 && wgs192 > wgs && wgs192 <= 256) return GemmPlan{192, sp};
-  return GemmPlan{kTile, sp};
+  // With the split count of the 256-wide plan, the NF4 kernel may take a
+  // narrower tile.  Examples: N = 28672 at 512 rows, 224 tiles of 256 but 256
+  // of 224; at 2048 rows 3.5 rounds of 256 but 4 full rounds of 224;
+  // N = 6144 at 2048 rows, 192 tiles of 256 but 256 of 192.
+  return GemmPlan{narrow ? tile_width(tm, N, sp, 192) : kTile, sp};
 }
 int gemm_bwd_splits(int M, int N, int K, int rr) {
   (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
@@ -1358,6 +1397,8 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
             "gemm_bwd: N=%d and rank %d must be multiples of 8", p.N, p.rr);
   if (p.M == 0 || p.K == 0) return LSQ_OK;
   p.splits = gemm_bwd_splits(p.M, p.N, p.K, p.rr);
+  // the NF4 DMA kernel also comes 224 columns wide (same split count)
+  p.bo = p.kind == LSQ_W_NF4 && bwd_dma_ok(p) ? tile_width((p.M + kTile - 1) / kTile, p.K, p.splits, 224) : kTile;
   const size_t need = gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr);
   LSQ_CHECK(need == 0 || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "gemm_bwd: needs %zu bytes of workspace",
             need);

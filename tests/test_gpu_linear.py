@@ -167,6 +167,9 @@ LINEAR_CASES = [
     # four ways, 256-wide unsplit
     (200, 1024, 7600, 16),
     (300, 256, 28680, 8),
+    # 224-wide tiles (two row tiles of 112 wide ones would leave 32 CUs idle),
+    # the last column tile ragged
+    (512, 256, 28632, 8),
 ]
 
 
@@ -218,11 +221,12 @@ def test_linear_bwd_with_no_tokens_clears_or_keeps_the_adapter_grads(gpu):
 IDENTITY_CASES = [
     # (M, K, N): 256-wide tiles with several row tiles; a ragged N with an odd
     # number of k-steps; the 192-wide forward tile (N = 6144 at 512 rows); a
-    # forward split four or more ways over its k-steps
+    # forward split four or more ways over its k-steps; the 224-wide tile
     (1024, 512, 1024),
     (600, 320, 600),
     (512, 512, 6144),
     (2048, 2048, 256),
+    (1024, 1024, 14336),   # 224-wide forward tiles: 256 of them against 224 of 256
 ]
 
 

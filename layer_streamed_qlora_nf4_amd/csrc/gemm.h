@@ -70,14 +70,16 @@ struct BwdParams {
 // reduction into a fixed number of ranges (a pure function of the shape),
 // writes float32 partials and sums them in split order in a second kernel.
 // Forward plan: tile width (256, or 224 or 192 for the NF4 DMA kernels when
-// 256-wide tiles would leave part of a round of workgroups idle) and split
-// count.  narrow: the launch can take a narrower tile (NF4 weights, operands
-// within 32-bit offsets).  The split count does not depend on narrow.
+// that fills the rounds of workgroups better) and split count.  narrow: the
+// launch can take a narrower tile (NF4 weights, operands within 32-bit
+// offsets).  The workspace sizes cover the plans with and without narrow.
 struct GemmPlan {
   int bn, splits;
 };
 GemmPlan gemm_fwd_plan(int M, int N, int K, bool narrow);
-int gemm_bwd_splits(int M, int N, int K, int rr);
+// Backward plan: output tile width (256, or 224 for the NF4 DMA kernel) and
+// split count of the reduction over N.
+GemmPlan gemm_bwd_plan(int M, int N, int K, bool narrow);
 size_t gemm_fwd_ws_bytes(int M, int N, int K);
 size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr);
 

@@ -1261,31 +1261,6 @@ void launch_reduce(const float* part, int splits, int M, int N, const uint16_t* 
     splitk_reduce_kernel<EPI_F32_RESID><<<grid, 256, 0, s>>>(part, splits, M, N, bias, resid, out, ldc);
 }
 
-// Split count from a small cost model: a launch runs in rounds of 256
-// workgroups (one large tile per CU), each round as long as its split's
-// reduction steps; every extra split writes and re-reads an fp32 partial of the
-// whole output.  Per-step time is the tile's flops at ~40% of one CU's MFMA
-// peak; partial traffic is priced at 4 TB/s.
-// Split count of a launch of 256 x 256 tiles: modelled time = whole rounds of
-// 256 workgroups x k-steps per split at 40% of the per-CU MFMA peak, plus the
-// fp32 partials of a split written and read back at 4 TB/s.
-int choose_splits(int tiles, int ksteps, double out_elems) {
-  const double step_us = 2.0 * kTile * kTile * BK / (0.4 * 2.5e15 / 256) * 1e6;
-  int best = 1;
-  double best_t = 1e30;
-  for (int sp = 1; sp <= 8; ++sp) {
-    if (sp > 1 && ksteps / sp < 4) break;
-    const double rounds = (double)((tiles * sp + 255) / 256);
-    const double steps = (double)((ksteps + sp - 1) / sp);
-    const double t = rounds * steps * step_us + (sp > 1 ? 8.0 * sp * out_elems / 4e6 : 0.0);
-    if (t < best_t * 0.97) {   // a split must win clearly to be taken
-      best_t = t;
-      best = sp;
-    }
-  }
-  return best;
-}
-
 template <int WK>
 void dispatch_fwd_epi(const FwdParams& p, int epi, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (epi == EPI_BF16) launch_fwd<WK, EPI_BF16>(p, s, e0, e1);
@@ -1303,56 +1278,62 @@ void dispatch_bwd_epi(const BwdParams& p, int epi, hipStream_t s, hipEvent_t e0,
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
-// Tile width along the output columns (n_cols of them) for tm row tiles and
-// sp splits: 256, or down to `narrowest` (224, 192) when a narrower tile
-// fills the rounds of 256 workgroups better.  Modelled time = rounds x the
-// tile's work per k-step, of which the activation DMA (about 15%) does not
-// shrink with the width; a narrower tile must win by 5% (on gfx950 the clock
-// rises a little when CUs idle in a partly filled round).  Every output
-// element sums the same products in the same order whatever the width, so
-// the choice never changes a result.
-static int tile_width(int tm, int n_cols, int sp, int narrowest) {
-  auto cost = [&](int w) {
-    const int wgs = tm * ((n_cols + w - 1) / w) * sp;
-    return (double)((wgs + 255) / 256) * (0.15 + 0.85 * w / 256.0);
-  };
-  int best = kTile;
-  double best_c = cost(kTile);
-  for (int w : {224, 192}) {
+// Tile width and split count of a launch from a small cost model.  A launch
+// runs in rounds of 256 workgroups (one tile per CU), each round as long as
+// its split's reduction steps at ~40% of one CU's MFMA peak for a 256-wide
+// tile; a narrower tile (224 or 192 output columns, NF4 DMA kernels only)
+// does proportionally less per step except for the activation DMA (about
+// 15%); every extra split writes and re-reads an fp32 partial of the whole
+// output, priced at 4 TB/s.  A split must win by 3% and a narrower tile by
+// 5% (on gfx950 the clock rises a little when CUs idle in a partly filled
+// round).  Examples: N = 28672 at 512 rows, 224 tiles of 256 but 256 of 224;
+// at 2048 rows 3.5 rounds of 256 but 4 full rounds of 224; N = 6144 at 2048
+// rows, 192 tiles of 256 but 256 of 192; the q/k/v product at 512 rows (a
+// 128-step reduction over the hi/lo input), 240 workgroups of 256 split 5
+// ways but 256 of 192 split 4 ways.  The width never changes a result (every
+// output element sums the same products in the same order); the split count
+// sets the order of the final fp32 sums.
+static GemmPlan plan_tiles(int tm, int n_cols, int ksteps, double out_elems, int narrowest) {
+  const double step_us = 2.0 * kTile * kTile * BK / (0.4 * 2.5e15 / 256) * 1e6;
+  GemmPlan best{kTile, 1};
+  double best_t = 1e30;
+  for (int w : {kTile, 224, 192}) {
     if (w < narrowest) break;
-    const double c = cost(w);
-    if (c < 0.95 * best_c) {
-      best_c = c;
-      best = w;
+    const double work = 0.15 + 0.85 * w / kTile, need = w == kTile ? 0.97 : 0.95;
+    for (int sp = 1; sp <= 8; ++sp) {
+      if (sp > 1 && ksteps / sp < 4) break;
+      const double rounds = (double)((tm * ((n_cols + w - 1) / w) * sp + 255) / 256);
+      const double steps = (double)((ksteps + sp - 1) / sp);
+      const double t = rounds * steps * step_us * work + (sp > 1 ? 8.0 * sp * out_elems / 4e6 : 0.0);
+      if (t < best_t * need) {
+        best_t = t;
+        best = GemmPlan{w, sp};
+      }
     }
   }
   return best;
 }
 
 GemmPlan gemm_fwd_plan(int M, int N, int K, bool narrow) {
-  const int tm = (M + kTile - 1) / kTile;
-  const int tiles = tm * ((N + kTile - 1) / kTile);
-  const int sp = choose_splits(tiles, K / 64, (double)M * N);
-  // With the split count of the 256-wide plan, the NF4 kernel may take a
-  // narrower tile.  Examples: N = 28672 at 512 rows, 224 tiles of 256 but 256
-  // of 224; at 2048 rows 3.5 rounds of 256 but 4 full rounds of 224;
-  // N = 6144 at 2048 rows, 192 tiles of 256 but 256 of 192.
-  return GemmPlan{narrow ? tile_width(tm, N, sp, 192) : kTile, sp};
+  return plan_tiles((M + kTile - 1) / kTile, N, K / 64, (double)M * N, narrow ? 192 : kTile);
 }
-int gemm_bwd_splits(int M, int N, int K, int rr) {
-  (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
-  return choose_splits(((M + kTile - 1) / kTile) * ((K + kTile - 1) / kTile), (N + 63) / 64, (double)M * K);
+GemmPlan gemm_bwd_plan(int M, int N, int K, bool narrow) {
+  return plan_tiles((M + kTile - 1) / kTile, K, (N + 63) / 64, (double)M * K, narrow ? 224 : kTile);
 }
-// Workspace of gemm_bwd: the split-K partials.
-static size_t gemm_bwd_part_bytes(int M, int N, int K, int rr) {
-  const int sp = gemm_bwd_splits(M, N, K, rr);
+// Workspace of gemm_bwd: the split-K partials, for whichever kernel the
+// launch can take.
+static size_t gemm_bwd_part_bytes(int M, int N, int K) {
+  const int sp = std::max(gemm_bwd_plan(M, N, K, true).splits, gemm_bwd_plan(M, N, K, false).splits);
   return sp > 1 ? ((size_t)sp * M * K * sizeof(float) + 255) / 256 * 256 : 0;
 }
 size_t gemm_fwd_ws_bytes(int M, int N, int K) {
-  const int sp = gemm_fwd_plan(M, N, K, true).splits;   // the tile width never changes the split count
+  const int sp = std::max(gemm_fwd_plan(M, N, K, true).splits, gemm_fwd_plan(M, N, K, false).splits);
   return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
-size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) { return gemm_bwd_part_bytes(M, N, K, rr); }
+size_t gemm_bwd_ws_bytes(int M, int N, int K, int rr) {
+  (void)rr;   // the LoRA term is added after the main loop, outside the split reduction
+  return gemm_bwd_part_bytes(M, N, K);
+}
 
 int gemm_fwd(const FwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_bytes, int* deferred_splits) {
   FwdParams p = p_in;
@@ -1396,9 +1377,9 @@ int gemm_bwd(const BwdParams& p_in, int epi, hipStream_t s, void* ws, size_t ws_
   LSQ_CHECK(p.N % 8 == 0 && p.rr % 8 == 0 && p.ldy % 8 == 0 && p.ldg % 8 == 0, LSQ_ERR_SHAPE,
             "gemm_bwd: N=%d and rank %d must be multiples of 8", p.N, p.rr);
   if (p.M == 0 || p.K == 0) return LSQ_OK;
-  p.splits = gemm_bwd_splits(p.M, p.N, p.K, p.rr);
-  // the NF4 DMA kernel also comes 224 columns wide (same split count)
-  p.bo = p.kind == LSQ_W_NF4 && bwd_dma_ok(p) ? tile_width((p.M + kTile - 1) / kTile, p.K, p.splits, 224) : kTile;
+  const GemmPlan plan = gemm_bwd_plan(p.M, p.N, p.K, p.kind == LSQ_W_NF4 && bwd_dma_ok(p));
+  p.bo = plan.bn;
+  p.splits = plan.splits;
   const size_t need = gemm_bwd_ws_bytes(p.M, p.N, p.K, p.rr);
   LSQ_CHECK(need == 0 || (ws && ws_bytes >= need), LSQ_ERR_WORKSPACE, "gemm_bwd: needs %zu bytes of workspace",
             need);

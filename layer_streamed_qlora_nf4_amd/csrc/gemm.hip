@@ -397,7 +397,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // 2048 rows gives 192 tiles of 256 but 256 of 192).  Each group decodes BN / 2
 // weight rows; the spare threads of a narrower tile load a duplicate row and
 // skip the store.
-template <int EPI, int BN>
+//
+// PAIR: the input is a hi/lo pair X = [X_hi | X_lo] over one weight (K = 2 Kw).
+// Without PAIR the reduction runs over the hi steps, then reads the weight
+// again for the lo steps.  With PAIR the steps alternate, hi then lo of the
+// same 64-wide weight block, and both read one decoded block: the block of
+// the next pair is decoded over the two decode halves of the current pair
+// (16 of a thread's 32 codes in each), so the weight is unpacked once for
+// two k-steps of matrix work.  A split covers whole pairs.
+template <int EPI, int BN, bool PAIR>
 __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   static_assert(BN % 32 == 0 && BN <= 256, "two 16-column-aligned wave columns per tile");
   constexpr int BM = 256, WM = 64, WN = BN / 2, TM = WM / 16, TN = WN / 16, GT = 256;
@@ -420,7 +428,7 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
 
   const int K = p.K, nk_all = K / BK, Kw = p.Kw, nkw = Kw / BK;
   const int split = ts.split;
-  const int per = (nk_all + p.splits - 1) / p.splits;
+  const int per = PAIR ? 2 * ((nkw + p.splits - 1) / p.splits) : (nk_all + p.splits - 1) / p.splits;
   const int kbeg = min(nk_all, split * per), nk = min(nk_all, kbeg + per);
 
   // X rows [m0, M), packed codes and absmax of weight rows [n0, N).
@@ -441,29 +449,36 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
   const uint32_t s_voff = (uint32_t)(brow * (Kw / 64) * 4);
 
   auto dma_x = [&](int kt, uint16_t* as) __attribute__((always_inline)) {
+    // PAIR: step kt reads X_hi (even kt) or X_lo (odd kt) of weight block kt / 2
+    const uint32_t koff = PAIR ? (uint32_t)((kt & 1) * Kw * 2 + (kt >> 1) * 128) : (uint32_t)(kt * 128);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rx, as + (xrow0 + i * 8) * 64, x_voff, (uint32_t)(kt * 128) + i * x_blk);
+    for (int i = 0; i < 4; ++i) dma16(rx, as + (xrow0 + i * 8) * 64, x_voff, koff + i * x_blk);
   };
-  // Two register sets for the prefetched codes, by k-step parity, so a decode
-  // half can issue the loads of k-step kt + 2 before it unpacks k-step kt + 1.
+  // Two register sets for the prefetched codes, by k-step parity (PAIR: by
+  // block parity), so a decode half can issue the loads of the step (block)
+  // after next before it unpacks the next one.
   uint4 rb[2];
   float rab[2];
-  auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
-    const int kq = kt - (kt >= nkw ? nkw : 0);   // the weight's reduction step
+  auto load_blk = [&](int kq, int set) __attribute__((always_inline)) {   // kq: the weight's block
     rb[set] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, (uint32_t)(kq * 32), 0));
     rab[set] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (uint32_t)(kq * 4), 0));
   };
-  auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) {
+  auto load_b = [&](int kt, int set) __attribute__((always_inline)) {
+    load_blk(kt - (kt >= nkw ? nkw : 0), set);   // the second pass reads the weight again
+  };
+  // Decode words [w0, w0 + nw) of the set's 4 (8 codes each) into the tile.
+  auto store_words = [&](uint16_t* bs, int set, int w0, int nw) __attribute__((always_inline)) {
     const uint32_t words[4] = {rb[set].x, rb[set].y, rb[set].z, rb[set].w};
     if (!bact) return;
     const NF4Planes pl = nf4_planes(rab[set]);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = w0; w < w0 + nw; ++w) {
       uint32_t o[4];
       decode_word_regs(words[w], pl, o);
       *reinterpret_cast<uint4*>(&bs[swz(brow, bh * 4 + w)]) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   };
+  auto store_b = [&](uint16_t* bs, int set) __attribute__((always_inline)) { store_words(bs, set, 0, 4); };
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -522,40 +537,109 @@ __global__ void __launch_bounds__(512, 1) gemm_fwd_nf4_dma_kernel(FwdParams p) {
     lds_barrier();
   };
 
-  // Prologue: stage 0 gets k-step kbeg (X by DMA, codes decoded), registers kbeg + 1.
-  if (kbeg < nk) {
-    dma_x(kbeg, As0);
-    load_b(kbeg, 0);
-  }
-  if (kbeg < nk) {
-    load_b(min(kbeg + 1, nk - 1), 1);
-    store_b(Bs0, 0);
-  }
-  wait_vmcnt<0>();
-  lds_barrier();
-
-  int kt = kbeg;
-  if (grp == 0) {
-    for (; kt + 1 < nk; kt += 2) {
-      mfma_half(kt, As0, Bs0, As1);
-      decode_half(kt, Bs1, 0);
-      mfma_half(kt + 1, As1, Bs1, As0);
-      decode_half(kt + 1, Bs0, 1);
+  if constexpr (PAIR) {
+    // Pairs of steps (hi, lo) of one block read one B stage; the block
+    // after it is decoded into the other stage over the pair's two decode
+    // halves (the first also loads the codes of the block after that), so the
+    // loop runs over two pairs, one per B stage.  bl: the split's last block;
+    // loads past it are clamped and decoded into the stage nobody reads any
+    // more.
+    const int bl = (nk - 1) >> 1;
+    auto dec_first = [&](uint16_t* bn, int set, int lset, int blk) __attribute__((always_inline)) {
+      load_blk(min(blk, bl), lset);
+      store_words(bn, set, 0, 2);
+      wait_vmcnt<2>();
+      lds_barrier();
+    };
+    auto dec_second = [&](uint16_t* bn, int set) __attribute__((always_inline)) {
+      store_words(bn, set, 2, 2);
+      wait_vmcnt<0>();
+      lds_barrier();
+    };
+    // Prologue: stage 0 gets block kbeg / 2 and X of step kbeg; registers the next block.
+    if (kbeg < nk) {
+      dma_x(kbeg, As0);
+      load_blk(kbeg >> 1, 0);
     }
-    if (kt < nk) {
-      last_mfma(As0, Bs0);
-      last_wait();
+    if (kbeg < nk) {
+      load_blk(min((kbeg >> 1) + 1, bl), 1);
+      store_b(Bs0, 0);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+
+    int kt = kbeg;
+    if (grp == 0) {
+      for (; kt + 3 < nk; kt += 4) {
+        mfma_half(kt, As0, Bs0, As1);
+        dec_first(Bs1, 1, 0, (kt >> 1) + 2);
+        mfma_half(kt + 1, As1, Bs0, As0);
+        dec_second(Bs1, 1);
+        mfma_half(kt + 2, As0, Bs1, As1);
+        dec_first(Bs0, 0, 1, (kt >> 1) + 3);
+        mfma_half(kt + 3, As1, Bs1, As0);
+        dec_second(Bs0, 0);
+      }
+      if (kt < nk) {   // one pair left, on stage 0
+        mfma_half(kt, As0, Bs0, As1);
+        last_wait();
+        last_mfma(As1, Bs0);
+        last_wait();
+      }
+    } else {
+      for (; kt + 3 < nk; kt += 4) {
+        dec_first(Bs1, 1, 0, (kt >> 1) + 2);
+        mfma_half(kt, As0, Bs0, As1);
+        dec_second(Bs1, 1);
+        mfma_half(kt + 1, As1, Bs0, As0);
+        dec_first(Bs0, 0, 1, (kt >> 1) + 3);
+        mfma_half(kt + 2, As0, Bs1, As1);
+        dec_second(Bs0, 0);
+        mfma_half(kt + 3, As1, Bs1, As0);
+      }
+      if (kt < nk) {
+        last_wait();
+        mfma_half(kt, As0, Bs0, As1);
+        last_wait();
+        last_mfma(As1, Bs0);
+      }
     }
   } else {
-    for (; kt + 1 < nk; kt += 2) {
-      decode_half(kt, Bs1, 0);
-      mfma_half(kt, As0, Bs0, As1);
-      decode_half(kt + 1, Bs0, 1);
-      mfma_half(kt + 1, As1, Bs1, As0);
+    // Prologue: stage 0 gets k-step kbeg (X by DMA, codes decoded), registers kbeg + 1.
+    if (kbeg < nk) {
+      dma_x(kbeg, As0);
+      load_b(kbeg, 0);
     }
-    if (kt < nk) {
-      last_wait();
-      last_mfma(As0, Bs0);
+    if (kbeg < nk) {
+      load_b(min(kbeg + 1, nk - 1), 1);
+      store_b(Bs0, 0);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+
+    int kt = kbeg;
+    if (grp == 0) {
+      for (; kt + 1 < nk; kt += 2) {
+        mfma_half(kt, As0, Bs0, As1);
+        decode_half(kt, Bs1, 0);
+        mfma_half(kt + 1, As1, Bs1, As0);
+        decode_half(kt + 1, Bs0, 1);
+      }
+      if (kt < nk) {
+        last_mfma(As0, Bs0);
+        last_wait();
+      }
+    } else {
+      for (; kt + 1 < nk; kt += 2) {
+        decode_half(kt, Bs1, 0);
+        mfma_half(kt, As0, Bs0, As1);
+        decode_half(kt + 1, Bs0, 1);
+        mfma_half(kt + 1, As1, Bs1, As0);
+      }
+      if (kt < nk) {
+        last_wait();
+        last_mfma(As0, Bs0);
+      }
     }
   }
   wait_vmcnt<0>();   // the clamped DMA / loads of the final pair
@@ -1219,6 +1303,16 @@ bool bwd_dma_ok(const BwdParams& p) {
 // (the NF4 one its activations, the bf16 one both operands); larger operands
 // and the backward's bf16 weights use the register-path kernels.
 // e0, e1: the timing events attached to the dispatch (null when timing is off).
+template <int EPI, bool PAIR>
+void launch_fwd_nf4(const FwdParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.bn == 192)
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 192, PAIR>, grid, block, 0, s, e0, e1, 0, p);
+  else if (p.bn == 224)
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 224, PAIR>, grid, block, 0, s, e0, e1, 0, p);
+  else
+    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 256, PAIR>, grid, block, 0, s, e0, e1, 0, p);
+}
+
 template <int WK, int EPI>
 void launch_fwd(const FwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((p.M + kTile - 1) / kTile) * ((p.N + p.bn - 1) / p.bn);
@@ -1227,12 +1321,14 @@ void launch_fwd(const FwdParams& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
     hipExtLaunchKernelGGL(gemm_fwd_bf16_dma_kernel<EPI>, grid, block, 0, s, e0, e1, 0, p);
   else if (WK != LSQ_W_NF4 || !fwd_dma_ok(p))
     hipExtLaunchKernelGGL(gemm_fwd_pp_kernel<WK, EPI>, grid, block, 0, s, e0, e1, 0, p);
-  else if (p.bn == 192)
-    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 192>, grid, block, 0, s, e0, e1, 0, p);
-  else if (p.bn == 224)
-    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 224>, grid, block, 0, s, e0, e1, 0, p);
-  else
-    hipExtLaunchKernelGGL(gemm_fwd_nf4_dma_kernel<EPI, 256>, grid, block, 0, s, e0, e1, 0, p);
+  else if constexpr (EPI == EPI_F32) {
+    if (p.Kw != p.K)   // the hi/lo pair of the q/k/v product
+      launch_fwd_nf4<EPI, true>(p, grid, block, s, e0, e1);
+    else
+      launch_fwd_nf4<EPI, false>(p, grid, block, s, e0, e1);
+  } else {
+    launch_fwd_nf4<EPI, false>(p, grid, block, s, e0, e1);
+  }
 }
 
 template <int WK, int EPI>

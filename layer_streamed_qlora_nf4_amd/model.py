@@ -28,7 +28,10 @@ def _ptr(t):
 class Store:
     """One layer blob per decoder layer in a host arena (pinned unless refused)."""
 
-    def __init__(self, cfg, device="cuda", flags=0, layer_source=None):
+    def __init__(self, cfg, device="cuda", flags=0, layer_source=None, distinct_layers=None):
+        """distinct_layers: when set, layer i takes the weights drawn for layer
+        i mod distinct_layers (each blob is still quantized and written on its
+        own), so a deep stack is built without drawing every layer on the host."""
         self.cfg = cfg
         self.ccfg = lib.model_cfg(cfg)
         h = C.c_void_p()
@@ -39,8 +42,15 @@ class Store:
         src = layer_source or (lambda i: synth.layer_weights(cfg, cfg.wid, i))
         stream = torch.cuda.current_stream(device)
         staging = torch.empty(self.layer_bytes + 256, dtype=torch.uint8, device=device)
+        nd = min(distinct_layers, cfg.n_layers) if distinct_layers else cfg.n_layers
+        drawn = {}
         for i in range(cfg.n_layers):
-            w = src(i)
+            d = i % nd
+            w = drawn.get(d)
+            if w is None:
+                w = src(d)
+                if nd < cfg.n_layers:
+                    drawn[d] = w   # kept on the host: the device holds one layer's weights at a time
             dev = {k: _bits_to_dev(v, device) for k, v in w.items()}
             ls = lib.LayerSrc()
             for j, name in enumerate(PROJ):
@@ -53,7 +63,7 @@ class Store:
             lib.call("shard_store_write_layer", h, i, C.byref(ls), _ptr(staging), staging.numel(),
                      lib.stream_handle(stream))
             del dev
-        del staging
+        del staging, drawn
 
     @classmethod
     def load(cls, cfg, path, flags=0):

@@ -442,3 +442,22 @@ def test_pool_copies_on_a_stream_that_runs_beside_compute(gpu):
         assert exact == total == cfg.n_layers * 14
         r.close()
     store.close()
+
+
+def test_store_with_repeated_layer_weights(gpu):
+    """A store whose layers reuse the weights of the first few (the deep
+    stack's build shortcut) holds, past each blob's header, the same bytes as
+    the full store's blob of layer i mod n, and every header names its own
+    layer."""
+    cfg = configs.TINY.with_(name="tiny-5L-rep", n_layers=5, wid=43)
+    print_case(test="store_repeated_layers", layers=cfg.n_layers)
+    full = model.Store(cfg)
+    rep = model.Store(cfg, distinct_layers=2)
+    hdr = 4096
+    for i in range(cfg.n_layers):
+        a, b = rep.host_blob(i), full.host_blob(i % 2)
+        assert np.array_equal(a[hdr:], b[hdr:]), f"layer {i}"
+        assert np.array_equal(a[:hdr], full.host_blob(i)[:hdr]), f"header of layer {i}"
+    assert not np.array_equal(full.host_blob(2)[hdr:], full.host_blob(0)[hdr:])
+    rep.close()
+    full.close()

@@ -261,9 +261,11 @@ int shard_store_load(const char* path, const lsq_model_cfg* expect, int32_t flag
  * N pre-allocated VRAM slots (2..8, default 2) and a dedicated copy stream:
  * layer i+1 is copied while layer i computes (LS-docs "Turn it on":
  * stream_buffers; "How it works").  Handoff is by hipEvent: a copy into a slot
- * waits on that slot's free event, recorded on the compute stream after the
- * last kernel that read the slot's previous layer; the compute stream waits on
- * the slot's ready event before reading it.  A layer still in a slot is not
+ * is issued once that slot's free event, recorded on the compute stream after
+ * the last kernel that read the slot's previous layer, has completed (the host
+ * waits for it in stream_layer_prefetch; a copy stream waiting on the compute
+ * stream's event instead slowed the copies and the kernels beside them); the
+ * compute stream waits on the slot's ready event before reading it.  A layer still in a slot is not
  * copied again (LS-docs "Roadmap": layer 0 at the step boundary; this pool
  * applies the same rule to every layer, e.g. at the forward/backward turn).
  * Resident mode (flags LSQ_POOL_RESIDENT, n_buffers == n_layers) copies every
@@ -293,7 +295,10 @@ void layer_pool_destroy(lsq_pool* pool);
  * replaced or was not given one). */
 int layer_pool_copy_stream(const lsq_pool* pool, void** stream);
 /* Enqueue the copy of `layer` into a free slot on the copy stream; no-op if it
- * is already in a slot.  LSQ_ERR_STATE if every slot is held. */
+ * is already in a slot.  Blocks the calling thread until the chosen slot's
+ * free event has completed (its work is already enqueued, so the wait ends):
+ * enqueue the current layer's kernels before prefetching the next.
+ * LSQ_ERR_STATE if every slot is held. */
 int stream_layer_prefetch(lsq_pool* pool, int32_t layer);
 /* Make the compute stream wait until `layer` is in its slot; returns the slot's
  * device address.  LSQ_ERR_STATE if the layer was never prefetched. */
